@@ -1,0 +1,194 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) hybrid compressed attention library (libcsa.so).
+ *
+ * The method is the hybrid attention of the DeepSeek-V4 write-ups ("DeepSeek-V4 深度分析报告",
+ * section 2.1 "混合注意力架构：CSA + HCA", Figure 2 and the list "其他注意力技术细节";
+ * stuffyNLP review, CSA/HCA and RoPE/sink paragraphs):
+ *   CSA  every m = 4 tokens become one compressed KV entry pooled from 2m = 8 tokens (the
+ *        entry's block and the previous one); a Lightning Indexer scores the entries and
+ *        the top-k are attended together with a 128-token sliding window;
+ *   HCA  every m' = 128 tokens become one entry (single block); all entries are attended
+ *        densely together with the same window;
+ *   both use shared-KV MQA (an entry is key and value for every head), partial RoPE on
+ *   the last 64 dims with an inverse RoPE of the output, and one learnable sink logit per
+ *   head that lets the attention weights sum to less than one.
+ *
+ * Conventions (all entry points)
+ *   - Every pointer argument that names tensor data is a DEVICE pointer, owned by the
+ *     caller.  Descriptor structs themselves (csa_seqs, csa_rows) live in host memory.
+ *   - No entry point allocates, frees or synchronises; work is enqueued on `stream`
+ *     (a hipStream_t passed as void*; NULL = the null stream) and runs asynchronously.
+ *   - Outputs are fully overwritten over the rows the call defines; nothing else is touched.
+ *   - Arguments are validated on the host before anything is enqueued; a failure returns
+ *     a negative csa_status and enqueues nothing.  csa_last_error() then describes it.
+ *   - Device-side data (offsets, lengths, idx) is trusted: it must satisfy the stated
+ *     preconditions.  idx entries of -1 are skipped.
+ *   - Results are batch invariant: every token's outputs are bit-identical whatever other
+ *     tokens share the launch ("DeepSeek-V4 深度分析报告" section 3.3; shijienb.com article
+ *     on batch invariance).  No reduction is split in a batch-dependent way.
+ *   - The library is thread-safe; the error string is per thread.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_EINVAL = -1,        /* invalid argument (null pointer, bad size, bad combination) */
+  CSA_EUNSUPPORTED = -2,  /* valid but not implemented (dtype / dim combination)        */
+  CSA_EWORKSPACE = -3,    /* workspace too small for a mandatory buffer                 */
+  CSA_EHIP = -4           /* the HIP runtime reported an error while enqueuing           */
+} csa_status;
+
+/* Row formats.  D = csa_rows.dim.
+ *   CSA_F32      D float32 values.
+ *   CSA_BF16     D bfloat16 values.
+ *   CSA_KV_SPLIT the KV-cache format of the pages (RoPE dims in BF16, the rest in FP8 with
+ *                the 1x128 scaling kept from DeepSeek-V3): the first Dn = D - 64 dims as OCP
+ *                fp8 e4m3fn codes (1 byte each), followed by the last 64 dims as bfloat16;
+ *                `scales` holds ceil(Dn/128) float32 per row (row-major, contiguous), one per
+ *                128-dim block of the fp8 part; value = code * scale.
+ *   CSA_MXFP4    OCP MXFP4: D/2 bytes of packed e2m1 codes (element 2i in the low nibble of
+ *                byte i); `scales` holds D/32 e8m0 bytes per row (contiguous); value =
+ *                e2m1 * 2^(e8m0 - 127). */
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_KV_SPLIT = 2, CSA_MXFP4 = 3 } csa_dtype;
+
+#define CSA_KV_SPLIT_BF16_DIMS 64
+
+typedef struct {
+  void* data;          /* device pointer to row 0                                          */
+  void* scales;        /* device pointer to the scales of row 0 (KV_SPLIT, MXFP4), else NULL */
+  int32_t dtype;       /* csa_dtype                                                        */
+  int32_t dim;         /* D: 32..512, a multiple of 32                                     */
+  int64_t row_stride;  /* bytes between rows of `data`; 0 = packed; multiple of 16         */
+} csa_rows;
+
+/* Ragged batch.  Sequence b has n_b = q_off[b+1] - q_off[b] new (query) tokens, stored as
+ * consecutive rows q_off[b] .. q_off[b+1]-1 of every per-token array (q, qI, w, idx, out,
+ * lse, score); its context length L_b = ctx_len[b] includes them, so query j of sequence b
+ * sits at position p = L_b - n_b + j.  Compressed entry i of sequence b is row
+ * entry_off[b] + i of the entry pools; token position t of sequence b is row
+ * tok_off[b] + (t - tok_lo[b]) of the token pools (valid for t >= tok_lo[b]).
+ * The arrays are device pointers; the host scalars only size launch grids and must be
+ * upper bounds of the device data (total_q exact). */
+typedef struct {
+  int32_t n_seqs;
+  const int32_t* q_off;      /* [n_seqs + 1], q_off[0] = 0, non-decreasing                 */
+  const int32_t* ctx_len;    /* [n_seqs], L_b >= n_b                                         */
+  const int64_t* entry_off;  /* [n_seqs]                                                     */
+  const int64_t* tok_off;    /* [n_seqs]                                                     */
+  const int32_t* tok_lo;     /* [n_seqs]                                                     */
+  int32_t total_q;           /* q_off[n_seqs]                                                */
+  int32_t max_q;             /* >= every n_b                                                 */
+  int32_t max_ctx;           /* >= every L_b                                                 */
+} csa_seqs;
+
+/* ---------------------------------------------------------------------------------------
+ * csa_compress -- KV compression (section 2.1: CSA "KV 压缩", overlapped 4:1 from 2m tokens;
+ * HCA 128:1 single block; Figure 2 "KV Compress").  Softmax-gated pooling: for entry i the
+ * source positions are S_i = {(i-overlap)*ratio .. (i+1)*ratio - 1} minus those below 0;
+ * slot(j) = j - (i-overlap)*ratio; per channel d,
+ *     w_j = softmax_{j in S_i}( z[j,d] + bias[slot(j), d] ),   e_i[d] = sum_j w_j c[j,d],
+ * then, if rope_dims > 0, the last rope_dims dims of e_i are rotated at position i*ratio
+ * (pairs (2q, 2q+1), frequency rope_theta^(-2q/rope_dims)).
+ * Writes the entries completed by each sequence's new tokens: i in
+ * [floor((L_b - n_b)/ratio), floor(L_b/ratio)), to row entry_off[b] + i of `entries`.
+ *   c        token rows (F32, BF16 or KV_SPLIT), dim D
+ *   z        gate-logit rows (F32 or BF16), dim D
+ *   bias     device float32 [(1 + overlap) * ratio, D], row-major
+ *   ratio    1..128;  overlap 0 or 1;  rope_dims even, 0..min(D, 128)
+ *   entries  output rows (F32, BF16, KV_SPLIT or MXFP4), dim D.  KV_SPLIT output: scale =
+ *            fp32(amax/448) per 128-dim block, code = e4m3fn RNE of value/scale, saturating;
+ *            an all-zero block gets scale 0.  MXFP4 output: per 32 dims, exponent
+ *            E = floor(log2 amax) - 2 clamped to [-127,127] (amax = 0 -> -127), element =
+ *            e2m1 RNE of value/2^E saturating at +-6.
+ * Precondition: the token pools hold every source position of the written entries. */
+int csa_compress(const csa_seqs* seqs, const csa_rows* c, const csa_rows* z, const float* bias, int ratio,
+                 int overlap, int rope_dims, double rope_theta, const csa_rows* entries, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_index_score -- Lightning-Indexer scores (section 2.1: DSA's lightweight indexer
+ * chooses the top-k compressed entries; Figure 2 "Lightning Indexer FP4 Precision";
+ * the stuffyNLP review names the indexer of DeepSeek-V3.2-Exp).  For query token t at
+ * position p, for every visible entry i < V(p) = floor((p+1)/ratio):
+ *     score[t, i] = sum_{h < n_I} w[t,h] * max(0, sum_d qI[t,h,d] * kI[entry_off[b]+i, d])
+ * with heads summed in ascending order.  Columns i >= V(p) are not written.
+ *   qI      rows [total_q * n_I, d_I] (F32, BF16 or MXFP4); row t*n_I + h
+ *   w       device float32 [total_q, n_I]
+ *   kI      entry pool rows (same dtype as qI), dim d_I
+ *   score   device float32 [total_q, score_stride]; score_stride >= floor(max_ctx/ratio) */
+int csa_index_score(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
+                    float* score, int64_t score_stride, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_topk -- top-k selection (section 2.1: select the k most relevant compressed entries;
+ * k = 1024 for V4-Pro, 512 for V4-Flash).  For token t with V = V(p) candidates
+ * score[t, 0..V-1]: the k largest, equal scores ranked by the lower index (+0 and -0
+ * compare equal), written to idx[t, 0..k-1] in ascending index order; when V <= k all V
+ * are selected and the rest of the row is -1.  Exact and deterministic.
+ *   k 1..4096;  idx device int32 [total_q, k] */
+int csa_topk(const csa_seqs* seqs, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
+             void* stream);
+
+/* csa_index_topk -- csa_index_score into the workspace followed by csa_topk.
+ * ws_bytes must be >= csa_workspace_bytes(CSA_OP_INDEX_TOPK, ...). */
+int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
+                   int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_attend -- sparse shared-KV MQA over the selected entries plus the sliding window
+ * (section 2.1 CSA, "滑动窗口分支"; Figure 2 "Top-k Sparse Attention" with the window
+ * "Concat"-ed in; "其他注意力技术细节": shared-KV MQA, partial RoPE, attention sink).
+ * For query token t at position p and head h, the key/value rows are
+ *     K = [ kv[entry_off[b] + idx[t,j]] : j = 0..k-1, idx >= 0 ]   (stored already rotated)
+ *      ++ [ rot(tok[t'], t') : t' = max(0, p-n_win+1, tok_lo[b]) .. p ]
+ * and with l_j = scale * <rot(q[t,h], p), K_j>:
+ *     Z = e^{sink[h]} + sum_j e^{l_j},  o = sum_j e^{l_j} K_j / Z,
+ *     out[t,h] = rot^-1(o, p),  lse[t,h] = log Z   (natural log).
+ * rot rotates the last rope_dims dims as in csa_compress.  q and tok rows are passed
+ * un-rotated.
+ *   q     rows [total_q * n_h, D] (F32 or BF16); row t*n_h + h
+ *   kv    entry pool (F32, BF16 or KV_SPLIT), dim D;  tok  token pool, same dtype as kv
+ *   idx   device int32 [total_q, k];  sink device float32 [n_h] (may be -inf)
+ *   out   rows [total_q * n_h, D] (F32 or BF16);  lse device float32 [total_q, n_h] or NULL
+ *   n_h 1..128;  n_win 0..1024;  k 1..4096
+ *   ws/ws_bytes  optional scratch.  With at least csa_workspace_bytes(CSA_OP_CSA_ATTEND, ...)
+ *         bytes the key list of each token is processed by several workgroups in parallel;
+ *         with less (or NULL) by one workgroup per token and head group.  Both give
+ *         bit-identical results: each token's key list is cut into fixed chunks whose
+ *         partial softmax states are folded in chunk order, starting from the sink. */
+int csa_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows* kv, const int32_t* idx, int k,
+               const csa_rows* tok, int n_win, const float* sink, float scale, int rope_dims, double rope_theta,
+               const csa_rows* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* hca_attend -- dense attention over all visible entries i < floor((p+1)/ratio) plus the
+ * window (section 2.1 HCA "密集注意力" and its window branch; Figure 2 "Dense Attention on All
+ * Compressed KV Entries").  Same arguments and semantics as csa_attend with the entry list
+ * 0 .. V(p)-1 in place of idx.  ratio 1..1048576 (128 for HCA; 4 gives dense CSA). */
+int hca_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows* kv, int ratio, const csa_rows* tok,
+               int n_win, const float* sink, float scale, int rope_dims, double rope_theta, const csa_rows* out,
+               float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace sizing (host only; reads only the host scalars of `seqs`). */
+enum { CSA_OP_INDEX_TOPK = 1, CSA_OP_CSA_ATTEND = 2, CSA_OP_HCA_ATTEND = 3 };
+/* op CSA_OP_INDEX_TOPK: ratio, k used; CSA_OP_CSA_ATTEND: n_h, dim, k, n_win used;
+ * CSA_OP_HCA_ATTEND: n_h, dim, ratio, n_win used.  Returns 0 for an invalid op. */
+size_t csa_workspace_bytes(int op, const csa_seqs* seqs, int n_h, int dim, int k, int ratio, int n_win);
+
+const char* csa_strerror(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* csa_last_error(void);
+/* Library version: major*10000 + minor*100 + patch. */
+int csa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

@@ -1,0 +1,348 @@
+// C ABI of libcsa.so: host-side validation, error reporting and dispatch to the gfx950
+// kernels.  Nothing here allocates device memory or synchronises.  Every argument is
+// checked before any launch; a failure returns a negative csa_status and leaves a
+// thread-local description readable through csa_last_error().
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/csa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return CSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CSA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t row_bytes(int dtype, int dim) {
+  switch (dtype) {
+    case CSA_F32: return 4LL * dim;
+    case CSA_BF16: return 2LL * dim;
+    case CSA_KV_SPLIT: return (int64_t)(dim - CSA_KV_SPLIT_BF16_DIMS) + 2LL * CSA_KV_SPLIT_BF16_DIMS;
+    case CSA_MXFP4: return dim / 2;
+    default: return -1;
+  }
+}
+
+const char* dtype_name(int dt) {
+  switch (dt) {
+    case CSA_F32: return "F32";
+    case CSA_BF16: return "BF16";
+    case CSA_KV_SPLIT: return "KV_SPLIT";
+    case CSA_MXFP4: return "MXFP4";
+    default: return "?";
+  }
+}
+
+// Validates a csa_rows descriptor; `allowed` is a bit mask of csa_dtype values.
+int check_rows(const csa_rows* r, const char* name, unsigned allowed) {
+  if (!r) return fail(CSA_EINVAL, "%s: null descriptor", name);
+  if (!r->data) return fail(CSA_EINVAL, "%s: null data pointer", name);
+  if (r->dtype < 0 || r->dtype > 3) return fail(CSA_EINVAL, "%s: unknown dtype %d", name, r->dtype);
+  if (!(allowed & (1u << r->dtype)))
+    return fail(CSA_EUNSUPPORTED, "%s: dtype %s not supported here", name, dtype_name(r->dtype));
+  if (r->dim < 32 || r->dim > csa::kMaxDim || r->dim % 32)
+    return fail(CSA_EINVAL, "%s: dim %d must be a multiple of 32 in [32, 512]", name, r->dim);
+  if (r->dtype == CSA_KV_SPLIT && r->dim < 2 * CSA_KV_SPLIT_BF16_DIMS)
+    return fail(CSA_EINVAL, "%s: KV_SPLIT needs dim >= 128 (got %d)", name, r->dim);
+  if ((r->dtype == CSA_KV_SPLIT || r->dtype == CSA_MXFP4) && !r->scales)
+    return fail(CSA_EINVAL, "%s: %s rows need a scales pointer", name, dtype_name(r->dtype));
+  const int64_t rb = row_bytes(r->dtype, r->dim);
+  if (r->row_stride != 0 && (r->row_stride < rb || r->row_stride % 16))
+    return fail(CSA_EINVAL, "%s: row_stride %lld must be 0 or a multiple of 16 that is >= %lld", name,
+                (long long)r->row_stride, (long long)rb);
+  if (r->row_stride == 0 && rb % 4)
+    return fail(CSA_EINVAL, "%s: packed rows of %lld bytes are not 4-byte aligned", name, (long long)rb);
+  return CSA_OK;
+}
+
+csa::RowsDev dev_rows(const csa_rows* r) {
+  csa::RowsDev d;
+  d.data = static_cast<const uint8_t*>(r->data);
+  d.scales = static_cast<const uint8_t*>(r->scales);
+  d.dtype = r->dtype;
+  d.dim = r->dim;
+  d.stride = r->row_stride ? r->row_stride : row_bytes(r->dtype, r->dim);
+  return d;
+}
+
+csa::RowsOut dev_out(const csa_rows* r) {
+  csa::RowsOut d;
+  d.data = static_cast<uint8_t*>(r->data);
+  d.scales = static_cast<uint8_t*>(r->scales);
+  d.dtype = r->dtype;
+  d.dim = r->dim;
+  d.stride = r->row_stride ? r->row_stride : row_bytes(r->dtype, r->dim);
+  return d;
+}
+
+int check_seqs(const csa_seqs* s) {
+  if (!s) return fail(CSA_EINVAL, "seqs: null descriptor");
+  if (s->n_seqs < 0) return fail(CSA_EINVAL, "seqs: n_seqs %d < 0", s->n_seqs);
+  if (s->total_q < 0 || s->max_q < 0 || s->max_ctx < 0)
+    return fail(CSA_EINVAL, "seqs: negative total_q/max_q/max_ctx");
+  if (s->n_seqs == 0) {
+    if (s->total_q != 0) return fail(CSA_EINVAL, "seqs: total_q %d with no sequences", s->total_q);
+    return CSA_OK;
+  }
+  if (!s->q_off || !s->ctx_len || !s->entry_off || !s->tok_off || !s->tok_lo)
+    return fail(CSA_EINVAL, "seqs: null device array");
+  if (s->max_q > s->max_ctx) return fail(CSA_EINVAL, "seqs: max_q %d > max_ctx %d", s->max_q, s->max_ctx);
+  if ((int64_t)s->total_q > (int64_t)s->n_seqs * s->max_q)
+    return fail(CSA_EINVAL, "seqs: total_q %d exceeds n_seqs*max_q", s->total_q);
+  return CSA_OK;
+}
+
+csa::SeqsDev dev_seqs(const csa_seqs* s) {
+  csa::SeqsDev d;
+  d.q_off = s->q_off;
+  d.ctx_len = s->ctx_len;
+  d.entry_off = s->entry_off;
+  d.tok_off = s->tok_off;
+  d.tok_lo = s->tok_lo;
+  d.n_seqs = s->n_seqs;
+  d.total_q = s->total_q;
+  return d;
+}
+
+int make_rope(int rope_dims, double theta, int dim, csa::RopeTab* tab) {
+  if (rope_dims < 0 || rope_dims % 2 || rope_dims > dim || rope_dims / 2 > csa::kMaxRopePairs)
+    return fail(CSA_EINVAL, "rope_dims %d must be even, <= dim and <= %d", rope_dims, 2 * csa::kMaxRopePairs);
+  if (rope_dims > 0 && !(theta > 1.0) )
+    return fail(CSA_EINVAL, "rope_theta %g must be > 1", theta);
+  std::memset(tab, 0, sizeof(*tab));
+  tab->dims = rope_dims;
+  for (int q = 0; q < rope_dims / 2; ++q) tab->inv_freq[q] = std::pow(theta, -2.0 * q / rope_dims);
+  return CSA_OK;
+}
+
+constexpr unsigned bit(int dt) { return 1u << dt; }
+
+int attend_common(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows* kv, const csa_rows* tok,
+                  int n_win, const float* sink, float scale, int rope_dims, double rope_theta, const csa_rows* out,
+                  csa::AttendArgs* a) {
+  int st;
+  if ((st = check_seqs(seqs))) return st;
+  if ((st = check_rows(q, "q", bit(CSA_F32) | bit(CSA_BF16)))) return st;
+  if ((st = check_rows(kv, "kv", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_KV_SPLIT)))) return st;
+  if ((st = check_rows(tok, "tok", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_KV_SPLIT)))) return st;
+  if ((st = check_rows(out, "out", bit(CSA_F32) | bit(CSA_BF16)))) return st;
+  if (kv->dim != q->dim || tok->dim != q->dim || out->dim != q->dim)
+    return fail(CSA_EINVAL, "q/kv/tok/out dims differ (%d/%d/%d/%d)", q->dim, kv->dim, tok->dim, out->dim);
+  if (kv->dtype != tok->dtype) return fail(CSA_EINVAL, "kv and tok must share a dtype");
+  if (kv->dtype == CSA_F32 && (q->dtype != CSA_F32 || out->dtype != CSA_F32))
+    return fail(CSA_EUNSUPPORTED, "F32 kv needs F32 q and out");
+  if (kv->dtype != CSA_F32 && (q->dtype != CSA_BF16 || out->dtype != CSA_BF16))
+    return fail(CSA_EUNSUPPORTED, "BF16/KV_SPLIT kv needs BF16 q and out");
+  if (n_h < 1 || n_h > 128) return fail(CSA_EINVAL, "n_h %d out of [1, 128]", n_h);
+  if (n_win < 0 || n_win > 1024) return fail(CSA_EINVAL, "n_win %d out of [0, 1024]", n_win);
+  if (!sink) return fail(CSA_EINVAL, "sink: null pointer");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(CSA_EINVAL, "scale must be finite and > 0");
+  if ((st = make_rope(rope_dims, rope_theta, q->dim, &a->rope))) return st;
+  a->S = dev_seqs(seqs);
+  a->q = dev_rows(q);
+  a->kv = dev_rows(kv);
+  a->tok = dev_rows(tok);
+  a->out = dev_out(out);
+  a->sink = sink;
+  a->n_h = n_h;
+  a->n_win = n_win;
+  a->scale_log2 = scale * csa::kLog2e;
+  a->max_ctx = seqs->max_ctx;
+  a->max_q = seqs->max_q;
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_version(void) { return 100; }
+
+const char* csa_strerror(int status) {
+  switch (status) {
+    case CSA_OK: return "success";
+    case CSA_EINVAL: return "invalid argument";
+    case CSA_EUNSUPPORTED: return "unsupported dtype or shape";
+    case CSA_EWORKSPACE: return "workspace too small";
+    case CSA_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* csa_last_error(void) { return g_err; }
+
+int csa_compress(const csa_seqs* seqs, const csa_rows* c, const csa_rows* z, const float* bias, int ratio, int overlap,
+                 int rope_dims, double rope_theta, const csa_rows* entries, void* stream) {
+  int st;
+  if ((st = check_seqs(seqs))) return st;
+  if ((st = check_rows(c, "c", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_KV_SPLIT)))) return st;
+  if ((st = check_rows(z, "z", bit(CSA_F32) | bit(CSA_BF16)))) return st;
+  if ((st = check_rows(entries, "entries", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_KV_SPLIT) | bit(CSA_MXFP4))))
+    return st;
+  if (z->dim != c->dim || entries->dim != c->dim)
+    return fail(CSA_EINVAL, "c/z/entries dims differ (%d/%d/%d)", c->dim, z->dim, entries->dim);
+  if (!bias) return fail(CSA_EINVAL, "bias: null pointer");
+  if (ratio < 1 || ratio > 128) return fail(CSA_EINVAL, "ratio %d out of [1, 128]", ratio);
+  if (overlap != 0 && overlap != 1) return fail(CSA_EINVAL, "overlap must be 0 or 1 (got %d)", overlap);
+  csa::RopeTab rope;
+  if ((st = make_rope(rope_dims, rope_theta, c->dim, &rope))) return st;
+  if (seqs->n_seqs == 0) return ok();
+  hipError_t e = csa::launch_compress(dev_seqs(seqs), dev_rows(c), dev_rows(z), bias, ratio, overlap, rope,
+                                      dev_out(entries), seqs->max_q, static_cast<hipStream_t>(stream));
+  return hip_status(e, "csa_compress launch");
+}
+
+static int index_checks(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI,
+                        int ratio) {
+  int st;
+  if ((st = check_seqs(seqs))) return st;
+  if ((st = check_rows(qI, "qI", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_MXFP4)))) return st;
+  if ((st = check_rows(kI, "kI", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_MXFP4)))) return st;
+  if (qI->dtype != kI->dtype) return fail(CSA_EINVAL, "qI and kI must share a dtype");
+  if (qI->dim != kI->dim) return fail(CSA_EINVAL, "qI dim %d != kI dim %d", qI->dim, kI->dim);
+  if (kI->dim != 32 && kI->dim != 64 && kI->dim != 128)
+    return fail(CSA_EUNSUPPORTED, "indexer dim %d: supported 32, 64, 128", kI->dim);
+  if (n_I < 1 || n_I > 64) return fail(CSA_EINVAL, "n_I %d out of [1, 64]", n_I);
+  if (!w) return fail(CSA_EINVAL, "w: null pointer");
+  if (ratio < 1) return fail(CSA_EINVAL, "ratio %d < 1", ratio);
+  return CSA_OK;
+}
+
+int csa_index_score(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
+                    float* score, int64_t score_stride, void* stream) {
+  int st;
+  if ((st = index_checks(seqs, qI, w, n_I, kI, ratio))) return st;
+  if (!score) return fail(CSA_EINVAL, "score: null pointer");
+  const int max_vis = seqs->max_ctx / ratio;
+  if (score_stride < max_vis)
+    return fail(CSA_EINVAL, "score_stride %lld < floor(max_ctx/ratio) = %d", (long long)score_stride, max_vis);
+  if (seqs->total_q == 0) return ok();
+  hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio, score,
+                                         score_stride, max_vis, static_cast<hipStream_t>(stream));
+  return hip_status(e, "csa_index_score launch");
+}
+
+int csa_topk(const csa_seqs* seqs, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
+             void* stream) {
+  int st;
+  if ((st = check_seqs(seqs))) return st;
+  if (!score || !idx) return fail(CSA_EINVAL, "score/idx: null pointer");
+  if (ratio < 1) return fail(CSA_EINVAL, "ratio %d < 1", ratio);
+  if (k < 1 || k > 4096) return fail(CSA_EINVAL, "k %d out of [1, 4096]", k);
+  const int max_vis = seqs->max_ctx / ratio;
+  if (score_stride < max_vis)
+    return fail(CSA_EINVAL, "score_stride %lld < floor(max_ctx/ratio) = %d", (long long)score_stride, max_vis);
+  if (seqs->total_q == 0) return ok();
+  hipError_t e = csa::launch_topk(dev_seqs(seqs), score, score_stride, ratio, k, idx, max_vis,
+                                  static_cast<hipStream_t>(stream));
+  return hip_status(e, "csa_topk launch");
+}
+
+int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
+                   int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  int st;
+  if ((st = index_checks(seqs, qI, w, n_I, kI, ratio))) return st;
+  if (!idx) return fail(CSA_EINVAL, "idx: null pointer");
+  if (k < 1 || k > 4096) return fail(CSA_EINVAL, "k %d out of [1, 4096]", k);
+  const size_t need = csa_workspace_bytes(CSA_OP_INDEX_TOPK, seqs, 0, 0, k, ratio, 0);
+  if (need && (!ws || ws_bytes < need))
+    return fail(CSA_EWORKSPACE, "csa_index_topk needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (seqs->total_q == 0) return ok();
+  const int max_vis = seqs->max_ctx / ratio;
+  const int64_t stride = max_vis > 0 ? max_vis : 1;
+  float* score = static_cast<float*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio, score, stride,
+                                         max_vis, s);
+  if (e != hipSuccess) return hip_status(e, "csa_index_topk score launch");
+  e = csa::launch_topk(dev_seqs(seqs), score, stride, ratio, k, idx, max_vis, s);
+  return hip_status(e, "csa_index_topk select launch");
+}
+
+int csa_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows* kv, const int32_t* idx, int k,
+               const csa_rows* tok, int n_win, const float* sink, float scale, int rope_dims, double rope_theta,
+               const csa_rows* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  csa::AttendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int st = attend_common(seqs, q, n_h, kv, tok, n_win, sink, scale, rope_dims, rope_theta, out, &a);
+  if (st) return st;
+  if (!idx) return fail(CSA_EINVAL, "idx: null pointer");
+  if (k < 1 || k > 4096) return fail(CSA_EINVAL, "k %d out of [1, 4096]", k);
+  a.idx = idx;
+  a.k = k;
+  a.csa = 1;
+  a.ratio = 1;
+  a.lse = lse;
+  if (seqs->total_q == 0) return ok();
+  return hip_status(csa::launch_attend(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), "csa_attend launch");
+}
+
+int hca_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows* kv, int ratio, const csa_rows* tok,
+               int n_win, const float* sink, float scale, int rope_dims, double rope_theta, const csa_rows* out,
+               float* lse, void* ws, size_t ws_bytes, void* stream) {
+  csa::AttendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int st = attend_common(seqs, q, n_h, kv, tok, n_win, sink, scale, rope_dims, rope_theta, out, &a);
+  if (st) return st;
+  if (ratio < 1 || ratio > (1 << 20)) return fail(CSA_EINVAL, "ratio %d out of [1, 2^20]", ratio);
+  a.idx = nullptr;
+  a.k = 0;
+  a.csa = 0;
+  a.ratio = ratio;
+  a.lse = lse;
+  if (seqs->total_q == 0) return ok();
+  return hip_status(csa::launch_attend(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), "hca_attend launch");
+}
+
+size_t csa_workspace_bytes(int op, const csa_seqs* seqs, int n_h, int dim, int k, int ratio, int n_win) {
+  if (!seqs || seqs->total_q <= 0) return 0;
+  switch (op) {
+    case CSA_OP_INDEX_TOPK: {
+      if (ratio < 1) return 0;
+      const int64_t max_vis = seqs->max_ctx / ratio;
+      return (size_t)seqs->total_q * (size_t)(max_vis > 0 ? max_vis : 1) * sizeof(float);
+    }
+    case CSA_OP_CSA_ATTEND:
+    case CSA_OP_HCA_ATTEND: {
+      if (n_h < 1 || dim < 1 || n_win < 0) return 0;
+      csa::AttendArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.S.total_q = seqs->total_q;
+      a.n_h = n_h;
+      a.q.dim = dim;
+      a.n_win = n_win;
+      a.max_ctx = seqs->max_ctx;
+      a.csa = op == CSA_OP_CSA_ATTEND;
+      a.k = k;
+      a.ratio = ratio < 1 ? 1 : ratio;
+      if (a.csa && k < 1) return 0;
+      return csa::attend_workspace_bytes(a);
+    }
+    default:
+      return 0;
+  }
+}
+
+}  // extern "C"

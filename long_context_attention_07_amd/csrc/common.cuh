@@ -1,0 +1,263 @@
+// Device helpers shared by the gfx950 kernels: row formats, RoPE angles, ragged-batch
+// lookup and the chunk-fold of the attention softmax.
+//
+// Formats follow the public OCP definitions (fp8 e4m3fn: bias 7, no infinities, S.1111.111
+// NaN, max 448; e2m1: bias 1, values 0..6; e8m0: 2^(code-127)); bf16 is the top half of an
+// IEEE float32, rounded to nearest even.  The pages name the formats only ("DeepSeek-V4
+// 深度分析报告", list "其他注意力技术细节": RoPE dims BF16, the rest FP8, indexer FP4; section 3.4
+// MXFP4; stuffyNLP review: FP8 1x128 kept from DeepSeek-V3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+enum Dtype : int { DT_F32 = 0, DT_BF16 = 1, DT_KV_SPLIT = 2, DT_MXFP4 = 3 };
+
+constexpr int kSplitBf16Dims = 64;   // trailing bf16 dims of a KV_SPLIT row
+constexpr int kKvBlock = 128;        // fp8 scale block
+constexpr int kMxBlock = 32;         // MXFP4 scale block
+constexpr int kMaxDim = 512;
+constexpr int kMaxRopePairs = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Device view of a csa_rows descriptor.
+struct RowsDev {
+  const uint8_t* data;
+  const uint8_t* scales;
+  int dtype;
+  int dim;
+  int64_t stride;  // bytes between rows
+};
+
+struct RowsOut {
+  uint8_t* data;
+  uint8_t* scales;
+  int dtype;
+  int dim;
+  int64_t stride;
+};
+
+// Ragged batch descriptor (device arrays).
+struct SeqsDev {
+  const int32_t* q_off;
+  const int32_t* ctx_len;
+  const int64_t* entry_off;
+  const int64_t* tok_off;
+  const int32_t* tok_lo;
+  int n_seqs;
+  int total_q;
+};
+
+// Inverse frequencies of the rotated pairs, computed once on the host in float64.
+struct RopeTab {
+  double inv_freq[kMaxRopePairs];
+  int dims;  // rotated trailing dims (even); 0 = none
+};
+
+// ------------------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                             // RNE
+  return u >> 16;
+}
+
+// ------------------------------------------------------------------------- fp8 e4m3fn
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  uint32_t s = (code & 0x80u) << 24;
+  uint32_t e = (code >> 3) & 0xfu;
+  uint32_t m = code & 0x7u;
+  if (e == 0xfu && m == 0x7u) return __uint_as_float(0x7fc00000u | s);
+  if (e == 0) {  // subnormal: m * 2^-9
+    float v = (float)m * 0.001953125f;
+    return __uint_as_float(__float_as_uint(v) | s);
+  }
+  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
+// Round-to-nearest-even onto the e4m3fn grid, saturating at +-448 (finite input).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fabsf(x);
+  uint32_t code;
+  if (!(a < 448.0f)) {
+    code = 0x7eu;
+  } else if (a < 0.015625f) {  // below 2^-6: subnormal grid with spacing 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8; 8 is the min normal (code 0x08)
+  } else {
+    int E = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;  // -6..8
+    float q = __builtin_rintf(a * __uint_as_float((uint32_t)(127 - E + 3) << 23));  // 8..16
+    uint32_t qi = (uint32_t)q;
+    if (qi == 16u) { E += 1; qi = 8u; }
+    code = ((uint32_t)(E + 7) << 3) | (qi - 8u);
+    if (code > 0x7eu) code = 0x7eu;
+  }
+  return code | sign;
+}
+
+// ------------------------------------------------------------------------- fp4 e2m1 / e8m0
+
+__device__ __forceinline__ float e2m1_to_f32(uint32_t code) {
+  uint32_t e = (code >> 1) & 3u;
+  uint32_t m = code & 1u;
+  float v = (e == 0) ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
+  return (code & 8u) ? -v : v;
+}
+
+__device__ __forceinline__ uint32_t f32_to_e2m1(float x) {
+  uint32_t sign = (__float_as_uint(x) >> 28) & 0x8u;
+  float a = fabsf(x);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return c | sign;
+}
+
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
+  if (code == 0xffu) return __uint_as_float(0x7fc00000u);
+  if (code == 0) return __uint_as_float(0x00400000u);  // 2^-127 (subnormal)
+  return __uint_as_float(code << 23);
+}
+
+// Shared MXFP4 exponent of a block with maximum magnitude amax: floor(log2 amax) - 2,
+// clamped to [-127, 127]; amax == 0 gives -127.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int e = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  int fl = (e == 0) ? (ilogbf(amax)) : (e - 127);
+  int E = fl - 2;
+  return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
+// ------------------------------------------------------------------------- row access
+
+// Element d of row r, decoded to float32.
+__device__ __forceinline__ float load_elem(const RowsDev& R, int64_t r, int d) {
+  const uint8_t* row = R.data + r * R.stride;
+  switch (R.dtype) {
+    case DT_F32:
+      return reinterpret_cast<const float*>(row)[d];
+    case DT_BF16:
+      return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(row)[d]);
+    case DT_KV_SPLIT: {
+      const int dn = R.dim - kSplitBf16Dims;
+      if (d < dn) {
+        const int nb = (dn + kKvBlock - 1) / kKvBlock;
+        float s = reinterpret_cast<const float*>(R.scales)[r * nb + d / kKvBlock];
+        return e4m3_to_f32(row[d]) * s;
+      }
+      return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(row + dn)[d - dn]);
+    }
+    default: {  // MXFP4
+      uint32_t byte = row[d >> 1];
+      uint32_t code = (d & 1) ? (byte >> 4) : (byte & 0xfu);
+      float s = e8m0_to_f32(R.scales[r * (R.dim / kMxBlock) + d / kMxBlock]);
+      return e2m1_to_f32(code) * s;
+    }
+  }
+}
+
+// Two adjacent elements (2c, 2c+1) of row r.
+__device__ __forceinline__ float2 load_pair(const RowsDev& R, int64_t r, int c) {
+  return make_float2(load_elem(R, r, 2 * c), load_elem(R, r, 2 * c + 1));
+}
+
+// ------------------------------------------------------------------------- RoPE
+
+// cos/sin of pos * inv_freq, with the angle formed and reduced modulo 2*pi in float64
+// (at positions near 2^20 a float32 angle would be off by ~0.06 rad).
+__device__ __forceinline__ void rope_cs(int64_t pos, double inv_freq, float* c, float* s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double a = (double)pos * inv_freq;
+  double k = __builtin_rint(a * (1.0 / two_pi));
+  double r = __builtin_fma(-k, two_pi, a);
+  sincosf((float)r, s, c);
+}
+
+// Rotate pair (x0, x1) of rotated-pair index q by position pos; sign = +1 or -1 (inverse).
+__device__ __forceinline__ float2 rope_pair(float2 x, int64_t pos, double inv_freq, float sign) {
+  float c, s;
+  rope_cs(pos, inv_freq, &c, &s);
+  s *= sign;
+  float y0 = __builtin_fmaf(x.x, c, -(x.y * s));
+  float y1 = __builtin_fmaf(x.x, s, x.y * c);
+  return make_float2(y0, y1);
+}
+
+// ------------------------------------------------------------------------- ragged batch
+
+// Sequence owning query row t: the largest b with q_off[b] <= t.
+__device__ __forceinline__ int seq_of_token(const SeqsDev& S, int t) {
+  int lo = 0, hi = S.n_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (S.q_off[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct TokenCtx {
+  int b;
+  int64_t p;        // position of the query token
+  int64_t entry0;   // pool row of entry 0
+  int64_t tok0;     // token-pool row of position tok_lo
+  int64_t tok_lo;
+};
+
+__device__ __forceinline__ TokenCtx token_ctx(const SeqsDev& S, int t) {
+  TokenCtx c;
+  c.b = seq_of_token(S, t);
+  int q0 = S.q_off[c.b], q1 = S.q_off[c.b + 1];
+  c.p = (int64_t)S.ctx_len[c.b] - (q1 - q0) + (t - q0);
+  c.entry0 = S.entry_off[c.b];
+  c.tok0 = S.tok_off[c.b];
+  c.tok_lo = S.tok_lo[c.b];
+  return c;
+}
+
+// ------------------------------------------------------------------------- softmax fold
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp2(x - M) for x <= M, exactly 1 when x == M (also when both are -inf).
+__device__ __forceinline__ float rescale(float x, float M) { return (x == M) ? 1.0f : ex2(x - M); }
+
+// Online fold state of one head in the log2 domain: M = running max of scaled logits,
+// Z = normaliser relative to M.  The fold starts from the sink and absorbs chunk partials
+// (m, l, o) in chunk order; every caller uses exactly these operations, so a token's
+// result does not depend on how its chunks were distributed over workgroups.
+struct FoldState {
+  float M;
+  float Z;
+};
+
+__device__ __forceinline__ FoldState fold_init(float sink_log2) {
+  FoldState f;
+  f.M = sink_log2;
+  f.Z = (sink_log2 == -INFINITY) ? 0.0f : 1.0f;
+  return f;
+}
+
+// Returns the factors (a for the running state, b for the chunk) and updates M, Z.
+__device__ __forceinline__ void fold_step(FoldState& f, float m, float l, float* a, float* b) {
+  float Mn = fmaxf(f.M, m);
+  *a = rescale(f.M, Mn);
+  *b = rescale(m, Mn);
+  f.Z = __builtin_fmaf(f.Z, *a, l * *b);
+  f.M = Mn;
+}
+
+}  // namespace csa

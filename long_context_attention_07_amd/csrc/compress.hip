@@ -1,0 +1,136 @@
+// KV compression kernel: softmax-gated pooling of token rows into compressed entries.
+//
+// "DeepSeek-V4 深度分析报告" section 2.1: CSA compresses every m = 4 tokens into one entry
+// drawn from 2m = 8 tokens (current and previous block overlap); HCA compresses every
+// m' = 128 tokens into one entry from a single block (Figure 2 "KV Compress 4:1 Overlapped",
+// "KV Compress 128:1 Single Block").  Partial RoPE is applied to the compressed KV (list
+// "其他注意力技术细节").  The pooling itself is the softmax-gated weighted pooling stated in
+// include/csa.h; the pages leave it open.
+//
+// One workgroup of 256 threads per new entry; thread c owns channel pair (2c, 2c+1), so a
+// 64-lane wavefront owns exactly one 128-dim fp8 scale block and each 16-lane group one
+// 32-dim MXFP4 block.  Sources are walked in ascending position with an online softmax,
+// in float32; the block maxima use a fixed butterfly, so the result depends on the entry
+// alone.  Memory bound: the grid is (sequence, new entry), entries of a sequence being
+// consecutive workgroups.
+
+#include "common.cuh"
+#include "kernels.h"
+
+namespace csa {
+
+__global__ void __launch_bounds__(256) compress_kernel(SeqsDev S, RowsDev c, RowsDev z, const float* __restrict__ bias,
+                                                       int ratio, int overlap, RopeTab rope, RowsOut out,
+                                                       int max_new) {
+  const int b = blockIdx.x / max_new;
+  const int jn = blockIdx.x % max_new;
+  if (b >= S.n_seqs) return;
+  const int n_b = S.q_off[b + 1] - S.q_off[b];
+  const int64_t L = S.ctx_len[b];
+  const int64_t i_lo = (L - n_b) / ratio;
+  const int64_t i_hi = L / ratio;
+  const int64_t i = i_lo + jn;
+  if (i >= i_hi) return;
+
+  const int D = c.dim;
+  const int pair = threadIdx.x;
+  const bool active = 2 * pair < D;
+  const int64_t lo = (i - overlap) * ratio;
+  const int64_t hi = (i + 1) * ratio;
+  const int64_t tok_lo = S.tok_lo[b];
+  const int64_t tok0 = S.tok_off[b];
+
+  float2 acc = make_float2(0.f, 0.f);
+  if (active) {
+    float m0 = -INFINITY, m1 = -INFINITY, s0 = 0.f, s1 = 0.f, a0 = 0.f, a1 = 0.f;
+    for (int64_t j = (lo < 0 ? 0 : lo); j < hi; ++j) {
+      const int slot = (int)(j - lo);
+      const int64_t r = tok0 + (j - tok_lo);
+      float2 cv = load_pair(c, r, pair);
+      float2 zv = load_pair(z, r, pair);
+      // gate logits in the log2 domain
+      float g0 = (zv.x + bias[(int64_t)slot * D + 2 * pair]) * kLog2e;
+      float g1 = (zv.y + bias[(int64_t)slot * D + 2 * pair + 1]) * kLog2e;
+      // online softmax over the sources, in ascending position
+      float n0 = fmaxf(m0, g0), n1 = fmaxf(m1, g1);
+      float r0 = rescale(m0, n0), r1 = rescale(m1, n1);
+      float e0 = ex2(g0 - n0), e1 = ex2(g1 - n1);
+      s0 = __builtin_fmaf(s0, r0, e0);
+      s1 = __builtin_fmaf(s1, r1, e1);
+      a0 = __builtin_fmaf(a0, r0, e0 * cv.x);
+      a1 = __builtin_fmaf(a1, r1, e1 * cv.y);
+      m0 = n0;
+      m1 = n1;
+    }
+    acc = make_float2(a0 / s0, a1 / s1);
+    const int d_n = D - rope.dims;
+    if (rope.dims > 0 && 2 * pair >= d_n) {
+      const int q = pair - d_n / 2;
+      acc = rope_pair(acc, i * ratio, rope.inv_freq[q], 1.0f);
+    }
+  }
+
+  // ---- store
+  const int64_t orow = S.entry_off[b] + i;
+  uint8_t* dst = out.data + orow * out.stride;
+  const int lane = threadIdx.x & 63;
+  switch (out.dtype) {
+    case DT_F32:
+      if (active) reinterpret_cast<float2*>(dst)[pair] = acc;
+      break;
+    case DT_BF16:
+      if (active) {
+        uint32_t v = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
+        reinterpret_cast<uint32_t*>(dst)[pair] = v;
+      }
+      break;
+    case DT_KV_SPLIT: {
+      const int dn = D - kSplitBf16Dims;
+      const bool fp8 = active && 2 * pair < dn;
+      float am = fp8 ? fmaxf(fabsf(acc.x), fabsf(acc.y)) : 0.f;
+      // the wavefront covers channels [128w, 128w+128): one scale block
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+      if (fp8) {
+        const float sc = am / 448.0f;
+        uint32_t c0 = 0, c1 = 0;
+        if (sc > 0.f) {
+          c0 = f32_to_e4m3(acc.x / sc);
+          c1 = f32_to_e4m3(acc.y / sc);
+        }
+        reinterpret_cast<uint16_t*>(dst)[pair] = (uint16_t)(c0 | (c1 << 8));
+        const int nb = (dn + kKvBlock - 1) / kKvBlock;
+        if (lane == 0) reinterpret_cast<float*>(out.scales)[orow * nb + (2 * pair) / kKvBlock] = sc;
+      } else if (active) {
+        uint32_t v = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
+        reinterpret_cast<uint32_t*>(dst + dn)[pair - dn / 2] = v;
+      }
+      break;
+    }
+    default: {  // MXFP4: 16 lanes = 32 dims per block
+      float am = active ? fmaxf(fabsf(acc.x), fabsf(acc.y)) : 0.f;
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+      if (active) {
+        const int E = mx_shared_exp(am);
+        const float inv = ldexpf(1.0f, -E);
+        uint32_t c0 = f32_to_e2m1(acc.x * inv), c1 = f32_to_e2m1(acc.y * inv);
+        dst[pair] = (uint8_t)(c0 | (c1 << 4));
+        if ((lane & 15) == 0) out.scales[orow * (D / kMxBlock) + (2 * pair) / kMxBlock] = (uint8_t)(E + 127);
+      }
+      break;
+    }
+  }
+}
+
+hipError_t launch_compress(const SeqsDev& S, const RowsDev& c, const RowsDev& z, const float* bias, int ratio,
+                           int overlap, const RopeTab& rope, const RowsOut& out, int max_q, hipStream_t stream) {
+  const int max_new = (max_q + ratio - 1) / ratio;
+  const int64_t blocks = (int64_t)S.n_seqs * max_new;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, S, c, z, bias, ratio, overlap,
+                     rope, out, max_new);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every entry point include/csa.h declares, and rejects
+invalid arguments on the host before anything is enqueued (no GPU needed: every call
+here fails validation, which precedes any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_attention_07_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+((?:csa|hca)_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.fail("libcsa.so is not built (python -m long_context_attention_07_amd.build)")
+    return ops.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"csa_compress", "csa_index_score", "csa_topk", "csa_index_topk", "csa_attend", "hca_attend"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in csa.h but not exported"
+    assert set(names) == set(ops.EXPORTS), "binding and header disagree"
+
+
+def test_strings_and_version(lib):
+    assert ops.csa_strerror(0) == "success"
+    assert ops.csa_strerror(-3) == "workspace too small"
+    assert ops.csa_version() >= 100
+
+
+def _seqs(n_seqs=1, total_q=1, max_q=1, max_ctx=100):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    return ops.csa_seqs(n_seqs, fake, fake, fake, fake, fake, total_q, max_q, max_ctx)
+
+
+def _rows(dtype=ops.BF16, dim=512, data=0x2000, scales=None, stride=0):
+    return ops.csa_rows(data, scales, dtype, dim, stride)
+
+
+def test_attend_validation_errors(lib):
+    s = _seqs()
+    q, kv, out = _rows(), _rows(), _rows()
+    sink = ctypes.c_void_p(0x3000)
+    idx = ctypes.c_void_p(0x4000)
+    P = ctypes.byref
+
+    def attend(**kw):
+        a = dict(seqs=P(s), q=P(q), n_h=8, kv=P(kv), idx=idx, k=16, tok=P(kv), n_win=128, sink=sink, scale=0.1,
+                 rope=64, theta=10000.0, out=P(out), lse=None, ws=None, wsb=0)
+        a.update(kw)
+        return lib.csa_attend(a["seqs"], a["q"], a["n_h"], a["kv"], a["idx"], a["k"], a["tok"], a["n_win"], a["sink"],
+                              a["scale"], a["rope"], a["theta"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+    assert attend(seqs=None) == -1 and "seqs" in ops.csa_last_error()
+    assert attend(k=0) == -1 and "k 0" in ops.csa_last_error()
+    assert attend(k=5000) == -1
+    assert attend(n_h=0) == -1 and "n_h" in ops.csa_last_error()
+    assert attend(n_win=-1) == -1
+    assert attend(rope=63) == -1 and "rope_dims" in ops.csa_last_error()
+    assert attend(rope=256) == -1
+    assert attend(scale=0.0) == -1
+    assert attend(sink=None) == -1
+    assert attend(idx=None) == -1
+    bad_dim = _rows(dim=500)
+    assert attend(q=P(bad_dim)) == -1 and "dim 500" in ops.csa_last_error()
+    other = _rows(dim=256)
+    assert attend(kv=P(other)) == -1 and "dims differ" in ops.csa_last_error()
+    f32 = _rows(dtype=ops.F32)
+    assert attend(out=P(f32)) == -2
+    mx = _rows(dtype=ops.MXFP4, scales=0x5000)
+    assert attend(kv=P(mx), tok=P(mx)) == -2
+    split_noscale = _rows(dtype=ops.KV_SPLIT)
+    assert attend(kv=P(split_noscale), tok=P(split_noscale)) == -1 and "scales" in ops.csa_last_error()
+    odd_stride = _rows(stride=1000)
+    assert attend(q=P(odd_stride)) == -1 and "row_stride" in ops.csa_last_error()
+    assert attend(seqs=P(_seqs(n_seqs=1, total_q=5, max_q=1))) == -1
+
+
+def test_compress_and_index_validation_errors(lib):
+    s = _seqs()
+    P = ctypes.byref
+    c = _rows()
+    bias = ctypes.c_void_p(0x3000)
+    assert lib.csa_compress(P(s), P(c), P(c), bias, 0, 1, 64, 10000.0, P(c), None) == -1
+    assert lib.csa_compress(P(s), P(c), P(c), bias, 4, 2, 64, 10000.0, P(c), None) == -1
+    assert lib.csa_compress(P(s), P(c), P(c), None, 4, 1, 64, 10000.0, P(c), None) == -1
+    assert lib.csa_compress(P(s), P(c), P(c), bias, 4, 1, 64, 1.0, P(c), None) == -1
+    mx = _rows(dtype=ops.MXFP4, scales=0x5000)
+    assert lib.csa_compress(P(s), P(mx), P(c), bias, 4, 1, 0, 10000.0, P(c), None) == -2
+    qI = _rows(dim=128)
+    w = ctypes.c_void_p(0x6000)
+    score = ctypes.c_void_p(0x7000)
+    assert lib.csa_index_score(P(s), P(qI), w, 65, P(qI), 4, score, 100, None) == -1
+    assert lib.csa_index_score(P(s), P(qI), w, 64, P(qI), 4, score, 10, None) == -1
+    assert "score_stride" in ops.csa_last_error()
+    i96 = _rows(dim=96)
+    assert lib.csa_index_score(P(s), P(i96), w, 64, P(i96), 4, score, 100, None) == -2
+    assert lib.csa_topk(P(s), score, 100, 4, 0, score, None) == -1
+    assert lib.csa_index_topk(P(s), P(qI), w, 64, P(qI), 4, 16, score, None, 0, None) == -3
+    assert "workspace" in ops.csa_last_error()
+
+
+def test_workspace_sizes(lib):
+    s = _seqs(n_seqs=4, total_q=4, max_q=1, max_ctx=1 << 20)
+    P = ctypes.byref
+    assert lib.csa_workspace_bytes(ops.OP_INDEX_TOPK, P(s), 0, 0, 512, 4, 0) == 4 * (1 << 18) * 4
+    assert lib.csa_workspace_bytes(99, P(s), 64, 512, 0, 128, 128) == 0
+    hca = lib.csa_workspace_bytes(ops.OP_HCA_ATTEND, P(s), 64, 512, 0, 128, 128)
+    assert hca > 0 and hca % (4 * 64 * 514 * 4) == 0

@@ -1,0 +1,418 @@
+"""GPU parity of each entry point against the float64 oracle, on seeded ragged batches
+that span several tiles and ragged tails, in every supported format, plus edge cases,
+split/single-mode bit equality and batch invariance.  All calls go through the C ABI."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_07_amd import ops
+from oracle import formats as F
+from oracle import pipeline as P
+from oracle.attention import attend_token
+from oracle.indexer import index_scores, topk_select, visible
+
+from harness import (DEV, assert_close, bf16, check_topk, empty_rows, f32, kv_split, log, make_batch, mxfp4,
+                     rows_values, score_error_bound)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.lib()
+
+
+def _rows_in(fmt, x64):
+    """Device Rows in format `fmt` + float64 stored values."""
+    if fmt == ops.F32:
+        t, h = f32(x64)
+        return ops.Rows.of(t), h
+    if fmt == ops.BF16:
+        t, h = bf16(x64)
+        return ops.Rows.of(t), h
+    if fmt == ops.KV_SPLIT:
+        return kv_split(x64)
+    return mxfp4(x64)
+
+
+# ----------------------------------------------------------------------------- compress
+
+COMPRESS_CASES = [
+    # (c fmt, z fmt, out fmt, D, ratio, overlap, rope)
+    (ops.F32, ops.F32, ops.F32, 128, 4, 1, 64),
+    (ops.F32, ops.F32, ops.F32, 32, 4, 1, 0),
+    (ops.BF16, ops.BF16, ops.BF16, 512, 4, 1, 64),
+    (ops.BF16, ops.BF16, ops.BF16, 512, 128, 0, 64),
+    (ops.KV_SPLIT, ops.BF16, ops.KV_SPLIT, 512, 4, 1, 64),
+    (ops.BF16, ops.BF16, ops.MXFP4, 128, 4, 1, 0),
+    (ops.F32, ops.F32, ops.KV_SPLIT, 256, 4, 1, 64),
+]
+
+
+def _grid_spacing(fmt_out, v):
+    """Spacing of the storage grid around the (scaled) value v."""
+    a = np.abs(v)
+    _, E = np.frexp(np.where(a > 0, a, 1.0))
+    e = E - 1
+    if fmt_out == "bf16":
+        return np.ldexp(1.0, np.maximum(e, -126) - 7)
+    if fmt_out == "e4m3":
+        return np.ldexp(1.0, np.maximum(e, -6) - 3)
+    return np.ldexp(1.0, np.maximum(e, 0) - 1)
+
+
+def _check_quantised(fmt, gpu_rows, ref, n):
+    """Stored entries against the oracle's exact values: each element must be one of the
+    grid points adjacent to the exact value (nearest, or its neighbour when the exact
+    value lies within a 1e-5 relative slack of the rounding midpoint)."""
+    got = rows_values(gpu_rows, n)
+    if fmt == ops.BF16:
+        sp = _grid_spacing("bf16", ref)
+        assert np.all(np.abs(got - ref) <= 0.5 * sp + 1e-5 * np.abs(ref) + 1e-30)
+    elif fmt == ops.KV_SPLIT:
+        dn = ref.shape[1] - 64
+        sc = gpu_rows.scales[:n].cpu().numpy().astype(np.float64)
+        for b, (lo, hi) in enumerate(F.kv_split_blocks(dn)):
+            amax = np.abs(ref[:, lo:hi]).max(1)
+            np.testing.assert_allclose(sc[:, b], amax / 448, rtol=1e-5, atol=1e-30)
+            s = np.where(sc[:, b:b + 1] > 0, sc[:, b:b + 1], 1.0)
+            v = ref[:, lo:hi] / s
+            gv = got[:, lo:hi] / s
+            sp = _grid_spacing("e4m3", v)
+            assert np.all(np.abs(gv - v) <= 0.5 * sp + 1e-5 * np.maximum(1, np.abs(v))), "fp8 code off the grid"
+        sp = _grid_spacing("bf16", ref[:, dn:])
+        assert np.all(np.abs(got[:, dn:] - ref[:, dn:]) <= 0.5 * sp + 1e-5 * np.abs(ref[:, dn:]) + 1e-30)
+    else:  # MXFP4
+        D = ref.shape[1]
+        sc = gpu_rows.scales[:n].cpu().numpy().astype(np.int64) - 127
+        blk = ref.reshape(n, D // 32, 32)
+        amax = np.abs(blk).max(-1)
+        _, E = np.frexp(np.where(amax > 0, amax, 1.0))
+        exp_e = np.clip(np.where(amax > 0, E - 1 - 2, -127), -127, 127)
+        near_pow2 = np.abs(amax / np.ldexp(1.0, E - 1) - 1.0) < 1e-5
+        assert np.all((sc == exp_e) | near_pow2), "e8m0 exponent differs"
+        v = blk / np.ldexp(1.0, sc)[..., None]
+        gv = got.reshape(n, D // 32, 32) / np.ldexp(1.0, sc)[..., None]
+        vc = np.clip(v, -6, 6)
+        sp = _grid_spacing("e2m1", vc)
+        assert np.all(np.abs(gv - vc) <= 0.5 * sp + 1e-5 * np.maximum(1, np.abs(v))), "e2m1 code off the grid"
+
+
+@pytest.mark.parametrize("case", COMPRESS_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_compress_matches_oracle(case):
+    cf, zf, of, D, ratio, overlap, rope = case
+    log(f"compress case {case}")
+    g = np.random.default_rng(100 + D + ratio)
+    # a prefill, a decode step, a multi-token step, a sequence with nothing to write
+    n_q = [37 * ratio // 4 + 3, 1, 9, 2]
+    ctx = [n_q[0], 250 * ratio, 50 * ratio // 4 + 3, 5]
+    hist = 2 * ratio + 8
+    ob, sq, n_ent, n_tok = make_batch(n_q, ctx, ratio, tok_hist=hist)
+    c_rows, c_val = _rows_in(cf, g.standard_normal((n_tok, D)))
+    z_rows, z_val = _rows_in(zf, g.standard_normal((n_tok, D)))
+    bias_np = g.standard_normal(((1 + overlap) * ratio, D)) / math.sqrt(D)
+    bias_t, bias_val = f32(bias_np)
+    out = empty_rows(n_ent, D, of)
+    ops.csa_compress(sq, c_rows, z_rows, bias_t, ratio, overlap, rope, 10000.0, out)
+    torch.cuda.synchronize()
+    ref = P.compress_batch(ob, c_val, z_val, bias_val, ratio, overlap, rope)
+    rows = sorted(ref)
+    assert rows, "case writes no entries"
+    got_all = rows_values(out, n_ent)
+    written = np.zeros(n_ent, bool)
+    written[rows] = True
+    assert np.all(got_all[~written] == 0), "rows outside the new entries were touched"
+    refm = np.stack([ref[r] for r in rows])
+    if of == ops.F32:
+        assert_close(got_all[rows], refm, 1e-5, "compress f32")
+    else:
+        sub = ops.Rows(out.data[rows], of, D, out.scales[rows] if out.scales is not None else None)
+        _check_quantised(of, sub, refm, len(rows))
+
+
+# ----------------------------------------------------------------------------- index scores
+
+
+@pytest.mark.parametrize("fmt,d_I,n_I", [(ops.F32, 32, 4), (ops.BF16, 128, 64), (ops.MXFP4, 128, 64),
+                                         (ops.F32, 64, 7)])
+def test_index_score_matches_oracle(fmt, d_I, n_I):
+    log(f"index_score fmt={fmt} d_I={d_I} n_I={n_I}")
+    g = np.random.default_rng(7 + d_I + n_I)
+    ratio = 4
+    n_q = [3, 1, 1, 5]
+    ctx = [700, 2051, 2, 1300]      # V up to 512: several 256-entry tiles and ragged tails; one V = 0
+    ob, sq, n_ent, _ = make_batch(n_q, ctx, ratio)
+    kI_rows, kI_val = _rows_in(fmt, g.standard_normal((n_ent, d_I)))
+    qI_rows, qI_val = _rows_in(fmt, g.standard_normal((sq.total_q * n_I, d_I)))
+    w_t, w_val = f32(g.standard_normal((sq.total_q, n_I)) / math.sqrt(n_I))
+    stride = sq.max_ctx // ratio + 3
+    score = torch.full((sq.total_q, stride), float("nan"), dtype=torch.float32, device=DEV)
+    ops.csa_index_score(sq, qI_rows, w_t, n_I, kI_rows, ratio, score)
+    torch.cuda.synchronize()
+    sc = score.cpu().numpy().astype(np.float64)
+    for row, b, p in ob.tokens():
+        V = visible(p, ratio)
+        kI = kI_val[ob.entry_off[b]: ob.entry_off[b] + V]
+        qI = qI_val[row * n_I:(row + 1) * n_I]
+        ref = index_scores(qI, w_val[row], kI)
+        bound = score_error_bound(qI, w_val[row], kI) if V else np.zeros(0)
+        assert np.all(np.abs(sc[row, :V] - ref) <= bound), f"token {row}: score error beyond float32 bound"
+        assert np.all(np.isnan(sc[row, V:])), f"token {row}: columns >= V written"
+
+
+# ----------------------------------------------------------------------------- top-k
+
+
+def test_topk_exact_on_identical_scores():
+    g = np.random.default_rng(21)
+    ratio = 1
+    # V: k-ties, V <= k, V = k + 1, staged (<= 32768) and streamed (> 32768) candidates
+    ctx = [300, 64, 65, 5000, 32768, 40000, 1]
+    n_q = [1] * len(ctx)
+    ks = 64
+    ob, sq, _, _ = make_batch(n_q, ctx, ratio)
+    stride = max(ctx)
+    s = np.full((len(ctx), stride), np.nan, dtype=np.float32)
+    for r, L in enumerate(ctx):
+        if r == 0:
+            s[r, :L] = np.round(g.standard_normal(L) * 2) / 4        # heavy exact ties
+        elif r == 3:
+            s[r, :L] = np.where(g.random(L) < 0.5, 0.0, -0.0)         # only +-0: all tie
+            s[r, 17] = 1.0
+        else:
+            s[r, :L] = g.standard_normal(L).astype(np.float32)
+    st = torch.from_numpy(s).to(DEV)
+    for k in (1, ks, 1000):
+        idx = torch.full((len(ctx), k), -7, dtype=torch.int32, device=DEV)
+        ops.csa_topk(sq, st, ratio, k, idx)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for r, L in enumerate(ctx):
+            ref = topk_select(s[r, :L].astype(np.float64), k)
+            assert list(got[r]) == list(ref), f"token {r} (V={L}, k={k})"
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def _attend_inputs(g, fmt, D, n_h, n_q, ctx, ratio, k, n_win, tok_hist=None, sink_scale=1.0):
+    ob, sq, n_ent, n_tok = make_batch(n_q, ctx, ratio, tok_hist=tok_hist)
+    qf = ops.F32 if fmt == ops.F32 else ops.BF16
+    q_rows, q_val = _rows_in(qf, g.standard_normal((sq.total_q * n_h, D)))
+    kv_rows, kv_val = _rows_in(fmt, g.standard_normal((max(n_ent, 1), D)))
+    tok_rows, tok_val = _rows_in(fmt, g.standard_normal((max(n_tok, 1), D)))
+    sink_t, sink_val = f32(g.standard_normal(n_h) * sink_scale)
+    idx = np.full((sq.total_q, max(k, 1)), -1, dtype=np.int32)
+    for row, b, p in ob.tokens():
+        V = visible(p, ratio)
+        if k == 0:
+            continue
+        if V > k:
+            idx[row] = np.sort(g.choice(V, size=k, replace=False))
+        else:
+            idx[row, :V] = np.arange(V)
+    return ob, sq, q_rows, q_val, kv_rows, kv_val, tok_rows, tok_val, sink_t, sink_val, idx
+
+
+def _oracle_attend(ob, q_val, kv_val, tok_val, idx, n_win, sink_val, scale, rope, n_h, D, csa, ratio):
+    q = q_val.reshape(-1, n_h, D)
+    if csa:
+        return P.csa_attend_batch(ob, q, kv_val, idx, tok_val, n_win, sink_val, scale, rope)
+    return P.hca_attend_batch(ob, q, kv_val, ratio, tok_val, n_win, sink_val, scale, rope)
+
+
+ATTEND_CASES = [
+    # (fmt, D, n_h, csa, ratio, k, n_win)
+    (ops.F32, 128, 8, True, 4, 64, 128),
+    (ops.F32, 128, 12, False, 4, 0, 128),
+    (ops.F32, 128, 8, False, 16, 0, 37),
+    (ops.BF16, 512, 64, True, 4, 512, 128),
+    (ops.BF16, 512, 64, False, 128, 0, 128),
+    (ops.BF16, 512, 16, True, 4, 100, 0),
+    (ops.KV_SPLIT, 512, 64, True, 4, 256, 128),
+]
+
+
+@pytest.mark.parametrize("case", ATTEND_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_attend_matches_oracle(case):
+    fmt, D, n_h, csa, ratio, k, n_win = case
+    log(f"attend case {case}")
+    g = np.random.default_rng(33 + D + n_h + ratio + k)
+    n_q = [5, 1, 1, 3, 0, 2]
+    ctx = [5, 3000 * ratio // 4, 129, 900 * ratio // 4, 10, 2 * ratio + 1]
+    data = _attend_inputs(g, fmt, D, n_h, n_q, ctx, ratio, k, n_win, tok_hist=n_win + 3)
+    ob, sq, q_rows, q_val, kv_rows, kv_val, tok_rows, tok_val, sink_t, sink_val, idx = data
+    scale = 1.0 / math.sqrt(D)
+    out = empty_rows(sq.total_q * n_h, D, ops.F32 if fmt == ops.F32 else ops.BF16)
+    lse = torch.zeros((sq.total_q, n_h), dtype=torch.float32, device=DEV)
+    idx_t = torch.from_numpy(idx).to(DEV)
+    if csa:
+        ops.csa_attend(sq, q_rows, n_h, kv_rows, idx_t, k, tok_rows, n_win, sink_t, scale, 64, 10000.0, out, lse)
+    else:
+        ops.hca_attend(sq, q_rows, n_h, kv_rows, ratio, tok_rows, n_win, sink_t, scale, 64, 10000.0, out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = _oracle_attend(ob, q_val, kv_val, tok_val, idx, n_win, sink_val, scale, 64, n_h, D, csa, ratio)
+    tol = 1e-5 if fmt == ops.F32 else 1e-2
+    got = rows_values(out).reshape(sq.total_q, n_h, D)
+    assert_close(got, ref_o, tol, "attend out")
+    assert_close(lse.cpu().numpy(), ref_l, tol, "attend lse")
+
+
+@pytest.mark.parametrize("fmt,D,n_h", [(ops.F32, 128, 8), (ops.BF16, 512, 64)])
+def test_attend_split_and_single_modes_bit_identical(fmt, D, n_h):
+    """With a workspace the key lists are spread over workgroups per chunk; without, one
+    workgroup walks them.  The outputs must agree bit for bit."""
+    g = np.random.default_rng(5)
+    n_q, ctx = [1, 1, 2], [4000, 70000, 600]
+    for csa, ratio, k in ((True, 4, 512), (False, 128, 0), (False, 4, 0)):
+        data = _attend_inputs(g, fmt, D, n_h, n_q, ctx, ratio, k, 128, tok_hist=140)
+        ob, sq, q_rows, _, kv_rows, _, tok_rows, _, sink_t, _, idx = data
+        idx_t = torch.from_numpy(idx).to(DEV)
+        op = ops.OP_CSA_ATTEND if csa else ops.OP_HCA_ATTEND
+        wsb = ops.csa_workspace_bytes(op, sq, n_h, D, k, ratio, 128)
+        ws = torch.empty(wsb // 4 + 1, dtype=torch.float32, device=DEV)
+        outs = []
+        for use_ws in (ws, None):
+            out = empty_rows(sq.total_q * n_h, D, ops.F32 if fmt == ops.F32 else ops.BF16)
+            lse = torch.zeros((sq.total_q, n_h), dtype=torch.float32, device=DEV)
+            if csa:
+                ops.csa_attend(sq, q_rows, n_h, kv_rows, idx_t, k, tok_rows, 128, sink_t, 0.05, 64, 10000.0, out,
+                               lse, ws=use_ws)
+            else:
+                ops.hca_attend(sq, q_rows, n_h, kv_rows, ratio, tok_rows, 128, sink_t, 0.05, 64, 10000.0, out, lse,
+                               ws=use_ws)
+            outs.append((out.data.clone(), lse.clone()))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), (csa, ratio)
+
+
+def test_attend_edge_cases():
+    """No visible entries (p < m-1), sink = -inf (plain softmax), no window with no entries
+    (empty key set: output 0, lse -inf), idx with scattered -1."""
+    g = np.random.default_rng(9)
+    D, n_h = 128, 8
+    n_q, ctx = [3, 1], [3, 40]
+    ob, sq, n_ent, n_tok = make_batch(n_q, ctx, 4)
+    q_rows, q_val = _rows_in(ops.F32, g.standard_normal((sq.total_q * n_h, D)))
+    kv_rows, kv_val = _rows_in(ops.F32, g.standard_normal((n_ent, D)))
+    tok_rows, tok_val = _rows_in(ops.F32, g.standard_normal((n_tok, D)))
+    sink_t = torch.full((n_h,), float("-inf"), device=DEV)
+    sink_val = np.full(n_h, -np.inf)
+    idx = np.full((sq.total_q, 8), -1, np.int32)
+    idx[3, [1, 4, 6]] = [2, 5, 9]
+    idx_t = torch.from_numpy(idx).to(DEV)
+    for n_win in (128, 1, 0):
+        out = empty_rows(sq.total_q * n_h, D, ops.F32)
+        lse = torch.zeros((sq.total_q, n_h), dtype=torch.float32, device=DEV)
+        ops.csa_attend(sq, q_rows, n_h, kv_rows, idx_t, 8, tok_rows, n_win, sink_t, 0.1, 64, 10000.0, out, lse)
+        torch.cuda.synchronize()
+        ref_o, ref_l = P.csa_attend_batch(ob, q_val.reshape(-1, n_h, D), kv_val, idx, tok_val, n_win, sink_val, 0.1,
+                                          64)
+        assert_close(rows_values(out).reshape(-1, n_h, D), ref_o, 1e-5, f"edge out n_win={n_win}")
+        gl, rl = lse.cpu().numpy(), ref_l
+        assert np.array_equal(np.isinf(gl), np.isinf(rl))
+        fin = np.isfinite(rl)
+        assert_close(gl[fin], rl[fin], 1e-5, "edge lse")
+
+
+# ----------------------------------------------------------------------------- validation
+
+
+def test_invalid_arguments_enqueue_nothing():
+    g = np.random.default_rng(1)
+    ob, sq, n_ent, n_tok = make_batch([1], [100], 4)
+    q_rows, _ = _rows_in(ops.BF16, g.standard_normal((8, 512)))
+    kv_rows, _ = _rows_in(ops.BF16, g.standard_normal((n_ent, 512)))
+    sink = torch.zeros(8, device=DEV)
+    out = empty_rows(8, 512, ops.BF16)
+    idx = torch.zeros((1, 4), dtype=torch.int32, device=DEV)
+    with pytest.raises(ops.CsaError) as e:
+        ops.csa_attend(sq, q_rows, 8, kv_rows, idx, 0, kv_rows, 128, sink, 0.1, 64, 10000.0, out)
+    assert e.value.status == -1 and "k 0" in str(e.value)
+    with pytest.raises(ops.CsaError) as e:
+        ops.hca_attend(sq, q_rows, 8, kv_rows, 4, kv_rows, 128, sink, 0.1, 63, 10000.0, out)
+    assert "rope_dims" in str(e.value)
+    f32rows = empty_rows(8, 512, ops.F32)
+    with pytest.raises(ops.CsaError) as e:
+        ops.hca_attend(sq, q_rows, 8, kv_rows, 4, kv_rows, 128, sink, 0.1, 64, 10000.0, f32rows)
+    assert e.value.status == -2
+    assert torch.all(out.data == 0)
+
+
+# ----------------------------------------------------------------------------- batch invariance
+
+
+def _run_all(sq, n_h, D, q_rows, kv_rows, tok_rows, sink_t, qI_rows, w_t, kI_rows, n_I, k, with_ws):
+    """index_topk -> csa_attend, and hca_attend (ratio 4) on the same pools; returns the
+    per-token outputs."""
+    ws = None
+    if with_ws:
+        nb = max(ops.csa_workspace_bytes(ops.OP_INDEX_TOPK, sq, k=k, ratio=4),
+                 ops.csa_workspace_bytes(ops.OP_CSA_ATTEND, sq, n_h, D, k, 4, 128),
+                 ops.csa_workspace_bytes(ops.OP_HCA_ATTEND, sq, n_h, D, 0, 4, 128))
+        ws = torch.empty(nb // 4 + 1, dtype=torch.float32, device=DEV)
+    idx = torch.empty((sq.total_q, k), dtype=torch.int32, device=DEV)
+    if with_ws:
+        ops.csa_index_topk(sq, qI_rows, w_t, n_I, kI_rows, 4, k, idx, ws=ws)
+    else:
+        nb = ops.csa_workspace_bytes(ops.OP_INDEX_TOPK, sq, k=k, ratio=4)
+        ops.csa_index_topk(sq, qI_rows, w_t, n_I, kI_rows, 4, k, idx,
+                           ws=torch.empty(nb // 4 + 1, dtype=torch.float32, device=DEV))
+    o1 = empty_rows(sq.total_q * n_h, D, ops.BF16)
+    l1 = torch.empty((sq.total_q, n_h), dtype=torch.float32, device=DEV)
+    ops.csa_attend(sq, q_rows, n_h, kv_rows, idx, k, tok_rows, 128, sink_t, 0.05, 64, 10000.0, o1, l1, ws=ws)
+    o2 = empty_rows(sq.total_q * n_h, D, ops.BF16)
+    l2 = torch.empty((sq.total_q, n_h), dtype=torch.float32, device=DEV)
+    ops.hca_attend(sq, q_rows, n_h, kv_rows, 4, tok_rows, 128, sink_t, 0.05, 64, 10000.0, o2, l2, ws=ws)
+    torch.cuda.synchronize()
+    return idx.cpu(), o1.data.cpu().view(sq.total_q, n_h, D), l1.cpu(), o2.data.cpu().view(sq.total_q, n_h, D), l2.cpu()
+
+
+def test_batch_invariance_small():
+    """Every token's idx / out / lse bits are identical whether its sequence runs alone,
+    in the full batch, or in a shuffled regrouping, with or without workspace."""
+    g = np.random.default_rng(77)
+    D, n_h, n_I, d_I, k = 512, 16, 8, 128, 64
+    lens = [300, 2000, 45, 9000, 700]
+    nqs = [3, 1, 5, 2, 1]
+    # per-sequence pools (entries, keys, tokens) and per-token inputs, drawn once
+    seqs = []
+    for L, nq in zip(lens, nqs):
+        E = L // 4
+        seqs.append(dict(L=L, nq=nq, kv=g.standard_normal((E, D)), kI=g.standard_normal((E, d_I)),
+                         tok=g.standard_normal((nq + 130, D)), q=g.standard_normal((nq * n_h, D)),
+                         qI=g.standard_normal((nq * n_I, d_I)), w=g.standard_normal((nq, n_I)) / 3))
+    sink_t, _ = f32(g.standard_normal(n_h))
+
+    def run(order, with_ws):
+        ent = np.concatenate([seqs[i]["kv"] for i in order])
+        kI = np.concatenate([seqs[i]["kI"] for i in order])
+        tok = np.concatenate([seqs[i]["tok"] for i in order])
+        q = np.concatenate([seqs[i]["q"] for i in order])
+        qI = np.concatenate([seqs[i]["qI"] for i in order])
+        w = np.concatenate([seqs[i]["w"] for i in order])
+        e_off = np.cumsum([0] + [seqs[i]["L"] // 4 for i in order])[:-1]
+        t_off = np.cumsum([0] + [seqs[i]["nq"] + 130 for i in order])[:-1]
+        t_lo = [seqs[i]["L"] - seqs[i]["nq"] - 130 for i in order]
+        sq = ops.Seqs([seqs[i]["nq"] for i in order], [seqs[i]["L"] for i in order], e_off, t_off, t_lo)
+        res = _run_all(sq, n_h, D, ops.Rows.of(bf16(q)[0]), ops.Rows.of(bf16(ent)[0]), ops.Rows.of(bf16(tok)[0]),
+                       sink_t, ops.Rows.of(bf16(qI)[0]), f32(w)[0], ops.Rows.of(bf16(kI)[0]), n_I, k, with_ws)
+        per = {}
+        r0 = 0
+        for i in order:
+            per[i] = [x[r0:r0 + seqs[i]["nq"]] for x in res]
+            r0 += seqs[i]["nq"]
+        return per
+
+    base = run(list(range(len(seqs))), True)
+    variants = [run([i], True) for i in range(len(seqs))]
+    variants += [run([4, 2, 0], False), run([3, 1], True), run([1, 3, 0, 4, 2], False)]
+    for v in variants:
+        for i, outs in v.items():
+            for a, b in zip(outs, base[i]):
+                assert torch.equal(a, b), f"sequence {i} differs across batch compositions"

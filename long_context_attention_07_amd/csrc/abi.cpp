@@ -133,7 +133,10 @@ int make_rope(int rope_dims, double theta, int dim, csa::RopeTab* tab) {
     return fail(CSA_EINVAL, "rope_theta %g must be > 1", theta);
   std::memset(tab, 0, sizeof(*tab));
   tab->dims = rope_dims;
-  for (int q = 0; q < rope_dims / 2; ++q) tab->inv_freq[q] = std::pow(theta, -2.0 * q / rope_dims);
+  for (int q = 0; q < rope_dims / 2; ++q) {
+    tab->inv_freq[q] = std::pow(theta, -2.0 * q / rope_dims);
+    tab->inv_freq_rev[q] = tab->inv_freq[q] / 6.283185307179586476925286766559;
+  }
   return CSA_OK;
 }
 

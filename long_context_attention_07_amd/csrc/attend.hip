@@ -16,83 +16,39 @@
 // the token -- not on the batch, the mode, or the grid.
 //
 // This file holds the generic kernel (any row format, float32 arithmetic): 8 heads x 32
-// keys per tile, logits and P.V on the vector ALUs.
+// keys per tile, logits and P.V on the vector ALUs; bf16 rows of 512 dims go to the
+// matrix-core kernel (attend_mfma.hip).
 
-#include "common.cuh"
-#include "kernels.h"
+#include "attend_common.cuh"
 
 namespace csa {
 
 constexpr int kValuHG = 8;       // heads per workgroup
 constexpr int kValuTK = 32;      // keys per tile
-constexpr int kValuChunk = 128;  // key slots per chunk
 constexpr int kValuRegs = kMaxDim / 32;
 
-struct SlotRef {
-  int64_t row;
-  int64_t pos;
-  int kind;  // 0 absent, 1 entry (stored rotated), 2 window token (rotated here)
-};
-
-__device__ __forceinline__ SlotRef resolve_slot(const AttendArgs& a, int t, const TokenCtx& ctx, int64_t n_ent,
-                                                int64_t s) {
-  SlotRef r;
-  r.kind = 0;
-  r.row = 0;
-  r.pos = 0;
-  if (s < n_ent) {
-    int64_t e = a.csa ? (int64_t)a.idx[(int64_t)t * a.k + s] : s;
-    if (e >= 0) {
-      r.kind = 1;
-      r.row = ctx.entry0 + e;
-    }
-  } else {
-    int64_t pos = ctx.p - a.n_win + 1 + (s - n_ent);
-    if (pos >= 0 && pos >= ctx.tok_lo) {
-      r.kind = 2;
-      r.row = ctx.tok0 + (pos - ctx.tok_lo);
-      r.pos = pos;
-    }
-  }
-  return r;
-}
-
-__device__ __forceinline__ int64_t entry_slots(const AttendArgs& a, const TokenCtx& ctx) {
-  return a.csa ? (int64_t)a.k : (ctx.p + 1) / a.ratio;
-}
-
-// Final normalisation, inverse RoPE at p, store; thread (head hl, lane l32) holds dims
-// l32 + 32 r.  Shared by the single-mode kernel and the combine kernel.
+// Final store of one head's output (thread (head, lane l32) holds dims l32 + 32 r).
 __device__ __forceinline__ void finalize_valu(const AttendArgs& a, int t, int h, int l32, int64_t p,
                                               const FoldState& f, const float* O, int D) {
-  const bool live = f.Z > 0.f;
-  const float inv = live ? 1.0f / f.Z : 0.f;
+  const float inv = (f.Z > 0.f) ? 1.0f / f.Z : 0.f;
   const int dn = D - a.rope.dims;
-  uint8_t* row = a.out.data + ((int64_t)t * a.n_h + h) * a.out.stride;
+  const int64_t orow = (int64_t)t * a.n_h + h;
 #pragma unroll
   for (int r = 0; r < kValuRegs; ++r) {
     const int d = l32 + 32 * r;
     if (d < D) {
-      float x = live ? O[r] * inv : 0.f;
-      float partner = __shfl_xor(x, 1, 32);
-      if (d >= dn) {
-        const int q = (d - dn) >> 1;
-        float2 pr = (d & 1) ? make_float2(partner, x) : make_float2(x, partner);
-        float2 y = rope_pair(pr, p, a.rope.inv_freq[q], -1.0f);
-        x = (d & 1) ? y.y : y.x;
-      }
-      if (a.out.dtype == DT_F32) reinterpret_cast<float*>(row)[d] = x;
-      else reinterpret_cast<uint16_t*>(row)[d] = (uint16_t)f32_to_bf16_bits(x);
-    } else {
-      (void)__shfl_xor(0.f, 1, 32);
+      const float x = O[r] * inv;
+      const float partner = __shfl_xor(x, 1, 32);
+      store_out(a, orow, d, finalize_elem<ROPE_ACCURATE>(x, partner, d, dn, p, a.rope));
     }
   }
-  if (a.lse && l32 == 0) a.lse[(int64_t)t * a.n_h + h] = live ? (f.M + log2f(f.Z)) * kLn2 : -INFINITY;
+  if (a.lse && l32 == 0) a.lse[orow] = lse_natural(f);
 }
 
 template <bool SPLIT>
 __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a, float* __restrict__ ws_o,
-                                                          float* __restrict__ ws_ml, int n_hg, int max_chunks) {
+                                                          float* __restrict__ ws_ml, int n_hg, int max_chunks,
+                                                          int chunk_slots) {
   __shared__ float qs[kValuHG][kMaxDim + 1];
   __shared__ float ks[kValuTK][kMaxDim + 1];
   __shared__ float ps[kValuHG][kValuTK];
@@ -109,7 +65,7 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a, float* _
   const TokenCtx ctx = token_ctx(a.S, t);
   const int64_t n_ent = entry_slots(a, ctx);
   const int64_t n_slots = n_ent + a.n_win;
-  const int n_chunks = (int)((n_slots + kValuChunk - 1) / kValuChunk);
+  const int n_chunks = (int)((n_slots + chunk_slots - 1) / chunk_slots);
   if (SPLIT && c_only >= n_chunks) return;
 
   const int D = a.q.dim;
@@ -145,8 +101,8 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a, float* _
     float o[kValuRegs];
 #pragma unroll
     for (int r = 0; r < kValuRegs; ++r) o[r] = 0.f;
-    for (int tile = 0; tile < kValuChunk / kValuTK; ++tile) {
-      const int64_t s0 = (int64_t)cc * kValuChunk + tile * kValuTK;
+    for (int tile = 0; tile < chunk_slots / kValuTK; ++tile) {
+      const int64_t s0 = (int64_t)cc * chunk_slots + tile * kValuTK;
       if (s0 >= n_slots) break;
       if (tid < kValuTK) {
         const int64_t s = s0 + tid;
@@ -221,43 +177,7 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a, float* _
   if (!SPLIT && hvalid) finalize_valu(a, t, h, l32, ctx.p, f, O, D);
 }
 
-// Fold of the chunk states written by the split-mode kernel, in chunk order from the sink.
-__global__ void __launch_bounds__(256) attend_combine_kernel(AttendArgs a, const float* __restrict__ ws_o,
-                                                             const float* __restrict__ ws_ml, int n_hg,
-                                                             int max_chunks, int chunk_slots) {
-  const int g = blockIdx.x % n_hg;
-  const int t = blockIdx.x / n_hg;
-  const int hl = threadIdx.x >> 5, l32 = threadIdx.x & 31;
-  const int h = g * kValuHG + hl;
-  if (h >= a.n_h) return;
-  const TokenCtx ctx = token_ctx(a.S, t);
-  const int64_t n_slots = entry_slots(a, ctx) + a.n_win;
-  const int n_chunks = (int)((n_slots + chunk_slots - 1) / chunk_slots);
-  const int D = a.q.dim;
-  FoldState f = fold_init(a.sink[h] * kLog2e);
-  float O[kValuRegs];
-#pragma unroll
-  for (int r = 0; r < kValuRegs; ++r) O[r] = 0.f;
-  for (int cc = 0; cc < n_chunks; ++cc) {
-    const int64_t base = ((int64_t)t * max_chunks + cc) * a.n_h + h;
-    const float m = ws_ml[2 * base], l = ws_ml[2 * base + 1];
-    float fa, fb;
-    fold_step(f, m, l, &fa, &fb);
-    const float* po = ws_o + base * D;
-#pragma unroll
-    for (int r = 0; r < kValuRegs; ++r) {
-      const int d = l32 + 32 * r;
-      const float o = (d < D) ? po[d] : 0.f;
-      O[r] = __builtin_fmaf(O[r], fa, o * fb);
-    }
-  }
-  finalize_valu(a, t, h, l32, ctx.p, f, O, D);
-}
-
-int attend_chunk_slots(const AttendArgs& a) {
-  (void)a;
-  return kValuChunk;
-}
+int attend_chunk_slots(const AttendArgs& a) { return chunk_slots_for(a.csa, a.k, a.n_win); }
 
 int64_t attend_max_chunks(const AttendArgs& a) {
   const int64_t n_ent = a.csa ? (int64_t)a.k : (int64_t)a.max_ctx / a.ratio;
@@ -270,9 +190,14 @@ size_t attend_workspace_bytes(const AttendArgs& a) {
   return (size_t)a.S.total_q * (size_t)mc * (size_t)a.n_h * ((size_t)a.q.dim + 2) * sizeof(float);
 }
 
+bool attend_mfma_supported(const AttendArgs& a);
+hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
+
 hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (a.S.total_q == 0) return hipSuccess;
+  if (attend_mfma_supported(a)) return launch_attend_mfma(a, ws, ws_bytes, stream);
   const int n_hg = (a.n_h + kValuHG - 1) / kValuHG;
+  const int C = attend_chunk_slots(a);
   const int64_t mc = attend_max_chunks(a);
   const size_t need = attend_workspace_bytes(a);
   const int64_t single_blocks = (int64_t)a.S.total_q * n_hg;
@@ -281,14 +206,15 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStre
     float* ws_o = reinterpret_cast<float*>(ws);
     float* ws_ml = ws_o + (size_t)a.S.total_q * mc * a.n_h * a.q.dim;
     hipLaunchKernelGGL(attend_valu_kernel<true>, dim3((unsigned)(single_blocks * mc)), dim3(256), 0, stream, a, ws_o,
-                       ws_ml, n_hg, (int)mc);
+                       ws_ml, n_hg, (int)mc, C);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)single_blocks), dim3(256), 0, stream, a, ws_o, ws_ml, n_hg,
-                       (int)mc, kValuChunk);
+    const int n_hg8 = (a.n_h + 7) / 8;
+    hipLaunchKernelGGL(attend_combine_kernel<ROPE_ACCURATE>, dim3((unsigned)(a.S.total_q * n_hg8)), dim3(256), 0,
+                       stream, a, ws_o, ws_ml, (int)mc, C);
   } else {
     hipLaunchKernelGGL(attend_valu_kernel<false>, dim3((unsigned)single_blocks), dim3(256), 0, stream, a, nullptr,
-                       nullptr, n_hg, 1);
+                       nullptr, n_hg, 1, C);
   }
   return hipGetLastError();
 }

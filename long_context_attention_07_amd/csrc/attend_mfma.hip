@@ -1,0 +1,364 @@
+// Shared-KV MQA on the matrix cores: bf16 rows of 512 dims ("DeepSeek-V4 深度分析报告"
+// section 2.1 and Figure 2: shared-KV MQA over the selected (CSA) or all (HCA) compressed
+// entries with the 128-token window concatenated; list "其他注意力技术细节": partial RoPE on
+// the last 64 dims, inverse RoPE of the output, learnable sink).
+//
+// Workgroup = (token, group of 16 query heads, chunk of the token's key list), 4 waves.
+// The key list is walked in tiles of 64 rows staged in LDS (rows padded to 1040 bytes);
+// the next tile is prefetched into registers (one 1 KiB row per wave instruction, any
+// row order, so the top-k gather is fully coalesced) while the current one is processed.
+//   QK   S^T[key, head] = K Q^T with v_mfma_f32_16x16x32_bf16: wave w owns keys
+//        16w..16w+15 of the tile (A operand from LDS), the 16 rotated query rows sit in
+//        registers as the B operand (64 VGPRs).
+//   softmax  in the log2 domain; per-head tile max and sum exchanged across the 4 waves in
+//        a fixed order; P rounded to bf16 (the sums use the rounded values).
+//   PV   O[head, dim] += P V: wave w owns dims 128w..128w+127; P is the A operand (LDS),
+//        V is read from the same row-major key tile with ds_read_b64_tr_b16, which hands
+//        each lane a column of 4 consecutive keys -- the B operand layout.
+// Chunk partials are folded in chunk order from the sink exactly as in the combine kernel
+// (attend_common.cuh), so split and single launches agree bit for bit, and a token's bits
+// never depend on the batch.  Window rows are rotated (RoPE at their own positions) as
+// they are staged; absent slots are staged as zero rows and masked.
+
+#include "attend_common.cuh"
+
+namespace csa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef i16x4_t __attribute__((address_space(3))) * lds_i16x4_ptr;
+
+constexpr int kT = 64;                 // keys per tile
+constexpr int kHG = 16;                // query heads per workgroup
+constexpr int kDM = 512;               // head dim of this kernel
+constexpr int kKStride = kDM * 2 + 16;  // bytes per staged key row
+constexpr int kPStride = kT * 2 + 16;   // bytes per P row (one head)
+
+struct __align__(16) MfmaLds {
+  uint8_t k[kT * kKStride];
+  uint8_t p[kHG * kPStride];
+  float red_max[4][kHG];
+  float red_sum[4][kHG];
+  float alpha[kHG];
+  float mc[kHG];
+  float lc[kHG];
+};
+
+struct TileStage {
+  uint4 v[16];      // row 16w+it, bytes 16*lane .. 16*lane+15
+  uint32_t valid;   // bit it: row present
+  uint32_t win;     // bit it: window row (rotated when staged)
+  int64_t pos0;     // position of window row it is pos0 + it
+};
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// Rotate the 4 pairs held in one 16-byte chunk (8 bf16 dims starting at pair index q0).
+__device__ __forceinline__ uint4 rotate_chunk(uint4 v, int64_t pos, const RopeTab& rope, int q0) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float c, s;
+    rope_cs_mode<ROPE_FAST>(pos, rope, q0 + i, &c, &s);
+    float2 y = rotate2(make_float2(bf_lo(w[i]), bf_hi(w[i])), c, s);
+    w[i] = pack_bf16(y.x, y.y);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ void load_tile(const AttendArgs& a, int t, const TokenCtx& ctx, int64_t n_ent,
+                                          int64_t s0, int w, int lane, TileStage& st) {
+  SlotRef r;
+  r.kind = 0;
+  r.row = 0;
+  r.pos = 0;
+  if (lane < 16) r = resolve_slot(a, t, ctx, n_ent, s0 + 16 * w + lane);
+  st.valid = (uint32_t)__ballot(lane < 16 && r.kind != 0);
+  st.win = (uint32_t)__ballot(lane < 16 && r.kind == 2);
+  st.pos0 = ctx.p - a.n_win + 1 + (s0 + 16 * w - n_ent);
+  const int row_lo = (int)(uint32_t)(r.row & 0xffffffffu);
+  const int row_hi = (int)(uint32_t)((uint64_t)r.row >> 32);
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    if ((st.valid >> it) & 1u) {
+      const int64_t row = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_hi, it) << 32) |
+                                    (uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_lo, it));
+      const RowsDev& R = ((st.win >> it) & 1u) ? a.tok : a.kv;
+      st.v[it] = reinterpret_cast<const uint4*>(R.data + row * R.stride)[lane];
+    } else {
+      st.v[it] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+}
+
+__device__ __forceinline__ void store_tile(MfmaLds& L, const AttendArgs& a, const TileStage& st, int w, int lane) {
+  const int dn = kDM - a.rope.dims;
+  const bool rope_lane = 8 * lane >= dn;
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    uint4 v = st.v[it];
+    if (((st.win >> it) & 1u) && rope_lane) v = rotate_chunk(v, st.pos0 + it, a.rope, (8 * lane - dn) >> 1);
+    *reinterpret_cast<uint4*>(&L.k[(16 * w + it) * kKStride + 16 * lane]) = v;
+  }
+}
+
+template <bool SPLIT>
+__global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* __restrict__ ws_o,
+                                                          float* __restrict__ ws_ml, int n_hg, int max_chunks,
+                                                          int chunk_slots, int n_logical) {
+  __shared__ MfmaLds L;
+  // XCD-aware order: consecutive logical workgroups (the head groups and chunks of one
+  // token) land on the same XCD and share its L2.
+  const int n_phys = gridDim.x;
+  const int per_xcd = n_phys / 8;
+  const int lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (lid >= n_logical) return;
+  int rest = lid;
+  const int hg = rest % n_hg;
+  rest /= n_hg;
+  int c_only = 0;
+  if (SPLIT) {
+    c_only = rest % max_chunks;
+    rest /= max_chunks;
+  }
+  const int t = rest;
+
+  const TokenCtx ctx = token_ctx(a.S, t);
+  const int64_t n_ent = entry_slots(a, ctx);
+  const int64_t n_slots = n_ent + a.n_win;
+  const int n_chunks = (int)((n_slots + chunk_slots - 1) / chunk_slots);
+  if (SPLIT && c_only >= n_chunks) return;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int dn = kDM - a.rope.dims;
+
+  // ---- rotated query fragments: head hg*16 + c16, dims 8g + 32kk .. +7
+  bf16x8_t qf[16];
+  {
+    const int h = hg * kHG + c16;
+    uint4 raw[16];
+    if (h < a.n_h) {
+      const uint8_t* qrow = a.q.data + ((int64_t)t * a.n_h + h) * a.q.stride;
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) raw[kk] = *reinterpret_cast<const uint4*>(qrow + (8 * g + 32 * kk) * 2);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) raw[kk] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const int d0 = 8 * g + 32 * kk;
+      if (d0 >= dn) raw[kk] = rotate_chunk(raw[kk], ctx.p, a.rope, (d0 - dn) >> 1);
+      qf[kk] = __builtin_bit_cast(bf16x8_t, raw[kk]);
+    }
+  }
+
+  // ---- fold state of heads 4g+j (output layout) and running O over chunks
+  FoldState fs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = hg * kHG + 4 * g + j;
+    fs[j] = fold_init(h < a.n_h ? a.sink[h] * kLog2e : -INFINITY);
+  }
+  f32x4_t O[8], Ot[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    Ot[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  float m_run = -INFINITY, l_run = 0.f;  // head c16 (S^T layout)
+
+  const int c_begin = SPLIT ? c_only : 0;
+  const int c_end = SPLIT ? c_only + 1 : n_chunks;
+  auto tiles_in = [&](int c) -> int {
+    const int64_t rem = n_slots - (int64_t)c * chunk_slots;
+    const int64_t len = rem < chunk_slots ? rem : chunk_slots;
+    return (int)((len + kT - 1) / kT);
+  };
+
+  int cc = c_begin, tile = 0, ntile = tiles_in(cc);
+  TileStage st;
+  load_tile(a, t, ctx, n_ent, (int64_t)cc * chunk_slots, w, lane, st);
+
+  while (true) {
+    __syncthreads();  // previous tile fully consumed
+    store_tile(L, a, st, w, lane);
+    const uint32_t valid = st.valid;
+    __syncthreads();  // tile visible
+
+    int ncc = cc, ntl = tile + 1;
+    if (ntl == ntile) {
+      ncc = cc + 1;
+      ntl = 0;
+    }
+    const bool has_next = ncc < c_end;
+    if (has_next) load_tile(a, t, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, w, lane, st);
+
+    // ---- S^T = K Q^T for keys 16w..16w+15
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint8_t* krow = &L.k[(16 * w + c16) * kKStride + 16 * g];
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(krow + 64 * kk);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], acc, 0, 0, 0);
+      }
+    }
+    float s[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] = ((valid >> (4 * g + j)) & 1u) ? acc[j] * a.scale_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (lane < 16) L.red_max[w][c16] = mx;
+    __syncthreads();
+    const float tmax = fmaxf(fmaxf(L.red_max[0][c16], L.red_max[1][c16]), fmaxf(L.red_max[2][c16], L.red_max[3][c16]));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = rescale(m_run, m_new);
+    float pr[4];
+    uint32_t pb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float pj = (s[j] == -INFINITY) ? 0.f : ex2(s[j] - m_new);
+      pb[j] = f32_to_bf16_bits(pj);
+      pr[j] = __uint_as_float(pb[j] << 16);
+    }
+    *reinterpret_cast<uint2*>(&L.p[c16 * kPStride + (16 * w + 4 * g) * 2]) =
+        make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16));
+    float ls = ((pr[0] + pr[1]) + pr[2]) + pr[3];
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    if (lane < 16) L.red_sum[w][c16] = ls;
+    if (w == 0 && lane < 16) L.alpha[c16] = alpha;
+    __syncthreads();
+    const float tsum = ((L.red_sum[0][c16] + L.red_sum[1][c16]) + L.red_sum[2][c16]) + L.red_sum[3][c16];
+    l_run = __builtin_fmaf(l_run, alpha, tsum);
+    m_run = m_new;
+
+    // ---- O[head 4g+j, dims 128w + 16nb + c16] = O * alpha + P V
+    {
+      float al[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) al[j] = L.alpha[4 * g + j];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) O[nb][j] *= al[j];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(&L.p[c16 * kPStride + (8 * g + 32 * ks) * 2]);
+        const int r0 = 32 * ks + 8 * g + (c16 >> 2);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const int n0 = 128 * w + 16 * nb + 4 * (c16 & 3);
+          uint8_t* base = &L.k[r0 * kKStride + n0 * 2];
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + 4 * kKStride));
+          typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
+          const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, both), O[nb], 0, 0, 0);
+        }
+      }
+    }
+
+    if (tile + 1 == ntile) {
+      // ---- chunk done: per-head (m, l) to the output layout, then fold or write
+      if (w == 0 && lane < 16) {
+        L.mc[c16] = m_run;
+        L.lc[c16] = l_run;
+      }
+      __syncthreads();
+      if (SPLIT) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int h = hg * kHG + 4 * g + j;
+          if (h < a.n_h) {
+            const int64_t base = ((int64_t)t * max_chunks + cc) * a.n_h + h;
+            float* po = ws_o + base * kDM + 128 * w + c16;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) po[16 * nb] = O[nb][j];
+            if (w == 0 && c16 == 0) {
+              ws_ml[2 * base] = L.mc[4 * g + j];
+              ws_ml[2 * base + 1] = L.lc[4 * g + j];
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float fa, fb;
+          fold_step(fs[j], L.mc[4 * g + j], L.lc[4 * g + j], &fa, &fb);
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) Ot[nb][j] = __builtin_fmaf(Ot[nb][j], fa, O[nb][j] * fb);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m_run = -INFINITY;
+      l_run = 0.f;
+    }
+    if (!has_next) break;
+    if (ntl == 0) ntile = tiles_in(ncc);
+    cc = ncc;
+    tile = ntl;
+  }
+
+  if (!SPLIT) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = hg * kHG + 4 * g + j;
+      const float inv = (fs[j].Z > 0.f) ? 1.0f / fs[j].Z : 0.f;
+      const int64_t orow = (int64_t)t * a.n_h + h;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int d = 128 * w + 16 * nb + c16;
+        const float x = Ot[nb][j] * inv;
+        const float partner = __shfl_xor(x, 1, 64);
+        if (h < a.n_h) store_out(a, orow, d, finalize_elem<ROPE_FAST>(x, partner, d, dn, ctx.p, a.rope));
+      }
+      if (a.lse && w == 0 && c16 == 0 && h < a.n_h) a.lse[orow] = lse_natural(fs[j]);
+    }
+  }
+}
+
+bool attend_mfma_supported(const AttendArgs& a) {
+  return a.q.dim == kDM && a.q.dtype == DT_BF16 && a.kv.dtype == DT_BF16 && a.tok.dtype == DT_BF16 &&
+         a.out.dtype == DT_BF16 && a.rope.dims % 8 == 0 && a.kv.stride % 16 == 0 && a.tok.stride % 16 == 0 &&
+         a.q.stride % 16 == 0;
+}
+
+hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int n_hg = (a.n_h + kHG - 1) / kHG;
+  const int C = chunk_slots_for(a.csa, a.k, a.n_win);
+  const int64_t mc = attend_max_chunks(a);
+  const size_t need = attend_workspace_bytes(a);
+  const int64_t single = (int64_t)a.S.total_q * n_hg;
+  const bool split = ws != nullptr && ws_bytes >= need && mc > 1 && single < 512;
+  if (split) {
+    float* ws_o = reinterpret_cast<float*>(ws);
+    float* ws_ml = ws_o + (size_t)a.S.total_q * mc * a.n_h * kDM;
+    const int64_t n_log = single * mc;
+    const int64_t n_phys = (n_log + 7) / 8 * 8;
+    hipLaunchKernelGGL(attend_mfma_kernel<true>, dim3((unsigned)n_phys), dim3(256), 0, stream, a, ws_o, ws_ml, n_hg,
+                       (int)mc, C, (int)n_log);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_hg8 = (a.n_h + 7) / 8;
+    hipLaunchKernelGGL(attend_combine_kernel<ROPE_FAST>, dim3((unsigned)(a.S.total_q * n_hg8)), dim3(256), 0, stream,
+                       a, ws_o, ws_ml, (int)mc, C);
+  } else {
+    const int64_t n_phys = (single + 7) / 8 * 8;
+    hipLaunchKernelGGL(attend_mfma_kernel<false>, dim3((unsigned)n_phys), dim3(256), 0, stream, a, nullptr, nullptr,
+                       n_hg, 1, C, (int)single);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -53,8 +53,9 @@ struct SeqsDev {
 
 // Inverse frequencies of the rotated pairs, computed once on the host in float64.
 struct RopeTab {
-  double inv_freq[kMaxRopePairs];
-  int dims;  // rotated trailing dims (even); 0 = none
+  double inv_freq[kMaxRopePairs];      // radians per position
+  double inv_freq_rev[kMaxRopePairs];  // revolutions per position (inv_freq / 2 pi)
+  int dims;                            // rotated trailing dims (even); 0 = none
 };
 
 // ------------------------------------------------------------------------- bf16

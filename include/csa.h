@@ -118,7 +118,8 @@ int csa_compress(const csa_seqs* seqs, const csa_rows* c, const csa_rows* z, con
  * the stuffyNLP review names the indexer of DeepSeek-V3.2-Exp).  For query token t at
  * position p, for every visible entry i < V(p) = floor((p+1)/ratio):
  *     score[t, i] = sum_{h < n_I} w[t,h] * max(0, sum_d qI[t,h,d] * kI[entry_off[b]+i, d])
- * with heads summed in ascending order.  Columns i >= V(p) are not written.
+ * accumulated in float32 in an order fixed per (token, entry).  Columns i >= V(p) are not
+ * written.
  *   qI      rows [total_q * n_I, d_I] (F32, BF16 or MXFP4); row t*n_I + h
  *   w       device float32 [total_q, n_I]
  *   kI      entry pool rows (same dtype as qI), dim d_I

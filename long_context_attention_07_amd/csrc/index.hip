@@ -3,7 +3,8 @@
 // DSA's lightweight indexer; Figure 2 "Lightning Indexer"; stuffyNLP review: the indexer of
 // DeepSeek-V3.2-Exp).
 //
-// Generic float32-arithmetic kernel used for F32 and MXFP4 rows: one workgroup per
+// Generic float32-arithmetic kernel used for F32 and MXFP4 rows (bf16 keys of 128 dims
+// go to the matrix-core kernel in index_mfma.hip): one workgroup per
 // (token, tile of 256 entries), one entry per thread, the token's qI block decoded into
 // LDS, the entry's key row decoded into registers; dims then heads are summed in
 // ascending order, so a score depends on its token and entry only.
@@ -52,8 +53,14 @@ __global__ void __launch_bounds__(256) index_score_valu_kernel(SeqsDev S, RowsDe
   score[(int64_t)t * score_stride + e] = s;
 }
 
+bool index_mfma_supported(const RowsDev& qI, const RowsDev& kI, int n_I, int64_t score_stride);
+hipError_t launch_index_score_mfma(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
+                                   int ratio, float* score, int64_t score_stride, int max_vis, hipStream_t stream);
+
 hipError_t launch_index_score(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
                               int ratio, float* score, int64_t score_stride, int max_vis, hipStream_t stream) {
+  if (index_mfma_supported(qI, kI, n_I, score_stride))
+    return launch_index_score_mfma(S, qI, w, n_I, kI, ratio, score, score_stride, max_vis, stream);
   const int n_tiles = (max_vis + kIdxTile - 1) / kIdxTile;
   const int64_t blocks = (int64_t)S.total_q * n_tiles;
   if (blocks == 0) return hipSuccess;

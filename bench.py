@@ -152,18 +152,26 @@ def make_lengths(wl):
 
 
 def time_fn(fn, layers, reps, stream):
-    """Average duration (ms) of fn(layer) over `reps` calls rotating over the layer sets,
-    bracketed by events on the launch stream."""
-    for i in range(len(layers)):
-        fn(layers[i])
+    """Average GPU duration (ms) of fn(layer): one call per layer set captured in a HIP
+    graph, replayed until `reps` calls have run, bracketed by events on the launch stream
+    (replaying a graph keeps host launch overhead out of the figure)."""
+    for L_ in layers:
+        fn(L_)
     stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for L_ in layers:
+            fn(L_)
+    g.replay()
+    stream.synchronize()
+    n = max(1, reps // len(layers))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for i in range(reps):
-        fn(layers[i % len(layers)])
+    for _ in range(n):
+        g.replay()
     e1.record(stream)
     e1.synchronize()
-    return e0.elapsed_time(e1) / reps
+    return e0.elapsed_time(e1) / (n * len(layers))
 
 
 def cpu_baseline(layer, budget_s=12.0):

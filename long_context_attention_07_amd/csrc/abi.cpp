@@ -10,7 +10,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/csa.h"
+#include "csa.h"
 #include "kernels.h"
 
 namespace {

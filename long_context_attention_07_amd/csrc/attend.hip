@@ -29,7 +29,7 @@ constexpr int kValuRegs = kMaxDim / 32;
 
 // Final store of one head's output (thread (head, lane l32) holds dims l32 + 32 r).
 __device__ __forceinline__ void finalize_valu(const AttendArgs& a, int t, int h, int l32, int64_t p,
-                                              const FoldState& f, const float* O, int D) {
+                                              const FoldState& f, const float* O, int D, const FreqLds& F) {
   const float inv = (f.Z > 0.f) ? 1.0f / f.Z : 0.f;
   const int dn = D - a.rope.dims;
   const int64_t orow = (int64_t)t * a.n_h + h;
@@ -39,7 +39,7 @@ __device__ __forceinline__ void finalize_valu(const AttendArgs& a, int t, int h,
     if (d < D) {
       const float x = O[r] * inv;
       const float partner = __shfl_xor(x, 1, 32);
-      store_out(a, orow, d, finalize_elem<ROPE_ACCURATE>(x, partner, d, dn, p, a.rope));
+      store_out(a, orow, d, finalize_elem<ROPE_ACCURATE>(x, partner, d, dn, p, F));
     }
   }
   if (a.lse && l32 == 0) a.lse[orow] = lse_natural(f);
@@ -53,6 +53,7 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a, float* _
   __shared__ float ks[kValuTK][kMaxDim + 1];
   __shared__ float ps[kValuHG][kValuTK];
   __shared__ SlotRef slots[kValuTK];
+  __shared__ FreqLds F;
 
   int64_t bid = blockIdx.x;
   int c_only = 0;
@@ -75,6 +76,8 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a, float* _
   const int hl = tid >> 5, l32 = tid & 31;
   const int h = g * kValuHG + hl;
   const bool hvalid = h < a.n_h;
+  load_freqs(F, a.rope);
+  __syncthreads();
 
   for (int x = tid; x < kValuHG * half; x += 256) {
     const int hh = x / half, pc = x % half;
@@ -82,7 +85,7 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a, float* _
     float2 v = make_float2(0.f, 0.f);
     if (hq < a.n_h) {
       v = load_pair(a.q, (int64_t)t * a.n_h + hq, pc);
-      if (2 * pc >= dn) v = rope_pair(v, ctx.p, a.rope.inv_freq[pc - dn / 2], 1.0f);
+      if (2 * pc >= dn) v = rope_pair(v, ctx.p, F.rad[pc - dn / 2], 1.0f);
     }
     qs[hh][2 * pc] = v.x;
     qs[hh][2 * pc + 1] = v.y;
@@ -117,7 +120,7 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a, float* _
           v = load_pair(a.kv, sr.row, pc);
         } else if (sr.kind == 2) {
           v = load_pair(a.tok, sr.row, pc);
-          if (2 * pc >= dn) v = rope_pair(v, sr.pos, a.rope.inv_freq[pc - dn / 2], 1.0f);
+          if (2 * pc >= dn) v = rope_pair(v, sr.pos, F.rad[pc - dn / 2], 1.0f);
         }
         ks[j][2 * pc] = v.x;
         ks[j][2 * pc + 1] = v.y;
@@ -174,7 +177,7 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a, float* _
       for (int r = 0; r < kValuRegs; ++r) O[r] = __builtin_fmaf(O[r], fa, o[r] * fb);
     }
   }
-  if (!SPLIT && hvalid) finalize_valu(a, t, h, l32, ctx.p, f, O, D);
+  if (!SPLIT && hvalid) finalize_valu(a, t, h, l32, ctx.p, f, O, D, F);
 }
 
 int attend_chunk_slots(const AttendArgs& a) { return chunk_slots_for(a.csa, a.k, a.n_win); }

@@ -14,12 +14,27 @@ namespace csa {
 // including its combine step, so the fold stays bit-identical across launch modes.
 enum RopeMode : int { ROPE_ACCURATE = 0, ROPE_FAST = 1 };
 
+// The frequency table lives in LDS (FreqLds, filled once per workgroup): indexing the
+// kernel-argument copy with a per-lane index would turn every lookup into a dependent
+// global load.
+struct FreqLds {
+  double rad[kMaxRopePairs];
+  double rev[kMaxRopePairs];
+};
+
+__device__ __forceinline__ void load_freqs(FreqLds& F, const RopeTab& rope) {
+  for (int i = threadIdx.x; i < rope.dims / 2; i += blockDim.x) {
+    F.rad[i] = rope.inv_freq[i];
+    F.rev[i] = rope.inv_freq_rev[i];
+  }
+}
+
 template <int MODE>
-__device__ __forceinline__ void rope_cs_mode(int64_t pos, const RopeTab& rope, int q, float* c, float* s) {
+__device__ __forceinline__ void rope_cs_mode(int64_t pos, const FreqLds& F, int q, float* c, float* s) {
   if (MODE == ROPE_ACCURATE) {
-    rope_cs(pos, rope.inv_freq[q], c, s);
+    rope_cs(pos, F.rad[q], c, s);
   } else {
-    double r = (double)pos * rope.inv_freq_rev[q];
+    double r = (double)pos * F.rev[q];
     r -= __builtin_rint(r);
     const float x = (float)r;
     *s = __builtin_amdgcn_sinf(x);
@@ -70,11 +85,11 @@ __device__ __forceinline__ SlotRef resolve_slot(const AttendArgs& a, int t, cons
 // Final value of one output element: normalise, inverse-rotate (RoPE dims), return.
 // `partner` is the normalised value of the other element of the pair (d ^ 1).
 template <int MODE>
-__device__ __forceinline__ float finalize_elem(float x, float partner, int d, int dn, int64_t p, const RopeTab& rope) {
+__device__ __forceinline__ float finalize_elem(float x, float partner, int d, int dn, int64_t p, const FreqLds& F) {
   if (d < dn) return x;
   const int q = (d - dn) >> 1;
   float c, s;
-  rope_cs_mode<MODE>(p, rope, q, &c, &s);
+  rope_cs_mode<MODE>(p, F, q, &c, &s);
   s = -s;
   float2 pr = (d & 1) ? make_float2(partner, x) : make_float2(x, partner);
   float2 y = rotate2(pr, c, s);
@@ -104,6 +119,9 @@ __global__ void __launch_bounds__(256) attend_combine_kernel(AttendArgs a, const
                                                              const float* __restrict__ ws_ml, int max_chunks,
                                                              int chunk_slots) {
   constexpr int kRegs = kMaxDim / 32;
+  __shared__ FreqLds F;
+  load_freqs(F, a.rope);
+  __syncthreads();
   const int n_hg8 = (a.n_h + 7) / 8;
   const int g = blockIdx.x % n_hg8;
   const int t = blockIdx.x / n_hg8;
@@ -138,7 +156,7 @@ __global__ void __launch_bounds__(256) attend_combine_kernel(AttendArgs a, const
     if (d < D) {
       const float x = O[r] * inv;
       const float partner = __shfl_xor(x, 1, 32);
-      store_out(a, orow, d, finalize_elem<MODE>(x, partner, d, dn, ctx.p, a.rope));
+      store_out(a, orow, d, finalize_elem<MODE>(x, partner, d, dn, ctx.p, F));
     }
   }
   if (a.lse && l32 == 0) a.lse[orow] = lse_natural(f);

@@ -35,8 +35,11 @@ constexpr int kDM = 512;               // head dim of this kernel
 constexpr int kKStride = kDM * 2 + 16;  // bytes per staged key row
 constexpr int kPStride = kT * 2 + 16;   // bytes per P row (one head)
 
+constexpr int kMaxIdx = 4096;           // largest k the in-LDS idx table holds
+
 struct __align__(16) MfmaLds {
   uint8_t k[kT * kKStride];
+  int32_t sidx[kMaxIdx];                // idx[t, s_lo .. s_hi) of this workgroup's chunks
   uint8_t p[kHG * kPStride];
   float red_max[4][kHG];
   float red_sum[4][kHG];
@@ -59,25 +62,50 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 }
 
 // Rotate the 4 pairs held in one 16-byte chunk (8 bf16 dims starting at pair index q0).
-__device__ __forceinline__ uint4 rotate_chunk(uint4 v, int64_t pos, const RopeTab& rope, int q0) {
+__device__ __forceinline__ uint4 rotate_chunk(uint4 v, int64_t pos, const FreqLds& F, int q0) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float c, s;
-    rope_cs_mode<ROPE_FAST>(pos, rope, q0 + i, &c, &s);
+    rope_cs_mode<ROPE_FAST>(pos, F, q0 + i, &c, &s);
     float2 y = rotate2(make_float2(bf_lo(w[i]), bf_hi(w[i])), c, s);
     w[i] = pack_bf16(y.x, y.y);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__device__ __forceinline__ void load_tile(const AttendArgs& a, int t, const TokenCtx& ctx, int64_t n_ent,
-                                          int64_t s0, int w, int lane, TileStage& st) {
+// Slot resolution from the LDS copy of the token's idx (entries) or by arithmetic (HCA
+// entries, window positions), so no tile load waits on an idx load.
+__device__ __forceinline__ SlotRef resolve_slot_lds(const AttendArgs& a, const TokenCtx& ctx, int64_t n_ent,
+                                                    int64_t s, const int32_t* sidx, int64_t s_lo) {
   SlotRef r;
   r.kind = 0;
   r.row = 0;
   r.pos = 0;
-  if (lane < 16) r = resolve_slot(a, t, ctx, n_ent, s0 + 16 * w + lane);
+  if (s < n_ent) {
+    const int64_t e = a.csa ? (int64_t)sidx[s - s_lo] : s;
+    if (e >= 0) {
+      r.kind = 1;
+      r.row = ctx.entry0 + e;
+    }
+  } else if (s < n_ent + a.n_win) {
+    const int64_t pos = ctx.p - a.n_win + 1 + (s - n_ent);
+    if (pos >= 0 && pos >= ctx.tok_lo) {
+      r.kind = 2;
+      r.row = ctx.tok0 + (pos - ctx.tok_lo);
+      r.pos = pos;
+    }
+  }
+  return r;
+}
+
+__device__ __forceinline__ void load_tile(const AttendArgs& a, const TokenCtx& ctx, int64_t n_ent, int64_t s0,
+                                          int w, int lane, TileStage& st, const int32_t* sidx, int64_t s_lo) {
+  SlotRef r;
+  r.kind = 0;
+  r.row = 0;
+  r.pos = 0;
+  if (lane < 16) r = resolve_slot_lds(a, ctx, n_ent, s0 + 16 * w + lane, sidx, s_lo);
   st.valid = (uint32_t)__ballot(lane < 16 && r.kind != 0);
   st.win = (uint32_t)__ballot(lane < 16 && r.kind == 2);
   st.pos0 = ctx.p - a.n_win + 1 + (s0 + 16 * w - n_ent);
@@ -88,6 +116,8 @@ __device__ __forceinline__ void load_tile(const AttendArgs& a, int t, const Toke
     if ((st.valid >> it) & 1u) {
       const int64_t row = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_hi, it) << 32) |
                                     (uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_lo, it));
+      // the row address stays scalar (uniform row index, pool base and stride from the
+      // kernel arguments): one SGPR base plus the lane offset per load
       const RowsDev& R = ((st.win >> it) & 1u) ? a.tok : a.kv;
       st.v[it] = reinterpret_cast<const uint4*>(R.data + row * R.stride)[lane];
     } else {
@@ -96,14 +126,27 @@ __device__ __forceinline__ void load_tile(const AttendArgs& a, int t, const Toke
   }
 }
 
-__device__ __forceinline__ void store_tile(MfmaLds& L, const AttendArgs& a, const TileStage& st, int w, int lane) {
-  const int dn = kDM - a.rope.dims;
-  const bool rope_lane = 8 * lane >= dn;
+// Stage the wave's 16 rows in LDS, then rotate the window rows among them in place (RoPE
+// at each row's own position), one pair per lane: a compact loop that runs only for the
+// tiles that hold window rows.
+__device__ __forceinline__ void store_tile(MfmaLds& L, const AttendArgs& a, const TileStage& st, int w, int lane,
+                                           const FreqLds& F) {
 #pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    uint4 v = st.v[it];
-    if (((st.win >> it) & 1u) && rope_lane) v = rotate_chunk(v, st.pos0 + it, a.rope, (8 * lane - dn) >> 1);
-    *reinterpret_cast<uint4*>(&L.k[(16 * w + it) * kKStride + 16 * lane]) = v;
+  for (int it = 0; it < 16; ++it) *reinterpret_cast<uint4*>(&L.k[(16 * w + it) * kKStride + 16 * lane]) = st.v[it];
+  const int n_pairs = a.rope.dims >> 1;
+  const int dn = kDM - a.rope.dims;
+  uint32_t wm = st.win;
+  while (wm) {
+    const int it = __ffs((int)wm) - 1;
+    wm &= wm - 1u;
+    if (lane < n_pairs) {
+      uint32_t* pp = reinterpret_cast<uint32_t*>(&L.k[(16 * w + it) * kKStride + (dn + 2 * lane) * 2]);
+      const uint32_t u = *pp;
+      float c, s;
+      rope_cs_mode<ROPE_FAST>(st.pos0 + it, F, lane, &c, &s);
+      const float2 y = rotate2(make_float2(bf_lo(u), bf_hi(u)), c, s);
+      *pp = pack_bf16(y.x, y.y);
+    }
   }
 }
 
@@ -112,6 +155,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
                                                           float* __restrict__ ws_ml, int n_hg, int max_chunks,
                                                           int chunk_slots, int n_logical) {
   __shared__ MfmaLds L;
+  __shared__ FreqLds F;
   // XCD-aware order: consecutive logical workgroups (the head groups and chunks of one
   // token) land on the same XCD and share its L2.
   const int n_phys = gridDim.x;
@@ -138,6 +182,20 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
   const int w = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
   const int dn = kDM - a.rope.dims;
+  load_freqs(F, a.rope);
+  const int c_begin = SPLIT ? c_only : 0;
+  const int c_end = SPLIT ? c_only + 1 : n_chunks;
+  const int64_t s_lo = (int64_t)c_begin * chunk_slots;
+  if (a.csa) {
+    const int64_t s_hi = min((int64_t)c_end * chunk_slots, n_ent);
+    const int32_t* src = a.idx + (int64_t)t * a.k;
+    for (int64_t s = s_lo + tid; s < s_hi; s += 256) L.sidx[s - s_lo] = src[s];
+  }
+  __syncthreads();
+
+  // first tile's rows are requested before the query rows, so the two latencies overlap
+  TileStage st;
+  load_tile(a, ctx, n_ent, s_lo, w, lane, st, L.sidx, s_lo);
 
   // ---- rotated query fragments: head hg*16 + c16, dims 8g + 32kk .. +7
   bf16x8_t qf[16];
@@ -155,7 +213,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       const int d0 = 8 * g + 32 * kk;
-      if (d0 >= dn) raw[kk] = rotate_chunk(raw[kk], ctx.p, a.rope, (d0 - dn) >> 1);
+      if (d0 >= dn) raw[kk] = rotate_chunk(raw[kk], ctx.p, F, (d0 - dn) >> 1);
       qf[kk] = __builtin_bit_cast(bf16x8_t, raw[kk]);
     }
   }
@@ -175,8 +233,6 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
   }
   float m_run = -INFINITY, l_run = 0.f;  // head c16 (S^T layout)
 
-  const int c_begin = SPLIT ? c_only : 0;
-  const int c_end = SPLIT ? c_only + 1 : n_chunks;
   auto tiles_in = [&](int c) -> int {
     const int64_t rem = n_slots - (int64_t)c * chunk_slots;
     const int64_t len = rem < chunk_slots ? rem : chunk_slots;
@@ -184,12 +240,10 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
   };
 
   int cc = c_begin, tile = 0, ntile = tiles_in(cc);
-  TileStage st;
-  load_tile(a, t, ctx, n_ent, (int64_t)cc * chunk_slots, w, lane, st);
 
   while (true) {
     __syncthreads();  // previous tile fully consumed
-    store_tile(L, a, st, w, lane);
+    store_tile(L, a, st, w, lane, F);
     const uint32_t valid = st.valid;
     __syncthreads();  // tile visible
 
@@ -199,7 +253,8 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
       ntl = 0;
     }
     const bool has_next = ncc < c_end;
-    if (has_next) load_tile(a, t, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, w, lane, st);
+    if (has_next)
+      load_tile(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, w, lane, st, L.sidx, s_lo);
 
     // ---- S^T = K Q^T for keys 16w..16w+15
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -321,7 +376,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
         const int d = 128 * w + 16 * nb + c16;
         const float x = Ot[nb][j] * inv;
         const float partner = __shfl_xor(x, 1, 64);
-        if (h < a.n_h) store_out(a, orow, d, finalize_elem<ROPE_FAST>(x, partner, d, dn, ctx.p, a.rope));
+        if (h < a.n_h) store_out(a, orow, d, finalize_elem<ROPE_FAST>(x, partner, d, dn, ctx.p, F));
       }
       if (a.lse && w == 0 && c16 == 0 && h < a.n_h) a.lse[orow] = lse_natural(fs[j]);
     }
@@ -329,7 +384,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
 }
 
 bool attend_mfma_supported(const AttendArgs& a) {
-  return a.q.dim == kDM && a.q.dtype == DT_BF16 && a.kv.dtype == DT_BF16 && a.tok.dtype == DT_BF16 &&
+  return (!a.csa || a.k <= kMaxIdx) && a.q.dim == kDM && a.q.dtype == DT_BF16 && a.kv.dtype == DT_BF16 && a.tok.dtype == DT_BF16 &&
          a.out.dtype == DT_BF16 && a.rope.dims % 8 == 0 && a.kv.stride % 16 == 0 && a.tok.stride % 16 == 0 &&
          a.q.stride % 16 == 0;
 }

@@ -171,8 +171,14 @@ __device__ __forceinline__ float load_elem(const RowsDev& R, int64_t r, int d) {
   }
 }
 
-// Two adjacent elements (2c, 2c+1) of row r.
+// Two adjacent elements (2c, 2c+1) of row r, with one vector load for F32 / BF16 rows.
 __device__ __forceinline__ float2 load_pair(const RowsDev& R, int64_t r, int c) {
+  const uint8_t* row = R.data + r * R.stride;
+  if (R.dtype == DT_F32) return reinterpret_cast<const float2*>(row)[c];
+  if (R.dtype == DT_BF16) {
+    const uint32_t u = reinterpret_cast<const uint32_t*>(row)[c];
+    return make_float2(bf16_bits_to_f32(u & 0xffffu), bf16_bits_to_f32(u >> 16));
+  }
   return make_float2(load_elem(R, r, 2 * c), load_elem(R, r, 2 * c + 1));
 }
 
@@ -200,12 +206,19 @@ __device__ __forceinline__ float2 rope_pair(float2 x, int64_t pos, double inv_fr
 
 // ------------------------------------------------------------------------- ragged batch
 
-// Sequence owning query row t: the largest b with q_off[b] <= t.
+// Sequence owning query row t: the largest b with q_off[b] <= t.  The wavefront probes 64
+// evenly spaced offsets per round (q_off is non-decreasing, so the probes that are <= t
+// form a prefix of the ballot), shrinking the interval 64-fold per dependent load.
 __device__ __forceinline__ int seq_of_token(const SeqsDev& S, int t) {
-  int lo = 0, hi = S.n_seqs - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (S.q_off[mid] <= t) lo = mid; else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = S.n_seqs;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) >> 6;
+    const int b = lo + lane * step;
+    const bool ok = b < hi && S.q_off[b] <= t;
+    const int cnt = __popcll(__ballot(ok));  // >= 1: q_off[lo] <= t
+    lo = lo + (cnt - 1) * step;
+    hi = min(hi, lo + step);
   }
   return lo;
 }

@@ -40,33 +40,50 @@ __global__ void __launch_bounds__(256) compress_kernel(SeqsDev S, RowsDev c, Row
   const int64_t tok_lo = S.tok_lo[b];
   const int64_t tok0 = S.tok_off[b];
 
+  __shared__ double s_freq[kMaxRopePairs];
+  for (int q = threadIdx.x; q < rope.dims / 2; q += blockDim.x) s_freq[q] = rope.inv_freq[q];
+  __syncthreads();
+
   float2 acc = make_float2(0.f, 0.f);
   if (active) {
     float m0 = -INFINITY, m1 = -INFINITY, s0 = 0.f, s1 = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int64_t j = (lo < 0 ? 0 : lo); j < hi; ++j) {
-      const int slot = (int)(j - lo);
-      const int64_t r = tok0 + (j - tok_lo);
-      float2 cv = load_pair(c, r, pair);
-      float2 zv = load_pair(z, r, pair);
-      // gate logits in the log2 domain
-      float g0 = (zv.x + bias[(int64_t)slot * D + 2 * pair]) * kLog2e;
-      float g1 = (zv.y + bias[(int64_t)slot * D + 2 * pair + 1]) * kLog2e;
-      // online softmax over the sources, in ascending position
-      float n0 = fmaxf(m0, g0), n1 = fmaxf(m1, g1);
-      float r0 = rescale(m0, n0), r1 = rescale(m1, n1);
-      float e0 = ex2(g0 - n0), e1 = ex2(g1 - n1);
-      s0 = __builtin_fmaf(s0, r0, e0);
-      s1 = __builtin_fmaf(s1, r1, e1);
-      a0 = __builtin_fmaf(a0, r0, e0 * cv.x);
-      a1 = __builtin_fmaf(a1, r1, e1 * cv.y);
-      m0 = n0;
-      m1 = n1;
+    const int64_t j0 = lo < 0 ? 0 : lo;
+    // sources in batches of 8: all loads of a batch are issued before the updates
+    for (int64_t jb = j0; jb < hi; jb += 8) {
+      float2 cv[8], zv[8], bv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t j = jb + u;
+        if (j < hi) {
+          const int64_t r = tok0 + (j - tok_lo);
+          cv[u] = load_pair(c, r, pair);
+          zv[u] = load_pair(z, r, pair);
+          bv[u] = reinterpret_cast<const float2*>(bias + (j - lo) * D)[pair];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (jb + u < hi) {
+          // gate logits in the log2 domain; online softmax in ascending position
+          const float g0 = (zv[u].x + bv[u].x) * kLog2e;
+          const float g1 = (zv[u].y + bv[u].y) * kLog2e;
+          const float n0 = fmaxf(m0, g0), n1 = fmaxf(m1, g1);
+          const float r0 = rescale(m0, n0), r1 = rescale(m1, n1);
+          const float e0 = ex2(g0 - n0), e1 = ex2(g1 - n1);
+          s0 = __builtin_fmaf(s0, r0, e0);
+          s1 = __builtin_fmaf(s1, r1, e1);
+          a0 = __builtin_fmaf(a0, r0, e0 * cv[u].x);
+          a1 = __builtin_fmaf(a1, r1, e1 * cv[u].y);
+          m0 = n0;
+          m1 = n1;
+        }
+      }
     }
     acc = make_float2(a0 / s0, a1 / s1);
     const int d_n = D - rope.dims;
     if (rope.dims > 0 && 2 * pair >= d_n) {
       const int q = pair - d_n / 2;
-      acc = rope_pair(acc, i * ratio, rope.inv_freq[q], 1.0f);
+      acc = rope_pair(acc, i * ratio, s_freq[q], 1.0f);
     }
   }
 

@@ -3,15 +3,20 @@
 // entries before top-k; Figure 2 "Lightning Indexer"; stuffyNLP review: the indexer of
 // DeepSeek-V3.2-Exp).  score[t, e] = sum_h w[t,h] * max(0, qI[t,h] . kI[e]).
 //
-// Workgroup = (token, tile of 512 entries), 4 waves; wave w scores 128 entries as 8 blocks
-// of 16.  Per block, S^T[entry, head] = kI qI^T with v_mfma_f32_16x16x32_bf16: the 16 key
-// rows go straight from HBM into the A operand (each lane loads 16 bytes of a row per
-// k-step), the token's <= 64 indexer heads sit in registers as the B operand (4 blocks of
-// 16 heads).  Each lane then forms sum_hb w*relu over its 4 head blocks (ascending) and a
-// fixed xor-butterfly over the 16 lanes of a column finishes the head sum: a score depends
-// on its token and entry alone.  The kernel streams 256 bytes of key per entry for
-// 16384 FLOP (64 FLOP per byte, far below the bf16 matrix-core ridge of ~314), so HBM
-// bandwidth bounds it.
+// The kernel streams 256 bytes of key per entry for 16384 FLOP (64 FLOP per byte, far below
+// the bf16 matrix-core ridge of ~314), so HBM bandwidth bounds it and the design is about
+// keeping bytes in flight:
+// * workgroup = (token, range of entries), 4 waves;
+// * the range's keys are contiguous, so they are moved with direct global->LDS loads: one
+//   wave instruction carries 1 KiB (4 key rows) into a ring of 64-entry tiles (16 KiB
+//   each), all but one slot in flight while the oldest tile is scored;
+// * each lane fetches the 16-byte chunk c ^ (row mod 16) of its row, an XOR swizzle that
+//   makes the MFMA operand reads (16 rows, same chunk) hit 16 distinct bank groups;
+// * per 16-entry block, S[head, entry] = qI kI^T with v_mfma_f32_16x16x32_bf16: the token's
+//   <= 64 indexer heads sit in registers as the A operand (4 blocks of 16), the keys are
+//   the B operand.  A lane then holds 16 heads of one entry and sums w_h * relu over them
+//   in a fixed order (head block, then row); two xor-shuffles across the lane groups finish
+//   the head sum, so a score depends on its token and entry only.
 
 #include "common.cuh"
 #include "kernels.h"
@@ -20,30 +25,68 @@ namespace csa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 ibf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float if32x4_t;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* gbl_void_ptr;
 
-constexpr int kIdxMTile = 512;  // entries per workgroup
+constexpr int kIT = 64;            // entries per tile
+constexpr int kIRow = 256;         // bytes per key row (128 bf16)
 
+// Wait until this wave's direct-to-LDS loads of a tile have landed: n later tiles (4
+// instructions each) may still be in flight.  Counting is conservative: stores issued
+// after those loads only make the wait longer.
+__device__ __forceinline__ void wait_tiles_in_flight(int n) {
+  if (n >= 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if (n == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int RING, int TILES>
 __global__ void __launch_bounds__(256) index_score_mfma_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
                                                                int n_I, RowsDev kI, int ratio,
                                                                float* __restrict__ score, int64_t score_stride,
-                                                               int n_tiles, int n_logical) {
-  // XCD-aware order: the tiles of one token share an XCD (its qI block stays in that L2).
-  const int per_xcd = gridDim.x / 8;
-  const int lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+                                                               int n_parts, int n_logical) {
+  static_assert(RING >= 2 && RING <= 4, "ring depth");
+  __shared__ __align__(16) uint8_t ring[RING][kIT * kIRow];
+  // Plain dispatch order: consecutive ranges of a token go to different XCDs, so unequal
+  // context lengths spread over the whole chip.
+  const int lid = blockIdx.x;
   if (lid >= n_logical) return;
-  const int t = lid / n_tiles;
-  const int tile = lid % n_tiles;
+  const int t = lid / n_parts;
+  const int part = lid % n_parts;
   const TokenCtx ctx = token_ctx(S, t);
   const int64_t V = (ctx.p + 1) / ratio;
-  const int64_t e0 = (int64_t)tile * kIdxMTile;
-  if (e0 >= V) return;
+  const int64_t e_begin = (int64_t)part * kIT * TILES;
+  if (e_begin >= V) return;
+  const int64_t left = V - e_begin;
+  const int n_tiles = (int)min((int64_t)TILES, (left + kIT - 1) / kIT);
 
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
+  const uint8_t* kbase = kI.data + ctx.entry0 * kI.stride;
 
-  // B operand: heads c16 + 16 hb, dims 8g + 32 kk .. +7
-  ibf16x8_t qb[4][4];
-  float wh[4];
+  // tile i -> ring slot i % RING; wave wv moves rows 16wv .. 16wv+15 (4 rows per instruction)
+  auto issue = [&](int i) {
+    const int64_t e_tile = e_begin + (int64_t)i * kIT;
+    uint8_t* slot = ring[i % RING];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * wv + 4 * q + (lane >> 4);
+      int64_t e = e_tile + r;
+      if (e >= V) e = V - 1;  // rows past the end re-read a valid row; their scores are not written
+      const int chunk = (lane & 15) ^ (r & 15);
+      const uint8_t* src = kbase + e * kI.stride + chunk * 16;
+      __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)(slot + (16 * wv + 4 * q) * kIRow), 16, 0, 0);
+    }
+  };
+
+  const int prologue = min(n_tiles, RING - 1);
+  for (int i = 0; i < prologue; ++i) issue(i);
+
+  // A operand: heads c16 + 16 hb, dims 8g + 32 kk .. +7 (requested after the key tiles).
+  // The result row of lane (g, j) is head 4g + j (+ 16 hb): its weight is kept per lane.
+  ibf16x8_t qa[4][4];
+  float wh[4][4];
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
     const int h = c16 + 16 * hb;
@@ -51,81 +94,63 @@ __global__ void __launch_bounds__(256) index_score_mfma_kernel(SeqsDev S, RowsDe
       const uint8_t* row = qI.data + ((int64_t)t * n_I + h) * qI.stride;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        qb[hb][kk] = __builtin_bit_cast(ibf16x8_t, *reinterpret_cast<const uint4*>(row + (8 * g + 32 * kk) * 2));
-      wh[hb] = w[(int64_t)t * n_I + h];
+        qa[hb][kk] = __builtin_bit_cast(ibf16x8_t, *reinterpret_cast<const uint4*>(row + (8 * g + 32 * kk) * 2));
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qb[hb][kk] = __builtin_bit_cast(ibf16x8_t, make_uint4(0u, 0u, 0u, 0u));
-      wh[hb] = 0.f;
+      for (int kk = 0; kk < 4; ++kk) qa[hb][kk] = __builtin_bit_cast(ibf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hr = 4 * g + j + 16 * hb;
+      wh[hb][j] = hr < n_I ? w[(int64_t)t * n_I + hr] : 0.f;
     }
   }
 
   float* srow = score + (int64_t)t * score_stride;
+  for (int i = 0; i < n_tiles; ++i) {
+    const int issued_after = min(n_tiles - 1, i + RING - 2) - i;
+    wait_tiles_in_flight(issued_after);
+    __syncthreads();  // tile i visible to all waves; slot (i-1) % RING free
+    if (i + RING - 1 < n_tiles) issue(i + RING - 1);
+
+    const uint8_t* rowp = ring[i % RING] + (16 * wv + c16) * kIRow;
+    if32x4_t acc[4];
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int64_t eb = e0 + 128 * wv + 64 * it;  // first entry of this group of 4 blocks
-    uint4 ka[4][4];
+    for (int hb = 0; hb < 4; ++hb) acc[hb] = if32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t e = eb + 16 * b + c16;
-      if (e < V) {
-        const uint8_t* row = kI.data + (ctx.entry0 + e) * kI.stride;
+    for (int kk = 0; kk < 4; ++kk) {
+      const ibf16x8_t b = *reinterpret_cast<const ibf16x8_t*>(rowp + (((g + 4 * kk) ^ c16) * 16));
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) ka[b][kk] = *reinterpret_cast<const uint4*>(row + (8 * g + 32 * kk) * 2);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) ka[b][kk] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int hb = 0; hb < 4; ++hb) acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hb][kk], b, acc[hb], 0, 0, 0);
     }
+    // acc[hb][j] = qI[head 4g+j+16hb] . kI[entry 16wv + c16 of the tile]
+    float s = 0.f;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if32x4_t acc[4];
+    for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb) acc[hb] = if32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const ibf16x8_t a = __builtin_bit_cast(ibf16x8_t, ka[b][kk]);
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[hb][kk], acc[hb], 0, 0, 0);
-      }
-      // acc[hb][j] = qI[head c16+16hb] . kI[entry 16b + 4g + j]
-      float part[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float s = 0.f;
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) s = __builtin_fmaf(wh[hb], fmaxf(acc[hb][j], 0.f), s);
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off, 64);
-        part[j] = s;
-      }
-      const int64_t e4 = eb + 16 * b + 4 * g;  // entries e4 .. e4+3
-      if (c16 == 0) {
-        if (e4 + 3 < V && ((reinterpret_cast<uintptr_t>(srow + e4) & 15) == 0)) {
-          *reinterpret_cast<float4*>(srow + e4) = make_float4(part[0], part[1], part[2], part[3]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (e4 + j < V) srow[e4 + j] = part[j];
-        }
-      }
-    }
+      for (int j = 0; j < 4; ++j) s = __builtin_fmaf(wh[hb][j], fmaxf(acc[hb][j], 0.f), s);
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    const int64_t e = e_begin + (int64_t)i * kIT + 16 * wv + c16;
+    if (g == 0 && e < V) srow[e] = s;
   }
 }
 
 bool index_mfma_supported(const RowsDev& qI, const RowsDev& kI, int n_I, int64_t score_stride) {
+  (void)score_stride;
   return qI.dtype == DT_BF16 && kI.dtype == DT_BF16 && kI.dim == 128 && n_I <= 64 && qI.stride % 16 == 0 &&
          kI.stride % 16 == 0;
 }
 
 hipError_t launch_index_score_mfma(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
                                    int ratio, float* score, int64_t score_stride, int max_vis, hipStream_t stream) {
-  const int n_tiles = (max_vis + kIdxMTile - 1) / kIdxMTile;
-  const int64_t n_log = (int64_t)S.total_q * n_tiles;
+  constexpr int kRing = 3, kTiles = 8;  // 48 KiB of LDS (3 workgroups per CU), 512 entries each
+  const int per_wg = kIT * kTiles;
+  const int n_parts = (max_vis + per_wg - 1) / per_wg;
+  const int64_t n_log = (int64_t)S.total_q * n_parts;
   if (n_log == 0) return hipSuccess;
-  const int64_t n_phys = (n_log + 7) / 8 * 8;
-  hipLaunchKernelGGL(index_score_mfma_kernel, dim3((unsigned)n_phys), dim3(256), 0, stream, S, qI, w, n_I, kI, ratio,
-                     score, score_stride, n_tiles, (int)n_log);
+  hipLaunchKernelGGL((index_score_mfma_kernel<kRing, kTiles>), dim3((unsigned)n_log), dim3(256), 0, stream, S, qI, w,
+                     n_I, kI, ratio, score, score_stride, n_parts, (int)n_log);
   return hipGetLastError();
 }
 

@@ -2,10 +2,12 @@
 // relevant compressed entries are selected, k = 1024 for V4-Pro and 512 for V4-Flash).
 //
 // One workgroup (1024 threads) per query token.  Scores are mapped to order-preserving
-// uint32 keys (-0 folded onto +0); a 4-pass, 8-bit radix select finds the k-th largest key
-// T and how many keys equal to T are still needed; a block-wide scan then keeps every key
-// > T and the lowest-index keys == T, writing indices in ascending order.  The selection is
-// a function of the token's scores alone.  Keys are staged in LDS when they fit (up to
+// uint32 keys (-0 folded onto +0); a 3-pass radix select (12, 12 and 8 bits; the wide
+// first digit spreads the few distinct float exponents of a score vector over many bins,
+// which keeps LDS-atomic contention low) finds the k-th largest key T and how many keys
+// equal to T are still needed; a block-wide scan then keeps every key > T and the
+// lowest-index keys == T, writing indices in ascending order.  The selection is a
+// function of the token's scores alone.  Keys are staged in LDS when they fit (up to
 // 32768 candidates, 128 KiB), otherwise every pass re-reads the scores from memory.
 
 #include "common.cuh"
@@ -51,50 +53,86 @@ __device__ __forceinline__ uint32_t key_at(const uint32_t* lds, const float* src
   return score_key(src[i]);
 }
 
+constexpr int kHistBins = 4096;
+
+struct TopkLds {
+  uint32_t hist[kHistBins];
+  uint32_t red[16];
+  uint32_t digit, above;
+};
+
 template <bool STAGED>
-__device__ void topk_select(const float* __restrict__ src, int n, int k, int32_t* __restrict__ out, uint32_t* lds) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t red[16];
-  __shared__ uint32_t s_digit, s_above;
+__device__ void topk_select(const float* __restrict__ src, int n, int k, int32_t* __restrict__ out, uint32_t* lds,
+                            TopkLds& sh) {
+  uint32_t* hist = sh.hist;
+  uint32_t* red = sh.red;
   const int tid = threadIdx.x;
   if (STAGED) {
-    for (int i = tid; i < n; i += kTopkThreads) lds[i] = score_key(src[i]);
+    // 8 loads in flight per thread before the LDS stores
+    for (int i0 = tid; i0 < n; i0 += 8 * kTopkThreads) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kTopkThreads;
+        v[u] = (i < n) ? src[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kTopkThreads;
+        if (i < n) lds[i] = score_key(v[u]);
+      }
+    }
   }
   uint32_t prefix = 0, mask = 0, remaining = (uint32_t)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
+  const int shifts[3] = {20, 8, 0};
+  const int widths[3] = {12, 12, 8};
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = shifts[pass];
+    const int nbins = 1 << widths[pass];
+    const uint32_t dmask = (uint32_t)nbins - 1u;
+    for (int b = tid; b < nbins; b += kTopkThreads) hist[b] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kTopkThreads) {
-      uint32_t key = key_at<STAGED>(lds, src, i);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      const uint32_t key = key_at<STAGED>(lds, src, i);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
     if (tid < 64) {
-      // lane l holds digits 4l..4l+3; suffix sums over lanes from the top digit down
-      uint32_t h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
-      uint32_t loc = h0 + h1 + h2 + h3;
+      // lane l owns digits [l*per, (l+1)*per); suffix sums over lanes from the top digit down
+      const int per = nbins / 64;
+      uint32_t loc = 0;
+      for (int d = 0; d < per; ++d) loc += hist[tid * per + d];
       uint32_t suf = loc;  // inclusive suffix sum over lanes >= tid
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        uint32_t y = __shfl_down(suf, off, 64);
+        const uint32_t y = __shfl_down(suf, off, 64);
         if (tid + off < 64) suf += y;
       }
-      uint32_t above = suf - loc;  // keys with digit > 4*tid+3
-      if (above < remaining && suf >= remaining) {
-        uint32_t d, acc = above;
-        if (acc + h3 >= remaining) d = 4 * tid + 3;
-        else if ((acc += h3) + h2 >= remaining) d = 4 * tid + 2;
-        else if ((acc += h2) + h1 >= remaining) d = 4 * tid + 1;
-        else { acc += h1; d = 4 * tid; }
-        s_digit = d;
-        s_above = acc;
+      const uint32_t above = suf - loc;  // keys with digit above this lane's range
+      const bool mine = above < remaining && suf >= remaining;
+      const uint64_t who = __ballot(mine);
+      const int L = __ffsll((unsigned long long)who) - 1;
+      const uint32_t above_L = __shfl(above, L, 64);
+      // the per (<= 64) digits of lane L, one per lane, suffix-summed again
+      const int dig = L * per + tid;
+      const uint32_t h = (tid < per) ? hist[dig] : 0u;
+      uint32_t suf2 = h;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_down(suf2, off, 64);
+        if (tid + off < 64) suf2 += y;
+      }
+      const uint32_t ab2 = above_L + suf2 - h;  // keys with digit > dig
+      if (tid < per && ab2 < remaining && ab2 + h >= remaining) {
+        sh.digit = (uint32_t)dig;
+        sh.above = ab2;
       }
     }
     __syncthreads();
-    prefix |= s_digit << shift;
-    mask |= 255u << shift;
-    remaining -= s_above;
+    prefix |= sh.digit << shift;
+    mask |= dmask << shift;
+    remaining -= sh.above;
     __syncthreads();
   }
   // prefix is the k-th largest key T; `remaining` keys equal to T are taken, lowest index first.
@@ -103,17 +141,17 @@ __device__ void topk_select(const float* __restrict__ src, int n, int k, int32_t
   const int i0 = min(n, tid * seg), i1 = min(n, i0 + seg);
   uint32_t gt = 0, eq = 0;
   for (int i = i0; i < i1; ++i) {
-    uint32_t key = key_at<STAGED>(lds, src, i);
+    const uint32_t key = key_at<STAGED>(lds, src, i);
     gt += key > T;
     eq += key == T;
   }
   uint32_t tot;
-  uint32_t gt_before = block_excl_scan(gt, red, &tot);
-  uint32_t eq_before = block_excl_scan(eq, red, &tot);
+  const uint32_t gt_before = block_excl_scan(gt, red, &tot);
+  const uint32_t eq_before = block_excl_scan(eq, red, &tot);
   uint32_t pos = gt_before + min(eq_before, remaining);
   uint32_t eq_rank = eq_before;
   for (int i = i0; i < i1; ++i) {
-    uint32_t key = key_at<STAGED>(lds, src, i);
+    const uint32_t key = key_at<STAGED>(lds, src, i);
     bool take = key > T;
     if (key == T) {
       take = eq_rank < remaining;
@@ -127,6 +165,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(SeqsDev S, const flo
                                                             int64_t score_stride, int ratio, int k,
                                                             int32_t* __restrict__ idx) {
   extern __shared__ uint32_t stage[];
+  __shared__ TopkLds sh;
   const int t = blockIdx.x;
   const TokenCtx ctx = token_ctx(S, t);
   const int64_t V = (ctx.p + 1) / ratio;
@@ -136,8 +175,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(SeqsDev S, const flo
     for (int i = threadIdx.x; i < k; i += kTopkThreads) out[i] = (i < V) ? i : -1;
     return;
   }
-  if (V <= kTopkStage) topk_select<true>(src, (int)V, k, out, stage);
-  else topk_select<false>(src, (int)V, k, out, stage);
+  if (V <= kTopkStage) topk_select<true>(src, (int)V, k, out, stage, sh);
+  else topk_select<false>(src, (int)V, k, out, stage, sh);
 }
 
 hipError_t launch_topk(const SeqsDev& S, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,

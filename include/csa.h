@@ -163,7 +163,8 @@ int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int
  *         bytes the key list of each token is processed by several workgroups in parallel;
  *         with less (or NULL) by one workgroup per token and head group.  Both give
  *         bit-identical results: each token's key list is cut into fixed chunks whose
- *         partial softmax states are folded in chunk order, starting from the sink. */
+ *         partial softmax states are folded in chunk order, starting from the sink.  The
+ *         workspace needs no initialisation; calls sharing one must be stream-ordered. */
 int csa_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows* kv, const int32_t* idx, int k,
                const csa_rows* tok, int n_win, const float* sink, float scale, int rope_dims, double rope_theta,
                const csa_rows* out, float* lse, void* ws, size_t ws_bytes, void* stream);

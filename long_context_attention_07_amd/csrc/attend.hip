@@ -104,12 +104,13 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a, float* _
     float o[kValuRegs];
 #pragma unroll
     for (int r = 0; r < kValuRegs; ++r) o[r] = 0.f;
-    for (int tile = 0; tile < chunk_slots / kValuTK; ++tile) {
+    const int64_t c_hi = min((int64_t)(cc + 1) * chunk_slots, n_slots);  // chunk end
+    for (int tile = 0;; ++tile) {
       const int64_t s0 = (int64_t)cc * chunk_slots + tile * kValuTK;
-      if (s0 >= n_slots) break;
+      if (s0 >= c_hi) break;
       if (tid < kValuTK) {
         const int64_t s = s0 + tid;
-        slots[tid] = (s < n_slots) ? resolve_slot(a, t, ctx, n_ent, s) : SlotRef{0, 0, 0};
+        slots[tid] = (s < c_hi) ? resolve_slot(a, t, ctx, n_ent, s) : SlotRef{0, 0, 0};
       }
       __syncthreads();
       for (int x = tid; x < kValuTK * half; x += 256) {

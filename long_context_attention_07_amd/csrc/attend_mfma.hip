@@ -15,14 +15,23 @@
 //   PV   O[head, dim] += P V: wave w owns dims 128w..128w+127; P is the A operand (LDS),
 //        V is read from the same row-major key tile with ds_read_b64_tr_b16, which hands
 //        each lane a column of 4 consecutive keys -- the B operand layout.
-// Chunk partials are folded in chunk order from the sink exactly as in the combine kernel
-// (attend_common.cuh), so split and single launches agree bit for bit, and a token's bits
-// never depend on the batch.  Window rows are rotated (RoPE at their own positions) as
+// Chunk partials are folded in chunk order from the sink; the combine kernel below (one
+// wave per head, 8 dims per lane) runs the same fold and finalisation arithmetic as the
+// single launch, so split and single launches agree bit for bit, and a token's bits never
+// depend on the batch.  The workgroup barriers wait for LDS instructions only: the next
+// tile's row loads stay in flight across them until the rows are staged.  Window rows are rotated (RoPE at their own positions) as
 // they are staged; absent slots are staged as zero rows and masked.
 
 #include "attend_common.cuh"
 
 namespace csa {
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
@@ -74,6 +83,25 @@ __device__ __forceinline__ uint4 rotate_chunk(uint4 v, int64_t pos, const FreqLd
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Final values of 8 consecutive output dims d0..d0+7 of one head (already normalised):
+// inverse RoPE of the pairs in the rotary range, rounded to bf16.  Shared by the single
+// launch and the combine kernel, so both produce the same bits.
+__device__ __forceinline__ uint4 finalize8(const float* x, int d0, int dn, int64_t p, const FreqLds& F) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float2 y = make_float2(x[2 * i], x[2 * i + 1]);
+    const int d = d0 + 2 * i;
+    if (d >= dn) {
+      float c, s;
+      rope_cs_mode<ROPE_FAST>(p, F, (d - dn) >> 1, &c, &s);
+      y = rotate2(y, c, -s);
+    }
+    w[i] = pack_bf16(y.x, y.y);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Slot resolution from the LDS copy of the token's idx (entries) or by arithmetic (HCA
 // entries, window positions), so no tile load waits on an idx load.
 __device__ __forceinline__ SlotRef resolve_slot_lds(const AttendArgs& a, const TokenCtx& ctx, int64_t n_ent,
@@ -111,6 +139,9 @@ __device__ __forceinline__ void load_tile(const AttendArgs& a, const TokenCtx& c
   st.pos0 = ctx.p - a.n_win + 1 + (s0 + 16 * w - n_ent);
   const int row_lo = (int)(uint32_t)(r.row & 0xffffffffu);
   const int row_hi = (int)(uint32_t)((uint64_t)r.row >> 32);
+  const uint8_t* kvp = a.kv.data;
+  const uint8_t* tokp = a.tok.data;
+  const int64_t kvs = a.kv.stride, toks = a.tok.stride;
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     if ((st.valid >> it) & 1u) {
@@ -118,8 +149,10 @@ __device__ __forceinline__ void load_tile(const AttendArgs& a, const TokenCtx& c
                                     (uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_lo, it));
       // the row address stays scalar (uniform row index, pool base and stride from the
       // kernel arguments): one SGPR base plus the lane offset per load
-      const RowsDev& R = ((st.win >> it) & 1u) ? a.tok : a.kv;
-      st.v[it] = reinterpret_cast<const uint4*>(R.data + row * R.stride)[lane];
+      const bool win = (st.win >> it) & 1u;
+      const uint8_t* base = win ? tokp : kvp;
+      const int64_t stride = win ? toks : kvs;
+      st.v[it] = reinterpret_cast<const uint4*>(base + row * stride)[lane];
     } else {
       st.v[it] = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -242,10 +275,10 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
   int cc = c_begin, tile = 0, ntile = tiles_in(cc);
 
   while (true) {
-    __syncthreads();  // previous tile fully consumed
+    lds_barrier();  // previous tile fully consumed
     store_tile(L, a, st, w, lane, F);
     const uint32_t valid = st.valid;
-    __syncthreads();  // tile visible
+    lds_barrier();  // tile visible
 
     int ncc = cc, ntl = tile + 1;
     if (ntl == ntile) {
@@ -273,7 +306,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     if (lane < 16) L.red_max[w][c16] = mx;
-    __syncthreads();
+    lds_barrier();
     const float tmax = fmaxf(fmaxf(L.red_max[0][c16], L.red_max[1][c16]), fmaxf(L.red_max[2][c16], L.red_max[3][c16]));
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = rescale(m_run, m_new);
@@ -292,7 +325,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
     ls += __shfl_xor(ls, 32, 64);
     if (lane < 16) L.red_sum[w][c16] = ls;
     if (w == 0 && lane < 16) L.alpha[c16] = alpha;
-    __syncthreads();
+    lds_barrier();
     const float tsum = ((L.red_sum[0][c16] + L.red_sum[1][c16]) + L.red_sum[2][c16]) + L.red_sum[3][c16];
     l_run = __builtin_fmaf(l_run, alpha, tsum);
     m_run = m_new;
@@ -383,10 +416,66 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
   }
 }
 
+// Fold of the chunk partials written by the split launch, in chunk order from the sink:
+// one wave per head, each lane 8 consecutive dims; same arithmetic as the single launch.
+__global__ void __launch_bounds__(256) attend_combine_mfma_kernel(AttendArgs a, const float* __restrict__ ws_o,
+                                                                  const float* __restrict__ ws_ml, int max_chunks,
+                                                                  int chunk_slots) {
+  __shared__ FreqLds F;
+  load_freqs(F, a.rope);
+  __syncthreads();
+  const int n_h4 = (a.n_h + 3) / 4;
+  const int t = blockIdx.x / n_h4;
+  const int h = (blockIdx.x % n_h4) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (h >= a.n_h) return;
+  const TokenCtx ctx = token_ctx(a.S, t);
+  const int n_chunks = token_chunks(a, ctx, chunk_slots);
+  const int d0 = 8 * lane;
+  FoldState f = fold_init(a.sink[h] * kLog2e);
+  float O[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) O[i] = 0.f;
+  const int64_t base0 = (int64_t)t * max_chunks * a.n_h + h;
+  float2 ml = n_chunks > 0 ? *reinterpret_cast<const float2*>(ws_ml + 2 * base0) : make_float2(0.f, 0.f);
+  float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
+  if (n_chunks > 0) {
+    o0 = *reinterpret_cast<const float4*>(ws_o + base0 * kDM + d0);
+    o1 = *reinterpret_cast<const float4*>(ws_o + base0 * kDM + d0 + 4);
+  }
+  for (int cc = 0; cc < n_chunks; ++cc) {
+    // next chunk's loads are in flight while this one is folded
+    float2 ml_n = ml;
+    float4 o0_n = o0, o1_n = o1;
+    if (cc + 1 < n_chunks) {
+      const int64_t b = base0 + (int64_t)(cc + 1) * a.n_h;
+      ml_n = *reinterpret_cast<const float2*>(ws_ml + 2 * b);
+      o0_n = *reinterpret_cast<const float4*>(ws_o + b * kDM + d0);
+      o1_n = *reinterpret_cast<const float4*>(ws_o + b * kDM + d0 + 4);
+    }
+    float fa, fb;
+    fold_step(f, ml.x, ml.y, &fa, &fb);
+    const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) O[i] = __builtin_fmaf(O[i], fa, o[i] * fb);
+    ml = ml_n;
+    o0 = o0_n;
+    o1 = o1_n;
+  }
+  const float inv = (f.Z > 0.f) ? 1.0f / f.Z : 0.f;
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = O[i] * inv;
+  const int dn = kDM - a.rope.dims;
+  *reinterpret_cast<uint4*>(a.out.data + ((int64_t)t * a.n_h + h) * a.out.stride + d0 * 2) =
+      finalize8(x, d0, dn, ctx.p, F);
+  if (a.lse && lane == 0) a.lse[(int64_t)t * a.n_h + h] = lse_natural(f);
+}
+
 bool attend_mfma_supported(const AttendArgs& a) {
   return (!a.csa || a.k <= kMaxIdx) && a.q.dim == kDM && a.q.dtype == DT_BF16 && a.kv.dtype == DT_BF16 && a.tok.dtype == DT_BF16 &&
          a.out.dtype == DT_BF16 && a.rope.dims % 8 == 0 && a.kv.stride % 16 == 0 && a.tok.stride % 16 == 0 &&
-         a.q.stride % 16 == 0;
+         a.q.stride % 16 == 0 && a.out.stride % 16 == 0;
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -405,9 +494,9 @@ hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hi
                        (int)mc, C, (int)n_log);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_hg8 = (a.n_h + 7) / 8;
-    hipLaunchKernelGGL(attend_combine_kernel<ROPE_FAST>, dim3((unsigned)(a.S.total_q * n_hg8)), dim3(256), 0, stream,
-                       a, ws_o, ws_ml, (int)mc, C);
+    const int n_h4 = (a.n_h + 3) / 4;
+    hipLaunchKernelGGL(attend_combine_mfma_kernel, dim3((unsigned)(a.S.total_q * n_h4)), dim3(256), 0, stream, a,
+                       ws_o, ws_ml, (int)mc, C);
   } else {
     const int64_t n_phys = (single + 7) / 8 * 8;
     hipLaunchKernelGGL(attend_mfma_kernel<false>, dim3((unsigned)n_phys), dim3(256), 0, stream, a, nullptr, nullptr,

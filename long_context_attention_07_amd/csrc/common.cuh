@@ -206,23 +206,6 @@ __device__ __forceinline__ float2 rope_pair(float2 x, int64_t pos, double inv_fr
 
 // ------------------------------------------------------------------------- ragged batch
 
-// Sequence owning query row t: the largest b with q_off[b] <= t.  The wavefront probes 64
-// evenly spaced offsets per round (q_off is non-decreasing, so the probes that are <= t
-// form a prefix of the ballot), shrinking the interval 64-fold per dependent load.
-__device__ __forceinline__ int seq_of_token(const SeqsDev& S, int t) {
-  const int lane = threadIdx.x & 63;
-  int lo = 0, hi = S.n_seqs;  // answer in [lo, hi)
-  while (hi - lo > 1) {
-    const int step = (hi - lo + 63) >> 6;
-    const int b = lo + lane * step;
-    const bool ok = b < hi && S.q_off[b] <= t;
-    const int cnt = __popcll(__ballot(ok));  // >= 1: q_off[lo] <= t
-    lo = lo + (cnt - 1) * step;
-    hi = min(hi, lo + step);
-  }
-  return lo;
-}
-
 struct TokenCtx {
   int b;
   int64_t p;        // position of the query token
@@ -231,14 +214,47 @@ struct TokenCtx {
   int64_t tok_lo;
 };
 
+__device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v & 0xffffffffu), lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), lane);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Context of query row t (called by all 64 lanes of a wave).  Its sequence is the largest
+// b with q_off[b] <= t (q_off is non-decreasing, so the probes that are <= t form a prefix
+// of a ballot).  While more than 64 candidates remain, the wave probes 64 evenly spaced
+// offsets per round, shrinking the interval 64-fold per dependent load.  In the final
+// round each lane probes one candidate and loads all of its fields at once, so they arrive
+// together with the probe and are read from the winning lane: with up to 64 sequences the
+// whole lookup is one round of loads.
 __device__ __forceinline__ TokenCtx token_ctx(const SeqsDev& S, int t) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = S.n_seqs;  // answer in [lo, hi)
+  while (hi - lo > 64) {
+    const int step = (hi - lo + 63) >> 6;
+    const int b = lo + lane * step;
+    const bool ok = b < hi && S.q_off[b] <= t;
+    const int cnt = __popcll(__ballot(ok));  // >= 1: q_off[lo] <= t
+    lo = lo + (cnt - 1) * step;
+    hi = min(hi, lo + step);
+  }
+  const int b = lo + lane;
+  const bool in = b < hi;
+  const int bc = in ? b : lo;
+  const int q0 = S.q_off[bc];
+  const int q1 = S.q_off[bc + 1];
+  const int cl = S.ctx_len[bc];
+  const int64_t e0 = S.entry_off[bc];
+  const int64_t t0 = S.tok_off[bc];
+  const int tl = S.tok_lo[bc];
+  const int win = __popcll(__ballot(in && q0 <= t)) - 1;  // >= 0: q_off[lo] <= t
   TokenCtx c;
-  c.b = seq_of_token(S, t);
-  int q0 = S.q_off[c.b], q1 = S.q_off[c.b + 1];
-  c.p = (int64_t)S.ctx_len[c.b] - (q1 - q0) + (t - q0);
-  c.entry0 = S.entry_off[c.b];
-  c.tok0 = S.tok_off[c.b];
-  c.tok_lo = S.tok_lo[c.b];
+  c.b = lo + win;
+  const int wq0 = __builtin_amdgcn_readlane(q0, win), wq1 = __builtin_amdgcn_readlane(q1, win);
+  c.p = (int64_t)__builtin_amdgcn_readlane(cl, win) - (wq1 - wq0) + (t - wq0);
+  c.entry0 = readlane64(e0, win);
+  c.tok0 = readlane64(t0, win);
+  c.tok_lo = __builtin_amdgcn_readlane(tl, win);
   return c;
 }
 

@@ -43,6 +43,7 @@ struct AttendArgs {
 int attend_chunk_slots(const AttendArgs& a);
 // Number of chunks of the longest key list the launch can see (grid / workspace sizing).
 int64_t attend_max_chunks(const AttendArgs& a);
+// Workspace: the chunk partials, o of every (token, chunk, head) then its (m, l), float32.
 size_t attend_workspace_bytes(const AttendArgs& a);
 hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -46,34 +46,19 @@ class DecodeLayer:
     def __init__(self, wl, lens, seed, dev):
         self.wl = wl
         n, D, ratio = wl.n_seqs, wl.d_c, wl.ratio
-        hist = wl.n_win + 2 * ratio
-        self.lens = lens
-        self.E = [L // ratio for L in lens]
-        self.entry_off = np.concatenate([[0], np.cumsum(self.E)[:-1]]).tolist()
-        self.tok_lo = [max(0, L - 1 - hist) for L in lens]
-        rows = [L - lo for L, lo in zip(lens, self.tok_lo)]
-        self.tok_off = np.concatenate([[0], np.cumsum(rows)[:-1]]).tolist()
-        n_ent, n_tok = int(sum(self.E)), int(sum(rows))
-        s = lambda tag: synth.sub_seed(seed, tag)  # noqa: E731
-        bf = torch.bfloat16
+        x = synth.decode_inputs(wl, lens, seed, dev)
+        self.lens, self.E = x["lens"], x["E"]
+        self.entry_off, self.tok_off, self.tok_lo = x["entry_off"], x["tok_off"], x["tok_lo"]
         self.seqs = ops.Seqs([1] * n, lens, self.entry_off, self.tok_off, self.tok_lo, device=dev)
-        self.kv = synth.device_normal((n_ent, D), s(1), dev).to(bf)
-        self.c = synth.device_normal((n_tok, D), s(2), dev).to(bf)
-        self.z = synth.device_normal((n_tok, D), s(3), dev).to(bf)
-        self.bias = synth.device_normal(((1 + wl.overlap) * ratio, D), s(4), dev, 1 / math.sqrt(D))
-        self.q = synth.device_normal((n * wl.n_h, D), s(5), dev).to(bf)
-        self.sink = synth.device_normal((wl.n_h,), s(6), dev)
+        for key in ("kv", "c", "z", "bias", "q", "sink"):
+            setattr(self, key, x[key])
+        bf = torch.bfloat16
         self.out = torch.empty((n * wl.n_h, D), dtype=bf, device=dev)
         self.lse = torch.empty((n, wl.n_h), dtype=torch.float32, device=dev)
         self.csa = wl.kind == "csa_decode"
         if self.csa:
-            dI = wl.d_I
-            self.kI = synth.device_normal((n_ent, dI), s(7), dev).to(bf)
-            self.cI = synth.device_normal((n_tok, dI), s(8), dev).to(bf)
-            self.zI = synth.device_normal((n_tok, dI), s(9), dev).to(bf)
-            self.biasI = synth.device_normal(((1 + wl.overlap) * ratio, dI), s(10), dev, 1 / math.sqrt(dI))
-            self.qI = synth.device_normal((n * wl.n_I, dI), s(11), dev).to(bf)
-            self.w = synth.device_normal((n, wl.n_I), s(12), dev, 1 / math.sqrt(wl.n_I))
+            for key in ("kI", "cI", "zI", "biasI", "qI", "w"):
+                setattr(self, key, x[key])
             self.idx = torch.empty((n, wl.k), dtype=torch.int32, device=dev)
             ws_i = ops.csa_workspace_bytes(ops.OP_INDEX_TOPK, self.seqs, k=wl.k, ratio=ratio)
             ws_a = ops.csa_workspace_bytes(ops.OP_CSA_ATTEND, self.seqs, wl.n_h, D, wl.k, ratio, wl.n_win)

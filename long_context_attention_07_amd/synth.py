@@ -77,3 +77,53 @@ def device_normal(shape, seed, device, std=1.0):
 def sub_seed(seed, tag):
     """Deterministic per-tensor seed: workload seed and a small tensor tag."""
     return (int(seed) * 1000003 + int(tag) * 7919) & 0x7FFFFFFF
+
+
+def decode_inputs(wl, lens, seed, device, n_q=None):
+    """Pools and per-step inputs of a decode batch (one or a few new tokens per sequence),
+    drawn on `device`.  Random draws and offsets only.
+
+    lens[b] is the context length L_b including the n_q[b] new tokens (default 1 each).
+    Entry pools hold floor(L_b / ratio) rows per sequence (the rows of entries the new
+    tokens complete are what the compress step rewrites); token pools hold the positions
+    [tok_lo_b, L_b) with tok_lo_b = max(0, L_b - n_q[b] - n_win - 2 * ratio), enough for the
+    window and for the sources of the new entries.  Every tensor has its own seed
+    sub_seed(seed, tag): kv 1, c 2, z 3, bias 4 (std 1/sqrt(d_c)), q 5, sink 6, and for
+    CSA kI 7, cI 8, zI 9, biasI 10 (std 1/sqrt(d_I)), qI 11, w 12 (std 1/sqrt(n_I)); all
+    N(0,1) unless noted, drawn in float32 and rounded to bf16 where stored as bf16.
+    Returns a dict of tensors plus the offsets (lists) and sizes.
+    """
+    import torch
+    n = len(lens)
+    n_q = [1] * n if n_q is None else [int(x) for x in n_q]
+    D, ratio = wl.d_c, wl.ratio
+    hist = wl.n_win + 2 * ratio
+    E = [int(L) // ratio for L in lens]
+    entry_off = [0] * n
+    for b in range(1, n):
+        entry_off[b] = entry_off[b - 1] + E[b - 1]
+    tok_lo = [max(0, int(L) - q - hist) for L, q in zip(lens, n_q)]
+    rows = [int(L) - lo for L, lo in zip(lens, tok_lo)]
+    tok_off = [0] * n
+    for b in range(1, n):
+        tok_off[b] = tok_off[b - 1] + rows[b - 1]
+    n_ent, n_tok, n_tokens = int(sum(E)), int(sum(rows)), int(sum(n_q))
+    s = lambda tag: sub_seed(seed, tag)  # noqa: E731
+    bf = torch.bfloat16
+    x = dict(lens=[int(L) for L in lens], n_q=n_q, E=E, entry_off=entry_off, tok_off=tok_off, tok_lo=tok_lo,
+             n_ent=n_ent, n_tok=n_tok, n_tokens=n_tokens)
+    x["kv"] = device_normal((max(n_ent, 1), D), s(1), device).to(bf)
+    x["c"] = device_normal((n_tok, D), s(2), device).to(bf)
+    x["z"] = device_normal((n_tok, D), s(3), device).to(bf)
+    x["bias"] = device_normal(((1 + wl.overlap) * ratio, D), s(4), device, 1 / math.sqrt(D))
+    x["q"] = device_normal((n_tokens * wl.n_h, D), s(5), device).to(bf)
+    x["sink"] = device_normal((wl.n_h,), s(6), device)
+    if wl.kind in ("csa_decode", "stress") and ratio == 4:
+        dI = wl.d_I
+        x["kI"] = device_normal((max(n_ent, 1), dI), s(7), device).to(bf)
+        x["cI"] = device_normal((n_tok, dI), s(8), device).to(bf)
+        x["zI"] = device_normal((n_tok, dI), s(9), device).to(bf)
+        x["biasI"] = device_normal(((1 + wl.overlap) * ratio, dI), s(10), device, 1 / math.sqrt(dI))
+        x["qI"] = device_normal((n_tokens * wl.n_I, dI), s(11), device).to(bf)
+        x["w"] = device_normal((n_tokens, wl.n_I), s(12), device, 1 / math.sqrt(wl.n_I))
+    return x

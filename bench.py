@@ -34,6 +34,11 @@ METRIC = "CSA/HCA decode tokens/s at 64K–1M ctx; achieved HBM GB/s and MFMA % 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 N_SETS = 8
+# kernels each operation launches (substrings of the kernel names in profiler output)
+OP_KERNELS = {"compress": ["compress_kernel"], "index_score": ["index_score_mfma_kernel"],
+              "topk": ["topk_kernel"], "attend": ["attend_mfma_kernel", "attend_combine_mfma_kernel"]}
+CALIB_BYTES = 256 << 20  # plain device copy used to calibrate the HBM byte counters
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(msg):
@@ -212,6 +217,94 @@ def cpu_baseline(layer, budget_s=12.0):
                       f"BLAS threads as configured, {cores} cores visible)"}
 
 
+def source_digest():
+    """sha256 of the library sources: traffic figures are used only for the kernels they were
+    measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "long_context_attention_07_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".hip", ".cuh", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(f.read())
+    with open(os.path.join(ROOT, "include", "csa.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profile_run(layers, stream, reps):
+    """Eager launches for the counter runs: each operation `reps` times per layer set, then
+    a plain device copy of CALIB_BYTES (four times) to calibrate the byte counters."""
+    for name in OP_KERNELS:
+        if not hasattr(layers[0], name) or (name in ("index_score", "topk") and not layers[0].csa):
+            continue
+        for _ in range(reps):
+            for L_ in layers:
+                getattr(L_, name)()
+        stream.synchronize()
+    a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=layers[0].q.device)
+    b = torch.empty_like(a)
+    for _ in range(4):
+        b.copy_(a)
+    stream.synchronize()
+
+
+def traffic_from_counters(fetch_dir, write_dir, workload, out_path):
+    """HBM bytes per launch of each operation from two rocprofv3 --pmc runs of
+    `bench.py --profile-run` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter
+    is scaled by the factor that maps its reading for the calibration copy onto the copy's
+    known bytes."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+
+    def copy_kib(vals):
+        big = [v for k, vs in vals.items() if "copy" in k.lower() for v in vs if v > CALIB_BYTES / 1024 / 8]
+        return float(np.median(big)) if big else None
+
+    cf, cw = copy_kib(fetch), copy_kib(write)
+    f_fetch = CALIB_BYTES / 1024 / cf if cf else 1.0
+    f_write = CALIB_BYTES / 1024 / cw if cw else 1.0
+    res = {"workload": workload, "source": source_digest(), "calibration": {
+        "copy_bytes": CALIB_BYTES, "fetch_kib": cf, "write_kib": cw, "fetch_factor": round(f_fetch, 4),
+        "write_factor": round(f_write, 4)}, "ops": {}}
+    for op, subs in OP_KERNELS.items():
+        tot, kern = 0.0, {}
+        for sub in subs:
+            fk = [v for k, vs in fetch.items() if sub in k for v in vs]
+            wk = [v for k, vs in write.items() if sub in k for v in vs]
+            if not fk or not wk:
+                continue
+            fb, wb = float(np.mean(fk)) * 1024 * f_fetch, float(np.mean(wk)) * 1024 * f_write
+            kern[sub] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": len(fk)}
+            tot += fb + wb
+        if kern:
+            res["ops"][op] = {"bytes_per_launch": round(tot), "kernels": kern}
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res, indent=1))
+
+
+def load_traffic(wl):
+    path = os.path.join(PROFILES, f"traffic_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    return t if t.get("source") == source_digest() else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,7 +314,16 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--sets", type=int, default=N_SETS)
+    ap.add_argument("--profile-run", type=int, default=0, metavar="REPS",
+                    help="only launch each operation REPS times per layer set (for rocprofv3), then exit")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs of --profile-run into profiles/traffic_<workload>.json")
     args = ap.parse_args()
+    if args.traffic:
+        wl = configs.CSA_DECODE_BF16 if args.workload == "csa_decode" else configs.HCA_DECODE_1M_BF16
+        traffic_from_counters(args.traffic[0], args.traffic[1], wl.name,
+                              os.path.join(PROFILES, f"traffic_{wl.name}.json"))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path shards by sequence "
               f"with no exchange, so N GPUs run N independent copies of this benchmark.", file=sys.stderr)
@@ -237,6 +339,12 @@ def main():
         layers = [DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100 + i), dev) for i in range(args.sets)]
         torch.cuda.synchronize()
         log(f"allocated {torch.cuda.memory_allocated() / 2**30:.2f} GiB for {args.sets} layer sets")
+        if args.profile_run:
+            for L_ in layers:
+                L_.step()
+            profile_run(layers, stream, args.profile_run)
+            log("profile run done")
+            return
         # eager warm-up, then capture one graph per layer set
         for i in range(max(args.warmup, len(layers))):
             layers[i % len(layers)].step()
@@ -285,8 +393,11 @@ def main():
         dom = max(op_ms, key=op_ms.get)
         db, df = work[dom]
         dt = op_ms[dom] * 1e-3
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(db / dt / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(db / dt / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+        traffic = load_traffic(wl)
+        t_op = traffic["ops"].get(dom) if traffic else None
+        roof = {"kernel": dom, "kernels": OP_KERNELS[dom], "bound": "hbm", "achieved": round(db / dt / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(db / dt / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": t_op["bytes_per_launch"] if t_op else None,
                 "bytes_per_launch": int(db), "avg_launch_us": round(op_ms[dom] * 1e3, 2)}
         step_bytes = sum(b for b, _ in work.values())
         step_flops = sum(f for _, f in work.values())

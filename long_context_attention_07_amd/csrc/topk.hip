@@ -5,7 +5,8 @@
 // uint32 keys (-0 folded onto +0); a 3-pass radix select (12, 12 and 8 bits; the wide
 // first digit spreads the few distinct float exponents of a score vector over many bins,
 // which keeps LDS-atomic contention low) finds the k-th largest key T and how many keys
-// equal to T are still needed; a block-wide scan then keeps every key > T and the
+// equal to T are still needed (each digit found by a workgroup-wide scan of the digit
+// counts); a block-wide scan then keeps every key > T and the
 // lowest-index keys == T, writing indices in ascending order.  The selection is a
 // function of the token's scores alone.  Keys are staged in LDS when they fit (up to
 // 32768 candidates, 128 KiB), otherwise every pass re-reads the scores from memory.
@@ -24,27 +25,38 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive prefix sum over the 1024 threads; `red` needs 16 words.  Returns the
-// exclusive prefix and writes the total.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t* total) {
+// Exclusive prefix sums over the 1024 threads of two counters at once; `red` needs 32
+// words.  Returns the exclusive prefixes and writes the totals.
+__device__ __forceinline__ uint2 block_excl_scan2(uint2 v, uint32_t* red, uint2* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint32_t x = v;
+  uint2 x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    uint32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
+    const uint32_t yx = __shfl_up(x.x, off, 64), yy = __shfl_up(x.y, off, 64);
+    if (lane >= off) {
+      x.x += yx;
+      x.y += yy;
+    }
   }
-  if (lane == 63) red[wv] = x;
+  if (lane == 63) {
+    red[wv] = x.x;
+    red[16 + wv] = x.y;
+  }
   __syncthreads();
-  uint32_t base = 0, tot = 0;
+  uint2 base = make_uint2(0u, 0u), tot = make_uint2(0u, 0u);
+#pragma unroll
   for (int i = 0; i < kTopkThreads / 64; ++i) {
-    uint32_t r = red[i];
-    if (i < wv) base += r;
-    tot += r;
+    const uint32_t rx = red[i], ry = red[16 + i];
+    if (i < wv) {
+      base.x += rx;
+      base.y += ry;
+    }
+    tot.x += rx;
+    tot.y += ry;
   }
   __syncthreads();
   *total = tot;
-  return base + x - v;
+  return make_uint2(base.x + x.x - v.x, base.y + x.y - v.y);
 }
 
 template <bool STAGED>
@@ -54,10 +66,12 @@ __device__ __forceinline__ uint32_t key_at(const uint32_t* lds, const float* src
 }
 
 constexpr int kHistBins = 4096;
+static_assert((kTopkStage / kTopkThreads) * (kTopkThreads / 64) <= 512 && 1024 <= kHistBins,
+              "per-(chunk, wave) counts of the staged compaction fit in the histogram");
 
 struct TopkLds {
   uint32_t hist[kHistBins];
-  uint32_t red[16];
+  uint32_t red[32];
   uint32_t digit, above;
 };
 
@@ -98,35 +112,29 @@ __device__ void topk_select(const float* __restrict__ src, int n, int k, int32_t
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
-    if (tid < 64) {
-      // lane l owns digits [l*per, (l+1)*per); suffix sums over lanes from the top digit down
-      const int per = nbins / 64;
+    {
+      // digit search over the whole workgroup: thread tid owns `per` consecutive digits,
+      // counted from the top digit down, so an exclusive scan over threads gives the number
+      // of keys above each thread's digits
+      const int per = nbins >= kTopkThreads ? nbins / kTopkThreads : 1;
+      const int owners = nbins / per;
+      const int d_hi = nbins - tid * per;  // digits [d_hi - per, d_hi)
       uint32_t loc = 0;
-      for (int d = 0; d < per; ++d) loc += hist[tid * per + d];
-      uint32_t suf = loc;  // inclusive suffix sum over lanes >= tid
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_down(suf, off, 64);
-        if (tid + off < 64) suf += y;
-      }
-      const uint32_t above = suf - loc;  // keys with digit above this lane's range
-      const bool mine = above < remaining && suf >= remaining;
-      const uint64_t who = __ballot(mine);
-      const int L = __ffsll((unsigned long long)who) - 1;
-      const uint32_t above_L = __shfl(above, L, 64);
-      // the per (<= 64) digits of lane L, one per lane, suffix-summed again
-      const int dig = L * per + tid;
-      const uint32_t h = (tid < per) ? hist[dig] : 0u;
-      uint32_t suf2 = h;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_down(suf2, off, 64);
-        if (tid + off < 64) suf2 += y;
-      }
-      const uint32_t ab2 = above_L + suf2 - h;  // keys with digit > dig
-      if (tid < per && ab2 < remaining && ab2 + h >= remaining) {
-        sh.digit = (uint32_t)dig;
-        sh.above = ab2;
+      if (tid < owners)
+        for (int d = 0; d < per; ++d) loc += hist[d_hi - 1 - d];
+      uint2 tot;
+      const uint32_t above = block_excl_scan2(make_uint2(loc, 0u), red, &tot).x;
+      if (tid < owners && above < remaining && above + loc >= remaining) {
+        uint32_t ab = above;
+        for (int d = 0; d < per; ++d) {
+          const uint32_t h = hist[d_hi - 1 - d];
+          if (ab + h >= remaining) {
+            sh.digit = (uint32_t)(d_hi - 1 - d);
+            sh.above = ab;
+            break;
+          }
+          ab += h;
+        }
       }
     }
     __syncthreads();
@@ -137,6 +145,52 @@ __device__ void topk_select(const float* __restrict__ src, int n, int k, int32_t
   }
   // prefix is the k-th largest key T; `remaining` keys equal to T are taken, lowest index first.
   const uint32_t T = prefix;
+  if (STAGED) {
+    // Keys staged in LDS (n <= 32768, at most 32 chunks of 1024): thread tid handles index
+    // 1024j + tid of chunk j (conflict-free LDS reads).  Per (chunk, wave) the counts of keys
+    // > T and == T are ballot popcounts; one scan over the (chunk, wave) counts in index
+    // order then gives every kept key its output slot.
+    const int lane = tid & 63, wv = tid >> 6;
+    const int n_chunks = (n + kTopkThreads - 1) / kTopkThreads;
+    uint32_t* cg = sh.hist;         // [chunk * 16 + wave], reused: the passes are done
+    uint32_t* ce = sh.hist + 512;
+    for (int j = 0; j < n_chunks; ++j) {
+      const int i = j * kTopkThreads + tid;
+      const uint32_t key = i < n ? lds[i] : 0u;
+      const uint64_t mg = __ballot(i < n && key > T);
+      const uint64_t me = __ballot(i < n && key == T);
+      if (lane == 0) {
+        cg[j * 16 + wv] = (uint32_t)__popcll(mg);
+        ce[j * 16 + wv] = (uint32_t)__popcll(me);
+      }
+    }
+    for (int x = n_chunks * 16 + tid; x < 512; x += kTopkThreads) {
+      cg[x] = 0u;
+      ce[x] = 0u;
+    }
+    __syncthreads();
+    uint2 tot;
+    const uint2 v = tid < 512 ? make_uint2(cg[tid], ce[tid]) : make_uint2(0u, 0u);
+    const uint2 ex = block_excl_scan2(v, red, &tot);
+    if (tid < 512) {
+      cg[tid] = ex.x;
+      ce[tid] = ex.y;
+    }
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int j = 0; j < n_chunks; ++j) {
+      const int i = j * kTopkThreads + tid;
+      const uint32_t key = i < n ? lds[i] : 0u;
+      const bool g = i < n && key > T, e = i < n && key == T;
+      const uint64_t mg = __ballot(g), me = __ballot(e);
+      const uint32_t gt_before = cg[j * 16 + wv] + (uint32_t)__popcll(mg & below);
+      const uint32_t eq_before = ce[j * 16 + wv] + (uint32_t)__popcll(me & below);
+      if (g) out[gt_before + min(eq_before, remaining)] = i;
+      else if (e && eq_before < remaining) out[gt_before + eq_before] = i;
+    }
+    return;
+  }
+  // scores read from memory: contiguous segments per thread
   const int seg = (n + kTopkThreads - 1) / kTopkThreads;
   const int i0 = min(n, tid * seg), i1 = min(n, i0 + seg);
   uint32_t gt = 0, eq = 0;
@@ -145,9 +199,9 @@ __device__ void topk_select(const float* __restrict__ src, int n, int k, int32_t
     gt += key > T;
     eq += key == T;
   }
-  uint32_t tot;
-  const uint32_t gt_before = block_excl_scan(gt, red, &tot);
-  const uint32_t eq_before = block_excl_scan(eq, red, &tot);
+  uint2 tot;
+  const uint2 before = block_excl_scan2(make_uint2(gt, eq), red, &tot);
+  const uint32_t gt_before = before.x, eq_before = before.y;
   uint32_t pos = gt_before + min(eq_before, remaining);
   uint32_t eq_rank = eq_before;
   for (int i = i0; i < i1; ++i) {

@@ -11,7 +11,8 @@ overlapped compression, a 64-head x 128-dim indexer, k = 512, window 128, bf16.
 
 Inputs are synthetic, seeded and resident in HBM before timing.  Eight independent layer
 sets (about 2.3 GB) are rotated step by step so that no set stays in the 256 MB
-Infinity Cache; each step is a captured HIP graph replayed on the current stream.
+Infinity Cache; the steps of the eight sets are captured in one HIP graph replayed on the
+launch stream.
 Prints one JSON line.
 """
 
@@ -35,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 N_SETS = 8
 # kernels each operation launches (substrings of the kernel names in profiler output)
-OP_KERNELS = {"compress": ["compress_kernel"], "index_score": ["index_score_mfma_kernel"],
+OP_KERNELS = {"compress": ["compress2_kernel", "compress_kernel"], "index_score": ["index_score_mfma_kernel"],
               "topk": ["topk_kernel"], "attend": ["attend_mfma_kernel", "attend_combine_mfma_kernel"]}
 CALIB_BYTES = 256 << 20  # plain device copy used to calibrate the HBM byte counters
 PROFILES = os.path.join(ROOT, "profiles")
@@ -78,12 +79,15 @@ class DecodeLayer:
 
     # -- the step's operations
     def compress(self):
+        """KV rows (and, for CSA, the indexer keys in the same launch)."""
         wl = self.wl
-        ops.csa_compress(self.seqs, self.R["c"], self.R["z"], self.bias, wl.ratio, wl.overlap, wl.rope_dims,
-                         wl.rope_theta, self.R["kv"])
         if self.csa:
-            ops.csa_compress(self.seqs, self.R["cI"], self.R["zI"], self.biasI, wl.ratio, wl.overlap, 0,
-                             wl.rope_theta, self.R["kI"])
+            ops.csa_compress2(self.seqs, wl.ratio, wl.overlap, wl.rope_theta,
+                              (self.R["c"], self.R["z"], self.bias, wl.rope_dims, self.R["kv"]),
+                              (self.R["cI"], self.R["zI"], self.biasI, 0, self.R["kI"]))
+        else:
+            ops.csa_compress(self.seqs, self.R["c"], self.R["z"], self.bias, wl.ratio, wl.overlap, wl.rope_dims,
+                             wl.rope_theta, self.R["kv"])
 
     def index_score(self):
         score = self.ws[: self.wl.n_seqs * self.ws_score_stride].view(self.wl.n_seqs, self.ws_score_stride)
@@ -345,20 +349,26 @@ def main():
             profile_run(layers, stream, args.profile_run)
             log("profile run done")
             return
-        # eager warm-up, then capture one graph per layer set
+        # eager warm-up, then capture the steps of all layer sets in one graph (one launch per
+        # round of layer sets, as a model's forward pass would be captured) and one graph
+        # per set for a remainder of steps
         for i in range(max(args.warmup, len(layers))):
             layers[i % len(layers)].step()
         torch.cuda.synchronize()
-        graphs = []
+        g_all, graphs = None, []
         if not args.no_graph:
+            g_all = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_all, stream=stream):
+                for L_ in layers:
+                    L_.step()
             for L_ in layers:
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
                     L_.step()
                 graphs.append(g)
             torch.cuda.synchronize()
-            for i in range(args.warmup):
-                graphs[i % len(graphs)].replay()
+            for i in range(max(1, args.warmup // len(layers))):
+                g_all.replay()
         torch.cuda.synchronize()
 
         # timed region: exactly K steps
@@ -366,10 +376,13 @@ def main():
         torch.cuda.synchronize()
         t_wall = time.perf_counter()
         e0.record(stream)
-        for i in range(args.steps):
-            if graphs:
-                graphs[i % len(graphs)].replay()
-            else:
+        if g_all is not None:
+            for _ in range(args.steps // len(layers)):
+                g_all.replay()
+            for i in range(args.steps % len(layers)):
+                graphs[i].replay()
+        else:
+            for i in range(args.steps):
                 layers[i % len(layers)].step()
         e1.record(stream)
         torch.cuda.synchronize()

@@ -112,6 +112,16 @@ typedef struct {
 int csa_compress(const csa_seqs* seqs, const csa_rows* c, const csa_rows* z, const float* bias, int ratio,
                  int overlap, int rope_dims, double rope_theta, const csa_rows* entries, void* stream);
 
+/* csa_compress2 -- two compressions of one ragged batch in a single launch: the KV rows and
+ * the indexer keys of a CSA layer, which share the sequences, ratio and overlap (section 2.1:
+ * the indexer scores compressed entries; Figure 2 feeds both from the same tokens).  Job j
+ * is exactly csa_compress(seqs, c_j, z_j, bias_j, ratio, overlap, rope_dims_j, rope_theta,
+ * entries_j) and writes the same bytes; arguments and errors as there (checked for both
+ * jobs before anything is launched). */
+int csa_compress2(const csa_seqs* seqs, int ratio, int overlap, double rope_theta, const csa_rows* c0,
+                  const csa_rows* z0, const float* bias0, int rope_dims0, const csa_rows* entries0, const csa_rows* c1,
+                  const csa_rows* z1, const float* bias1, int rope_dims1, const csa_rows* entries1, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * csa_index_score -- Lightning-Indexer scores (section 2.1: DSA's lightweight indexer
  * chooses the top-k compressed entries; Figure 2 "Lightning Indexer FP4 Precision";

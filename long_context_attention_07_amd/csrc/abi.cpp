@@ -196,10 +196,9 @@ const char* csa_strerror(int status) {
 
 const char* csa_last_error(void) { return g_err; }
 
-int csa_compress(const csa_seqs* seqs, const csa_rows* c, const csa_rows* z, const float* bias, int ratio, int overlap,
-                 int rope_dims, double rope_theta, const csa_rows* entries, void* stream) {
+static int compress_checks(const csa_rows* c, const csa_rows* z, const float* bias, const csa_rows* entries,
+                           int ratio, int overlap, int rope_dims, double rope_theta, csa::RopeTab* rope) {
   int st;
-  if ((st = check_seqs(seqs))) return st;
   if ((st = check_rows(c, "c", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_KV_SPLIT)))) return st;
   if ((st = check_rows(z, "z", bit(CSA_F32) | bit(CSA_BF16)))) return st;
   if ((st = check_rows(entries, "entries", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_KV_SPLIT) | bit(CSA_MXFP4))))
@@ -209,12 +208,34 @@ int csa_compress(const csa_seqs* seqs, const csa_rows* c, const csa_rows* z, con
   if (!bias) return fail(CSA_EINVAL, "bias: null pointer");
   if (ratio < 1 || ratio > 128) return fail(CSA_EINVAL, "ratio %d out of [1, 128]", ratio);
   if (overlap != 0 && overlap != 1) return fail(CSA_EINVAL, "overlap must be 0 or 1 (got %d)", overlap);
+  return make_rope(rope_dims, rope_theta, c->dim, rope);
+}
+
+int csa_compress(const csa_seqs* seqs, const csa_rows* c, const csa_rows* z, const float* bias, int ratio, int overlap,
+                 int rope_dims, double rope_theta, const csa_rows* entries, void* stream) {
+  int st;
+  if ((st = check_seqs(seqs))) return st;
   csa::RopeTab rope;
-  if ((st = make_rope(rope_dims, rope_theta, c->dim, &rope))) return st;
+  if ((st = compress_checks(c, z, bias, entries, ratio, overlap, rope_dims, rope_theta, &rope))) return st;
   if (seqs->n_seqs == 0) return ok();
   hipError_t e = csa::launch_compress(dev_seqs(seqs), dev_rows(c), dev_rows(z), bias, ratio, overlap, rope,
                                       dev_out(entries), seqs->max_q, static_cast<hipStream_t>(stream));
   return hip_status(e, "csa_compress launch");
+}
+
+int csa_compress2(const csa_seqs* seqs, int ratio, int overlap, double rope_theta, const csa_rows* c0,
+                  const csa_rows* z0, const float* bias0, int rope_dims0, const csa_rows* entries0, const csa_rows* c1,
+                  const csa_rows* z1, const float* bias1, int rope_dims1, const csa_rows* entries1, void* stream) {
+  int st;
+  if ((st = check_seqs(seqs))) return st;
+  csa::RopeTab rope0, rope1;
+  if ((st = compress_checks(c0, z0, bias0, entries0, ratio, overlap, rope_dims0, rope_theta, &rope0))) return st;
+  if ((st = compress_checks(c1, z1, bias1, entries1, ratio, overlap, rope_dims1, rope_theta, &rope1))) return st;
+  if (seqs->n_seqs == 0) return ok();
+  hipError_t e = csa::launch_compress2(dev_seqs(seqs), dev_rows(c0), dev_rows(z0), bias0, rope0, dev_out(entries0),
+                                       dev_rows(c1), dev_rows(z1), bias1, rope1, dev_out(entries1), ratio, overlap,
+                                       seqs->max_q, static_cast<hipStream_t>(stream));
+  return hip_status(e, "csa_compress2 launch");
 }
 
 static int index_checks(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI,

@@ -7,7 +7,8 @@
 // "其他注意力技术细节").  The pooling itself is the softmax-gated weighted pooling stated in
 // include/csa.h; the pages leave it open.
 //
-// One workgroup of 256 threads per new entry; thread c owns channel pair (2c, 2c+1), so a
+// One workgroup of 256 threads per new entry (and per job: the KV rows and indexer keys of
+// a layer can be compressed in one launch); thread c owns channel pair (2c, 2c+1), so a
 // 64-lane wavefront owns exactly one 128-dim fp8 scale block and each 16-lane group one
 // 32-dim MXFP4 block.  Sources are walked in ascending position with an online softmax,
 // in float32; the block maxima use a fixed butterfly, so the result depends on the entry
@@ -19,11 +20,19 @@
 
 namespace csa {
 
-__global__ void __launch_bounds__(256) compress_kernel(SeqsDev S, RowsDev c, RowsDev z, const float* __restrict__ bias,
-                                                       int ratio, int overlap, RopeTab rope, RowsOut out,
-                                                       int max_new) {
-  const int b = blockIdx.x / max_new;
-  const int jn = blockIdx.x % max_new;
+// One compression job: the token rows, gate rows, slot bias, RoPE table and output pool.
+struct CompressJob {
+  RowsDev c, z;
+  const float* bias;
+  RopeTab rope;
+  RowsOut out;
+};
+
+__device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& c, const RowsDev& z,
+                                               const float* __restrict__ bias, int ratio, int overlap,
+                                               const RopeTab& rope, const RowsOut& out, int max_new, int blk) {
+  const int b = blk / max_new;
+  const int jn = blk % max_new;
   if (b >= S.n_seqs) return;
   const int n_b = S.q_off[b + 1] - S.q_off[b];
   const int64_t L = S.ctx_len[b];
@@ -140,13 +149,43 @@ __global__ void __launch_bounds__(256) compress_kernel(SeqsDev S, RowsDev c, Row
   }
 }
 
+__global__ void __launch_bounds__(256) compress_kernel(SeqsDev S, CompressJob j0, int ratio, int overlap,
+                                                       int max_new) {
+  compress_block(S, j0.c, j0.z, j0.bias, ratio, overlap, j0.rope, j0.out, max_new, blockIdx.x);
+}
+
+// Two jobs over the same batch in one launch (KV rows and indexer keys of a CSA layer): the
+// first S.n_seqs * max_new workgroups run job 0, the rest job 1, with the same arithmetic
+// as two separate launches.
+__global__ void __launch_bounds__(256) compress2_kernel(SeqsDev S, CompressJob j0, CompressJob j1, int ratio,
+                                                        int overlap, int max_new) {
+  const int per_job = S.n_seqs * max_new;
+  if ((int)blockIdx.x < per_job)
+    compress_block(S, j0.c, j0.z, j0.bias, ratio, overlap, j0.rope, j0.out, max_new, blockIdx.x);
+  else
+    compress_block(S, j1.c, j1.z, j1.bias, ratio, overlap, j1.rope, j1.out, max_new, blockIdx.x - per_job);
+}
+
 hipError_t launch_compress(const SeqsDev& S, const RowsDev& c, const RowsDev& z, const float* bias, int ratio,
                            int overlap, const RopeTab& rope, const RowsOut& out, int max_q, hipStream_t stream) {
   const int max_new = (max_q + ratio - 1) / ratio;
   const int64_t blocks = (int64_t)S.n_seqs * max_new;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, S, c, z, bias, ratio, overlap,
-                     rope, out, max_new);
+  const CompressJob j0{c, z, bias, rope, out};
+  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, S, j0, ratio, overlap, max_new);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress2(const SeqsDev& S, const RowsDev& c0, const RowsDev& z0, const float* bias0,
+                            const RopeTab& rope0, const RowsOut& out0, const RowsDev& c1, const RowsDev& z1,
+                            const float* bias1, const RopeTab& rope1, const RowsOut& out1, int ratio, int overlap,
+                            int max_q, hipStream_t stream) {
+  const int max_new = (max_q + ratio - 1) / ratio;
+  const int64_t blocks = (int64_t)S.n_seqs * max_new;
+  if (blocks == 0) return hipSuccess;
+  const CompressJob j0{c0, z0, bias0, rope0, out0}, j1{c1, z1, bias1, rope1, out1};
+  hipLaunchKernelGGL(compress2_kernel, dim3((unsigned)(2 * blocks)), dim3(256), 0, stream, S, j0, j1, ratio, overlap,
+                     max_new);
   return hipGetLastError();
 }
 

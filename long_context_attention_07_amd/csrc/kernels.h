@@ -9,6 +9,10 @@ namespace csa {
 
 hipError_t launch_compress(const SeqsDev& S, const RowsDev& c, const RowsDev& z, const float* bias, int ratio,
                            int overlap, const RopeTab& rope, const RowsOut& out, int max_q, hipStream_t stream);
+hipError_t launch_compress2(const SeqsDev& S, const RowsDev& c0, const RowsDev& z0, const float* bias0,
+                            const RopeTab& rope0, const RowsOut& out0, const RowsDev& c1, const RowsDev& z1,
+                            const float* bias1, const RopeTab& rope1, const RowsOut& out1, int ratio, int overlap,
+                            int max_q, hipStream_t stream);
 
 hipError_t launch_index_score(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
                               int ratio, float* score, int64_t score_stride, int max_vis, hipStream_t stream);

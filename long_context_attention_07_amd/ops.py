@@ -17,7 +17,7 @@ F32, BF16, KV_SPLIT, MXFP4 = 0, 1, 2, 3
 KV_SPLIT_BF16_DIMS = 64
 OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND = 1, 2, 3
 
-EXPORTS = ("csa_compress", "csa_index_score", "csa_topk", "csa_index_topk", "csa_attend", "hca_attend",
+EXPORTS = ("csa_compress", "csa_compress2", "csa_index_score", "csa_topk", "csa_index_topk", "csa_attend", "hca_attend",
            "csa_workspace_bytes", "csa_strerror", "csa_last_error", "csa_version")
 
 
@@ -52,6 +52,8 @@ def lib():
                                       ctypes.c_double, ctypes.c_size_t)
         P = ctypes.POINTER
         L.csa_compress.argtypes = [P(csa_seqs), P(csa_rows), P(csa_rows), vp, i32, i32, i32, f64, P(csa_rows), vp]
+        L.csa_compress2.argtypes = [P(csa_seqs), i32, i32, f64, P(csa_rows), P(csa_rows), vp, i32, P(csa_rows),
+                                    P(csa_rows), P(csa_rows), vp, i32, P(csa_rows), vp]
         L.csa_index_score.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, vp, i64, vp]
         L.csa_topk.argtypes = [P(csa_seqs), vp, i64, i32, i32, vp, vp]
         L.csa_index_topk.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, i32, vp, vp, sz, vp]
@@ -66,7 +68,7 @@ def lib():
         L.csa_last_error.argtypes = []
         L.csa_last_error.restype = ctypes.c_char_p
         L.csa_version.restype = i32
-        for f in ("csa_compress", "csa_index_score", "csa_topk", "csa_index_topk", "csa_attend", "hca_attend"):
+        for f in ("csa_compress", "csa_compress2", "csa_index_score", "csa_topk", "csa_index_topk", "csa_attend", "hca_attend"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -149,6 +151,15 @@ def csa_workspace_bytes(op, seqs, n_h=0, dim=0, k=0, ratio=1, n_win=0):
 def csa_compress(seqs, c, z, bias, ratio, overlap, rope_dims, rope_theta, entries, stream=None):
     _check(lib().csa_compress(ctypes.byref(seqs.c), ctypes.byref(c.c), ctypes.byref(z.c), _ptr(bias), ratio, overlap,
                               rope_dims, rope_theta, ctypes.byref(entries.c), _stream(stream)), "csa_compress")
+
+
+def csa_compress2(seqs, ratio, overlap, rope_theta, job0, job1, stream=None):
+    """Two compressions in one launch; job = (c, z, bias, rope_dims, entries)."""
+    c0, z0, b0, r0, e0 = job0
+    c1, z1, b1, r1, e1 = job1
+    _check(lib().csa_compress2(ctypes.byref(seqs.c), ratio, overlap, rope_theta, ctypes.byref(c0.c), ctypes.byref(z0.c),
+                               _ptr(b0), r0, ctypes.byref(e0.c), ctypes.byref(c1.c), ctypes.byref(z1.c), _ptr(b1), r1,
+                               ctypes.byref(e1.c), _stream(stream)), "csa_compress2")
 
 
 def csa_index_score(seqs, qI, w, n_I, kI, ratio, score, stream=None):

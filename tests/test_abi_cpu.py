@@ -100,6 +100,11 @@ def test_compress_and_index_validation_errors(lib):
     assert lib.csa_compress(P(s), P(c), P(c), bias, 4, 1, 64, 1.0, P(c), None) == -1
     mx = _rows(dtype=ops.MXFP4, scales=0x5000)
     assert lib.csa_compress(P(s), P(mx), P(c), bias, 4, 1, 0, 10000.0, P(c), None) == -2
+    # the paired launch checks both jobs before launching anything
+    good = (P(c), P(c), bias, 64, P(c))
+    assert lib.csa_compress2(P(s), 4, 1, 10000.0, *good, P(mx), P(c), bias, 0, P(c), None) == -2
+    assert lib.csa_compress2(P(s), 4, 1, 10000.0, *good, P(c), P(c), None, 0, P(c), None) == -1
+    assert lib.csa_compress2(P(s), 0, 1, 10000.0, *good, *good, None) == -1
     qI = _rows(dim=128)
     w = ctypes.c_void_p(0x6000)
     score = ctypes.c_void_p(0x7000)

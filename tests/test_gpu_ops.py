@@ -135,6 +135,32 @@ def test_compress_matches_oracle(case):
         _check_quantised(of, sub, refm, len(rows))
 
 
+def test_compress2_equals_two_compress_calls():
+    """The paired launch (KV rows + indexer keys) writes exactly the bytes of two launches."""
+    g = np.random.default_rng(11)
+    ratio, D, dI = 4, 512, 128
+    n_q, ctx = [5, 1, 1, 12], [800, 4096, 3, 2047]
+    ob, sq, n_ent, n_tok = make_batch(n_q, ctx, ratio, tok_hist=2 * ratio + 8)
+    c, _ = _rows_in(ops.BF16, g.standard_normal((n_tok, D)))
+    z, _ = _rows_in(ops.BF16, g.standard_normal((n_tok, D)))
+    cI, _ = _rows_in(ops.BF16, g.standard_normal((n_tok, dI)))
+    zI, _ = _rows_in(ops.BF16, g.standard_normal((n_tok, dI)))
+    b, _ = f32(g.standard_normal((2 * ratio, D)) / math.sqrt(D))
+    bI, _ = f32(g.standard_normal((2 * ratio, dI)) / math.sqrt(dI))
+    outs = []
+    for paired in (False, True):
+        kv, kI = empty_rows(n_ent, D, ops.KV_SPLIT), empty_rows(n_ent, dI, ops.MXFP4)
+        if paired:
+            ops.csa_compress2(sq, ratio, 1, 10000.0, (c, z, b, 64, kv), (cI, zI, bI, 0, kI))
+        else:
+            ops.csa_compress(sq, c, z, b, ratio, 1, 64, 10000.0, kv)
+            ops.csa_compress(sq, cI, zI, bI, ratio, 1, 0, 10000.0, kI)
+        outs.append((kv, kI))
+    torch.cuda.synchronize()
+    for x, y in zip(outs[0], outs[1]):
+        assert torch.equal(x.data, y.data) and torch.equal(x.scales, y.scales)
+
+
 # ----------------------------------------------------------------------------- index scores
 
 

@@ -13,7 +13,8 @@
 // * each lane fetches the 16-byte chunk c ^ (row mod 16) of its row, an XOR swizzle that
 //   makes the MFMA operand reads (16 rows, same chunk) hit 16 distinct bank groups;
 // * per 16-entry block, S[head, entry] = qI kI^T with v_mfma_f32_16x16x32_bf16: the token's
-//   <= 64 indexer heads sit in registers as the A operand (4 blocks of 16), the keys are
+//   <= 64 indexer heads (staged once through LDS) sit in registers as the A operand (4
+//   blocks of 16), the keys are
 //   the B operand.  A lane then holds 16 heads of one entry and sums w_h * relu over them
 //   in a fixed order (head block, then row); two xor-shuffles across the lane groups finish
 //   the head sum, so a score depends on its token and entry only.
@@ -80,30 +81,50 @@ __global__ void __launch_bounds__(256) index_score_mfma_kernel(SeqsDev S, RowsDe
     }
   };
 
-  const int prologue = min(n_tiles, RING - 1);
-  for (int i = 0; i < prologue; ++i) issue(i);
-
-  // A operand: heads c16 + 16 hb, dims 8g + 32 kk .. +7 (requested after the key tiles).
-  // The result row of lane (g, j) is head 4g + j (+ 16 hb): its weight is kept per lane.
-  ibf16x8_t qa[4][4];
+  // The token's indexer queries (n_I rows of 256 B, the A operand) are staged once per
+  // workgroup in the last ring slot, which no key tile uses before the loop starts: one
+  // direct-to-LDS load per 4 rows (same XOR chunk swizzle as the keys).  Groups of 4 heads
+  // wholly past n_I are zeroed; in a partly filled group the rows past n_I repeat a valid
+  // row, and their weights are 0.  Weights of the result rows: head 4g + j + 16 hb.
+  uint8_t* qslot = ring[RING - 1];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r0 = 16 * wv + 4 * q;
+    if (r0 >= n_I) *reinterpret_cast<uint4*>(qslot + r0 * kIRow + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r0 = 16 * wv + 4 * q;
+    if (r0 < n_I) {
+      const int r = min(r0 + (lane >> 4), n_I - 1);
+      const int chunk = (lane & 15) ^ (r & 15);
+      const uint8_t* src = qI.data + ((int64_t)t * n_I + r) * qI.stride + chunk * 16;
+      __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)(qslot + r0 * kIRow), 16, 0, 0);
+    }
+  }
   float wh[4][4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    const int h = c16 + 16 * hb;
-    if (h < n_I) {
-      const uint8_t* row = qI.data + ((int64_t)t * n_I + h) * qI.stride;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        qa[hb][kk] = __builtin_bit_cast(ibf16x8_t, *reinterpret_cast<const uint4*>(row + (8 * g + 32 * kk) * 2));
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qa[hb][kk] = __builtin_bit_cast(ibf16x8_t, make_uint4(0u, 0u, 0u, 0u));
-    }
+  for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int hr = 4 * g + j + 16 * hb;
       wh[hb][j] = hr < n_I ? w[(int64_t)t * n_I + hr] : 0.f;
     }
+
+  const int prologue = min(n_tiles, RING - 1);
+  for (int i = 0; i < prologue; ++i) issue(i);
+
+  // queries landed (only the prologue tiles may still be in flight), visible to all waves
+  wait_tiles_in_flight(prologue);
+  __syncthreads();
+  // A operand: heads c16 + 16 hb, dims 8g + 32 kk .. +7
+  ibf16x8_t qa[4][4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const uint8_t* qrow = qslot + (c16 + 16 * hb) * kIRow;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qa[hb][kk] = *reinterpret_cast<const ibf16x8_t*>(qrow + (((g + 4 * kk) ^ c16) * 16));
   }
 
   float* srow = score + (int64_t)t * score_stride;

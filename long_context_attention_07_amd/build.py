@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["abi.cpp", "compress.hip", "index.hip", "index_mfma.hip", "topk.hip", "attend.hip", "attend_mfma.hip"]
+SOURCES = ["abi.cpp", "compress.hip", "index.hip", "index_mfma.hip", "index_mx.hip", "topk.hip", "attend.hip",
+           "attend_mfma.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -264,7 +264,7 @@ int csa_index_score(const csa_seqs* seqs, const csa_rows* qI, const float* w, in
     return fail(CSA_EINVAL, "score_stride %lld < floor(max_ctx/ratio) = %d", (long long)score_stride, max_vis);
   if (seqs->total_q == 0) return ok();
   hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio, score,
-                                         score_stride, max_vis, static_cast<hipStream_t>(stream));
+                                         score_stride, max_vis, seqs->max_q, static_cast<hipStream_t>(stream));
   return hip_status(e, "csa_index_score launch");
 }
 
@@ -299,7 +299,7 @@ int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int
   float* score = static_cast<float*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio, score, stride,
-                                         max_vis, s);
+                                         max_vis, seqs->max_q, s);
   if (e != hipSuccess) return hip_status(e, "csa_index_topk score launch");
   e = csa::launch_topk(dev_seqs(seqs), score, stride, ratio, k, idx, max_vis, s);
   return hip_status(e, "csa_index_topk select launch");

@@ -208,6 +208,7 @@ __device__ __forceinline__ float2 rope_pair(float2 x, int64_t pos, double inv_fr
 
 struct TokenCtx {
   int b;
+  int q_end;        // first query row past the sequence's queries
   int64_t p;        // position of the query token
   int64_t entry0;   // pool row of entry 0
   int64_t tok0;     // token-pool row of position tok_lo
@@ -250,6 +251,7 @@ __device__ __forceinline__ TokenCtx token_ctx(const SeqsDev& S, int t) {
   const int win = __popcll(__ballot(in && q0 <= t)) - 1;  // >= 0: q_off[lo] <= t
   TokenCtx c;
   c.b = lo + win;
+  c.q_end = __builtin_amdgcn_readlane(q1, win);
   const int wq0 = __builtin_amdgcn_readlane(q0, win), wq1 = __builtin_amdgcn_readlane(q1, win);
   c.p = (int64_t)__builtin_amdgcn_readlane(cl, win) - (wq1 - wq0) + (t - wq0);
   c.entry0 = readlane64(e0, win);

@@ -3,8 +3,9 @@
 // DSA's lightweight indexer; Figure 2 "Lightning Indexer"; stuffyNLP review: the indexer of
 // DeepSeek-V3.2-Exp).
 //
-// Generic float32-arithmetic kernel used for F32 and MXFP4 rows (bf16 keys of 128 dims
-// go to the matrix-core kernel in index_mfma.hip): one workgroup per
+// Generic float32-arithmetic kernel used for F32 rows and for MXFP4 rows of 32 or 64 dims
+// (bf16 keys of 128 dims go to the matrix-core kernel in index_mfma.hip, MXFP4 keys of 128
+// dims to the scaled matrix-core kernel in index_mx.hip): one workgroup per
 // (token, tile of 256 entries), one entry per thread, the token's qI block decoded into
 // LDS, the entry's key row decoded into registers; dims then heads are summed in
 // ascending order, so a score depends on its token and entry only.
@@ -54,13 +55,20 @@ __global__ void __launch_bounds__(256) index_score_valu_kernel(SeqsDev S, RowsDe
 }
 
 bool index_mfma_supported(const RowsDev& qI, const RowsDev& kI, int n_I, int64_t score_stride);
+bool index_mx_supported(const RowsDev& qI, const RowsDev& kI, int n_I);
+hipError_t launch_index_score_mx(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
+                                 int ratio, float* score, int64_t score_stride, int max_vis, int max_q,
+                                 hipStream_t stream);
 hipError_t launch_index_score_mfma(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
                                    int ratio, float* score, int64_t score_stride, int max_vis, hipStream_t stream);
 
 hipError_t launch_index_score(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
-                              int ratio, float* score, int64_t score_stride, int max_vis, hipStream_t stream) {
+                              int ratio, float* score, int64_t score_stride, int max_vis, int max_q,
+                              hipStream_t stream) {
   if (index_mfma_supported(qI, kI, n_I, score_stride))
     return launch_index_score_mfma(S, qI, w, n_I, kI, ratio, score, score_stride, max_vis, stream);
+  if (index_mx_supported(qI, kI, n_I))
+    return launch_index_score_mx(S, qI, w, n_I, kI, ratio, score, score_stride, max_vis, max_q, stream);
   const int n_tiles = (max_vis + kIdxTile - 1) / kIdxTile;
   const int64_t blocks = (int64_t)S.total_q * n_tiles;
   if (blocks == 0) return hipSuccess;

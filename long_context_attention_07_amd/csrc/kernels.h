@@ -15,7 +15,8 @@ hipError_t launch_compress2(const SeqsDev& S, const RowsDev& c0, const RowsDev& 
                             int max_q, hipStream_t stream);
 
 hipError_t launch_index_score(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
-                              int ratio, float* score, int64_t score_stride, int max_vis, hipStream_t stream);
+                              int ratio, float* score, int64_t score_stride, int max_vis, int max_q,
+                              hipStream_t stream);
 
 hipError_t launch_topk(const SeqsDev& S, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
                        int max_vis, hipStream_t stream);

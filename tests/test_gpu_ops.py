@@ -191,6 +191,32 @@ def test_index_score_matches_oracle(fmt, d_I, n_I):
         assert np.all(np.isnan(sc[row, V:])), f"token {row}: columns >= V written"
 
 
+def test_index_score_mxfp4_query_blocks():
+    """MXFP4 scores on the scaled matrix cores with query blocks: several sequences with many
+    new tokens each, so blocks of consecutive query rows cross sequence boundaries."""
+    g = np.random.default_rng(23)
+    ratio, d_I, n_I = 4, 128, 64
+    n_q = [17, 1, 23, 6, 40]
+    ctx = [300, 2051, 23, 1600, 900]
+    ob, sq, n_ent, _ = make_batch(n_q, ctx, ratio)
+    kI_rows, kI_val = _rows_in(ops.MXFP4, g.standard_normal((n_ent, d_I)))
+    qI_rows, qI_val = _rows_in(ops.MXFP4, g.standard_normal((sq.total_q * n_I, d_I)))
+    w_t, w_val = f32(g.standard_normal((sq.total_q, n_I)) / math.sqrt(n_I))
+    stride = sq.max_ctx // ratio + 3
+    score = torch.full((sq.total_q, stride), float("nan"), dtype=torch.float32, device=DEV)
+    ops.csa_index_score(sq, qI_rows, w_t, n_I, kI_rows, ratio, score)
+    torch.cuda.synchronize()
+    sc = score.cpu().numpy().astype(np.float64)
+    for row, b, p in ob.tokens():
+        V = visible(p, ratio)
+        kI = kI_val[ob.entry_off[b]: ob.entry_off[b] + V]
+        qI = qI_val[row * n_I:(row + 1) * n_I]
+        ref = index_scores(qI, w_val[row], kI)
+        bound = score_error_bound(qI, w_val[row], kI) if V else np.zeros(0)
+        assert np.all(np.abs(sc[row, :V] - ref) <= bound), f"token {row}: score error beyond float32 bound"
+        assert np.all(np.isnan(sc[row, V:])), f"token {row}: columns >= V written"
+
+
 # ----------------------------------------------------------------------------- top-k
 
 

@@ -1,26 +1,33 @@
-// Shared-KV MQA on the matrix cores: bf16 rows of 512 dims ("DeepSeek-V4 深度分析报告"
-// section 2.1 and Figure 2: shared-KV MQA over the selected (CSA) or all (HCA) compressed
-// entries with the 128-token window concatenated; list "其他注意力技术细节": partial RoPE on
-// the last 64 dims, inverse RoPE of the output, learnable sink).
+// Shared-KV MQA on the matrix cores over rows of 512 dims: bf16 rows, or fp8 e4m3 rows with
+// one fp32 scale per 128 dims and a bf16 rotary tail ("DeepSeek-V4 深度分析报告" section 2.1
+// and Figure 2: shared-KV MQA over the selected (CSA) or all (HCA) compressed entries with
+// the 128-token window concatenated; list "其他注意力技术细节": partial RoPE on the last 64
+// dims, inverse RoPE of the output, learnable sink; section 3.4: fp8 KV with 1x128 scales).
 //
 // Workgroup = (token, group of 16 query heads, chunk of the token's key list), 4 waves.
 // The key list is walked in tiles of 64 rows staged in LDS (rows padded to 1040 bytes);
-// the next tile is prefetched into registers (one 1 KiB row per wave instruction, any
-// row order, so the top-k gather is fully coalesced) while the current one is processed.
-//   QK   S^T[key, head] = K Q^T with v_mfma_f32_16x16x32_bf16: wave w owns keys
+// the next tile is prefetched into registers (one row per wave instruction, any row order,
+// so the top-k gather is fully coalesced) while the current one is processed.  The tile
+// format is bf16 for bf16 rows; fp8 rows are staged as their codes in fp16 (exact), the
+// block scales kept apart in fp32.
+//   QK   S^T[key, head] = K Q^T with v_mfma_f32_16x16x32_{bf16,f16}: wave w owns keys
 //        16w..16w+15 of the tile (A operand from LDS), the 16 rotated query rows sit in
-//        registers as the B operand (64 VGPRs).
+//        registers as the B operand (64 VGPRs).  fp8 rows: one partial per code block,
+//        scaled in fp32.  Rotated dims carry hi + lo residual terms on both sides.
 //   softmax  in the log2 domain; per-head tile max and sum exchanged across the 4 waves in
-//        a fixed order; P rounded to bf16 (the sums use the rounded values).
-//   PV   O[head, dim] += P V: wave w owns dims 128w..128w+127; P is the A operand (LDS),
-//        V is read from the same row-major key tile with ds_read_b64_tr_b16, which hands
-//        each lane a column of 4 consecutive keys -- the B operand layout.
+//        a fixed order; P rounded to the tile format (fp8 rows: hi + lo), the sums use the
+//        rounded values.
+//   PV   O[head, dim] += P V: wave w owns dims 128w..128w+127 (for fp8 rows: code block w,
+//        whose per-key scale is folded into P); P is the A operand (LDS), V is read from
+//        the same row-major key tile with ds_read_b64_tr_b16, which hands each lane a
+//        column of 4 consecutive keys -- the B operand layout.
 // Chunk partials are folded in chunk order from the sink; the combine kernel below (one
 // wave per head, 8 dims per lane) runs the same fold and finalisation arithmetic as the
 // single launch, so split and single launches agree bit for bit, and a token's bits never
 // depend on the batch.  The workgroup barriers wait for LDS instructions only: the next
-// tile's row loads stay in flight across them until the rows are staged.  Window rows are rotated (RoPE at their own positions) as
-// they are staged; absent slots are staged as zero rows and masked.
+// tile's row loads stay in flight across them until the rows are staged.  Window rows are
+// rotated (RoPE at their own positions) as they are staged; absent slots are staged as
+// zero rows and masked.
 
 #include "attend_common.cuh"
 
@@ -43,6 +50,8 @@ constexpr int kHG = 16;                // query heads per workgroup
 constexpr int kDM = 512;               // head dim of this kernel
 constexpr int kKStride = kDM * 2 + 16;  // bytes per staged key row
 constexpr int kPStride = kT * 2 + 16;   // bytes per P row (one head)
+constexpr int kRopeMax = 64;            // rotary dims this kernel takes (the row's last 64 at most)
+constexpr int kLoStride = kRopeMax * 2 + 16;  // bytes per row of the rotated-dims residual tile
 
 constexpr int kMaxIdx = 4096;           // largest k the in-LDS idx table holds
 
@@ -50,6 +59,9 @@ struct __align__(16) MfmaLds {
   uint8_t k[kT * kKStride];
   int32_t sidx[kMaxIdx];                // idx[t, s_lo .. s_hi) of this workgroup's chunks
   uint8_t p[kHG * kPStride];
+  uint8_t p_lo[kHG * kPStride];  // fp16 tiles: residual of P (P = hi + lo to ~22 bits)
+  uint8_t klo[kT * kLoStride];   // window rows: residual of their rotated last 64 dims
+  float scl[4][kT];              // fp8 rows: the fp32 scale of each 128-dim code block
   float red_max[4][kHG];
   float red_sum[4][kHG];
   float alpha[kHG];
@@ -58,11 +70,17 @@ struct __align__(16) MfmaLds {
 };
 
 struct TileStage {
-  uint4 v[16];      // row 16w+it, bytes 16*lane .. 16*lane+15
+  uint4 v[16];      // row 16w+it, bytes 16*lane .. 16*lane+15 of the stored row
+  float sc[16];     // fp8 rows: lanes 0, 8, 16, 24 hold the scale of code block lane / 8
   uint32_t valid;   // bit it: row present
   uint32_t win;     // bit it: window row (rotated when staged)
   int64_t pos0;     // position of window row it is pos0 + it
 };
+
+// KV split rows (448 fp8 e4m3 codes with one fp32 scale per 128 dims, then 64 bf16 dims)
+// are 576 bytes: lanes 0..27 carry 16 codes each, lanes 28..35 the bf16 tail.
+constexpr int kSplitCodeLanes = (kDM - kSplitBf16Dims) / 16;
+constexpr int kSplitLanes = kSplitCodeLanes + kSplitBf16Dims * 2 / 16;
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -70,17 +88,63 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
 }
 
+// The tile's 16-bit element type: bf16 for bf16 rows; fp16 (11-bit significand) for rows
+// decoded from fp8 blocks, whose scaled values would lose too much in bf16 next to
+// outliers.  Conversions round to nearest even.
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ float f16_val(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+  return F16 ? (f16_bits(a) | (f16_bits(b) << 16)) : pack_bf16(a, b);
+}
+template <bool F16>
+__device__ __forceinline__ float2 unpack16(uint32_t u) {
+  return F16 ? make_float2(f16_val(u & 0xffffu), f16_val(u >> 16)) : make_float2(bf_lo(u), bf_hi(u));
+}
+template <bool F16>
+__device__ __forceinline__ uint32_t bits16(float x) {
+  return F16 ? f16_bits(x) : f32_to_bf16_bits(x);
+}
+template <bool F16>
+__device__ __forceinline__ float val16(uint32_t b) {
+  return F16 ? f16_val(b) : __uint_as_float(b << 16);
+}
+template <bool F16>
+__device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+  if (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                0, 0, 0);
+}
+// bf16 pairs -> the tile's format (exact for fp16 when the value is in its range)
+template <bool F16>
+__device__ __forceinline__ uint4 from_bf16(uint4 v) {
+  if (!F16) return v;
+  return make_uint4(pack16<true>(bf_lo(v.x), bf_hi(v.x)), pack16<true>(bf_lo(v.y), bf_hi(v.y)),
+                    pack16<true>(bf_lo(v.z), bf_hi(v.z)), pack16<true>(bf_lo(v.w), bf_hi(v.w)));
+}
+
 // Rotate the 4 pairs held in one 16-byte chunk (8 bf16 dims starting at pair index q0).
-__device__ __forceinline__ uint4 rotate_chunk(uint4 v, int64_t pos, const FreqLds& F, int q0) {
+// The rotated values in the tile format go to *hi, their rounding residuals to *lo.
+template <bool F16>
+__device__ __forceinline__ void rotate_chunk(uint4 v, int64_t pos, const FreqLds& F, int q0, uint4* hi, uint4* lo) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t r[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float c, s;
     rope_cs_mode<ROPE_FAST>(pos, F, q0 + i, &c, &s);
-    float2 y = rotate2(make_float2(bf_lo(w[i]), bf_hi(w[i])), c, s);
-    w[i] = pack_bf16(y.x, y.y);
+    const float2 y = rotate2(make_float2(bf_lo(w[i]), bf_hi(w[i])), c, s);
+    w[i] = pack16<F16>(y.x, y.y);
+    const float2 yh = unpack16<F16>(w[i]);
+    r[i] = pack16<F16>(y.x - yh.x, y.y - yh.y);
   }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  *hi = make_uint4(w[0], w[1], w[2], w[3]);
+  *lo = make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 // Final values of 8 consecutive output dims d0..d0+7 of one head (already normalised):
@@ -127,6 +191,7 @@ __device__ __forceinline__ SlotRef resolve_slot_lds(const AttendArgs& a, const T
   return r;
 }
 
+template <bool KVF>
 __device__ __forceinline__ void load_tile(const AttendArgs& a, const TokenCtx& ctx, int64_t n_ent, int64_t s0,
                                           int w, int lane, TileStage& st, const int32_t* sidx, int64_t s_lo) {
   SlotRef r;
@@ -142,8 +207,13 @@ __device__ __forceinline__ void load_tile(const AttendArgs& a, const TokenCtx& c
   const uint8_t* kvp = a.kv.data;
   const uint8_t* tokp = a.tok.data;
   const int64_t kvs = a.kv.stride, toks = a.tok.stride;
+  const float* kvsc = reinterpret_cast<const float*>(a.kv.scales);
+  const float* toksc = reinterpret_cast<const float*>(a.tok.scales);
+  constexpr int nb = (kDM - kSplitBf16Dims + kKvBlock - 1) / kKvBlock;
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
+    st.v[it] = make_uint4(0u, 0u, 0u, 0u);
+    st.sc[it] = 0.f;
     if ((st.valid >> it) & 1u) {
       const int64_t row = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_hi, it) << 32) |
                                     (uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_lo, it));
@@ -152,38 +222,74 @@ __device__ __forceinline__ void load_tile(const AttendArgs& a, const TokenCtx& c
       const bool win = (st.win >> it) & 1u;
       const uint8_t* base = win ? tokp : kvp;
       const int64_t stride = win ? toks : kvs;
-      st.v[it] = reinterpret_cast<const uint4*>(base + row * stride)[lane];
-    } else {
-      st.v[it] = make_uint4(0u, 0u, 0u, 0u);
+      if (!KVF) {
+        st.v[it] = reinterpret_cast<const uint4*>(base + row * stride)[lane];
+      } else {
+        if (lane < kSplitLanes) st.v[it] = reinterpret_cast<const uint4*>(base + row * stride)[lane];
+        if (lane < kSplitCodeLanes && (lane & 7) == 0) st.sc[it] = (win ? toksc : kvsc)[row * nb + (lane >> 3)];
+      }
     }
   }
 }
 
-// Stage the wave's 16 rows in LDS, then rotate the window rows among them in place (RoPE
-// at each row's own position), one pair per lane: a compact loop that runs only for the
-// tiles that hold window rows.
+// Stage the wave's 16 rows in LDS in the tile format.  fp8 rows are staged as their e4m3
+// codes (exact in fp16) with the block scales in L.scl: the scales are applied in fp32
+// after the products, so a key's logit carries no rounding of its scaled values.  Their
+// bf16 tail is converted to fp16 (exact in range).  Then, for waves that hold window
+// rows, the rows' last 64 dims are rotated in place (RoPE at each row's own position) and
+// the rounding residual of every rotated value goes to L.klo (zero for the other rows), so
+// that the rotated keys enter the logits to about twice the tile format's precision.
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t two) {
+  return pack16<true>(e4m3_to_f32(two & 0xffu), e4m3_to_f32((two >> 8) & 0xffu));
+}
+
+template <bool KVF>
 __device__ __forceinline__ void store_tile(MfmaLds& L, const AttendArgs& a, const TileStage& st, int w, int lane,
                                            const FreqLds& F) {
+  if (!KVF) {
 #pragma unroll
-  for (int it = 0; it < 16; ++it) *reinterpret_cast<uint4*>(&L.k[(16 * w + it) * kKStride + 16 * lane]) = st.v[it];
-  const int n_pairs = a.rope.dims >> 1;
-  const int dn = kDM - a.rope.dims;
-  uint32_t wm = st.win;
-  while (wm) {
-    const int it = __ffs((int)wm) - 1;
-    wm &= wm - 1u;
-    if (lane < n_pairs) {
-      uint32_t* pp = reinterpret_cast<uint32_t*>(&L.k[(16 * w + it) * kKStride + (dn + 2 * lane) * 2]);
-      const uint32_t u = *pp;
-      float c, s;
-      rope_cs_mode<ROPE_FAST>(st.pos0 + it, F, lane, &c, &s);
-      const float2 y = rotate2(make_float2(bf_lo(u), bf_hi(u)), c, s);
-      *pp = pack_bf16(y.x, y.y);
+    for (int it = 0; it < 16; ++it) *reinterpret_cast<uint4*>(&L.k[(16 * w + it) * kKStride + 16 * lane]) = st.v[it];
+  } else if (lane < kSplitCodeLanes) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const uint4 v = st.v[it];
+      const uint4 lo = make_uint4(fp8x2_to_f16x2(v.x), fp8x2_to_f16x2(v.x >> 16), fp8x2_to_f16x2(v.y),
+                                  fp8x2_to_f16x2(v.y >> 16));
+      const uint4 hi = make_uint4(fp8x2_to_f16x2(v.z), fp8x2_to_f16x2(v.z >> 16), fp8x2_to_f16x2(v.w),
+                                  fp8x2_to_f16x2(v.w >> 16));
+      uint4* dst = reinterpret_cast<uint4*>(&L.k[(16 * w + it) * kKStride + 32 * lane]);
+      dst[0] = lo;
+      dst[1] = hi;
+      if ((lane & 7) == 0) L.scl[lane >> 3][16 * w + it] = st.sc[it];
+    }
+  } else if (lane < kSplitLanes) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it)
+      *reinterpret_cast<uint4*>(&L.k[(16 * w + it) * kKStride + 2 * (kDM - kSplitBf16Dims) +
+                                     16 * (lane - kSplitCodeLanes)]) = from_bf16<true>(st.v[it]);
+  }
+  if (st.win != 0u && lane < kRopeMax / 2) {
+    // pair `lane` of the last 64 dims; rotary pairs start at dim kDM - rope.dims
+    const int d = kDM - kRopeMax + 2 * lane;
+    const int dn = kDM - a.rope.dims;
+    for (int it = 0; it < 16; ++it) {
+      uint32_t res = 0u;
+      if (((st.win >> it) & 1u) && d >= dn) {
+        uint32_t* pp = reinterpret_cast<uint32_t*>(&L.k[(16 * w + it) * kKStride + d * 2]);
+        float c, s;
+        rope_cs_mode<ROPE_FAST>(st.pos0 + it, F, (d - dn) >> 1, &c, &s);
+        const float2 y = rotate2(unpack16<KVF>(*pp), c, s);
+        const uint32_t hi = pack16<KVF>(y.x, y.y);
+        const float2 yh = unpack16<KVF>(hi);
+        *pp = hi;
+        res = pack16<KVF>(y.x - yh.x, y.y - yh.y);
+      }
+      *reinterpret_cast<uint32_t*>(&L.klo[(16 * w + it) * kLoStride + 4 * lane]) = res;
     }
   }
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool KVF>
 __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* __restrict__ ws_o,
                                                           float* __restrict__ ws_ml, int n_hg, int max_chunks,
                                                           int chunk_slots, int n_logical) {
@@ -228,10 +334,11 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
 
   // first tile's rows are requested before the query rows, so the two latencies overlap
   TileStage st;
-  load_tile(a, ctx, n_ent, s_lo, w, lane, st, L.sidx, s_lo);
+  load_tile<KVF>(a, ctx, n_ent, s_lo, w, lane, st, L.sidx, s_lo);
 
   // ---- rotated query fragments: head hg*16 + c16, dims 8g + 32kk .. +7
-  bf16x8_t qf[16];
+  uint4 qf[16];  // in the tile format
+  uint4 qlo[2];  // rounding residuals of the rotated dims among 448..511 (zero elsewhere)
   {
     const int h = hg * kHG + c16;
     uint4 raw[16];
@@ -243,11 +350,18 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) raw[kk] = make_uint4(0u, 0u, 0u, 0u);
     }
+    // rotary dims lie within the last 64 (dn >= 448): only chunks 14 and 15 can hold them
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
+    for (int kk = 0; kk < 14; ++kk) qf[kk] = from_bf16<KVF>(raw[kk]);
+#pragma unroll
+    for (int kk = 14; kk < 16; ++kk) {
       const int d0 = 8 * g + 32 * kk;
-      if (d0 >= dn) raw[kk] = rotate_chunk(raw[kk], ctx.p, F, (d0 - dn) >> 1);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, raw[kk]);
+      if (d0 >= dn) {
+        rotate_chunk<KVF>(raw[kk], ctx.p, F, (d0 - dn) >> 1, &qf[kk], &qlo[kk - 14]);
+      } else {
+        qf[kk] = from_bf16<KVF>(raw[kk]);
+        qlo[kk - 14] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   }
 
@@ -276,8 +390,8 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
 
   while (true) {
     lds_barrier();  // previous tile fully consumed
-    store_tile(L, a, st, w, lane, F);
-    const uint32_t valid = st.valid;
+    store_tile<KVF>(L, a, st, w, lane, F);
+    const uint32_t valid = st.valid, winm = st.win;
     lds_barrier();  // tile visible
 
     int ncc = cc, ntl = tile + 1;
@@ -287,16 +401,43 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
     }
     const bool has_next = ncc < c_end;
     if (has_next)
-      load_tile(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, w, lane, st, L.sidx, s_lo);
+      load_tile<KVF>(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, w, lane, st, L.sidx, s_lo);
 
-    // ---- S^T = K Q^T for keys 16w..16w+15
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- S^T = K Q^T for keys 16w..16w+15.  Partial products per 128-dim block: for fp8
+    // rows blocks 0..3 hold the code products (scaled below), block 4 the bf16 tail.  The
+    // rotated dims add the query residual times the keys and, for window rows, the key
+    // residual times the query.
+    f32x4_t part[5];
+#pragma unroll
+    for (int b = 0; b < 5; ++b) part[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     {
       const uint8_t* krow = &L.k[(16 * w + c16) * kKStride + 16 * g];
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(krow + 64 * kk);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], acc, 0, 0, 0);
+        const int b = KVF ? (kk < 14 ? kk / 4 : 4) : 0;
+        const uint4 ka = *reinterpret_cast<const uint4*>(krow + 64 * kk);
+        part[b] = mfma16<KVF>(ka, qf[kk], part[b]);
+        if (kk >= 14) part[KVF ? 4 : 0] = mfma16<KVF>(ka, qlo[kk - 14], part[KVF ? 4 : 0]);
+      }
+      if (winm != 0u) {
+        const uint8_t* lrow = &L.klo[(16 * w + c16) * kLoStride + 16 * g];
+#pragma unroll
+        for (int kk = 14; kk < 16; ++kk) {
+          const uint4 kl = *reinterpret_cast<const uint4*>(lrow + 64 * (kk - 14));
+          part[KVF ? 4 : 0] = mfma16<KVF>(kl, qf[kk], part[KVF ? 4 : 0]);
+        }
+      }
+    }
+    f32x4_t acc = part[KVF ? 4 : 0];
+    if (KVF) {
+      // logit of key 16w+4g+j: tail + sum over code blocks of scale * code products
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float4 sb = *reinterpret_cast<const float4*>(&L.scl[b][16 * w + 4 * g]);
+        acc[0] = __builtin_fmaf(sb.x, part[b][0], acc[0]);
+        acc[1] = __builtin_fmaf(sb.y, part[b][1], acc[1]);
+        acc[2] = __builtin_fmaf(sb.z, part[b][2], acc[2]);
+        acc[3] = __builtin_fmaf(sb.w, part[b][3], acc[3]);
       }
     }
     float s[4];
@@ -310,16 +451,25 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
     const float tmax = fmaxf(fmaxf(L.red_max[0][c16], L.red_max[1][c16]), fmaxf(L.red_max[2][c16], L.red_max[3][c16]));
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = rescale(m_run, m_new);
+    // P in the tile format; for fp16 tiles also its residual, so that P (hi + lo) keeps
+    // ~22 bits next to large values (both products go through the matrix cores)
     float pr[4];
-    uint32_t pb[4];
+    uint32_t pb[4], pl[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float pj = (s[j] == -INFINITY) ? 0.f : ex2(s[j] - m_new);
-      pb[j] = f32_to_bf16_bits(pj);
-      pr[j] = __uint_as_float(pb[j] << 16);
+      pb[j] = bits16<KVF>(pj);
+      pr[j] = val16<KVF>(pb[j]);
+      if (KVF) {
+        pl[j] = bits16<true>(pj - pr[j]);
+        pr[j] += val16<true>(pl[j]);
+      }
     }
     *reinterpret_cast<uint2*>(&L.p[c16 * kPStride + (16 * w + 4 * g) * 2]) =
         make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16));
+    if (KVF)
+      *reinterpret_cast<uint2*>(&L.p_lo[c16 * kPStride + (16 * w + 4 * g) * 2]) =
+          make_uint2(pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16));
     float ls = ((pr[0] + pr[1]) + pr[2]) + pr[3];
     ls += __shfl_xor(ls, 16, 64);
     ls += __shfl_xor(ls, 32, 64);
@@ -341,8 +491,33 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
         for (int j = 0; j < 4; ++j) O[nb][j] *= al[j];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8_t pa = *reinterpret_cast<const bf16x8_t*>(&L.p[c16 * kPStride + (8 * g + 32 * ks) * 2]);
-        const int r0 = 32 * ks + 8 * g + (c16 >> 2);
+        const int key0 = 8 * g + 32 * ks;
+        const uint4 pa = *reinterpret_cast<const uint4*>(&L.p[c16 * kPStride + key0 * 2]);
+        uint4 pa_lo = make_uint4(0u, 0u, 0u, 0u);
+        // fp8 rows: the code block of this wave's dims (block w; wave 3's dims 448..511 are
+        // the unscaled tail) carries each key's scale, which is folded into P
+        uint4 ps = pa, ps_lo = pa_lo, pt = pa, pt_lo = pa_lo;
+        if (KVF) {
+          pa_lo = *reinterpret_cast<const uint4*>(&L.p_lo[c16 * kPStride + key0 * 2]);
+          const float4 s0 = *reinterpret_cast<const float4*>(&L.scl[w][key0]);
+          const float4 s1 = *reinterpret_cast<const float4*>(&L.scl[w][key0 + 4]);
+          const float sk[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+          const uint32_t ph[4] = {pa.x, pa.y, pa.z, pa.w}, pl2[4] = {pa_lo.x, pa_lo.y, pa_lo.z, pa_lo.w};
+          uint32_t qh[4], ql[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float2 h2 = unpack16<true>(ph[i]), l2 = unpack16<true>(pl2[i]);
+            const float x0 = (h2.x + l2.x) * sk[2 * i], x1 = (h2.y + l2.y) * sk[2 * i + 1];
+            qh[i] = pack16<true>(x0, x1);
+            const float2 r2 = unpack16<true>(qh[i]);
+            ql[i] = pack16<true>(x0 - r2.x, x1 - r2.y);
+          }
+          ps = make_uint4(qh[0], qh[1], qh[2], qh[3]);
+          ps_lo = make_uint4(ql[0], ql[1], ql[2], ql[3]);
+          pt = w < 3 ? ps : pa;
+          pt_lo = w < 3 ? ps_lo : pa_lo;
+        }
+        const int r0 = key0 + (c16 >> 2);
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
           const int n0 = 128 * w + 16 * nb + 4 * (c16 & 3);
@@ -351,7 +526,13 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + 4 * kKStride));
           typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
           const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8_t, both), O[nb], 0, 0, 0);
+          const uint4 vb = __builtin_bit_cast(uint4, both);
+          if (!KVF) {
+            O[nb] = mfma16<false>(pa, vb, O[nb]);
+          } else {
+            O[nb] = mfma16<true>(nb < 4 ? ps : pt, vb, O[nb]);
+            O[nb] = mfma16<true>(nb < 4 ? ps_lo : pt_lo, vb, O[nb]);
+          }
         }
       }
     }
@@ -473,9 +654,23 @@ __global__ void __launch_bounds__(256) attend_combine_mfma_kernel(AttendArgs a, 
 }
 
 bool attend_mfma_supported(const AttendArgs& a) {
-  return (!a.csa || a.k <= kMaxIdx) && a.q.dim == kDM && a.q.dtype == DT_BF16 && a.kv.dtype == DT_BF16 && a.tok.dtype == DT_BF16 &&
-         a.out.dtype == DT_BF16 && a.rope.dims % 8 == 0 && a.kv.stride % 16 == 0 && a.tok.stride % 16 == 0 &&
-         a.q.stride % 16 == 0 && a.out.stride % 16 == 0;
+  const bool rows_ok = (a.kv.dtype == DT_BF16 && a.tok.dtype == DT_BF16) ||
+                       (a.kv.dtype == DT_KV_SPLIT && a.tok.dtype == DT_KV_SPLIT && a.kv.dim == kDM && a.tok.dim == kDM);
+  return (!a.csa || a.k <= kMaxIdx) && a.q.dim == kDM && a.q.dtype == DT_BF16 && rows_ok && a.out.dtype == DT_BF16 &&
+         a.rope.dims % 8 == 0 && a.rope.dims <= kRopeMax && a.kv.stride % 16 == 0 && a.tok.stride % 16 == 0 && a.q.stride % 16 == 0 &&
+         a.out.stride % 16 == 0;
+}
+
+template <bool SPLIT>
+static void launch_attend_mfma_kernel(const AttendArgs& a, float* ws_o, float* ws_ml, int n_hg, int mc, int C,
+                                      int64_t n_log, hipStream_t stream) {
+  const int64_t n_phys = (n_log + 7) / 8 * 8;
+  if (a.kv.dtype == DT_KV_SPLIT)
+    hipLaunchKernelGGL((attend_mfma_kernel<SPLIT, true>), dim3((unsigned)n_phys), dim3(256), 0, stream, a, ws_o, ws_ml,
+                       n_hg, mc, C, (int)n_log);
+  else
+    hipLaunchKernelGGL((attend_mfma_kernel<SPLIT, false>), dim3((unsigned)n_phys), dim3(256), 0, stream, a, ws_o,
+                       ws_ml, n_hg, mc, C, (int)n_log);
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -488,19 +683,14 @@ hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hi
   if (split) {
     float* ws_o = reinterpret_cast<float*>(ws);
     float* ws_ml = ws_o + (size_t)a.S.total_q * mc * a.n_h * kDM;
-    const int64_t n_log = single * mc;
-    const int64_t n_phys = (n_log + 7) / 8 * 8;
-    hipLaunchKernelGGL(attend_mfma_kernel<true>, dim3((unsigned)n_phys), dim3(256), 0, stream, a, ws_o, ws_ml, n_hg,
-                       (int)mc, C, (int)n_log);
+    launch_attend_mfma_kernel<true>(a, ws_o, ws_ml, n_hg, (int)mc, C, single * mc, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_h4 = (a.n_h + 3) / 4;
     hipLaunchKernelGGL(attend_combine_mfma_kernel, dim3((unsigned)(a.S.total_q * n_h4)), dim3(256), 0, stream, a,
                        ws_o, ws_ml, (int)mc, C);
   } else {
-    const int64_t n_phys = (single + 7) / 8 * 8;
-    hipLaunchKernelGGL(attend_mfma_kernel<false>, dim3((unsigned)n_phys), dim3(256), 0, stream, a, nullptr, nullptr,
-                       n_hg, 1, C, (int)single);
+    launch_attend_mfma_kernel<false>(a, nullptr, nullptr, n_hg, 1, C, single, stream);
   }
   return hipGetLastError();
 }

@@ -287,6 +287,7 @@ ATTEND_CASES = [
     (ops.BF16, 512, 64, False, 128, 0, 128),
     (ops.BF16, 512, 16, True, 4, 100, 0),
     (ops.KV_SPLIT, 512, 64, True, 4, 256, 128),
+    (ops.KV_SPLIT, 512, 64, False, 128, 0, 128),
 ]
 
 
@@ -315,7 +316,7 @@ def test_attend_matches_oracle(case):
     assert_close(lse.cpu().numpy(), ref_l, tol, "attend lse")
 
 
-@pytest.mark.parametrize("fmt,D,n_h", [(ops.F32, 128, 8), (ops.BF16, 512, 64)])
+@pytest.mark.parametrize("fmt,D,n_h", [(ops.F32, 128, 8), (ops.BF16, 512, 64), (ops.KV_SPLIT, 512, 64)])
 def test_attend_split_and_single_modes_bit_identical(fmt, D, n_h):
     """With a workspace the key lists are spread over workgroups per chunk; without, one
     workgroup walks them.  The outputs must agree bit for bit."""

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from long_context_attention_07_amd import ops
+from long_context_attention_07_amd import ops, synth
 from oracle import formats as F
 from oracle import pipeline as P
 from oracle.attention import attend_token
@@ -252,12 +252,19 @@ def test_topk_exact_on_identical_scores():
 # ----------------------------------------------------------------------------- attention
 
 
-def _attend_inputs(g, fmt, D, n_h, n_q, ctx, ratio, k, n_win, tok_hist=None, sink_scale=1.0):
+def _attend_inputs(g, fmt, D, n_h, n_q, ctx, ratio, k, n_win, tok_hist=None, sink_scale=1.0, outliers=False):
+    """Seeded attention inputs; with `outliers`, +-20 values at rate 1e-3 in q and the rows
+    (they make the logits sensitive to how rotated dims and scaled codes are rounded)."""
     ob, sq, n_ent, n_tok = make_batch(n_q, ctx, ratio, tok_hist=tok_hist)
     qf = ops.F32 if fmt == ops.F32 else ops.BF16
-    q_rows, q_val = _rows_in(qf, g.standard_normal((sq.total_q * n_h, D)))
-    kv_rows, kv_val = _rows_in(fmt, g.standard_normal((max(n_ent, 1), D)))
-    tok_rows, tok_val = _rows_in(fmt, g.standard_normal((max(n_tok, 1), D)))
+
+    def draw(shape):
+        x = g.standard_normal(shape)
+        return x + synth.outlier_mask(g, shape) if outliers else x
+
+    q_rows, q_val = _rows_in(qf, draw((sq.total_q * n_h, D)))
+    kv_rows, kv_val = _rows_in(fmt, draw((max(n_ent, 1), D)))
+    tok_rows, tok_val = _rows_in(fmt, draw((max(n_tok, 1), D)))
     sink_t, sink_val = f32(g.standard_normal(n_h) * sink_scale)
     idx = np.full((sq.total_q, max(k, 1)), -1, dtype=np.int32)
     for row, b, p in ob.tokens():
@@ -288,17 +295,23 @@ ATTEND_CASES = [
     (ops.BF16, 512, 16, True, 4, 100, 0),
     (ops.KV_SPLIT, 512, 64, True, 4, 256, 128),
     (ops.KV_SPLIT, 512, 64, False, 128, 0, 128),
+    # (..., outliers)
+    (ops.BF16, 512, 64, True, 4, 512, 128, True),
+    (ops.KV_SPLIT, 512, 64, True, 4, 1024, 128, True),
 ]
 
 
 @pytest.mark.parametrize("case", ATTEND_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_attend_matches_oracle(case):
-    fmt, D, n_h, csa, ratio, k, n_win = case
+    fmt, D, n_h, csa, ratio, k, n_win = case[:7]
+    outliers = len(case) > 7 and case[7]
     log(f"attend case {case}")
-    g = np.random.default_rng(33 + D + n_h + ratio + k)
+    g = np.random.default_rng(33 + D + n_h + ratio + k + outliers)
     n_q = [5, 1, 1, 3, 0, 2]
     ctx = [5, 3000 * ratio // 4, 129, 900 * ratio // 4, 10, 2 * ratio + 1]
-    data = _attend_inputs(g, fmt, D, n_h, n_q, ctx, ratio, k, n_win, tok_hist=n_win + 3)
+    if outliers:
+        n_q, ctx = [3, 4, 2], [4093, 2000, 900]
+    data = _attend_inputs(g, fmt, D, n_h, n_q, ctx, ratio, k, n_win, tok_hist=n_win + 3, outliers=outliers)
     ob, sq, q_rows, q_val, kv_rows, kv_val, tok_rows, tok_val, sink_t, sink_val, idx = data
     scale = 1.0 / math.sqrt(D)
     out = empty_rows(sq.total_q * n_h, D, ops.F32 if fmt == ops.F32 else ops.BF16)

@@ -191,9 +191,17 @@ __device__ __forceinline__ SlotRef resolve_slot_lds(const AttendArgs& a, const T
   return r;
 }
 
+// Rows of the wave's 16 slots s0 + 16w .. +15: lane i < 16 resolves slot i and forms the
+// byte address of its row (and, for fp8 rows, of its scales) once, in vector registers.
+struct TileAddr {
+  uint64_t row;  // lanes 0..15: address of the slot's row
+  uint64_t sc;   // lanes 0..15: address of the row's block scales (fp8 rows)
+};
+
 template <bool KVF>
-__device__ __forceinline__ void load_tile(const AttendArgs& a, const TokenCtx& ctx, int64_t n_ent, int64_t s0,
-                                          int w, int lane, TileStage& st, const int32_t* sidx, int64_t s_lo) {
+__device__ __forceinline__ TileAddr resolve_tile(const AttendArgs& a, const TokenCtx& ctx, int64_t n_ent,
+                                                 int64_t s0, int w, int lane, TileStage& st, const int32_t* sidx,
+                                                 int64_t s_lo) {
   SlotRef r;
   r.kind = 0;
   r.row = 0;
@@ -202,34 +210,54 @@ __device__ __forceinline__ void load_tile(const AttendArgs& a, const TokenCtx& c
   st.valid = (uint32_t)__ballot(lane < 16 && r.kind != 0);
   st.win = (uint32_t)__ballot(lane < 16 && r.kind == 2);
   st.pos0 = ctx.p - a.n_win + 1 + (s0 + 16 * w - n_ent);
-  const int row_lo = (int)(uint32_t)(r.row & 0xffffffffu);
-  const int row_hi = (int)(uint32_t)((uint64_t)r.row >> 32);
-  const uint8_t* kvp = a.kv.data;
-  const uint8_t* tokp = a.tok.data;
-  const int64_t kvs = a.kv.stride, toks = a.tok.stride;
-  const float* kvsc = reinterpret_cast<const float*>(a.kv.scales);
-  const float* toksc = reinterpret_cast<const float*>(a.tok.scales);
+  const bool win = r.kind == 2;
   constexpr int nb = (kDM - kSplitBf16Dims + kKvBlock - 1) / kKvBlock;
+  TileAddr ad;
+  ad.row = reinterpret_cast<uint64_t>(win ? a.tok.data : a.kv.data) + (uint64_t)(r.row * (win ? a.tok.stride : a.kv.stride));
+  ad.sc = KVF ? reinterpret_cast<uint64_t>(win ? a.tok.scales : a.kv.scales) + (uint64_t)(r.row * nb * 4) : 0u;
+  return ad;
+}
+
+// Loads of the wave's rows IT0 .. IT1-1: per row two lane reads give the row's address as
+// a scalar base, and each lane loads its 16 bytes (the tile's loads are issued in two
+// halves between the compute phases).
+// Loads through a uniform 64-bit global address (scalar base plus the lane's offset).
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4_t;
+__device__ __forceinline__ uint4 load_global_u4(uint64_t base, int i) {
+  const u32x4_t r = ((const __attribute__((address_space(1))) u32x4_t*)base)[i];
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+__device__ __forceinline__ float load_global_f32(uint64_t base, int i) {
+  return ((const __attribute__((address_space(1))) float*)base)[i];
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int i) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), i) << 32) |
+         (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, i);
+}
+
+template <bool KVF, int IT0, int IT1>
+__device__ __forceinline__ void issue_tile(int lane, TileStage& st, const TileAddr& ad) {
 #pragma unroll
-  for (int it = 0; it < 16; ++it) {
+  for (int it = IT0; it < IT1; ++it) {
     st.v[it] = make_uint4(0u, 0u, 0u, 0u);
     st.sc[it] = 0.f;
     if ((st.valid >> it) & 1u) {
-      const int64_t row = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_hi, it) << 32) |
-                                    (uint64_t)(uint32_t)__builtin_amdgcn_readlane(row_lo, it));
-      // the row address stays scalar (uniform row index, pool base and stride from the
-      // kernel arguments): one SGPR base plus the lane offset per load
-      const bool win = (st.win >> it) & 1u;
-      const uint8_t* base = win ? tokp : kvp;
-      const int64_t stride = win ? toks : kvs;
+      const uint64_t rowp = readlane_u64(ad.row, it);
       if (!KVF) {
-        st.v[it] = reinterpret_cast<const uint4*>(base + row * stride)[lane];
+        st.v[it] = load_global_u4(rowp, lane);
       } else {
-        if (lane < kSplitLanes) st.v[it] = reinterpret_cast<const uint4*>(base + row * stride)[lane];
-        if (lane < kSplitCodeLanes && (lane & 7) == 0) st.sc[it] = (win ? toksc : kvsc)[row * nb + (lane >> 3)];
+        if (lane < kSplitLanes) st.v[it] = load_global_u4(rowp, lane);
+        if (lane < kSplitCodeLanes && (lane & 7) == 0) st.sc[it] = load_global_f32(readlane_u64(ad.sc, it), lane >> 3);
       }
     }
   }
+}
+
+template <bool KVF>
+__device__ __forceinline__ void load_tile(const AttendArgs& a, const TokenCtx& ctx, int64_t n_ent, int64_t s0,
+                                          int w, int lane, TileStage& st, const int32_t* sidx, int64_t s_lo) {
+  const TileAddr ad = resolve_tile<KVF>(a, ctx, n_ent, s0, w, lane, st, sidx, s_lo);
+  issue_tile<KVF, 0, 16>(lane, st, ad);
 }
 
 // Stage the wave's 16 rows in LDS in the tile format.  fp8 rows are staged as their e4m3
@@ -272,16 +300,19 @@ __device__ __forceinline__ void store_tile(MfmaLds& L, const AttendArgs& a, cons
     // pair `lane` of the last 64 dims; rotary pairs start at dim kDM - rope.dims
     const int d = kDM - kRopeMax + 2 * lane;
     const int dn = kDM - a.rope.dims;
+    uint32_t u[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) u[it] = *reinterpret_cast<const uint32_t*>(&L.k[(16 * w + it) * kKStride + d * 2]);
+#pragma unroll
     for (int it = 0; it < 16; ++it) {
       uint32_t res = 0u;
       if (((st.win >> it) & 1u) && d >= dn) {
-        uint32_t* pp = reinterpret_cast<uint32_t*>(&L.k[(16 * w + it) * kKStride + d * 2]);
         float c, s;
         rope_cs_mode<ROPE_FAST>(st.pos0 + it, F, (d - dn) >> 1, &c, &s);
-        const float2 y = rotate2(unpack16<KVF>(*pp), c, s);
+        const float2 y = rotate2(unpack16<KVF>(u[it]), c, s);
         const uint32_t hi = pack16<KVF>(y.x, y.y);
         const float2 yh = unpack16<KVF>(hi);
-        *pp = hi;
+        *reinterpret_cast<uint32_t*>(&L.k[(16 * w + it) * kKStride + d * 2]) = hi;
         res = pack16<KVF>(y.x - yh.x, y.y - yh.y);
       }
       *reinterpret_cast<uint32_t*>(&L.klo[(16 * w + it) * kLoStride + 4 * lane]) = res;
@@ -311,28 +342,61 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
   }
   const int t = rest;
 
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int dn = kDM - a.rope.dims;
+
+  // The query block (16 heads x 1 KiB) and the chunk's first entry ids depend only on the
+  // token, so they are requested before the token's context is resolved: the latencies
+  // overlap.  Each thread loads 64 bytes of the query block once for all four waves.
+  uint4 qv[4];
+  {
+    const int h = hg * kHG + (tid >> 4);
+    const uint8_t* qrow = a.q.data + ((int64_t)t * a.n_h + (h < a.n_h ? h : 0)) * a.q.stride + 64 * (tid & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      qv[i] = h < a.n_h ? reinterpret_cast<const uint4*>(qrow)[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const int c_begin = SPLIT ? c_only : 0;
+  const int64_t s_lo = (int64_t)c_begin * chunk_slots;
+  constexpr int kEarlyIds = 2;  // entry ids per thread requested up front
+  int32_t iv[kEarlyIds];
+  int64_t s_hi = 0;
+  if (a.csa) {
+    // CSA: the key list has k entry slots whatever the context
+    const int n_chunks_csa = (int)(((int64_t)a.k + a.n_win + chunk_slots - 1) / chunk_slots);
+    s_hi = min((int64_t)(SPLIT ? c_only + 1 : n_chunks_csa) * chunk_slots, (int64_t)a.k);
+    const int32_t* src = a.idx + (int64_t)t * a.k;
+#pragma unroll
+    for (int i = 0; i < kEarlyIds; ++i) {
+      const int64_t s = s_lo + tid + 256 * i;
+      iv[i] = s < s_hi ? src[s] : -1;
+    }
+  }
+  load_freqs(F, a.rope);
+
   const TokenCtx ctx = token_ctx(a.S, t);
   const int64_t n_ent = entry_slots(a, ctx);
   const int64_t n_slots = n_ent + a.n_win;
   const int n_chunks = (int)((n_slots + chunk_slots - 1) / chunk_slots);
   if (SPLIT && c_only >= n_chunks) return;
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int dn = kDM - a.rope.dims;
-  load_freqs(F, a.rope);
-  const int c_begin = SPLIT ? c_only : 0;
   const int c_end = SPLIT ? c_only + 1 : n_chunks;
-  const int64_t s_lo = (int64_t)c_begin * chunk_slots;
+
   if (a.csa) {
-    const int64_t s_hi = min((int64_t)c_end * chunk_slots, n_ent);
+#pragma unroll
+    for (int i = 0; i < kEarlyIds; ++i) {
+      const int64_t s = s_lo + tid + 256 * i;
+      if (s < s_hi) L.sidx[s - s_lo] = iv[i];
+    }
     const int32_t* src = a.idx + (int64_t)t * a.k;
-    for (int64_t s = s_lo + tid; s < s_hi; s += 256) L.sidx[s - s_lo] = src[s];
+    for (int64_t s = s_lo + tid + 256 * kEarlyIds; s < s_hi; s += 256) L.sidx[s - s_lo] = src[s];
   }
+  // query block staged in the (still free) key tile: head r at row r
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&L.k[(tid >> 4) * kKStride + 64 * (tid & 15) + 16 * i]) = qv[i];
   __syncthreads();
 
-  // first tile's rows are requested before the query rows, so the two latencies overlap
   TileStage st;
   load_tile<KVF>(a, ctx, n_ent, s_lo, w, lane, st, L.sidx, s_lo);
 
@@ -340,16 +404,9 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
   uint4 qf[16];  // in the tile format
   uint4 qlo[2];  // rounding residuals of the rotated dims among 448..511 (zero elsewhere)
   {
-    const int h = hg * kHG + c16;
     uint4 raw[16];
-    if (h < a.n_h) {
-      const uint8_t* qrow = a.q.data + ((int64_t)t * a.n_h + h) * a.q.stride;
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) raw[kk] = *reinterpret_cast<const uint4*>(qrow + (8 * g + 32 * kk) * 2);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) raw[kk] = make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int kk = 0; kk < 16; ++kk) raw[kk] = *reinterpret_cast<const uint4*>(&L.k[c16 * kKStride + (8 * g + 32 * kk) * 2]);
     // rotary dims lie within the last 64 (dn >= 448): only chunks 14 and 15 can hold them
 #pragma unroll
     for (int kk = 0; kk < 14; ++kk) qf[kk] = from_bf16<KVF>(raw[kk]);
@@ -400,8 +457,11 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
       ntl = 0;
     }
     const bool has_next = ncc < c_end;
-    if (has_next)
-      load_tile<KVF>(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, w, lane, st, L.sidx, s_lo);
+    TileAddr nad = {0u, 0u};
+    if (has_next) {
+      nad = resolve_tile<KVF>(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, w, lane, st, L.sidx, s_lo);
+      issue_tile<KVF, 0, 8>(lane, st, nad);
+    }
 
     // ---- S^T = K Q^T for keys 16w..16w+15.  Partial products per 128-dim block: for fp8
     // rows blocks 0..3 hold the code products (scaled below), block 4 the bf16 tail.  The
@@ -412,12 +472,14 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
     for (int b = 0; b < 5; ++b) part[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     {
       const uint8_t* krow = &L.k[(16 * w + c16) * kKStride + 16 * g];
+      uint4 ka[16];
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) ka[kk] = *reinterpret_cast<const uint4*>(krow + 64 * kk);
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk) {
         const int b = KVF ? (kk < 14 ? kk / 4 : 4) : 0;
-        const uint4 ka = *reinterpret_cast<const uint4*>(krow + 64 * kk);
-        part[b] = mfma16<KVF>(ka, qf[kk], part[b]);
-        if (kk >= 14) part[KVF ? 4 : 0] = mfma16<KVF>(ka, qlo[kk - 14], part[KVF ? 4 : 0]);
+        part[b] = mfma16<KVF>(ka[kk], qf[kk], part[b]);
+        if (kk >= 14) part[KVF ? 4 : 0] = mfma16<KVF>(ka[kk], qlo[kk - 14], part[KVF ? 4 : 0]);
       }
       if (winm != 0u) {
         const uint8_t* lrow = &L.klo[(16 * w + c16) * kLoStride + 16 * g];
@@ -480,6 +542,8 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
     l_run = __builtin_fmaf(l_run, alpha, tsum);
     m_run = m_new;
 
+    if (has_next) issue_tile<KVF, 8, 16>(lane, st, nad);
+
     // ---- O[head 4g+j, dims 128w + 16nb + c16] = O * alpha + P V
     {
       float al[4];
@@ -518,6 +582,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
           pt_lo = w < 3 ? ps_lo : pa_lo;
         }
         const int r0 = key0 + (c16 >> 2);
+        uint4 vbs[8];
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
           const int n0 = 128 * w + 16 * nb + 4 * (c16 & 3);
@@ -526,7 +591,11 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + 4 * kKStride));
           typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
           const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const uint4 vb = __builtin_bit_cast(uint4, both);
+          vbs[nb] = __builtin_bit_cast(uint4, both);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const uint4 vb = vbs[nb];
           if (!KVF) {
             O[nb] = mfma16<false>(pa, vb, O[nb]);
           } else {

@@ -666,6 +666,330 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// bf16 rows, wave-pair variant: 8 waves per workgroup (two per SIMD, so one wave's LDS and
+// memory latencies overlap the other's work).  Workgroup = (token, 16 heads, chunk) as
+// above; wave pair p = w % 4 owns rows 16p..16p+15 of every 64-slot tile and runs its own
+// online softmax over them; the two waves of a pair (half h2 = w / 4) each load and stage
+// 8 of the pair's rows, each computes the partial logits S^T of half the dims (the halves
+// are exchanged through LDS and added in a fixed order, so both hold the same logits), and
+// each accumulates half of the output dims, transposed: O^T[dim, head] += V^T P^T with
+// v_mfma_f32_16x16x16_bf16, whose B operand (P^T, 4 keys x 1 head per lane) is the logit
+// accumulator layout itself and whose A operand (V^T, 4 keys of one dim per lane) is one
+// ds_read_b64_tr_b16 of the staged rows.  The four pair states of a chunk are merged in a
+// fixed order (pair 0..3) through LDS.  A pair raises its running max only when a tile's
+// max exceeds it by more than 8 (log2 units): P stays below 2^8 and O is rescaled only
+// then.
+constexpr float kMaxSlack = 8.0f;
+constexpr int kMergeStride = 260;  // floats per head row of the merge scratch (256 dims + pad)
+
+// Stage rows roff .. roff+7 of the pair's 16 (held in st.v[0..7]), then rotate the window
+// rows among them and write the rotation residuals of those rows.
+__device__ __forceinline__ void store_rows8(MfmaLds& L, const AttendArgs& a, const TileStage& st, int p, int roff,
+                                            int lane, const FreqLds& F) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&L.k[(16 * p + roff + i) * kKStride + 16 * lane]) = st.v[i];
+  if (st.win != 0u && lane < kRopeMax / 2) {
+    const int d = kDM - kRopeMax + 2 * lane;
+    const int dn = kDM - a.rope.dims;
+    uint32_t u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = *reinterpret_cast<const uint32_t*>(&L.k[(16 * p + roff + i) * kKStride + d * 2]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int it = roff + i;
+      uint32_t res = 0u;
+      if (((st.win >> it) & 1u) && d >= dn) {
+        float c, s;
+        rope_cs_mode<ROPE_FAST>(st.pos0 + it, F, (d - dn) >> 1, &c, &s);
+        const float2 y = rotate2(unpack16<false>(u[i]), c, s);
+        const uint32_t hi = pack16<false>(y.x, y.y);
+        const float2 yh = unpack16<false>(hi);
+        *reinterpret_cast<uint32_t*>(&L.k[(16 * p + it) * kKStride + d * 2]) = hi;
+        res = pack16<false>(y.x - yh.x, y.y - yh.y);
+      }
+      *reinterpret_cast<uint32_t*>(&L.klo[(16 * p + it) * kLoStride + 4 * lane]) = res;
+    }
+  }
+}
+
+// Loads of rows roff .. roff+7 of the pair's 16 into st.v[0..7].
+__device__ __forceinline__ void issue_rows8(int lane, TileStage& st, const TileAddr& ad, int roff) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    st.v[i] = make_uint4(0u, 0u, 0u, 0u);
+    if ((st.valid >> (roff + i)) & 1u) st.v[i] = load_global_u4(readlane_u64(ad.row, roff + i), lane);
+  }
+}
+
+template <bool SPLIT>
+__global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* __restrict__ ws_o,
+                                                          float* __restrict__ ws_ml, int n_hg, int max_chunks,
+                                                          int chunk_slots, int n_logical) {
+  __shared__ MfmaLds L;
+  __shared__ FreqLds F;
+  __shared__ f32x4_t sx[8][64];  // partial logits of each wave
+  const int n_phys = gridDim.x;
+  const int per_xcd = n_phys / 8;
+  const int lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (lid >= n_logical) return;
+  int rest = lid;
+  const int hg = rest % n_hg;
+  rest /= n_hg;
+  int c_only = 0;
+  if (SPLIT) {
+    c_only = rest % max_chunks;
+    rest /= max_chunks;
+  }
+  const int t = rest;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int p = w & 3, h2 = w >> 2, roff = 8 * h2;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int dn = kDM - a.rope.dims;
+
+  // query block (16 heads x 1 KiB): 32 bytes per thread; chunk's first entry ids
+  uint4 qv[2];
+  {
+    const int h = hg * kHG + (tid >> 5);
+    const uint8_t* qrow = a.q.data + ((int64_t)t * a.n_h + (h < a.n_h ? h : 0)) * a.q.stride + 32 * (tid & 31);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      qv[i] = h < a.n_h ? reinterpret_cast<const uint4*>(qrow)[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const int c_begin = SPLIT ? c_only : 0;
+  const int64_t s_lo = (int64_t)c_begin * chunk_slots;
+  int32_t iv = -1;
+  int64_t s_hi = 0;
+  if (a.csa) {
+    const int n_chunks_csa = (int)(((int64_t)a.k + a.n_win + chunk_slots - 1) / chunk_slots);
+    s_hi = min((int64_t)(SPLIT ? c_only + 1 : n_chunks_csa) * chunk_slots, (int64_t)a.k);
+    if (s_lo + tid < s_hi) iv = a.idx[(int64_t)t * a.k + s_lo + tid];
+  }
+  load_freqs(F, a.rope);
+
+  const TokenCtx ctx = token_ctx(a.S, t);
+  const int64_t n_ent = entry_slots(a, ctx);
+  const int64_t n_slots = n_ent + a.n_win;
+  const int n_chunks = (int)((n_slots + chunk_slots - 1) / chunk_slots);
+  if (SPLIT && c_only >= n_chunks) return;
+  const int c_end = SPLIT ? c_only + 1 : n_chunks;
+
+  if (a.csa) {
+    if (s_lo + tid < s_hi) L.sidx[tid] = iv;
+    const int32_t* src = a.idx + (int64_t)t * a.k;
+    for (int64_t s = s_lo + tid + 512; s < s_hi; s += 512) L.sidx[s - s_lo] = src[s];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(&L.k[(tid >> 5) * kKStride + 32 * (tid & 31) + 16 * i]) = qv[i];
+  __syncthreads();
+
+  TileStage st;
+  {
+    const TileAddr ad = resolve_tile<false>(a, ctx, n_ent, s_lo, p, lane, st, L.sidx, s_lo);
+    issue_rows8(lane, st, ad, roff);
+  }
+
+  // query fragments of this wave's half of the dims: chunks kk = 8 h2 + i
+  uint4 qf[8];
+  uint4 qlo[2];  // half 1: residuals of the rotated dims among 448..511
+  {
+    const uint8_t* qrow = &L.k[c16 * kKStride + (8 * g + 256 * h2) * 2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qf[i] = *reinterpret_cast<const uint4*>(qrow + 64 * i);
+    qlo[0] = qlo[1] = make_uint4(0u, 0u, 0u, 0u);
+    if (h2 == 1) {
+#pragma unroll
+      for (int i = 6; i < 8; ++i) {
+        const int d0 = 8 * g + 256 + 32 * i;
+        if (d0 >= dn) rotate_chunk<false>(qf[i], ctx.p, F, (d0 - dn) >> 1, &qf[i], &qlo[i - 6]);
+      }
+    }
+  }
+
+  // merge layout: thread (head th, dims 8 td + 256 r + i)
+  const int th = tid >> 5, td = tid & 31;
+  const int h_m = hg * kHG + th;
+  FoldState fs = fold_init(h_m < a.n_h ? a.sink[h_m] * kLog2e : -INFINITY);
+  float Ot[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) Ot[i] = 0.f;
+  f32x4_t OT[16];  // O^T[dim 256 h2 + 16nb + 4g + j, head c16]
+#pragma unroll
+  for (int nb = 0; nb < 16; ++nb) OT[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto tiles_in = [&](int c) -> int {
+    const int64_t rem = n_slots - (int64_t)c * chunk_slots;
+    const int64_t len = rem < chunk_slots ? rem : chunk_slots;
+    return (int)((len + kT - 1) / kT);
+  };
+  int cc = c_begin, tile = 0, ntile = tiles_in(cc);
+
+  while (true) {
+    lds_barrier();  // the pair's previous rows (and the query block) fully consumed
+    store_rows8(L, a, st, p, roff, lane, F);
+    const uint32_t valid = st.valid, winm = st.win;
+    lds_barrier();  // the pair's 16 rows staged
+
+    int ncc = cc, ntl = tile + 1;
+    if (ntl == ntile) {
+      ncc = cc + 1;
+      ntl = 0;
+    }
+    const bool has_next = ncc < c_end;
+    if (has_next) {
+      const TileAddr nad =
+          resolve_tile<false>(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, p, lane, st, L.sidx, s_lo);
+      issue_rows8(lane, st, nad, roff);
+    }
+
+    // ---- S^T = K Q^T for the pair's keys: this wave's half of the dims, then the
+    // halves exchanged and added (half 0 + half 1)
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint8_t* krow = &L.k[(16 * p + c16) * kKStride + (16 * g + 512 * h2)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(krow + 64 * i);
+        acc = mfma16<false>(ka, qf[i], acc);
+        if (i >= 6 && h2 == 1) acc = mfma16<false>(ka, qlo[i - 6], acc);
+      }
+      if (winm != 0u && h2 == 1) {
+        const uint8_t* lrow = &L.klo[(16 * p + c16) * kLoStride + 16 * g];
+#pragma unroll
+        for (int i = 6; i < 8; ++i) {
+          const uint4 kl = *reinterpret_cast<const uint4*>(lrow + 64 * (i - 6));
+          acc = mfma16<false>(kl, qf[i], acc);
+        }
+      }
+    }
+    sx[w][lane] = acc;
+    lds_barrier();
+    {
+      const f32x4_t other = sx[w ^ 4][lane];
+      acc = h2 == 0 ? acc + other : other + acc;
+    }
+
+    // ---- online softmax of head c16 over the pair's 16 keys
+    float sv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sv[j] = ((valid >> (4 * g + j)) & 1u) ? acc[j] * a.scale_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = (mx > m_run + kMaxSlack) ? mx : m_run;
+    const float alpha = rescale(m_run, m_new);
+    uint32_t pb[4];
+    float ls = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float pj = (sv[j] == -INFINITY) ? 0.f : ex2(sv[j] - m_new);
+      pb[j] = f32_to_bf16_bits(pj);
+      ls += __uint_as_float(pb[j] << 16);
+    }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    l_run = __builtin_fmaf(l_run, alpha, ls);
+    m_run = m_new;
+
+    // ---- O^T[dim, head] = O^T * alpha + V^T P^T over this wave's 256 dims
+    if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb) OT[nb] *= alpha;
+    }
+    {
+      const i16x4_t pv = __builtin_bit_cast(i16x4_t, make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)));
+      uint8_t* vbase = &L.k[(16 * p + 4 * g + (c16 >> 2)) * kKStride + (256 * h2 + 4 * (c16 & 3)) * 2];
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb) {
+        const i16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vbase + 32 * nb));
+        OT[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pv, OT[nb], 0, 0, 0);
+      }
+    }
+
+    if (tile + 1 == ntile) {
+      // ---- chunk done: merge the four pair states in pair order
+      if (h2 == 0 && lane < 16) {
+        L.red_max[p][c16] = m_run;
+        L.red_sum[p][c16] = l_run;
+      }
+      lds_barrier();
+      // head th: merged max, the pairs' factors and the merged sum (same in every thread)
+      const float Mh = fmaxf(fmaxf(L.red_max[0][th], L.red_max[1][th]), fmaxf(L.red_max[2][th], L.red_max[3][th]));
+      float fp[4];
+      float lh = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        fp[pp] = rescale(L.red_max[pp][th], Mh);
+        lh = __builtin_fmaf(L.red_sum[pp][th], fp[pp], lh);
+      }
+      float fa = 0.f, fb = 0.f;
+      if (!SPLIT) fold_step(fs, Mh, lh, &fa, &fb);
+      const int64_t base = ((int64_t)t * max_chunks + cc) * a.n_h + h_m;
+      if (SPLIT && td == 0 && h_m < a.n_h) {
+        ws_ml[2 * base] = Mh;
+        ws_ml[2 * base + 1] = lh;
+      }
+      float* scratch = reinterpret_cast<float*>(L.k);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (h2 == r) {
+#pragma unroll
+          for (int nb = 0; nb < 16; ++nb)
+            *reinterpret_cast<f32x4_t*>(&scratch[(p * kHG + c16) * kMergeStride + 16 * nb + 4 * g]) = OT[nb];
+        }
+        lds_barrier();
+#pragma unroll
+        for (int i4 = 0; i4 < 2; ++i4) {
+          f32x4_t sum = *reinterpret_cast<const f32x4_t*>(&scratch[(0 * kHG + th) * kMergeStride + 8 * td + 4 * i4]) * fp[0];
+#pragma unroll
+          for (int pp = 1; pp < 4; ++pp) {
+            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&scratch[(pp * kHG + th) * kMergeStride + 8 * td + 4 * i4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum[e] = __builtin_fmaf(v[e], fp[pp], sum[e]);
+          }
+          if (SPLIT) {
+            if (h_m < a.n_h)
+              *reinterpret_cast<float4*>(ws_o + base * kDM + 256 * r + 8 * td + 4 * i4) =
+                  make_float4(sum[0], sum[1], sum[2], sum[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float& o = Ot[8 * r + 4 * i4 + e];
+              o = __builtin_fmaf(o, fa, sum[e] * fb);
+            }
+          }
+        }
+        lds_barrier();
+      }
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb) OT[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m_run = -INFINITY;
+      l_run = 0.f;
+    }
+    if (!has_next) break;
+    if (ntl == 0) ntile = tiles_in(ncc);
+    cc = ncc;
+    tile = ntl;
+  }
+
+  if (!SPLIT && h_m < a.n_h) {
+    const float inv = (fs.Z > 0.f) ? 1.0f / fs.Z : 0.f;
+    const int64_t orow = (int64_t)t * a.n_h + h_m;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = Ot[8 * r + i] * inv;
+      const int d0 = 256 * r + 8 * td;
+      *reinterpret_cast<uint4*>(a.out.data + orow * a.out.stride + d0 * 2) = finalize8(x, d0, dn, ctx.p, F);
+    }
+    if (a.lse && td == 0) a.lse[orow] = lse_natural(fs);
+  }
+}
+
 // Fold of the chunk partials written by the split launch, in chunk order from the sink:
 // one wave per head, each lane 8 consecutive dims; same arithmetic as the single launch.
 __global__ void __launch_bounds__(256) attend_combine_mfma_kernel(AttendArgs a, const float* __restrict__ ws_o,
@@ -738,8 +1062,8 @@ static void launch_attend_mfma_kernel(const AttendArgs& a, float* ws_o, float* w
     hipLaunchKernelGGL((attend_mfma_kernel<SPLIT, true>), dim3((unsigned)n_phys), dim3(256), 0, stream, a, ws_o, ws_ml,
                        n_hg, mc, C, (int)n_log);
   else
-    hipLaunchKernelGGL((attend_mfma_kernel<SPLIT, false>), dim3((unsigned)n_phys), dim3(256), 0, stream, a, ws_o,
-                       ws_ml, n_hg, mc, C, (int)n_log);
+    hipLaunchKernelGGL((attend_pair_kernel<SPLIT>), dim3((unsigned)n_phys), dim3(512), 0, stream, a, ws_o, ws_ml, n_hg,
+                       mc, C, (int)n_log);
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {

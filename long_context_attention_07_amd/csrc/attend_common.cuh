@@ -164,9 +164,9 @@ __global__ void __launch_bounds__(256) attend_combine_kernel(AttendArgs a, const
 
 // Chunk length in key slots: CSA key lists have a fixed length k + n_win, cut into
 // ceil((k + n_win) / 384) equal chunks rounded up to whole 64-key tiles; HCA lists grow
-// with the context and use 512-slot chunks.  Depends on op parameters only.
+// with the context and use 576-slot (9-tile) chunks.  Depends on op parameters only.
 __host__ __device__ inline int chunk_slots_for(int csa, int k, int n_win) {
-  if (!csa) return 512;
+  if (!csa) return 576;
   const int S = k + n_win;
   const int n = (S + 383) / 384;
   const int c = (S + n - 1) / n;

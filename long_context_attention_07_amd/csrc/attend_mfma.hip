@@ -681,7 +681,23 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
 // max exceeds it by more than 8 (log2 units): P stays below 2^8 and O is rescaled only
 // then.
 constexpr float kMaxSlack = 8.0f;
-constexpr int kMergeStride = 260;  // floats per head row of the merge scratch (256 dims + pad)
+constexpr int kMergeStride = 260;
+
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with the
+// row-swap permutes: v_permlane16_swap pairs rows (0,1) and (2,3), v_permlane32_swap the
+// two halves; every lane ends with the same value.
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}  // floats per head row of the merge scratch (256 dims + pad)
 
 // Stage rows roff .. roff+7 of the pair's 16 (held in st.v[0..7]), then rotate the window
 // rows among them and write the rotation residuals of those rows.
@@ -695,13 +711,22 @@ __device__ __forceinline__ void store_rows8(MfmaLds& L, const AttendArgs& a, con
     uint32_t u[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[i] = *reinterpret_cast<const uint32_t*>(&L.k[(16 * p + roff + i) * kKStride + d * 2]);
+    // the rows' positions are consecutive: rotate the angle of the first by one position
+    // per row (angle addition; error ~1e-6 after the 7 steps)
+    const int q = d >= dn ? (d - dn) >> 1 : 0;
+    float c, s, c1, s1;
+    rope_cs_mode<ROPE_FAST>(st.pos0 + roff, F, q, &c, &s);
+    rope_cs_mode<ROPE_FAST>(1, F, q, &c1, &s1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int it = roff + i;
       uint32_t res = 0u;
+      if (i > 0) {
+        const float cn = __builtin_fmaf(c, c1, -(s * s1));
+        s = __builtin_fmaf(s, c1, c * s1);
+        c = cn;
+      }
       if (((st.win >> it) & 1u) && d >= dn) {
-        float c, s;
-        rope_cs_mode<ROPE_FAST>(st.pos0 + it, F, (d - dn) >> 1, &c, &s);
         const float2 y = rotate2(unpack16<false>(u[i]), c, s);
         const uint32_t hi = pack16<false>(y.x, y.y);
         const float2 yh = unpack16<false>(hi);
@@ -713,10 +738,13 @@ __device__ __forceinline__ void store_rows8(MfmaLds& L, const AttendArgs& a, con
   }
 }
 
-// Loads of rows roff .. roff+7 of the pair's 16 into st.v[0..7].
-__device__ __forceinline__ void issue_rows8(int lane, TileStage& st, const TileAddr& ad, int roff) {
+// Loads of rows roff + I0 .. roff + I1 - 1 of the pair's 16 into st.v[I0 .. I1-1].  A
+// wave's loads stall at issue once the CU's memory pipeline is full, so the step issues
+// its eight in pairs between the compute phases.
+template <int I0, int I1>
+__device__ __forceinline__ void issue_rows(int lane, TileStage& st, const TileAddr& ad, int roff) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = I0; i < I1; ++i) {
     st.v[i] = make_uint4(0u, 0u, 0u, 0u);
     if ((st.valid >> (roff + i)) & 1u) st.v[i] = load_global_u4(readlane_u64(ad.row, roff + i), lane);
   }
@@ -788,7 +816,7 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
   TileStage st;
   {
     const TileAddr ad = resolve_tile<false>(a, ctx, n_ent, s_lo, p, lane, st, L.sidx, s_lo);
-    issue_rows8(lane, st, ad, roff);
+    issue_rows<0, 8>(lane, st, ad, roff);
   }
 
   // query fragments of this wave's half of the dims: chunks kk = 8 h2 + i
@@ -839,10 +867,10 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
       ntl = 0;
     }
     const bool has_next = ncc < c_end;
+    TileAddr nad = {0u, 0u};
     if (has_next) {
-      const TileAddr nad =
-          resolve_tile<false>(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, p, lane, st, L.sidx, s_lo);
-      issue_rows8(lane, st, nad, roff);
+      nad = resolve_tile<false>(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, p, lane, st, L.sidx, s_lo);
+      issue_rows<0, 2>(lane, st, nad, roff);
     }
 
     // ---- S^T = K Q^T for the pair's keys: this wave's half of the dims, then the
@@ -866,6 +894,7 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
       }
     }
     sx[w][lane] = acc;
+    if (has_next) issue_rows<2, 4>(lane, st, nad, roff);
     lds_barrier();
     {
       const f32x4_t other = sx[w ^ 4][lane];
@@ -876,9 +905,7 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
     float sv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sv[j] = ((valid >> (4 * g + j)) & 1u) ? acc[j] * a.scale_log2 : -INFINITY;
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mx = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     const float m_new = (mx > m_run + kMaxSlack) ? mx : m_run;
     const float alpha = rescale(m_run, m_new);
     uint32_t pb[4];
@@ -889,10 +916,10 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
       pb[j] = f32_to_bf16_bits(pj);
       ls += __uint_as_float(pb[j] << 16);
     }
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
+    ls = rows_sum(ls);
     l_run = __builtin_fmaf(l_run, alpha, ls);
     m_run = m_new;
+    if (has_next) issue_rows<4, 6>(lane, st, nad, roff);
 
     // ---- O^T[dim, head] = O^T * alpha + V^T P^T over this wave's 256 dims
     if (__ballot(alpha != 1.0f) != 0ull) {
@@ -908,6 +935,7 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
         OT[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pv, OT[nb], 0, 0, 0);
       }
     }
+    if (has_next) issue_rows<6, 8>(lane, st, nad, roff);
 
     if (tile + 1 == ntile) {
       // ---- chunk done: merge the four pair states in pair order

@@ -8,8 +8,9 @@
 // equal to T are still needed (each digit found by a workgroup-wide scan of the digit
 // counts); a block-wide scan then keeps every key > T and the
 // lowest-index keys == T, writing indices in ascending order.  The selection is a
-// function of the token's scores alone.  Keys are staged in LDS when they fit (up to
-// 32768 candidates, 128 KiB), otherwise every pass re-reads the scores from memory.
+// function of the token's scores alone.  Up to 32768 candidates the keys stay in
+// registers (8, 16 or 32 per thread), each pass has its own LDS histogram and the digit
+// searches use DPP wave scans; longer lists re-read the scores from memory every pass.
 
 #include "common.cuh"
 #include "kernels.h"
@@ -17,7 +18,6 @@
 namespace csa {
 
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkStage = 32768;
 
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -59,15 +59,7 @@ __device__ __forceinline__ uint2 block_excl_scan2(uint2 v, uint32_t* red, uint2*
   return make_uint2(base.x + x.x - v.x, base.y + x.y - v.y);
 }
 
-template <bool STAGED>
-__device__ __forceinline__ uint32_t key_at(const uint32_t* lds, const float* src, int64_t i) {
-  if (STAGED) return lds[i];
-  return score_key(src[i]);
-}
-
 constexpr int kHistBins = 4096;
-static_assert((kTopkStage / kTopkThreads) * (kTopkThreads / 64) <= 512 && 1024 <= kHistBins,
-              "per-(chunk, wave) counts of the staged compaction fit in the histogram");
 
 struct TopkLds {
   uint32_t hist[kHistBins];
@@ -75,28 +67,13 @@ struct TopkLds {
   uint32_t digit, above;
 };
 
-template <bool STAGED>
-__device__ void topk_select(const float* __restrict__ src, int n, int k, int32_t* __restrict__ out, uint32_t* lds,
-                            TopkLds& sh) {
+// Selection for key lists longer than the register path takes: every pass re-reads the
+// scores from memory; contiguous segments per thread for the compaction.
+__device__ void topk_select_mem(const float* __restrict__ src, int n, int k, int32_t* __restrict__ out,
+                                TopkLds& sh) {
   uint32_t* hist = sh.hist;
   uint32_t* red = sh.red;
   const int tid = threadIdx.x;
-  if (STAGED) {
-    // 8 loads in flight per thread before the LDS stores
-    for (int i0 = tid; i0 < n; i0 += 8 * kTopkThreads) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kTopkThreads;
-        v[u] = (i < n) ? src[i] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kTopkThreads;
-        if (i < n) lds[i] = score_key(v[u]);
-      }
-    }
-  }
   uint32_t prefix = 0, mask = 0, remaining = (uint32_t)k;
   const int shifts[3] = {20, 8, 0};
   const int widths[3] = {12, 12, 8};
@@ -108,14 +85,13 @@ __device__ void topk_select(const float* __restrict__ src, int n, int k, int32_t
     for (int b = tid; b < nbins; b += kTopkThreads) hist[b] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kTopkThreads) {
-      const uint32_t key = key_at<STAGED>(lds, src, i);
+      const uint32_t key = score_key(src[i]);
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
     {
-      // digit search over the whole workgroup: thread tid owns `per` consecutive digits,
-      // counted from the top digit down, so an exclusive scan over threads gives the number
-      // of keys above each thread's digits
+      // thread tid owns `per` consecutive digits counted from the top digit down, so an
+      // exclusive scan over threads gives the number of keys above each thread's digits
       const int per = nbins >= kTopkThreads ? nbins / kTopkThreads : 1;
       const int owners = nbins / per;
       const int d_hi = nbins - tid * per;  // digits [d_hi - per, d_hi)
@@ -145,67 +121,20 @@ __device__ void topk_select(const float* __restrict__ src, int n, int k, int32_t
   }
   // prefix is the k-th largest key T; `remaining` keys equal to T are taken, lowest index first.
   const uint32_t T = prefix;
-  if (STAGED) {
-    // Keys staged in LDS (n <= 32768, at most 32 chunks of 1024): thread tid handles index
-    // 1024j + tid of chunk j (conflict-free LDS reads).  Per (chunk, wave) the counts of keys
-    // > T and == T are ballot popcounts; one scan over the (chunk, wave) counts in index
-    // order then gives every kept key its output slot.
-    const int lane = tid & 63, wv = tid >> 6;
-    const int n_chunks = (n + kTopkThreads - 1) / kTopkThreads;
-    uint32_t* cg = sh.hist;         // [chunk * 16 + wave], reused: the passes are done
-    uint32_t* ce = sh.hist + 512;
-    for (int j = 0; j < n_chunks; ++j) {
-      const int i = j * kTopkThreads + tid;
-      const uint32_t key = i < n ? lds[i] : 0u;
-      const uint64_t mg = __ballot(i < n && key > T);
-      const uint64_t me = __ballot(i < n && key == T);
-      if (lane == 0) {
-        cg[j * 16 + wv] = (uint32_t)__popcll(mg);
-        ce[j * 16 + wv] = (uint32_t)__popcll(me);
-      }
-    }
-    for (int x = n_chunks * 16 + tid; x < 512; x += kTopkThreads) {
-      cg[x] = 0u;
-      ce[x] = 0u;
-    }
-    __syncthreads();
-    uint2 tot;
-    const uint2 v = tid < 512 ? make_uint2(cg[tid], ce[tid]) : make_uint2(0u, 0u);
-    const uint2 ex = block_excl_scan2(v, red, &tot);
-    if (tid < 512) {
-      cg[tid] = ex.x;
-      ce[tid] = ex.y;
-    }
-    __syncthreads();
-    const uint64_t below = (1ull << lane) - 1ull;
-    for (int j = 0; j < n_chunks; ++j) {
-      const int i = j * kTopkThreads + tid;
-      const uint32_t key = i < n ? lds[i] : 0u;
-      const bool g = i < n && key > T, e = i < n && key == T;
-      const uint64_t mg = __ballot(g), me = __ballot(e);
-      const uint32_t gt_before = cg[j * 16 + wv] + (uint32_t)__popcll(mg & below);
-      const uint32_t eq_before = ce[j * 16 + wv] + (uint32_t)__popcll(me & below);
-      if (g) out[gt_before + min(eq_before, remaining)] = i;
-      else if (e && eq_before < remaining) out[gt_before + eq_before] = i;
-    }
-    return;
-  }
-  // scores read from memory: contiguous segments per thread
   const int seg = (n + kTopkThreads - 1) / kTopkThreads;
   const int i0 = min(n, tid * seg), i1 = min(n, i0 + seg);
   uint32_t gt = 0, eq = 0;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t key = key_at<STAGED>(lds, src, i);
+    const uint32_t key = score_key(src[i]);
     gt += key > T;
     eq += key == T;
   }
   uint2 tot;
   const uint2 before = block_excl_scan2(make_uint2(gt, eq), red, &tot);
-  const uint32_t gt_before = before.x, eq_before = before.y;
-  uint32_t pos = gt_before + min(eq_before, remaining);
-  uint32_t eq_rank = eq_before;
+  uint32_t pos = before.x + min(before.y, remaining);
+  uint32_t eq_rank = before.y;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t key = key_at<STAGED>(lds, src, i);
+    const uint32_t key = score_key(src[i]);
     bool take = key > T;
     if (key == T) {
       take = eq_rank < remaining;
@@ -215,11 +144,156 @@ __device__ void topk_select(const float* __restrict__ src, int n, int k, int32_t
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts within each 16-lane
+// row, then the row totals broadcast into the following rows.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+struct TopkRegLds {
+  uint32_t hist0[4096];  // first digit (12 bits)
+  uint32_t hist1[4096];  // second digit (12 bits)
+  uint32_t hist2[256];   // last digit (8 bits)
+  uint32_t cnt[2][512];  // per (chunk, wave): keys > T, keys == T, then their exclusive prefixes
+  uint32_t red[2][16];
+  uint32_t digit, above;
+};
+
+// Find the digit holding the `remaining`-th largest key of a histogram of `nbins` digits
+// (4096 or 256): thread t owns nbins / 1024 (at least 1) consecutive digits counted from the
+// top; a wave scan plus the 16 wave totals give each thread the count above its digits.
+// Returns (digit, keys above it) to every thread.
+__device__ __forceinline__ uint2 topk_find_digit(const uint32_t* hist, int nbins, uint32_t remaining,
+                                                 TopkRegLds& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = nbins >= kTopkThreads ? nbins / kTopkThreads : 1;
+  const int owners = nbins / per;
+  const int d_hi = nbins - tid * per;
+  uint32_t loc = 0;
+  if (tid < owners)
+    for (int d = 0; d < per; ++d) loc += hist[d_hi - 1 - d];
+  const uint32_t incl = wave_incl_scan(loc);
+  if (lane == 63) sh.red[0][wv] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkThreads / 64; ++i) base += (i < wv) ? sh.red[0][i] : 0u;
+  uint32_t ab = base + incl - loc;
+  if (tid < owners && ab < remaining && ab + loc >= remaining) {
+    for (int d = 0; d < per; ++d) {
+      const uint32_t h = hist[d_hi - 1 - d];
+      if (ab + h >= remaining) {
+        sh.digit = (uint32_t)(d_hi - 1 - d);
+        sh.above = ab;
+        break;
+      }
+      ab += h;
+    }
+  }
+  __syncthreads();
+  return make_uint2(sh.digit, sh.above);
+}
+
+// Selection with the keys held in registers: NPT keys per thread, key j of thread tid is
+// index 1024 j + tid (n <= 1024 NPT).  Three digit passes (12, 12, 8 bits) with one
+// histogram each, then the ballot compaction in index order.
+template <int NPT>
+__device__ void topk_select_reg(const float* __restrict__ src, int n, int k, int32_t* __restrict__ out,
+                                TopkRegLds& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t key[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int i = j * kTopkThreads + tid;
+    key[j] = i < n ? score_key(src[i]) : 0u;
+  }
+  for (int b = tid; b < 4096; b += kTopkThreads) {
+    sh.hist0[b] = 0u;
+    sh.hist1[b] = 0u;
+  }
+  if (tid < 256) sh.hist2[tid] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NPT; ++j)
+    if (j * kTopkThreads + tid < n) atomicAdd(&sh.hist0[key[j] >> 20], 1u);
+  __syncthreads();
+  uint32_t remaining = (uint32_t)k;
+  uint2 r = topk_find_digit(sh.hist0, 4096, remaining, sh);
+  const uint32_t d0 = r.x;
+  remaining -= r.y;
+#pragma unroll
+  for (int j = 0; j < NPT; ++j)
+    if (j * kTopkThreads + tid < n && (key[j] >> 20) == d0) atomicAdd(&sh.hist1[(key[j] >> 8) & 0xfffu], 1u);
+  __syncthreads();
+  r = topk_find_digit(sh.hist1, 4096, remaining, sh);
+  const uint32_t p1 = (d0 << 12) | r.x;  // top 24 bits
+  remaining -= r.y;
+#pragma unroll
+  for (int j = 0; j < NPT; ++j)
+    if (j * kTopkThreads + tid < n && (key[j] >> 8) == p1) atomicAdd(&sh.hist2[key[j] & 0xffu], 1u);
+  __syncthreads();
+  r = topk_find_digit(sh.hist2, 256, remaining, sh);
+  const uint32_t T = (p1 << 8) | r.x;  // the k-th largest key
+  remaining -= r.y;                     // keys == T still to take, lowest index first
+
+  // per (chunk j, wave) counts of keys > T and == T
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const bool ok = j * kTopkThreads + tid < n;
+    const uint64_t mg = __ballot(ok && key[j] > T);
+    const uint64_t me = __ballot(ok && key[j] == T);
+    if (lane == 0) {
+      sh.cnt[0][j * 16 + wv] = (uint32_t)__popcll(mg);
+      sh.cnt[1][j * 16 + wv] = (uint32_t)__popcll(me);
+    }
+  }
+  __syncthreads();
+  // exclusive prefixes over the NPT * 16 (chunk, wave) entries in index order
+  {
+    const int m = NPT * 16;
+    const uint32_t vg = tid < m ? sh.cnt[0][tid] : 0u, ve = tid < m ? sh.cnt[1][tid] : 0u;
+    const uint32_t ig = wave_incl_scan(vg), ie = wave_incl_scan(ve);
+    if (lane == 63) {
+      sh.red[0][wv] = ig;
+      sh.red[1][wv] = ie;
+    }
+    __syncthreads();
+    uint32_t bg = 0, be = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkThreads / 64; ++i) {
+      bg += (i < wv) ? sh.red[0][i] : 0u;
+      be += (i < wv) ? sh.red[1][i] : 0u;
+    }
+    if (tid < m) {
+      sh.cnt[0][tid] = bg + ig - vg;
+      sh.cnt[1][tid] = be + ie - ve;
+    }
+  }
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int i = j * kTopkThreads + tid;
+    const bool g = i < n && key[j] > T, e = i < n && key[j] == T;
+    const uint64_t mg = __ballot(g), me = __ballot(e);
+    const uint32_t gt_before = sh.cnt[0][j * 16 + wv] + (uint32_t)__popcll(mg & below);
+    const uint32_t eq_before = sh.cnt[1][j * 16 + wv] + (uint32_t)__popcll(me & below);
+    if (g) out[gt_before + min(eq_before, remaining)] = i;
+    else if (e && eq_before < remaining) out[gt_before + eq_before] = i;
+  }
+}
+
 __global__ void __launch_bounds__(kTopkThreads) topk_kernel(SeqsDev S, const float* __restrict__ score,
                                                             int64_t score_stride, int ratio, int k,
                                                             int32_t* __restrict__ idx) {
-  extern __shared__ uint32_t stage[];
   __shared__ TopkLds sh;
+  __shared__ TopkRegLds rsh;
   const int t = blockIdx.x;
   const TokenCtx ctx = token_ctx(S, t);
   const int64_t V = (ctx.p + 1) / ratio;
@@ -229,20 +303,17 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(SeqsDev S, const flo
     for (int i = threadIdx.x; i < k; i += kTopkThreads) out[i] = (i < V) ? i : -1;
     return;
   }
-  if (V <= kTopkStage) topk_select<true>(src, (int)V, k, out, stage, sh);
-  else topk_select<false>(src, (int)V, k, out, stage, sh);
+  if (V <= 8 * kTopkThreads) topk_select_reg<8>(src, (int)V, k, out, rsh);
+  else if (V <= 16 * kTopkThreads) topk_select_reg<16>(src, (int)V, k, out, rsh);
+  else if (V <= 32 * kTopkThreads) topk_select_reg<32>(src, (int)V, k, out, rsh);
+  else topk_select_mem(src, (int)V, k, out, sh);
 }
 
 hipError_t launch_topk(const SeqsDev& S, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
                        int max_vis, hipStream_t stream) {
+  (void)max_vis;
   if (S.total_q == 0) return hipSuccess;
-  const size_t lds = (size_t)min(max_vis, kTopkStage) * sizeof(uint32_t);
-  // allow the full staging buffer (beyond the 64 KiB default) once per process
-  static const hipError_t attr = hipFuncSetAttribute((const void*)topk_kernel,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     kTopkStage * (int)sizeof(uint32_t));
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(topk_kernel, dim3(S.total_q), dim3(kTopkThreads), lds, stream, S, score, score_stride, ratio, k,
+  hipLaunchKernelGGL(topk_kernel, dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score, score_stride, ratio, k,
                      idx);
   return hipGetLastError();
 }

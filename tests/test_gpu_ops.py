@@ -223,8 +223,9 @@ def test_index_score_mxfp4_query_blocks():
 def test_topk_exact_on_identical_scores():
     g = np.random.default_rng(21)
     ratio = 1
-    # V: k-ties, V <= k, V = k + 1, staged (<= 32768) and streamed (> 32768) candidates
-    ctx = [300, 64, 65, 5000, 32768, 40000, 1]
+    # V: k-ties, V <= k, V = k + 1, keys held in registers (8, 16 or 32 per thread up to
+    # 32768, with the 8192 / 16384 boundaries) and streamed (> 32768) candidates
+    ctx = [300, 64, 65, 5000, 32768, 40000, 1, 8193, 12000, 16384]
     n_q = [1] * len(ctx)
     ks = 64
     ob, sq, _, _ = make_batch(n_q, ctx, ratio)

@@ -191,7 +191,9 @@ int64_t attend_max_chunks(const AttendArgs& a) {
 
 size_t attend_workspace_bytes(const AttendArgs& a) {
   const int64_t mc = attend_max_chunks(a);
-  return (size_t)a.S.total_q * (size_t)mc * (size_t)a.n_h * ((size_t)a.q.dim + 2) * sizeof(float);
+  // chunk partials (o, then m and l) and a 16-byte record per token (position, chunk count)
+  return (size_t)a.S.total_q * (size_t)mc * (size_t)a.n_h * ((size_t)a.q.dim + 2) * sizeof(float) +
+         (size_t)a.S.total_q * 16;
 }
 
 bool attend_mfma_supported(const AttendArgs& a);

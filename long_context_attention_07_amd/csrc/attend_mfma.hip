@@ -320,6 +320,13 @@ __device__ __forceinline__ void store_tile(MfmaLds& L, const AttendArgs& a, cons
   }
 }
 
+// Per-token record the split launch leaves after the (m, l) partials: the token's position
+// and chunk count, written by the workgroup of its first chunk and head group, so the
+// combine step needs no context lookup.
+__device__ __forceinline__ int64_t* split_meta(float* ws_ml, const AttendArgs& a, int max_chunks) {
+  return reinterpret_cast<int64_t*>(ws_ml + (size_t)a.S.total_q * max_chunks * a.n_h * 2);
+}
+
 template <bool SPLIT, bool KVF>
 __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* __restrict__ ws_o,
                                                           float* __restrict__ ws_ml, int n_hg, int max_chunks,
@@ -380,6 +387,11 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* _
   const int64_t n_ent = entry_slots(a, ctx);
   const int64_t n_slots = n_ent + a.n_win;
   const int n_chunks = (int)((n_slots + chunk_slots - 1) / chunk_slots);
+  if (SPLIT && c_only == 0 && hg == 0 && threadIdx.x == 0) {
+    int64_t* meta = split_meta(ws_ml, a, max_chunks);
+    meta[2 * t] = ctx.p;
+    meta[2 * t + 1] = n_chunks;
+  }
   if (SPLIT && c_only >= n_chunks) return;
   const int c_end = SPLIT ? c_only + 1 : n_chunks;
 
@@ -801,6 +813,11 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
   const int64_t n_ent = entry_slots(a, ctx);
   const int64_t n_slots = n_ent + a.n_win;
   const int n_chunks = (int)((n_slots + chunk_slots - 1) / chunk_slots);
+  if (SPLIT && c_only == 0 && hg == 0 && threadIdx.x == 0) {
+    int64_t* meta = split_meta(ws_ml, a, max_chunks);
+    meta[2 * t] = ctx.p;
+    meta[2 * t + 1] = n_chunks;
+  }
   if (SPLIT && c_only >= n_chunks) return;
   const int c_end = SPLIT ? c_only + 1 : n_chunks;
 
@@ -1020,57 +1037,64 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
 
 // Fold of the chunk partials written by the split launch, in chunk order from the sink:
 // one wave per head, each lane 8 consecutive dims; same arithmetic as the single launch.
+// The first kCB chunks are requested together with the token record, before it is read.
 __global__ void __launch_bounds__(256) attend_combine_mfma_kernel(AttendArgs a, const float* __restrict__ ws_o,
                                                                   const float* __restrict__ ws_ml, int max_chunks,
                                                                   int chunk_slots) {
+  (void)chunk_slots;
+  constexpr int kCB = 8;
   __shared__ FreqLds F;
-  load_freqs(F, a.rope);
-  __syncthreads();
   const int n_h4 = (a.n_h + 3) / 4;
   const int t = blockIdx.x / n_h4;
   const int h = (blockIdx.x % n_h4) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (h >= a.n_h) return;
-  const TokenCtx ctx = token_ctx(a.S, t);
-  const int n_chunks = token_chunks(a, ctx, chunk_slots);
+  const bool on = h < a.n_h;
+  const int hh = on ? h : 0;
+  const int64_t* meta = split_meta(const_cast<float*>(ws_ml), a, max_chunks);
+  const int64_t p = meta[2 * t];
+  const int n_chunks = (int)meta[2 * t + 1];
   const int d0 = 8 * lane;
-  FoldState f = fold_init(a.sink[h] * kLog2e);
+  const int64_t base0 = (int64_t)t * max_chunks * a.n_h + hh;
+  FoldState f = fold_init(on ? a.sink[hh] * kLog2e : -INFINITY);
   float O[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) O[i] = 0.f;
-  const int64_t base0 = (int64_t)t * max_chunks * a.n_h + h;
-  float2 ml = n_chunks > 0 ? *reinterpret_cast<const float2*>(ws_ml + 2 * base0) : make_float2(0.f, 0.f);
-  float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
-  if (n_chunks > 0) {
-    o0 = *reinterpret_cast<const float4*>(ws_o + base0 * kDM + d0);
-    o1 = *reinterpret_cast<const float4*>(ws_o + base0 * kDM + d0 + 4);
-  }
-  for (int cc = 0; cc < n_chunks; ++cc) {
-    // next chunk's loads are in flight while this one is folded
-    float2 ml_n = ml;
-    float4 o0_n = o0, o1_n = o1;
-    if (cc + 1 < n_chunks) {
-      const int64_t b = base0 + (int64_t)(cc + 1) * a.n_h;
-      ml_n = *reinterpret_cast<const float2*>(ws_ml + 2 * b);
-      o0_n = *reinterpret_cast<const float4*>(ws_o + b * kDM + d0);
-      o1_n = *reinterpret_cast<const float4*>(ws_o + b * kDM + d0 + 4);
-    }
-    float fa, fb;
-    fold_step(f, ml.x, ml.y, &fa, &fb);
-    const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+  load_freqs(F, a.rope);
+  for (int c0 = 0; c0 < max_chunks; c0 += kCB) {
+    float2 ml[kCB];
+    float4 o0[kCB], o1[kCB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) O[i] = __builtin_fmaf(O[i], fa, o[i] * fb);
-    ml = ml_n;
-    o0 = o0_n;
-    o1 = o1_n;
+    for (int i = 0; i < kCB; ++i) {
+      // first batch: every chunk slot the workspace holds (in bounds, unused past n_chunks)
+      const int c = c0 + i;
+      if (c < (c0 == 0 ? max_chunks : n_chunks)) {
+        const int64_t b = base0 + (int64_t)c * a.n_h;
+        ml[i] = *reinterpret_cast<const float2*>(ws_ml + 2 * b);
+        o0[i] = *reinterpret_cast<const float4*>(ws_o + b * kDM + d0);
+        o1[i] = *reinterpret_cast<const float4*>(ws_o + b * kDM + d0 + 4);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kCB; ++i) {
+      if (c0 + i < n_chunks) {
+        float fa, fb;
+        fold_step(f, ml[i].x, ml[i].y, &fa, &fb);
+        const float o[8] = {o0[i].x, o0[i].y, o0[i].z, o0[i].w, o1[i].x, o1[i].y, o1[i].z, o1[i].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) O[e] = __builtin_fmaf(O[e], fa, o[e] * fb);
+      }
+    }
+    if (c0 + kCB >= n_chunks) break;
   }
+  __syncthreads();  // frequency table
+  if (!on) return;
   const float inv = (f.Z > 0.f) ? 1.0f / f.Z : 0.f;
   float x[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = O[i] * inv;
   const int dn = kDM - a.rope.dims;
   *reinterpret_cast<uint4*>(a.out.data + ((int64_t)t * a.n_h + h) * a.out.stride + d0 * 2) =
-      finalize8(x, d0, dn, ctx.p, F);
+      finalize8(x, d0, dn, p, F);
   if (a.lse && lane == 0) a.lse[(int64_t)t * a.n_h + h] = lse_natural(f);
 }
 

@@ -28,6 +28,64 @@ struct CompressJob {
   RowsOut out;
 };
 
+// Online-softmax state of one channel pair over part of an entry's sources.
+struct PoolState {
+  float m0, m1, s0, s1, a0, a1;
+};
+
+template <int DT>
+__device__ __forceinline__ float2 load_pair_as(const RowsDev& R, int64_t r, int c) {
+  const uint8_t* row = R.data + r * R.stride;
+  if (DT == DT_F32) return reinterpret_cast<const float2*>(row)[c];
+  if (DT == DT_BF16) {
+    const uint32_t u = reinterpret_cast<const uint32_t*>(row)[c];
+    return make_float2(bf16_bits_to_f32(u & 0xffffu), bf16_bits_to_f32(u >> 16));
+  }
+  return load_pair(R, r, c);
+}
+
+// Online softmax of channel pair `pair` over sources j0 .. j1-1 (row tok_shift + j of the
+// token pools), ascending; loads in batches of NB issued unconditionally (rows past the end
+// repeat the last row and are skipped), with the row format fixed at compile time.
+template <int CD, int ZD, int NB>
+__device__ __forceinline__ PoolState pool_rows(const RowsDev& c, const RowsDev& z, const float* __restrict__ bsrc,
+                                               int D, int64_t tok_shift, int64_t j0, int64_t j1, int pair) {
+  float m0 = -INFINITY, m1 = -INFINITY, s0 = 0.f, s1 = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int64_t jb = j0; jb < j1; jb += NB) {
+    float2 cv[NB], zv[NB], bv[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int64_t j = min(jb + u, j1 - 1);
+      cv[u] = load_pair_as<CD>(c, tok_shift + j, pair);
+      zv[u] = load_pair_as<ZD>(z, tok_shift + j, pair);
+      bv[u] = reinterpret_cast<const float2*>(bsrc + j * D)[pair];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the batch's loads all go out before its updates
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if (jb + u < j1) {
+        // gate logits in the log2 domain; online softmax in ascending position
+        const float g0 = (zv[u].x + bv[u].x) * kLog2e;
+        const float g1 = (zv[u].y + bv[u].y) * kLog2e;
+        const float n0 = fmaxf(m0, g0), n1 = fmaxf(m1, g1);
+        const float r0 = rescale(m0, n0), r1 = rescale(m1, n1);
+        const float e0 = ex2(g0 - n0), e1 = ex2(g1 - n1);
+        s0 = __builtin_fmaf(s0, r0, e0);
+        s1 = __builtin_fmaf(s1, r1, e1);
+        a0 = __builtin_fmaf(a0, r0, e0 * cv[u].x);
+        a1 = __builtin_fmaf(a1, r1, e1 * cv[u].y);
+        m0 = n0;
+        m1 = n1;
+      }
+    }
+  }
+  return PoolState{m0, m1, s0, s1, a0, a1};
+}
+
+// RG row groups of 256 threads each pool a contiguous share of the entry's sources (loads
+// issued in batches of 8, unconditionally: rows past the end repeat the last row and are
+// skipped), then group 0 merges the group states in group order.
+template <int RG>
 __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& c, const RowsDev& z,
                                                const float* __restrict__ bias, int ratio, int overlap,
                                                const RopeTab& rope, const RowsOut& out, int max_new, int blk) {
@@ -42,7 +100,8 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
   if (i >= i_hi) return;
 
   const int D = c.dim;
-  const int pair = threadIdx.x;
+  const int pair = threadIdx.x & 255;
+  const int grp = threadIdx.x >> 8;
   const bool active = 2 * pair < D;
   const int64_t lo = (i - overlap) * ratio;
   const int64_t hi = (i + 1) * ratio;
@@ -50,45 +109,49 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
   const int64_t tok0 = S.tok_off[b];
 
   __shared__ double s_freq[kMaxRopePairs];
+  __shared__ PoolState s_part[RG > 1 ? RG - 1 : 1][256];
   for (int q = threadIdx.x; q < rope.dims / 2; q += blockDim.x) s_freq[q] = rope.inv_freq[q];
-  __syncthreads();
 
   float2 acc = make_float2(0.f, 0.f);
+  PoolState st{-INFINITY, -INFINITY, 0.f, 0.f, 0.f, 0.f};
   if (active) {
-    float m0 = -INFINITY, m1 = -INFINITY, s0 = 0.f, s1 = 0.f, a0 = 0.f, a1 = 0.f;
-    const int64_t j0 = lo < 0 ? 0 : lo;
-    // sources in batches of 8: all loads of a batch are issued before the updates
-    for (int64_t jb = j0; jb < hi; jb += 8) {
-      float2 cv[8], zv[8], bv[8];
+    const int64_t j_first = lo < 0 ? 0 : lo;
+    const int64_t n_src = hi - j_first;
+    const int64_t share = (n_src + RG - 1) / RG;
+    const int64_t j0 = j_first + grp * share;
+    const int64_t j1 = min(hi, j0 + share);
+    const float* bsrc = bias - lo * D;  // row j of the slot bias is bsrc + j * D
+    if (c.dtype == DT_BF16 && z.dtype == DT_BF16)
+      st = pool_rows<DT_BF16, DT_BF16, RG == 1 ? 8 : 16>(c, z, bsrc, D, tok0 - tok_lo, j0, j1, pair);
+    else if (c.dtype == DT_F32 && z.dtype == DT_F32)
+      st = pool_rows<DT_F32, DT_F32, RG == 1 ? 8 : 16>(c, z, bsrc, D, tok0 - tok_lo, j0, j1, pair);
+    else
+      st = pool_rows<-1, -1, 8>(c, z, bsrc, D, tok0 - tok_lo, j0, j1, pair);
+  }
+  if (RG > 1) {
+    if (grp > 0) s_part[grp - 1][pair] = st;
+    __syncthreads();
+    if (grp > 0) return;
+    if (active) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t j = jb + u;
-        if (j < hi) {
-          const int64_t r = tok0 + (j - tok_lo);
-          cv[u] = load_pair(c, r, pair);
-          zv[u] = load_pair(z, r, pair);
-          bv[u] = reinterpret_cast<const float2*>(bias + (j - lo) * D)[pair];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (jb + u < hi) {
-          // gate logits in the log2 domain; online softmax in ascending position
-          const float g0 = (zv[u].x + bv[u].x) * kLog2e;
-          const float g1 = (zv[u].y + bv[u].y) * kLog2e;
-          const float n0 = fmaxf(m0, g0), n1 = fmaxf(m1, g1);
-          const float r0 = rescale(m0, n0), r1 = rescale(m1, n1);
-          const float e0 = ex2(g0 - n0), e1 = ex2(g1 - n1);
-          s0 = __builtin_fmaf(s0, r0, e0);
-          s1 = __builtin_fmaf(s1, r1, e1);
-          a0 = __builtin_fmaf(a0, r0, e0 * cv[u].x);
-          a1 = __builtin_fmaf(a1, r1, e1 * cv[u].y);
-          m0 = n0;
-          m1 = n1;
-        }
+      for (int g2 = 1; g2 < RG; ++g2) {
+        const PoolState o = s_part[g2 - 1][pair];
+        const float n0 = fmaxf(st.m0, o.m0), n1 = fmaxf(st.m1, o.m1);
+        const float r0 = rescale(st.m0, n0), r1 = rescale(st.m1, n1);
+        const float q0 = rescale(o.m0, n0), q1 = rescale(o.m1, n1);
+        st.s0 = __builtin_fmaf(st.s0, r0, o.s0 * q0);
+        st.s1 = __builtin_fmaf(st.s1, r1, o.s1 * q1);
+        st.a0 = __builtin_fmaf(st.a0, r0, o.a0 * q0);
+        st.a1 = __builtin_fmaf(st.a1, r1, o.a1 * q1);
+        st.m0 = n0;
+        st.m1 = n1;
       }
     }
-    acc = make_float2(a0 / s0, a1 / s1);
+  } else {
+    __syncthreads();
+  }
+  if (active) {
+    acc = make_float2(st.a0 / st.s0, st.a1 / st.s1);
     const int d_n = D - rope.dims;
     if (rope.dims > 0 && 2 * pair >= d_n) {
       const int q = pair - d_n / 2;
@@ -149,22 +212,27 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
   }
 }
 
-__global__ void __launch_bounds__(256) compress_kernel(SeqsDev S, CompressJob j0, int ratio, int overlap,
-                                                       int max_new) {
-  compress_block(S, j0.c, j0.z, j0.bias, ratio, overlap, j0.rope, j0.out, max_new, blockIdx.x);
+template <int RG>
+__global__ void __launch_bounds__(256 * RG) compress_kernel(SeqsDev S, CompressJob j0, int ratio, int overlap,
+                                                            int max_new) {
+  compress_block<RG>(S, j0.c, j0.z, j0.bias, ratio, overlap, j0.rope, j0.out, max_new, blockIdx.x);
 }
 
 // Two jobs over the same batch in one launch (KV rows and indexer keys of a CSA layer): the
 // first S.n_seqs * max_new workgroups run job 0, the rest job 1, with the same arithmetic
 // as two separate launches.
-__global__ void __launch_bounds__(256) compress2_kernel(SeqsDev S, CompressJob j0, CompressJob j1, int ratio,
-                                                        int overlap, int max_new) {
+template <int RG>
+__global__ void __launch_bounds__(256 * RG) compress2_kernel(SeqsDev S, CompressJob j0, CompressJob j1, int ratio,
+                                                             int overlap, int max_new) {
   const int per_job = S.n_seqs * max_new;
   if ((int)blockIdx.x < per_job)
-    compress_block(S, j0.c, j0.z, j0.bias, ratio, overlap, j0.rope, j0.out, max_new, blockIdx.x);
+    compress_block<RG>(S, j0.c, j0.z, j0.bias, ratio, overlap, j0.rope, j0.out, max_new, blockIdx.x);
   else
-    compress_block(S, j1.c, j1.z, j1.bias, ratio, overlap, j1.rope, j1.out, max_new, blockIdx.x - per_job);
+    compress_block<RG>(S, j1.c, j1.z, j1.bias, ratio, overlap, j1.rope, j1.out, max_new, blockIdx.x - per_job);
 }
+
+// Sources per entry from which the pooling is split over four row groups.
+constexpr int kSplitSources = 64;
 
 hipError_t launch_compress(const SeqsDev& S, const RowsDev& c, const RowsDev& z, const float* bias, int ratio,
                            int overlap, const RopeTab& rope, const RowsOut& out, int max_q, hipStream_t stream) {
@@ -172,7 +240,12 @@ hipError_t launch_compress(const SeqsDev& S, const RowsDev& c, const RowsDev& z,
   const int64_t blocks = (int64_t)S.n_seqs * max_new;
   if (blocks == 0) return hipSuccess;
   const CompressJob j0{c, z, bias, rope, out};
-  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, S, j0, ratio, overlap, max_new);
+  if (ratio * (1 + overlap) >= kSplitSources)
+    hipLaunchKernelGGL(compress_kernel<4>, dim3((unsigned)blocks), dim3(1024), 0, stream, S, j0, ratio, overlap,
+                       max_new);
+  else
+    hipLaunchKernelGGL(compress_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, S, j0, ratio, overlap,
+                       max_new);
   return hipGetLastError();
 }
 
@@ -184,8 +257,12 @@ hipError_t launch_compress2(const SeqsDev& S, const RowsDev& c0, const RowsDev& 
   const int64_t blocks = (int64_t)S.n_seqs * max_new;
   if (blocks == 0) return hipSuccess;
   const CompressJob j0{c0, z0, bias0, rope0, out0}, j1{c1, z1, bias1, rope1, out1};
-  hipLaunchKernelGGL(compress2_kernel, dim3((unsigned)(2 * blocks)), dim3(256), 0, stream, S, j0, j1, ratio, overlap,
-                     max_new);
+  if (ratio * (1 + overlap) >= kSplitSources)
+    hipLaunchKernelGGL(compress2_kernel<4>, dim3((unsigned)(2 * blocks)), dim3(1024), 0, stream, S, j0, j1, ratio,
+                       overlap, max_new);
+  else
+    hipLaunchKernelGGL(compress2_kernel<1>, dim3((unsigned)(2 * blocks)), dim3(256), 0, stream, S, j0, j1, ratio,
+                       overlap, max_new);
   return hipGetLastError();
 }
 

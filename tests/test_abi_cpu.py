@@ -124,4 +124,6 @@ def test_workspace_sizes(lib):
     assert lib.csa_workspace_bytes(ops.OP_INDEX_TOPK, P(s), 0, 0, 512, 4, 0) == 4 * (1 << 18) * 4
     assert lib.csa_workspace_bytes(99, P(s), 64, 512, 0, 128, 128) == 0
     hca = lib.csa_workspace_bytes(ops.OP_HCA_ATTEND, P(s), 64, 512, 0, 128, 128)
-    assert hca > 0 and hca % (4 * 64 * 514 * 4) == 0
+    # 4 tokens x 15 chunks (8192 entries + 128 window slots in 576-slot chunks) x 64 heads x
+    # (512 dims + m, l) floats, plus a 16-byte record per token
+    assert hca == 4 * 15 * 64 * 514 * 4 + 4 * 16

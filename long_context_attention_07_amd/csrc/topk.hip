@@ -9,8 +9,9 @@
 // counts); a block-wide scan then keeps every key > T and the
 // lowest-index keys == T, writing indices in ascending order.  The selection is a
 // function of the token's scores alone.  Up to 32768 candidates the keys stay in
-// registers (8, 16 or 32 per thread), each pass has its own LDS histogram and the digit
-// searches use DPP wave scans; longer lists re-read the scores from memory every pass.
+// registers (8, 16 or 32 consecutive keys per thread), each pass has its own LDS histogram
+// and the digit searches and the compaction offsets use DPP wave scans; longer lists
+// re-read the scores from memory every pass.
 
 #include "common.cuh"
 #include "kernels.h"
@@ -160,7 +161,6 @@ struct TopkRegLds {
   uint32_t hist0[4096];  // first digit (12 bits)
   uint32_t hist1[4096];  // second digit (12 bits)
   uint32_t hist2[256];   // last digit (8 bits)
-  uint32_t cnt[2][512];  // per (chunk, wave): keys > T, keys == T, then their exclusive prefixes
   uint32_t red[2][16];
   uint32_t digit, above;
 };
@@ -200,18 +200,29 @@ __device__ __forceinline__ uint2 topk_find_digit(const uint32_t* hist, int nbins
   return make_uint2(sh.digit, sh.above);
 }
 
-// Selection with the keys held in registers: NPT keys per thread, key j of thread tid is
-// index 1024 j + tid (n <= 1024 NPT).  Three digit passes (12, 12, 8 bits) with one
-// histogram each, then the ballot compaction in index order.
+// Selection with the keys held in registers: thread tid holds the NPT consecutive keys
+// NPT tid .. NPT tid + NPT-1 (n <= 1024 NPT), loaded 16 bytes at a time when the row is
+// 16-byte aligned.  Three digit passes (12, 12, 8 bits) with one histogram each; then each
+// thread counts its keys > T and == T, one block scan gives its output offsets, and it
+// writes its kept indices in ascending order.
 template <int NPT>
 __device__ void topk_select_reg(const float* __restrict__ src, int n, int k, int32_t* __restrict__ out,
                                 TopkRegLds& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int i0 = NPT * tid;
   uint32_t key[NPT];
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) == 0 && i0 + NPT <= n) {
 #pragma unroll
-  for (int j = 0; j < NPT; ++j) {
-    const int i = j * kTopkThreads + tid;
-    key[j] = i < n ? score_key(src[i]) : 0u;
+    for (int q = 0; q < NPT / 4; ++q) {
+      const float4 v = reinterpret_cast<const float4*>(src + i0)[q];
+      key[4 * q] = score_key(v.x);
+      key[4 * q + 1] = score_key(v.y);
+      key[4 * q + 2] = score_key(v.z);
+      key[4 * q + 3] = score_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) key[j] = i0 + j < n ? score_key(src[i0 + j]) : 0u;
   }
   for (int b = tid; b < 4096; b += kTopkThreads) {
     sh.hist0[b] = 0u;
@@ -221,7 +232,7 @@ __device__ void topk_select_reg(const float* __restrict__ src, int n, int k, int
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < NPT; ++j)
-    if (j * kTopkThreads + tid < n) atomicAdd(&sh.hist0[key[j] >> 20], 1u);
+    if (i0 + j < n) atomicAdd(&sh.hist0[key[j] >> 20], 1u);
   __syncthreads();
   uint32_t remaining = (uint32_t)k;
   uint2 r = topk_find_digit(sh.hist0, 4096, remaining, sh);
@@ -229,63 +240,49 @@ __device__ void topk_select_reg(const float* __restrict__ src, int n, int k, int
   remaining -= r.y;
 #pragma unroll
   for (int j = 0; j < NPT; ++j)
-    if (j * kTopkThreads + tid < n && (key[j] >> 20) == d0) atomicAdd(&sh.hist1[(key[j] >> 8) & 0xfffu], 1u);
+    if (i0 + j < n && (key[j] >> 20) == d0) atomicAdd(&sh.hist1[(key[j] >> 8) & 0xfffu], 1u);
   __syncthreads();
   r = topk_find_digit(sh.hist1, 4096, remaining, sh);
   const uint32_t p1 = (d0 << 12) | r.x;  // top 24 bits
   remaining -= r.y;
 #pragma unroll
   for (int j = 0; j < NPT; ++j)
-    if (j * kTopkThreads + tid < n && (key[j] >> 8) == p1) atomicAdd(&sh.hist2[key[j] & 0xffu], 1u);
+    if (i0 + j < n && (key[j] >> 8) == p1) atomicAdd(&sh.hist2[key[j] & 0xffu], 1u);
   __syncthreads();
   r = topk_find_digit(sh.hist2, 256, remaining, sh);
   const uint32_t T = (p1 << 8) | r.x;  // the k-th largest key
   remaining -= r.y;                     // keys == T still to take, lowest index first
 
-  // per (chunk j, wave) counts of keys > T and == T
+  uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
-    const bool ok = j * kTopkThreads + tid < n;
-    const uint64_t mg = __ballot(ok && key[j] > T);
-    const uint64_t me = __ballot(ok && key[j] == T);
-    if (lane == 0) {
-      sh.cnt[0][j * 16 + wv] = (uint32_t)__popcll(mg);
-      sh.cnt[1][j * 16 + wv] = (uint32_t)__popcll(me);
-    }
+    const bool ok = i0 + j < n;
+    gt += (ok && key[j] > T) ? 1u : 0u;
+    eq += (ok && key[j] == T) ? 1u : 0u;
+  }
+  const uint32_t ig = wave_incl_scan(gt), ie = wave_incl_scan(eq);
+  if (lane == 63) {
+    sh.red[0][wv] = ig;
+    sh.red[1][wv] = ie;
   }
   __syncthreads();
-  // exclusive prefixes over the NPT * 16 (chunk, wave) entries in index order
-  {
-    const int m = NPT * 16;
-    const uint32_t vg = tid < m ? sh.cnt[0][tid] : 0u, ve = tid < m ? sh.cnt[1][tid] : 0u;
-    const uint32_t ig = wave_incl_scan(vg), ie = wave_incl_scan(ve);
-    if (lane == 63) {
-      sh.red[0][wv] = ig;
-      sh.red[1][wv] = ie;
-    }
-    __syncthreads();
-    uint32_t bg = 0, be = 0;
+  uint32_t bg = 0, be = 0;
 #pragma unroll
-    for (int i = 0; i < kTopkThreads / 64; ++i) {
-      bg += (i < wv) ? sh.red[0][i] : 0u;
-      be += (i < wv) ? sh.red[1][i] : 0u;
-    }
-    if (tid < m) {
-      sh.cnt[0][tid] = bg + ig - vg;
-      sh.cnt[1][tid] = be + ie - ve;
-    }
+  for (int i = 0; i < kTopkThreads / 64; ++i) {
+    bg += (i < wv) ? sh.red[0][i] : 0u;
+    be += (i < wv) ? sh.red[1][i] : 0u;
   }
-  __syncthreads();
-  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t eq_rank = be + ie - eq;
+  uint32_t pos = bg + ig - gt + min(eq_rank, remaining);
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
-    const int i = j * kTopkThreads + tid;
-    const bool g = i < n && key[j] > T, e = i < n && key[j] == T;
-    const uint64_t mg = __ballot(g), me = __ballot(e);
-    const uint32_t gt_before = sh.cnt[0][j * 16 + wv] + (uint32_t)__popcll(mg & below);
-    const uint32_t eq_before = sh.cnt[1][j * 16 + wv] + (uint32_t)__popcll(me & below);
-    if (g) out[gt_before + min(eq_before, remaining)] = i;
-    else if (e && eq_before < remaining) out[gt_before + eq_before] = i;
+    const bool ok = i0 + j < n;
+    bool take = ok && key[j] > T;
+    if (ok && key[j] == T) {
+      take = eq_rank < remaining;
+      ++eq_rank;
+    }
+    if (take) out[pos++] = i0 + j;
   }
 }
 

@@ -239,15 +239,18 @@ def test_topk_exact_on_identical_scores():
             s[r, 17] = 1.0
         else:
             s[r, :L] = g.standard_normal(L).astype(np.float32)
-    st = torch.from_numpy(s).to(DEV)
-    for k in (1, ks, 1000):
-        idx = torch.full((len(ctx), k), -7, dtype=torch.int32, device=DEV)
-        ops.csa_topk(sq, st, ratio, k, idx)
-        torch.cuda.synchronize()
-        got = idx.cpu().numpy()
-        for r, L in enumerate(ctx):
-            ref = topk_select(s[r, :L].astype(np.float64), k)
-            assert list(got[r]) == list(ref), f"token {r} (V={L}, k={k})"
+    # rows 16-byte aligned (stride a multiple of 4 floats) and not (odd stride)
+    wide = np.full((len(ctx), stride + 1), np.nan, dtype=np.float32)
+    wide[:, :stride] = s
+    for st in (torch.from_numpy(s).to(DEV), torch.from_numpy(wide).to(DEV)[:, :stride]):
+        for k in (1, ks, 1000):
+            idx = torch.full((len(ctx), k), -7, dtype=torch.int32, device=DEV)
+            ops.csa_topk(sq, st, ratio, k, idx)
+            torch.cuda.synchronize()
+            got = idx.cpu().numpy()
+            for r, L in enumerate(ctx):
+                ref = topk_select(s[r, :L].astype(np.float64), k)
+                assert list(got[r]) == list(ref), f"token {r} (V={L}, k={k}, row stride {st.stride(0)})"
 
 
 # ----------------------------------------------------------------------------- attention

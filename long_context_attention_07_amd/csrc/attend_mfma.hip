@@ -4,30 +4,20 @@
 // the 128-token window concatenated; list "其他注意力技术细节": partial RoPE on the last 64
 // dims, inverse RoPE of the output, learnable sink; section 3.4: fp8 KV with 1x128 scales).
 //
-// Workgroup = (token, group of 16 query heads, chunk of the token's key list), 4 waves.
-// The key list is walked in tiles of 64 rows staged in LDS (rows padded to 1040 bytes);
-// the next tile is prefetched into registers (one row per wave instruction, any row order,
-// so the top-k gather is fully coalesced) while the current one is processed.  The tile
-// format is bf16 for bf16 rows; fp8 rows are staged as their codes in fp16 (exact), the
-// block scales kept apart in fp32.
-//   QK   S^T[key, head] = K Q^T with v_mfma_f32_16x16x32_{bf16,f16}: wave w owns keys
-//        16w..16w+15 of the tile (A operand from LDS), the 16 rotated query rows sit in
-//        registers as the B operand (64 VGPRs).  fp8 rows: one partial per code block,
-//        scaled in fp32.  Rotated dims carry hi + lo residual terms on both sides.
-//   softmax  in the log2 domain; per-head tile max and sum exchanged across the 4 waves in
-//        a fixed order; P rounded to the tile format (fp8 rows: hi + lo), the sums use the
-//        rounded values.
-//   PV   O[head, dim] += P V: wave w owns dims 128w..128w+127 (for fp8 rows: code block w,
-//        whose per-key scale is folded into P); P is the A operand (LDS), V is read from
-//        the same row-major key tile with ds_read_b64_tr_b16, which hands each lane a
-//        column of 4 consecutive keys -- the B operand layout.
-// Chunk partials are folded in chunk order from the sink; the combine kernel below (one
-// wave per head, 8 dims per lane) runs the same fold and finalisation arithmetic as the
-// single launch, so split and single launches agree bit for bit, and a token's bits never
-// depend on the batch.  The workgroup barriers wait for LDS instructions only: the next
-// tile's row loads stay in flight across them until the rows are staged.  Window rows are
-// rotated (RoPE at their own positions) as they are staged; absent slots are staged as
-// zero rows and masked.
+// Workgroup = (token, group of 16 query heads, chunk of the token's key list), 8 waves in 4
+// pairs (see the kernel).  The key list is walked in tiles of 64 rows staged in LDS (rows
+// padded to 1040 bytes); each wave prefetches its share of the next tile into registers
+// (one row per wave instruction, any row order, so the top-k gather is fully coalesced).
+// The tile format is bf16 for bf16 rows; fp8 rows are staged as their codes in fp16
+// (exact, hardware conversion), the block scales kept apart in fp32 and applied to
+// per-block partial logits and, for the value side, folded into P.  Rotated query dims and
+// rotated window-key dims carry hi + lo residual terms.  Chunk partials are folded in chunk
+// order from the sink; the combine kernel below (one wave per head, 8 dims per lane) runs
+// the same fold and finalisation arithmetic as the single launch, so split and single
+// launches agree bit for bit, and a token's bits never depend on the batch.  The workgroup
+// barriers wait for LDS instructions only: the next tile's row loads stay in flight across
+// them until the rows are staged.  Window rows are rotated (RoPE at their own positions) as
+// they are staged; absent slots are staged as zero rows and masked.
 
 #include "attend_common.cuh"
 
@@ -49,30 +39,24 @@ constexpr int kT = 64;                 // keys per tile
 constexpr int kHG = 16;                // query heads per workgroup
 constexpr int kDM = 512;               // head dim of this kernel
 constexpr int kKStride = kDM * 2 + 16;  // bytes per staged key row
-constexpr int kPStride = kT * 2 + 16;   // bytes per P row (one head)
 constexpr int kRopeMax = 64;            // rotary dims this kernel takes (the row's last 64 at most)
 constexpr int kLoStride = kRopeMax * 2 + 16;  // bytes per row of the rotated-dims residual tile
 
 constexpr int kMaxIdx = 4096;           // largest k the in-LDS idx table holds
 
 struct __align__(16) MfmaLds {
-  uint8_t k[kT * kKStride];
-  int32_t sidx[kMaxIdx];                // idx[t, s_lo .. s_hi) of this workgroup's chunks
-  uint8_t p[kHG * kPStride];
-  uint8_t p_lo[kHG * kPStride];  // fp16 tiles: residual of P (P = hi + lo to ~22 bits)
+  uint8_t k[kT * kKStride];      // the tile's 64 rows (pair p: rows 16p..16p+15); merge scratch
+  int32_t sidx[kMaxIdx];         // idx[t, s_lo .. s_hi) of this workgroup's chunks
   uint8_t klo[kT * kLoStride];   // window rows: residual of their rotated last 64 dims
   float scl[4][kT];              // fp8 rows: the fp32 scale of each 128-dim code block
-  float red_max[4][kHG];
+  float red_max[4][kHG];         // pair states at the end of a chunk
   float red_sum[4][kHG];
-  float alpha[kHG];
-  float mc[kHG];
-  float lc[kHG];
 };
 
 struct TileStage {
-  uint4 v[16];      // row 16w+it, bytes 16*lane .. 16*lane+15 of the stored row
+  uint4 v[16];      // row it of the wave's share, bytes 16*lane .. 16*lane+15 of the stored row
   float sc[16];     // fp8 rows: lanes 0, 8, 16, 24 hold the scale of code block lane / 8
-  uint32_t valid;   // bit it: row present
+  uint32_t valid;   // bit it: row it of the pair's 16 present
   uint32_t win;     // bit it: window row (rotated when staged)
   int64_t pos0;     // position of window row it is pos0 + it
 };
@@ -92,6 +76,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // decoded from fp8 blocks, whose scaled values would lose too much in bf16 next to
 // outliers.  Conversions round to nearest even.
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4_t;
 __device__ __forceinline__ uint32_t f16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
@@ -103,14 +88,6 @@ __device__ __forceinline__ uint32_t pack16(float a, float b) {
 template <bool F16>
 __device__ __forceinline__ float2 unpack16(uint32_t u) {
   return F16 ? make_float2(f16_val(u & 0xffffu), f16_val(u >> 16)) : make_float2(bf_lo(u), bf_hi(u));
-}
-template <bool F16>
-__device__ __forceinline__ uint32_t bits16(float x) {
-  return F16 ? f16_bits(x) : f32_to_bf16_bits(x);
-}
-template <bool F16>
-__device__ __forceinline__ float val16(uint32_t b) {
-  return F16 ? f16_val(b) : __uint_as_float(b << 16);
 }
 template <bool F16>
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
@@ -218,9 +195,6 @@ __device__ __forceinline__ TileAddr resolve_tile(const AttendArgs& a, const Toke
   return ad;
 }
 
-// Loads of the wave's rows IT0 .. IT1-1: per row two lane reads give the row's address as
-// a scalar base, and each lane loads its 16 bytes (the tile's loads are issued in two
-// halves between the compute phases).
 // Loads through a uniform 64-bit global address (scalar base plus the lane's offset).
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4_t;
 __device__ __forceinline__ uint4 load_global_u4(uint64_t base, int i) {
@@ -235,89 +209,12 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int i) {
          (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, i);
 }
 
-template <bool KVF, int IT0, int IT1>
-__device__ __forceinline__ void issue_tile(int lane, TileStage& st, const TileAddr& ad) {
-#pragma unroll
-  for (int it = IT0; it < IT1; ++it) {
-    st.v[it] = make_uint4(0u, 0u, 0u, 0u);
-    st.sc[it] = 0.f;
-    if ((st.valid >> it) & 1u) {
-      const uint64_t rowp = readlane_u64(ad.row, it);
-      if (!KVF) {
-        st.v[it] = load_global_u4(rowp, lane);
-      } else {
-        if (lane < kSplitLanes) st.v[it] = load_global_u4(rowp, lane);
-        if (lane < kSplitCodeLanes && (lane & 7) == 0) st.sc[it] = load_global_f32(readlane_u64(ad.sc, it), lane >> 3);
-      }
-    }
-  }
-}
-
-template <bool KVF>
-__device__ __forceinline__ void load_tile(const AttendArgs& a, const TokenCtx& ctx, int64_t n_ent, int64_t s0,
-                                          int w, int lane, TileStage& st, const int32_t* sidx, int64_t s_lo) {
-  const TileAddr ad = resolve_tile<KVF>(a, ctx, n_ent, s0, w, lane, st, sidx, s_lo);
-  issue_tile<KVF, 0, 16>(lane, st, ad);
-}
-
-// Stage the wave's 16 rows in LDS in the tile format.  fp8 rows are staged as their e4m3
-// codes (exact in fp16) with the block scales in L.scl: the scales are applied in fp32
-// after the products, so a key's logit carries no rounding of its scaled values.  Their
-// bf16 tail is converted to fp16 (exact in range).  Then, for waves that hold window
-// rows, the rows' last 64 dims are rotated in place (RoPE at each row's own position) and
-// the rounding residual of every rotated value goes to L.klo (zero for the other rows), so
-// that the rotated keys enter the logits to about twice the tile format's precision.
-__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t two) {
-  return pack16<true>(e4m3_to_f32(two & 0xffu), e4m3_to_f32((two >> 8) & 0xffu));
-}
-
-template <bool KVF>
-__device__ __forceinline__ void store_tile(MfmaLds& L, const AttendArgs& a, const TileStage& st, int w, int lane,
-                                           const FreqLds& F) {
-  if (!KVF) {
-#pragma unroll
-    for (int it = 0; it < 16; ++it) *reinterpret_cast<uint4*>(&L.k[(16 * w + it) * kKStride + 16 * lane]) = st.v[it];
-  } else if (lane < kSplitCodeLanes) {
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const uint4 v = st.v[it];
-      const uint4 lo = make_uint4(fp8x2_to_f16x2(v.x), fp8x2_to_f16x2(v.x >> 16), fp8x2_to_f16x2(v.y),
-                                  fp8x2_to_f16x2(v.y >> 16));
-      const uint4 hi = make_uint4(fp8x2_to_f16x2(v.z), fp8x2_to_f16x2(v.z >> 16), fp8x2_to_f16x2(v.w),
-                                  fp8x2_to_f16x2(v.w >> 16));
-      uint4* dst = reinterpret_cast<uint4*>(&L.k[(16 * w + it) * kKStride + 32 * lane]);
-      dst[0] = lo;
-      dst[1] = hi;
-      if ((lane & 7) == 0) L.scl[lane >> 3][16 * w + it] = st.sc[it];
-    }
-  } else if (lane < kSplitLanes) {
-#pragma unroll
-    for (int it = 0; it < 16; ++it)
-      *reinterpret_cast<uint4*>(&L.k[(16 * w + it) * kKStride + 2 * (kDM - kSplitBf16Dims) +
-                                     16 * (lane - kSplitCodeLanes)]) = from_bf16<true>(st.v[it]);
-  }
-  if (st.win != 0u && lane < kRopeMax / 2) {
-    // pair `lane` of the last 64 dims; rotary pairs start at dim kDM - rope.dims
-    const int d = kDM - kRopeMax + 2 * lane;
-    const int dn = kDM - a.rope.dims;
-    uint32_t u[16];
-#pragma unroll
-    for (int it = 0; it < 16; ++it) u[it] = *reinterpret_cast<const uint32_t*>(&L.k[(16 * w + it) * kKStride + d * 2]);
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      uint32_t res = 0u;
-      if (((st.win >> it) & 1u) && d >= dn) {
-        float c, s;
-        rope_cs_mode<ROPE_FAST>(st.pos0 + it, F, (d - dn) >> 1, &c, &s);
-        const float2 y = rotate2(unpack16<KVF>(u[it]), c, s);
-        const uint32_t hi = pack16<KVF>(y.x, y.y);
-        const float2 yh = unpack16<KVF>(hi);
-        *reinterpret_cast<uint32_t*>(&L.k[(16 * w + it) * kKStride + d * 2]) = hi;
-        res = pack16<KVF>(y.x - yh.x, y.y - yh.y);
-      }
-      *reinterpret_cast<uint32_t*>(&L.klo[(16 * w + it) * kLoStride + 4 * lane]) = res;
-    }
-  }
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
+// Two e4m3 codes (word HI of `four`) to two fp16 values, exact: the hardware conversion
+// with unit scale.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t four) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(four, 1.0f, HI));
 }
 
 // Per-token record the split launch leaves after the (m, l) partials: the token's position
@@ -327,373 +224,22 @@ __device__ __forceinline__ int64_t* split_meta(float* ws_ml, const AttendArgs& a
   return reinterpret_cast<int64_t*>(ws_ml + (size_t)a.S.total_q * max_chunks * a.n_h * 2);
 }
 
-template <bool SPLIT, bool KVF>
-__global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a, float* __restrict__ ws_o,
-                                                          float* __restrict__ ws_ml, int n_hg, int max_chunks,
-                                                          int chunk_slots, int n_logical) {
-  __shared__ MfmaLds L;
-  __shared__ FreqLds F;
-  // XCD-aware order: consecutive logical workgroups (the head groups and chunks of one
-  // token) land on the same XCD and share its L2.
-  const int n_phys = gridDim.x;
-  const int per_xcd = n_phys / 8;
-  const int lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (lid >= n_logical) return;
-  int rest = lid;
-  const int hg = rest % n_hg;
-  rest /= n_hg;
-  int c_only = 0;
-  if (SPLIT) {
-    c_only = rest % max_chunks;
-    rest /= max_chunks;
-  }
-  const int t = rest;
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int dn = kDM - a.rope.dims;
-
-  // The query block (16 heads x 1 KiB) and the chunk's first entry ids depend only on the
-  // token, so they are requested before the token's context is resolved: the latencies
-  // overlap.  Each thread loads 64 bytes of the query block once for all four waves.
-  uint4 qv[4];
-  {
-    const int h = hg * kHG + (tid >> 4);
-    const uint8_t* qrow = a.q.data + ((int64_t)t * a.n_h + (h < a.n_h ? h : 0)) * a.q.stride + 64 * (tid & 15);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      qv[i] = h < a.n_h ? reinterpret_cast<const uint4*>(qrow)[i] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  const int c_begin = SPLIT ? c_only : 0;
-  const int64_t s_lo = (int64_t)c_begin * chunk_slots;
-  constexpr int kEarlyIds = 2;  // entry ids per thread requested up front
-  int32_t iv[kEarlyIds];
-  int64_t s_hi = 0;
-  if (a.csa) {
-    // CSA: the key list has k entry slots whatever the context
-    const int n_chunks_csa = (int)(((int64_t)a.k + a.n_win + chunk_slots - 1) / chunk_slots);
-    s_hi = min((int64_t)(SPLIT ? c_only + 1 : n_chunks_csa) * chunk_slots, (int64_t)a.k);
-    const int32_t* src = a.idx + (int64_t)t * a.k;
-#pragma unroll
-    for (int i = 0; i < kEarlyIds; ++i) {
-      const int64_t s = s_lo + tid + 256 * i;
-      iv[i] = s < s_hi ? src[s] : -1;
-    }
-  }
-  load_freqs(F, a.rope);
-
-  const TokenCtx ctx = token_ctx(a.S, t);
-  const int64_t n_ent = entry_slots(a, ctx);
-  const int64_t n_slots = n_ent + a.n_win;
-  const int n_chunks = (int)((n_slots + chunk_slots - 1) / chunk_slots);
-  if (SPLIT && c_only == 0 && hg == 0 && threadIdx.x == 0) {
-    int64_t* meta = split_meta(ws_ml, a, max_chunks);
-    meta[2 * t] = ctx.p;
-    meta[2 * t + 1] = n_chunks;
-  }
-  if (SPLIT && c_only >= n_chunks) return;
-  const int c_end = SPLIT ? c_only + 1 : n_chunks;
-
-  if (a.csa) {
-#pragma unroll
-    for (int i = 0; i < kEarlyIds; ++i) {
-      const int64_t s = s_lo + tid + 256 * i;
-      if (s < s_hi) L.sidx[s - s_lo] = iv[i];
-    }
-    const int32_t* src = a.idx + (int64_t)t * a.k;
-    for (int64_t s = s_lo + tid + 256 * kEarlyIds; s < s_hi; s += 256) L.sidx[s - s_lo] = src[s];
-  }
-  // query block staged in the (still free) key tile: head r at row r
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&L.k[(tid >> 4) * kKStride + 64 * (tid & 15) + 16 * i]) = qv[i];
-  __syncthreads();
-
-  TileStage st;
-  load_tile<KVF>(a, ctx, n_ent, s_lo, w, lane, st, L.sidx, s_lo);
-
-  // ---- rotated query fragments: head hg*16 + c16, dims 8g + 32kk .. +7
-  uint4 qf[16];  // in the tile format
-  uint4 qlo[2];  // rounding residuals of the rotated dims among 448..511 (zero elsewhere)
-  {
-    uint4 raw[16];
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) raw[kk] = *reinterpret_cast<const uint4*>(&L.k[c16 * kKStride + (8 * g + 32 * kk) * 2]);
-    // rotary dims lie within the last 64 (dn >= 448): only chunks 14 and 15 can hold them
-#pragma unroll
-    for (int kk = 0; kk < 14; ++kk) qf[kk] = from_bf16<KVF>(raw[kk]);
-#pragma unroll
-    for (int kk = 14; kk < 16; ++kk) {
-      const int d0 = 8 * g + 32 * kk;
-      if (d0 >= dn) {
-        rotate_chunk<KVF>(raw[kk], ctx.p, F, (d0 - dn) >> 1, &qf[kk], &qlo[kk - 14]);
-      } else {
-        qf[kk] = from_bf16<KVF>(raw[kk]);
-        qlo[kk - 14] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  }
-
-  // ---- fold state of heads 4g+j (output layout) and running O over chunks
-  FoldState fs[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int h = hg * kHG + 4 * g + j;
-    fs[j] = fold_init(h < a.n_h ? a.sink[h] * kLog2e : -INFINITY);
-  }
-  f32x4_t O[8], Ot[8];
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    Ot[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  float m_run = -INFINITY, l_run = 0.f;  // head c16 (S^T layout)
-
-  auto tiles_in = [&](int c) -> int {
-    const int64_t rem = n_slots - (int64_t)c * chunk_slots;
-    const int64_t len = rem < chunk_slots ? rem : chunk_slots;
-    return (int)((len + kT - 1) / kT);
-  };
-
-  int cc = c_begin, tile = 0, ntile = tiles_in(cc);
-
-  while (true) {
-    lds_barrier();  // previous tile fully consumed
-    store_tile<KVF>(L, a, st, w, lane, F);
-    const uint32_t valid = st.valid, winm = st.win;
-    lds_barrier();  // tile visible
-
-    int ncc = cc, ntl = tile + 1;
-    if (ntl == ntile) {
-      ncc = cc + 1;
-      ntl = 0;
-    }
-    const bool has_next = ncc < c_end;
-    TileAddr nad = {0u, 0u};
-    if (has_next) {
-      nad = resolve_tile<KVF>(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, w, lane, st, L.sidx, s_lo);
-      issue_tile<KVF, 0, 8>(lane, st, nad);
-    }
-
-    // ---- S^T = K Q^T for keys 16w..16w+15.  Partial products per 128-dim block: for fp8
-    // rows blocks 0..3 hold the code products (scaled below), block 4 the bf16 tail.  The
-    // rotated dims add the query residual times the keys and, for window rows, the key
-    // residual times the query.
-    f32x4_t part[5];
-#pragma unroll
-    for (int b = 0; b < 5; ++b) part[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    {
-      const uint8_t* krow = &L.k[(16 * w + c16) * kKStride + 16 * g];
-      uint4 ka[16];
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) ka[kk] = *reinterpret_cast<const uint4*>(krow + 64 * kk);
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const int b = KVF ? (kk < 14 ? kk / 4 : 4) : 0;
-        part[b] = mfma16<KVF>(ka[kk], qf[kk], part[b]);
-        if (kk >= 14) part[KVF ? 4 : 0] = mfma16<KVF>(ka[kk], qlo[kk - 14], part[KVF ? 4 : 0]);
-      }
-      if (winm != 0u) {
-        const uint8_t* lrow = &L.klo[(16 * w + c16) * kLoStride + 16 * g];
-#pragma unroll
-        for (int kk = 14; kk < 16; ++kk) {
-          const uint4 kl = *reinterpret_cast<const uint4*>(lrow + 64 * (kk - 14));
-          part[KVF ? 4 : 0] = mfma16<KVF>(kl, qf[kk], part[KVF ? 4 : 0]);
-        }
-      }
-    }
-    f32x4_t acc = part[KVF ? 4 : 0];
-    if (KVF) {
-      // logit of key 16w+4g+j: tail + sum over code blocks of scale * code products
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float4 sb = *reinterpret_cast<const float4*>(&L.scl[b][16 * w + 4 * g]);
-        acc[0] = __builtin_fmaf(sb.x, part[b][0], acc[0]);
-        acc[1] = __builtin_fmaf(sb.y, part[b][1], acc[1]);
-        acc[2] = __builtin_fmaf(sb.z, part[b][2], acc[2]);
-        acc[3] = __builtin_fmaf(sb.w, part[b][3], acc[3]);
-      }
-    }
-    float s[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] = ((valid >> (4 * g + j)) & 1u) ? acc[j] * a.scale_log2 : -INFINITY;
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (lane < 16) L.red_max[w][c16] = mx;
-    lds_barrier();
-    const float tmax = fmaxf(fmaxf(L.red_max[0][c16], L.red_max[1][c16]), fmaxf(L.red_max[2][c16], L.red_max[3][c16]));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = rescale(m_run, m_new);
-    // P in the tile format; for fp16 tiles also its residual, so that P (hi + lo) keeps
-    // ~22 bits next to large values (both products go through the matrix cores)
-    float pr[4];
-    uint32_t pb[4], pl[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float pj = (s[j] == -INFINITY) ? 0.f : ex2(s[j] - m_new);
-      pb[j] = bits16<KVF>(pj);
-      pr[j] = val16<KVF>(pb[j]);
-      if (KVF) {
-        pl[j] = bits16<true>(pj - pr[j]);
-        pr[j] += val16<true>(pl[j]);
-      }
-    }
-    *reinterpret_cast<uint2*>(&L.p[c16 * kPStride + (16 * w + 4 * g) * 2]) =
-        make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16));
-    if (KVF)
-      *reinterpret_cast<uint2*>(&L.p_lo[c16 * kPStride + (16 * w + 4 * g) * 2]) =
-          make_uint2(pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16));
-    float ls = ((pr[0] + pr[1]) + pr[2]) + pr[3];
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    if (lane < 16) L.red_sum[w][c16] = ls;
-    if (w == 0 && lane < 16) L.alpha[c16] = alpha;
-    lds_barrier();
-    const float tsum = ((L.red_sum[0][c16] + L.red_sum[1][c16]) + L.red_sum[2][c16]) + L.red_sum[3][c16];
-    l_run = __builtin_fmaf(l_run, alpha, tsum);
-    m_run = m_new;
-
-    if (has_next) issue_tile<KVF, 8, 16>(lane, st, nad);
-
-    // ---- O[head 4g+j, dims 128w + 16nb + c16] = O * alpha + P V
-    {
-      float al[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) al[j] = L.alpha[4 * g + j];
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) O[nb][j] *= al[j];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int key0 = 8 * g + 32 * ks;
-        const uint4 pa = *reinterpret_cast<const uint4*>(&L.p[c16 * kPStride + key0 * 2]);
-        uint4 pa_lo = make_uint4(0u, 0u, 0u, 0u);
-        // fp8 rows: the code block of this wave's dims (block w; wave 3's dims 448..511 are
-        // the unscaled tail) carries each key's scale, which is folded into P
-        uint4 ps = pa, ps_lo = pa_lo, pt = pa, pt_lo = pa_lo;
-        if (KVF) {
-          pa_lo = *reinterpret_cast<const uint4*>(&L.p_lo[c16 * kPStride + key0 * 2]);
-          const float4 s0 = *reinterpret_cast<const float4*>(&L.scl[w][key0]);
-          const float4 s1 = *reinterpret_cast<const float4*>(&L.scl[w][key0 + 4]);
-          const float sk[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-          const uint32_t ph[4] = {pa.x, pa.y, pa.z, pa.w}, pl2[4] = {pa_lo.x, pa_lo.y, pa_lo.z, pa_lo.w};
-          uint32_t qh[4], ql[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float2 h2 = unpack16<true>(ph[i]), l2 = unpack16<true>(pl2[i]);
-            const float x0 = (h2.x + l2.x) * sk[2 * i], x1 = (h2.y + l2.y) * sk[2 * i + 1];
-            qh[i] = pack16<true>(x0, x1);
-            const float2 r2 = unpack16<true>(qh[i]);
-            ql[i] = pack16<true>(x0 - r2.x, x1 - r2.y);
-          }
-          ps = make_uint4(qh[0], qh[1], qh[2], qh[3]);
-          ps_lo = make_uint4(ql[0], ql[1], ql[2], ql[3]);
-          pt = w < 3 ? ps : pa;
-          pt_lo = w < 3 ? ps_lo : pa_lo;
-        }
-        const int r0 = key0 + (c16 >> 2);
-        uint4 vbs[8];
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          const int n0 = 128 * w + 16 * nb + 4 * (c16 & 3);
-          uint8_t* base = &L.k[r0 * kKStride + n0 * 2];
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + 4 * kKStride));
-          typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
-          const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          vbs[nb] = __builtin_bit_cast(uint4, both);
-        }
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          const uint4 vb = vbs[nb];
-          if (!KVF) {
-            O[nb] = mfma16<false>(pa, vb, O[nb]);
-          } else {
-            O[nb] = mfma16<true>(nb < 4 ? ps : pt, vb, O[nb]);
-            O[nb] = mfma16<true>(nb < 4 ? ps_lo : pt_lo, vb, O[nb]);
-          }
-        }
-      }
-    }
-
-    if (tile + 1 == ntile) {
-      // ---- chunk done: per-head (m, l) to the output layout, then fold or write
-      if (w == 0 && lane < 16) {
-        L.mc[c16] = m_run;
-        L.lc[c16] = l_run;
-      }
-      __syncthreads();
-      if (SPLIT) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int h = hg * kHG + 4 * g + j;
-          if (h < a.n_h) {
-            const int64_t base = ((int64_t)t * max_chunks + cc) * a.n_h + h;
-            float* po = ws_o + base * kDM + 128 * w + c16;
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) po[16 * nb] = O[nb][j];
-            if (w == 0 && c16 == 0) {
-              ws_ml[2 * base] = L.mc[4 * g + j];
-              ws_ml[2 * base + 1] = L.lc[4 * g + j];
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float fa, fb;
-          fold_step(fs[j], L.mc[4 * g + j], L.lc[4 * g + j], &fa, &fb);
-#pragma unroll
-          for (int nb = 0; nb < 8; ++nb) Ot[nb][j] = __builtin_fmaf(Ot[nb][j], fa, O[nb][j] * fb);
-        }
-      }
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      m_run = -INFINITY;
-      l_run = 0.f;
-    }
-    if (!has_next) break;
-    if (ntl == 0) ntile = tiles_in(ncc);
-    cc = ncc;
-    tile = ntl;
-  }
-
-  if (!SPLIT) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = hg * kHG + 4 * g + j;
-      const float inv = (fs[j].Z > 0.f) ? 1.0f / fs[j].Z : 0.f;
-      const int64_t orow = (int64_t)t * a.n_h + h;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int d = 128 * w + 16 * nb + c16;
-        const float x = Ot[nb][j] * inv;
-        const float partner = __shfl_xor(x, 1, 64);
-        if (h < a.n_h) store_out(a, orow, d, finalize_elem<ROPE_FAST>(x, partner, d, dn, ctx.p, F));
-      }
-      if (a.lse && w == 0 && c16 == 0 && h < a.n_h) a.lse[orow] = lse_natural(fs[j]);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------------------
-// bf16 rows, wave-pair variant: 8 waves per workgroup (two per SIMD, so one wave's LDS and
+// The kernel: 8 waves per workgroup (two per SIMD, so one wave's LDS and
 // memory latencies overlap the other's work).  Workgroup = (token, 16 heads, chunk) as
 // above; wave pair p = w % 4 owns rows 16p..16p+15 of every 64-slot tile and runs its own
 // online softmax over them; the two waves of a pair (half h2 = w / 4) each load and stage
 // 8 of the pair's rows, each computes the partial logits S^T of half the dims (the halves
 // are exchanged through LDS and added in a fixed order, so both hold the same logits), and
 // each accumulates half of the output dims, transposed: O^T[dim, head] += V^T P^T with
-// v_mfma_f32_16x16x16_bf16, whose B operand (P^T, 4 keys x 1 head per lane) is the logit
+// v_mfma_f32_16x16x16_{bf16,f16}, whose B operand (P^T, 4 keys x 1 head per lane) is the logit
 // accumulator layout itself and whose A operand (V^T, 4 keys of one dim per lane) is one
 // ds_read_b64_tr_b16 of the staged rows.  The four pair states of a chunk are merged in a
 // fixed order (pair 0..3) through LDS.  A pair raises its running max only when a tile's
 // max exceeds it by more than 8 (log2 units): P stays below 2^8 and O is rescaled only
 // then.
 constexpr float kMaxSlack = 8.0f;
-constexpr int kMergeStride = 260;
+constexpr int kMergeStride = 260;  // floats per head row of the merge scratch (256 dims + pad)
 
 // Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48) with the
 // row-swap permutes: v_permlane16_swap pairs rows (0,1) and (2,3), v_permlane32_swap the
@@ -709,14 +255,34 @@ __device__ __forceinline__ float rows_sum(float x) {
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}  // floats per head row of the merge scratch (256 dims + pad)
+}
 
-// Stage rows roff .. roff+7 of the pair's 16 (held in st.v[0..7]), then rotate the window
+// Stage rows roff .. roff+7 of the pair's 16 (held in st.v[0..7]) in the tile format (fp8
+// rows: codes in fp16, block scales to L.scl, bf16 tail in fp16), then rotate the window
 // rows among them and write the rotation residuals of those rows.
+template <bool KVF>
 __device__ __forceinline__ void store_rows8(MfmaLds& L, const AttendArgs& a, const TileStage& st, int p, int roff,
                                             int lane, const FreqLds& F) {
+  if (!KVF) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&L.k[(16 * p + roff + i) * kKStride + 16 * lane]) = st.v[i];
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&L.k[(16 * p + roff + i) * kKStride + 16 * lane]) = st.v[i];
+  } else if (lane < kSplitCodeLanes) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 v = st.v[i];
+      uint4* dst = reinterpret_cast<uint4*>(&L.k[(16 * p + roff + i) * kKStride + 32 * lane]);
+      dst[0] = make_uint4(fp8x2_to_f16x2<false>(v.x), fp8x2_to_f16x2<true>(v.x), fp8x2_to_f16x2<false>(v.y),
+                          fp8x2_to_f16x2<true>(v.y));
+      dst[1] = make_uint4(fp8x2_to_f16x2<false>(v.z), fp8x2_to_f16x2<true>(v.z), fp8x2_to_f16x2<false>(v.w),
+                          fp8x2_to_f16x2<true>(v.w));
+      if ((lane & 7) == 0) L.scl[lane >> 3][16 * p + roff + i] = st.sc[i];
+    }
+  } else if (lane < kSplitLanes) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<uint4*>(&L.k[(16 * p + roff + i) * kKStride + 2 * (kDM - kSplitBf16Dims) +
+                                     16 * (lane - kSplitCodeLanes)]) = from_bf16<true>(st.v[i]);
+  }
   if (st.win != 0u && lane < kRopeMax / 2) {
     const int d = kDM - kRopeMax + 2 * lane;
     const int dn = kDM - a.rope.dims;
@@ -739,11 +305,11 @@ __device__ __forceinline__ void store_rows8(MfmaLds& L, const AttendArgs& a, con
         c = cn;
       }
       if (((st.win >> it) & 1u) && d >= dn) {
-        const float2 y = rotate2(unpack16<false>(u[i]), c, s);
-        const uint32_t hi = pack16<false>(y.x, y.y);
-        const float2 yh = unpack16<false>(hi);
+        const float2 y = rotate2(unpack16<KVF>(u[i]), c, s);
+        const uint32_t hi = pack16<KVF>(y.x, y.y);
+        const float2 yh = unpack16<KVF>(hi);
         *reinterpret_cast<uint32_t*>(&L.k[(16 * p + it) * kKStride + d * 2]) = hi;
-        res = pack16<false>(y.x - yh.x, y.y - yh.y);
+        res = pack16<KVF>(y.x - yh.x, y.y - yh.y);
       }
       *reinterpret_cast<uint32_t*>(&L.klo[(16 * p + it) * kLoStride + 4 * lane]) = res;
     }
@@ -753,22 +319,35 @@ __device__ __forceinline__ void store_rows8(MfmaLds& L, const AttendArgs& a, con
 // Loads of rows roff + I0 .. roff + I1 - 1 of the pair's 16 into st.v[I0 .. I1-1].  A
 // wave's loads stall at issue once the CU's memory pipeline is full, so the step issues
 // its eight in pairs between the compute phases.
-template <int I0, int I1>
+template <int I0, int I1, bool KVF>
 __device__ __forceinline__ void issue_rows(int lane, TileStage& st, const TileAddr& ad, int roff) {
 #pragma unroll
   for (int i = I0; i < I1; ++i) {
     st.v[i] = make_uint4(0u, 0u, 0u, 0u);
-    if ((st.valid >> (roff + i)) & 1u) st.v[i] = load_global_u4(readlane_u64(ad.row, roff + i), lane);
+    st.sc[i] = 0.f;
+    if ((st.valid >> (roff + i)) & 1u) {
+      const uint64_t rowp = readlane_u64(ad.row, roff + i);
+      if (!KVF) {
+        st.v[i] = load_global_u4(rowp, lane);
+      } else {
+        if (lane < kSplitLanes) st.v[i] = load_global_u4(rowp, lane);
+        if (lane < kSplitCodeLanes && (lane & 7) == 0)
+          st.sc[i] = load_global_f32(readlane_u64(ad.sc, roff + i), lane >> 3);
+      }
+    }
   }
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool KVF>
 __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* __restrict__ ws_o,
                                                           float* __restrict__ ws_ml, int n_hg, int max_chunks,
                                                           int chunk_slots, int n_logical) {
   __shared__ MfmaLds L;
   __shared__ FreqLds F;
   __shared__ f32x4_t sx[8][64];  // partial logits of each wave
+  // single launch: the folded output of every thread's 16 values, element-major (each
+  // thread touches only its own entries; kept in LDS to spare registers)
+  __shared__ float ofold[SPLIT ? 1 : 16 * 512];
   const int n_phys = gridDim.x;
   const int per_xcd = n_phys / 8;
   const int lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -832,23 +411,27 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
 
   TileStage st;
   {
-    const TileAddr ad = resolve_tile<false>(a, ctx, n_ent, s_lo, p, lane, st, L.sidx, s_lo);
-    issue_rows<0, 8>(lane, st, ad, roff);
+    const TileAddr ad = resolve_tile<KVF>(a, ctx, n_ent, s_lo, p, lane, st, L.sidx, s_lo);
+    issue_rows<0, 8, KVF>(lane, st, ad, roff);
   }
 
-  // query fragments of this wave's half of the dims: chunks kk = 8 h2 + i
+  // query fragments of this wave's half of the dims (chunks kk = 8 h2 + i), in the tile
+  // format
   uint4 qf[8];
   uint4 qlo[2];  // half 1: residuals of the rotated dims among 448..511
   {
     const uint8_t* qrow = &L.k[c16 * kKStride + (8 * g + 256 * h2) * 2];
+    uint4 raw[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qf[i] = *reinterpret_cast<const uint4*>(qrow + 64 * i);
+    for (int i = 0; i < 8; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + 64 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qf[i] = from_bf16<KVF>(raw[i]);
     qlo[0] = qlo[1] = make_uint4(0u, 0u, 0u, 0u);
     if (h2 == 1) {
 #pragma unroll
       for (int i = 6; i < 8; ++i) {
         const int d0 = 8 * g + 256 + 32 * i;
-        if (d0 >= dn) rotate_chunk<false>(qf[i], ctx.p, F, (d0 - dn) >> 1, &qf[i], &qlo[i - 6]);
+        if (d0 >= dn) rotate_chunk<KVF>(raw[i], ctx.p, F, (d0 - dn) >> 1, &qf[i], &qlo[i - 6]);
       }
     }
   }
@@ -857,9 +440,10 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
   const int th = tid >> 5, td = tid & 31;
   const int h_m = hg * kHG + th;
   FoldState fs = fold_init(h_m < a.n_h ? a.sink[h_m] * kLog2e : -INFINITY);
-  float Ot[16];
+  if (!SPLIT) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) Ot[i] = 0.f;
+    for (int i = 0; i < 16; ++i) ofold[i * 512 + tid] = 0.f;
+  }
   f32x4_t OT[16];  // O^T[dim 256 h2 + 16nb + 4g + j, head c16]
 #pragma unroll
   for (int nb = 0; nb < 16; ++nb) OT[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -874,7 +458,7 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
 
   while (true) {
     lds_barrier();  // the pair's previous rows (and the query block) fully consumed
-    store_rows8(L, a, st, p, roff, lane, F);
+    store_rows8<KVF>(L, a, st, p, roff, lane, F);
     const uint32_t valid = st.valid, winm = st.win;
     lds_barrier();  // the pair's 16 rows staged
 
@@ -886,32 +470,52 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
     const bool has_next = ncc < c_end;
     TileAddr nad = {0u, 0u};
     if (has_next) {
-      nad = resolve_tile<false>(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, p, lane, st, L.sidx, s_lo);
-      issue_rows<0, 2>(lane, st, nad, roff);
+      nad = resolve_tile<KVF>(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, p, lane, st, L.sidx, s_lo);
+      issue_rows<0, 2, KVF>(lane, st, nad, roff);
     }
 
     // ---- S^T = K Q^T for the pair's keys: this wave's half of the dims, then the
-    // halves exchanged and added (half 0 + half 1)
+    // halves exchanged and added (half 0 + half 1).  fp8 rows: partial products per code
+    // block (this half: blocks 2 h2 and 2 h2 + 1; half 1's last two chunks are the bf16
+    // tail), scaled in fp32.
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float4 sA = make_float4(1.f, 1.f, 1.f, 1.f), sB = sA;  // block scales of keys 16p + 4g + j
     {
+      f32x4_t part[3];
+#pragma unroll
+      for (int b = 0; b < 3; ++b) part[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const uint8_t* krow = &L.k[(16 * p + c16) * kKStride + (16 * g + 512 * h2)];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        const int b = KVF ? (i < 4 ? 0 : (i < 6 ? 1 : 2)) : 0;
         const uint4 ka = *reinterpret_cast<const uint4*>(krow + 64 * i);
-        acc = mfma16<false>(ka, qf[i], acc);
-        if (i >= 6 && h2 == 1) acc = mfma16<false>(ka, qlo[i - 6], acc);
+        part[b] = mfma16<KVF>(ka, qf[i], part[b]);
+        if (i >= 6 && h2 == 1) part[KVF ? 2 : 0] = mfma16<KVF>(ka, qlo[i - 6], part[KVF ? 2 : 0]);
       }
       if (winm != 0u && h2 == 1) {
         const uint8_t* lrow = &L.klo[(16 * p + c16) * kLoStride + 16 * g];
 #pragma unroll
         for (int i = 6; i < 8; ++i) {
           const uint4 kl = *reinterpret_cast<const uint4*>(lrow + 64 * (i - 6));
-          acc = mfma16<false>(kl, qf[i], acc);
+          part[KVF ? 2 : 0] = mfma16<KVF>(kl, qf[i], part[KVF ? 2 : 0]);
+        }
+      }
+      if (!KVF) {
+        acc = part[0];
+      } else {
+        sA = *reinterpret_cast<const float4*>(&L.scl[2 * h2][16 * p + 4 * g]);
+        sB = *reinterpret_cast<const float4*>(&L.scl[2 * h2 + 1][16 * p + 4 * g]);
+        const float a0[4] = {sA.x, sA.y, sA.z, sA.w}, b0[4] = {sB.x, sB.y, sB.z, sB.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x = part[0][j] * a0[j];
+          x = __builtin_fmaf(part[1][j], b0[j], x);
+          acc[j] = __builtin_fmaf(part[2][j], h2 == 0 ? b0[j] : 1.0f, x);
         }
       }
     }
     sx[w][lane] = acc;
-    if (has_next) issue_rows<2, 4>(lane, st, nad, roff);
+    if (has_next) issue_rows<2, 4, KVF>(lane, st, nad, roff);
     lds_barrier();
     {
       const f32x4_t other = sx[w ^ 4][lane];
@@ -925,18 +529,24 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
     const float mx = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     const float m_new = (mx > m_run + kMaxSlack) ? mx : m_run;
     const float alpha = rescale(m_run, m_new);
-    uint32_t pb[4];
+    uint32_t pb[4];  // bf16 rows: P in bf16
+    float pr[4];     // the values of P the sums and products use
     float ls = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float pj = (sv[j] == -INFINITY) ? 0.f : ex2(sv[j] - m_new);
-      pb[j] = f32_to_bf16_bits(pj);
-      ls += __uint_as_float(pb[j] << 16);
+      if (!KVF) {
+        pb[j] = f32_to_bf16_bits(pj);
+        pr[j] = __uint_as_float(pb[j] << 16);
+      } else {
+        pr[j] = pj;  // rounded per value block below
+      }
+      ls += pr[j];
     }
     ls = rows_sum(ls);
     l_run = __builtin_fmaf(l_run, alpha, ls);
     m_run = m_new;
-    if (has_next) issue_rows<4, 6>(lane, st, nad, roff);
+    if (has_next) issue_rows<4, 6, KVF>(lane, st, nad, roff);
 
     // ---- O^T[dim, head] = O^T * alpha + V^T P^T over this wave's 256 dims
     if (__ballot(alpha != 1.0f) != 0ull) {
@@ -944,15 +554,37 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
       for (int nb = 0; nb < 16; ++nb) OT[nb] *= alpha;
     }
     {
-      const i16x4_t pv = __builtin_bit_cast(i16x4_t, make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)));
       uint8_t* vbase = &L.k[(16 * p + 4 * g + (c16 >> 2)) * kKStride + (256 * h2 + 4 * (c16 & 3)) * 2];
+      if (!KVF) {
+        const i16x4_t pv = __builtin_bit_cast(i16x4_t, make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)));
 #pragma unroll
-      for (int nb = 0; nb < 16; ++nb) {
-        const i16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vbase + 32 * nb));
-        OT[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pv, OT[nb], 0, 0, 0);
+        for (int nb = 0; nb < 16; ++nb) {
+          const i16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vbase + 32 * nb));
+          OT[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pv, OT[nb], 0, 0, 0);
+        }
+      } else {
+        // fp8 rows: the value block's scale of each key folded into P, rounded to fp16:
+        // set A for dims 256 h2 .. +127, set B for the next 64 (h2 = 1) or 128 (h2 = 0)
+        // dims, and for half 1's last 64 dims (the bf16 tail) P itself
+        const float a0[4] = {sA.x, sA.y, sA.z, sA.w}, b0[4] = {sB.x, sB.y, sB.z, sB.w};
+        f16x4_t ph[3];
+#pragma unroll
+        for (int set = 0; set < 3; ++set)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float sc = set == 0 ? a0[j] : (set == 1 ? b0[j] : (h2 == 0 ? b0[j] : 1.0f));
+            ph[set][j] = (_Float16)(pr[j] * sc);
+          }
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) {
+          const int set = nb < 8 ? 0 : (nb < 12 ? 1 : 2);
+          const f16x4_t vt = __builtin_bit_cast(
+              f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vbase + 32 * nb)));
+          OT[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vt, ph[set], OT[nb], 0, 0, 0);
+        }
       }
     }
-    if (has_next) issue_rows<6, 8>(lane, st, nad, roff);
+    if (has_next) issue_rows<6, 8, KVF>(lane, st, nad, roff);
 
     if (tile + 1 == ntile) {
       // ---- chunk done: merge the four pair states in pair order
@@ -1002,7 +634,7 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              float& o = Ot[8 * r + 4 * i4 + e];
+              float& o = ofold[(8 * r + 4 * i4 + e) * 512 + tid];
               o = __builtin_fmaf(o, fa, sum[e] * fb);
             }
           }
@@ -1027,7 +659,7 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
     for (int r = 0; r < 2; ++r) {
       float x[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = Ot[8 * r + i] * inv;
+      for (int i = 0; i < 8; ++i) x[i] = ofold[(8 * r + i) * 512 + tid] * inv;
       const int d0 = 256 * r + 8 * td;
       *reinterpret_cast<uint4*>(a.out.data + orow * a.out.stride + d0 * 2) = finalize8(x, d0, dn, ctx.p, F);
     }
@@ -1111,11 +743,11 @@ static void launch_attend_mfma_kernel(const AttendArgs& a, float* ws_o, float* w
                                       int64_t n_log, hipStream_t stream) {
   const int64_t n_phys = (n_log + 7) / 8 * 8;
   if (a.kv.dtype == DT_KV_SPLIT)
-    hipLaunchKernelGGL((attend_mfma_kernel<SPLIT, true>), dim3((unsigned)n_phys), dim3(256), 0, stream, a, ws_o, ws_ml,
+    hipLaunchKernelGGL((attend_pair_kernel<SPLIT, true>), dim3((unsigned)n_phys), dim3(512), 0, stream, a, ws_o, ws_ml,
                        n_hg, mc, C, (int)n_log);
   else
-    hipLaunchKernelGGL((attend_pair_kernel<SPLIT>), dim3((unsigned)n_phys), dim3(512), 0, stream, a, ws_o, ws_ml, n_hg,
-                       mc, C, (int)n_log);
+    hipLaunchKernelGGL((attend_pair_kernel<SPLIT, false>), dim3((unsigned)n_phys), dim3(512), 0, stream, a, ws_o,
+                       ws_ml, n_hg, mc, C, (int)n_log);
 }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -56,8 +56,8 @@ struct __align__(16) MfmaLds {
 struct TileStage {
   uint4 v[16];      // row it of the wave's share, bytes 16*lane .. 16*lane+15 of the stored row
   float sc[16];     // fp8 rows: lanes 0, 8, 16, 24 hold the scale of code block lane / 8
-  uint32_t valid;   // bit it: row it of the pair's 16 present
-  uint32_t win;     // bit it: window row (rotated when staged)
+  uint64_t valid;   // bit it: row it present (a pair's 16 rows, or a tile's 64)
+  uint64_t win;     // bit it: window row (rotated when staged)
   int64_t pos0;     // position of window row it is pos0 + it
 };
 
@@ -184,8 +184,8 @@ __device__ __forceinline__ TileAddr resolve_tile(const AttendArgs& a, const Toke
   r.row = 0;
   r.pos = 0;
   if (lane < 16) r = resolve_slot_lds(a, ctx, n_ent, s0 + 16 * w + lane, sidx, s_lo);
-  st.valid = (uint32_t)__ballot(lane < 16 && r.kind != 0);
-  st.win = (uint32_t)__ballot(lane < 16 && r.kind == 2);
+  st.valid = __ballot(lane < 16 && r.kind != 0);
+  st.win = __ballot(lane < 16 && r.kind == 2);
   st.pos0 = ctx.p - a.n_win + 1 + (s0 + 16 * w - n_ent);
   const bool win = r.kind == 2;
   constexpr int nb = (kDM - kSplitBf16Dims + kKvBlock - 1) / kKvBlock;
@@ -257,61 +257,63 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Stage rows roff .. roff+7 of the pair's 16 (held in st.v[0..7]) in the tile format (fp8
-// rows: codes in fp16, block scales to L.scl, bf16 tail in fp16), then rotate the window
-// rows among them and write the rotation residuals of those rows.
-template <bool KVF>
-__device__ __forceinline__ void store_rows8(MfmaLds& L, const AttendArgs& a, const TileStage& st, int p, int roff,
-                                            int lane, const FreqLds& F) {
+// Stage rows row0 + i, i < NR, of the tile from st.v[i] in the tile format (fp8 rows: codes
+// in fp16, block scales to L.scl, bf16 tail in fp16); their window bits and positions are
+// bit and offset it0 + i of st.  Then, when `winmask` (the rows whose logits read the
+// residual tile together with these) holds a window row, rotate the window rows among them
+// and write the rotation residuals of these rows (zero for the others).
+template <bool KVF, int NR>
+__device__ __forceinline__ void store_rows(MfmaLds& L, const AttendArgs& a, const TileStage& st, int row0, int it0,
+                                           uint64_t winmask, int lane, const FreqLds& F) {
   if (!KVF) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&L.k[(16 * p + roff + i) * kKStride + 16 * lane]) = st.v[i];
+    for (int i = 0; i < NR; ++i) *reinterpret_cast<uint4*>(&L.k[(row0 + i) * kKStride + 16 * lane]) = st.v[i];
   } else if (lane < kSplitCodeLanes) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NR; ++i) {
       const uint4 v = st.v[i];
-      uint4* dst = reinterpret_cast<uint4*>(&L.k[(16 * p + roff + i) * kKStride + 32 * lane]);
+      uint4* dst = reinterpret_cast<uint4*>(&L.k[(row0 + i) * kKStride + 32 * lane]);
       dst[0] = make_uint4(fp8x2_to_f16x2<false>(v.x), fp8x2_to_f16x2<true>(v.x), fp8x2_to_f16x2<false>(v.y),
                           fp8x2_to_f16x2<true>(v.y));
       dst[1] = make_uint4(fp8x2_to_f16x2<false>(v.z), fp8x2_to_f16x2<true>(v.z), fp8x2_to_f16x2<false>(v.w),
                           fp8x2_to_f16x2<true>(v.w));
-      if ((lane & 7) == 0) L.scl[lane >> 3][16 * p + roff + i] = st.sc[i];
+      if ((lane & 7) == 0) L.scl[lane >> 3][row0 + i] = st.sc[i];
     }
   } else if (lane < kSplitLanes) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint4*>(&L.k[(16 * p + roff + i) * kKStride + 2 * (kDM - kSplitBf16Dims) +
+    for (int i = 0; i < NR; ++i)
+      *reinterpret_cast<uint4*>(&L.k[(row0 + i) * kKStride + 2 * (kDM - kSplitBf16Dims) +
                                      16 * (lane - kSplitCodeLanes)]) = from_bf16<true>(st.v[i]);
   }
-  if (st.win != 0u && lane < kRopeMax / 2) {
+  if (winmask != 0u && lane < kRopeMax / 2) {
     const int d = kDM - kRopeMax + 2 * lane;
     const int dn = kDM - a.rope.dims;
-    uint32_t u[8];
+    uint32_t u[NR];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] = *reinterpret_cast<const uint32_t*>(&L.k[(16 * p + roff + i) * kKStride + d * 2]);
+    for (int i = 0; i < NR; ++i) u[i] = *reinterpret_cast<const uint32_t*>(&L.k[(row0 + i) * kKStride + d * 2]);
     // the rows' positions are consecutive: rotate the angle of the first by one position
-    // per row (angle addition; error ~1e-6 after the 7 steps)
+    // per row (angle addition; error ~1e-6 after the 15 steps)
     const int q = d >= dn ? (d - dn) >> 1 : 0;
     float c, s, c1, s1;
-    rope_cs_mode<ROPE_FAST>(st.pos0 + roff, F, q, &c, &s);
+    rope_cs_mode<ROPE_FAST>(st.pos0 + it0, F, q, &c, &s);
     rope_cs_mode<ROPE_FAST>(1, F, q, &c1, &s1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int it = roff + i;
+    for (int i = 0; i < NR; ++i) {
+      const int it = it0 + i;
       uint32_t res = 0u;
       if (i > 0) {
         const float cn = __builtin_fmaf(c, c1, -(s * s1));
         s = __builtin_fmaf(s, c1, c * s1);
         c = cn;
       }
-      if (((st.win >> it) & 1u) && d >= dn) {
+      if (((st.win >> it) & 1ull) && d >= dn) {
         const float2 y = rotate2(unpack16<KVF>(u[i]), c, s);
         const uint32_t hi = pack16<KVF>(y.x, y.y);
         const float2 yh = unpack16<KVF>(hi);
-        *reinterpret_cast<uint32_t*>(&L.k[(16 * p + it) * kKStride + d * 2]) = hi;
+        *reinterpret_cast<uint32_t*>(&L.k[(row0 + i) * kKStride + d * 2]) = hi;
         res = pack16<KVF>(y.x - yh.x, y.y - yh.y);
       }
-      *reinterpret_cast<uint32_t*>(&L.klo[(16 * p + it) * kLoStride + 4 * lane]) = res;
+      *reinterpret_cast<uint32_t*>(&L.klo[(row0 + i) * kLoStride + 4 * lane]) = res;
     }
   }
 }
@@ -325,7 +327,7 @@ __device__ __forceinline__ void issue_rows(int lane, TileStage& st, const TileAd
   for (int i = I0; i < I1; ++i) {
     st.v[i] = make_uint4(0u, 0u, 0u, 0u);
     st.sc[i] = 0.f;
-    if ((st.valid >> (roff + i)) & 1u) {
+    if ((st.valid >> (roff + i)) & 1ull) {
       const uint64_t rowp = readlane_u64(ad.row, roff + i);
       if (!KVF) {
         st.v[i] = load_global_u4(rowp, lane);
@@ -458,8 +460,8 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
 
   while (true) {
     lds_barrier();  // the pair's previous rows (and the query block) fully consumed
-    store_rows8<KVF>(L, a, st, p, roff, lane, F);
-    const uint32_t valid = st.valid, winm = st.win;
+    store_rows<KVF, 8>(L, a, st, 16 * p + roff, roff, st.win, lane, F);
+    const uint32_t valid = (uint32_t)st.valid, winm = (uint32_t)st.win;
     lds_barrier();  // the pair's 16 rows staged
 
     int ncc = cc, ntl = tile + 1;
@@ -667,6 +669,246 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Long bf16 key lists (CSA with k >= 1024: prefill, long-context layers): one workgroup
+// per (token, 64 heads), 4 waves, wave w owns heads 16w..16w+15 for all 512 dims.  Each
+// 64-row tile is staged once for all 64 heads (16 rows per wave), so a gathered row is read
+// once per token instead of once per 16 heads.  A wave computes S^T for all 64 keys of the
+// tile (4 key blocks), runs the online softmax of its heads over them alone, and
+// accumulates O^T[512 dims x 16 heads] with v_mfma_f32_16x16x32: the B operand (P^T) joins
+// the logit accumulators of two key blocks (k index 8g + i <-> key 16(2kp + i / 4) + 4g +
+// i % 4), the A operand (V^T) is the two matching transposing reads.  No cross-wave state.
+// Such lists are one chunk (the chunk length rule), so the fold from the sink takes the one
+// chunk state at the end.  (fp8 rows stay on the pair kernel: with per-block scales this
+// kernel's 64-key tiles need more registers than a wave has.)
+constexpr int kHeadsLong = 64;       // heads per workgroup in this kernel
+constexpr int kLongKeys = 1024;      // bf16 CSA key lists from this length use this kernel
+
+// Slots s0 .. s0+63 of the tile: lane l resolves slot s0 + l.
+__device__ __forceinline__ TileAddr resolve_tile64(const AttendArgs& a, const TokenCtx& ctx, int64_t n_ent,
+                                                   int64_t s0, int lane, TileStage& st, const int32_t* sidx,
+                                                   int64_t s_lo) {
+  const SlotRef r = resolve_slot_lds(a, ctx, n_ent, s0 + lane, sidx, s_lo);
+  st.valid = __ballot(r.kind != 0);
+  st.win = __ballot(r.kind == 2);
+  st.pos0 = ctx.p - a.n_win + 1 + (s0 - n_ent);
+  const bool win = r.kind == 2;
+  TileAddr ad;
+  ad.row = reinterpret_cast<uint64_t>(win ? a.tok.data : a.kv.data) + (uint64_t)(r.row * (win ? a.tok.stride : a.kv.stride));
+  ad.sc = 0u;
+  return ad;
+}
+
+// Final values of 4 consecutive output dims d0..d0+3 of one head: inverse RoPE of the two
+// pairs in the rotary range, rounded to bf16 (same arithmetic as finalize8).
+__device__ __forceinline__ uint2 finalize4(const float* x, int d0, int dn, int64_t p, const FreqLds& F) {
+  uint32_t w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float2 y = make_float2(x[2 * i], x[2 * i + 1]);
+    const int d = d0 + 2 * i;
+    if (d >= dn) {
+      float c, s;
+      rope_cs_mode<ROPE_FAST>(p, F, (d - dn) >> 1, &c, &s);
+      y = rotate2(y, c, -s);
+    }
+    w[i] = pack_bf16(y.x, y.y);
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+__global__ void __launch_bounds__(256) attend_heads_kernel(AttendArgs a, int n_hg, int chunk_slots, int n_logical) {
+  constexpr bool KVF = false;
+  __shared__ MfmaLds L;
+  __shared__ FreqLds F;
+  const int n_phys = gridDim.x;
+  const int per_xcd = n_phys / 8;
+  const int lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (lid >= n_logical) return;
+  const int hg = lid % n_hg;
+  const int t = lid / n_hg;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int dn = kDM - a.rope.dims;
+  const int h = hg * kHeadsLong + 16 * w + c16;  // the head of this lane's logit and output columns
+  const bool h_ok = h < a.n_h;
+
+  // query fragments of head h, dims 8g + 32kk .. +7: loaded straight into registers
+  uint4 raw[16];
+  {
+    const uint8_t* qrow = a.q.data + ((int64_t)t * a.n_h + (h_ok ? h : 0)) * a.q.stride;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+      raw[kk] = h_ok ? *reinterpret_cast<const uint4*>(qrow + (8 * g + 32 * kk) * 2) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  load_freqs(F, a.rope);
+
+  const TokenCtx ctx = token_ctx(a.S, t);
+  const int64_t n_ent = entry_slots(a, ctx);
+  const int64_t n_slots = n_ent + a.n_win;
+  const int c_end = (int)((n_slots + chunk_slots - 1) / chunk_slots);
+  {
+    const int32_t* src = a.idx + (int64_t)t * a.k;
+    for (int s = tid; s < a.k; s += 256) L.sidx[s] = src[s];
+  }
+  __syncthreads();
+
+  TileStage st;
+  {
+    const TileAddr ad = resolve_tile64(a, ctx, n_ent, 0, lane, st, L.sidx, 0);
+    issue_rows<0, 16, KVF>(lane, st, ad, 16 * w);
+  }
+
+  uint4 qf[16];
+  uint4 qlo[2];
+#pragma unroll
+  for (int kk = 0; kk < 14; ++kk) qf[kk] = from_bf16<KVF>(raw[kk]);
+#pragma unroll
+  for (int kk = 14; kk < 16; ++kk) {
+    const int d0 = 8 * g + 32 * kk;
+    if (d0 >= dn) {
+      rotate_chunk<KVF>(raw[kk], ctx.p, F, (d0 - dn) >> 1, &qf[kk], &qlo[kk - 14]);
+    } else {
+      qf[kk] = from_bf16<KVF>(raw[kk]);
+      qlo[kk - 14] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  FoldState fs = fold_init(h_ok ? a.sink[h] * kLog2e : -INFINITY);
+  f32x4_t OT[32];  // O^T[dim 16nb + 4g + j, head h]
+#pragma unroll
+  for (int nb = 0; nb < 32; ++nb) OT[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto tiles_in = [&](int c) -> int {
+    const int64_t rem = n_slots - (int64_t)c * chunk_slots;
+    const int64_t len = rem < chunk_slots ? rem : chunk_slots;
+    return (int)((len + kT - 1) / kT);
+  };
+  int cc = 0, tile = 0, ntile = tiles_in(cc);
+
+  while (true) {
+    lds_barrier();  // previous tile fully consumed
+    store_rows<KVF, 16>(L, a, st, 16 * w, 16 * w, (st.win >> (16 * w)) & 0xffffull, lane, F);
+    const uint64_t valid = st.valid, winm = st.win;
+    lds_barrier();  // tile staged
+
+    int ncc = cc, ntl = tile + 1;
+    if (ntl == ntile) {
+      ncc = cc + 1;
+      ntl = 0;
+    }
+    const bool has_next = ncc < c_end;
+    TileAddr nad = {0u, 0u};
+    if (has_next) {
+      nad = resolve_tile64(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, lane, st, L.sidx, 0);
+      issue_rows<0, 4, KVF>(lane, st, nad, 16 * w);
+    }
+
+    // ---- S^T = K Q^T, key block kb = keys 16kb .. 16kb+15 of the tile
+    float sv[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = &L.k[(16 * kb + c16) * kKStride + 16 * g];
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(krow + 64 * kk);
+        acc = mfma16<false>(ka, qf[kk], acc);
+        if (kk >= 14) acc = mfma16<false>(ka, qlo[kk - 14], acc);
+      }
+      if (((winm >> (16 * kb)) & 0xffffull) != 0ull) {
+        const uint8_t* lrow = &L.klo[(16 * kb + c16) * kLoStride + 16 * g];
+#pragma unroll
+        for (int kk = 14; kk < 16; ++kk)
+          acc = mfma16<false>(*reinterpret_cast<const uint4*>(lrow + 64 * (kk - 14)), qf[kk], acc);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sv[kb][j] = ((valid >> (16 * kb + 4 * g + j)) & 1ull) ? acc[j] * a.scale_log2 : -INFINITY;
+      __builtin_amdgcn_sched_barrier(0);  // one key block's partials live at a time
+    }
+    if (has_next) issue_rows<4, 8, KVF>(lane, st, nad, 16 * w);
+
+    // ---- online softmax of head h over the tile's 64 keys
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(sv[kb][0], sv[kb][1]), fmaxf(sv[kb][2], sv[kb][3])));
+    mx = rows_max(mx);
+    const float m_new = (mx > m_run + kMaxSlack) ? mx : m_run;
+    const float alpha = rescale(m_run, m_new);
+    float pr[4][4];
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pj = (sv[kb][j] == -INFINITY) ? 0.f : ex2(sv[kb][j] - m_new);
+        pr[kb][j] = __uint_as_float(f32_to_bf16_bits(pj) << 16);
+        ls += pr[kb][j];
+      }
+    ls = rows_sum(ls);
+    l_run = __builtin_fmaf(l_run, alpha, ls);
+    m_run = m_new;
+    if (has_next) issue_rows<8, 12, KVF>(lane, st, nad, 16 * w);
+
+    // ---- O^T[dim, head] = O^T * alpha + V^T P^T
+    if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+      for (int nb = 0; nb < 32; ++nb) OT[nb] *= alpha;
+    }
+    {
+      // B operands: keys {16(2kp) + 4g + i, 16(2kp+1) + 4g + i}, bf16
+      uint4 pk[2];
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = pr[2 * kp + i / 4][i % 4];
+        pk[kp] = make_uint4(pack16<false>(x[0], x[1]), pack16<false>(x[2], x[3]), pack16<false>(x[4], x[5]),
+                            pack16<false>(x[6], x[7]));
+      }
+#pragma unroll
+      for (int nb = 0; nb < 32; ++nb) {
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          uint8_t* base = &L.k[(32 * kp + 4 * g + (c16 >> 2)) * kKStride + (16 * nb + 4 * (c16 & 3)) * 2];
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + 16 * kKStride));
+          typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
+          const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          OT[nb] = mfma16<false>(__builtin_bit_cast(uint4, both), pk[kp], OT[nb]);
+        }
+      }
+    }
+    if (has_next) issue_rows<12, 16, KVF>(lane, st, nad, 16 * w);
+
+    if (!has_next) break;
+    if (ntl == 0) ntile = tiles_in(ncc);
+    cc = ncc;
+    tile = ntl;
+  }
+
+  // the fold from the sink over the single chunk: O = 0 * fa + O_chunk * fb
+  float fa, fb;
+  fold_step(fs, m_run, l_run, &fa, &fb);
+  if (h_ok) {
+    const float inv = (fs.Z > 0.f) ? 1.0f / fs.Z : 0.f;
+    const int64_t orow = (int64_t)t * a.n_h + h;
+#pragma unroll
+    for (int nb = 0; nb < 32; ++nb) {
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = __builtin_fmaf(0.f, fa, OT[nb][j] * fb) * inv;
+      const int d0 = 16 * nb + 4 * g;
+      *reinterpret_cast<uint2*>(a.out.data + orow * a.out.stride + d0 * 2) = finalize4(x, d0, dn, ctx.p, F);
+    }
+    if (a.lse && g == 0) a.lse[orow] = lse_natural(fs);
+  }
+}
+
 // Fold of the chunk partials written by the split launch, in chunk order from the sink:
 // one wave per head, each lane 8 consecutive dims; same arithmetic as the single launch.
 // The first kCB chunks are requested together with the token record, before it is read.
@@ -750,9 +992,22 @@ static void launch_attend_mfma_kernel(const AttendArgs& a, float* ws_o, float* w
                        ws_ml, n_hg, mc, C, (int)n_log);
 }
 
+// Which kernel a call uses depends on the operation's parameters only (the key list
+// length), never on the batch, so a token's bits do not depend on the batch either.
+static bool attend_long_lists(const AttendArgs& a) { return a.csa && a.k >= kLongKeys && a.kv.dtype == DT_BF16; }
+
 hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (attend_long_lists(a)) {
+    const int n_hg = (a.n_h + kHeadsLong - 1) / kHeadsLong;
+    const int C = chunk_slots_for(a.csa, a.k, a.n_win, a.kv.dtype);
+    const int64_t n_log = (int64_t)a.S.total_q * n_hg;
+    const int64_t n_phys = (n_log + 7) / 8 * 8;
+    hipLaunchKernelGGL(attend_heads_kernel, dim3((unsigned)n_phys), dim3(256), 0, stream, a, n_hg, C,
+                       (int)n_log);
+    return hipGetLastError();
+  }
   const int n_hg = (a.n_h + kHG - 1) / kHG;
-  const int C = chunk_slots_for(a.csa, a.k, a.n_win);
+  const int C = chunk_slots_for(a.csa, a.k, a.n_win, a.kv.dtype);
   const int64_t mc = attend_max_chunks(a);
   const size_t need = attend_workspace_bytes(a);
   const int64_t single = (int64_t)a.S.total_q * n_hg;

@@ -301,6 +301,7 @@ ATTEND_CASES = [
     (ops.KV_SPLIT, 512, 64, False, 128, 0, 128),
     # (..., outliers)
     (ops.BF16, 512, 64, True, 4, 512, 128, True),
+    (ops.BF16, 512, 64, True, 4, 1024, 128, True),
     (ops.KV_SPLIT, 512, 64, True, 4, 1024, 128, True),
 ]
 

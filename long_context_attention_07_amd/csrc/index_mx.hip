@@ -11,12 +11,17 @@
 // its key fragment (16 bytes of one key row) and its scale byte straight from memory: no
 // LDS staging, one coalesced 1 KiB load per 16 entries per wave.
 //
-// Workgroup = (block of QB consecutive query rows, range of 1024 entries), 4 waves; the
-// block's queries of one sequence share every key fragment (QB x 4 MFMAs per fragment), so
-// causal prefill reuses each key across QB queries.  Rows of a block that belong to
-// another sequence are handled as a separate run with their own keys.  Every score is the
-// same MFMA arithmetic on its own query row and key column followed by the head sum in a
-// fixed order, so it does not depend on which other queries share the workgroup.
+// Two kernels, one arithmetic.  Few query rows per sequence (decode): workgroup = (query
+// row, range of 1024 entries), 4 waves, each wave 16-entry blocks of the range.  Many
+// (prefill): workgroup = (16 consecutive query rows, part of 4096 entries), wave w owns 4
+// of the rows (64 heads each, operands held in registers for the whole part) and walks
+// the part in steps of 64 entries with the next step's key fragments in flight; the keys
+// (64 B a row, 2 MiB for 32768 entries) stay resident in each XCD's L2.  Rows of a wave
+// that belong to different sequences are handled as separate runs with their own keys.
+// In both, a score is the MFMAs of its own query row and key column, a per-lane sum over
+// the lane's 16 heads in (block, register) order, then the sum over the four lane groups
+// as (g0 + g1) + (g2 + g3); so its bits do not depend on the kernel or on which other
+// queries share the workgroup.
 
 #include "common.cuh"
 #include "kernels.h"
@@ -26,7 +31,9 @@ namespace csa {
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int mx_v8i;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float mx_v4f;
 
-constexpr int kMxRange = 1024;  // entries per workgroup
+constexpr int kMxRange = 1024;  // entries per workgroup, one query row each
+constexpr int kMxPart = 4096;   // entries per workgroup, 16 query rows each
+constexpr int kMxQW = 4;        // query rows per wave of the block kernel
 constexpr int kMxFmtE2M1 = 4;   // operand format code of e2m1 in the scaled MFMA
 
 __device__ __forceinline__ mx_v8i mx_operand(uint4 v) {
@@ -120,6 +127,111 @@ __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev 
   }
 }
 
+// The block kernel (see above).  Lane (g, c16) holds, for each of the wave's rows i, the
+// partial sum over heads 4g + j + 16hb of entry c16 of the step's block; the four partials
+// of a row are combined by two exchanges that also spread the rows over the lane groups
+// (lane group g ends with row ((g & 1) << 1) | (g >> 1)), so all 64 lanes store.
+__global__ void __launch_bounds__(256) index_score_mx_block_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
+                                                                   int n_I, RowsDev kI, int ratio,
+                                                                   float* __restrict__ score, int64_t score_stride,
+                                                                   int n_parts) {
+  const int qb = blockIdx.x / n_parts, part = blockIdx.x % n_parts;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t_w = (qb * 4 + wv) * kMxQW;
+  const int t_end = min(t_w + kMxQW, S.total_q);
+  const int64_t e_begin = (int64_t)part * kMxPart;
+  const int my_row = ((g & 1) << 1) | (g >> 1);  // the row this lane stores
+
+  for (int t0 = t_w; t0 < t_end;) {
+    const TokenCtx ctx = token_ctx(S, t0);
+    const int nq = min(t_end, ctx.q_end) - t0;
+    const int64_t v_max = (ctx.p + nq) / ratio;  // visible entries of the run's last row
+    if (e_begin < v_max) {
+      uint4 qa[kMxQW][4];
+      uint32_t qs[kMxQW][4];
+      float wr[kMxQW][4][4];
+#pragma unroll
+      for (int i = 0; i < kMxQW; ++i)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          const int h = c16 + 16 * hb;
+          const bool on = i < nq && h < n_I;
+          const int64_t row = (int64_t)(t0 + (on ? i : 0)) * n_I + (on ? h : 0);
+          qa[i][hb] = on ? *reinterpret_cast<const uint4*>(qI.data + row * qI.stride + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
+          qs[i][hb] = on ? (uint32_t)qI.scales[row * (128 / kMxBlock) + g] : 127u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int hw = 4 * g + j + 16 * hb;
+            wr[i][hb][j] = (i < nq && hw < n_I) ? w[(int64_t)(t0 + i) * n_I + hw] : 0.f;
+          }
+        }
+      const int64_t e_stop = min(e_begin + (int64_t)kMxPart, v_max);
+      const int64_t v_row = (ctx.p + my_row + 1) / ratio;  // visible entries of the stored row
+      const bool row_on = my_row < nq;
+      float* srow = score + (int64_t)(t0 + (row_on ? my_row : 0)) * score_stride;
+      const uint8_t* kbase = kI.data + ctx.entry0 * kI.stride + 16 * g;
+      const uint8_t* sbase = kI.scales + ctx.entry0 * (128 / kMxBlock) + g;
+      // key fragments of the step's four 16-entry blocks (entries past the run's last
+      // visible one read that entry instead: a valid row, never stored)
+      auto fetch = [&](int64_t e0, uint4* kb, uint32_t* ks) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          int64_t e = e0 + 16 * u + c16;
+          if (e >= v_max) e = v_max - 1;
+          kb[u] = *reinterpret_cast<const uint4*>(kbase + e * kI.stride);
+          ks[u] = (uint32_t)sbase[e * (128 / kMxBlock)];
+        }
+      };
+      uint4 kb[4];
+      uint32_t ks[4];
+      fetch(e_begin, kb, ks);
+      for (int64_t e0 = e_begin; e0 < e_stop; e0 += 64) {
+        uint4 kn[4];
+        uint32_t ksn[4];
+        fetch(e0 + 64, kn, ksn);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t eb = e0 + 16 * u;
+          if (eb >= e_stop) break;
+          const mx_v8i b = mx_operand(kb[u]);
+          float s[kMxQW];
+#pragma unroll
+          for (int i = 0; i < kMxQW; ++i) {
+            s[i] = 0.f;
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) {
+              const mx_v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  mx_operand(qa[i][hb]), b, mx_v4f{0.f, 0.f, 0.f, 0.f}, kMxFmtE2M1, kMxFmtE2M1, 0, (int)qs[i][hb], 0,
+                  (int)ks[u]);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) s[i] = __builtin_fmaf(wr[i][hb][j], fmaxf(acc[j], 0.f), s[i]);
+            }
+          }
+          // lane groups g, g^1: even groups keep rows 0, 1, odd groups rows 2, 3
+          const bool odd = g & 1;
+          const float x0 = odd ? s[2] : s[0], x1 = odd ? s[3] : s[1];
+          const float y0 = odd ? s[0] : s[2], y1 = odd ? s[1] : s[3];
+          const float a0 = x0 + __shfl_xor(y0, 16, 64);
+          const float a1 = x1 + __shfl_xor(y1, 16, 64);
+          // lane groups g, g^2: groups 0, 1 keep their first row, groups 2, 3 their second
+          const bool hi = g & 2;
+          const float kp = hi ? a1 : a0, sn = hi ? a0 : a1;
+          const float tot = kp + __shfl_xor(sn, 32, 64);
+          const int64_t e = eb + c16;
+          if (row_on && e < v_row && e < e_stop) srow[e] = tot;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          kb[u] = kn[u];
+          ks[u] = ksn[u];
+        }
+      }
+    }
+    t0 += nq;
+  }
+}
+
 bool index_mx_supported(const RowsDev& qI, const RowsDev& kI, int n_I) {
   return qI.dtype == DT_MXFP4 && kI.dtype == DT_MXFP4 && kI.dim == 128 && qI.dim == 128 && n_I <= 64 &&
          qI.stride % 16 == 0 && kI.stride % 16 == 0;
@@ -131,10 +243,11 @@ hipError_t launch_index_score_mx(const SeqsDev& S, const RowsDev& qI, const floa
   const int n_parts = (max_vis + kMxRange - 1) / kMxRange;
   if (n_parts == 0 || S.total_q == 0) return hipSuccess;
   if (max_q >= 16) {
-    constexpr int QB = 4;
-    const int64_t blocks = (int64_t)((S.total_q + QB - 1) / QB) * n_parts;
-    hipLaunchKernelGGL(index_score_mx_kernel<QB>, dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I, kI,
-                       ratio, score, score_stride, n_parts);
+    const int parts = (max_vis + kMxPart - 1) / kMxPart;
+    const int rows_per_block = 4 * kMxQW;
+    const int64_t blocks = (int64_t)((S.total_q + rows_per_block - 1) / rows_per_block) * parts;
+    hipLaunchKernelGGL(index_score_mx_block_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I, kI,
+                       ratio, score, score_stride, parts);
   } else {
     const int64_t blocks = (int64_t)S.total_q * n_parts;
     hipLaunchKernelGGL(index_score_mx_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I, kI,

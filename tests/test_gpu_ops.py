@@ -193,11 +193,13 @@ def test_index_score_matches_oracle(fmt, d_I, n_I):
 
 def test_index_score_mxfp4_query_blocks():
     """MXFP4 scores on the scaled matrix cores with query blocks: several sequences with many
-    new tokens each, so blocks of consecutive query rows cross sequence boundaries."""
+    new tokens each, so blocks of consecutive query rows cross sequence boundaries, and one
+    long sequence whose visible entries span two 4096-entry parts with a ragged tail.  The
+    same tokens scored one per sequence (the one-row kernel) give the same bits."""
     g = np.random.default_rng(23)
     ratio, d_I, n_I = 4, 128, 64
-    n_q = [17, 1, 23, 6, 40]
-    ctx = [300, 2051, 23, 1600, 900]
+    n_q = [17, 1, 23, 6, 40, 21]
+    ctx = [300, 2051, 23, 1600, 900, 18003]
     ob, sq, n_ent, _ = make_batch(n_q, ctx, ratio)
     kI_rows, kI_val = _rows_in(ops.MXFP4, g.standard_normal((n_ent, d_I)))
     qI_rows, qI_val = _rows_in(ops.MXFP4, g.standard_normal((sq.total_q * n_I, d_I)))
@@ -205,9 +207,18 @@ def test_index_score_mxfp4_query_blocks():
     stride = sq.max_ctx // ratio + 3
     score = torch.full((sq.total_q, stride), float("nan"), dtype=torch.float32, device=DEV)
     ops.csa_index_score(sq, qI_rows, w_t, n_I, kI_rows, ratio, score)
+    # every token as a sequence of its own (one query row: the one-row kernel)
+    toks = list(ob.tokens())
+    single = ops.Seqs([1] * len(toks), [p + 1 for _, _, p in toks], [ob.entry_off[b] for _, b, _ in toks],
+                      [0] * len(toks), [0] * len(toks))
+    assert single.max_q == 1 and sq.max_q >= 16
+    score1 = torch.full_like(score, float("nan"))
+    ops.csa_index_score(single, qI_rows, w_t, n_I, kI_rows, ratio, score1)
     torch.cuda.synchronize()
+    assert torch.equal(score.isnan(), score1.isnan())
+    assert torch.equal(torch.nan_to_num(score), torch.nan_to_num(score1)), "scores depend on the kernel"
     sc = score.cpu().numpy().astype(np.float64)
-    for row, b, p in ob.tokens():
+    for row, b, p in toks:
         V = visible(p, ratio)
         kI = kI_val[ob.entry_off[b]: ob.entry_off[b] + V]
         qI = qI_val[row * n_I:(row + 1) * n_I]

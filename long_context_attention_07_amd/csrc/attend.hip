@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(256) attend_valu_kernel(AttendArgs a, float* _
   if (!SPLIT && hvalid) finalize_valu(a, t, h, l32, ctx.p, f, O, D, F);
 }
 
-int attend_chunk_slots(const AttendArgs& a) { return chunk_slots_for(a.csa, a.k, a.n_win, a.kv.dtype); }
+int attend_chunk_slots(const AttendArgs& a) { return chunk_slots_for(a.csa, a.k, a.n_win); }
 
 int64_t attend_max_chunks(const AttendArgs& a) {
   const int64_t n_ent = a.csa ? (int64_t)a.k : (int64_t)a.max_ctx / a.ratio;

@@ -163,13 +163,13 @@ __global__ void __launch_bounds__(256) attend_combine_kernel(AttendArgs a, const
 }
 
 // Chunk length in key slots: CSA key lists have a fixed length k + n_win, cut into
-// ceil((k + n_win) / 384) equal chunks rounded up to whole 64-key tiles, except that bf16
-// lists with k >= 1024 are one chunk (their kernel gives each token all 64 heads at once);
+// ceil((k + n_win) / 384) equal chunks rounded up to whole 64-key tiles, except that lists
+// with k >= 1024 are one chunk (their kernel gives each token all 64 heads at once);
 // HCA lists grow with the context and use 576-slot (9-tile) chunks.  Depends on op
 // parameters only.
-__host__ __device__ inline int chunk_slots_for(int csa, int k, int n_win, int kv_dtype) {
+__host__ __device__ inline int chunk_slots_for(int csa, int k, int n_win) {
   if (!csa) return 576;
-  if (k >= 1024 && kv_dtype == DT_BF16) return ((k + n_win + 63) / 64) * 64;
+  if (k >= 1024) return ((k + n_win + 63) / 64) * 64;
   const int S = k + n_win;
   const int n = (S + 383) / 384;
   const int c = (S + n - 1) / n;

@@ -670,32 +670,35 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
 }
 
 // ---------------------------------------------------------------------------------------
-// Long bf16 key lists (CSA with k >= 1024: prefill, long-context layers): one workgroup
-// per (token, 64 heads), 4 waves, wave w owns heads 16w..16w+15 for all 512 dims.  Each
-// 64-row tile is staged once for all 64 heads (16 rows per wave), so a gathered row is read
-// once per token instead of once per 16 heads.  A wave computes S^T for all 64 keys of the
-// tile (4 key blocks), runs the online softmax of its heads over them alone, and
-// accumulates O^T[512 dims x 16 heads] with v_mfma_f32_16x16x32: the B operand (P^T) joins
+// Long key lists (CSA with k >= 1024: prefill, long-context layers), bf16 or fp8 rows: one
+// workgroup per (token, 64 heads), 8 waves.  Wave pair p = w % 4 owns heads 16p..16p+15
+// over all 64 rows of each tile; the two waves of a pair (h2 = w / 4) split the 512 dims
+// as in the pair kernel: each computes the partial logits of its half for the tile's four
+// 16-key blocks (exchanged through LDS, added half 0 + half 1, so both hold the same
+// logits), runs the same online softmax of its 16 heads over the tile's 64 keys, and
+// accumulates O^T[256 dims x 16 heads] with v_mfma_f32_16x16x32: the B operand (P^T) joins
 // the logit accumulators of two key blocks (k index 8g + i <-> key 16(2kp + i / 4) + 4g +
-// i % 4), the A operand (V^T) is the two matching transposing reads.  No cross-wave state.
-// Such lists are one chunk (the chunk length rule), so the fold from the sink takes the one
-// chunk state at the end.  (fp8 rows stay on the pair kernel: with per-block scales this
-// kernel's 64-key tiles need more registers than a wave has.)
+// i % 4), the A operand (V^T) is the two matching transposing reads.  Wave w loads and
+// stages rows 8w..8w+7 of every tile, so a gathered row is read (and an fp8 row decoded)
+// once per token instead of once per 16 heads.  Such lists are one chunk (the chunk length
+// rule), so the fold from the sink takes the one chunk state at the end.
 constexpr int kHeadsLong = 64;       // heads per workgroup in this kernel
-constexpr int kLongKeys = 1024;      // bf16 CSA key lists from this length use this kernel
+constexpr int kLongKeys = 1024;      // CSA key lists from this length use this kernel
 
-// Slots s0 .. s0+63 of the tile: lane l resolves slot s0 + l.
+// Slots s0 .. s0+63 of the tile: lane l resolves slot s0 + l (rows, and the block scales of
+// fp8 rows), so every wave knows the whole tile's valid and window masks.
+template <bool KVF>
 __device__ __forceinline__ TileAddr resolve_tile64(const AttendArgs& a, const TokenCtx& ctx, int64_t n_ent,
-                                                   int64_t s0, int lane, TileStage& st, const int32_t* sidx,
-                                                   int64_t s_lo) {
-  const SlotRef r = resolve_slot_lds(a, ctx, n_ent, s0 + lane, sidx, s_lo);
+                                                   int64_t s0, int lane, TileStage& st, const int32_t* sidx) {
+  const SlotRef r = resolve_slot_lds(a, ctx, n_ent, s0 + lane, sidx, 0);
   st.valid = __ballot(r.kind != 0);
   st.win = __ballot(r.kind == 2);
   st.pos0 = ctx.p - a.n_win + 1 + (s0 - n_ent);
   const bool win = r.kind == 2;
+  constexpr int nb = (kDM - kSplitBf16Dims + kKvBlock - 1) / kKvBlock;
   TileAddr ad;
   ad.row = reinterpret_cast<uint64_t>(win ? a.tok.data : a.kv.data) + (uint64_t)(r.row * (win ? a.tok.stride : a.kv.stride));
-  ad.sc = 0u;
+  ad.sc = KVF ? reinterpret_cast<uint64_t>(win ? a.tok.scales : a.kv.scales) + (uint64_t)(r.row * nb * 4) : 0u;
   return ad;
 }
 
@@ -717,10 +720,11 @@ __device__ __forceinline__ uint2 finalize4(const float* x, int d0, int dn, int64
   return make_uint2(w[0], w[1]);
 }
 
-__global__ void __launch_bounds__(256) attend_heads_kernel(AttendArgs a, int n_hg, int chunk_slots, int n_logical) {
-  constexpr bool KVF = false;
+template <bool KVF>
+__global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg, int n_logical) {
   __shared__ MfmaLds L;
   __shared__ FreqLds F;
+  __shared__ f32x4_t sx[8][4][64];  // partial logits of each wave, per key block
   const int n_phys = gridDim.x;
   const int per_xcd = n_phys / 8;
   const int lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -730,165 +734,184 @@ __global__ void __launch_bounds__(256) attend_heads_kernel(AttendArgs a, int n_h
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
+  const int p = w & 3, h2 = w >> 2;
   const int g = lane >> 4, c16 = lane & 15;
   const int dn = kDM - a.rope.dims;
-  const int h = hg * kHeadsLong + 16 * w + c16;  // the head of this lane's logit and output columns
+  const int h = hg * kHeadsLong + 16 * p + c16;  // the head of this lane's logit and output columns
   const bool h_ok = h < a.n_h;
 
-  // query fragments of head h, dims 8g + 32kk .. +7: loaded straight into registers
-  uint4 raw[16];
+  // query fragments of head h, dims 8g + 32i + 256h2 .. +7, straight into registers
+  uint4 raw[8];
   {
     const uint8_t* qrow = a.q.data + ((int64_t)t * a.n_h + (h_ok ? h : 0)) * a.q.stride;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-      raw[kk] = h_ok ? *reinterpret_cast<const uint4*>(qrow + (8 * g + 32 * kk) * 2) : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 8; ++i)
+      raw[i] = h_ok ? *reinterpret_cast<const uint4*>(qrow + (8 * g + 32 * i + 256 * h2) * 2) : make_uint4(0u, 0u, 0u, 0u);
   }
   load_freqs(F, a.rope);
-
   const TokenCtx ctx = token_ctx(a.S, t);
   const int64_t n_ent = entry_slots(a, ctx);
   const int64_t n_slots = n_ent + a.n_win;
-  const int c_end = (int)((n_slots + chunk_slots - 1) / chunk_slots);
   {
     const int32_t* src = a.idx + (int64_t)t * a.k;
-    for (int s = tid; s < a.k; s += 256) L.sidx[s] = src[s];
+    for (int s = tid; s < a.k; s += 512) L.sidx[s] = src[s];
   }
   __syncthreads();
 
   TileStage st;
   {
-    const TileAddr ad = resolve_tile64(a, ctx, n_ent, 0, lane, st, L.sidx, 0);
-    issue_rows<0, 16, KVF>(lane, st, ad, 16 * w);
+    const TileAddr ad = resolve_tile64<KVF>(a, ctx, n_ent, 0, lane, st, L.sidx);
+    issue_rows<0, 8, KVF>(lane, st, ad, 8 * w);
   }
 
-  uint4 qf[16];
-  uint4 qlo[2];
+  uint4 qf[8];
+  uint4 qlo[2];  // half 1: residuals of the rotated dims among 448..511
 #pragma unroll
-  for (int kk = 0; kk < 14; ++kk) qf[kk] = from_bf16<KVF>(raw[kk]);
+  for (int i = 0; i < 8; ++i) qf[i] = from_bf16<KVF>(raw[i]);
+  qlo[0] = qlo[1] = make_uint4(0u, 0u, 0u, 0u);
+  if (h2 == 1) {
 #pragma unroll
-  for (int kk = 14; kk < 16; ++kk) {
-    const int d0 = 8 * g + 32 * kk;
-    if (d0 >= dn) {
-      rotate_chunk<KVF>(raw[kk], ctx.p, F, (d0 - dn) >> 1, &qf[kk], &qlo[kk - 14]);
-    } else {
-      qf[kk] = from_bf16<KVF>(raw[kk]);
-      qlo[kk - 14] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 6; i < 8; ++i) {
+      const int d0 = 8 * g + 256 + 32 * i;
+      if (d0 >= dn) rotate_chunk<KVF>(raw[i], ctx.p, F, (d0 - dn) >> 1, &qf[i], &qlo[i - 6]);
     }
   }
 
   FoldState fs = fold_init(h_ok ? a.sink[h] * kLog2e : -INFINITY);
-  f32x4_t OT[32];  // O^T[dim 16nb + 4g + j, head h]
+  f32x4_t OT[16];  // O^T[dim 256 h2 + 16nb + 4g + j, head h]
 #pragma unroll
-  for (int nb = 0; nb < 32; ++nb) OT[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < 16; ++nb) OT[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  const int ntile = (int)((n_slots + kT - 1) / kT);
 
-  auto tiles_in = [&](int c) -> int {
-    const int64_t rem = n_slots - (int64_t)c * chunk_slots;
-    const int64_t len = rem < chunk_slots ? rem : chunk_slots;
-    return (int)((len + kT - 1) / kT);
-  };
-  int cc = 0, tile = 0, ntile = tiles_in(cc);
-
-  while (true) {
+  for (int tile = 0;; ++tile) {
     lds_barrier();  // previous tile fully consumed
-    store_rows<KVF, 16>(L, a, st, 16 * w, 16 * w, (st.win >> (16 * w)) & 0xffffull, lane, F);
+    store_rows<KVF, 8>(L, a, st, 8 * w, 8 * w, (st.win >> (8 * w)) & 0xffull, lane, F);
     const uint64_t valid = st.valid, winm = st.win;
     lds_barrier();  // tile staged
 
-    int ncc = cc, ntl = tile + 1;
-    if (ntl == ntile) {
-      ncc = cc + 1;
-      ntl = 0;
-    }
-    const bool has_next = ncc < c_end;
+    const bool has_next = tile + 1 < ntile;
     TileAddr nad = {0u, 0u};
     if (has_next) {
-      nad = resolve_tile64(a, ctx, n_ent, (int64_t)ncc * chunk_slots + (int64_t)ntl * kT, lane, st, L.sidx, 0);
-      issue_rows<0, 4, KVF>(lane, st, nad, 16 * w);
+      nad = resolve_tile64<KVF>(a, ctx, n_ent, (int64_t)(tile + 1) * kT, lane, st, L.sidx);
+      issue_rows<0, 2, KVF>(lane, st, nad, 8 * w);
     }
 
-    // ---- S^T = K Q^T, key block kb = keys 16kb .. 16kb+15 of the tile
+    // ---- S^T = K Q^T, key block kb = keys 16kb .. 16kb+15, this wave's half of the dims.
+    // fp8 rows: partial products per code block (blocks 2 h2 and 2 h2 + 1; half 1's last
+    // two chunks are the bf16 tail), scaled in fp32.
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4_t part[3];
+#pragma unroll
+      for (int b = 0; b < 3; ++b) part[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = &L.k[(16 * kb + c16) * kKStride + (16 * g + 512 * h2)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int b = KVF ? (i < 4 ? 0 : (i < 6 ? 1 : 2)) : 0;
+        const uint4 ka = *reinterpret_cast<const uint4*>(krow + 64 * i);
+        part[b] = mfma16<KVF>(ka, qf[i], part[b]);
+        if (i >= 6 && h2 == 1) part[KVF ? 2 : 0] = mfma16<KVF>(ka, qlo[i - 6], part[KVF ? 2 : 0]);
+      }
+      if (((winm >> (16 * kb)) & 0xffffull) != 0ull && h2 == 1) {
+        const uint8_t* lrow = &L.klo[(16 * kb + c16) * kLoStride + 16 * g];
+#pragma unroll
+        for (int i = 6; i < 8; ++i)
+          part[KVF ? 2 : 0] = mfma16<KVF>(*reinterpret_cast<const uint4*>(lrow + 64 * (i - 6)), qf[i], part[KVF ? 2 : 0]);
+      }
+      f32x4_t acc = part[0];
+      if (KVF) {
+        const float4 sA = *reinterpret_cast<const float4*>(&L.scl[2 * h2][16 * kb + 4 * g]);
+        const float4 sB = *reinterpret_cast<const float4*>(&L.scl[2 * h2 + 1][16 * kb + 4 * g]);
+        const float a0[4] = {sA.x, sA.y, sA.z, sA.w}, b0[4] = {sB.x, sB.y, sB.z, sB.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x = part[0][j] * a0[j];
+          x = __builtin_fmaf(part[1][j], b0[j], x);
+          acc[j] = __builtin_fmaf(part[2][j], h2 == 0 ? b0[j] : 1.0f, x);
+        }
+      }
+      sx[w][kb][lane] = acc;
+    }
+    if (has_next) issue_rows<2, 4, KVF>(lane, st, nad, 8 * w);
+    lds_barrier();
+
+    // ---- online softmax of head h over the tile's 64 keys (both waves of the pair alike)
     float sv[4][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = &L.k[(16 * kb + c16) * kKStride + 16 * g];
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(krow + 64 * kk);
-        acc = mfma16<false>(ka, qf[kk], acc);
-        if (kk >= 14) acc = mfma16<false>(ka, qlo[kk - 14], acc);
-      }
-      if (((winm >> (16 * kb)) & 0xffffull) != 0ull) {
-        const uint8_t* lrow = &L.klo[(16 * kb + c16) * kLoStride + 16 * g];
-#pragma unroll
-        for (int kk = 14; kk < 16; ++kk)
-          acc = mfma16<false>(*reinterpret_cast<const uint4*>(lrow + 64 * (kk - 14)), qf[kk], acc);
-      }
+      const f32x4_t mine = sx[w][kb][lane], other = sx[w ^ 4][kb][lane];
+      const f32x4_t lg = h2 == 0 ? mine + other : other + mine;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sv[kb][j] = ((valid >> (16 * kb + 4 * g + j)) & 1ull) ? acc[j] * a.scale_log2 : -INFINITY;
-      __builtin_amdgcn_sched_barrier(0);  // one key block's partials live at a time
+        sv[kb][j] = ((valid >> (16 * kb + 4 * g + j)) & 1ull) ? lg[j] * a.scale_log2 : -INFINITY;
     }
-    if (has_next) issue_rows<4, 8, KVF>(lane, st, nad, 16 * w);
-
-    // ---- online softmax of head h over the tile's 64 keys
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(sv[kb][0], sv[kb][1]), fmaxf(sv[kb][2], sv[kb][3])));
     mx = rows_max(mx);
     const float m_new = (mx > m_run + kMaxSlack) ? mx : m_run;
     const float alpha = rescale(m_run, m_new);
-    float pr[4][4];
+    float pr[4][4];  // bf16 rows: P rounded to bf16; fp8 rows: rounded per value block below
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float pj = (sv[kb][j] == -INFINITY) ? 0.f : ex2(sv[kb][j] - m_new);
-        pr[kb][j] = __uint_as_float(f32_to_bf16_bits(pj) << 16);
+        pr[kb][j] = KVF ? pj : __uint_as_float(f32_to_bf16_bits(pj) << 16);
         ls += pr[kb][j];
       }
     ls = rows_sum(ls);
     l_run = __builtin_fmaf(l_run, alpha, ls);
     m_run = m_new;
-    if (has_next) issue_rows<8, 12, KVF>(lane, st, nad, 16 * w);
+    if (has_next) issue_rows<4, 6, KVF>(lane, st, nad, 8 * w);
 
-    // ---- O^T[dim, head] = O^T * alpha + V^T P^T
+    // ---- O^T[dim, head] = O^T * alpha + V^T P^T over this wave's 256 dims
     if (__ballot(alpha != 1.0f) != 0ull) {
 #pragma unroll
-      for (int nb = 0; nb < 32; ++nb) OT[nb] *= alpha;
+      for (int nb = 0; nb < 16; ++nb) OT[nb] *= alpha;
     }
     {
-      // B operands: keys {16(2kp) + 4g + i, 16(2kp+1) + 4g + i}, bf16
-      uint4 pk[2];
+      // B operands for keys {16(2kp) + 4g + i, 16(2kp+1) + 4g + i}, formed as the dim loop
+      // reaches each value block.  fp8 rows: the block's scale folded into P, rounded to
+      // fp16: set 0 for dims 256 h2 .. +127 (code block 2 h2), set 1 for the next 64 (block
+      // 2 h2 + 1), set 2 for the last 64 (block 1 for half 0, the unscaled bf16 tail for
+      // half 1).
 #pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = pr[2 * kp + i / 4][i % 4];
-        pk[kp] = make_uint4(pack16<false>(x[0], x[1]), pack16<false>(x[2], x[3]), pack16<false>(x[4], x[5]),
-                            pack16<false>(x[6], x[7]));
-      }
-#pragma unroll
-      for (int nb = 0; nb < 32; ++nb) {
+      for (int set = 0; set < (KVF ? 3 : 1); ++set) {
+        uint4 pk[2];
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
-          uint8_t* base = &L.k[(32 * kp + 4 * g + (c16 >> 2)) * kKStride + (16 * nb + 4 * (c16 & 3)) * 2];
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + 16 * kKStride));
-          typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
-          const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          OT[nb] = mfma16<false>(__builtin_bit_cast(uint4, both), pk[kp], OT[nb]);
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int kb = 2 * kp + i / 4, j = i % 4;
+            float sc = 1.0f;
+            if (KVF && !(set == 2 && h2 == 1)) sc = L.scl[set == 0 ? 2 * h2 : 2 * h2 + 1][16 * kb + 4 * g + j];
+            x[i] = pr[kb][j] * sc;
+          }
+          pk[kp] = make_uint4(pack16<KVF>(x[0], x[1]), pack16<KVF>(x[2], x[3]), pack16<KVF>(x[4], x[5]),
+                              pack16<KVF>(x[6], x[7]));
+        }
+        const int nb_lo = KVF ? (set == 0 ? 0 : (set == 1 ? 8 : 12)) : 0;
+        const int nb_hi = KVF ? (set == 0 ? 8 : (set == 1 ? 12 : 16)) : 16;
+#pragma unroll
+        for (int nb = nb_lo; nb < nb_hi; ++nb) {
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp) {
+            uint8_t* base = &L.k[(32 * kp + 4 * g + (c16 >> 2)) * kKStride + (256 * h2 + 16 * nb + 4 * (c16 & 3)) * 2];
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + 16 * kKStride));
+            typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
+            const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            OT[nb] = mfma16<KVF>(__builtin_bit_cast(uint4, both), pk[kp], OT[nb]);
+          }
         }
       }
     }
-    if (has_next) issue_rows<12, 16, KVF>(lane, st, nad, 16 * w);
-
+    if (has_next) issue_rows<6, 8, KVF>(lane, st, nad, 8 * w);
     if (!has_next) break;
-    if (ntl == 0) ntile = tiles_in(ncc);
-    cc = ncc;
-    tile = ntl;
   }
 
   // the fold from the sink over the single chunk: O = 0 * fa + O_chunk * fb
@@ -898,14 +921,14 @@ __global__ void __launch_bounds__(256) attend_heads_kernel(AttendArgs a, int n_h
     const float inv = (fs.Z > 0.f) ? 1.0f / fs.Z : 0.f;
     const int64_t orow = (int64_t)t * a.n_h + h;
 #pragma unroll
-    for (int nb = 0; nb < 32; ++nb) {
+    for (int nb = 0; nb < 16; ++nb) {
       float x[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[j] = __builtin_fmaf(0.f, fa, OT[nb][j] * fb) * inv;
-      const int d0 = 16 * nb + 4 * g;
+      const int d0 = 256 * h2 + 16 * nb + 4 * g;
       *reinterpret_cast<uint2*>(a.out.data + orow * a.out.stride + d0 * 2) = finalize4(x, d0, dn, ctx.p, F);
     }
-    if (a.lse && g == 0) a.lse[orow] = lse_natural(fs);
+    if (a.lse && g == 0 && h2 == 0) a.lse[orow] = lse_natural(fs);
   }
 }
 
@@ -994,20 +1017,21 @@ static void launch_attend_mfma_kernel(const AttendArgs& a, float* ws_o, float* w
 
 // Which kernel a call uses depends on the operation's parameters only (the key list
 // length), never on the batch, so a token's bits do not depend on the batch either.
-static bool attend_long_lists(const AttendArgs& a) { return a.csa && a.k >= kLongKeys && a.kv.dtype == DT_BF16; }
+static bool attend_long_lists(const AttendArgs& a) { return a.csa && a.k >= kLongKeys; }
 
 hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (attend_long_lists(a)) {
     const int n_hg = (a.n_h + kHeadsLong - 1) / kHeadsLong;
-    const int C = chunk_slots_for(a.csa, a.k, a.n_win, a.kv.dtype);
     const int64_t n_log = (int64_t)a.S.total_q * n_hg;
     const int64_t n_phys = (n_log + 7) / 8 * 8;
-    hipLaunchKernelGGL(attend_heads_kernel, dim3((unsigned)n_phys), dim3(256), 0, stream, a, n_hg, C,
-                       (int)n_log);
+    if (a.kv.dtype == DT_KV_SPLIT)
+      hipLaunchKernelGGL((attend_long_kernel<true>), dim3((unsigned)n_phys), dim3(512), 0, stream, a, n_hg, (int)n_log);
+    else
+      hipLaunchKernelGGL((attend_long_kernel<false>), dim3((unsigned)n_phys), dim3(512), 0, stream, a, n_hg, (int)n_log);
     return hipGetLastError();
   }
   const int n_hg = (a.n_h + kHG - 1) / kHG;
-  const int C = chunk_slots_for(a.csa, a.k, a.n_win, a.kv.dtype);
+  const int C = chunk_slots_for(a.csa, a.k, a.n_win);
   const int64_t mc = attend_max_chunks(a);
   const size_t need = attend_workspace_bytes(a);
   const int64_t single = (int64_t)a.S.total_q * n_hg;

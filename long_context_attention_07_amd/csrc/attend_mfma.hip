@@ -262,8 +262,8 @@ __device__ __forceinline__ float rows_sum(float x) {
 // bit and offset it0 + i of st.  Then, when `winmask` (the rows whose logits read the
 // residual tile together with these) holds a window row, rotate the window rows among them
 // and write the rotation residuals of these rows (zero for the others).
-template <bool KVF, int NR>
-__device__ __forceinline__ void store_rows(MfmaLds& L, const AttendArgs& a, const TileStage& st, int row0, int it0,
+template <bool KVF, int NR, class Lds>
+__device__ __forceinline__ void store_rows(Lds& L, const AttendArgs& a, const TileStage& st, int row0, int it0,
                                            uint64_t winmask, int lane, const FreqLds& F) {
   if (!KVF) {
 #pragma unroll
@@ -680,17 +680,44 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
 // the logit accumulators of two key blocks (k index 8g + i <-> key 16(2kp + i / 4) + 4g +
 // i % 4), the A operand (V^T) is the two matching transposing reads.  Wave w loads and
 // stages rows 8w..8w+7 of every tile, so a gathered row is read (and an fp8 row decoded)
-// once per token instead of once per 16 heads.  Such lists are one chunk (the chunk length
-// rule), so the fold from the sink takes the one chunk state at the end.
+// once per token instead of once per 16 heads: bf16 rows through registers, fp8 rows (576
+// bytes) by the memory-to-LDS path into a raw buffer decoded at the next tile, which
+// leaves the registers to the operands.  Each lane holds the entry id of its slot of the
+// tile after next.  Such lists are one chunk (the chunk length rule), so the fold from the
+// sink takes the one chunk state at the end.
 constexpr int kHeadsLong = 64;       // heads per workgroup in this kernel
 constexpr int kLongKeys = 1024;      // CSA key lists from this length use this kernel
+constexpr int kSplitRowBytes = (kDM - kSplitBf16Dims) + 2 * kSplitBf16Dims;  // 576
 
-// Slots s0 .. s0+63 of the tile: lane l resolves slot s0 + l (rows, and the block scales of
-// fp8 rows), so every wave knows the whole tile's valid and window masks.
+struct __align__(16) LongLds {
+  uint8_t k[kT * kKStride];      // the tile's 64 rows in the tile format
+  uint8_t klo[kT * kLoStride];   // window rows: residual of their rotated last 64 dims
+  float scl[4][kT];              // fp8 rows: the fp32 scale of each 128-dim code block
+};
+
+// Slot s0 + lane of the tile from the entry id `e` of that slot (idx, in a register): every
+// wave resolves all 64 slots, so it knows the whole tile's valid and window masks, and the
+// rows' (and fp8 rows' scale) addresses.
 template <bool KVF>
 __device__ __forceinline__ TileAddr resolve_tile64(const AttendArgs& a, const TokenCtx& ctx, int64_t n_ent,
-                                                   int64_t s0, int lane, TileStage& st, const int32_t* sidx) {
-  const SlotRef r = resolve_slot_lds(a, ctx, n_ent, s0 + lane, sidx, 0);
+                                                   int64_t s0, int lane, TileStage& st, int32_t e) {
+  const int64_t s = s0 + lane;
+  SlotRef r;
+  r.kind = 0;
+  r.row = 0;
+  r.pos = 0;
+  if (s < n_ent) {
+    if (e >= 0) {
+      r.kind = 1;
+      r.row = ctx.entry0 + e;
+    }
+  } else if (s < n_ent + a.n_win) {
+    const int64_t pos = ctx.p - a.n_win + 1 + (s - n_ent);
+    if (pos >= 0 && pos >= ctx.tok_lo) {
+      r.kind = 2;
+      r.row = ctx.tok0 + (pos - ctx.tok_lo);
+    }
+  }
   st.valid = __ballot(r.kind != 0);
   st.win = __ballot(r.kind == 2);
   st.pos0 = ctx.p - a.n_win + 1 + (s0 - n_ent);
@@ -700,6 +727,28 @@ __device__ __forceinline__ TileAddr resolve_tile64(const AttendArgs& a, const To
   ad.row = reinterpret_cast<uint64_t>(win ? a.tok.data : a.kv.data) + (uint64_t)(r.row * (win ? a.tok.stride : a.kv.stride));
   ad.sc = KVF ? reinterpret_cast<uint64_t>(win ? a.tok.scales : a.kv.scales) + (uint64_t)(r.row * nb * 4) : 0u;
   return ad;
+}
+
+typedef const __attribute__((address_space(1))) void* global_cvp;
+typedef __attribute__((address_space(3))) void* lds_vp;
+
+// fp8 rows 8w .. 8w+7 of the tile straight into the raw row buffer (576 bytes a row, lanes
+// 0..35 one 16-byte piece each) and their four block scales into rsc (lanes 0..7, one row
+// each), by the memory-to-LDS path: no registers hold rows in flight.
+__device__ __forceinline__ void issue_rows_lds(int w, int lane, const TileStage& st, const TileAddr& ad, uint8_t* raw,
+                                               float* rsc) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * w + i;
+    if ((st.valid >> r) & 1ull) {
+      const uint64_t rowp = readlane_u64(ad.row, r);
+      if (lane < kSplitLanes)
+        __builtin_amdgcn_global_load_lds((global_cvp)(rowp + 16u * lane), (lds_vp)(raw + r * kSplitRowBytes), 16, 0, 0);
+    }
+  }
+  const uint64_t scp = __shfl(ad.sc, 8 * w + (lane & 7));
+  if (lane < 8 && ((st.valid >> (8 * w + lane)) & 1ull))
+    __builtin_amdgcn_global_load_lds((global_cvp)scp, (lds_vp)(rsc + 32 * w), 16, 0, 0);
 }
 
 // Final values of 4 consecutive output dims d0..d0+3 of one head: inverse RoPE of the two
@@ -722,9 +771,12 @@ __device__ __forceinline__ uint2 finalize4(const float* x, int d0, int dn, int64
 
 template <bool KVF>
 __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg, int n_logical) {
-  __shared__ MfmaLds L;
+  __shared__ LongLds L;
   __shared__ FreqLds F;
   __shared__ f32x4_t sx[8][4][64];  // partial logits of each wave, per key block
+  // fp8 rows: the next tile's rows and block scales as they arrive from memory
+  __shared__ __align__(16) uint8_t rawrows[KVF ? kT * kSplitRowBytes : 16];
+  __shared__ __align__(16) float rawsc[KVF ? kT * 4 : 4];
   const int n_phys = gridDim.x;
   const int per_xcd = n_phys / 8;
   const int lid = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -740,7 +792,8 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
   const int h = hg * kHeadsLong + 16 * p + c16;  // the head of this lane's logit and output columns
   const bool h_ok = h < a.n_h;
 
-  // query fragments of head h, dims 8g + 32i + 256h2 .. +7, straight into registers
+  // query fragments of head h, dims 8g + 32i + 256h2 .. +7, straight into registers; the
+  // entry ids of the first two tiles' slots (each lane one slot)
   uint4 raw[8];
   {
     const uint8_t* qrow = a.q.data + ((int64_t)t * a.n_h + (h_ok ? h : 0)) * a.q.stride;
@@ -748,20 +801,22 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
     for (int i = 0; i < 8; ++i)
       raw[i] = h_ok ? *reinterpret_cast<const uint4*>(qrow + (8 * g + 32 * i + 256 * h2) * 2) : make_uint4(0u, 0u, 0u, 0u);
   }
+  const int32_t* idx_t = a.idx + (int64_t)t * a.k;
+  const int32_t ix0 = lane < a.k ? idx_t[lane] : -1;
+  int32_t ix_next = kT + lane < a.k ? idx_t[kT + lane] : -1;
   load_freqs(F, a.rope);
   const TokenCtx ctx = token_ctx(a.S, t);
   const int64_t n_ent = entry_slots(a, ctx);
   const int64_t n_slots = n_ent + a.n_win;
-  {
-    const int32_t* src = a.idx + (int64_t)t * a.k;
-    for (int s = tid; s < a.k; s += 512) L.sidx[s] = src[s];
-  }
   __syncthreads();
 
   TileStage st;
   {
-    const TileAddr ad = resolve_tile64<KVF>(a, ctx, n_ent, 0, lane, st, L.sidx);
-    issue_rows<0, 8, KVF>(lane, st, ad, 8 * w);
+    const TileAddr ad = resolve_tile64<KVF>(a, ctx, n_ent, 0, lane, st, ix0);
+    if (KVF)
+      issue_rows_lds(w, lane, st, ad, rawrows, rawsc);
+    else
+      issue_rows<0, 8, KVF>(lane, st, ad, 8 * w);
   }
 
   uint4 qf[8];
@@ -785,16 +840,39 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
   const int ntile = (int)((n_slots + kT - 1) / kT);
 
   for (int tile = 0;; ++tile) {
-    lds_barrier();  // previous tile fully consumed
-    store_rows<KVF, 8>(L, a, st, 8 * w, 8 * w, (st.win >> (8 * w)) & 0xffull, lane, F);
+    if (KVF) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows are in LDS
+    lds_barrier();  // previous tile fully consumed (fp8: every wave's rows arrived)
+    if (KVF) {
+      // decode the raw rows 8w .. 8w+7 into the tile format (absent rows: zeros)
+      TileStage sv;
+      sv.valid = st.valid;
+      sv.win = st.win;
+      sv.pos0 = st.pos0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * w + i;
+        const bool on = (st.valid >> r) & 1ull;
+        sv.v[i] = (on && lane < kSplitLanes) ? *reinterpret_cast<const uint4*>(&rawrows[r * kSplitRowBytes + 16 * lane])
+                                             : make_uint4(0u, 0u, 0u, 0u);
+        sv.sc[i] = (on && lane < kSplitCodeLanes && (lane & 7) == 0) ? rawsc[4 * r + (lane >> 3)] : 0.f;
+      }
+      store_rows<KVF, 8>(L, a, sv, 8 * w, 8 * w, (st.win >> (8 * w)) & 0xffull, lane, F);
+    } else {
+      store_rows<KVF, 8>(L, a, st, 8 * w, 8 * w, (st.win >> (8 * w)) & 0xffull, lane, F);
+    }
     const uint64_t valid = st.valid, winm = st.win;
-    lds_barrier();  // tile staged
+    lds_barrier();  // tile staged (fp8: the raw buffer free again)
 
     const bool has_next = tile + 1 < ntile;
     TileAddr nad = {0u, 0u};
     if (has_next) {
-      nad = resolve_tile64<KVF>(a, ctx, n_ent, (int64_t)(tile + 1) * kT, lane, st, L.sidx);
-      issue_rows<0, 2, KVF>(lane, st, nad, 8 * w);
+      nad = resolve_tile64<KVF>(a, ctx, n_ent, (int64_t)(tile + 1) * kT, lane, st, ix_next);
+      if (KVF)
+        issue_rows_lds(w, lane, st, nad, rawrows, rawsc);
+      else
+        issue_rows<0, 2, KVF>(lane, st, nad, 8 * w);
+      const int64_t s2 = (int64_t)(tile + 2) * kT + lane;
+      ix_next = s2 < a.k ? idx_t[s2] : -1;
     }
 
     // ---- S^T = K Q^T, key block kb = keys 16kb .. 16kb+15, this wave's half of the dims.
@@ -833,7 +911,7 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
       }
       sx[w][kb][lane] = acc;
     }
-    if (has_next) issue_rows<2, 4, KVF>(lane, st, nad, 8 * w);
+    if (!KVF && has_next) issue_rows<2, 4, KVF>(lane, st, nad, 8 * w);
     lds_barrier();
 
     // ---- online softmax of head h over the tile's 64 keys (both waves of the pair alike)
@@ -865,7 +943,7 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
     ls = rows_sum(ls);
     l_run = __builtin_fmaf(l_run, alpha, ls);
     m_run = m_new;
-    if (has_next) issue_rows<4, 6, KVF>(lane, st, nad, 8 * w);
+    if (!KVF && has_next) issue_rows<4, 6, KVF>(lane, st, nad, 8 * w);
 
     // ---- O^T[dim, head] = O^T * alpha + V^T P^T over this wave's 256 dims
     if (__ballot(alpha != 1.0f) != 0ull) {
@@ -910,7 +988,7 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
         }
       }
     }
-    if (has_next) issue_rows<6, 8, KVF>(lane, st, nad, 8 * w);
+    if (!KVF && has_next) issue_rows<6, 8, KVF>(lane, st, nad, 8 * w);
     if (!has_next) break;
   }
 

@@ -45,8 +45,8 @@ N_SETS = 8
 OP_KERNELS = {"compress": ["compress2_kernel", "compress_kernel"], "index_score": ["index_score_mfma_kernel"],
               "topk": ["topk_kernel"],
               "attend": ["attend_pair_kernel", "attend_combine_mfma_kernel"]}
-PREFILL_KERNELS = {"compress": ["compress2_kernel"], "index_score": ["index_score_mx_kernel"],
-                   "topk": ["topk_kernel"], "attend": ["attend_pair_kernel"]}
+PREFILL_KERNELS = {"compress": ["compress2_kernel"], "index_score": ["index_score_mx_block_kernel"],
+                   "topk": ["topk_kernel"], "attend": ["attend_long_kernel"]}
 CALIB_BYTES = 256 << 20  # plain device copy used to calibrate the HBM byte counters
 PROFILES = os.path.join(ROOT, "profiles")
 

@@ -4,10 +4,13 @@
 // the 128-token window concatenated; list "其他注意力技术细节": partial RoPE on the last 64
 // dims, inverse RoPE of the output, learnable sink; section 3.4: fp8 KV with 1x128 scales).
 //
-// Workgroup = (token, group of 16 query heads, chunk of the token's key list), 8 waves in 4
-// pairs (see the kernel).  The key list is walked in tiles of 64 rows staged in LDS (rows
-// padded to 1040 bytes); each wave prefetches its share of the next tile into registers
-// (one row per wave instruction, any row order, so the top-k gather is fully coalesced).
+// Two kernels.  The pair kernel (HCA, and CSA with k < 1024): workgroup = (token, group of
+// 16 query heads, chunk of the token's key list), 8 waves in 4 pairs.  The long-list kernel
+// (CSA with k >= 1024, one chunk): workgroup = (token, 64 heads), 8 waves, so each gathered
+// row is read once per token (see the kernels).  The key list is walked in tiles of 64 rows
+// staged in LDS (rows padded to 1040 bytes); each wave prefetches its share of the next
+// tile into registers, or for fp8 rows in the long-list kernel straight into LDS (one row
+// per wave instruction, any row order, so the top-k gather is fully coalesced).
 // The tile format is bf16 for bf16 rows; fp8 rows are staged as their codes in fp16
 // (exact, hardware conversion), the block scales kept apart in fp32 and applied to
 // per-block partial logits and, for the value side, folded into P.  Rotated query dims and
@@ -884,12 +887,14 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
 #pragma unroll
       for (int b = 0; b < 3; ++b) part[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const uint8_t* krow = &L.k[(16 * kb + c16) * kKStride + (16 * g + 512 * h2)];
+      uint4 ka[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ka[i] = *reinterpret_cast<const uint4*>(krow + 64 * i);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int b = KVF ? (i < 4 ? 0 : (i < 6 ? 1 : 2)) : 0;
-        const uint4 ka = *reinterpret_cast<const uint4*>(krow + 64 * i);
-        part[b] = mfma16<KVF>(ka, qf[i], part[b]);
-        if (i >= 6 && h2 == 1) part[KVF ? 2 : 0] = mfma16<KVF>(ka, qlo[i - 6], part[KVF ? 2 : 0]);
+        part[b] = mfma16<KVF>(ka[i], qf[i], part[b]);
+        if (i >= 6 && h2 == 1) part[KVF ? 2 : 0] = mfma16<KVF>(ka[i], qlo[i - 6], part[KVF ? 2 : 0]);
       }
       if (((winm >> (16 * kb)) & 0xffffull) != 0ull && h2 == 1) {
         const uint8_t* lrow = &L.klo[(16 * kb + c16) * kLoStride + 16 * g];
@@ -974,17 +979,26 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
         }
         const int nb_lo = KVF ? (set == 0 ? 0 : (set == 1 ? 8 : 12)) : 0;
         const int nb_hi = KVF ? (set == 0 ? 8 : (set == 1 ? 12 : 16)) : 16;
+        // V^T operands of 2 dim blocks read together, then their MFMAs
 #pragma unroll
-        for (int nb = nb_lo; nb < nb_hi; ++nb) {
+        for (int nb0 = nb_lo; nb0 < nb_hi; nb0 += 2) {
+          typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
+          i16x8_t vt[2][2];
 #pragma unroll
-          for (int kp = 0; kp < 2; ++kp) {
-            uint8_t* base = &L.k[(32 * kp + 4 * g + (c16 >> 2)) * kKStride + (256 * h2 + 16 * nb + 4 * (c16 & 3)) * 2];
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + 16 * kKStride));
-            typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
-            const i16x8_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            OT[nb] = mfma16<KVF>(__builtin_bit_cast(uint4, both), pk[kp], OT[nb]);
-          }
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+              uint8_t* base = &L.k[(32 * kp + 4 * g + (c16 >> 2)) * kKStride + (256 * h2 + 16 * (nb0 + q) + 4 * (c16 & 3)) * 2];
+              const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base));
+              const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + 16 * kKStride));
+              vt[q][kp] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) OT[nb0 + q] = mfma16<KVF>(__builtin_bit_cast(uint4, vt[q][kp]), pk[kp], OT[nb0 + q]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
       }
     }

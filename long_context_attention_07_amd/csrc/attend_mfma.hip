@@ -265,29 +265,13 @@ __device__ __forceinline__ float rows_sum(float x) {
 // bit and offset it0 + i of st.  Then, when `winmask` (the rows whose logits read the
 // residual tile together with these) holds a window row, rotate the window rows among them
 // and write the rotation residuals of these rows (zero for the others).
+// Window rows among rows row0 .. row0+NR-1 of the tile (already staged; window bits and
+// positions are bit and offset it0 + i of st): when `winmask` (the rows whose logits read the
+// residual tile together with these) holds a window row, rotate the window rows among them
+// in place and write the rotation residuals of these rows (zero for the others).
 template <bool KVF, int NR, class Lds>
-__device__ __forceinline__ void store_rows(Lds& L, const AttendArgs& a, const TileStage& st, int row0, int it0,
-                                           uint64_t winmask, int lane, const FreqLds& F) {
-  if (!KVF) {
-#pragma unroll
-    for (int i = 0; i < NR; ++i) *reinterpret_cast<uint4*>(&L.k[(row0 + i) * kKStride + 16 * lane]) = st.v[i];
-  } else if (lane < kSplitCodeLanes) {
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const uint4 v = st.v[i];
-      uint4* dst = reinterpret_cast<uint4*>(&L.k[(row0 + i) * kKStride + 32 * lane]);
-      dst[0] = make_uint4(fp8x2_to_f16x2<false>(v.x), fp8x2_to_f16x2<true>(v.x), fp8x2_to_f16x2<false>(v.y),
-                          fp8x2_to_f16x2<true>(v.y));
-      dst[1] = make_uint4(fp8x2_to_f16x2<false>(v.z), fp8x2_to_f16x2<true>(v.z), fp8x2_to_f16x2<false>(v.w),
-                          fp8x2_to_f16x2<true>(v.w));
-      if ((lane & 7) == 0) L.scl[lane >> 3][row0 + i] = st.sc[i];
-    }
-  } else if (lane < kSplitLanes) {
-#pragma unroll
-    for (int i = 0; i < NR; ++i)
-      *reinterpret_cast<uint4*>(&L.k[(row0 + i) * kKStride + 2 * (kDM - kSplitBf16Dims) +
-                                     16 * (lane - kSplitCodeLanes)]) = from_bf16<true>(st.v[i]);
-  }
+__device__ __forceinline__ void rotate_window_rows(Lds& L, const AttendArgs& a, const TileStage& st, int row0,
+                                                   int it0, uint64_t winmask, int lane, const FreqLds& F) {
   if (winmask != 0u && lane < kRopeMax / 2) {
     const int d = kDM - kRopeMax + 2 * lane;
     const int dn = kDM - a.rope.dims;
@@ -319,6 +303,32 @@ __device__ __forceinline__ void store_rows(Lds& L, const AttendArgs& a, const Ti
       *reinterpret_cast<uint32_t*>(&L.klo[(row0 + i) * kLoStride + 4 * lane]) = res;
     }
   }
+}
+
+template <bool KVF, int NR, class Lds>
+__device__ __forceinline__ void store_rows(Lds& L, const AttendArgs& a, const TileStage& st, int row0, int it0,
+                                           uint64_t winmask, int lane, const FreqLds& F) {
+  if (!KVF) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) *reinterpret_cast<uint4*>(&L.k[(row0 + i) * kKStride + 16 * lane]) = st.v[i];
+  } else if (lane < kSplitCodeLanes) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const uint4 v = st.v[i];
+      uint4* dst = reinterpret_cast<uint4*>(&L.k[(row0 + i) * kKStride + 32 * lane]);
+      dst[0] = make_uint4(fp8x2_to_f16x2<false>(v.x), fp8x2_to_f16x2<true>(v.x), fp8x2_to_f16x2<false>(v.y),
+                          fp8x2_to_f16x2<true>(v.y));
+      dst[1] = make_uint4(fp8x2_to_f16x2<false>(v.z), fp8x2_to_f16x2<true>(v.z), fp8x2_to_f16x2<false>(v.w),
+                          fp8x2_to_f16x2<true>(v.w));
+      if ((lane & 7) == 0) L.scl[lane >> 3][row0 + i] = st.sc[i];
+    }
+  } else if (lane < kSplitLanes) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      *reinterpret_cast<uint4*>(&L.k[(row0 + i) * kKStride + 2 * (kDM - kSplitBf16Dims) +
+                                     16 * (lane - kSplitCodeLanes)]) = from_bf16<true>(st.v[i]);
+  }
+  rotate_window_rows<KVF, NR>(L, a, st, row0, it0, winmask, lane, F);
 }
 
 // Loads of rows roff + I0 .. roff + I1 - 1 of the pair's 16 into st.v[I0 .. I1-1].  A
@@ -846,20 +856,36 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
     if (KVF) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows are in LDS
     lds_barrier();  // previous tile fully consumed (fp8: every wave's rows arrived)
     if (KVF) {
-      // decode the raw rows 8w .. 8w+7 into the tile format (absent rows: zeros)
-      TileStage sv;
-      sv.valid = st.valid;
-      sv.win = st.win;
-      sv.pos0 = st.pos0;
+      // decode the raw rows 8w .. 8w+7 into the tile format (absent rows: zeros), the work
+      // spread over all 64 lanes: 8 x 28 pieces of 16 codes, 8 x 8 pieces of the bf16 tail,
+      // 8 x 4 block scales
+      const int r0 = 8 * w;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * w + i;
-        const bool on = (st.valid >> r) & 1ull;
-        sv.v[i] = (on && lane < kSplitLanes) ? *reinterpret_cast<const uint4*>(&rawrows[r * kSplitRowBytes + 16 * lane])
-                                             : make_uint4(0u, 0u, 0u, 0u);
-        sv.sc[i] = (on && lane < kSplitCodeLanes && (lane & 7) == 0) ? rawsc[4 * r + (lane >> 3)] : 0.f;
+      for (int it = 0; it < (8 * kSplitCodeLanes + 63) / 64; ++it) {
+        const int task = 64 * it + lane;
+        if (task < 8 * kSplitCodeLanes) {
+          const int r = r0 + task / kSplitCodeLanes, c = task % kSplitCodeLanes;
+          uint4 v = make_uint4(0u, 0u, 0u, 0u);
+          if ((st.valid >> r) & 1ull) v = *reinterpret_cast<const uint4*>(&rawrows[r * kSplitRowBytes + 16 * c]);
+          uint4* dst = reinterpret_cast<uint4*>(&L.k[r * kKStride + 32 * c]);
+          dst[0] = make_uint4(fp8x2_to_f16x2<false>(v.x), fp8x2_to_f16x2<true>(v.x), fp8x2_to_f16x2<false>(v.y),
+                              fp8x2_to_f16x2<true>(v.y));
+          dst[1] = make_uint4(fp8x2_to_f16x2<false>(v.z), fp8x2_to_f16x2<true>(v.z), fp8x2_to_f16x2<false>(v.w),
+                              fp8x2_to_f16x2<true>(v.w));
+        }
       }
-      store_rows<KVF, 8>(L, a, sv, 8 * w, 8 * w, (st.win >> (8 * w)) & 0xffull, lane, F);
+      {
+        const int r = r0 + (lane >> 3), c = lane & 7;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if ((st.valid >> r) & 1ull)
+          v = *reinterpret_cast<const uint4*>(&rawrows[r * kSplitRowBytes + (kDM - kSplitBf16Dims) + 16 * c]);
+        *reinterpret_cast<uint4*>(&L.k[r * kKStride + 2 * (kDM - kSplitBf16Dims) + 16 * c]) = from_bf16<true>(v);
+        if (lane < 32) {
+          const int rs = r0 + (lane >> 2), b = lane & 3;
+          L.scl[b][rs] = ((st.valid >> rs) & 1ull) ? rawsc[4 * rs + b] : 0.f;
+        }
+      }
+      rotate_window_rows<KVF, 8>(L, a, st, r0, r0, (st.win >> r0) & 0xffull, lane, F);
     } else {
       store_rows<KVF, 8>(L, a, st, 8 * w, 8 * w, (st.win >> (8 * w)) & 0xffull, lane, F);
     }
@@ -921,13 +947,13 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
 
     // ---- online softmax of head h over the tile's 64 keys (both waves of the pair alike)
     float sv[4][4];
+    const uint64_t vlane = valid >> (4 * g);  // bit 16kb + j: key 16kb + 4g + j present
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const f32x4_t mine = sx[w][kb][lane], other = sx[w ^ 4][kb][lane];
       const f32x4_t lg = h2 == 0 ? mine + other : other + mine;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sv[kb][j] = ((valid >> (16 * kb + 4 * g + j)) & 1ull) ? lg[j] * a.scale_log2 : -INFINITY;
+      for (int j = 0; j < 4; ++j) sv[kb][j] = ((vlane >> (16 * kb + j)) & 1ull) ? lg[j] * a.scale_log2 : -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll

@@ -961,13 +961,16 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
     mx = rows_max(mx);
     const float m_new = (mx > m_run + kMaxSlack) ? mx : m_run;
     const float alpha = rescale(m_run, m_new);
+    // absent keys have sv = -inf and exp2(-inf) = 0; m_new is -inf only if every key so far
+    // is absent, and then P is 0 through the finite stand-in
+    const float m_sub = m_new == -INFINITY ? 0.f : m_new;
     float pr[4][4];  // bf16 rows: P rounded to bf16; fp8 rows: rounded per value block below
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float pj = (sv[kb][j] == -INFINITY) ? 0.f : ex2(sv[kb][j] - m_new);
+        const float pj = ex2(sv[kb][j] - m_sub);
         pr[kb][j] = KVF ? pj : __uint_as_float(f32_to_bf16_bits(pj) << 16);
         ls += pr[kb][j];
       }

@@ -82,13 +82,16 @@ __device__ __forceinline__ PoolState pool_rows(const RowsDev& c, const RowsDev& 
   return PoolState{m0, m1, s0, s1, a0, a1};
 }
 
-// RG row groups of 256 threads each pool a contiguous share of the entry's sources (loads
-// issued in batches of 8, unconditionally: rows past the end repeat the last row and are
-// skipped), then group 0 merges the group states in group order.
-template <int RG>
+// The workgroup's CW channel pairs starting at pair CW * cg (a wavefront-multiple, so the
+// fp8 and MXFP4 scale blocks stay within one wavefront): RG row groups of CW threads each
+// pool a contiguous share of the entry's sources (loads issued in batches, unconditionally:
+// rows past the end repeat the last row and are skipped), then group 0 merges the group
+// states in group order.
+template <int RG, int CW>
 __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& c, const RowsDev& z,
                                                const float* __restrict__ bias, int ratio, int overlap,
-                                               const RopeTab& rope, const RowsOut& out, int max_new, int blk) {
+                                               const RopeTab& rope, const RowsOut& out, int max_new, int blk, int cg) {
+  static_assert(CW % 64 == 0 && CW <= 256, "channel pairs per workgroup");
   const int b = blk / max_new;
   const int jn = blk % max_new;
   if (b >= S.n_seqs) return;
@@ -100,8 +103,10 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
   if (i >= i_hi) return;
 
   const int D = c.dim;
-  const int pair = threadIdx.x & 255;
-  const int grp = threadIdx.x >> 8;
+  if (2 * CW * cg >= D) return;
+  const int pair = CW * cg + (int)(threadIdx.x % CW);
+  const int tp = threadIdx.x % CW;  // the thread's pair within the workgroup
+  const int grp = threadIdx.x / CW;
   const bool active = 2 * pair < D;
   const int64_t lo = (i - overlap) * ratio;
   const int64_t hi = (i + 1) * ratio;
@@ -109,7 +114,7 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
   const int64_t tok0 = S.tok_off[b];
 
   __shared__ double s_freq[kMaxRopePairs];
-  __shared__ PoolState s_part[RG > 1 ? RG - 1 : 1][256];
+  __shared__ PoolState s_part[RG > 1 ? RG - 1 : 1][CW];
   for (int q = threadIdx.x; q < rope.dims / 2; q += blockDim.x) s_freq[q] = rope.inv_freq[q];
 
   float2 acc = make_float2(0.f, 0.f);
@@ -122,20 +127,20 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
     const int64_t j1 = min(hi, j0 + share);
     const float* bsrc = bias - lo * D;  // row j of the slot bias is bsrc + j * D
     if (c.dtype == DT_BF16 && z.dtype == DT_BF16)
-      st = pool_rows<DT_BF16, DT_BF16, RG == 1 ? 8 : 16>(c, z, bsrc, D, tok0 - tok_lo, j0, j1, pair);
+      st = pool_rows<DT_BF16, DT_BF16, 8>(c, z, bsrc, D, tok0 - tok_lo, j0, j1, pair);
     else if (c.dtype == DT_F32 && z.dtype == DT_F32)
-      st = pool_rows<DT_F32, DT_F32, RG == 1 ? 8 : 16>(c, z, bsrc, D, tok0 - tok_lo, j0, j1, pair);
+      st = pool_rows<DT_F32, DT_F32, 8>(c, z, bsrc, D, tok0 - tok_lo, j0, j1, pair);
     else
       st = pool_rows<-1, -1, 8>(c, z, bsrc, D, tok0 - tok_lo, j0, j1, pair);
   }
   if (RG > 1) {
-    if (grp > 0) s_part[grp - 1][pair] = st;
+    if (grp > 0) s_part[grp - 1][tp] = st;
     __syncthreads();
     if (grp > 0) return;
     if (active) {
 #pragma unroll
       for (int g2 = 1; g2 < RG; ++g2) {
-        const PoolState o = s_part[g2 - 1][pair];
+        const PoolState o = s_part[g2 - 1][tp];
         const float n0 = fmaxf(st.m0, o.m0), n1 = fmaxf(st.m1, o.m1);
         const float r0 = rescale(st.m0, n0), r1 = rescale(st.m1, n1);
         const float q0 = rescale(o.m0, n0), q1 = rescale(o.m1, n1);
@@ -212,27 +217,32 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
   }
 }
 
-template <int RG>
-__global__ void __launch_bounds__(256 * RG) compress_kernel(SeqsDev S, CompressJob j0, int ratio, int overlap,
-                                                            int max_new) {
-  compress_block<RG>(S, j0.c, j0.z, j0.bias, ratio, overlap, j0.rope, j0.out, max_new, blockIdx.x);
+template <int RG, int CW>
+__global__ void __launch_bounds__(CW * RG) compress_kernel(SeqsDev S, CompressJob j0, int ratio, int overlap,
+                                                           int max_new, int n_cg) {
+  compress_block<RG, CW>(S, j0.c, j0.z, j0.bias, ratio, overlap, j0.rope, j0.out, max_new, blockIdx.x / n_cg,
+                         blockIdx.x % n_cg);
 }
 
 // Two jobs over the same batch in one launch (KV rows and indexer keys of a CSA layer): the
-// first S.n_seqs * max_new workgroups run job 0, the rest job 1, with the same arithmetic
-// as two separate launches.
-template <int RG>
-__global__ void __launch_bounds__(256 * RG) compress2_kernel(SeqsDev S, CompressJob j0, CompressJob j1, int ratio,
-                                                             int overlap, int max_new) {
-  const int per_job = S.n_seqs * max_new;
+// first S.n_seqs * max_new * n_cg workgroups run job 0, the rest job 1, with the same
+// arithmetic as two separate launches.
+template <int RG, int CW>
+__global__ void __launch_bounds__(CW * RG) compress2_kernel(SeqsDev S, CompressJob j0, CompressJob j1, int ratio,
+                                                            int overlap, int max_new, int n_cg) {
+  const int per_job = S.n_seqs * max_new * n_cg;
+  const int k = (int)blockIdx.x < per_job ? (int)blockIdx.x : (int)blockIdx.x - per_job;
   if ((int)blockIdx.x < per_job)
-    compress_block<RG>(S, j0.c, j0.z, j0.bias, ratio, overlap, j0.rope, j0.out, max_new, blockIdx.x);
+    compress_block<RG, CW>(S, j0.c, j0.z, j0.bias, ratio, overlap, j0.rope, j0.out, max_new, k / n_cg, k % n_cg);
   else
-    compress_block<RG>(S, j1.c, j1.z, j1.bias, ratio, overlap, j1.rope, j1.out, max_new, blockIdx.x - per_job);
+    compress_block<RG, CW>(S, j1.c, j1.z, j1.bias, ratio, overlap, j1.rope, j1.out, max_new, k / n_cg, k % n_cg);
 }
 
-// Sources per entry from which the pooling is split over four row groups.
+// Sources per entry from which the pooling is split: 16 row groups (8 sources each for a
+// 128-token block, one batch of loads per thread) over 64 channel pairs per workgroup, so an
+// entry's channels spread over several workgroups.
 constexpr int kSplitSources = 64;
+constexpr int kSplitGroups = 16, kSplitPairs = 64;
 
 hipError_t launch_compress(const SeqsDev& S, const RowsDev& c, const RowsDev& z, const float* bias, int ratio,
                            int overlap, const RopeTab& rope, const RowsOut& out, int max_q, hipStream_t stream) {
@@ -240,12 +250,14 @@ hipError_t launch_compress(const SeqsDev& S, const RowsDev& c, const RowsDev& z,
   const int64_t blocks = (int64_t)S.n_seqs * max_new;
   if (blocks == 0) return hipSuccess;
   const CompressJob j0{c, z, bias, rope, out};
-  if (ratio * (1 + overlap) >= kSplitSources)
-    hipLaunchKernelGGL(compress_kernel<4>, dim3((unsigned)blocks), dim3(1024), 0, stream, S, j0, ratio, overlap,
-                       max_new);
-  else
-    hipLaunchKernelGGL(compress_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, S, j0, ratio, overlap,
-                       max_new);
+  if (ratio * (1 + overlap) >= kSplitSources) {
+    const int n_cg = (c.dim / 2 + kSplitPairs - 1) / kSplitPairs;
+    hipLaunchKernelGGL((compress_kernel<kSplitGroups, kSplitPairs>), dim3((unsigned)(blocks * n_cg)),
+                       dim3(kSplitGroups * kSplitPairs), 0, stream, S, j0, ratio, overlap, max_new, n_cg);
+  } else {
+    hipLaunchKernelGGL((compress_kernel<1, 256>), dim3((unsigned)blocks), dim3(256), 0, stream, S, j0, ratio, overlap,
+                       max_new, 1);
+  }
   return hipGetLastError();
 }
 
@@ -257,12 +269,14 @@ hipError_t launch_compress2(const SeqsDev& S, const RowsDev& c0, const RowsDev& 
   const int64_t blocks = (int64_t)S.n_seqs * max_new;
   if (blocks == 0) return hipSuccess;
   const CompressJob j0{c0, z0, bias0, rope0, out0}, j1{c1, z1, bias1, rope1, out1};
-  if (ratio * (1 + overlap) >= kSplitSources)
-    hipLaunchKernelGGL(compress2_kernel<4>, dim3((unsigned)(2 * blocks)), dim3(1024), 0, stream, S, j0, j1, ratio,
-                       overlap, max_new);
-  else
-    hipLaunchKernelGGL(compress2_kernel<1>, dim3((unsigned)(2 * blocks)), dim3(256), 0, stream, S, j0, j1, ratio,
-                       overlap, max_new);
+  if (ratio * (1 + overlap) >= kSplitSources) {
+    const int n_cg = (max(c0.dim, c1.dim) / 2 + kSplitPairs - 1) / kSplitPairs;
+    hipLaunchKernelGGL((compress2_kernel<kSplitGroups, kSplitPairs>), dim3((unsigned)(2 * blocks * n_cg)),
+                       dim3(kSplitGroups * kSplitPairs), 0, stream, S, j0, j1, ratio, overlap, max_new, n_cg);
+  } else {
+    hipLaunchKernelGGL((compress2_kernel<1, 256>), dim3((unsigned)(2 * blocks)), dim3(256), 0, stream, S, j0, j1,
+                       ratio, overlap, max_new, 1);
+  }
   return hipGetLastError();
 }
 

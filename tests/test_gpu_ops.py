@@ -51,6 +51,11 @@ COMPRESS_CASES = [
     (ops.KV_SPLIT, ops.BF16, ops.KV_SPLIT, 512, 4, 1, 64),
     (ops.BF16, ops.BF16, ops.MXFP4, 128, 4, 1, 0),
     (ops.F32, ops.F32, ops.KV_SPLIT, 256, 4, 1, 64),
+    # sources split over row groups and channels over workgroups (>= 64 sources per entry):
+    # fp8 scale blocks per wavefront, MXFP4 blocks, a part-filled last channel group
+    (ops.BF16, ops.BF16, ops.KV_SPLIT, 512, 128, 0, 64),
+    (ops.BF16, ops.BF16, ops.MXFP4, 128, 128, 0, 0),
+    (ops.F32, ops.F32, ops.F32, 160, 32, 1, 32),
 ]
 
 
@@ -135,10 +140,12 @@ def test_compress_matches_oracle(case):
         _check_quantised(of, sub, refm, len(rows))
 
 
-def test_compress2_equals_two_compress_calls():
-    """The paired launch (KV rows + indexer keys) writes exactly the bytes of two launches."""
+@pytest.mark.parametrize("ratio", [4, 32])
+def test_compress2_equals_two_compress_calls(ratio):
+    """The paired launch (KV rows + indexer keys) writes exactly the bytes of two launches
+    (ratio 32 with overlap: 64 sources per entry, the split pooling)."""
     g = np.random.default_rng(11)
-    ratio, D, dI = 4, 512, 128
+    D, dI = 512, 128
     n_q, ctx = [5, 1, 1, 12], [800, 4096, 3, 2047]
     ob, sq, n_ent, n_tok = make_batch(n_q, ctx, ratio, tok_hist=2 * ratio + 8)
     c, _ = _rows_in(ops.BF16, g.standard_normal((n_tok, D)))

@@ -8,7 +8,7 @@
 // 16 query heads, chunk of the token's key list), 8 waves in 4 pairs.  The long-list kernel
 // (CSA with k >= 1024, one chunk): workgroup = (token, 64 heads), 8 waves, so each gathered
 // row is read once per token (see the kernels).  The key list is walked in tiles of 64 rows
-// staged in LDS (rows padded to 1040 bytes); each wave prefetches its share of the next
+// staged in LDS (rows padded to 1056 bytes); each wave prefetches its share of the next
 // tile into registers, or for fp8 rows in the long-list kernel straight into LDS (one row
 // per wave instruction, any row order, so the top-k gather is fully coalesced).
 // The tile format is bf16 for bf16 rows; fp8 rows are staged as their codes in fp16
@@ -41,7 +41,7 @@ typedef i16x4_t __attribute__((address_space(3))) * lds_i16x4_ptr;
 constexpr int kT = 64;                 // keys per tile
 constexpr int kHG = 16;                // query heads per workgroup
 constexpr int kDM = 512;               // head dim of this kernel
-constexpr int kKStride = kDM * 2 + 16;  // bytes per staged key row
+constexpr int kKStride = kDM * 2 + 32;  // bytes per staged key row (the pad spreads LDS banks)
 constexpr int kRopeMax = 64;            // rotary dims this kernel takes (the row's last 64 at most)
 constexpr int kLoStride = kRopeMax * 2 + 16;  // bytes per row of the rotated-dims residual tile
 

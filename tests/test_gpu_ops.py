@@ -320,6 +320,11 @@ ATTEND_CASES = [
     (ops.BF16, 512, 16, True, 4, 100, 0),
     (ops.KV_SPLIT, 512, 64, True, 4, 256, 128),
     (ops.KV_SPLIT, 512, 64, False, 128, 0, 128),
+    # the 64-head kernel for k >= 1024: tokens with no visible entry (whole tiles absent),
+    # a part-filled head group, a 64-token window
+    (ops.BF16, 512, 64, True, 4, 2048, 128),
+    (ops.KV_SPLIT, 512, 64, True, 4, 1024, 128),
+    (ops.KV_SPLIT, 512, 40, True, 4, 4096, 64),
     # (..., outliers)
     (ops.BF16, 512, 64, True, 4, 512, 128, True),
     (ops.BF16, 512, 64, True, 4, 1024, 128, True),

@@ -1060,7 +1060,7 @@ __global__ void __launch_bounds__(256) attend_combine_mfma_kernel(AttendArgs a, 
                                                                   const float* __restrict__ ws_ml, int max_chunks,
                                                                   int chunk_slots) {
   (void)chunk_slots;
-  constexpr int kCB = 8;
+  constexpr int kCB = 16;
   __shared__ FreqLds F;
   const int n_h4 = (a.n_h + 3) / 4;
   const int t = blockIdx.x / n_h4;

@@ -260,51 +260,57 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Stage rows row0 + i, i < NR, of the tile from st.v[i] in the tile format (fp8 rows: codes
-// in fp16, block scales to L.scl, bf16 tail in fp16); their window bits and positions are
-// bit and offset it0 + i of st.  Then, when `winmask` (the rows whose logits read the
-// residual tile together with these) holds a window row, rotate the window rows among them
-// and write the rotation residuals of these rows (zero for the others).
 // Window rows among rows row0 .. row0+NR-1 of the tile (already staged; window bits and
 // positions are bit and offset it0 + i of st): when `winmask` (the rows whose logits read the
 // residual tile together with these) holds a window row, rotate the window rows among them
-// in place and write the rotation residuals of these rows (zero for the others).
-template <bool KVF, int NR, class Lds>
+// in place and write the rotation residuals of these rows (zero for the others).  WIDE: lane
+// l takes rotary pair l % 32 of rows l / 32, l / 32 + 2, ...; otherwise lanes 0..31 take
+// pair l of every row (fewer registers).  The rows' positions are consecutive, so the angle
+// of a lane's first row is advanced by the row step per row (angle addition; error ~1e-6
+// after the steps a tile needs).
+template <bool KVF, int NR, bool WIDE, class Lds>
 __device__ __forceinline__ void rotate_window_rows(Lds& L, const AttendArgs& a, const TileStage& st, int row0,
                                                    int it0, uint64_t winmask, int lane, const FreqLds& F) {
-  if (winmask != 0u && lane < kRopeMax / 2) {
-    const int d = kDM - kRopeMax + 2 * lane;
+  constexpr int RS = WIDE ? 2 : 1;  // row step of a lane
+  static_assert(NR % RS == 0, "rows come in pairs");
+  if (winmask != 0u && (WIDE || lane < kRopeMax / 2)) {
+    const int qp = lane & (kRopeMax / 2 - 1);
+    const int first = WIDE ? lane / (kRopeMax / 2) : 0;
+    const int d = kDM - kRopeMax + 2 * qp;
     const int dn = kDM - a.rope.dims;
-    uint32_t u[NR];
+    uint32_t u[NR / RS];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) u[i] = *reinterpret_cast<const uint32_t*>(&L.k[(row0 + i) * kKStride + d * 2]);
-    // the rows' positions are consecutive: rotate the angle of the first by one position
-    // per row (angle addition; error ~1e-6 after the 15 steps)
+    for (int m = 0; m < NR / RS; ++m)
+      u[m] = *reinterpret_cast<const uint32_t*>(&L.k[(row0 + first + RS * m) * kKStride + d * 2]);
     const int q = d >= dn ? (d - dn) >> 1 : 0;
-    float c, s, c1, s1;
-    rope_cs_mode<ROPE_FAST>(st.pos0 + it0, F, q, &c, &s);
-    rope_cs_mode<ROPE_FAST>(1, F, q, &c1, &s1);
+    float c, s, cs, ss;
+    rope_cs_mode<ROPE_FAST>(st.pos0 + it0 + first, F, q, &c, &s);
+    rope_cs_mode<ROPE_FAST>(RS, F, q, &cs, &ss);
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int it = it0 + i;
+    for (int m = 0; m < NR / RS; ++m) {
+      const int i = first + RS * m, it = it0 + i;
       uint32_t res = 0u;
-      if (i > 0) {
-        const float cn = __builtin_fmaf(c, c1, -(s * s1));
-        s = __builtin_fmaf(s, c1, c * s1);
+      if (m > 0) {
+        const float cn = __builtin_fmaf(c, cs, -(s * ss));
+        s = __builtin_fmaf(s, cs, c * ss);
         c = cn;
       }
       if (((st.win >> it) & 1ull) && d >= dn) {
-        const float2 y = rotate2(unpack16<KVF>(u[i]), c, s);
+        const float2 y = rotate2(unpack16<KVF>(u[m]), c, s);
         const uint32_t hi = pack16<KVF>(y.x, y.y);
         const float2 yh = unpack16<KVF>(hi);
         *reinterpret_cast<uint32_t*>(&L.k[(row0 + i) * kKStride + d * 2]) = hi;
         res = pack16<KVF>(y.x - yh.x, y.y - yh.y);
       }
-      *reinterpret_cast<uint32_t*>(&L.klo[(row0 + i) * kLoStride + 4 * lane]) = res;
+      *reinterpret_cast<uint32_t*>(&L.klo[(row0 + i) * kLoStride + 4 * qp]) = res;
     }
   }
 }
 
+// Stage rows row0 + i, i < NR, of the tile from st.v[i] in the tile format (fp8 rows: codes
+// in fp16, block scales to L.scl, bf16 tail in fp16); their window bits and positions are
+// bit and offset it0 + i of st.  Then rotate the window rows among them (above; all 64
+// lanes for bf16 rows, 32 for fp8 rows, whose decode needs the registers).
 template <bool KVF, int NR, class Lds>
 __device__ __forceinline__ void store_rows(Lds& L, const AttendArgs& a, const TileStage& st, int row0, int it0,
                                            uint64_t winmask, int lane, const FreqLds& F) {
@@ -328,7 +334,7 @@ __device__ __forceinline__ void store_rows(Lds& L, const AttendArgs& a, const Ti
       *reinterpret_cast<uint4*>(&L.k[(row0 + i) * kKStride + 2 * (kDM - kSplitBf16Dims) +
                                      16 * (lane - kSplitCodeLanes)]) = from_bf16<true>(st.v[i]);
   }
-  rotate_window_rows<KVF, NR>(L, a, st, row0, it0, winmask, lane, F);
+  rotate_window_rows<KVF, NR, !KVF>(L, a, st, row0, it0, winmask, lane, F);
 }
 
 // Loads of rows roff + I0 .. roff + I1 - 1 of the pair's 16 into st.v[I0 .. I1-1].  A
@@ -885,7 +891,7 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
           L.scl[b][rs] = ((st.valid >> rs) & 1ull) ? rawsc[4 * rs + b] : 0.f;
         }
       }
-      rotate_window_rows<KVF, 8>(L, a, st, r0, r0, (st.win >> r0) & 0xffull, lane, F);
+      rotate_window_rows<KVF, 8, false>(L, a, st, r0, r0, (st.win >> r0) & 0xffull, lane, F);
     } else {
       store_rows<KVF, 8>(L, a, st, 8 * w, 8 * w, (st.win >> (8 * w)) & 0xffull, lane, F);
     }

@@ -71,9 +71,15 @@ constexpr int kSplitLanes = kSplitCodeLanes + kSplitBf16Dims * 2 / 16;
 
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+// Two floats to bf16 (a in the low half), nearest even, by the hardware conversion
+// (v_cvt_pk_bf16_f32: one instruction for the pair, no NaN branch).
+typedef __attribute__((ext_vector_type(2))) float cvt_f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 cvt_bf16x2_t;
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((cvt_f32x2_t){a, b}, cvt_bf16x2_t));
 }
+// One float to bf16 bits (low 16), nearest even, hardware conversion.
+__device__ __forceinline__ uint32_t bf16_rne(float x) { return pack_bf16(x, 0.f) & 0xffffu; }
 
 // The tile's 16-bit element type: bf16 for bf16 rows; fp16 (11-bit significand) for rows
 // decoded from fp8 blocks, whose scaled values would lose too much in bf16 next to
@@ -557,7 +563,7 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
     for (int j = 0; j < 4; ++j) {
       const float pj = (sv[j] == -INFINITY) ? 0.f : ex2(sv[j] - m_new);
       if (!KVF) {
-        pb[j] = f32_to_bf16_bits(pj);
+        pb[j] = bf16_rne(pj);
         pr[j] = __uint_as_float(pb[j] << 16);
       } else {
         pr[j] = pj;  // rounded per value block below
@@ -977,7 +983,7 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float pj = ex2(sv[kb][j] - m_sub);
-        pr[kb][j] = KVF ? pj : __uint_as_float(f32_to_bf16_bits(pj) << 16);
+        pr[kb][j] = KVF ? pj : __uint_as_float(bf16_rne(pj) << 16);
         ls += pr[kb][j];
       }
     ls = rows_sum(ls);

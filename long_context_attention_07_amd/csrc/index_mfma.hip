@@ -16,8 +16,9 @@
 //   <= 64 indexer heads (staged once through LDS) sit in registers as the A operand (4
 //   blocks of 16), the keys are
 //   the B operand.  A lane then holds 16 heads of one entry and sums w_h * relu over them
-//   in a fixed order (head block, then row); two xor-shuffles across the lane groups finish
-//   the head sum, so a score depends on its token and entry only.
+//   in a fixed order (head block, then row; max(0, x) as an integer max of the bits); two
+//   row-swap permutes across the lane groups finish the head sum, so a score depends on its
+//   token and entry only.
 
 #include "common.cuh"
 #include "kernels.h"
@@ -149,9 +150,15 @@ __global__ void __launch_bounds__(256) index_score_mfma_kernel(SeqsDev S, RowsDe
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s = __builtin_fmaf(wh[hb][j], fmaxf(acc[hb][j], 0.f), s);
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
+      for (int j = 0; j < 4; ++j)
+        s = __builtin_fmaf(wh[hb][j], __int_as_float(max(__float_as_int(acc[hb][j]), 0)), s);  // w * max(0, x)
+    // (g0 + g1) + (g2 + g3) across the lane groups by the row-swap permutes
+    {
+      auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+      s = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+      s = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+    }
     const int64_t e = e_begin + (int64_t)i * kIT + 16 * wv + c16;
     if (g == 0 && e < V) srow[e] = s;
   }

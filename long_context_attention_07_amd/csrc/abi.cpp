@@ -279,7 +279,7 @@ int csa_topk(const csa_seqs* seqs, const float* score, int64_t score_stride, int
   if (score_stride < max_vis)
     return fail(CSA_EINVAL, "score_stride %lld < floor(max_ctx/ratio) = %d", (long long)score_stride, max_vis);
   if (seqs->total_q == 0) return ok();
-  hipError_t e = csa::launch_topk(dev_seqs(seqs), score, score_stride, ratio, k, idx, max_vis,
+  hipError_t e = csa::launch_topk(dev_seqs(seqs), score, score_stride, ratio, k, idx, max_vis, seqs->max_q,
                                   static_cast<hipStream_t>(stream));
   return hip_status(e, "csa_topk launch");
 }
@@ -301,7 +301,7 @@ int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int
   hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio, score, stride,
                                          max_vis, seqs->max_q, s);
   if (e != hipSuccess) return hip_status(e, "csa_index_topk score launch");
-  e = csa::launch_topk(dev_seqs(seqs), score, stride, ratio, k, idx, max_vis, s);
+  e = csa::launch_topk(dev_seqs(seqs), score, stride, ratio, k, idx, max_vis, seqs->max_q, s);
   return hip_status(e, "csa_index_topk select launch");
 }
 

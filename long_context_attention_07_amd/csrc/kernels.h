@@ -19,7 +19,7 @@ hipError_t launch_index_score(const SeqsDev& S, const RowsDev& qI, const float* 
                               hipStream_t stream);
 
 hipError_t launch_topk(const SeqsDev& S, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
-                       int max_vis, hipStream_t stream);
+                       int max_vis, int max_q, hipStream_t stream);
 
 // Attention over per-token key lists.  mode_csa: keys = idx entries (k slots) then the
 // window; otherwise keys = entries 0..V(p)-1 then the window.

@@ -181,9 +181,8 @@ __device__ __forceinline__ uint2 topk_find_digit(const uint32_t* hist, int nbins
   const uint32_t incl = wave_incl_scan(loc);
   if (lane == 63) sh.red[0][wv] = incl;
   __syncthreads();
-  uint32_t base = 0;
-#pragma unroll
-  for (int i = 0; i < kTopkThreads / 64; ++i) base += (i < wv) ? sh.red[0][i] : 0u;
+  // keys in the waves before this one: lane i < wv reads wave i's total, one scan sums them
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(lane < wv ? sh.red[0][lane] : 0u), 63);
   uint32_t ab = base + incl - loc;
   if (tid < owners && ab < remaining && ab + loc >= remaining) {
     for (int d = 0; d < per; ++d) {
@@ -205,13 +204,12 @@ __device__ __forceinline__ uint2 topk_find_digit(const uint32_t* hist, int nbins
 // 16-byte aligned.  Three digit passes (12, 12, 8 bits) with one histogram each; then each
 // thread counts its keys > T and == T, one block scan gives its output offsets, and it
 // writes its kept indices in ascending order.
+// Thread tid's keys NPT tid .. NPT tid + NPT-1 of the row, those below `lim` (16 bytes at a
+// time when the row is 16-byte aligned); the rest 0.
 template <int NPT>
-__device__ void topk_select_reg(const float* __restrict__ src, int n, int k, int32_t* __restrict__ out,
-                                TopkRegLds& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int i0 = NPT * tid;
-  uint32_t key[NPT];
-  if ((reinterpret_cast<uintptr_t>(src) & 15u) == 0 && i0 + NPT <= n) {
+__device__ __forceinline__ void topk_load_keys(const float* __restrict__ src, int lim, uint32_t (&key)[NPT]) {
+  const int i0 = NPT * (int)threadIdx.x;
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) == 0 && i0 + NPT <= lim) {
 #pragma unroll
     for (int q = 0; q < NPT / 4; ++q) {
       const float4 v = reinterpret_cast<const float4*>(src + i0)[q];
@@ -222,8 +220,16 @@ __device__ void topk_select_reg(const float* __restrict__ src, int n, int k, int
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < NPT; ++j) key[j] = i0 + j < n ? score_key(src[i0 + j]) : 0u;
+    for (int j = 0; j < NPT; ++j) key[j] = i0 + j < lim ? score_key(src[i0 + j]) : 0u;
   }
+}
+
+// The selection over keys held as above; keys at n and beyond take no part.
+template <int NPT>
+__device__ void topk_select_keys(const uint32_t (&key)[NPT], int n, int k, int32_t* __restrict__ out,
+                                 TopkRegLds& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int i0 = NPT * tid;
   for (int b = tid; b < 4096; b += kTopkThreads) {
     sh.hist0[b] = 0u;
     sh.hist1[b] = 0u;
@@ -266,12 +272,8 @@ __device__ void topk_select_reg(const float* __restrict__ src, int n, int k, int
     sh.red[1][wv] = ie;
   }
   __syncthreads();
-  uint32_t bg = 0, be = 0;
-#pragma unroll
-  for (int i = 0; i < kTopkThreads / 64; ++i) {
-    bg += (i < wv) ? sh.red[0][i] : 0u;
-    be += (i < wv) ? sh.red[1][i] : 0u;
-  }
+  const uint32_t bg = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(lane < wv ? sh.red[0][lane] : 0u), 63);
+  const uint32_t be = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(lane < wv ? sh.red[1][lane] : 0u), 63);
   uint32_t eq_rank = be + ie - eq;
   uint32_t pos = bg + ig - gt + min(eq_rank, remaining);
 #pragma unroll
@@ -284,6 +286,14 @@ __device__ void topk_select_reg(const float* __restrict__ src, int n, int k, int
     }
     if (take) out[pos++] = i0 + j;
   }
+}
+
+template <int NPT>
+__device__ __forceinline__ void topk_select_reg(const float* __restrict__ src, int n, int k, int32_t* __restrict__ out,
+                                                TopkRegLds& sh) {
+  uint32_t key[NPT];
+  topk_load_keys<NPT>(src, n, key);
+  topk_select_keys<NPT>(key, n, k, out, sh);
 }
 
 __global__ void __launch_bounds__(kTopkThreads) topk_kernel(SeqsDev S, const float* __restrict__ score,
@@ -306,10 +316,49 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(SeqsDev S, const flo
   else topk_select_mem(src, (int)V, k, out, sh);
 }
 
+// One query row per sequence (decode): the row's address does not depend on the context
+// lookup, so the keys below min(row stride, 1024 NPT) are requested first and the lookup
+// overlaps them; keys at V and beyond take no part.  The selection is the same function
+// of the row, so a token's indices do not depend on the kernel.
+template <int NPT>
+__global__ void __launch_bounds__(kTopkThreads) topk_decode_kernel(SeqsDev S, const float* __restrict__ score,
+                                                                   int64_t score_stride, int ratio, int k,
+                                                                   int32_t* __restrict__ idx) {
+  __shared__ TopkLds sh;
+  __shared__ TopkRegLds rsh;
+  const int t = blockIdx.x;
+  const float* src = score + (int64_t)t * score_stride;
+  uint32_t key[NPT];
+  topk_load_keys<NPT>(src, (int)min(score_stride, (int64_t)NPT * kTopkThreads), key);
+  const TokenCtx ctx = token_ctx(S, t);
+  const int64_t V = (ctx.p + 1) / ratio;
+  int32_t* out = idx + (int64_t)t * k;
+  if (V <= k) {
+    for (int i = threadIdx.x; i < k; i += kTopkThreads) out[i] = (i < V) ? i : -1;
+    return;
+  }
+  if (V > NPT * kTopkThreads) {
+    topk_select_mem(src, (int)V, k, out, sh);
+    return;
+  }
+  topk_select_keys<NPT>(key, (int)V, k, out, rsh);
+}
+
 hipError_t launch_topk(const SeqsDev& S, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
-                       int max_vis, hipStream_t stream) {
-  (void)max_vis;
+                       int max_vis, int max_q, hipStream_t stream) {
   if (S.total_q == 0) return hipSuccess;
+  if (max_q == 1 && max_vis > k && max_vis <= 32 * kTopkThreads) {
+    if (max_vis <= 8 * kTopkThreads)
+      hipLaunchKernelGGL(topk_decode_kernel<8>, dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score, score_stride,
+                         ratio, k, idx);
+    else if (max_vis <= 16 * kTopkThreads)
+      hipLaunchKernelGGL(topk_decode_kernel<16>, dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score,
+                         score_stride, ratio, k, idx);
+    else
+      hipLaunchKernelGGL(topk_decode_kernel<32>, dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score,
+                         score_stride, ratio, k, idx);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(topk_kernel, dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score, score_stride, ratio, k,
                      idx);
   return hipGetLastError();

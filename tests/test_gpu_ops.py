@@ -241,21 +241,27 @@ def test_index_score_mxfp4_query_blocks():
 # ----------------------------------------------------------------------------- top-k
 
 
-def test_topk_exact_on_identical_scores():
+@pytest.mark.parametrize("keep", ["all", "upto32768", "upto8192"])
+def test_topk_exact_on_identical_scores(keep):
+    """Exact selection with ties.  One query row per sequence: with every row (one longer
+    than 32768) the general kernel runs; without the longest, the decode kernel that loads
+    the keys before the context lookup (32 or 8 keys per thread)."""
     g = np.random.default_rng(21)
     ratio = 1
     # V: k-ties, V <= k, V = k + 1, keys held in registers (8, 16 or 32 per thread up to
     # 32768, with the 8192 / 16384 boundaries) and streamed (> 32768) candidates
-    ctx = [300, 64, 65, 5000, 32768, 40000, 1, 8193, 12000, 16384]
+    ctx_all = [300, 64, 65, 5000, 32768, 40000, 1, 8193, 12000, 16384]
+    lim = {"all": 10 ** 9, "upto32768": 32768, "upto8192": 8192}[keep]
+    ctx = [c for c in ctx_all if c <= lim]
     n_q = [1] * len(ctx)
     ks = 64
     ob, sq, _, _ = make_batch(n_q, ctx, ratio)
     stride = max(ctx)
     s = np.full((len(ctx), stride), np.nan, dtype=np.float32)
     for r, L in enumerate(ctx):
-        if r == 0:
+        if L == 300:
             s[r, :L] = np.round(g.standard_normal(L) * 2) / 4        # heavy exact ties
-        elif r == 3:
+        elif L == 5000:
             s[r, :L] = np.where(g.random(L) < 0.5, 0.0, -0.0)         # only +-0: all tie
             s[r, 17] = 1.0
         else:

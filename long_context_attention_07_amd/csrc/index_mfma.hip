@@ -172,7 +172,7 @@ bool index_mfma_supported(const RowsDev& qI, const RowsDev& kI, int n_I, int64_t
 
 hipError_t launch_index_score_mfma(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
                                    int ratio, float* score, int64_t score_stride, int max_vis, hipStream_t stream) {
-  constexpr int kRing = 3, kTiles = 8;  // 48 KiB of LDS (3 workgroups per CU), 512 entries each
+  constexpr int kRing = 3, kTiles = 6;  // 48 KiB of LDS (3 workgroups per CU), 384 entries each
   const int per_wg = kIT * kTiles;
   const int n_parts = (max_vis + per_wg - 1) / per_wg;
   const int64_t n_log = (int64_t)S.total_q * n_parts;

@@ -366,6 +366,29 @@ def test_attend_matches_oracle(case):
     assert_close(lse.cpu().numpy(), ref_l, tol, "attend lse")
 
 
+@pytest.mark.parametrize("fmt,k,rope,n_win", [(ops.BF16, 512, 32, 128), (ops.BF16, 1024, 32, 128),
+                                              (ops.KV_SPLIT, 1024, 0, 128), (ops.BF16, 1024, 64, 0),
+                                              (ops.KV_SPLIT, 256, 32, 128)])
+def test_attend_rope_widths_and_no_window(fmt, k, rope, n_win):
+    """Rotary widths other than 64 (32 dims, none) in the pair kernel (k < 1024) and the
+    64-head kernel (k >= 1024), and the 64-head kernel without a window."""
+    log(f"attend rope={rope} fmt={fmt} k={k} n_win={n_win}")
+    g = np.random.default_rng(71 + k + rope + n_win)
+    D, n_h, ratio = 512, 64, 4
+    n_q, ctx = [2, 1, 3], [4093, 2000, 900]
+    data = _attend_inputs(g, fmt, D, n_h, n_q, ctx, ratio, k, n_win, tok_hist=n_win + 3)
+    ob, sq, q_rows, q_val, kv_rows, kv_val, tok_rows, tok_val, sink_t, sink_val, idx = data
+    scale = 1.0 / math.sqrt(D)
+    out = empty_rows(sq.total_q * n_h, D, ops.BF16)
+    lse = torch.zeros((sq.total_q, n_h), dtype=torch.float32, device=DEV)
+    ops.csa_attend(sq, q_rows, n_h, kv_rows, torch.from_numpy(idx).to(DEV), k, tok_rows, n_win, sink_t, scale, rope,
+                   10000.0, out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = _oracle_attend(ob, q_val, kv_val, tok_val, idx, n_win, sink_val, scale, rope, n_h, D, True, ratio)
+    assert_close(rows_values(out).reshape(sq.total_q, n_h, D), ref_o, 1e-2, "attend out")
+    assert_close(lse.cpu().numpy(), ref_l, 1e-2, "attend lse")
+
+
 @pytest.mark.parametrize("fmt,D,n_h", [(ops.F32, 128, 8), (ops.BF16, 512, 64), (ops.KV_SPLIT, 512, 64)])
 def test_attend_split_and_single_modes_bit_identical(fmt, D, n_h):
     """With a workspace the key lists are spread over workgroups per chunk; without, one

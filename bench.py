@@ -39,6 +39,7 @@ from long_context_attention_07_amd import configs, ops, synth  # noqa: E402
 METRIC = "CSA/HCA decode tokens/s at 64K–1M ctx; achieved HBM GB/s and MFMA % of peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6   # dense bf16 / fp16 MFMA
+FP8_PEAK_TFLOPS = 5033.2    # dense fp8 MFMA
 FP4_PEAK_TFLOPS = 10100.0   # dense MXFP4 (scaled fp4) MFMA
 N_SETS = 8
 # kernels each operation launches (substrings of the kernel names in profiler output)
@@ -237,13 +238,60 @@ def source_digest():
     h = hashlib.sha256()
     src = os.path.join(ROOT, "long_context_attention_07_amd", "csrc")
     for name in sorted(os.listdir(src)):
-        if name.endswith((".hip", ".cuh", ".h", ".cpp")):
+        if name.endswith((".hip", ".cuh", ".h", ".cpp")) and name != "probe.hip":
             h.update(name.encode())
             with open(os.path.join(src, name), "rb") as f:
                 h.update(f.read())
     with open(os.path.join(ROOT, "include", "csa.h"), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def achievable_peaks(stream, copy_bytes=1 << 30, reps=5):
+    """What this device reaches on the two priced resources, beside the published peaks:
+    a plain device copy of `copy_bytes` (HBM bytes = twice that), a read-only stream of the
+    same bytes, and back-to-back
+    matrix-core instructions per operand format, two waves per SIMD (libcsa_probe.so).
+    Context only: every roofline fraction is computed against the published peak."""
+    from long_context_attention_07_amd import probe
+    n_cu, khz = probe.device()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    src = torch.ones(copy_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    probe.copy(src, dst, copy_bytes, stream)
+    e0.record(stream)
+    for _ in range(reps):
+        probe.copy(src, dst, copy_bytes, stream)
+    e1.record(stream)
+    e1.synchronize()
+    copy_gbs = 2.0 * copy_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    words = torch.zeros(4 * probe.STREAM_WG_PER_CU * n_cu, dtype=torch.int32, device="cuda")
+    probe.read(src, copy_bytes, words, stream)
+    e0.record(stream)
+    for _ in range(reps):
+        probe.read(src, copy_bytes, words, stream)
+    e1.record(stream)
+    e1.synchronize()
+    read_gbs = 1.0 * copy_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst, words
+    n_wg = 2 * n_cu  # 4 waves per workgroup: 8 waves per compute unit, 2 per SIMD
+    sink = torch.empty(n_wg * 4, dtype=torch.float32, device="cuda")
+    iters = {"bf16": 16384, "fp8": 8192, "mxfp4": 8192}
+    peaks = {"bf16": BF16_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS, "mxfp4": FP4_PEAK_TFLOPS}
+    rate = {}
+    for name, fmt in probe.FORMATS.items():
+        probe.mfma(fmt, n_wg, iters[name], sink, stream)
+        e0.record(stream)
+        for _ in range(3):
+            probe.mfma(fmt, n_wg, iters[name], sink, stream)
+        e1.record(stream)
+        e1.synchronize()
+        rate[name] = 3 * probe.mfma_flop(fmt, n_wg, iters[name]) / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    return {"n_cu": n_cu, "clock_MHz": round(khz / 1000.0), "copy_bytes": copy_bytes,
+            "copy_GBs": round(copy_gbs, 1), "copy_frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "read_GBs": round(read_gbs, 1), "read_frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4),
+            "mfma_TFLOPs": {k: round(v, 1) for k, v in rate.items()},
+            "mfma_frac_of_peak": {k: round(v / peaks[k], 4) for k, v in rate.items()}}
 
 
 def profile_run(layers, stream, reps):
@@ -489,6 +537,7 @@ def run_prefill(args):
                 "frac": round(f / dt / 1e12 / peak, 4), "traffic": None, "flops_per_launch": int(f),
                 "avg_launch_us": round(dt * 1e6, 1)}
         log(f"prefill step {ms:.2f} ms, {value:.0f} tokens/s; per-op {json.dumps(kernels)}")
+        achievable = None if args.no_probe else achievable_peaks(stream)
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -498,6 +547,7 @@ def run_prefill(args):
                    "kv": "fp8 e4m3 1x128 + bf16 RoPE"},
         "roofline": roof,
         "kernels": kernels,
+        "achievable": achievable,
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
@@ -511,6 +561,7 @@ def main():
     ap.add_argument("--workload", default="csa_decode", choices=["csa_decode", "hca_decode", "csa_prefill"])
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-probe", action="store_true", help="skip the achievable-peak probes")
     ap.add_argument("--sets", type=int, default=N_SETS)
     ap.add_argument("--profile-run", type=int, default=0, metavar="REPS",
                     help="only launch each operation REPS times per layer set (for rocprofv3), then exit")
@@ -612,6 +663,10 @@ def main():
         step_bytes = sum(b for b, _ in work.values())
         step_flops = sum(f for _, f in work.values())
         log(f"per-op: {json.dumps(kernels)}")
+        achievable = None
+        if not args.no_probe:
+            achievable = achievable_peaks(stream)
+            log(f"achievable on this device: {json.dumps(achievable)}")
 
         cpu = None
         if not args.no_cpu:
@@ -632,6 +687,7 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_mfma_frac": round(step_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "kernels": kernels,
+        "achievable": achievable,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -1,9 +1,10 @@
-"""Build libcsa.so (the C-ABI HIP library) in-tree for gfx950.
+"""Build libcsa.so (the C-ABI HIP library) and libcsa_probe.so (the roofline probes) in-tree
+for gfx950.
 
     python -m long_context_attention_07_amd.build [--jobs N]
 
 Each source under csrc/ is compiled by hipcc to an object in _build/, then linked into
-long_context_attention_07_amd/libcsa.so.  Always rebuilds.
+long_context_attention_07_amd/libcsa.so (or libcsa_probe.so).  Always rebuilds.
 """
 
 import argparse
@@ -18,10 +19,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
+PROBE_LIB = os.path.join(PKG, "libcsa_probe.so")
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["abi.cpp", "compress.hip", "index.hip", "index_mfma.hip", "index_mx.hip", "topk.hip", "attend.hip",
            "attend_mfma.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -54,22 +57,27 @@ def _compile(src):
     return obj, r.stderr
 
 
-def build(jobs=None, verbose=False):
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4) // 2))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, srcs))
-    objs = []
-    for obj, err in results:
-        objs.append(obj)
-        if verbose and err.strip():
-            print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link failed for {os.path.basename(lib)}:\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(jobs=None, verbose=False):
+    srcs = [s for s in SOURCES + PROBE_SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4) // 2))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_compile, srcs))
+    objs = {}
+    for src, (obj, err) in zip(srcs, results):
+        objs[src] = obj
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    _link([objs[s] for s in srcs if s in SOURCES], LIB)
+    _link([objs[s] for s in srcs if s in PROBE_SOURCES], PROBE_LIB)
     return LIB
 
 

@@ -133,13 +133,14 @@ __device__ __forceinline__ void rotate_chunk(uint4 v, int64_t pos, const FreqLds
   *lo = make_uint4(r[0], r[1], r[2], r[3]);
 }
 
-// Final values of 8 consecutive output dims d0..d0+7 of one head (already normalised):
-// inverse RoPE of the pairs in the rotary range, rounded to bf16.  Shared by the single
-// launch and the combine kernel, so both produce the same bits.
-__device__ __forceinline__ uint4 finalize8(const float* x, int d0, int dn, int64_t p, const FreqLds& F) {
-  uint32_t w[4];
+// Final values of 2 NP consecutive output dims d0.. of one head (already normalised): inverse
+// RoPE of the pairs in the rotary range, rounded to bf16, pair i in w[i].  Shared by the
+// single launch and the combine kernel, so both produce the same bits.
+template <int NP>
+__device__ __forceinline__ void finalize_pairs(const float* x, int d0, int dn, int64_t p, const FreqLds& F,
+                                               uint32_t* w) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NP; ++i) {
     float2 y = make_float2(x[2 * i], x[2 * i + 1]);
     const int d = d0 + 2 * i;
     if (d >= dn) {
@@ -149,6 +150,11 @@ __device__ __forceinline__ uint4 finalize8(const float* x, int d0, int dn, int64
     }
     w[i] = pack_bf16(y.x, y.y);
   }
+}
+
+__device__ __forceinline__ uint4 finalize8(const float* x, int d0, int dn, int64_t p, const FreqLds& F) {
+  uint32_t w[4];
+  finalize_pairs<4>(x, d0, dn, p, F, w);
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -776,21 +782,9 @@ __device__ __forceinline__ void issue_rows_lds(int w, int lane, const TileStage&
     __builtin_amdgcn_global_load_lds((global_cvp)scp, (lds_vp)(rsc + 32 * w), 16, 0, 0);
 }
 
-// Final values of 4 consecutive output dims d0..d0+3 of one head: inverse RoPE of the two
-// pairs in the rotary range, rounded to bf16 (same arithmetic as finalize8).
 __device__ __forceinline__ uint2 finalize4(const float* x, int d0, int dn, int64_t p, const FreqLds& F) {
   uint32_t w[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    float2 y = make_float2(x[2 * i], x[2 * i + 1]);
-    const int d = d0 + 2 * i;
-    if (d >= dn) {
-      float c, s;
-      rope_cs_mode<ROPE_FAST>(p, F, (d - dn) >> 1, &c, &s);
-      y = rotate2(y, c, -s);
-    }
-    w[i] = pack_bf16(y.x, y.y);
-  }
+  finalize_pairs<2>(x, d0, dn, p, F, w);
   return make_uint2(w[0], w[1]);
 }
 
@@ -1066,33 +1060,38 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
 }
 
 // Fold of the chunk partials written by the split launch, in chunk order from the sink:
-// one wave per head, each lane 8 consecutive dims; same arithmetic as the single launch.
-// The first kCB chunks are requested together with the token record, before it is read.
+// each output dim is folded on its own (the per-head state M, Z is recomputed alike by
+// every lane), so the lanes of a head may take DPL = 8, 4 or 2 consecutive dims without
+// changing a bit: 64, 128 or 256 threads per head, the finer splits spreading a small batch
+// over more compute units.  Same arithmetic as the single launch.  The first kCB chunks
+// are requested together with the token record, before it is read.
+template <int DPL>
 __global__ void __launch_bounds__(256) attend_combine_mfma_kernel(AttendArgs a, const float* __restrict__ ws_o,
-                                                                  const float* __restrict__ ws_ml, int max_chunks,
-                                                                  int chunk_slots) {
-  (void)chunk_slots;
+                                                                  const float* __restrict__ ws_ml, int max_chunks) {
   constexpr int kCB = 16;
+  constexpr int TPH = kDM / DPL;  // threads per head
+  constexpr int HPW = 256 / TPH;  // heads per workgroup
+  static_assert(DPL == 2 || DPL == 4 || DPL == 8, "dims per lane");
   __shared__ FreqLds F;
-  const int n_h4 = (a.n_h + 3) / 4;
-  const int t = blockIdx.x / n_h4;
-  const int h = (blockIdx.x % n_h4) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const int n_hw = (a.n_h + HPW - 1) / HPW;
+  const int t = blockIdx.x / n_hw;
+  const int h = (blockIdx.x % n_hw) * HPW + (int)threadIdx.x / TPH;
+  const int lane = (int)threadIdx.x % TPH;
   const bool on = h < a.n_h;
   const int hh = on ? h : 0;
   const int64_t* meta = split_meta(const_cast<float*>(ws_ml), a, max_chunks);
   const int64_t p = meta[2 * t];
   const int n_chunks = (int)meta[2 * t + 1];
-  const int d0 = 8 * lane;
+  const int d0 = DPL * lane;
   const int64_t base0 = (int64_t)t * max_chunks * a.n_h + hh;
   FoldState f = fold_init(on ? a.sink[hh] * kLog2e : -INFINITY);
-  float O[8];
+  float O[DPL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) O[i] = 0.f;
+  for (int i = 0; i < DPL; ++i) O[i] = 0.f;
   load_freqs(F, a.rope);
   for (int c0 = 0; c0 < max_chunks; c0 += kCB) {
     float2 ml[kCB];
-    float4 o0[kCB], o1[kCB];
+    float o[kCB][DPL];
 #pragma unroll
     for (int i = 0; i < kCB; ++i) {
       // first batch: every chunk slot the workspace holds (in bounds, unused past n_chunks)
@@ -1100,8 +1099,21 @@ __global__ void __launch_bounds__(256) attend_combine_mfma_kernel(AttendArgs a, 
       if (c < (c0 == 0 ? max_chunks : n_chunks)) {
         const int64_t b = base0 + (int64_t)c * a.n_h;
         ml[i] = *reinterpret_cast<const float2*>(ws_ml + 2 * b);
-        o0[i] = *reinterpret_cast<const float4*>(ws_o + b * kDM + d0);
-        o1[i] = *reinterpret_cast<const float4*>(ws_o + b * kDM + d0 + 4);
+        const float* po = ws_o + b * kDM + d0;
+        if (DPL == 2) {
+          const float2 v = *reinterpret_cast<const float2*>(po);
+          o[i][0] = v.x;
+          o[i][1 % DPL] = v.y;
+        } else {
+#pragma unroll
+          for (int q = 0; q < DPL / 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(po + 4 * q);
+            o[i][(4 * q) % DPL] = v.x;
+            o[i][(4 * q + 1) % DPL] = v.y;
+            o[i][(4 * q + 2) % DPL] = v.z;
+            o[i][(4 * q + 3) % DPL] = v.w;
+          }
+        }
       }
     }
 #pragma unroll
@@ -1109,9 +1121,8 @@ __global__ void __launch_bounds__(256) attend_combine_mfma_kernel(AttendArgs a, 
       if (c0 + i < n_chunks) {
         float fa, fb;
         fold_step(f, ml[i].x, ml[i].y, &fa, &fb);
-        const float o[8] = {o0[i].x, o0[i].y, o0[i].z, o0[i].w, o1[i].x, o1[i].y, o1[i].z, o1[i].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) O[e] = __builtin_fmaf(O[e], fa, o[e] * fb);
+        for (int e = 0; e < DPL; ++e) O[e] = __builtin_fmaf(O[e], fa, o[i][e] * fb);
       }
     }
     if (c0 + kCB >= n_chunks) break;
@@ -1119,12 +1130,16 @@ __global__ void __launch_bounds__(256) attend_combine_mfma_kernel(AttendArgs a, 
   __syncthreads();  // frequency table
   if (!on) return;
   const float inv = (f.Z > 0.f) ? 1.0f / f.Z : 0.f;
-  float x[8];
+  float x[DPL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = O[i] * inv;
+  for (int i = 0; i < DPL; ++i) x[i] = O[i] * inv;
   const int dn = kDM - a.rope.dims;
-  *reinterpret_cast<uint4*>(a.out.data + ((int64_t)t * a.n_h + h) * a.out.stride + d0 * 2) =
-      finalize8(x, d0, dn, p, F);
+  uint32_t w[DPL / 2];
+  finalize_pairs<DPL / 2>(x, d0, dn, p, F, w);
+  uint8_t* dst = a.out.data + ((int64_t)t * a.n_h + h) * a.out.stride + d0 * 2;
+  if (DPL == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1 % (DPL / 2)], w[2 % (DPL / 2)], w[3 % (DPL / 2)]);
+  else if (DPL == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1 % (DPL / 2)]);
+  else *reinterpret_cast<uint32_t*>(dst) = w[0];
   if (a.lse && lane == 0) a.lse[(int64_t)t * a.n_h + h] = lse_natural(f);
 }
 
@@ -1152,6 +1167,8 @@ static void launch_attend_mfma_kernel(const AttendArgs& a, float* ws_o, float* w
 // length), never on the batch, so a token's bits do not depend on the batch either.
 static bool attend_long_lists(const AttendArgs& a) { return a.csa && a.k >= kLongKeys; }
 
+constexpr int64_t kCombineWideWgs = 256;  // combine workgroups from which 8 dims per lane are used
+
 hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (attend_long_lists(a)) {
     const int n_hg = (a.n_h + kHeadsLong - 1) / kHeadsLong;
@@ -1175,9 +1192,18 @@ hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hi
     launch_attend_mfma_kernel<true>(a, ws_o, ws_ml, n_hg, (int)mc, C, single * mc, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_h4 = (a.n_h + 3) / 4;
-    hipLaunchKernelGGL(attend_combine_mfma_kernel, dim3((unsigned)(a.S.total_q * n_h4)), dim3(256), 0, stream, a,
-                       ws_o, ws_ml, (int)mc, C);
+    // dims per lane: the widest split that still gives every compute unit a workgroup
+    // (which lanes fold which dims does not change the result)
+    const int64_t wg8 = a.S.total_q * ((a.n_h + 3) / 4);
+    if (wg8 >= kCombineWideWgs)
+      hipLaunchKernelGGL(attend_combine_mfma_kernel<8>, dim3((unsigned)wg8), dim3(256), 0, stream, a, ws_o, ws_ml,
+                         (int)mc);
+    else if (2 * wg8 >= kCombineWideWgs)
+      hipLaunchKernelGGL(attend_combine_mfma_kernel<4>, dim3((unsigned)(a.S.total_q * ((a.n_h + 1) / 2))), dim3(256),
+                         0, stream, a, ws_o, ws_ml, (int)mc);
+    else
+      hipLaunchKernelGGL(attend_combine_mfma_kernel<2>, dim3((unsigned)(a.S.total_q * a.n_h)), dim3(256), 0, stream,
+                         a, ws_o, ws_ml, (int)mc);
   } else {
     launch_attend_mfma_kernel<false>(a, nullptr, nullptr, n_hg, 1, C, single, stream);
   }

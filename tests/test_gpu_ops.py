@@ -417,6 +417,46 @@ def test_attend_split_and_single_modes_bit_identical(fmt, D, n_h):
         assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), (csa, ratio)
 
 
+def test_attend_combine_split_of_dims_keeps_bits():
+    """The combine step gives each lane 8, 4 or 2 dims of a head depending on how many
+    workgroups the batch fills; a token's outputs must not depend on it.  48 single-query
+    sequences (8 dims per lane) against their first 8 (4 dims) and first 2 (2 dims), and
+    against the single launch."""
+    g = np.random.default_rng(11)
+    n_seqs, n_h, D = 48, 64, 512
+    # contexts long enough for two or more chunks per token
+    for csa, ratio, k, lo, hi in ((True, 4, 512, 3000, 9000), (False, 128, 0, 80000, 200000)):
+        ctx = [int(v) for v in g.integers(lo, hi, size=n_seqs)]
+        data = _attend_inputs(g, ops.BF16, D, n_h, [1] * n_seqs, ctx, ratio, k, 128, tok_hist=140)
+        ob, sq, q_rows, _, kv_rows, _, tok_rows, _, sink_t, _, idx = data
+        idx_t = torch.from_numpy(idx).to(DEV)
+        op = ops.OP_CSA_ATTEND if csa else ops.OP_HCA_ATTEND
+
+        def run(m, use_ws):
+            sub = ops.Seqs(sq.n_q[:m], sq.ctx_len[:m], sq.entry_off[:m], sq.tok_off[:m], sq.tok_lo[:m], device=DEV)
+            ws = None
+            if use_ws:
+                ws = torch.empty(ops.csa_workspace_bytes(op, sub, n_h, D, k, ratio, 128) // 4 + 1,
+                                 dtype=torch.float32, device=DEV)
+            out = empty_rows(m * n_h, D, ops.BF16)
+            lse = torch.zeros((m, n_h), dtype=torch.float32, device=DEV)
+            if csa:
+                ops.csa_attend(sub, q_rows, n_h, kv_rows, idx_t, k, tok_rows, 128, sink_t, 0.05, 64, 10000.0, out,
+                               lse, ws=ws)
+            else:
+                ops.hca_attend(sub, q_rows, n_h, kv_rows, ratio, tok_rows, 128, sink_t, 0.05, 64, 10000.0, out, lse,
+                               ws=ws)
+            torch.cuda.synchronize()
+            return out.data.clone(), lse.clone()
+
+        full_o, full_l = run(n_seqs, True)
+        single_o, single_l = run(n_seqs, False)
+        assert torch.equal(full_o, single_o) and torch.equal(full_l, single_l), (csa, "split vs single")
+        for m in (8, 2):
+            o, l = run(m, True)
+            assert torch.equal(o, full_o[: m * n_h]) and torch.equal(l, full_l[:m]), (csa, m)
+
+
 def test_attend_edge_cases():
     """No visible entries (p < m-1), sink = -inf (plain softmax), no window with no entries
     (empty key set: output 0, lse -inf), idx with scattered -1."""

@@ -6,7 +6,8 @@
 // first digit spreads the few distinct float exponents of a score vector over many bins,
 // which keeps LDS-atomic contention low) finds the k-th largest key T and how many keys
 // equal to T are still needed (each digit found by a workgroup-wide scan of the digit
-// counts); a block-wide scan then keeps every key > T and the
+// counts; when the digit's bin is taken whole, the lower digits cannot change the set and
+// the remaining passes are skipped); a block-wide scan then keeps every key > T and the
 // lowest-index keys == T, writing indices in ascending order.  The selection is a
 // function of the token's scores alone.  Up to 32768 candidates the keys stay in
 // registers (8, 16 or 32 consecutive keys per thread), each pass has its own LDS histogram
@@ -65,7 +66,7 @@ constexpr int kHistBins = 4096;
 struct TopkLds {
   uint32_t hist[kHistBins];
   uint32_t red[32];
-  uint32_t digit, above;
+  uint32_t digit, above, count;
 };
 
 // Selection for key lists longer than the register path takes: every pass re-reads the
@@ -108,6 +109,7 @@ __device__ void topk_select_mem(const float* __restrict__ src, int n, int k, int
           if (ab + h >= remaining) {
             sh.digit = (uint32_t)(d_hi - 1 - d);
             sh.above = ab;
+            sh.count = h;
             break;
           }
           ab += h;
@@ -118,9 +120,17 @@ __device__ void topk_select_mem(const float* __restrict__ src, int n, int k, int
     prefix |= sh.digit << shift;
     mask |= dmask << shift;
     remaining -= sh.above;
+    const uint32_t count = sh.count;
     __syncthreads();
+    if (pass < 2 && count == remaining && prefix != 0u) {
+      // every key of the bin is taken: the set is the keys >= prefix, whatever the lower digits
+      prefix -= 1u;
+      remaining = 0u;
+      break;
+    }
   }
-  // prefix is the k-th largest key T; `remaining` keys equal to T are taken, lowest index first.
+  // Keys > T are taken, and the `remaining` lowest-index keys equal to T (T is the k-th
+  // largest key, or one below the lowest key of a bin taken whole, with remaining = 0).
   const uint32_t T = prefix;
   const int seg = (n + kTopkThreads - 1) / kTopkThreads;
   const int i0 = min(n, tid * seg), i1 = min(n, i0 + seg);
@@ -162,14 +172,14 @@ struct TopkRegLds {
   uint32_t hist1[4096];  // second digit (12 bits)
   uint32_t hist2[256];   // last digit (8 bits)
   uint32_t red[2][16];
-  uint32_t digit, above;
+  uint32_t digit, above, count;
 };
 
 // Find the digit holding the `remaining`-th largest key of a histogram of `nbins` digits
 // (4096 or 256): thread t owns nbins / 1024 (at least 1) consecutive digits counted from the
 // top; a wave scan plus the 16 wave totals give each thread the count above its digits.
-// Returns (digit, keys above it) to every thread.
-__device__ __forceinline__ uint2 topk_find_digit(const uint32_t* hist, int nbins, uint32_t remaining,
+// Returns (digit, keys above it, keys in it) to every thread.
+__device__ __forceinline__ uint3 topk_find_digit(const uint32_t* hist, int nbins, uint32_t remaining,
                                                  TopkRegLds& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int per = nbins >= kTopkThreads ? nbins / kTopkThreads : 1;
@@ -190,18 +200,19 @@ __device__ __forceinline__ uint2 topk_find_digit(const uint32_t* hist, int nbins
       if (ab + h >= remaining) {
         sh.digit = (uint32_t)(d_hi - 1 - d);
         sh.above = ab;
+        sh.count = h;
         break;
       }
       ab += h;
     }
   }
   __syncthreads();
-  return make_uint2(sh.digit, sh.above);
+  return make_uint3(sh.digit, sh.above, sh.count);
 }
 
 // Selection with the keys held in registers: thread tid holds the NPT consecutive keys
 // NPT tid .. NPT tid + NPT-1 (n <= 1024 NPT), loaded 16 bytes at a time when the row is
-// 16-byte aligned.  Three digit passes (12, 12, 8 bits) with one histogram each; then each
+// 16-byte aligned.  Up to three digit passes (12, 12, 8 bits) with one histogram each; then each
 // thread counts its keys > T and == T, one block scan gives its output offsets, and it
 // writes its kept indices in ascending order.
 // Thread tid's keys NPT tid .. NPT tid + NPT-1 of the row, those below `lim` (16 bytes at a
@@ -240,24 +251,39 @@ __device__ void topk_select_keys(const uint32_t (&key)[NPT], int n, int k, int32
   for (int j = 0; j < NPT; ++j)
     if (i0 + j < n) atomicAdd(&sh.hist0[key[j] >> 20], 1u);
   __syncthreads();
+  // Keys > T are taken, and the `remaining` lowest-index keys equal to T: T is the k-th
+  // largest key, or, once a digit's bin is taken whole (its count is what is still needed),
+  // one below the lowest key of that bin with remaining = 0, and the later passes are
+  // skipped (same set).
   uint32_t remaining = (uint32_t)k;
-  uint2 r = topk_find_digit(sh.hist0, 4096, remaining, sh);
+  uint32_t T;
+  uint3 r = topk_find_digit(sh.hist0, 4096, remaining, sh);
   const uint32_t d0 = r.x;
   remaining -= r.y;
+  if (r.z == remaining && d0 != 0u) {
+    T = (d0 << 20) - 1u;
+    remaining = 0u;
+  } else {
 #pragma unroll
-  for (int j = 0; j < NPT; ++j)
-    if (i0 + j < n && (key[j] >> 20) == d0) atomicAdd(&sh.hist1[(key[j] >> 8) & 0xfffu], 1u);
-  __syncthreads();
-  r = topk_find_digit(sh.hist1, 4096, remaining, sh);
-  const uint32_t p1 = (d0 << 12) | r.x;  // top 24 bits
-  remaining -= r.y;
+    for (int j = 0; j < NPT; ++j)
+      if (i0 + j < n && (key[j] >> 20) == d0) atomicAdd(&sh.hist1[(key[j] >> 8) & 0xfffu], 1u);
+    __syncthreads();
+    r = topk_find_digit(sh.hist1, 4096, remaining, sh);
+    const uint32_t p1 = (d0 << 12) | r.x;  // top 24 bits
+    remaining -= r.y;
+    if (r.z == remaining && p1 != 0u) {
+      T = (p1 << 8) - 1u;
+      remaining = 0u;
+    } else {
 #pragma unroll
-  for (int j = 0; j < NPT; ++j)
-    if (i0 + j < n && (key[j] >> 8) == p1) atomicAdd(&sh.hist2[key[j] & 0xffu], 1u);
-  __syncthreads();
-  r = topk_find_digit(sh.hist2, 256, remaining, sh);
-  const uint32_t T = (p1 << 8) | r.x;  // the k-th largest key
-  remaining -= r.y;                     // keys == T still to take, lowest index first
+      for (int j = 0; j < NPT; ++j)
+        if (i0 + j < n && (key[j] >> 8) == p1) atomicAdd(&sh.hist2[key[j] & 0xffu], 1u);
+      __syncthreads();
+      r = topk_find_digit(sh.hist2, 256, remaining, sh);
+      T = (p1 << 8) | r.x;  // the k-th largest key
+      remaining -= r.y;     // keys == T still to take, lowest index first
+    }
+  }
 
   uint32_t gt = 0, eq = 0;
 #pragma unroll

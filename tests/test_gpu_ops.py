@@ -280,6 +280,44 @@ def test_topk_exact_on_identical_scores(keep):
                 assert list(got[r]) == list(ref), f"token {r} (V={L}, k={k}, row stride {st.stride(0)})"
 
 
+@pytest.mark.parametrize("keep", ["all", "upto16384"])
+def test_topk_bin_taken_whole(keep):
+    """Rows built so that the bin of the k-th key holds exactly the keys still needed after
+    the first digit (12 bits) or after the second (24 bits), the cases where the selection
+    stops early, next to a row where the boundary falls inside a bin; with a 40000-key row
+    the streaming path runs, without it the register path."""
+    g = np.random.default_rng(23)
+    k, ratio = 512, 1
+    ctx_all = [3000, 3000, 3000, 16384, 40000]
+    ctx = [c for c in ctx_all if keep == "all" or c <= 16384]
+    ob, sq, _, _ = make_batch([1] * len(ctx), ctx, ratio)
+    stride = max(ctx)
+    s = np.full((len(ctx), stride), np.nan, dtype=np.float32)
+    for r, L in enumerate(ctx):
+        pos = g.permutation(L)
+        if r % 3 == 0:
+            # k keys in [4, 4.5) (one 12-bit bin: sign, exponent, 3 mantissa bits), the rest
+            # in [1, 1.125)
+            s[r, :L] = 1.0 + g.random(L) * 0.125
+            s[r, pos[:k]] = 4.0 + g.random(k) * 0.5
+        elif r % 3 == 1:
+            # 300 keys above 5, and 212 keys in one 24-bit bin of [4, 4.5) whose neighbours
+            # below (same 12-bit bin) are not taken
+            s[r, :L] = 4.0 + g.random(L) * 0.25
+            s[r, pos[:300]] = 5.0 + g.random(300)
+            s[r, pos[300:k]] = np.float32(4.375) + np.arange(k - 300, dtype=np.float32) * np.float32(2.0 ** -21)
+        else:
+            s[r, :L] = g.standard_normal(L).astype(np.float32)
+    st = torch.from_numpy(s).to(DEV)
+    idx = torch.full((len(ctx), k), -7, dtype=torch.int32, device=DEV)
+    ops.csa_topk(sq, st, ratio, k, idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for r, L in enumerate(ctx):
+        ref = topk_select(s[r, :L].astype(np.float64), k)
+        assert list(got[r]) == list(ref), f"row {r} (V={L})"
+
+
 # ----------------------------------------------------------------------------- attention
 
 

@@ -91,7 +91,7 @@ template <int RG, int CW>
 __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& c, const RowsDev& z,
                                                const float* __restrict__ bias, int ratio, int overlap,
                                                const RopeTab& rope, const RowsOut& out, int max_new, int blk, int cg) {
-  static_assert(CW % 64 == 0 && CW <= 256, "channel pairs per workgroup");
+  static_assert(CW % 16 == 0 && CW <= 256, "channel pairs per workgroup");
   const int b = blk / max_new;
   const int jn = blk % max_new;
   if (b >= S.n_seqs) return;
@@ -179,6 +179,9 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
       }
       break;
     case DT_KV_SPLIT: {
+      // a scale block needs a whole wavefront of pairs; narrower workgroups are launched
+      // for float32 / bf16 outputs only
+      if constexpr (CW % 64 != 0) break;
       const int dn = D - kSplitBf16Dims;
       const bool fp8 = active && 2 * pair < dn;
       float am = fp8 ? fmaxf(fabsf(acc.x), fabsf(acc.y)) : 0.f;
@@ -202,6 +205,7 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
       break;
     }
     default: {  // MXFP4: 16 lanes = 32 dims per block
+      if constexpr (CW % 64 != 0) break;
       float am = active ? fmaxf(fabsf(acc.x), fabsf(acc.y)) : 0.f;
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
@@ -239,10 +243,14 @@ __global__ void __launch_bounds__(CW * RG) compress2_kernel(SeqsDev S, CompressJ
 }
 
 // Sources per entry from which the pooling is split: 16 row groups (8 sources each for a
-// 128-token block, one batch of loads per thread) over 64 channel pairs per workgroup, so an
-// entry's channels spread over several workgroups.
+// 128-token block, one batch of loads per thread) over 64 channel pairs per workgroup, or
+// 16 when the outputs are float32 / bf16 (no scale block to keep within a wavefront), so an
+// entry's channels spread over several workgroups.  The pairs per workgroup do not enter a
+// channel's arithmetic.
 constexpr int kSplitSources = 64;
-constexpr int kSplitGroups = 16, kSplitPairs = 64;
+constexpr int kSplitGroups = 16, kSplitPairs = 64, kSplitPairsPlain = 16;
+
+__host__ __device__ inline bool plain_out(const RowsOut& o) { return o.dtype == DT_F32 || o.dtype == DT_BF16; }
 
 hipError_t launch_compress(const SeqsDev& S, const RowsDev& c, const RowsDev& z, const float* bias, int ratio,
                            int overlap, const RopeTab& rope, const RowsOut& out, int max_q, hipStream_t stream) {
@@ -250,7 +258,11 @@ hipError_t launch_compress(const SeqsDev& S, const RowsDev& c, const RowsDev& z,
   const int64_t blocks = (int64_t)S.n_seqs * max_new;
   if (blocks == 0) return hipSuccess;
   const CompressJob j0{c, z, bias, rope, out};
-  if (ratio * (1 + overlap) >= kSplitSources) {
+  if (ratio * (1 + overlap) >= kSplitSources && plain_out(out)) {
+    const int n_cg = (c.dim / 2 + kSplitPairsPlain - 1) / kSplitPairsPlain;
+    hipLaunchKernelGGL((compress_kernel<kSplitGroups, kSplitPairsPlain>), dim3((unsigned)(blocks * n_cg)),
+                       dim3(kSplitGroups * kSplitPairsPlain), 0, stream, S, j0, ratio, overlap, max_new, n_cg);
+  } else if (ratio * (1 + overlap) >= kSplitSources) {
     const int n_cg = (c.dim / 2 + kSplitPairs - 1) / kSplitPairs;
     hipLaunchKernelGGL((compress_kernel<kSplitGroups, kSplitPairs>), dim3((unsigned)(blocks * n_cg)),
                        dim3(kSplitGroups * kSplitPairs), 0, stream, S, j0, ratio, overlap, max_new, n_cg);
@@ -269,7 +281,11 @@ hipError_t launch_compress2(const SeqsDev& S, const RowsDev& c0, const RowsDev& 
   const int64_t blocks = (int64_t)S.n_seqs * max_new;
   if (blocks == 0) return hipSuccess;
   const CompressJob j0{c0, z0, bias0, rope0, out0}, j1{c1, z1, bias1, rope1, out1};
-  if (ratio * (1 + overlap) >= kSplitSources) {
+  if (ratio * (1 + overlap) >= kSplitSources && plain_out(out0) && plain_out(out1)) {
+    const int n_cg = (max(c0.dim, c1.dim) / 2 + kSplitPairsPlain - 1) / kSplitPairsPlain;
+    hipLaunchKernelGGL((compress2_kernel<kSplitGroups, kSplitPairsPlain>), dim3((unsigned)(2 * blocks * n_cg)),
+                       dim3(kSplitGroups * kSplitPairsPlain), 0, stream, S, j0, j1, ratio, overlap, max_new, n_cg);
+  } else if (ratio * (1 + overlap) >= kSplitSources) {
     const int n_cg = (max(c0.dim, c1.dim) / 2 + kSplitPairs - 1) / kSplitPairs;
     hipLaunchKernelGGL((compress2_kernel<kSplitGroups, kSplitPairs>), dim3((unsigned)(2 * blocks * n_cg)),
                        dim3(kSplitGroups * kSplitPairs), 0, stream, S, j0, j1, ratio, overlap, max_new, n_cg);

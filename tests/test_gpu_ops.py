@@ -56,6 +56,10 @@ COMPRESS_CASES = [
     (ops.BF16, ops.BF16, ops.KV_SPLIT, 512, 128, 0, 64),
     (ops.BF16, ops.BF16, ops.MXFP4, 128, 128, 0, 0),
     (ops.F32, ops.F32, ops.F32, 160, 32, 1, 32),
+    # float32 / bf16 outputs take 16 channel pairs (32 dims) per workgroup: three groups,
+    # and the narrowest row (one group)
+    (ops.BF16, ops.BF16, ops.BF16, 96, 128, 0, 0),
+    (ops.F32, ops.F32, ops.F32, 32, 64, 0, 0),
 ]
 
 

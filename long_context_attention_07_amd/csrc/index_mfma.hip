@@ -43,20 +43,14 @@ __device__ __forceinline__ void wait_tiles_in_flight(int n) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Entries [part * 64 TILES, (part + 1) * 64 TILES) of token t (position ctx.p, pool row of
+// entry 0 ctx.entry0), by the whole workgroup.
 template <int RING, int TILES>
-__global__ void __launch_bounds__(256) index_score_mfma_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
-                                                               int n_I, RowsDev kI, int ratio,
-                                                               float* __restrict__ score, int64_t score_stride,
-                                                               int n_parts, int n_logical) {
+__device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], int t, const TokenCtx& ctx, int part,
+                                            const RowsDev& qI, const float* __restrict__ w, int n_I,
+                                            const RowsDev& kI, int ratio, float* __restrict__ score,
+                                            int64_t score_stride) {
   static_assert(RING >= 2 && RING <= 4, "ring depth");
-  __shared__ __align__(16) uint8_t ring[RING][kIT * kIRow];
-  // Plain dispatch order: consecutive ranges of a token go to different XCDs, so unequal
-  // context lengths spread over the whole chip.
-  const int lid = blockIdx.x;
-  if (lid >= n_logical) return;
-  const int t = lid / n_parts;
-  const int part = lid % n_parts;
-  const TokenCtx ctx = token_ctx(S, t);
   const int64_t V = (ctx.p + 1) / ratio;
   const int64_t e_begin = (int64_t)part * kIT * TILES;
   if (e_begin >= V) return;
@@ -164,6 +158,89 @@ __global__ void __launch_bounds__(256) index_score_mfma_kernel(SeqsDev S, RowsDe
   }
 }
 
+// Workgroup = (token, range) in plain dispatch order: consecutive ranges of a token go to
+// different XCDs, so unequal context lengths spread over the whole chip; ranges past a
+// token's visible entries exit at once.
+template <int RING, int TILES>
+__global__ void __launch_bounds__(256) index_score_mfma_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
+                                                               int n_I, RowsDev kI, int ratio,
+                                                               float* __restrict__ score, int64_t score_stride,
+                                                               int n_parts, int n_logical) {
+  __shared__ __align__(16) uint8_t ring[RING][kIT * kIRow];
+  const int lid = blockIdx.x;
+  if (lid >= n_logical) return;
+  const int t = lid / n_parts;
+  const int part = lid % n_parts;
+  const TokenCtx ctx = token_ctx(S, t);
+  score_range<RING, TILES>(ring, t, ctx, lid % n_parts, qI, w, n_I, kI, ratio, score, score_stride);
+}
+
+// Few sequences and query rows (decode): the (token, range) units with entries to score
+// are numbered densely, unit u = the u-th range in token order, and workgroup u takes unit
+// u (the grid is the padded count; workgroups past the last unit exit), so the busy
+// workgroups are the first dispatched and spread evenly over the compute units instead of
+// following the padded (token, range) grid.  Every wave derives the numbering from one
+// round of loads (lane l = sequence l); a unit's scores are computed exactly as in the
+// kernel above.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+template <int RING, int TILES>
+__global__ void __launch_bounds__(256) index_score_mfma_units_kernel(SeqsDev S, RowsDev qI,
+                                                                     const float* __restrict__ w, int n_I,
+                                                                     RowsDev kI, int ratio, float* __restrict__ score,
+                                                                     int64_t score_stride) {
+  __shared__ __align__(16) uint8_t ring[RING][kIT * kIRow];
+  constexpr int64_t kPer = (int64_t)kIT * TILES;
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < S.n_seqs;
+  const int q0 = in ? S.q_off[lane] : 0;
+  const int q1 = in ? S.q_off[lane + 1] : 0;
+  const int len = in ? S.ctx_len[lane] : 0;
+  const int64_t e0 = in ? S.entry_off[lane] : 0;
+  int units = 0;
+  for (int j = 0; j < q1 - q0; ++j) {
+    const int64_t V = ((int64_t)len - (q1 - q0) + j + 1) / ratio;
+    units += (int)((V + kPer - 1) / kPer);
+  }
+  const int incl = wave_incl_sum(units);
+  const int excl = incl - units;
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  const int u = blockIdx.x;
+  if (u >= total) return;
+  {
+    // the last sequence whose first unit is <= u, then its token holding unit u
+    const int b = __popcll(__ballot(in && excl <= u)) - 1;
+    const int bq0 = __builtin_amdgcn_readlane(q0, b), bn = __builtin_amdgcn_readlane(q1, b) - bq0;
+    const int blen = __builtin_amdgcn_readlane(len, b);
+    int rem = u - __builtin_amdgcn_readlane(excl, b);
+    int j = 0;
+    for (; j < bn - 1; ++j) {
+      const int64_t V = ((int64_t)blen - bn + j + 1) / ratio;
+      const int uj = (int)((V + kPer - 1) / kPer);
+      if (rem < uj) break;
+      rem -= uj;
+    }
+    TokenCtx ctx;
+    ctx.b = b;
+    ctx.q_end = bq0 + bn;
+    ctx.p = (int64_t)blen - bn + j;
+    ctx.entry0 = readlane64(e0, b);
+    ctx.tok0 = 0;
+    ctx.tok_lo = 0;
+    score_range<RING, TILES>(ring, bq0 + j, ctx, rem, qI, w, n_I, kI, ratio, score, score_stride);
+  }
+}
+
+constexpr int kUnitsMaxRows = 64;  // query rows up to which the dense unit numbering is used
+
 bool index_mfma_supported(const RowsDev& qI, const RowsDev& kI, int n_I, int64_t score_stride) {
   (void)score_stride;
   return qI.dtype == DT_BF16 && kI.dtype == DT_BF16 && kI.dim == 128 && n_I <= 64 && qI.stride % 16 == 0 &&
@@ -172,11 +249,16 @@ bool index_mfma_supported(const RowsDev& qI, const RowsDev& kI, int n_I, int64_t
 
 hipError_t launch_index_score_mfma(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
                                    int ratio, float* score, int64_t score_stride, int max_vis, hipStream_t stream) {
-  constexpr int kRing = 3, kTiles = 6;  // 48 KiB of LDS (3 workgroups per CU), 384 entries each
+  constexpr int kRing = 3, kTiles = 7;  // 48 KiB of LDS (3 workgroups per CU), 448 entries each
   const int per_wg = kIT * kTiles;
   const int n_parts = (max_vis + per_wg - 1) / per_wg;
   const int64_t n_log = (int64_t)S.total_q * n_parts;
   if (n_log == 0) return hipSuccess;
+  if (S.n_seqs <= 64 && S.total_q <= kUnitsMaxRows) {
+    hipLaunchKernelGGL((index_score_mfma_units_kernel<kRing, kTiles>), dim3((unsigned)n_log), dim3(256), 0, stream, S,
+                       qI, w, n_I, kI, ratio, score, score_stride);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((index_score_mfma_kernel<kRing, kTiles>), dim3((unsigned)n_log), dim3(256), 0, stream, S, qI, w,
                      n_I, kI, ratio, score, score_stride, n_parts, (int)n_log);
   return hipGetLastError();

@@ -43,7 +43,7 @@ FP8_PEAK_TFLOPS = 5033.2    # dense fp8 MFMA
 FP4_PEAK_TFLOPS = 10100.0   # dense MXFP4 (scaled fp4) MFMA
 N_SETS = 8
 # kernels each operation launches (substrings of the kernel names in profiler output)
-OP_KERNELS = {"compress": ["compress2_kernel", "compress_kernel"], "index_score": ["index_score_mfma_kernel"],
+OP_KERNELS = {"compress": ["compress2_kernel", "compress_kernel"], "index_score": ["index_score_mfma_kernel", "index_score_mfma_units_kernel"],
               "topk": ["topk_kernel", "topk_decode_kernel"],
               "attend": ["attend_pair_kernel", "attend_combine_mfma_kernel"]}
 PREFILL_KERNELS = {"compress": ["compress2_kernel"], "index_score": ["index_score_mx_block_kernel"],

@@ -169,12 +169,17 @@ int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int
  *   idx   device int32 [total_q, k];  sink device float32 [n_h] (may be -inf)
  *   out   rows [total_q * n_h, D] (F32 or BF16);  lse device float32 [total_q, n_h] or NULL
  *   n_h 1..128;  n_win 0..1024;  k 1..4096
- *   ws/ws_bytes  optional scratch.  With at least csa_workspace_bytes(CSA_OP_CSA_ATTEND, ...)
- *         bytes the key list of each token is processed by several workgroups in parallel;
- *         with less (or NULL) by one workgroup per token and head group.  Both give
- *         bit-identical results: each token's key list is cut into fixed chunks whose
- *         partial softmax states are folded in chunk order, starting from the sink.  The
- *         workspace needs no initialisation; calls sharing one must be stream-ordered. */
+ *   ws/ws_bytes  optional scratch.  csa_workspace_bytes(CSA_OP_CSA_ATTEND, ...) is what the
+ *         call can use: nonzero only when a token's key list has more than one chunk and
+ *         the batch is small (fewer than 512 workgroups of one token and 16 heads for
+ *         512-dim rows, fewer than 1024 of one token and 8 heads otherwise); never for CSA
+ *         with k >= 1024 over 512-dim rows, whose lists run whole on one 64-head workgroup
+ *         per token.  With at least that many bytes the chunks of a list run on separate
+ *         workgroups and a second kernel folds them; with less (or NULL) one workgroup
+ *         walks all chunks of its token.  Both give bit-identical results: each token's
+ *         key list is cut into fixed chunks whose partial softmax states are folded in
+ *         chunk order, starting from the sink.  The workspace needs no initialisation;
+ *         calls sharing one must be stream-ordered. */
 int csa_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows* kv, const int32_t* idx, int k,
                const csa_rows* tok, int n_win, const float* sink, float scale, int rope_dims, double rope_theta,
                const csa_rows* out, float* lse, void* ws, size_t ws_bytes, void* stream);
@@ -190,7 +195,10 @@ int hca_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows*
 /* Workspace sizing (host only; reads only the host scalars of `seqs`). */
 enum { CSA_OP_INDEX_TOPK = 1, CSA_OP_CSA_ATTEND = 2, CSA_OP_HCA_ATTEND = 3 };
 /* op CSA_OP_INDEX_TOPK: ratio, k used; CSA_OP_CSA_ATTEND: n_h, dim, k, n_win used;
- * CSA_OP_HCA_ATTEND: n_h, dim, ratio, n_win used.  Returns 0 for an invalid op. */
+ * CSA_OP_HCA_ATTEND: n_h, dim, ratio, n_win used.  Returns the bytes the call uses: for
+ * CSA_OP_INDEX_TOPK total_q * floor(max_ctx/ratio) float32 scores (mandatory); for the
+ * attention ops the chunk partials when the call would split its key lists (see
+ * csa_attend), else 0.  Returns 0 for an invalid op. */
 size_t csa_workspace_bytes(int op, const csa_seqs* seqs, int n_h, int dim, int k, int ratio, int n_win);
 
 const char* csa_strerror(int status);

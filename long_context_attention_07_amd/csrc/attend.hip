@@ -189,12 +189,29 @@ int64_t attend_max_chunks(const AttendArgs& a) {
   return (n_ent + a.n_win + C - 1) / C;
 }
 
-size_t attend_workspace_bytes(const AttendArgs& a) {
+// Whether a call cuts its key lists over several workgroups (the combine kernel then folds
+// the chunk partials): only when a list has more than one chunk, the kernel family works
+// chunk by chunk (the 64-head long-list kernel for CSA with k >= 1024 over 512-dim rows
+// walks whole lists), and the batch is too small to fill the chip with one workgroup per
+// token and head group.  Depends on host scalars only, never on the row format, so the
+// workspace query and the launch agree.
+bool attend_split_wanted(const AttendArgs& a) {
+  if (attend_max_chunks(a) <= 1) return false;
+  if (a.q.dim == kMfmaHeadDim) {
+    if (a.csa && a.k >= kLongListKeys) return false;
+    return (int64_t)a.S.total_q * ((a.n_h + 15) / 16) < 512;
+  }
+  return (int64_t)a.S.total_q * ((a.n_h + kValuHG - 1) / kValuHG) < 1024;
+}
+
+size_t attend_partials_bytes(const AttendArgs& a) {
   const int64_t mc = attend_max_chunks(a);
   // chunk partials (o, then m and l) and a 16-byte record per token (position, chunk count)
   return (size_t)a.S.total_q * (size_t)mc * (size_t)a.n_h * ((size_t)a.q.dim + 2) * sizeof(float) +
          (size_t)a.S.total_q * 16;
 }
+
+size_t attend_workspace_bytes(const AttendArgs& a) { return attend_split_wanted(a) ? attend_partials_bytes(a) : 0; }
 
 bool attend_mfma_supported(const AttendArgs& a);
 hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -207,7 +224,7 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStre
   const int64_t mc = attend_max_chunks(a);
   const size_t need = attend_workspace_bytes(a);
   const int64_t single_blocks = (int64_t)a.S.total_q * n_hg;
-  const bool split = ws != nullptr && ws_bytes >= need && mc > 1 && single_blocks < 1024;
+  const bool split = need > 0 && ws != nullptr && ws_bytes >= need;
   if (split) {
     float* ws_o = reinterpret_cast<float*>(ws);
     float* ws_ml = ws_o + (size_t)a.S.total_q * mc * a.n_h * a.q.dim;

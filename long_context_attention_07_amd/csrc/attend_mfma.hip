@@ -717,7 +717,7 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
 // tile after next.  Such lists are one chunk (the chunk length rule), so the fold from the
 // sink takes the one chunk state at the end.
 constexpr int kHeadsLong = 64;       // heads per workgroup in this kernel
-constexpr int kLongKeys = 1024;      // CSA key lists from this length use this kernel
+constexpr int kLongKeys = kLongListKeys;  // CSA key lists from this length use this kernel
 constexpr int kSplitRowBytes = (kDM - kSplitBf16Dims) + 2 * kSplitBf16Dims;  // 576
 
 struct __align__(16) LongLds {
@@ -1185,7 +1185,7 @@ hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hi
   const int64_t mc = attend_max_chunks(a);
   const size_t need = attend_workspace_bytes(a);
   const int64_t single = (int64_t)a.S.total_q * n_hg;
-  const bool split = ws != nullptr && ws_bytes >= need && mc > 1 && single < 512;
+  const bool split = need > 0 && ws != nullptr && ws_bytes >= need;
   if (split) {
     float* ws_o = reinterpret_cast<float*>(ws);
     float* ws_ml = ws_o + (size_t)a.S.total_q * mc * a.n_h * kDM;

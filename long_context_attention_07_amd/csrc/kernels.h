@@ -48,7 +48,15 @@ struct AttendArgs {
 int attend_chunk_slots(const AttendArgs& a);
 // Number of chunks of the longest key list the launch can see (grid / workspace sizing).
 int64_t attend_max_chunks(const AttendArgs& a);
-// Workspace: the chunk partials, o of every (token, chunk, head) then its (m, l), float32.
+constexpr int kMfmaHeadDim = 512;    // head dim of the matrix-core attention kernels
+constexpr int kLongListKeys = 1024;  // CSA key lists from this k run whole on the 64-head kernel
+
+// Whether the call splits key lists over workgroups (host scalars only).
+bool attend_split_wanted(const AttendArgs& a);
+// Size of the chunk partials: o of every (token, chunk, head) then its (m, l), float32,
+// and a 16-byte record per token.
+size_t attend_partials_bytes(const AttendArgs& a);
+// Workspace the call uses: the chunk partials when it splits, else 0.
 size_t attend_workspace_bytes(const AttendArgs& a);
 hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
 

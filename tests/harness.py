@@ -4,11 +4,14 @@ same bytes decoded to float64 for the oracle, and the comparison rules.
 Comparison rules (readings of the tolerance statement for this path):
 * floating-point outputs: per element |gpu - oracle| <= tol * max(1, |oracle|), with
   tol = 1e-5 for float32 inputs and 1e-2 for bf16 / fp8 / MXFP4 inputs;
-* top-k index sets: exact, except that entries whose oracle score lies within a band of
-  the k-th score may be exchanged.  The band is max(1e-6 * max(1, |tau|), E), where E
-  bounds the float32 rounding of the kernel's score (dims and heads summed in float32
-  from inputs exactly representable in float32): a decision that float32 rounding can
-  flip is a tie at the kernel's precision;
+* quantised outputs (entries written in bf16, fp8 1x128 or MXFP4): compared in the code
+  domain.  Scales: fp32 block scales within 1e-6 relative, e8m0 exponents equal (or the
+  neighbouring exponent when the block's amax lies within 1e-6 of a power of two).
+  Codes: equal to the oracle's rounding of its exact value, or the adjacent code when
+  the exact value lies within 1e-6 of a rounding boundary, 1e-6 being relative to the
+  block's largest magnitude (the quantity that sets the block's scale);
+* top-k index sets: exact, except that entries whose oracle score lies within
+  1e-6 * max(1, |tau|) of the oracle's k-th score tau may be exchanged;
 * top-k on identical float32 scores: exact (both sides decide in float32 values).
 """
 
@@ -141,10 +144,11 @@ def score_error_bound(qI, w, kI, extra_rel=0.0):
     return (gamma + extra_rel) * (a @ np.abs(w)) + 1e-30
 
 
-def check_topk(gpu_idx, ref_idx, scores, k, band):
+def check_topk(gpu_idx, ref_idx, scores, k, rel=1e-6):
     """Tie-aware comparison of one token's selection (ascending, -1 padded).  `scores` are
-    the oracle's float64 scores of the token's visible entries, `band` a per-entry bound
-    on the kernel's score error."""
+    the oracle's float64 scores of the token's visible entries; an entry of one set that
+    is missing from the other must score within rel * max(1, |tau|) of the oracle's k-th
+    score tau.  Returns the number of exchanged pairs."""
     g = [int(i) for i in gpu_idx if i >= 0]
     r = [int(i) for i in ref_idx if i >= 0]
     assert g == sorted(g), "selection not ascending"
@@ -154,10 +158,124 @@ def check_topk(gpu_idx, ref_idx, scores, k, band):
     if g == r:
         return 0
     order = np.lexsort((np.arange(len(scores)), -scores))
-    kth = order[k - 1]
-    tau = scores[kth]
+    tau = scores[order[k - 1]]
+    width = rel * max(1.0, abs(tau))
     for i in set(g) ^ set(r):
-        width = max(1e-6 * max(1.0, abs(tau)), band[i] + band[kth])
         assert 0 <= i < len(scores) and abs(scores[i] - tau) <= width, \
             f"entry {i} (score {scores[i]!r}) exchanged outside the tie band {width:.3e} around {tau!r}"
     return len(set(g) ^ set(r)) // 2
+
+
+# ----------------------------------------------------------------------------- quantised outputs
+
+
+def _codes_allowed(rnd, v, delta, got):
+    """Monotone rounding `rnd`: the codes any value in [v - delta, v + delta] rounds to
+    form the range [rnd(v - delta), rnd(v + delta)]; `got` must lie in it."""
+    lo, hi = rnd(v - delta), rnd(v + delta)
+    return (got >= lo) & (got <= hi)
+
+
+def _raw(rows, n):
+    d = rows.data[:n] if n is not None else rows.data
+    sc = None
+    if rows.scales is not None:
+        sc = (rows.scales[:n] if n is not None else rows.scales).cpu().numpy()
+    return d, sc
+
+
+def check_codes(gpu_rows, ref, n=None, rel=1e-6, what="entries"):
+    """Code-domain comparison of quantised rows written by the GPU with the oracle's exact
+    float64 rows `ref` (the rule in the module docstring).  Returns the number of codes
+    that took the neighbouring value next to a rounding boundary."""
+    ref = np.asarray(ref, dtype=np.float64)
+    d, sc = _raw(gpu_rows, n)
+    flips = 0
+
+    def bf16_part(bits, x):
+        g = F.decode_bf16(bits)
+        amax = np.max(np.abs(x), axis=-1, keepdims=True)
+        ok = _codes_allowed(F.bf16_round, x, rel * amax, g)
+        assert np.all(ok), f"{what}: {int((~ok).sum())} bf16 values off the allowed codes"
+        return int(np.sum(g != F.bf16_round(x)))
+
+    if gpu_rows.dtype == ops.BF16:
+        bits = d.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return bf16_part(bits, ref)
+    if gpu_rows.dtype == ops.KV_SPLIT:
+        raw = d.cpu().numpy()
+        dn = gpu_rows.dim - 64
+        scg = sc.astype(np.float64)
+        for b, (lo, hi) in enumerate(F.kv_split_blocks(dn)):
+            x = ref[:, lo:hi]
+            amax = np.max(np.abs(x), axis=1)
+            s_ref = (amax / F.E4M3_MAX).astype(np.float32).astype(np.float64)
+            assert np.all(np.abs(scg[:, b] - s_ref) <= rel * s_ref), f"{what}: fp32 block scale {b} off"
+            s = np.where(s_ref > 0, s_ref, 1.0)[:, None]
+            v = np.where(s_ref[:, None] > 0, x / s, 0.0)
+            g = F.decode_e4m3fn(raw[:, lo:hi])
+            ok = _codes_allowed(F.e4m3fn_round, v, rel * F.E4M3_MAX, g)
+            assert np.all(ok), f"{what}: {int((~ok).sum())} fp8 codes of block {b} off the allowed codes"
+            flips += int(np.sum(g != F.e4m3fn_round(v)))
+        bits = raw[:, dn:].copy().view(np.uint16)
+        return flips + bf16_part(bits, ref[:, dn:])
+    if gpu_rows.dtype == ops.MXFP4:
+        D = gpu_rows.dim
+        m = ref.shape[0]
+        blk = ref.reshape(m, D // 32, 32)
+        amax = np.max(np.abs(blk), axis=-1)
+
+        def expo(a):
+            _, E = np.frexp(np.where(a > 0, a, 1.0))
+            return np.clip(np.where(a > 0, E - 1 - 2, -127), -127, 127)
+
+        eg = sc.astype(np.int64) - 127
+        ok = (eg >= expo(amax * (1 - rel))) & (eg <= expo(amax * (1 + rel)))
+        assert np.all(ok), f"{what}: {int((~ok).sum())} e8m0 exponents off"
+        flips += int(np.sum(eg != expo(amax)))
+        unit = np.ldexp(1.0, eg)[..., None]
+        v = blk / unit
+        g = F.decode_e2m1(F.unpack_e2m1(d.cpu().numpy())).reshape(m, D // 32, 32)
+        ok = _codes_allowed(F.e2m1_round, v, rel * amax[..., None] / unit, g)
+        assert np.all(ok), f"{what}: {int((~ok).sum())} e2m1 codes off the allowed codes"
+        return flips + int(np.sum(g != F.e2m1_round(v)))
+    raise ValueError("check_codes takes BF16, KV_SPLIT or MXFP4 rows")
+
+
+# ----------------------------------------------------------------------------- device-drawn inputs
+
+
+def device_outlier_normal(gen, shape, device, std=1.0, p=0.001, magnitude=20.0):
+    """float32 N(0, std^2) drawn with the torch generator `gen` on `device`, plus a
+    Bernoulli(p) mask of +-magnitude values of random sign (the outlier recipe of the
+    mixed-precision prefill inputs).  Draw order: values, mask, signs."""
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    m = torch.rand(shape, generator=gen, device=device) < p
+    sgn = torch.where(torch.rand(shape, generator=gen, device=device) < 0.5, -magnitude, magnitude)
+    return torch.where(m, x + sgn, x)
+
+
+def mxfp4_encode_torch(x):
+    """float32 rows [n, d] (any torch device) -> (packed e2m1 uint8 [n, d/2], e8m0 uint8
+    [n, d/32]) by the OCP MXFP4 recipe the oracle's quant_mxfp4 states: per 32 values
+    E = floor(log2 amax) - 2 (frexp, exact), clamped to [-127, 127], amax = 0 -> -127;
+    element = e2m1 round-to-nearest-even of x / 2^E saturating at +-6, sign kept for -0;
+    element 2i in the low nibble.  Input generation for large tensors that are drawn on the
+    device (pinned against the oracle's encoder in a CPU test)."""
+    n, d = x.shape
+    xb = x.reshape(n, d // 32, 32)
+    amax = xb.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)
+    E = torch.where(amax > 0, ex.to(torch.int32) - 1 - 2, torch.full_like(ex, -127, dtype=torch.int32))
+    E = E.clamp(-127, 127)
+    y = xb * torch.ldexp(torch.ones_like(amax), -E)[:, :, None]
+    mag = y.abs().clamp(max=6.0)
+    step = torch.where(mag < 2.0, 0.5, torch.where(mag < 4.0, 1.0, 2.0))
+    r = torch.round(mag / step) * step  # round half to even on the grid step
+    code = torch.where(r < 2.0, r * 2.0, torch.where(r < 4.0, r + 2.0, r * 0.5 + 4.0)).to(torch.uint8)
+    code = code | torch.where(torch.signbit(y), 8, 0).to(torch.uint8)
+    code = code.reshape(n, d)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+    return packed, (E + 127).to(torch.uint8).contiguous()

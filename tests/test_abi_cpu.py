@@ -127,3 +127,34 @@ def test_workspace_sizes(lib):
     # 4 tokens x 15 chunks (8192 entries + 128 window slots in 576-slot chunks) x 64 heads x
     # (512 dims + m, l) floats, plus a 16-byte record per token
     assert hca == 4 * 15 * 64 * 514 * 4 + 4 * 16
+
+
+def test_workspace_sizes_follow_the_launch(lib):
+    """The attention workspace is exactly what the call would use: the chunk partials when
+    key lists are cut over several workgroups, 0 when they are not (one chunk per list,
+    the whole-list kernel for CSA with k >= 1024 over 512-dim rows, or a batch that fills
+    the chip with one workgroup per token and head group)."""
+    P = ctypes.byref
+    ws = lambda s, op, n_h, d, k, r, w: lib.csa_workspace_bytes(op, P(s), n_h, d, k, r, w)  # noqa: E731
+    c2 = _seqs(n_seqs=32, total_q=32, max_q=1, max_ctx=65536)
+    # k = 512, window 128: 640 slots in two 320-slot chunks
+    assert ws(c2, ops.OP_CSA_ATTEND, 64, 512, 512, 4, 128) == 32 * 2 * 64 * 514 * 4 + 32 * 16
+    # k >= 1024: whole lists on the 64-head kernel, no workspace (prefill and decode alike)
+    c4 = _seqs(n_seqs=1, total_q=131072, max_q=131072, max_ctx=131072)
+    assert ws(c4, ops.OP_CSA_ATTEND, 64, 512, 1024, 4, 128) == 0
+    assert ws(c2, ops.OP_CSA_ATTEND, 64, 512, 1024, 4, 128) == 0
+    # one chunk per list: k + window <= 384 slots
+    assert ws(c2, ops.OP_CSA_ATTEND, 64, 512, 64, 4, 128) == 0
+    # large batches run one workgroup per (token, 16 heads): 128 tokens x 4 groups = 512
+    big = _seqs(n_seqs=128, total_q=128, max_q=1, max_ctx=65536)
+    assert ws(big, ops.OP_CSA_ATTEND, 64, 512, 512, 4, 128) == 0
+    small = _seqs(n_seqs=127, total_q=127, max_q=1, max_ctx=65536)
+    assert ws(small, ops.OP_CSA_ATTEND, 64, 512, 512, 4, 128) > 0
+    # other head dims (float32 kernel): 8 heads per workgroup, up to 1023 workgroups
+    f = _seqs(n_seqs=1, total_q=1023, max_q=1023, max_ctx=4096)
+    assert ws(f, ops.OP_CSA_ATTEND, 8, 128, 512, 4, 128) == 1023 * 2 * 8 * 130 * 4 + 1023 * 16
+    f = _seqs(n_seqs=1, total_q=1024, max_q=1024, max_ctx=4096)
+    assert ws(f, ops.OP_CSA_ATTEND, 8, 128, 512, 4, 128) == 0
+    # HCA: the chunk count follows the longest context
+    h = _seqs(n_seqs=4, total_q=4, max_q=1, max_ctx=1000)
+    assert ws(h, ops.OP_HCA_ATTEND, 64, 512, 0, 128, 128) == 0   # 7 entries + 128 window: one chunk

@@ -152,6 +152,20 @@ int csa_topk(const csa_seqs* seqs, const float* score, int64_t score_stride, int
 int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
                    int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
+/* csa_index_topk_noalloc -- csa_index_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and the same idx bits, with the scores kept in a fixed scratch
+ * array of the library instead of a caller workspace.  Allocates and frees nothing.
+ *   Limit: total_q * floor(max_ctx/ratio) * 4 bytes must not exceed 64 MiB (e.g. 64 query
+ *   tokens at 1M context with ratio 4); larger calls return CSA_EWORKSPACE unlaunched.
+ *   The scratch belongs to the calling thread's current device (one 64 MiB array per GPU,
+ *   held until the process ends); `stream` must belong to that device.  Every call on a
+ *   GPU shares that GPU's array: calls that overlap on one GPU (different streams or
+ *   threads without ordering) race and give undefined results; calls on one stream are
+ *   ordered and safe.  No part of the array needs clearing between calls. */
+int csa_index_topk_noalloc(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI,
+                           int ratio, int k, int32_t* idx, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * csa_attend -- sparse shared-KV MQA over the selected entries plus the sliding window
  * (section 2.1 CSA, "滑动窗口分支"; Figure 2 "Top-k Sparse Attention" with the window

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "csa.h"
 #include "kernels.h"
@@ -177,6 +178,48 @@ int attend_common(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_ro
   return CSA_OK;
 }
 
+// Scratch of csa_index_topk_noalloc: a fixed device array instead of a caller workspace.
+// Each GPU the library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: kernels get the address
+// hipGetSymbolAddress returns for the current device (kept per device below).
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CSA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(CSA_EUNSUPPORTED, "device ordinal %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(CSA_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return CSA_OK;
+}
+
+// Index scores into `score` (float32 [total_q, stride]) then the selection; arguments
+// already validated.
+int index_topk_launch(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
+                      int k, int32_t* idx, float* score, hipStream_t s) {
+  const int max_vis = seqs->max_ctx / ratio;
+  const int64_t stride = max_vis > 0 ? max_vis : 1;
+  hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio, score, stride,
+                                         max_vis, seqs->max_q, s);
+  if (e != hipSuccess) return hip_status(e, "index_topk score launch");
+  e = csa::launch_topk(dev_seqs(seqs), score, stride, ratio, k, idx, max_vis, seqs->max_q, s);
+  return hip_status(e, "index_topk select launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -294,15 +337,27 @@ int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int
   if (need && (!ws || ws_bytes < need))
     return fail(CSA_EWORKSPACE, "csa_index_topk needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
   if (seqs->total_q == 0) return ok();
-  const int max_vis = seqs->max_ctx / ratio;
-  const int64_t stride = max_vis > 0 ? max_vis : 1;
-  float* score = static_cast<float*>(ws);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio, score, stride,
-                                         max_vis, seqs->max_q, s);
-  if (e != hipSuccess) return hip_status(e, "csa_index_topk score launch");
-  e = csa::launch_topk(dev_seqs(seqs), score, stride, ratio, k, idx, max_vis, seqs->max_q, s);
-  return hip_status(e, "csa_index_topk select launch");
+  return index_topk_launch(seqs, qI, w, n_I, kI, ratio, k, idx, static_cast<float*>(ws),
+                           static_cast<hipStream_t>(stream));
+}
+
+int csa_index_topk_noalloc(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI,
+                           int ratio, int k, int32_t* idx, void* stream) {
+  int st;
+  if ((st = index_checks(seqs, qI, w, n_I, kI, ratio))) return st;
+  if (!idx) return fail(CSA_EINVAL, "idx: null pointer");
+  if (k < 1 || k > 4096) return fail(CSA_EINVAL, "k %d out of [1, 4096]", k);
+  const size_t need = csa_workspace_bytes(CSA_OP_INDEX_TOPK, seqs, 0, 0, k, ratio, 0);
+  if (need > kNoallocScratchBytes)
+    return fail(CSA_EWORKSPACE,
+                "csa_index_topk_noalloc needs %zu bytes of scores (total_q * floor(max_ctx/ratio) * 4), more than "
+                "its fixed %zu-byte scratch",
+                need, kNoallocScratchBytes);
+  if (seqs->total_q == 0) return ok();
+  void* ptr = nullptr;
+  if ((st = scratch_on_current_device(&ptr))) return st;
+  return index_topk_launch(seqs, qI, w, n_I, kI, ratio, k, idx, static_cast<float*>(ptr),
+                           static_cast<hipStream_t>(stream));
 }
 
 int csa_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows* kv, const int32_t* idx, int k,

@@ -17,8 +17,8 @@ F32, BF16, KV_SPLIT, MXFP4 = 0, 1, 2, 3
 KV_SPLIT_BF16_DIMS = 64
 OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND = 1, 2, 3
 
-EXPORTS = ("csa_compress", "csa_compress2", "csa_index_score", "csa_topk", "csa_index_topk", "csa_attend", "hca_attend",
-           "csa_workspace_bytes", "csa_strerror", "csa_last_error", "csa_version")
+EXPORTS = ("csa_compress", "csa_compress2", "csa_index_score", "csa_topk", "csa_index_topk", "csa_index_topk_noalloc",
+           "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_strerror", "csa_last_error", "csa_version")
 
 
 class CsaError(RuntimeError):
@@ -57,6 +57,7 @@ def lib():
         L.csa_index_score.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, vp, i64, vp]
         L.csa_topk.argtypes = [P(csa_seqs), vp, i64, i32, i32, vp, vp]
         L.csa_index_topk.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, i32, vp, vp, sz, vp]
+        L.csa_index_topk_noalloc.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, i32, vp, vp]
         L.csa_attend.argtypes = [P(csa_seqs), P(csa_rows), i32, P(csa_rows), vp, i32, P(csa_rows), i32, vp, f32, i32,
                                  f64, P(csa_rows), vp, vp, sz, vp]
         L.hca_attend.argtypes = [P(csa_seqs), P(csa_rows), i32, P(csa_rows), i32, P(csa_rows), i32, vp, f32, i32, f64,
@@ -68,7 +69,8 @@ def lib():
         L.csa_last_error.argtypes = []
         L.csa_last_error.restype = ctypes.c_char_p
         L.csa_version.restype = i32
-        for f in ("csa_compress", "csa_compress2", "csa_index_score", "csa_topk", "csa_index_topk", "csa_attend", "hca_attend"):
+        for f in ("csa_compress", "csa_compress2", "csa_index_score", "csa_topk", "csa_index_topk",
+                  "csa_index_topk_noalloc", "csa_attend", "hca_attend"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -176,6 +178,11 @@ def csa_index_topk(seqs, qI, w, n_I, kI, ratio, k, idx, ws=None, stream=None):
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib().csa_index_topk(ctypes.byref(seqs.c), ctypes.byref(qI.c), _ptr(w), n_I, ctypes.byref(kI.c), ratio, k,
                                 _ptr(idx), _ptr(ws), nbytes, _stream(stream)), "csa_index_topk")
+
+
+def csa_index_topk_noalloc(seqs, qI, w, n_I, kI, ratio, k, idx, stream=None):
+    _check(lib().csa_index_topk_noalloc(ctypes.byref(seqs.c), ctypes.byref(qI.c), _ptr(w), n_I, ctypes.byref(kI.c),
+                                        ratio, k, _ptr(idx), _stream(stream)), "csa_index_topk_noalloc")
 
 
 def csa_attend(seqs, q, n_h, kv, idx, k, tok, n_win, sink, scale, rope_dims, rope_theta, out, lse=None, ws=None,

@@ -158,3 +158,17 @@ def test_workspace_sizes_follow_the_launch(lib):
     # HCA: the chunk count follows the longest context
     h = _seqs(n_seqs=4, total_q=4, max_q=1, max_ctx=1000)
     assert ws(h, ops.OP_HCA_ATTEND, 64, 512, 0, 128, 128) == 0   # 7 entries + 128 window: one chunk
+
+
+def test_noalloc_validation_before_any_device_call(lib):
+    """Argument errors and oversized calls of the allocation-free entry point are refused on
+    the host, before the scratch lookup (no GPU is touched)."""
+    P = ctypes.byref
+    qI = _rows(dim=128)
+    w = ctypes.c_void_p(0x6000)
+    idx = ctypes.c_void_p(0x7000)
+    s = _seqs(n_seqs=1, total_q=70, max_q=70, max_ctx=1 << 20)
+    assert lib.csa_index_topk_noalloc(P(s), P(qI), w, 64, P(qI), 4, 64, idx, None) == -3
+    assert "scratch" in ops.csa_last_error()
+    assert lib.csa_index_topk_noalloc(P(s), P(qI), w, 64, P(qI), 4, 0, idx, None) == -1
+    assert lib.csa_index_topk_noalloc(P(s), P(qI), w, 64, P(qI), 4, 64, None, None) == -1

@@ -1,0 +1,66 @@
+"""The allocation-free index + top-k entry point (scores in the library's fixed per-device
+scratch) gives the same idx bits as csa_index_topk with a caller workspace, on two calls
+in a row with the second smaller than the first (the scratch keeps the first call's
+scores), in the fp32, bf16 and MXFP4 indexer formats; oversized calls are refused."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_attention_07_amd import ops
+
+from harness import DEV, bf16, f32, make_batch, mxfp4
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.lib()
+
+
+def _inputs(g, fmt, n_q, ctx, n_I, d_I, ratio):
+    ob, sq, n_ent, _ = make_batch(n_q, ctx, ratio)
+    mk = {"f32": lambda x: (ops.Rows.of(f32(x)[0]), None), "bf16": lambda x: (ops.Rows.of(bf16(x)[0]), None),
+          "mxfp4": lambda x: (mxfp4(x)[0], None)}[fmt]
+    kI, _ = mk(g.standard_normal((n_ent, d_I)))
+    qI, _ = mk(g.standard_normal((sq.total_q * n_I, d_I)))
+    w, _ = f32(g.standard_normal((sq.total_q, n_I)) / math.sqrt(n_I))
+    return sq, qI, w, kI
+
+
+@pytest.mark.parametrize("fmt,n_I,d_I", [("f32", 4, 32), ("bf16", 64, 128), ("mxfp4", 64, 128)])
+def test_noalloc_index_topk_matches_workspace_call(fmt, n_I, d_I):
+    g = np.random.default_rng(41)
+    ratio, k = 4, 64
+    calls = [([1] * 24 + [30], [9000 + 977 * i for i in range(24)] + [60000]),   # larger first
+             ([1, 3, 2], [5000, 700, 3000])]                                       # then smaller
+    for n_q, ctx in calls:
+        sq, qI, w, kI = _inputs(g, fmt, n_q, ctx, n_I, d_I, ratio)
+        ref = torch.full((sq.total_q, k), -7, dtype=torch.int32, device=DEV)
+        got = torch.full((sq.total_q, k), -9, dtype=torch.int32, device=DEV)
+        ws = torch.empty(ops.csa_workspace_bytes(ops.OP_INDEX_TOPK, sq, k=k, ratio=ratio) // 4 + 1, device=DEV)
+        ops.csa_index_topk(sq, qI, w, n_I, kI, ratio, k, ref, ws=ws)
+        ops.csa_index_topk_noalloc(sq, qI, w, n_I, kI, ratio, k, got)
+        torch.cuda.synchronize()
+        assert torch.equal(ref, got), f"{fmt}: idx differs from the workspace call ({sq.total_q} tokens)"
+        print(f"noalloc {fmt}: {sq.total_q} tokens, max ctx {sq.max_ctx}: idx identical", flush=True)
+
+
+def test_noalloc_refuses_oversized_calls():
+    g = np.random.default_rng(43)
+    # 70 query tokens at ctx 1M: 70 * 262144 * 4 bytes > 64 MiB
+    n_q, ctx = [70], [1 << 20]
+    sq = ops.Seqs(n_q, ctx, [0])
+    kI = ops.Rows.of(torch.zeros((8, 128), dtype=torch.bfloat16, device=DEV))
+    qI = ops.Rows.of(torch.zeros((70 * 64, 128), dtype=torch.bfloat16, device=DEV))
+    w = torch.zeros((70, 64), device=DEV)
+    idx = torch.empty((70, 64), dtype=torch.int32, device=DEV)
+    with pytest.raises(ops.CsaError) as e:
+        ops.csa_index_topk_noalloc(sq, qI, w, 64, kI, 4, 64, idx)
+    assert e.value.status == -3 and "scratch" in str(e.value)
+    del g

@@ -1,24 +1,28 @@
-"""Benchmark of the CSA decode step on one MI355X.
+"""Benchmark of the hybrid compressed attention (CSA / HCA) decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload csa_decode|hca_decode|csa_prefill]
+                    [--no-sweep] [--no-cpu] [--no-probe]
 
 A step is one pass of the whole hot path over one decode batch: compress the entries the
 new tokens complete (KV rows and indexer keys), score and select the top-k entries, and
-attend over them plus the 128-token window with the sink.  The default workload is the
-CSA decode batch: 32 sequences with contexts log-uniform in [8K, 64K] (seed 1), one new
-token each, 64 query heads sharing one 512-dim KV head (last 64 dims RoPE), m = 4
+attend over them plus the 128-token window with the sink.  The headline workload (`value`)
+is the CSA decode batch: 32 sequences with contexts log-uniform in [8K, 64K] (seed 1), one
+new token each, 64 query heads sharing one 512-dim KV head (last 64 dims RoPE), m = 4
 overlapped compression, a 64-head x 128-dim indexer, k = 512, window 128, bf16.
 
-Inputs are synthetic, seeded and resident in HBM before timing.  Eight independent layer
-sets (about 2.3 GB) are rotated step by step so that no set stays in the 256 MB
-Infinity Cache; the steps of the eight sets are captured in one HIP graph replayed on the
-launch stream.
-Prints one JSON line.
+The same JSON line carries, under `sweep`, the decode step over the metric's whole context
+range: CSA at 64K / 256K / 1M (batch 32, k = 512) with bf16 and with MXFP4 indexer keys
+and queries, CSA with k = 1024 (batch 32, 8K-64K), and HCA at 64K / 256K / 1M (batch 4);
+each with tokens/s, median / p10 / p90 step times, the per-operation times and the
+roofline entry of its dominant operation.  Under `prefill` it carries the mixed-precision
+prefill (131072 causal tokens, fp8 1x128 KV rows with bf16 RoPE dims, MXFP4 indexer,
+k = 1024), priced against the fp8 matrix-core peak with the peak of the instruction used
+beside it.
 
-`--workload csa_prefill` measures the mixed-precision prefill instead (one sequence of
-131072 causal tokens: fp8 1x128 KV rows with bf16 RoPE dims, MXFP4 indexer, k = 1024):
-inputs are drawn on the GPU from a seeded generator (N(0,1) with 0.1% +-20 outliers) and
-quantized there; its roofline is the matrix-core throughput of the dominant kernel.
+Inputs are synthetic, seeded and resident in HBM before timing.  Several independent layer
+sets (more than 512 MB in all) are rotated step by step so that no set stays in the 256 MB
+Infinity Cache; the steps of all sets are captured in one HIP graph replayed on the launch
+stream.  Prints one JSON line.
 """
 
 import argparse
@@ -41,11 +45,14 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6   # dense bf16 / fp16 MFMA
 FP8_PEAK_TFLOPS = 5033.2    # dense fp8 MFMA
 FP4_PEAK_TFLOPS = 10100.0   # dense MXFP4 (scaled fp4) MFMA
-N_SETS = 8
+SET_BYTES = 512 << 20       # layer sets rotated per timed loop: at least this many bytes in all
+MAX_SETS = 64
 # kernels each operation launches (substrings of the kernel names in profiler output)
-OP_KERNELS = {"compress": ["compress2_kernel", "compress_kernel"], "index_score": ["index_score_mfma_kernel", "index_score_mfma_units_kernel"],
+OP_KERNELS = {"compress": ["compress2_kernel", "compress_kernel"],
+              "index_score": ["index_score_mfma_kernel", "index_score_mfma_units_kernel", "index_score_mx_kernel",
+                              "index_score_mx_block_kernel"],
               "topk": ["topk_kernel", "topk_decode_kernel"],
-              "attend": ["attend_pair_kernel", "attend_combine_mfma_kernel"]}
+              "attend": ["attend_pair_kernel", "attend_combine_mfma_kernel", "attend_long_kernel"]}
 PREFILL_KERNELS = {"compress": ["compress2_kernel"], "index_score": ["index_score_mx_block_kernel"],
                    "topk": ["topk_kernel"], "attend": ["attend_long_kernel"]}
 CALIB_BYTES = 256 << 20  # plain device copy used to calibrate the HBM byte counters
@@ -56,11 +63,57 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-class DecodeLayer:
-    """One layer's pools and per-step inputs for a decode batch (CSA or HCA)."""
+# ----------------------------------------------------------------------------- inputs
 
-    def __init__(self, wl, lens, seed, dev):
-        self.wl = wl
+def mxfp4_rows(x):
+    """float32 [n, d] on the GPU -> MXFP4 Rows by the OCP recipe (32-value blocks, e8m0
+    exponent floor(log2 amax) - 2, e2m1 round-to-nearest-even saturating at +-6, low nibble
+    first), in chunks of 2^20 rows (input generation)."""
+    n, d = x.shape
+    packed = torch.empty((n, d // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((n, d // 32), dtype=torch.uint8, device=x.device)
+    for r0 in range(0, n, 1 << 20):
+        xb = x[r0:r0 + (1 << 20)].reshape(-1, d // 32, 32)
+        amax = xb.abs().amax(dim=2)
+        _, ex = torch.frexp(amax)
+        E = torch.where(amax > 0, ex.to(torch.int32) - 3, torch.full_like(ex, -127, dtype=torch.int32)).clamp(-127, 127)
+        y = xb * torch.ldexp(torch.ones_like(amax), -E)[:, :, None]
+        mag = y.abs().clamp(max=6.0)
+        step = torch.where(mag < 2.0, 0.5, torch.where(mag < 4.0, 1.0, 2.0))
+        r = torch.round(mag / step) * step
+        code = torch.where(r < 2.0, r * 2.0, torch.where(r < 4.0, r + 2.0, r * 0.5 + 4.0)).to(torch.uint8)
+        code = (code | torch.where(torch.signbit(y), 8, 0).to(torch.uint8)).reshape(-1, d)
+        packed[r0:r0 + code.shape[0]] = code[:, 0::2] | (code[:, 1::2] << 4)
+        scales[r0:r0 + code.shape[0]] = (E + 127).to(torch.uint8)
+    return ops.Rows(packed, ops.MXFP4, d, scales)
+
+
+def kv_split_rows(x):
+    """float32 [n, 512] on the GPU -> KV split Rows: e4m3 codes of dims 0..447 with one fp32
+    scale (amax / 448) per 128 dims, then the last 64 dims in bf16 (input generation)."""
+    n, D = x.shape
+    dn = D - 64
+    nb = (dn + 127) // 128
+    codes = torch.empty((n, dn), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((n, nb), dtype=torch.float32, device=x.device)
+    for b in range(nb):
+        blk = x[:, 128 * b: min(dn, 128 * b + 128)]
+        sc = blk.abs().amax(dim=1) / 448.0
+        scales[:, b] = sc
+        y = (blk / torch.where(sc > 0, sc, torch.ones_like(sc))[:, None]).clamp(-448.0, 448.0)
+        codes[:, 128 * b: min(dn, 128 * b + 128)] = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    row = torch.empty((n, dn + 128), dtype=torch.uint8, device=x.device)
+    row[:, :dn] = codes
+    row[:, dn:] = x[:, dn:].to(torch.bfloat16).contiguous().view(torch.uint8)
+    return ops.Rows(row, ops.KV_SPLIT, D, scales)
+
+
+class DecodeLayer:
+    """One layer's pools and per-step inputs for a decode batch (CSA or HCA).  `kfmt` is the
+    indexer format: "bf16", or "mxfp4" (keys, queries and the keys the compress step writes)."""
+
+    def __init__(self, wl, lens, seed, dev, kfmt="bf16"):
+        self.wl, self.kfmt = wl, kfmt
         n, D, ratio = wl.n_seqs, wl.d_c, wl.ratio
         x = synth.decode_inputs(wl, lens, seed, dev)
         self.lens, self.E = x["lens"], x["E"]
@@ -72,9 +125,15 @@ class DecodeLayer:
         self.out = torch.empty((n * wl.n_h, D), dtype=bf, device=dev)
         self.lse = torch.empty((n, wl.n_h), dtype=torch.float32, device=dev)
         self.csa = wl.kind == "csa_decode"
+        self.R = {k: ops.Rows.of(getattr(self, k)) for k in ("kv", "c", "z", "q", "out")}
         if self.csa:
             for key in ("kI", "cI", "zI", "biasI", "qI", "w"):
                 setattr(self, key, x[key])
+            self.R.update({k: ops.Rows.of(getattr(self, k)) for k in ("kI", "cI", "zI", "qI")})
+            if kfmt == "mxfp4":
+                self.R["kI"] = mxfp4_rows(self.kI.float())
+                self.R["qI"] = mxfp4_rows(self.qI.float())
+                del self.kI, self.qI
             self.idx = torch.empty((n, wl.k), dtype=torch.int32, device=dev)
             ws_i = ops.csa_workspace_bytes(ops.OP_INDEX_TOPK, self.seqs, k=wl.k, ratio=ratio)
             ws_a = ops.csa_workspace_bytes(ops.OP_CSA_ATTEND, self.seqs, wl.n_h, D, wl.k, ratio, wl.n_win)
@@ -83,9 +142,6 @@ class DecodeLayer:
             ws_i = 0
             ws_a = ops.csa_workspace_bytes(ops.OP_HCA_ATTEND, self.seqs, wl.n_h, D, 0, ratio, wl.n_win)
         self.ws = torch.empty(max(ws_i, ws_a, 4) // 4 + 1, dtype=torch.float32, device=dev)
-        self.R = {k: ops.Rows.of(getattr(self, k)) for k in ("kv", "c", "z", "q", "out")}
-        if self.csa:
-            self.R.update({k: ops.Rows.of(getattr(self, k)) for k in ("kI", "cI", "zI", "qI")})
 
     # -- the step's operations
     def compress(self):
@@ -99,13 +155,14 @@ class DecodeLayer:
             ops.csa_compress(self.seqs, self.R["c"], self.R["z"], self.bias, wl.ratio, wl.overlap, wl.rope_dims,
                              wl.rope_theta, self.R["kv"])
 
+    def _score(self):
+        return self.ws[: self.wl.n_seqs * self.ws_score_stride].view(self.wl.n_seqs, self.ws_score_stride)
+
     def index_score(self):
-        score = self.ws[: self.wl.n_seqs * self.ws_score_stride].view(self.wl.n_seqs, self.ws_score_stride)
-        ops.csa_index_score(self.seqs, self.R["qI"], self.w, self.wl.n_I, self.R["kI"], self.wl.ratio, score)
+        ops.csa_index_score(self.seqs, self.R["qI"], self.w, self.wl.n_I, self.R["kI"], self.wl.ratio, self._score())
 
     def topk(self):
-        score = self.ws[: self.wl.n_seqs * self.ws_score_stride].view(self.wl.n_seqs, self.ws_score_stride)
-        ops.csa_topk(self.seqs, score, self.wl.ratio, self.wl.k, self.idx)
+        ops.csa_topk(self.seqs, self._score(), self.wl.ratio, self.wl.k, self.idx)
 
     def attend(self):
         wl = self.wl
@@ -117,12 +174,12 @@ class DecodeLayer:
             ops.hca_attend(self.seqs, self.R["q"], wl.n_h, self.R["kv"], wl.ratio, self.R["c"], wl.n_win, self.sink,
                            scale, wl.rope_dims, wl.rope_theta, self.R["out"], self.lse, ws=self.ws)
 
+    def ops_in_step(self):
+        return ["compress", "index_score", "topk", "attend"] if self.csa else ["compress", "attend"]
+
     def step(self):
-        self.compress()
-        if self.csa:
-            self.index_score()
-            self.topk()
-        self.attend()
+        for name in self.ops_in_step():
+            getattr(self, name)()
 
     # -- algorithmic bytes / flops per call of each operation
     def work(self):
@@ -137,9 +194,10 @@ class DecodeLayer:
         qo = n * nh * D * 2 * 2 + n * nh * 4
         if self.csa:
             dI, nI = wl.d_I, wl.n_I
-            comp_b += new_ent.sum() * (src * 2 * dI * 2 + dI * 2)
+            key_b = dI * 2 if self.kfmt == "bf16" else dI // 2 + dI // 32   # stored key (+ e8m0 scales)
+            comp_b += new_ent.sum() * (src * 2 * dI * 2 + key_b)
             w["compress"] = (comp_b, 0.0)
-            w["index_score"] = (float((V * (dI * 2 + 4)).sum() + n * (nI * dI * 2 + nI * 4)),
+            w["index_score"] = (float((V * (key_b + 4)).sum() + n * (nI * key_b + nI * 4)),
                                 float((V * nI * dI * 2).sum()))
             w["topk"] = (float((V * 4).sum() + n * wl.k * 4), 0.0)
             keys = np.minimum(V, wl.k) + win
@@ -178,58 +236,198 @@ def time_fn(fn, layers, reps, stream):
     return e0.elapsed_time(e1) / (n * len(layers))
 
 
-def cpu_baseline(layer, budget_s=12.0):
-    """The float64 oracle on the host cores: a bounded sample of the same decode batch
-    (whole tokens, in sequence order, until the time budget is spent)."""
-    from oracle import pipeline as P
+def build_layers(wl, dev, kfmt="bf16", max_sets=MAX_SETS, min_sets=2):
+    """Layer sets for a decode workload: enough independent sets that the bytes their steps
+    touch exceed SET_BYTES together (twice the Infinity Cache, so no set's rows stay there
+    from one use to the next), between min_sets and max_sets."""
+    lens = make_lengths(wl)
+    layers = [DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100), dev, kfmt)]
+    touched = sum(b for b, _ in layers[0].work().values())
+    n_sets = int(min(max_sets, max(min_sets, math.ceil(SET_BYTES / max(touched, 1.0)))))
+    for i in range(1, n_sets):
+        layers.append(DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100 + i), dev, kfmt))
+    return layers, lens
+
+
+def timed_steps(layers, steps, warmup, stream, graph=True):
+    """Warm-up, then exactly `steps` steps (rotating the layer sets) between two events,
+    with a synchronisation on both sides.  Returns (ms per step, per-replay step times in
+    ms, wall seconds).  The steps of all sets are one HIP graph, replayed; a remainder of
+    steps replays per-set graphs."""
+    for i in range(max(warmup, len(layers))):
+        layers[i % len(layers)].step()
+    torch.cuda.synchronize()
+    g_all, graphs = None, []
+    if graph:
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all, stream=stream):
+            for L_ in layers:
+                L_.step()
+        for L_ in layers:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                L_.step()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for _ in range(max(1, warmup // len(layers))):
+            g_all.replay()
+    torch.cuda.synchronize()
+    n_rep = steps // len(layers) if graph else 0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    if graph:
+        ev[0].record(stream)
+        for r in range(n_rep):
+            g_all.replay()
+            ev[r + 1].record(stream)
+        for i in range(steps % len(layers)):
+            graphs[i].replay()
+    else:
+        for i in range(steps):
+            layers[i % len(layers)].step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / steps
+    per_step = [ev[r].elapsed_time(ev[r + 1]) / len(layers) for r in range(n_rep)]
+    return ms, per_step, t_wall
+
+
+def percentiles(xs):
+    if not xs:
+        return None
+    a = np.asarray(xs)
+    return {"median": round(float(np.median(a)) * 1e3, 2), "p10": round(float(np.percentile(a, 10)) * 1e3, 2),
+            "p90": round(float(np.percentile(a, 90)) * 1e3, 2), "n": int(a.size), "unit": "us"}
+
+
+def op_breakdown(layers, reps, stream):
+    """Per-operation time (graph replays of that operation alone over the layer sets) and
+    its algorithmic bytes and flops; the roofline entry of the dominant operation."""
+    work = layers[0].work()
+    op_ms = {name: time_fn(lambda L_: getattr(L_, name)(), layers, reps, stream) for name in work}
+    kernels = {}
+    for name, (b, f) in work.items():
+        t = op_ms[name] * 1e-3
+        kernels[name] = {"us": round(op_ms[name] * 1e3, 2), "GB/s": round(b / t / 1e9, 1),
+                         "hbm_frac": round(b / t / 1e9 / HBM_PEAK_GBS, 4), "TFLOP/s": round(f / t / 1e12, 2),
+                         "bytes": int(b), "flops": int(f)}
+    dom = max(op_ms, key=op_ms.get)
+    db, _ = work[dom]
+    dt = op_ms[dom] * 1e-3
+    roof = {"kernel": dom, "kernels": OP_KERNELS[dom], "bound": "hbm", "achieved": round(db / dt / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(db / dt / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch": int(db), "avg_launch_us": round(op_ms[dom] * 1e3, 2)}
+    return kernels, roof, work
+
+
+def run_decode(wl, dev, stream, steps, warmup, kfmt="bf16", graph=True, max_sets=MAX_SETS):
+    """One decode workload: tokens/s over exactly `steps` steps, step-time percentiles,
+    per-operation times and the dominant operation's roofline entry."""
+    layers, lens = build_layers(wl, dev, kfmt, max_sets=max_sets)
+    torch.cuda.synchronize()
+    log(f"{wl.name} ({kfmt} indexer): {wl.n_seqs} seqs, ctx {min(lens)}..{max(lens)}, {len(layers)} layer sets, "
+        f"{torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated")
+    ms, per_step, wall = timed_steps(layers, steps, warmup, stream, graph)
+    kernels, roof, work = op_breakdown(layers, max(64, steps // 4), stream)
+    step_bytes = sum(b for b, _ in work.values())
+    res = {"workload": wl.name, "indexer": kfmt if layers[0].csa else None, "tokens_per_s": round(wl.n_seqs / (ms * 1e-3), 1),
+           "ms_per_step": round(ms, 5), "step_time": percentiles(per_step), "wall_s": round(wall, 3),
+           "batch": wl.n_seqs, "ctx": [min(lens), max(lens)], "k": wl.k if layers[0].csa else None,
+           "layer_sets": len(layers),
+           "rotation_MB": round(len(layers) * sum(b for b, _ in layers[0].work().values()) / 1e6, 1),
+           "step_hbm_GBs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+           "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "roofline": roof, "kernels": kernels}
+    log(f"  step {ms * 1e3:.1f} us, {res['tokens_per_s']:.0f} tokens/s; dominant {roof['kernel']} "
+        f"{roof['avg_launch_us']} us = {roof['frac']:.3f} of HBM peak")
+    return res, layers
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def _oracle_worker(task):
+    """Process-pool worker: the float64 oracle pipeline (compress the new entries, index and
+    select for CSA, attend) over its tokens, repeated until `budget_s` has passed.  Returns
+    (tokens done, seconds)."""
+    from threadpoolctl import threadpool_limits
     from oracle.attention import attend_token
     from oracle.compress import compress_entries, new_entry_range
     from oracle.indexer import index_scores, topk_select
 
-    wl = layer.wl
-    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
-    sink = f64(layer.sink)
-    bias = f64(layer.bias)
-    scale = 1.0 / math.sqrt(wl.d_c)
-    done, t_oracle = 0, 0.0
-    for b in range(wl.n_seqs):
-        L = layer.lens[b]
-        e0, E = layer.entry_off[b], layer.E[b]
-        t0r = layer.tok_off[b]
-        nrow = L - layer.tok_lo[b]
-        # host copies of this sequence's rows (setup, not timed)
-        kv = f64(layer.kv[e0: e0 + E])
-        c = f64(layer.c[t0r: t0r + nrow])
-        z = f64(layer.z[t0r: t0r + nrow])
-        q = f64(layer.q[b * wl.n_h:(b + 1) * wl.n_h])
-        if layer.csa:
-            kI = f64(layer.kI[e0: e0 + E])
-            cI, zI = f64(layer.cI[t0r: t0r + nrow]), f64(layer.zI[t0r: t0r + nrow])
-            biasI = f64(layer.biasI)
-            qI = f64(layer.qI[b * wl.n_I:(b + 1) * wl.n_I])
-            w = f64(layer.w[b])
-        t0 = time.perf_counter()
-        ids = list(new_entry_range(L, 1, wl.ratio))
-        if ids:
-            kv[ids] = compress_entries(c, z, bias, wl.ratio, wl.overlap, ids, wl.rope_dims, wl.rope_theta,
-                                       tok_lo=layer.tok_lo[b])
-            if layer.csa:
-                kI[ids] = compress_entries(cI, zI, biasI, wl.ratio, wl.overlap, ids, 0, tok_lo=layer.tok_lo[b])
-        p = L - 1
-        if layer.csa:
-            sel = list(topk_select(index_scores(qI, w, kI[: (p + 1) // wl.ratio]), wl.k))
-        else:
-            sel = list(range((p + 1) // wl.ratio))
-        attend_token(q, p, kv, sel, c, wl.n_win, sink, scale, wl.rope_dims, wl.rope_theta, tok_lo=layer.tok_lo[b])
-        t_oracle += time.perf_counter() - t0
-        done += 1
-        if t_oracle > budget_s:
-            break
-    cores = len(os.sched_getaffinity(0))
-    return {"value": done / t_oracle, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {wl.n_seqs} decode tokens of set 0 (whole per-token pipeline, float64 NumPy; "
-                      f"BLAS threads as configured, {cores} cores visible)"}
+    toks, cfg, budget_s = task
+    bf = lambda u: (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa: E731
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            for t in toks:
+                L, lo, ratio = t["L"], t["tok_lo"], cfg["ratio"]
+                kv, c, z = bf(t["kv"]), bf(t["c"]), bf(t["z"])
+                ids = list(new_entry_range(L, 1, ratio))
+                if ids:
+                    kv[ids] = compress_entries(c, z, t["bias"], ratio, cfg["overlap"], ids, cfg["rope_dims"],
+                                               cfg["rope_theta"], tok_lo=lo)
+                p = L - 1
+                if cfg["csa"]:
+                    kI = bf(t["kI"])
+                    if ids:
+                        kI[ids] = compress_entries(bf(t["cI"]), bf(t["zI"]), t["biasI"], ratio, cfg["overlap"], ids, 0,
+                                                   tok_lo=lo)
+                    sel = list(topk_select(index_scores(bf(t["qI"]), t["w"], kI[: (p + 1) // ratio]), cfg["k"]))
+                else:
+                    sel = list(range((p + 1) // ratio))
+                attend_token(bf(t["q"]), p, kv, sel, c, cfg["n_win"], t["sink"], cfg["scale"], cfg["rope_dims"],
+                             cfg["rope_theta"], tok_lo=lo)
+                done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    return done, time.perf_counter() - t0
 
+
+def cpu_baseline(layers, budget_s=2.0, max_workers=16):
+    """The float64 oracle on the host cores, one worker process per core (BLAS limited to one
+    thread each), over a bounded sample of the same decode batch: the tokens of the first
+    two layer sets dealt round-robin to the workers, each worker repeating its tokens for
+    `budget_s` seconds.  tokens/s = tokens done / the slowest worker's time."""
+    import multiprocessing as mp
+
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(max_workers, cores))
+    u16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    wl = layers[0].wl
+    toks = []
+    for layer in layers[:2]:
+        for b in range(wl.n_seqs):
+            e0, E, t0r = layer.entry_off[b], layer.E[b], layer.tok_off[b]
+            nrow = layer.lens[b] - layer.tok_lo[b]
+            t = {"L": layer.lens[b], "tok_lo": layer.tok_lo[b], "kv": u16(layer.kv[e0:e0 + E]),
+                 "c": u16(layer.c[t0r:t0r + nrow]), "z": u16(layer.z[t0r:t0r + nrow]),
+                 "q": u16(layer.q[b * wl.n_h:(b + 1) * wl.n_h]), "bias": f64(layer.bias), "sink": f64(layer.sink)}
+            if layer.csa:
+                t.update({"kI": u16(layer.kI[e0:e0 + E]), "cI": u16(layer.cI[t0r:t0r + nrow]),
+                          "zI": u16(layer.zI[t0r:t0r + nrow]), "qI": u16(layer.qI[b * wl.n_I:(b + 1) * wl.n_I]),
+                          "w": f64(layer.w[b]), "biasI": f64(layer.biasI)})
+            toks.append(t)
+    cfg = {"ratio": wl.ratio, "overlap": wl.overlap, "rope_dims": wl.rope_dims, "rope_theta": wl.rope_theta,
+           "csa": layers[0].csa, "k": wl.k, "n_win": wl.n_win, "scale": 1.0 / math.sqrt(wl.d_c)}
+    tasks = [(toks[i::workers], cfg, budget_s) for i in range(workers)]
+    ctx = mp.get_context("spawn")   # fresh interpreters: the workers never touch the GPU
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_worker, [([], cfg, 0.0)] * workers)   # start-up outside the timing
+        res = pool.map(_oracle_worker, tasks)
+    done = sum(d for d, _ in res)
+    secs = max(s for _, s in res)
+    return {"value": round(done / secs, 2), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{len(toks)} decode tokens of {wl.name} (2 layer sets), {workers} worker processes with "
+                      f"one BLAS thread each repeating their tokens for {budget_s:.0f} s ({done} tokens in all); "
+                      f"whole per-token pipeline in float64 NumPy"}
+
+
+# ----------------------------------------------------------------------------- counters
 
 def source_digest():
     """sha256 of the library sources: traffic figures are used only for the kernels they were
@@ -238,7 +436,7 @@ def source_digest():
     h = hashlib.sha256()
     src = os.path.join(ROOT, "long_context_attention_07_amd", "csrc")
     for name in sorted(os.listdir(src)):
-        if name.endswith((".hip", ".cuh", ".h", ".cpp")) and name != "probe.hip":
+        if name.endswith((".hip", ".h", ".hpp", ".cpp")) and name != "probe.hip":
             h.update(name.encode())
             with open(os.path.join(src, name), "rb") as f:
                 h.update(f.read())
@@ -250,9 +448,9 @@ def source_digest():
 def achievable_peaks(stream, copy_bytes=1 << 30, reps=5):
     """What this device reaches on the two priced resources, beside the published peaks:
     a plain device copy of `copy_bytes` (HBM bytes = twice that), a read-only stream of the
-    same bytes, and back-to-back
-    matrix-core instructions per operand format, two waves per SIMD (libcsa_probe.so).
-    Context only: every roofline fraction is computed against the published peak."""
+    same bytes, and back-to-back matrix-core instructions per operand format, two waves per
+    SIMD (libcsa_probe.so).  Context only: every roofline fraction is computed against the
+    published peak."""
     from long_context_attention_07_amd import probe
     n_cu, khz = probe.device()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -297,9 +495,7 @@ def achievable_peaks(stream, copy_bytes=1 << 30, reps=5):
 def profile_run(layers, stream, reps):
     """Eager launches for the counter runs: each operation `reps` times per layer set, then
     a plain device copy of CALIB_BYTES (four times) to calibrate the byte counters."""
-    for name in OP_KERNELS:
-        if not hasattr(layers[0], name) or (name in ("index_score", "topk") and not layers[0].csa):
-            continue
+    for name in layers[0].ops_in_step():
         for _ in range(reps):
             for L_ in layers:
                 getattr(L_, name)()
@@ -330,7 +526,7 @@ def traffic_from_counters(fetch_dir, write_dir, workload, out_path):
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
 
     def copy_kib(vals):
-        big = [v for k, vs in vals.items() if "copy" in k.lower() for v in vs if v > CALIB_BYTES / 1024 / 8]
+        big = [v for k, vs in vals.items() if "copy" in k.lower() for v in vs if v > CALIB_BYTES / 1024 / 16]
         return float(np.median(big)) if big else None
 
     cf, cw = copy_kib(fetch), copy_kib(write)
@@ -358,12 +554,17 @@ def traffic_from_counters(fetch_dir, write_dir, workload, out_path):
 
 
 def load_traffic(wl):
+    """Counter bytes for `wl` when they were taken on the current sources and the copy
+    calibration read the copy's bytes within 25% (factor in [0.8, 1.25]); else None: a
+    calibration far from one means the counters saw only part of the chip."""
     path = os.path.join(PROFILES, f"traffic_{wl.name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    return t if t.get("source") == source_digest() else None
+    cal = t.get("calibration", {})
+    ok = all(0.8 <= float(cal.get(k, 0.0)) <= 1.25 for k in ("fetch_factor", "write_factor"))
+    return t if ok and t.get("source") == source_digest() else None
 
 
 # ----------------------------------------------------------------------------- prefill
@@ -377,44 +578,10 @@ def _gpu_normal(gen, shape, dev, scale=1.0, outliers=False):
     return x
 
 
-def _kv_split_rows(x):
-    """float32 [n, 512] on the GPU -> KV split Rows: e4m3 codes of dims 0..447 with one fp32
-    scale (amax / 448) per 128 dims, then the last 64 dims in bf16 (input generation)."""
-    n, D = x.shape
-    dn = D - 64
-    nb = (dn + 127) // 128
-    codes = torch.empty((n, dn), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((n, nb), dtype=torch.float32, device=x.device)
-    for b in range(nb):
-        blk = x[:, 128 * b: min(dn, 128 * b + 128)]
-        sc = blk.abs().amax(dim=1) / 448.0
-        scales[:, b] = sc
-        y = (blk / torch.where(sc > 0, sc, torch.ones_like(sc))[:, None]).clamp(-448.0, 448.0)
-        codes[:, 128 * b: min(dn, 128 * b + 128)] = y.to(torch.float8_e4m3fn).view(torch.uint8)
-    row = torch.empty((n, dn + 128), dtype=torch.uint8, device=x.device)
-    row[:, :dn] = codes
-    row[:, dn:] = x[:, dn:].to(torch.bfloat16).contiguous().view(torch.uint8)
-    return ops.Rows(row, ops.KV_SPLIT, D, scales)
-
-
-def _mxfp4_rows(x):
-    """float32 [n, d] on the GPU -> MXFP4 Rows: 32-element blocks, e8m0 scale
-    2^(floor(log2 amax) - 2), nearest e2m1 value, low nibble first (input generation)."""
-    n, d = x.shape
-    xb = x.view(n, d // 32, 32)
-    amax = xb.abs().amax(dim=2)
-    E = torch.where(amax > 0, torch.floor(torch.log2(amax.clamp_min(1e-30))) - 2, torch.zeros_like(amax))
-    y = xb / torch.exp2(E)[:, :, None]
-    grid = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], device=x.device)
-    mag = (y.abs().clamp(max=6.0)[..., None] - grid).abs().argmin(dim=-1)
-    code = (mag | torch.where(y < 0, 8, 0)).to(torch.uint8).view(n, d)
-    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
-    scales = (E + 127).to(torch.uint8).contiguous()
-    return ops.Rows(packed, ops.MXFP4, d, scales)
-
-
 class PrefillLayer:
-    """One CSA layer of the mixed-precision prefill: pools, per-token inputs and outputs."""
+    """One CSA layer of the mixed-precision prefill: pools, per-token inputs and outputs,
+    drawn on the GPU from a seeded generator (N(0,1) with 0.1% +-20 outliers) and quantized
+    there."""
 
     def __init__(self, wl, dev):
         N, D, n_h, n_I, d_I, ratio = wl.ctx_hi, wl.d_c, wl.n_h, wl.n_I, wl.d_I, wl.ratio
@@ -422,15 +589,17 @@ class PrefillLayer:
         gen = torch.Generator(device=dev)
         gen.manual_seed(wl.seed)
         self.seqs = ops.Seqs([N], [N], [0])
-        self.c = _kv_split_rows(_gpu_normal(gen, (N, D), dev, outliers=True))
+        self.c = kv_split_rows(_gpu_normal(gen, (N, D), dev, outliers=True))
         self.z = ops.Rows.of(_gpu_normal(gen, (N, D), dev).to(torch.bfloat16))
         self.cI = ops.Rows.of(_gpu_normal(gen, (N, d_I), dev, outliers=True).to(torch.bfloat16))
         self.zI = ops.Rows.of(_gpu_normal(gen, (N, d_I), dev).to(torch.bfloat16))
-        qI = _gpu_normal(gen, (N * n_I, d_I), dev, outliers=True)
-        self.qI = _mxfp4_rows(qI)
-        del qI
+        self.qI = mxfp4_rows(_gpu_normal(gen, (N * n_I, d_I), dev, outliers=True))
         self.w = _gpu_normal(gen, (N, n_I), dev, 1.0 / 8)
-        self.q = ops.Rows.of(_gpu_normal(gen, (N * n_h, D), dev, outliers=True).to(torch.bfloat16))
+        q = torch.empty((N * n_h, D), dtype=torch.bfloat16, device=dev)
+        for r0 in range(0, N * n_h, 1 << 20):
+            rows = min(1 << 20, N * n_h - r0)
+            q[r0:r0 + rows] = _gpu_normal(gen, (rows, D), dev, outliers=True).to(torch.bfloat16)
+        self.q = ops.Rows.of(q)
         self.sink = _gpu_normal(gen, (n_h,), dev)
         self.bias = _gpu_normal(gen, (2 * ratio, D), dev, 1.0 / math.sqrt(D))
         self.biasI = _gpu_normal(gen, (2 * ratio, d_I), dev, 1.0 / math.sqrt(d_I))
@@ -443,8 +612,8 @@ class PrefillLayer:
         self.idx = torch.empty((N, wl.k), dtype=torch.int32, device=dev)
         self.out = ops.Rows.of(torch.empty((N * n_h, D), dtype=torch.bfloat16, device=dev))
         self.lse = torch.empty((N, n_h), dtype=torch.float32, device=dev)
-        self.ws = torch.empty(ops.csa_workspace_bytes(ops.OP_CSA_ATTEND, self.seqs, n_h, D, wl.k, ratio, wl.n_win)
-                              // 4 + 1, dtype=torch.float32, device=dev)
+        wsb = ops.csa_workspace_bytes(ops.OP_CSA_ATTEND, self.seqs, n_h, D, wl.k, ratio, wl.n_win)
+        self.ws = torch.empty(wsb // 4 + 1, dtype=torch.float32, device=dev) if wsb else None
 
     def compress(self):
         wl = self.wl
@@ -480,7 +649,8 @@ class PrefillLayer:
         return {
             "compress": (E * (2 * wl.ratio * (row_b + D * 2) + row_b) + E * (2 * wl.ratio * dI * 4 + dI // 2 + 4),
                          0.0, None),
-            "index_score": (float(V.sum() * (dI // 2 + dI // 32 + 4) + N * nI * (dI // 2 + 4 + 4)),
+            # keys and queries read once, every causal score written once
+            "index_score": (float(E * (dI // 2 + dI // 32) + N * nI * (dI // 2 + dI // 32 + 4) + V.sum() * 4),
                             float(V.sum() * nI * dI * 2), FP4_PEAK_TFLOPS),
             "topk": (float(V.sum() * 4 + N * wl.k * 4), 0.0, None),
             "attend": (float((keys * row_b).sum() + N * wl.k * 4 + N * nh * D * 4), float((keys * nh * D * 4).sum()),
@@ -488,69 +658,70 @@ class PrefillLayer:
         }
 
 
-def run_prefill(args):
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    ops.lib()
+def run_prefill(dev, stream, steps=3, warmup=1):
+    """The mixed-precision prefill: per-operation times over `steps` steps; each matrix-core
+    operation priced against the fp8 peak (the gate's denominator) with the peak of the
+    instruction it uses beside it."""
     wl = configs.CSA_PREFILL_MIXED
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        layer = PrefillLayer(wl, dev)
-        torch.cuda.synchronize()
-        log(f"prefill {wl.name}: {layer.N} tokens, {layer.E} entries; "
-            f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
-        steps, warmup = max(1, min(args.steps, 5)), max(1, min(args.warmup, 2))
-        for _ in range(warmup):
-            layer.step()
-        torch.cuda.synchronize()
-        ev = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for n in ("compress", "index_score", "topk", "attend")}
-        op_ms = {n: 0.0 for n in ev}
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        total = 0.0
-        for _ in range(steps):
-            e0.record(stream)
-            for n in ("compress", "index_score", "topk", "attend"):
-                ev[n][0].record(stream)
-                getattr(layer, n)()
-                ev[n][1].record(stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            total += e0.elapsed_time(e1)
-            for n in ev:
-                op_ms[n] += ev[n][0].elapsed_time(ev[n][1])
-        ms = total / steps
-        value = layer.N / (ms * 1e-3)
-        work = layer.work()
-        kernels = {}
-        for n, (b, f, peak) in work.items():
-            t = op_ms[n] / steps * 1e-3
-            kernels[n] = {"us": round(t * 1e6, 1), "GB/s": round(b / t / 1e9, 1), "TFLOP/s": round(f / t / 1e12, 1),
-                          "mfma_frac": round(f / t / 1e12 / peak, 4) if peak else None, "bytes": int(b),
-                          "flops": int(f)}
-        dom = max(op_ms, key=op_ms.get)
-        b, f, peak = work[dom]
-        dt = op_ms[dom] / steps * 1e-3
-        roof = {"kernel": dom, "kernels": PREFILL_KERNELS[dom], "bound": "mfma",
-                "achieved": round(f / dt / 1e12, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(f / dt / 1e12 / peak, 4), "traffic": None, "flops_per_launch": int(f),
-                "avg_launch_us": round(dt * 1e6, 1)}
-        log(f"prefill step {ms:.2f} ms, {value:.0f} tokens/s; per-op {json.dumps(kernels)}")
-        achievable = None if args.no_probe else achievable_peaks(stream)
-    res = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8 KV (fp16 MFMA) + MXFP4 indexer (fp4 MFMA)", "data": "synthetic",
-        "config": {"workload": wl.name, "batch": 1, "seq_len": layer.N, "n_h": wl.n_h, "d_c": wl.d_c,
-                   "ratio": wl.ratio, "k": wl.k, "n_win": wl.n_win, "indexer": f"{wl.n_I}x{wl.d_I} MXFP4",
-                   "kv": "fp8 e4m3 1x128 + bf16 RoPE"},
-        "roofline": roof,
-        "kernels": kernels,
-        "achievable": achievable,
-        "cpu_baseline": None,
-    }
-    print(json.dumps(res), flush=True)
+    layer = PrefillLayer(wl, dev)
+    torch.cuda.synchronize()
+    log(f"prefill {wl.name}: {layer.N} tokens, {layer.E} entries; "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    names = ("compress", "index_score", "topk", "attend")
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+          for n in names}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(steps):
+        for n in names:
+            ev[n][s][0].record(stream)
+            getattr(layer, n)()
+            ev[n][s][1].record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    op_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
+    work = layer.work()
+    kernels = {}
+    for n, (b, f, peak) in work.items():
+        t = op_ms[n] * 1e-3
+        kernels[n] = {"us": round(t * 1e6, 1), "GB/s": round(b / t / 1e9, 1), "TFLOP/s": round(f / t / 1e12, 1),
+                      "fp8_frac": round(f / t / 1e12 / FP8_PEAK_TFLOPS, 4) if peak else None,
+                      "instr_peak_TFLOPs": peak, "instr_frac": round(f / t / 1e12 / peak, 4) if peak else None,
+                      "bytes": int(b), "flops": int(f)}
+    dom = max(op_ms, key=op_ms.get)
+    b, f, peak = work[dom]
+    dt = op_ms[dom] * 1e-3
+    roof = {"kernel": dom, "kernels": PREFILL_KERNELS[dom], "bound": "mfma", "achieved": round(f / dt / 1e12, 1),
+            "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(f / dt / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "instr_peak": peak, "instr_frac": round(f / dt / 1e12 / peak, 4), "traffic": None,
+            "flops_per_launch": int(f), "avg_launch_us": round(dt * 1e6, 1)}
+    res = {"workload": wl.name, "tokens_per_s": round(layer.N / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+           "steps": steps, "seq_len": layer.N, "k": wl.k, "kv": "fp8 e4m3 1x128 + bf16 RoPE",
+           "indexer": f"{wl.n_I}x{wl.d_I} MXFP4", "roofline": roof, "kernels": kernels}
+    log(f"prefill step {ms:.2f} ms; per-op {json.dumps(kernels)}")
+    del layer
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- main
+
+def run_sweep(dev, stream, steps, warmup):
+    """The decode step over the metric's context range (see the module docstring)."""
+    out = []
+    points = [(wl, "bf16") for wl in configs.CSA_DECODE_SWEEP] + [(wl, "mxfp4") for wl in configs.CSA_DECODE_SWEEP]
+    points += [(configs.CSA_DECODE_K1024, "bf16")] + [(wl, "bf16") for wl in configs.HCA_DECODE_SWEEP]
+    for wl, kfmt in points:
+        res, layers = run_decode(wl, dev, stream, steps, warmup, kfmt, max_sets=MAX_SETS)
+        out.append(res)
+        del layers
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -562,14 +733,15 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-probe", action="store_true", help="skip the achievable-peak probes")
-    ap.add_argument("--sets", type=int, default=N_SETS)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the context sweep and the prefill")
+    ap.add_argument("--sweep-steps", type=int, default=80)
     ap.add_argument("--profile-run", type=int, default=0, metavar="REPS",
                     help="only launch each operation REPS times per layer set (for rocprofv3), then exit")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of --profile-run into profiles/traffic_<workload>.json")
     args = ap.parse_args()
+    wl = configs.CSA_DECODE_BF16 if args.workload == "csa_decode" else configs.HCA_DECODE_1M_BF16
     if args.traffic:
-        wl = configs.CSA_DECODE_BF16 if args.workload == "csa_decode" else configs.HCA_DECODE_1M_BF16
         traffic_from_counters(args.traffic[0], args.traffic[1], wl.name,
                               os.path.join(PROFILES, f"traffic_{wl.name}.json"))
         return
@@ -577,116 +749,63 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path shards by sequence "
               f"with no exchange, so N GPUs run N independent copies of this benchmark.", file=sys.stderr)
         sys.exit(2)
-    if args.workload == "csa_prefill":
-        run_prefill(args)
-        return
     dev = "cuda:0"
     torch.cuda.set_device(0)
     ops.lib()
-    wl = configs.CSA_DECODE_BF16 if args.workload == "csa_decode" else configs.HCA_DECODE_1M_BF16
-    lens = make_lengths(wl)
-    log(f"workload {wl.name}: {wl.n_seqs} seqs, ctx min {min(lens)} max {max(lens)} mean {np.mean(lens):.0f}")
     stream = torch.cuda.Stream()  # default priority; graphs cannot be captured on the null stream
     with torch.cuda.stream(stream):
-        layers = [DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100 + i), dev) for i in range(args.sets)]
-        torch.cuda.synchronize()
-        log(f"allocated {torch.cuda.memory_allocated() / 2**30:.2f} GiB for {args.sets} layer sets")
+        if args.workload == "csa_prefill":
+            res = run_prefill(dev, stream, steps=max(1, min(args.steps, 5)), warmup=max(1, min(args.warmup, 2)))
+            out = {"metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                   "steps": res["steps"], "warmup": 1, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+                   "scaling": "weak", "vs_baseline": None, "dtype": "fp8 KV (fp16 MFMA) + MXFP4 indexer (fp4 MFMA)",
+                   "data": "synthetic", "config": {"workload": res["workload"], "batch": 1, "seq_len": res["seq_len"]},
+                   "roofline": res["roofline"], "kernels": res["kernels"], "cpu_baseline": None}
+            print(json.dumps(out), flush=True)
+            return
         if args.profile_run:
+            layers, _ = build_layers(wl, dev)
             for L_ in layers:
                 L_.step()
             profile_run(layers, stream, args.profile_run)
             log("profile run done")
             return
-        # eager warm-up, then capture the steps of all layer sets in one graph (one launch per
-        # round of layer sets, as a model's forward pass would be captured) and one graph
-        # per set for a remainder of steps
-        for i in range(max(args.warmup, len(layers))):
-            layers[i % len(layers)].step()
-        torch.cuda.synchronize()
-        g_all, graphs = None, []
-        if not args.no_graph:
-            g_all = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_all, stream=stream):
-                for L_ in layers:
-                    L_.step()
-            for L_ in layers:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    L_.step()
-                graphs.append(g)
-            torch.cuda.synchronize()
-            for i in range(max(1, args.warmup // len(layers))):
-                g_all.replay()
-        torch.cuda.synchronize()
-
-        # timed region: exactly K steps
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter()
-        e0.record(stream)
-        if g_all is not None:
-            for _ in range(args.steps // len(layers)):
-                g_all.replay()
-            for i in range(args.steps % len(layers)):
-                graphs[i].replay()
-        else:
-            for i in range(args.steps):
-                layers[i % len(layers)].step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter() - t_wall
-        ms = e0.elapsed_time(e1) / args.steps
-        tokens_per_step = wl.n_seqs
-        value = tokens_per_step / (ms * 1e-3)
-        log(f"step {ms * 1e3:.1f} us (wall {t_wall / args.steps * 1e6:.1f} us), {value:.0f} tokens/s")
-
-        # per-operation timing (eager launches, rotating sets) for the roofline
-        work = layers[0].work()
-        reps = max(64, args.steps // 4)
-        op_ms = {}
-        for name in work:
-            op_ms[name] = time_fn(lambda L_: getattr(L_, name)(), layers, reps, stream)
-        kernels = {}
-        for name, (b, f) in work.items():
-            t = op_ms[name] * 1e-3
-            kernels[name] = {"us": round(op_ms[name] * 1e3, 2), "GB/s": round(b / t / 1e9, 1),
-                             "TFLOP/s": round(f / t / 1e12, 2), "bytes": int(b), "flops": int(f)}
-        dom = max(op_ms, key=op_ms.get)
-        db, df = work[dom]
-        dt = op_ms[dom] * 1e-3
+        main_res, layers = run_decode(wl, dev, stream, args.steps, args.warmup, graph=not args.no_graph)
         traffic = load_traffic(wl)
-        t_op = traffic["ops"].get(dom) if traffic else None
-        roof = {"kernel": dom, "kernels": OP_KERNELS[dom], "bound": "hbm", "achieved": round(db / dt / 1e9, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(db / dt / 1e9 / HBM_PEAK_GBS, 4),
-                "traffic": t_op["bytes_per_launch"] if t_op else None,
-                "bytes_per_launch": int(db), "avg_launch_us": round(op_ms[dom] * 1e3, 2)}
-        step_bytes = sum(b for b, _ in work.values())
-        step_flops = sum(f for _, f in work.values())
-        log(f"per-op: {json.dumps(kernels)}")
+        t_op = traffic["ops"].get(main_res["roofline"]["kernel"]) if traffic else None
+        main_res["roofline"]["traffic"] = t_op["bytes_per_launch"] if t_op else None
+        cpu = None
+        if not args.no_cpu:
+            log("timing the oracle on the host (bounded sample, process pool)...")
+            cpu = cpu_baseline(layers)
+            log(f"oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} cores")
+        del layers
+        torch.cuda.empty_cache()
+        sweep = prefill = None
+        if not args.no_sweep:
+            sweep = run_sweep(dev, stream, args.sweep_steps, max(8, args.warmup // 4))
+            prefill = run_prefill(dev, stream)
         achievable = None
         if not args.no_probe:
             achievable = achievable_peaks(stream)
             log(f"achievable on this device: {json.dumps(achievable)}")
 
-        cpu = None
-        if not args.no_cpu:
-            log("timing the oracle on the host (bounded sample)...")
-            cpu = cpu_baseline(layers[0])
-            log(f"oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} cores")
-
     res = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": main_res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.n_seqs, "ctx": f"log-uniform [{wl.ctx_lo}, {wl.ctx_hi}] "
-                   f"seed {wl.seed}", "n_h": wl.n_h, "d_c": wl.d_c, "ratio": wl.ratio, "k": wl.k,
-                   "n_win": wl.n_win, "indexer": f"{wl.n_I}x{wl.d_I}" if wl.kind == "csa_decode" else None,
-                   "layer_sets": args.sets, "graph": not args.no_graph},
-        "roofline": roof,
-        "step_hbm_GBs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
-        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "step_mfma_frac": round(step_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-        "kernels": kernels,
+                   f"seed {wl.seed}", "n_h": wl.n_h, "d_c": wl.d_c, "ratio": wl.ratio,
+                   "k": wl.k if wl.kind == "csa_decode" else None, "n_win": wl.n_win,
+                   "indexer": f"{wl.n_I}x{wl.d_I} bf16" if wl.kind == "csa_decode" else None,
+                   "layer_sets": main_res["layer_sets"], "graph": not args.no_graph},
+        "step_time": main_res["step_time"],
+        "roofline": main_res["roofline"],
+        "step_hbm_GBs": main_res["step_hbm_GBs"],
+        "step_hbm_frac": main_res["step_hbm_frac"],
+        "kernels": main_res["kernels"],
+        "sweep": sweep,
+        "prefill": prefill,
         "achievable": achievable,
         "cpu_baseline": cpu,
     }

@@ -55,3 +55,23 @@ STRESS_BF16 = Workload("stress_bf16_64x1k-1m", "stress", "bf16", n_seqs=64, k=10
                        ctx_lo=1024, ctx_hi=1 << 20, q_lo=1, q_hi=16)
 
 ALL = [TINY_CSA_F32, CSA_DECODE_BF16, HCA_DECODE_1M_BF16, CSA_PREFILL_MIXED, STRESS_BF16]
+
+
+def _fixed_ctx(base, name, L, **kw):
+    from dataclasses import replace
+    return replace(base, name=name, ctx_lo=L, ctx_hi=L, **kw)
+
+
+# The decode sweep over the metric's context range (batch 32, one new token per sequence,
+# every sequence at the same context length): CSA at 64K / 256K / 1M with k = 512 and the
+# indexer keys and queries in bf16 or MXFP4 ("DeepSeek-V4 深度分析报告" Figure 2: the
+# indexer in FP4), and HCA at the same lengths (batch 4, like the 1M workload).
+CSA_DECODE_SWEEP = [_fixed_ctx(CSA_DECODE_BF16, f"csa_decode_32x{tag}", L, seed=11 + i)
+                    for i, (tag, L) in enumerate((("64k", 1 << 16), ("256k", 1 << 18), ("1m", 1 << 20)))]
+HCA_DECODE_SWEEP = [_fixed_ctx(HCA_DECODE_1M_BF16, f"hca_decode_4x{tag}", L, seed=21 + i)
+                    for i, (tag, L) in enumerate((("64k", 1 << 16), ("256k", 1 << 18)))] + [HCA_DECODE_1M_BF16]
+
+# V4-Pro's top-k (k = 1024) on the CSA decode batch: 32 sequences, contexts log-uniform in
+# [8K, 64K], one new token each ("DeepSeek-V4 深度分析报告" section 2.1: k = 1024 for Pro).
+CSA_DECODE_K1024 = Workload("csa_decode_bf16_k1024_32x8k-64k", "csa_decode", "bf16", n_seqs=32, k=1024, seed=1,
+                            ctx_lo=8192, ctx_hi=65536)

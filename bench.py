@@ -162,7 +162,9 @@ class DecodeLayer:
         ops.csa_index_score(self.seqs, self.R["qI"], self.w, self.wl.n_I, self.R["kI"], self.wl.ratio, self._score())
 
     def topk(self):
-        ops.csa_topk(self.seqs, self._score(), self.wl.ratio, self.wl.k, self.idx)
+        # the selection's candidate lists follow the scores in the workspace (as in csa_index_topk)
+        n = self.wl.n_seqs * self.ws_score_stride
+        ops.csa_topk(self.seqs, self._score(), self.wl.ratio, self.wl.k, self.idx, ws=self.ws[n:])
 
     def attend(self):
         wl = self.wl

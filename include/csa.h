@@ -143,12 +143,17 @@ int csa_index_score(const csa_seqs* seqs, const csa_rows* qI, const float* w, in
  * score[t, 0..V-1]: the k largest, equal scores ranked by the lower index (+0 and -0
  * compare equal), written to idx[t, 0..k-1] in ascending index order; when V <= k all V
  * are selected and the rest of the row is -1.  Exact and deterministic.
- *   k 1..4096;  idx device int32 [total_q, k] */
+ *   k 1..4096;  idx device int32 [total_q, k]
+ *   ws/ws_bytes  optional scratch.  With at least csa_workspace_bytes(CSA_OP_TOPK, ...)
+ *         bytes (nonzero when floor(max_ctx/ratio) > 32768 and k allows), rows of more than
+ *         32768 candidates are cut into slices selected by separate workgroups and merged;
+ *         otherwise one workgroup per token walks the row.  The selection is the same. */
 int csa_topk(const csa_seqs* seqs, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
-             void* stream);
+             void* ws, size_t ws_bytes, void* stream);
 
-/* csa_index_topk -- csa_index_score into the workspace followed by csa_topk.
- * ws_bytes must be >= csa_workspace_bytes(CSA_OP_INDEX_TOPK, ...). */
+/* csa_index_topk -- csa_index_score into the workspace followed by csa_topk (its
+ * candidate lists after the scores).  ws_bytes must be >=
+ * csa_workspace_bytes(CSA_OP_INDEX_TOPK, ...). */
 int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
                    int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
@@ -156,8 +161,9 @@ int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
  * the same computation and the same idx bits, with the scores kept in a fixed scratch
  * array of the library instead of a caller workspace.  Allocates and frees nothing.
- *   Limit: total_q * floor(max_ctx/ratio) * 4 bytes must not exceed 64 MiB (e.g. 64 query
- *   tokens at 1M context with ratio 4); larger calls return CSA_EWORKSPACE unlaunched.
+ *   Limit: csa_workspace_bytes(CSA_OP_INDEX_TOPK, ...) must not exceed 64 MiB (e.g. 60 query
+ *   tokens at 1M context with ratio 4 and k = 512); larger calls return CSA_EWORKSPACE
+ *   unlaunched.
  *   The scratch belongs to the calling thread's current device (one 64 MiB array per GPU,
  *   held until the process ends); `stream` must belong to that device.  Every call on a
  *   GPU shares that GPU's array: calls that overlap on one GPU (different streams or
@@ -207,10 +213,12 @@ int hca_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows*
                float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace sizing (host only; reads only the host scalars of `seqs`). */
-enum { CSA_OP_INDEX_TOPK = 1, CSA_OP_CSA_ATTEND = 2, CSA_OP_HCA_ATTEND = 3 };
+enum { CSA_OP_INDEX_TOPK = 1, CSA_OP_CSA_ATTEND = 2, CSA_OP_HCA_ATTEND = 3, CSA_OP_TOPK = 4 };
 /* op CSA_OP_INDEX_TOPK: ratio, k used; CSA_OP_CSA_ATTEND: n_h, dim, k, n_win used;
- * CSA_OP_HCA_ATTEND: n_h, dim, ratio, n_win used.  Returns the bytes the call uses: for
- * CSA_OP_INDEX_TOPK total_q * floor(max_ctx/ratio) float32 scores (mandatory); for the
+ * CSA_OP_HCA_ATTEND: n_h, dim, ratio, n_win used; CSA_OP_TOPK: ratio, k used.  Returns
+ * the bytes the call uses: for CSA_OP_INDEX_TOPK total_q * floor(max_ctx/ratio) float32
+ * scores plus the selection's candidate lists (mandatory); for CSA_OP_TOPK the candidate
+ * lists of the sliced selection (optional, see csa_topk); for the
  * attention ops the chunk partials when the call would split its key lists (see
  * csa_attend), else 0.  Returns 0 for an invalid op. */
 size_t csa_workspace_bytes(int op, const csa_seqs* seqs, int n_h, int dim, int k, int ratio, int n_win);

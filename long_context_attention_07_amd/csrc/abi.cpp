@@ -216,7 +216,10 @@ int index_topk_launch(const csa_seqs* seqs, const csa_rows* qI, const float* w, 
   hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio, score, stride,
                                          max_vis, seqs->max_q, s);
   if (e != hipSuccess) return hip_status(e, "index_topk score launch");
-  e = csa::launch_topk(dev_seqs(seqs), score, stride, ratio, k, idx, max_vis, seqs->max_q, s);
+  // the selection's candidate lists follow the scores in the workspace
+  const size_t cand = csa::topk_workspace_bytes(seqs->total_q, max_vis, k);
+  e = csa::launch_topk(dev_seqs(seqs), score, stride, ratio, k, idx, max_vis, seqs->max_q,
+                       score + (size_t)seqs->total_q * stride, cand, s);
   return hip_status(e, "index_topk select launch");
 }
 
@@ -312,7 +315,7 @@ int csa_index_score(const csa_seqs* seqs, const csa_rows* qI, const float* w, in
 }
 
 int csa_topk(const csa_seqs* seqs, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
-             void* stream) {
+             void* ws, size_t ws_bytes, void* stream) {
   int st;
   if ((st = check_seqs(seqs))) return st;
   if (!score || !idx) return fail(CSA_EINVAL, "score/idx: null pointer");
@@ -322,8 +325,8 @@ int csa_topk(const csa_seqs* seqs, const float* score, int64_t score_stride, int
   if (score_stride < max_vis)
     return fail(CSA_EINVAL, "score_stride %lld < floor(max_ctx/ratio) = %d", (long long)score_stride, max_vis);
   if (seqs->total_q == 0) return ok();
-  hipError_t e = csa::launch_topk(dev_seqs(seqs), score, score_stride, ratio, k, idx, max_vis, seqs->max_q,
-                                  static_cast<hipStream_t>(stream));
+  hipError_t e = csa::launch_topk(dev_seqs(seqs), score, score_stride, ratio, k, idx, max_vis, seqs->max_q, ws,
+                                  ws ? ws_bytes : 0, static_cast<hipStream_t>(stream));
   return hip_status(e, "csa_topk launch");
 }
 
@@ -350,7 +353,7 @@ int csa_index_topk_noalloc(const csa_seqs* seqs, const csa_rows* qI, const float
   const size_t need = csa_workspace_bytes(CSA_OP_INDEX_TOPK, seqs, 0, 0, k, ratio, 0);
   if (need > kNoallocScratchBytes)
     return fail(CSA_EWORKSPACE,
-                "csa_index_topk_noalloc needs %zu bytes of scores (total_q * floor(max_ctx/ratio) * 4), more than "
+                "csa_index_topk_noalloc needs %zu bytes of scores and candidates, more than "
                 "its fixed %zu-byte scratch",
                 need, kNoallocScratchBytes);
   if (seqs->total_q == 0) return ok();
@@ -399,9 +402,14 @@ size_t csa_workspace_bytes(int op, const csa_seqs* seqs, int n_h, int dim, int k
   if (!seqs || seqs->total_q <= 0) return 0;
   switch (op) {
     case CSA_OP_INDEX_TOPK: {
-      if (ratio < 1) return 0;
+      if (ratio < 1 || k < 1) return 0;
       const int64_t max_vis = seqs->max_ctx / ratio;
-      return (size_t)seqs->total_q * (size_t)(max_vis > 0 ? max_vis : 1) * sizeof(float);
+      return (size_t)seqs->total_q * (size_t)(max_vis > 0 ? max_vis : 1) * sizeof(float) +
+             csa::topk_workspace_bytes(seqs->total_q, (int)max_vis, k);
+    }
+    case CSA_OP_TOPK: {
+      if (ratio < 1 || k < 1) return 0;
+      return csa::topk_workspace_bytes(seqs->total_q, seqs->max_ctx / ratio, k);
     }
     case CSA_OP_CSA_ATTEND:
     case CSA_OP_HCA_ATTEND: {

@@ -11,8 +11,9 @@
 // lowest-index keys == T, writing indices in ascending order.  The selection is a
 // function of the token's scores alone.  Up to 32768 candidates the keys stay in
 // registers (8, 16 or 32 consecutive keys per thread), each pass has its own LDS histogram
-// and the digit searches and the compaction offsets use DPP wave scans; longer lists
-// re-read the scores from memory every pass.
+// and the digit searches and the compaction offsets use DPP wave scans.  Longer lists run
+// in two stages over several workgroups when a workspace is given (below), else one
+// workgroup re-reads the scores from memory every pass.
 
 #include "common.cuh"
 #include "kernels.h"
@@ -235,10 +236,12 @@ __device__ __forceinline__ void topk_load_keys(const float* __restrict__ src, in
   }
 }
 
-// The selection over keys held as above; keys at n and beyond take no part.
-template <int NPT>
-__device__ void topk_select_keys(const uint32_t (&key)[NPT], int n, int k, int32_t* __restrict__ out,
-                                 TopkRegLds& sh) {
+// The selection over keys held as above; keys at n and beyond take no part.  Every kept
+// key j of this thread is handed to emit(pos, j, key[j]), pos being its rank among the
+// kept keys in ascending position order (0 .. min(k, n) - 1).
+template <int NPT, class Emit>
+__device__ __forceinline__ void topk_select_keys_emit(const uint32_t (&key)[NPT], int n, int k, TopkRegLds& sh,
+                                                      Emit emit) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int i0 = NPT * tid;
   for (int b = tid; b < 4096; b += kTopkThreads) {
@@ -310,8 +313,15 @@ __device__ void topk_select_keys(const uint32_t (&key)[NPT], int n, int k, int32
       take = eq_rank < remaining;
       ++eq_rank;
     }
-    if (take) out[pos++] = i0 + j;
+    if (take) emit(pos++, j, key[j]);
   }
+}
+
+template <int NPT>
+__device__ void topk_select_keys(const uint32_t (&key)[NPT], int n, int k, int32_t* __restrict__ out,
+                                 TopkRegLds& sh) {
+  const int i0 = NPT * (int)threadIdx.x;
+  topk_select_keys_emit<NPT>(key, n, k, sh, [&](uint32_t pos, int j, uint32_t) { out[pos] = i0 + j; });
 }
 
 template <int NPT>
@@ -370,9 +380,154 @@ __global__ void __launch_bounds__(kTopkThreads) topk_decode_kernel(SeqsDev S, co
   topk_select_keys<NPT>(key, (int)V, k, out, rsh);
 }
 
+// ---------------------------------------------------------------------------------------
+// Long rows on several workgroups.  A row of V > 32768 candidates is cut into slices of SL
+// consecutive entries (SL = 16384 or 32768, fixed per launch from the longest row and k).
+// Stage one: one workgroup per (token, slice) keeps the slice's exact top-k (or all of its
+// entries when it has no more than k), as (key, entry) pairs in ascending entry order,
+// padded with key 0 (below every key of a real score) to k pairs.  Every entry of the
+// row's top-k is in the top-k of its own slice: fewer than k entries beat it in the row,
+// so fewer than k beat it in the slice, under the same order (score, then lower index).
+// Stage two: one workgroup per token selects the top-k among the n_slices * k pairs, which
+// lie in ascending entry order, so the same selection (ties to the lower position) keeps
+// the row's own set and writes it in ascending order.  Rows of one slice are selected
+// completely in stage one.  The result is the exact selection, whatever the slicing.
+
+constexpr int kTopkRegMax = 32 * kTopkThreads;  // longest row the one-workgroup path holds in registers
+
+template <int NPT>
+__global__ void __launch_bounds__(kTopkThreads) topk_slice_kernel(SeqsDev S, const float* __restrict__ score,
+                                                                  int64_t score_stride, int ratio, int k,
+                                                                  int32_t* __restrict__ idx,
+                                                                  uint32_t* __restrict__ cand_key,
+                                                                  int32_t* __restrict__ cand_idx, int n_slices) {
+  __shared__ TopkRegLds rsh;
+  constexpr int SL = NPT * kTopkThreads;
+  const int t = blockIdx.x / n_slices, s = blockIdx.x % n_slices;
+  const TokenCtx ctx = token_ctx(S, t);
+  const int64_t V = (ctx.p + 1) / ratio;
+  const int ns = (int)((V + SL - 1) / SL);
+  const float* row = score + (int64_t)t * score_stride;
+  if (ns <= 1) {  // the whole row is one slice: the final selection
+    if (s != 0) return;
+    int32_t* out = idx + (int64_t)t * k;
+    if (V <= k) {
+      for (int i = threadIdx.x; i < k; i += kTopkThreads) out[i] = (i < V) ? i : -1;
+      return;
+    }
+    topk_select_reg<NPT>(row, (int)V, k, out, rsh);
+    return;
+  }
+  if (s >= ns) return;
+  const int64_t base = (int64_t)s * SL;
+  const int len = (int)min((int64_t)SL, V - base);
+  const float* src = row + base;
+  uint32_t* ck = cand_key + ((int64_t)t * n_slices + s) * k;
+  int32_t* ci = cand_idx + ((int64_t)t * n_slices + s) * k;
+  if (len <= k) {
+    for (int i = threadIdx.x; i < k; i += kTopkThreads) {
+      ck[i] = i < len ? score_key(src[i]) : 0u;
+      ci[i] = i < len ? (int32_t)(base + i) : -1;
+    }
+    return;
+  }
+  uint32_t key[NPT];
+  topk_load_keys<NPT>(src, len, key);
+  const int i0 = NPT * (int)threadIdx.x;
+  topk_select_keys_emit<NPT>(key, len, k, rsh, [&](uint32_t pos, int j, uint32_t kv) {
+    ck[pos] = kv;
+    ci[pos] = (int32_t)(base + i0 + j);
+  });
+}
+
+// Thread tid's pairs NPT tid .. NPT tid + NPT - 1 of a token's candidates, those below lim.
+template <int NPT>
+__device__ __forceinline__ void topk_load_u32(const uint32_t* __restrict__ src, int lim, uint32_t (&key)[NPT]) {
+  const int i0 = NPT * (int)threadIdx.x;
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) == 0 && i0 + NPT <= lim) {
+#pragma unroll
+    for (int q = 0; q < NPT / 4; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(src + i0)[q];
+      key[4 * q] = v.x;
+      key[4 * q + 1] = v.y;
+      key[4 * q + 2] = v.z;
+      key[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) key[j] = i0 + j < lim ? src[i0 + j] : 0u;
+  }
+}
+
+template <int NPT>
+__global__ void __launch_bounds__(kTopkThreads) topk_merge_kernel(SeqsDev S, int ratio, int k, int SL,
+                                                                  int32_t* __restrict__ idx,
+                                                                  const uint32_t* __restrict__ cand_key,
+                                                                  const int32_t* __restrict__ cand_idx, int n_slices) {
+  __shared__ TopkRegLds rsh;
+  const int t = blockIdx.x;
+  const TokenCtx ctx = token_ctx(S, t);
+  const int64_t V = (ctx.p + 1) / ratio;
+  const int ns = (int)((V + SL - 1) / SL);
+  if (ns <= 1) return;  // selected completely by the slice kernel
+  const int n = ns * k;
+  const uint32_t* ck = cand_key + (int64_t)t * n_slices * k;
+  const int32_t* ci = cand_idx + (int64_t)t * n_slices * k;
+  uint32_t key[NPT];
+  topk_load_u32<NPT>(ck, n, key);
+  int32_t* out = idx + (int64_t)t * k;
+  const int i0 = NPT * (int)threadIdx.x;
+  topk_select_keys_emit<NPT>(key, n, k, rsh, [&](uint32_t pos, int j, uint32_t) { out[pos] = ci[i0 + j]; });
+}
+
+// Slice length of the two-stage path for rows up to max_vis and this k, or 0 when the
+// one-workgroup path runs: rows that fit in registers, or candidate lists that would not.
+static int topk_slice_len(int max_vis, int k) {
+  if (max_vis <= kTopkRegMax) return 0;
+  for (int SL : {16 * kTopkThreads, 32 * kTopkThreads}) {
+    const int64_t ns = ((int64_t)max_vis + SL - 1) / SL;
+    if (ns * k <= kTopkRegMax) return SL;
+  }
+  return 0;
+}
+
+size_t topk_workspace_bytes(int total_q, int max_vis, int k) {
+  const int SL = topk_slice_len(max_vis, k);
+  if (SL == 0 || total_q <= 0) return 0;
+  const int64_t ns = ((int64_t)max_vis + SL - 1) / SL;
+  return (size_t)total_q * (size_t)ns * (size_t)k * (sizeof(uint32_t) + sizeof(int32_t));
+}
+
 hipError_t launch_topk(const SeqsDev& S, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
-                       int max_vis, int max_q, hipStream_t stream) {
+                       int max_vis, int max_q, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (S.total_q == 0) return hipSuccess;
+  const size_t need = topk_workspace_bytes(S.total_q, max_vis, k);
+  if (need > 0 && ws != nullptr && ws_bytes >= need) {
+    const int SL = topk_slice_len(max_vis, k);
+    const int ns = (int)(((int64_t)max_vis + SL - 1) / SL);
+    uint32_t* ck = static_cast<uint32_t*>(ws);
+    int32_t* ci = reinterpret_cast<int32_t*>(ck + (size_t)S.total_q * ns * k);
+    const dim3 grid1((unsigned)((int64_t)S.total_q * ns));
+    if (SL == 16 * kTopkThreads)
+      hipLaunchKernelGGL(topk_slice_kernel<16>, grid1, dim3(kTopkThreads), 0, stream, S, score, score_stride, ratio, k,
+                         idx, ck, ci, ns);
+    else
+      hipLaunchKernelGGL(topk_slice_kernel<32>, grid1, dim3(kTopkThreads), 0, stream, S, score, score_stride, ratio, k,
+                         idx, ck, ci, ns);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t cands = (int64_t)ns * k;
+    const dim3 grid2((unsigned)S.total_q);
+    if (cands <= 8 * kTopkThreads)
+      hipLaunchKernelGGL(topk_merge_kernel<8>, grid2, dim3(kTopkThreads), 0, stream, S, ratio, k, SL, idx, ck, ci, ns);
+    else if (cands <= 16 * kTopkThreads)
+      hipLaunchKernelGGL(topk_merge_kernel<16>, grid2, dim3(kTopkThreads), 0, stream, S, ratio, k, SL, idx, ck, ci,
+                         ns);
+    else
+      hipLaunchKernelGGL(topk_merge_kernel<32>, grid2, dim3(kTopkThreads), 0, stream, S, ratio, k, SL, idx, ck, ci,
+                         ns);
+    return hipGetLastError();
+  }
   if (max_q == 1 && max_vis > k && max_vis <= 32 * kTopkThreads) {
     if (max_vis <= 8 * kTopkThreads)
       hipLaunchKernelGGL(topk_decode_kernel<8>, dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score, score_stride,

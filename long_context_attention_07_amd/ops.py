@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 F32, BF16, KV_SPLIT, MXFP4 = 0, 1, 2, 3
 KV_SPLIT_BF16_DIMS = 64
-OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND = 1, 2, 3
+OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND, OP_TOPK = 1, 2, 3, 4
 
 EXPORTS = ("csa_compress", "csa_compress2", "csa_index_score", "csa_topk", "csa_index_topk", "csa_index_topk_noalloc",
            "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_strerror", "csa_last_error", "csa_version")
@@ -55,7 +55,7 @@ def lib():
         L.csa_compress2.argtypes = [P(csa_seqs), i32, i32, f64, P(csa_rows), P(csa_rows), vp, i32, P(csa_rows),
                                     P(csa_rows), P(csa_rows), vp, i32, P(csa_rows), vp]
         L.csa_index_score.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, vp, i64, vp]
-        L.csa_topk.argtypes = [P(csa_seqs), vp, i64, i32, i32, vp, vp]
+        L.csa_topk.argtypes = [P(csa_seqs), vp, i64, i32, i32, vp, vp, sz, vp]
         L.csa_index_topk.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, i32, vp, vp, sz, vp]
         L.csa_index_topk_noalloc.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, i32, vp, vp]
         L.csa_attend.argtypes = [P(csa_seqs), P(csa_rows), i32, P(csa_rows), vp, i32, P(csa_rows), i32, vp, f32, i32,
@@ -169,9 +169,10 @@ def csa_index_score(seqs, qI, w, n_I, kI, ratio, score, stream=None):
                                  _ptr(score), score.stride(0), _stream(stream)), "csa_index_score")
 
 
-def csa_topk(seqs, score, ratio, k, idx, stream=None):
-    _check(lib().csa_topk(ctypes.byref(seqs.c), _ptr(score), score.stride(0), ratio, k, _ptr(idx), _stream(stream)),
-           "csa_topk")
+def csa_topk(seqs, score, ratio, k, idx, ws=None, stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().csa_topk(ctypes.byref(seqs.c), _ptr(score), score.stride(0), ratio, k, _ptr(idx), _ptr(ws), nbytes,
+                          _stream(stream)), "csa_topk")
 
 
 def csa_index_topk(seqs, qI, w, n_I, kI, ratio, k, idx, ws=None, stream=None):

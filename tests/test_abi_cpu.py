@@ -113,7 +113,7 @@ def test_compress_and_index_validation_errors(lib):
     assert "score_stride" in ops.csa_last_error()
     i96 = _rows(dim=96)
     assert lib.csa_index_score(P(s), P(i96), w, 64, P(i96), 4, score, 100, None) == -2
-    assert lib.csa_topk(P(s), score, 100, 4, 0, score, None) == -1
+    assert lib.csa_topk(P(s), score, 100, 4, 0, score, None, 0, None) == -1
     assert lib.csa_index_topk(P(s), P(qI), w, 64, P(qI), 4, 16, score, None, 0, None) == -3
     assert "workspace" in ops.csa_last_error()
 
@@ -121,7 +121,7 @@ def test_compress_and_index_validation_errors(lib):
 def test_workspace_sizes(lib):
     s = _seqs(n_seqs=4, total_q=4, max_q=1, max_ctx=1 << 20)
     P = ctypes.byref
-    assert lib.csa_workspace_bytes(ops.OP_INDEX_TOPK, P(s), 0, 0, 512, 4, 0) == 4 * (1 << 18) * 4
+    assert lib.csa_workspace_bytes(ops.OP_INDEX_TOPK, P(s), 0, 0, 512, 4, 0) == 4 * (1 << 18) * 4 + 4 * 16 * 512 * 8
     assert lib.csa_workspace_bytes(99, P(s), 64, 512, 0, 128, 128) == 0
     hca = lib.csa_workspace_bytes(ops.OP_HCA_ATTEND, P(s), 64, 512, 0, 128, 128)
     # 4 tokens x 15 chunks (8192 entries + 128 window slots in 576-slot chunks) x 64 heads x
@@ -172,3 +172,19 @@ def test_noalloc_validation_before_any_device_call(lib):
     assert "scratch" in ops.csa_last_error()
     assert lib.csa_index_topk_noalloc(P(s), P(qI), w, 64, P(qI), 4, 0, idx, None) == -1
     assert lib.csa_index_topk_noalloc(P(s), P(qI), w, 64, P(qI), 4, 64, None, None) == -1
+
+
+def test_topk_workspace_sizes(lib):
+    """The sliced selection's candidate lists: rows above 32768 candidates, slices of 16384
+    (or 32768 when k would overflow the merge), k (key, index) pairs of 8 bytes per slice;
+    none for rows that fit one workgroup's registers."""
+    P = ctypes.byref
+    s = _seqs(n_seqs=32, total_q=32, max_q=1, max_ctx=1 << 20)
+    assert lib.csa_workspace_bytes(ops.OP_TOPK, P(s), 0, 0, 512, 4, 0) == 32 * 16 * 512 * 8
+    assert lib.csa_workspace_bytes(ops.OP_TOPK, P(s), 0, 0, 4096, 4, 0) == 32 * 8 * 4096 * 8
+    assert lib.csa_workspace_bytes(ops.OP_INDEX_TOPK, P(s), 0, 0, 512, 4, 0) == 32 * (1 << 18) * 4 + 32 * 16 * 512 * 8
+    c2 = _seqs(n_seqs=32, total_q=32, max_q=1, max_ctx=65536)
+    assert lib.csa_workspace_bytes(ops.OP_TOPK, P(c2), 0, 0, 512, 4, 0) == 0
+    # 1M candidates per row with k = 4096 would need 32 slices of 32768: one workgroup instead
+    big = _seqs(n_seqs=1, total_q=1, max_q=1, max_ctx=1 << 20)
+    assert lib.csa_workspace_bytes(ops.OP_TOPK, P(big), 0, 0, 4096, 1, 0) == 0

@@ -271,6 +271,48 @@ def test_topk_exact_on_identical_scores(keep):
                 assert list(got[r]) == list(ref), f"token {r} (V={L}, k={k}, row stride {st.stride(0)})"
 
 
+@pytest.mark.parametrize("k", [1, 512, 1024, 4096])
+def test_topk_sliced_rows_exact(k):
+    """Rows longer than 32768 candidates on several workgroups (slices, then a merge):
+    exact against the oracle's selection on the same float32 scores, with heavy ties, a row
+    whose every score ties, the k largest all in one slice, +-0, a row with a ragged last
+    slice shorter than k, and rows that fit one slice next to them; the one-workgroup
+    path (no workspace) gives the same indices."""
+    g = np.random.default_rng(31 + k)
+    ratio = 1
+    ctx = [262144, 40000, 32769, 98304 + 7, 65536 + k // 2, 20000, 3000]
+    ob, sq, _, _ = make_batch([1] * len(ctx), ctx, ratio)
+    stride = max(ctx) + 3
+    s = np.full((len(ctx), stride), np.nan, dtype=np.float32)
+    for r, L in enumerate(ctx):
+        if r == 0:
+            s[r, :L] = np.round(g.standard_normal(L) * 3) / 4        # heavy exact ties
+        elif r == 1:
+            s[r, :L] = 0.5                                          # every score ties
+        elif r == 2:
+            s[r, :L] = g.standard_normal(L).astype(np.float32)
+            s[r, 16384:16384 + min(k, 16385)] += 100.0              # the k largest in one slice
+        elif r == 3:
+            s[r, :L] = np.where(g.random(L) < 0.5, 0.0, -0.0)       # only +-0
+            s[r, L - 3:L] = 1.0
+        else:
+            s[r, :L] = g.standard_normal(L).astype(np.float32)
+    st = torch.from_numpy(s).to(DEV)
+    ws_bytes = ops.csa_workspace_bytes(ops.OP_TOPK, sq, k=k, ratio=ratio)
+    assert ws_bytes > 0
+    ws = torch.empty(ws_bytes // 4 + 1, dtype=torch.float32, device=DEV)
+    got = torch.full((len(ctx), k), -7, dtype=torch.int32, device=DEV)
+    one = torch.full((len(ctx), k), -9, dtype=torch.int32, device=DEV)
+    ops.csa_topk(sq, st, ratio, k, got, ws=ws)
+    ops.csa_topk(sq, st, ratio, k, one)
+    torch.cuda.synchronize()
+    assert torch.equal(got, one), "sliced and one-workgroup selections differ"
+    gi = got.cpu().numpy()
+    for r, L in enumerate(ctx):
+        ref = topk_select(s[r, :L].astype(np.float64), k)
+        assert list(gi[r]) == list(ref), f"row {r} (V={L}, k={k})"
+
+
 @pytest.mark.parametrize("keep", ["all", "upto16384"])
 def test_topk_bin_taken_whole(keep):
     """Rows built so that the bin of the k-th key holds exactly the keys still needed after

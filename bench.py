@@ -11,8 +11,8 @@ new token each, 64 query heads sharing one 512-dim KV head (last 64 dims RoPE), 
 overlapped compression, a 64-head x 128-dim indexer, k = 512, window 128, bf16.
 
 The same JSON line carries, under `sweep`, the decode step over the metric's whole context
-range: CSA at 64K / 256K / 1M (batch 32, k = 512) with bf16 and with MXFP4 indexer keys
-and queries, CSA with k = 1024 (batch 32, 8K-64K), and HCA at 64K / 256K / 1M (batch 4);
+range: CSA at 64K / 256K / 1M (batch 32, k = 512) with bf16, MXFP4 and fp8 (1x128)
+indexer keys and queries, CSA with k = 1024 (batch 32, 8K-64K), and HCA at 64K / 256K / 1M (batch 4);
 each with tokens/s, median / p10 / p90 step times, the per-operation times and the
 roofline entry of its dominant operation.  Under `prefill` it carries the mixed-precision
 prefill (131072 causal tokens, fp8 1x128 KV rows with bf16 RoPE dims, MXFP4 indexer,
@@ -88,6 +88,15 @@ def mxfp4_rows(x):
     return ops.Rows(packed, ops.MXFP4, d, scales)
 
 
+def fp8_b128_rows(x):
+    """float32 [n, 128] on the GPU -> FP8 1x128 Rows: one fp32 scale (amax / 448) per row,
+    e4m3 codes of x / scale (input generation)."""
+    sc = x.abs().amax(dim=1) / 448.0
+    y = (x / torch.where(sc > 0, sc, torch.ones_like(sc))[:, None]).clamp(-448.0, 448.0)
+    return ops.Rows(y.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), ops.FP8_B128, x.shape[1],
+                    sc[:, None].contiguous())
+
+
 def kv_split_rows(x):
     """float32 [n, 512] on the GPU -> KV split Rows: e4m3 codes of dims 0..447 with one fp32
     scale (amax / 448) per 128 dims, then the last 64 dims in bf16 (input generation)."""
@@ -110,7 +119,8 @@ def kv_split_rows(x):
 
 class DecodeLayer:
     """One layer's pools and per-step inputs for a decode batch (CSA or HCA).  `kfmt` is the
-    indexer format: "bf16", or "mxfp4" (keys, queries and the keys the compress step writes)."""
+    indexer format: "bf16", "mxfp4" or "fp8" (keys, queries and the keys the compress step
+    writes)."""
 
     def __init__(self, wl, lens, seed, dev, kfmt="bf16"):
         self.wl, self.kfmt = wl, kfmt
@@ -130,9 +140,10 @@ class DecodeLayer:
             for key in ("kI", "cI", "zI", "biasI", "qI", "w"):
                 setattr(self, key, x[key])
             self.R.update({k: ops.Rows.of(getattr(self, k)) for k in ("kI", "cI", "zI", "qI")})
-            if kfmt == "mxfp4":
-                self.R["kI"] = mxfp4_rows(self.kI.float())
-                self.R["qI"] = mxfp4_rows(self.qI.float())
+            if kfmt in ("mxfp4", "fp8"):
+                conv = mxfp4_rows if kfmt == "mxfp4" else fp8_b128_rows
+                self.R["kI"] = conv(self.kI.float())
+                self.R["qI"] = conv(self.qI.float())
                 del self.kI, self.qI
             self.idx = torch.empty((n, wl.k), dtype=torch.int32, device=dev)
             ws_i = ops.csa_workspace_bytes(ops.OP_INDEX_TOPK, self.seqs, k=wl.k, ratio=ratio)
@@ -196,7 +207,8 @@ class DecodeLayer:
         qo = n * nh * D * 2 * 2 + n * nh * 4
         if self.csa:
             dI, nI = wl.d_I, wl.n_I
-            key_b = dI * 2 if self.kfmt == "bf16" else dI // 2 + dI // 32   # stored key (+ e8m0 scales)
+            # stored key (+ its scales): bf16, MXFP4 (+ e8m0 per 32) or fp8 (+ one fp32)
+            key_b = {"bf16": dI * 2, "mxfp4": dI // 2 + dI // 32, "fp8": dI + 4}[self.kfmt]
             comp_b += new_ent.sum() * (src * 2 * dI * 2 + key_b)
             w["compress"] = (comp_b, 0.0)
             w["index_score"] = (float((V * (key_b + 4)).sum() + n * (nI * key_b + nI * 4)),
@@ -716,7 +728,7 @@ def run_prefill(dev, stream, steps=3, warmup=1):
 def run_sweep(dev, stream, steps, warmup):
     """The decode step over the metric's context range (see the module docstring)."""
     out = []
-    points = [(wl, "bf16") for wl in configs.CSA_DECODE_SWEEP] + [(wl, "mxfp4") for wl in configs.CSA_DECODE_SWEEP]
+    points = [(wl, f) for f in ("bf16", "mxfp4", "fp8") for wl in configs.CSA_DECODE_SWEEP]
     points += [(configs.CSA_DECODE_K1024, "bf16")] + [(wl, "bf16") for wl in configs.HCA_DECODE_SWEEP]
     for wl, kfmt in points:
         res, layers = run_decode(wl, dev, stream, steps, warmup, kfmt, max_sets=MAX_SETS)

@@ -56,8 +56,12 @@ typedef enum {
  *                128-dim block of the fp8 part; value = code * scale.
  *   CSA_MXFP4    OCP MXFP4: D/2 bytes of packed e2m1 codes (element 2i in the low nibble of
  *                byte i); `scales` holds D/32 e8m0 bytes per row (contiguous); value =
- *                e2m1 * 2^(e8m0 - 127). */
-typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_KV_SPLIT = 2, CSA_MXFP4 = 3 } csa_dtype;
+ *                e2m1 * 2^(e8m0 - 127).
+ *   CSA_FP8E4M3_B128  the FP8 1x128 scheme kept from DeepSeek-V3 (stuffyNLP review) over a
+ *                whole row: D OCP fp8 e4m3fn codes; `scales` holds ceil(D/128) float32 per
+ *                row (contiguous), one per 128-dim block; value = code * scale.  Used for
+ *                indexer queries and keys (the fp8 alternative to MXFP4). */
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_KV_SPLIT = 2, CSA_MXFP4 = 3, CSA_FP8E4M3_B128 = 4 } csa_dtype;
 
 #define CSA_KV_SPLIT_BF16_DIMS 64
 
@@ -103,9 +107,9 @@ typedef struct {
  *   z        gate-logit rows (F32 or BF16), dim D
  *   bias     device float32 [(1 + overlap) * ratio, D], row-major
  *   ratio    1..128;  overlap 0 or 1;  rope_dims even, 0..min(D, 128)
- *   entries  output rows (F32, BF16, KV_SPLIT or MXFP4), dim D.  KV_SPLIT output: scale =
- *            fp32(amax/448) per 128-dim block, code = e4m3fn RNE of value/scale, saturating;
- *            an all-zero block gets scale 0.  MXFP4 output: per 32 dims, exponent
+ *   entries  output rows (F32, BF16, KV_SPLIT, MXFP4 or FP8E4M3_B128), dim D.  KV_SPLIT and
+ *            FP8E4M3_B128 output: scale = fp32(amax/448) per 128-dim block of the fp8 dims,
+ *            code = e4m3fn RNE of value/scale, saturating; an all-zero block gets scale 0.  MXFP4 output: per 32 dims, exponent
  *            E = floor(log2 amax) - 2 clamped to [-127,127] (amax = 0 -> -127), element =
  *            e2m1 RNE of value/2^E saturating at +-6.
  * Precondition: the token pools hold every source position of the written entries. */
@@ -130,7 +134,10 @@ int csa_compress2(const csa_seqs* seqs, int ratio, int overlap, double rope_thet
  *     score[t, i] = sum_{h < n_I} w[t,h] * max(0, sum_d qI[t,h,d] * kI[entry_off[b]+i, d])
  * accumulated in float32 in an order fixed per (token, entry).  Columns i >= V(p) are not
  * written.
- *   qI      rows [total_q * n_I, d_I] (F32, BF16 or MXFP4); row t*n_I + h
+ *   qI      rows [total_q * n_I, d_I] (F32, BF16, MXFP4 or FP8E4M3_B128); row t*n_I + h.
+ *           For FP8E4M3_B128 with d_I = 128 the float32 sum is fixed as
+ *           s = scale_k * sum_h (w_h * scale_q[h]) * max(0, code_q[h] . code_k)
+ *           (the code dot product exact on the fp8 matrix cores; the scales are >= 0).
  *   w       device float32 [total_q, n_I]
  *   kI      entry pool rows (same dtype as qI), dim d_I
  *   score   device float32 [total_q, score_stride]; score_stride >= floor(max_ctx/ratio) */

@@ -42,6 +42,7 @@ int64_t row_bytes(int dtype, int dim) {
     case CSA_BF16: return 2LL * dim;
     case CSA_KV_SPLIT: return (int64_t)(dim - CSA_KV_SPLIT_BF16_DIMS) + 2LL * CSA_KV_SPLIT_BF16_DIMS;
     case CSA_MXFP4: return dim / 2;
+    case CSA_FP8E4M3_B128: return dim;
     default: return -1;
   }
 }
@@ -52,6 +53,7 @@ const char* dtype_name(int dt) {
     case CSA_BF16: return "BF16";
     case CSA_KV_SPLIT: return "KV_SPLIT";
     case CSA_MXFP4: return "MXFP4";
+    case CSA_FP8E4M3_B128: return "FP8E4M3_B128";
     default: return "?";
   }
 }
@@ -60,14 +62,14 @@ const char* dtype_name(int dt) {
 int check_rows(const csa_rows* r, const char* name, unsigned allowed) {
   if (!r) return fail(CSA_EINVAL, "%s: null descriptor", name);
   if (!r->data) return fail(CSA_EINVAL, "%s: null data pointer", name);
-  if (r->dtype < 0 || r->dtype > 3) return fail(CSA_EINVAL, "%s: unknown dtype %d", name, r->dtype);
+  if (r->dtype < 0 || r->dtype > 4) return fail(CSA_EINVAL, "%s: unknown dtype %d", name, r->dtype);
   if (!(allowed & (1u << r->dtype)))
     return fail(CSA_EUNSUPPORTED, "%s: dtype %s not supported here", name, dtype_name(r->dtype));
   if (r->dim < 32 || r->dim > csa::kMaxDim || r->dim % 32)
     return fail(CSA_EINVAL, "%s: dim %d must be a multiple of 32 in [32, 512]", name, r->dim);
   if (r->dtype == CSA_KV_SPLIT && r->dim < 2 * CSA_KV_SPLIT_BF16_DIMS)
     return fail(CSA_EINVAL, "%s: KV_SPLIT needs dim >= 128 (got %d)", name, r->dim);
-  if ((r->dtype == CSA_KV_SPLIT || r->dtype == CSA_MXFP4) && !r->scales)
+  if ((r->dtype == CSA_KV_SPLIT || r->dtype == CSA_MXFP4 || r->dtype == CSA_FP8E4M3_B128) && !r->scales)
     return fail(CSA_EINVAL, "%s: %s rows need a scales pointer", name, dtype_name(r->dtype));
   const int64_t rb = row_bytes(r->dtype, r->dim);
   if (r->row_stride != 0 && (r->row_stride < rb || r->row_stride % 16))
@@ -247,7 +249,8 @@ static int compress_checks(const csa_rows* c, const csa_rows* z, const float* bi
   int st;
   if ((st = check_rows(c, "c", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_KV_SPLIT)))) return st;
   if ((st = check_rows(z, "z", bit(CSA_F32) | bit(CSA_BF16)))) return st;
-  if ((st = check_rows(entries, "entries", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_KV_SPLIT) | bit(CSA_MXFP4))))
+  if ((st = check_rows(entries, "entries",
+                       bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_KV_SPLIT) | bit(CSA_MXFP4) | bit(CSA_FP8E4M3_B128))))
     return st;
   if (z->dim != c->dim || entries->dim != c->dim)
     return fail(CSA_EINVAL, "c/z/entries dims differ (%d/%d/%d)", c->dim, z->dim, entries->dim);
@@ -288,8 +291,9 @@ static int index_checks(const csa_seqs* seqs, const csa_rows* qI, const float* w
                         int ratio) {
   int st;
   if ((st = check_seqs(seqs))) return st;
-  if ((st = check_rows(qI, "qI", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_MXFP4)))) return st;
-  if ((st = check_rows(kI, "kI", bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_MXFP4)))) return st;
+  const unsigned ifmts = bit(CSA_F32) | bit(CSA_BF16) | bit(CSA_MXFP4) | bit(CSA_FP8E4M3_B128);
+  if ((st = check_rows(qI, "qI", ifmts))) return st;
+  if ((st = check_rows(kI, "kI", ifmts))) return st;
   if (qI->dtype != kI->dtype) return fail(CSA_EINVAL, "qI and kI must share a dtype");
   if (qI->dim != kI->dim) return fail(CSA_EINVAL, "qI dim %d != kI dim %d", qI->dim, kI->dim);
   if (kI->dim != 32 && kI->dim != 64 && kI->dim != 128)

@@ -13,7 +13,7 @@
 
 namespace csa {
 
-enum Dtype : int { DT_F32 = 0, DT_BF16 = 1, DT_KV_SPLIT = 2, DT_MXFP4 = 3 };
+enum Dtype : int { DT_F32 = 0, DT_BF16 = 1, DT_KV_SPLIT = 2, DT_MXFP4 = 3, DT_FP8_B128 = 4 };
 
 constexpr int kSplitBf16Dims = 64;   // trailing bf16 dims of a KV_SPLIT row
 constexpr int kKvBlock = 128;        // fp8 scale block
@@ -161,6 +161,10 @@ __device__ __forceinline__ float load_elem(const RowsDev& R, int64_t r, int d) {
         return e4m3_to_f32(row[d]) * s;
       }
       return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(row + dn)[d - dn]);
+    }
+    case DT_FP8_B128: {
+      const int nb = (R.dim + kKvBlock - 1) / kKvBlock;
+      return e4m3_to_f32(row[d]) * reinterpret_cast<const float*>(R.scales)[r * nb + d / kKvBlock];
     }
     default: {  // MXFP4
       uint32_t byte = row[d >> 1];

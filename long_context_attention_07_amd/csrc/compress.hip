@@ -9,10 +9,10 @@
 //
 // One workgroup of 256 threads per new entry (and per job: the KV rows and indexer keys of
 // a layer can be compressed in one launch); thread c owns channel pair (2c, 2c+1), so a
-// 64-lane wavefront owns exactly one 128-dim fp8 scale block and each 16-lane group one
-// 32-dim MXFP4 block.  Sources are walked in ascending position with an online softmax,
-// in float32; the block maxima use a fixed butterfly, so the result depends on the entry
-// alone.  Memory bound: the grid is (sequence, new entry), entries of a sequence being
+// 64-lane wavefront owns exactly one 128-dim fp8 scale block (KV split and FP8 1x128
+// rows) and each 16-lane group one 32-dim MXFP4 block.  Sources are walked in ascending
+// position with an online softmax, in float32; the block maxima use a fixed butterfly, so
+// the result depends on the entry alone.  Memory bound: the grid is (sequence, new entry), entries of a sequence being
 // consecutive workgroups.
 
 #include "common.cuh"
@@ -201,6 +201,25 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
       } else if (active) {
         uint32_t v = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
         reinterpret_cast<uint32_t*>(dst + dn)[pair - dn / 2] = v;
+      }
+      break;
+    }
+    case DT_FP8_B128: {
+      // every dim fp8; the wavefront covers channels [128w, 128w+128): one scale block
+      if constexpr (CW % 64 != 0) break;
+      float am = active ? fmaxf(fabsf(acc.x), fabsf(acc.y)) : 0.f;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+      if (active) {
+        const float sc = am / 448.0f;
+        uint32_t c0 = 0, c1 = 0;
+        if (sc > 0.f) {
+          c0 = f32_to_e4m3(acc.x / sc);
+          c1 = f32_to_e4m3(acc.y / sc);
+        }
+        reinterpret_cast<uint16_t*>(dst)[pair] = (uint16_t)(c0 | (c1 << 8));
+        const int nb = (D + kKvBlock - 1) / kKvBlock;
+        if (lane == 0) reinterpret_cast<float*>(out.scales)[orow * nb + (2 * pair) / kKvBlock] = sc;
       }
       break;
     }

@@ -1,7 +1,14 @@
-// Lightning-Indexer scores for MXFP4 queries and keys of 128 dims on the scaled matrix
-// cores ("DeepSeek-V4 深度分析报告" section 3.4: the indexer runs in FP4; section 2.1 and
-// Figure 2 "Lightning Indexer FP4 Precision"; the stuffyNLP review: MXFP4 indexer, the
-// indexer of DeepSeek-V3.2-Exp).  score[t, e] = sum_h w[t,h] * max(0, qI[t,h] . kI[e]).
+// Lightning-Indexer scores for MXFP4 (or fp8 1x128) queries and keys of 128 dims on the
+// scaled matrix cores ("DeepSeek-V4 深度分析报告" section 3.4: the indexer runs in FP4; section
+// 2.1 and Figure 2 "Lightning Indexer FP4 Precision"; the stuffyNLP review: MXFP4 indexer,
+// the indexer of DeepSeek-V3.2-Exp, and the FP8 1x128 scheme kept from DeepSeek-V3).
+// score[t, e] = sum_h w[t,h] * max(0, qI[t,h] . kI[e]).
+//
+// fp8 rows (CSA_FP8E4M3_B128, one fp32 scale per 128-dim row) run the same kernels with
+// e4m3 operands: a lane's operand is then 32 bytes (the 32 codes of its k-range), the
+// instruction's block scales are 1 and the fp32 row scales are applied outside the
+// product, which is exact on the codes: s = scale_k * sum_h (w_h scale_q,h) max(0, dot_h),
+// the weights w_h scale_q,h formed once per query row.
 //
 // One v_mfma_scale_f32_16x16x128_f8f6f4 (both operands e2m1, one e8m0 scale per 32 dims)
 // computes the full 128-dim dot products of 16 heads x 16 entries.  In its operand layout a
@@ -33,7 +40,54 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float mx_v4f;
 
 constexpr int kMxRange = 1024;  // entries per workgroup, one query row each
 constexpr int kMxPart = 32768;  // entries per workgroup, 8 query rows each
-constexpr int kMxFmtE2M1 = 4;   // operand format code of e2m1 in the scaled MFMA
+constexpr int kMxFmtE2M1 = 4;   // operand format codes of the scaled MFMA: e2m1
+constexpr int kMxFmtE4M3 = 0;   // and fp8 e4m3
+constexpr int kE8m0One = 127;   // e8m0 code of 2^0
+
+// Operand formats of the kernels: F8 = false for MXFP4 rows (16 bytes and one e8m0 scale
+// per lane and row), true for fp8 1x128 rows (32 bytes per lane, one fp32 scale per row).
+template <bool F8>
+struct MxOperand {
+  mx_v8i v;
+  uint32_t e8;  // MXFP4: the e8m0 scale of the lane's 32-element block
+  float sc;     // fp8: the row's fp32 scale
+};
+
+template <bool F8>
+__device__ __forceinline__ MxOperand<F8> load_operand(const RowsDev& R, int64_t row, int g) {
+  MxOperand<F8> o;
+  const uint8_t* p = R.data + row * R.stride;
+  if (F8) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p + 32 * g);
+    const uint4 b = *reinterpret_cast<const uint4*>(p + 32 * g + 16);
+    o.v = mx_v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    o.e8 = kE8m0One;
+    o.sc = reinterpret_cast<const float*>(R.scales)[row];
+  } else {
+    const uint4 a = *reinterpret_cast<const uint4*>(p + 16 * g);
+    o.v = mx_v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    o.e8 = (uint32_t)R.scales[row * (128 / kMxBlock) + g];
+    o.sc = 1.0f;
+  }
+  return o;
+}
+
+template <bool F8>
+__device__ __forceinline__ MxOperand<F8> zero_operand() {
+  MxOperand<F8> o;
+  o.v = mx_v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  o.e8 = kE8m0One;
+  o.sc = 0.f;
+  return o;
+}
+
+// Dot products of 16 heads x 16 entries over the 128 dims (codes for fp8).
+template <bool F8>
+__device__ __forceinline__ mx_v4f mx_dot(const MxOperand<F8>& q, const MxOperand<F8>& k) {
+  constexpr int fmt = F8 ? kMxFmtE4M3 : kMxFmtE2M1;
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.v, k.v, mx_v4f{0.f, 0.f, 0.f, 0.f}, fmt, fmt, 0,
+                                                          (int)q.e8, 0, (int)k.e8);
+}
 
 // max(x, 0) as one integer max of the bits (negative floats, -0 included, are negative
 // integers; +0 and positive floats keep their bits).
@@ -52,12 +106,7 @@ __device__ __forceinline__ float head_sum(const mx_v4f (&acc)[4], const float (&
   return (t[0] + t[1]) + (t[2] + t[3]);
 }
 
-__device__ __forceinline__ mx_v8i mx_operand(uint4 v) {
-  mx_v8i r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-  return r;
-}
-
-template <int QB>
+template <int QB, bool F8>
 __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
                                                              int n_I, RowsDev kI, int ratio, float* __restrict__ score,
                                                              int64_t score_stride, int n_parts) {
@@ -74,20 +123,17 @@ __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev 
     const int nq = min(t_end, ctx.q_end) - t0;
     const int64_t v_max = (ctx.p + nq) / ratio;  // visible entries of the run's last query
     if (e_begin < v_max) {
-      // query fragments and scales: head c16 + 16 hb, dims 32g .. 32g+31
-      uint4 qa[QB][4];
-      uint32_t qs[QB][4];
+      // query fragments: head c16 + 16 hb, dims 32g .. 32g+31
+      MxOperand<F8> qa[QB][4];
 #pragma unroll
       for (int i = 0; i < QB; ++i)
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
           const int h = c16 + 16 * hb;
           const bool on = i < nq && h < n_I;
-          const int64_t row = (int64_t)(t0 + (on ? i : 0)) * n_I + (on ? h : 0);
-          qa[i][hb] = on ? *reinterpret_cast<const uint4*>(qI.data + row * qI.stride + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
-          qs[i][hb] = on ? (uint32_t)qI.scales[row * (128 / kMxBlock) + g] : 127u;
+          qa[i][hb] = on ? load_operand<F8>(qI, (int64_t)(t0 + i) * n_I + h, g) : zero_operand<F8>();
         }
-      // weights of the result rows: head 4g + j + 16 hb
+      // weights of the result rows: head 4g + j + 16 hb (fp8: times the head's query scale)
       float wr[QB][4][4];
 #pragma unroll
       for (int i = 0; i < QB; ++i)
@@ -96,39 +142,37 @@ __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev 
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int h = 4 * g + j + 16 * hb;
-            wr[i][hb][j] = (i < nq && h < n_I) ? w[(int64_t)(t0 + i) * n_I + h] : 0.f;
+            const bool on = i < nq && h < n_I;
+            const int64_t row = (int64_t)(t0 + i) * n_I + h;
+            float wv_ = on ? w[row] : 0.f;
+            if (F8 && on) wv_ *= reinterpret_cast<const float*>(qI.scales)[row];
+            wr[i][hb][j] = wv_;
           }
       const int64_t e_stop = min(e_begin + (int64_t)kMxRange, v_max);
-      const uint8_t* kbase = kI.data + ctx.entry0 * kI.stride;
-      const uint8_t* sbase = kI.scales + ctx.entry0 * (128 / kMxBlock);
       // wave wv takes the 16-entry blocks e_begin + 16 (wv + 4 it); 4 blocks in flight
       for (int64_t e0 = e_begin + 16 * wv; e0 < e_stop; e0 += 4 * 64) {
-        uint4 kb[4];
-        uint32_t ks[4];
+        MxOperand<F8> kb[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           int64_t e = e0 + 64 * u + c16;
           if (e >= v_max) e = v_max - 1;  // past the run's last visible entry: a valid row, not written
-          kb[u] = *reinterpret_cast<const uint4*>(kbase + e * kI.stride + 16 * g);
-          ks[u] = (uint32_t)sbase[e * (128 / kMxBlock) + g];
+          kb[u] = load_operand<F8>(kI, ctx.entry0 + e, g);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int64_t eb = e0 + 64 * u;
           if (eb >= e_stop) break;
-          const mx_v8i b = mx_operand(kb[u]);
 #pragma unroll
           for (int i = 0; i < QB; ++i) {
             if (i >= nq) break;
             mx_v4f acc[4];
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb)  // acc[hb][j] = qI[head 4g+j+16hb] . kI[entry eb + c16]
-              acc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  mx_operand(qa[i][hb]), b, mx_v4f{0.f, 0.f, 0.f, 0.f}, kMxFmtE2M1, kMxFmtE2M1, 0, (int)qs[i][hb], 0,
-                  (int)ks[u]);
+              acc[hb] = mx_dot<F8>(qa[i][hb], kb[u]);
             float s = head_sum(acc, wr[i]);
             s += __shfl_xor(s, 16, 64);
             s += __shfl_xor(s, 32, 64);
+            if (F8) s *= kb[u].sc;
             const int64_t e = eb + c16;
             const int64_t v_i = (ctx.p + i + 1) / ratio;
             if (g == 0 && e < v_i && e < e_stop) score[(int64_t)(t0 + i) * score_stride + e] = s;
@@ -158,10 +202,10 @@ __device__ __forceinline__ float pair_sum32(float x) {
 }
 
 // Two waves per SIMD: room for the 8 accumulators of a block in ordinary VGPRs.
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) index_score_mx_block_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
-                                                                   int n_I, RowsDev kI, int ratio,
-                                                                   float* __restrict__ score, int64_t score_stride,
-                                                                   int n_parts) {
+template <bool F8>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+index_score_mx_block_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w, int n_I, RowsDev kI, int ratio,
+                            float* __restrict__ score, int64_t score_stride, int n_parts) {
   // Consecutive workgroups (dealt round-robin to the eight XCDs) take consecutive query
   // blocks of one part, the latest (most entries) first, so every XCD gets an even share
   // of the causal triangle and the longest rows start early.
@@ -179,8 +223,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int nq = min(t_end, ctx.q_end) - t0;
     const int v_max = (int)((ctx.p + nq) / ratio);  // visible entries of the run's last row
     if (e_begin < v_max) {
-      uint4 qa[kMxQW][4];
-      uint32_t qs[kMxQW][4];
+      MxOperand<F8> qa[kMxQW][4];
       float wr[kMxQW][4][4];
 #pragma unroll
       for (int i = 0; i < kMxQW; ++i)
@@ -188,13 +231,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int hb = 0; hb < 4; ++hb) {
           const int h = c16 + 16 * hb;
           const bool on = i < nq && h < n_I;
-          const int64_t row = (int64_t)(t0 + (on ? i : 0)) * n_I + (on ? h : 0);
-          qa[i][hb] = on ? *reinterpret_cast<const uint4*>(qI.data + row * qI.stride + 16 * g) : make_uint4(0u, 0u, 0u, 0u);
-          qs[i][hb] = on ? (uint32_t)qI.scales[row * (128 / kMxBlock) + g] : 127u;
+          qa[i][hb] = on ? load_operand<F8>(qI, (int64_t)(t0 + i) * n_I + h, g) : zero_operand<F8>();
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int hw = 4 * g + j + 16 * hb;
-            wr[i][hb][j] = (i < nq && hw < n_I) ? w[(int64_t)(t0 + i) * n_I + hw] : 0.f;
+            const bool onw = i < nq && hw < n_I;
+            const int64_t row = (int64_t)(t0 + i) * n_I + hw;
+            float wv_ = onw ? w[row] : 0.f;
+            if (F8 && onw) wv_ *= reinterpret_cast<const float*>(qI.scales)[row];
+            wr[i][hb][j] = wv_;
           }
         }
       const int e_stop = min(e_begin + kMxPart, v_max);
@@ -202,52 +247,44 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       const bool row_on = g < 2 && my_row < nq;
       const int e_lim = row_on ? min((int)((ctx.p + my_row + 1) / ratio), e_stop) : 0;
       float* srow = score + (int64_t)(t0 + (row_on ? my_row : 0)) * score_stride;
-      const uint8_t* kbase = kI.data + ctx.entry0 * kI.stride + 16 * g;
-      const uint8_t* sbase = kI.scales + ctx.entry0 * (128 / kMxBlock) + g;
-      const uint32_t kst = (uint32_t)kI.stride;
       // key fragments of a step's four 16-entry blocks (entries past the run's last visible
       // one read that entry instead: a valid row, never stored)
-      auto fetch = [&](int e0, uint4* kb, uint32_t* ks) {
+      auto fetch = [&](int e0, MxOperand<F8>* kb) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint32_t e = (uint32_t)min(e0 + 16 * u + c16, v_max - 1);
-          kb[u] = *reinterpret_cast<const uint4*>(kbase + (uint64_t)e * kst);
-          ks[u] = (uint32_t)sbase[e * (128 / kMxBlock)];
+          const int e = min(e0 + 16 * u + c16, v_max - 1);
+          kb[u] = load_operand<F8>(kI, ctx.entry0 + e, g);
         }
       };
       // the 64 entries e0 .. e0+63: 8 MFMAs per 16-entry block, then the head sums
-      auto step = [&](int e0, const uint4* kb, const uint32_t* ks) {
+      auto step = [&](int e0, const MxOperand<F8>* kb) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int eb = e0 + 16 * u;
           if (eb >= e_stop) break;
-          const mx_v8i b = mx_operand(kb[u]);
           mx_v4f acc[kMxQW][4];
 #pragma unroll
           for (int i = 0; i < kMxQW; ++i)
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb)
-              acc[i][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  mx_operand(qa[i][hb]), b, mx_v4f{0.f, 0.f, 0.f, 0.f}, kMxFmtE2M1, kMxFmtE2M1, 0, (int)qs[i][hb], 0,
-                  (int)ks[u]);
+            for (int hb = 0; hb < 4; ++hb) acc[i][hb] = mx_dot<F8>(qa[i][hb], kb[u]);
           float sr[kMxQW];
 #pragma unroll
           for (int i = 0; i < kMxQW; ++i) sr[i] = head_sum(acc[i], wr[i]);
-          const float tot = pair_sum32(pair_sum16(sr[1], sr[0]));
+          float tot = pair_sum32(pair_sum16(sr[1], sr[0]));
+          if (F8) tot *= kb[u].sc;
           const int e = eb + c16;
           if (e < e_lim) srow[e] = tot;
         }
       };
       // two register sets in turn: the next step's fragments load during this step
-      uint4 ka[4], kc[4];
-      uint32_t sa[4], sc[4];
-      fetch(e_begin, ka, sa);
+      MxOperand<F8> ka[4], kc[4];
+      fetch(e_begin, ka);
       for (int e0 = e_begin; e0 < e_stop; e0 += 128) {
-        fetch(e0 + 64, kc, sc);
-        step(e0, ka, sa);
+        fetch(e0 + 64, kc);
+        step(e0, ka);
         if (e0 + 64 >= e_stop) break;
-        fetch(e0 + 128, ka, sa);
-        step(e0 + 64, kc, sc);
+        fetch(e0 + 128, ka);
+        step(e0 + 64, kc);
       }
     }
     t0 += nq;
@@ -255,25 +292,35 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 bool index_mx_supported(const RowsDev& qI, const RowsDev& kI, int n_I) {
-  return qI.dtype == DT_MXFP4 && kI.dtype == DT_MXFP4 && kI.dim == 128 && qI.dim == 128 && n_I <= 64 &&
-         qI.stride % 16 == 0 && kI.stride % 16 == 0;
+  const bool fmt_ok = (qI.dtype == DT_MXFP4 && kI.dtype == DT_MXFP4) ||
+                      (qI.dtype == DT_FP8_B128 && kI.dtype == DT_FP8_B128);
+  return fmt_ok && kI.dim == 128 && qI.dim == 128 && n_I <= 64 && qI.stride % 16 == 0 && kI.stride % 16 == 0;
+}
+
+template <bool F8>
+static void launch_mx(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI, int ratio,
+                      float* score, int64_t score_stride, int max_vis, int max_q, hipStream_t stream) {
+  if (max_q >= 16) {
+    const int parts = (max_vis + kMxPart - 1) / kMxPart;
+    const int64_t blocks = (int64_t)((S.total_q + 4 * kMxQW - 1) / (4 * kMxQW)) * parts;
+    hipLaunchKernelGGL(index_score_mx_block_kernel<F8>, dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I,
+                       kI, ratio, score, score_stride, parts);
+  } else {
+    const int n_parts = (max_vis + kMxRange - 1) / kMxRange;
+    const int64_t blocks = (int64_t)S.total_q * n_parts;
+    hipLaunchKernelGGL((index_score_mx_kernel<1, F8>), dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I,
+                       kI, ratio, score, score_stride, n_parts);
+  }
 }
 
 hipError_t launch_index_score_mx(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
                                  int ratio, float* score, int64_t score_stride, int max_vis, int max_q,
                                  hipStream_t stream) {
-  const int n_parts = (max_vis + kMxRange - 1) / kMxRange;
-  if (n_parts == 0 || S.total_q == 0) return hipSuccess;
-  if (max_q >= 16) {
-    const int parts = (max_vis + kMxPart - 1) / kMxPart;
-    const int64_t blocks = (int64_t)((S.total_q + 4 * kMxQW - 1) / (4 * kMxQW)) * parts;
-    hipLaunchKernelGGL(index_score_mx_block_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I, kI,
-                       ratio, score, score_stride, parts);
-  } else {
-    const int64_t blocks = (int64_t)S.total_q * n_parts;
-    hipLaunchKernelGGL(index_score_mx_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I, kI,
-                       ratio, score, score_stride, n_parts);
-  }
+  if (max_vis <= 0 || S.total_q == 0) return hipSuccess;
+  if (qI.dtype == DT_FP8_B128)
+    launch_mx<true>(S, qI, w, n_I, kI, ratio, score, score_stride, max_vis, max_q, stream);
+  else
+    launch_mx<false>(S, qI, w, n_I, kI, ratio, score, score_stride, max_vis, max_q, stream);
   return hipGetLastError();
 }
 

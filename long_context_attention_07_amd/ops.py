@@ -13,7 +13,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
-F32, BF16, KV_SPLIT, MXFP4 = 0, 1, 2, 3
+F32, BF16, KV_SPLIT, MXFP4, FP8_B128 = 0, 1, 2, 3, 4
 KV_SPLIT_BF16_DIMS = 64
 OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND, OP_TOPK = 1, 2, 3, 4
 
@@ -102,7 +102,7 @@ class Rows:
     @staticmethod
     def of(t, scales=None, dtype=None, dim=None):
         """Rows from a 2-D tensor: float32 -> F32, bfloat16 -> BF16; uint8 with explicit
-        dtype (KV_SPLIT / MXFP4) and dim."""
+        dtype (KV_SPLIT / MXFP4 / FP8_B128) and dim."""
         if dtype is None:
             dtype = {torch.float32: F32, torch.bfloat16: BF16}[t.dtype]
             dim = t.shape[-1]

@@ -17,7 +17,8 @@ Readings (the pages are silent on the recipe):
 * FP8 1x128 (KV rows): the first d_n = D - 64 dims are cut into 128-wide blocks
   (448 = 128+128+128+64); scale_b = fp32(amax_b / 448); code = RNE_e4m3(x / scale_b),
   saturating at +-448; an all-zero block gets scale 0 and zero codes.  The trailing
-  64 RoPE dims are stored as bf16.
+  64 RoPE dims are stored as bf16.  The same recipe over all D dims (no bf16 tail) is
+  the fp8 alternative for indexer queries and keys.
 * MXFP4: 32-element blocks; shared exponent E = floor(log2(amax)) - 2 (2 = emax of e2m1),
   clamped to [-127, 127]; element = RNE_e2m1(x / 2^E) saturating at +-6; amax == 0
   gives E = -127 and zero codes.  Packing: element 2i in the low nibble of byte i.
@@ -198,6 +199,18 @@ def dequant_kv_split(codes, scales, rope_bits):
         out[..., lo:hi] = decode_e4m3fn(codes[..., lo:hi]) * np.asarray(scales, dtype=np.float64)[..., b:b + 1]
     out[..., d_n:] = decode_bf16(rope_bits)
     return out
+
+
+def quant_fp8_b128(x):
+    """Rows [..., D] float64 -> (codes uint8 [..., D], scales float32 [..., ceil(D/128)]):
+    the FP8 1x128 recipe of the KV rows applied to every dim (no bf16 tail)."""
+    codes, scales, _ = quant_kv_split(x, 0)
+    return codes, scales
+
+
+def dequant_fp8_b128(codes, scales):
+    codes = np.asarray(codes, dtype=np.uint8)
+    return dequant_kv_split(codes, scales, np.zeros(codes.shape[:-1] + (0,), dtype=np.uint16))
 
 
 def quant_mxfp4(x):

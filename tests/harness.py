@@ -62,6 +62,14 @@ def kv_split(x64, rope=64):
     return ops.Rows(data, ops.KV_SPLIT, dn + rope, sc), F.dequant_kv_split(codes, scales, rbits)
 
 
+def fp8_b128(x64):
+    """float64 rows -> (Rows in FP8_B128 format on the device, float64 stored values)."""
+    codes, scales = F.quant_fp8_b128(x64)
+    data = torch.from_numpy(np.ascontiguousarray(codes)).to(DEV)
+    sc = torch.from_numpy(np.ascontiguousarray(scales)).to(DEV)
+    return ops.Rows(data, ops.FP8_B128, x64.shape[-1], sc), F.dequant_fp8_b128(codes, scales)
+
+
 def mxfp4(x64):
     packed, sc = F.quant_mxfp4(x64)
     data = torch.from_numpy(np.ascontiguousarray(packed)).to(DEV)
@@ -83,6 +91,8 @@ def rows_values(rows, n=None):
         return F.dequant_kv_split(raw[:, :dn], sc, raw[:, dn:].copy().view(np.uint16))
     raw = d.cpu().numpy()
     sc = (rows.scales[:n] if n is not None else rows.scales).cpu().numpy()
+    if rows.dtype == ops.FP8_B128:
+        return F.dequant_fp8_b128(raw, sc)
     return F.dequant_mxfp4(raw, sc)
 
 
@@ -95,6 +105,9 @@ def empty_rows(n, dim, dtype):
         dn = dim - 64
         return ops.Rows(torch.zeros((n, dn + 128), dtype=torch.uint8, device=DEV), ops.KV_SPLIT, dim,
                         torch.zeros((n, (dn + 127) // 128), dtype=torch.float32, device=DEV))
+    if dtype == ops.FP8_B128:
+        return ops.Rows(torch.zeros((n, dim), dtype=torch.uint8, device=DEV), ops.FP8_B128, dim,
+                        torch.zeros((n, (dim + 127) // 128), dtype=torch.float32, device=DEV))
     return ops.Rows(torch.zeros((n, dim // 2), dtype=torch.uint8, device=DEV), ops.MXFP4, dim,
                     torch.zeros((n, dim // 32), dtype=torch.uint8, device=DEV))
 
@@ -202,9 +215,9 @@ def check_codes(gpu_rows, ref, n=None, rel=1e-6, what="entries"):
     if gpu_rows.dtype == ops.BF16:
         bits = d.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         return bf16_part(bits, ref)
-    if gpu_rows.dtype == ops.KV_SPLIT:
+    if gpu_rows.dtype in (ops.KV_SPLIT, ops.FP8_B128):
         raw = d.cpu().numpy()
-        dn = gpu_rows.dim - 64
+        dn = gpu_rows.dim - 64 if gpu_rows.dtype == ops.KV_SPLIT else gpu_rows.dim
         scg = sc.astype(np.float64)
         for b, (lo, hi) in enumerate(F.kv_split_blocks(dn)):
             x = ref[:, lo:hi]
@@ -217,6 +230,8 @@ def check_codes(gpu_rows, ref, n=None, rel=1e-6, what="entries"):
             ok = _codes_allowed(F.e4m3fn_round, v, rel * F.E4M3_MAX, g)
             assert np.all(ok), f"{what}: {int((~ok).sum())} fp8 codes of block {b} off the allowed codes"
             flips += int(np.sum(g != F.e4m3fn_round(v)))
+        if gpu_rows.dtype == ops.FP8_B128:
+            return flips
         bits = raw[:, dn:].copy().view(np.uint16)
         return flips + bf16_part(bits, ref[:, dn:])
     if gpu_rows.dtype == ops.MXFP4:
@@ -239,7 +254,7 @@ def check_codes(gpu_rows, ref, n=None, rel=1e-6, what="entries"):
         ok = _codes_allowed(F.e2m1_round, v, rel * amax[..., None] / unit, g)
         assert np.all(ok), f"{what}: {int((~ok).sum())} e2m1 codes off the allowed codes"
         return flips + int(np.sum(g != F.e2m1_round(v)))
-    raise ValueError("check_codes takes BF16, KV_SPLIT or MXFP4 rows")
+    raise ValueError("check_codes takes BF16, KV_SPLIT, FP8_B128 or MXFP4 rows")
 
 
 # ----------------------------------------------------------------------------- device-drawn inputs

@@ -14,8 +14,8 @@ from oracle import pipeline as P
 from oracle.attention import attend_token
 from oracle.indexer import index_scores, topk_select, visible
 
-from harness import (DEV, assert_close, bf16, check_codes, check_topk, empty_rows, f32, kv_split, log, make_batch,
-                     mxfp4, rows_values, score_error_bound)
+from harness import (DEV, assert_close, bf16, check_codes, check_topk, empty_rows, f32, fp8_b128, kv_split, log,
+                     make_batch, mxfp4, rows_values, score_error_bound)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,8 @@ def _rows_in(fmt, x64):
         return ops.Rows.of(t), h
     if fmt == ops.KV_SPLIT:
         return kv_split(x64)
+    if fmt == ops.FP8_B128:
+        return fp8_b128(x64)
     return mxfp4(x64)
 
 
@@ -60,6 +62,10 @@ COMPRESS_CASES = [
     # and the narrowest row (one group)
     (ops.BF16, ops.BF16, ops.BF16, 96, 128, 0, 0),
     (ops.F32, ops.F32, ops.F32, 32, 64, 0, 0),
+    # fp8 1x128 indexer keys: one block, the split pooling, a 64-dim (part-filled) block
+    (ops.BF16, ops.BF16, ops.FP8_B128, 128, 4, 1, 0),
+    (ops.BF16, ops.BF16, ops.FP8_B128, 128, 128, 0, 0),
+    (ops.F32, ops.F32, ops.FP8_B128, 64, 4, 1, 0),
 ]
 
 
@@ -128,7 +134,8 @@ def test_compress2_equals_two_compress_calls(ratio):
 
 
 @pytest.mark.parametrize("fmt,d_I,n_I", [(ops.F32, 32, 4), (ops.BF16, 128, 64), (ops.MXFP4, 128, 64),
-                                         (ops.F32, 64, 7)])
+                                         (ops.F32, 64, 7), (ops.FP8_B128, 128, 64), (ops.FP8_B128, 128, 20),
+                                         (ops.FP8_B128, 64, 8)])
 def test_index_score_matches_oracle(fmt, d_I, n_I):
     log(f"index_score fmt={fmt} d_I={d_I} n_I={n_I}")
     g = np.random.default_rng(7 + d_I + n_I)
@@ -189,9 +196,10 @@ def test_index_score_bf16_many_query_rows():
     log(f"bf16 indexer, {sq.total_q} query rows: scores within the float32 bound, top-k tie swaps {swaps}")
 
 
-def test_index_score_mxfp4_query_blocks():
-    """MXFP4 scores on the scaled matrix cores with query blocks: several sequences with many
-    new tokens each, so blocks of consecutive query rows cross sequence boundaries, and one
+@pytest.mark.parametrize("fmt", [ops.MXFP4, ops.FP8_B128])
+def test_index_score_scaled_query_blocks(fmt):
+    """MXFP4 and fp8 1x128 scores on the scaled matrix cores with query blocks (keys of widely
+    varying scale): several sequences with many new tokens each, so blocks of consecutive query rows cross sequence boundaries, and one
     long sequence whose visible entries span two 32768-entry parts with a ragged tail.  The
     same tokens scored one per sequence (the one-row kernel) give the same bits; the oracle
     checks every token but the first 15 of the long sequence."""
@@ -200,8 +208,8 @@ def test_index_score_mxfp4_query_blocks():
     n_q = [17, 1, 23, 6, 40, 19]
     ctx = [300, 2051, 23, 1600, 900, 131145]
     ob, sq, n_ent, _ = make_batch(n_q, ctx, ratio)
-    kI_rows, kI_val = _rows_in(ops.MXFP4, g.standard_normal((n_ent, d_I)))
-    qI_rows, qI_val = _rows_in(ops.MXFP4, g.standard_normal((sq.total_q * n_I, d_I)))
+    kI_rows, kI_val = _rows_in(fmt, g.standard_normal((n_ent, d_I)) * np.exp(g.uniform(-3, 3, (n_ent, 1))))
+    qI_rows, qI_val = _rows_in(fmt, g.standard_normal((sq.total_q * n_I, d_I)))
     w_t, w_val = f32(g.standard_normal((sq.total_q, n_I)) / math.sqrt(n_I))
     stride = sq.max_ctx // ratio + 3
     score = torch.full((sq.total_q, stride), float("nan"), dtype=torch.float32, device=DEV)

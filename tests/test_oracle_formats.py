@@ -148,6 +148,30 @@ def test_kv_split_recipe_and_roundtrip():
     assert np.all(zc == 0) and np.all(zs == 0)
 
 
+def test_fp8_b128_recipe_matches_torch_cast():
+    """The FP8 1x128 rows of the indexer: scale = fp32(amax / 448) per 128 dims, codes the
+    e4m3fn rounding of x / scale -- checked against torch's own float8_e4m3fn cast of the
+    scaled values (saturation at the block maximum, a ragged last block of 64 dims, a zero
+    block)."""
+    g = np.random.default_rng(6)
+    x = g.standard_normal((50, 192)) * np.exp(g.uniform(-6, 6, (50, 1)))
+    x[7, 5] = -300.0
+    x[9, 128:] = 0.0
+    codes, scales = F.quant_fp8_b128(x)
+    assert codes.shape == (50, 192) and scales.shape == (50, 2) and scales.dtype == np.float32
+    for b, (lo, hi) in enumerate([(0, 128), (128, 192)]):
+        sc = (np.abs(x[:, lo:hi]).max(1) / 448).astype(np.float32)
+        np.testing.assert_array_equal(scales[:, b], sc)
+        safe = np.where(sc > 0, sc, 1).astype(np.float64)[:, None]
+        y = torch.from_numpy(np.clip(x[:, lo:hi] / safe, -448, 448)).to(torch.float8_e4m3fn)
+        want = y.view(torch.uint8).numpy()
+        want = np.where(sc[:, None] > 0, want, 0)
+        np.testing.assert_array_equal(codes[:, lo:hi], want)
+    deq = F.dequant_fp8_b128(codes, scales)
+    assert np.all(deq[9, 128:] == 0)
+    assert deq[7, 5] == -448 * float(scales[7, 0])
+
+
 def _golden_kv():
     vals = {}
     with open(os.path.join(GOLD, "kv_bytes_per_token.txt")) as f:

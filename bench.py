@@ -122,8 +122,8 @@ class DecodeLayer:
     indexer format: "bf16", "mxfp4" or "fp8" (keys, queries and the keys the compress step
     writes)."""
 
-    def __init__(self, wl, lens, seed, dev, kfmt="bf16"):
-        self.wl, self.kfmt = wl, kfmt
+    def __init__(self, wl, lens, seed, dev, kfmt="bf16", scores="f32"):
+        self.wl, self.kfmt, self.scores = wl, kfmt, scores
         n, D, ratio = wl.n_seqs, wl.d_c, wl.ratio
         x = synth.decode_inputs(wl, lens, seed, dev)
         self.lens, self.E = x["lens"], x["E"]
@@ -146,9 +146,10 @@ class DecodeLayer:
                 self.R["qI"] = conv(self.qI.float())
                 del self.kI, self.qI
             self.idx = torch.empty((n, wl.k), dtype=torch.int32, device=dev)
-            ws_i = ops.csa_workspace_bytes(ops.OP_INDEX_TOPK, self.seqs, k=wl.k, ratio=ratio)
+            op = ops.OP_INDEX_TOPK_BF16 if scores == "bf16" else ops.OP_INDEX_TOPK
+            ws_i = ops.csa_workspace_bytes(op, self.seqs, k=wl.k, ratio=ratio)
             ws_a = ops.csa_workspace_bytes(ops.OP_CSA_ATTEND, self.seqs, wl.n_h, D, wl.k, ratio, wl.n_win)
-            self.ws_score_stride = max(1, max(lens) // ratio)
+            self.ws_score_stride = (max(1, max(lens) // ratio) + 7) // 8 * 8   # 16-byte aligned rows
         else:
             ws_i = 0
             ws_a = ops.csa_workspace_bytes(ops.OP_HCA_ATTEND, self.seqs, wl.n_h, D, 0, ratio, wl.n_win)
@@ -167,15 +168,22 @@ class DecodeLayer:
                              wl.rope_theta, self.R["kv"])
 
     def _score(self):
-        return self.ws[: self.wl.n_seqs * self.ws_score_stride].view(self.wl.n_seqs, self.ws_score_stride)
+        n, st = self.wl.n_seqs, self.ws_score_stride
+        if self.scores == "bf16":
+            return self.ws.view(torch.int16)[: n * st].view(n, st)
+        return self.ws[: n * st].view(n, st)
 
     def index_score(self):
-        ops.csa_index_score(self.seqs, self.R["qI"], self.w, self.wl.n_I, self.R["kI"], self.wl.ratio, self._score())
+        f = ops.csa_index_score_bf16 if self.scores == "bf16" else ops.csa_index_score
+        f(self.seqs, self.R["qI"], self.w, self.wl.n_I, self.R["kI"], self.wl.ratio, self._score())
 
     def topk(self):
-        # the selection's candidate lists follow the scores in the workspace (as in csa_index_topk)
-        n = self.wl.n_seqs * self.ws_score_stride
-        ops.csa_topk(self.seqs, self._score(), self.wl.ratio, self.wl.k, self.idx, ws=self.ws[n:])
+        # the selection's candidate lists follow the scores in the workspace (as in
+        # csa_index_topk: the score bytes padded to 256)
+        sb = self.wl.n_seqs * self.ws_score_stride * (2 if self.scores == "bf16" else 4)
+        off = (sb + 255) // 256 * 256 // 4
+        f = ops.csa_topk_bf16 if self.scores == "bf16" else ops.csa_topk
+        f(self.seqs, self._score(), self.wl.ratio, self.wl.k, self.idx, ws=self.ws[off:])
 
     def attend(self):
         wl = self.wl
@@ -211,9 +219,10 @@ class DecodeLayer:
             key_b = {"bf16": dI * 2, "mxfp4": dI // 2 + dI // 32, "fp8": dI + 4}[self.kfmt]
             comp_b += new_ent.sum() * (src * 2 * dI * 2 + key_b)
             w["compress"] = (comp_b, 0.0)
-            w["index_score"] = (float((V * (key_b + 4)).sum() + n * (nI * key_b + nI * 4)),
+            sc_b = 2 if self.scores == "bf16" else 4
+            w["index_score"] = (float((V * (key_b + sc_b)).sum() + n * (nI * key_b + nI * 4)),
                                 float((V * nI * dI * 2).sum()))
-            w["topk"] = (float((V * 4).sum() + n * wl.k * 4), 0.0)
+            w["topk"] = (float((V * sc_b).sum() + n * wl.k * 4), 0.0)
             keys = np.minimum(V, wl.k) + win
             w["attend"] = (float((keys * D * 2).sum() + n * wl.k * 4 + qo), float((keys * nh * D * 4).sum()))
         else:
@@ -250,16 +259,16 @@ def time_fn(fn, layers, reps, stream):
     return e0.elapsed_time(e1) / (n * len(layers))
 
 
-def build_layers(wl, dev, kfmt="bf16", max_sets=MAX_SETS, min_sets=2):
+def build_layers(wl, dev, kfmt="bf16", max_sets=MAX_SETS, min_sets=2, scores="f32"):
     """Layer sets for a decode workload: enough independent sets that the bytes their steps
     touch exceed SET_BYTES together (twice the Infinity Cache, so no set's rows stay there
     from one use to the next), between min_sets and max_sets."""
     lens = make_lengths(wl)
-    layers = [DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100), dev, kfmt)]
+    layers = [DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100), dev, kfmt, scores)]
     touched = sum(b for b, _ in layers[0].work().values())
     n_sets = int(min(max_sets, max(min_sets, math.ceil(SET_BYTES / max(touched, 1.0)))))
     for i in range(1, n_sets):
-        layers.append(DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100 + i), dev, kfmt))
+        layers.append(DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100 + i), dev, kfmt, scores))
     return layers, lens
 
 
@@ -338,17 +347,18 @@ def op_breakdown(layers, reps, stream):
     return kernels, roof, work
 
 
-def run_decode(wl, dev, stream, steps, warmup, kfmt="bf16", graph=True, max_sets=MAX_SETS):
+def run_decode(wl, dev, stream, steps, warmup, kfmt="bf16", graph=True, max_sets=MAX_SETS, scores="f32"):
     """One decode workload: tokens/s over exactly `steps` steps, step-time percentiles,
     per-operation times and the dominant operation's roofline entry."""
-    layers, lens = build_layers(wl, dev, kfmt, max_sets=max_sets)
+    layers, lens = build_layers(wl, dev, kfmt, max_sets=max_sets, scores=scores)
     torch.cuda.synchronize()
-    log(f"{wl.name} ({kfmt} indexer): {wl.n_seqs} seqs, ctx {min(lens)}..{max(lens)}, {len(layers)} layer sets, "
+    log(f"{wl.name} ({kfmt} indexer, {scores} scores): {wl.n_seqs} seqs, ctx {min(lens)}..{max(lens)}, {len(layers)} layer sets, "
         f"{torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated")
     ms, per_step, wall = timed_steps(layers, steps, warmup, stream, graph)
     kernels, roof, work = op_breakdown(layers, max(64, steps // 4), stream)
     step_bytes = sum(b for b, _ in work.values())
-    res = {"workload": wl.name, "indexer": kfmt if layers[0].csa else None, "tokens_per_s": round(wl.n_seqs / (ms * 1e-3), 1),
+    res = {"workload": wl.name, "indexer": kfmt if layers[0].csa else None,
+           "scores": scores if layers[0].csa else None, "tokens_per_s": round(wl.n_seqs / (ms * 1e-3), 1),
            "ms_per_step": round(ms, 5), "step_time": percentiles(per_step), "wall_s": round(wall, 3),
            "batch": wl.n_seqs, "ctx": [min(lens), max(lens)], "k": wl.k if layers[0].csa else None,
            "layer_sets": len(layers),
@@ -623,6 +633,8 @@ class PrefillLayer:
         self.kI = ops.Rows(torch.zeros((E, d_I // 2), dtype=torch.uint8, device=dev), ops.MXFP4, d_I,
                            torch.zeros((E, d_I // 32), dtype=torch.uint8, device=dev))
         self.score = torch.empty((N, E), dtype=torch.float32, device=dev)
+        self.score16 = torch.empty((N, E), dtype=torch.int16, device=dev)
+        self.idx16 = torch.empty((N, wl.k), dtype=torch.int32, device=dev)
         self.idx = torch.empty((N, wl.k), dtype=torch.int32, device=dev)
         self.out = ops.Rows.of(torch.empty((N * n_h, D), dtype=torch.bfloat16, device=dev))
         self.lse = torch.empty((N, n_h), dtype=torch.float32, device=dev)
@@ -640,6 +652,20 @@ class PrefillLayer:
 
     def topk(self):
         ops.csa_topk(self.seqs, self.score, self.wl.ratio, self.wl.k, self.idx)
+
+    def index_score_bf16(self):
+        ops.csa_index_score_bf16(self.seqs, self.qI, self.w, self.wl.n_I, self.kI, self.wl.ratio, self.score16)
+
+    def topk_bf16(self):
+        ops.csa_topk_bf16(self.seqs, self.score16, self.wl.ratio, self.wl.k, self.idx16)
+
+    def recall_bf16(self, rows=512):
+        """Mean fraction of the float32 selection the bf16-score selection keeps, over evenly
+        spaced query rows."""
+        r = torch.linspace(self.N // 8, self.N - 1, rows, device=self.idx.device).long()
+        a, b = self.idx[r], self.idx16[r]
+        hit = (a[:, :, None] == b[:, None, :]).any(dim=2) & (a >= 0)
+        return float((hit.sum(1).float() / (a >= 0).sum(1).clamp_min(1).float()).mean())
 
     def attend(self):
         wl = self.wl
@@ -667,6 +693,9 @@ class PrefillLayer:
             "index_score": (float(E * (dI // 2 + dI // 32) + N * nI * (dI // 2 + dI // 32 + 4) + V.sum() * 4),
                             float(V.sum() * nI * dI * 2), FP4_PEAK_TFLOPS),
             "topk": (float(V.sum() * 4 + N * wl.k * 4), 0.0, None),
+            "index_score_bf16": (float(E * (dI // 2 + dI // 32) + N * nI * (dI // 2 + dI // 32 + 4) + V.sum() * 2),
+                                 float(V.sum() * nI * dI * 2), FP4_PEAK_TFLOPS),
+            "topk_bf16": (float(V.sum() * 2 + N * wl.k * 4), 0.0, None),
             "attend": (float((keys * row_b).sum() + N * wl.k * 4 + N * nh * D * 4), float((keys * nh * D * 4).sum()),
                        BF16_PEAK_TFLOPS),
         }
@@ -685,8 +714,9 @@ def run_prefill(dev, stream, steps=3, warmup=1):
         layer.step()
     torch.cuda.synchronize()
     names = ("compress", "index_score", "topk", "attend")
+    extra = ("index_score_bf16", "topk_bf16")   # the bf16-score selector, timed beside the step
     ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-          for n in names}
+          for n in names + extra}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -698,7 +728,14 @@ def run_prefill(dev, stream, steps=3, warmup=1):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    op_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
+    for s_ in range(steps):
+        for n in extra:
+            ev[n][s_][0].record(stream)
+            getattr(layer, n)()
+            ev[n][s_][1].record(stream)
+    torch.cuda.synchronize()
+    recall = layer.recall_bf16()
+    op_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names + extra}
     work = layer.work()
     kernels = {}
     for n, (b, f, peak) in work.items():
@@ -707,7 +744,7 @@ def run_prefill(dev, stream, steps=3, warmup=1):
                       "fp8_frac": round(f / t / 1e12 / FP8_PEAK_TFLOPS, 4) if peak else None,
                       "instr_peak_TFLOPs": peak, "instr_frac": round(f / t / 1e12 / peak, 4) if peak else None,
                       "bytes": int(b), "flops": int(f)}
-    dom = max(op_ms, key=op_ms.get)
+    dom = max(names, key=op_ms.get)
     b, f, peak = work[dom]
     dt = op_ms[dom] * 1e-3
     roof = {"kernel": dom, "kernels": PREFILL_KERNELS[dom], "bound": "mfma", "achieved": round(f / dt / 1e12, 1),
@@ -716,7 +753,10 @@ def run_prefill(dev, stream, steps=3, warmup=1):
             "flops_per_launch": int(f), "avg_launch_us": round(dt * 1e6, 1)}
     res = {"workload": wl.name, "tokens_per_s": round(layer.N / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
            "steps": steps, "seq_len": layer.N, "k": wl.k, "kv": "fp8 e4m3 1x128 + bf16 RoPE",
-           "indexer": f"{wl.n_I}x{wl.d_I} MXFP4", "roofline": roof, "kernels": kernels}
+           "indexer": f"{wl.n_I}x{wl.d_I} MXFP4", "roofline": roof, "kernels": kernels,
+           "bf16_scores": {"index_score_us": kernels["index_score_bf16"]["us"], "topk_us": kernels["topk_bf16"]["us"],
+                           "topk_speedup": round(op_ms["topk"] / op_ms["topk_bf16"], 3),
+                           "recall_of_f32_selection": round(recall, 5), "recall_rows": 512}}
     log(f"prefill step {ms:.2f} ms; per-op {json.dumps(kernels)}")
     del layer
     torch.cuda.empty_cache()
@@ -728,10 +768,12 @@ def run_prefill(dev, stream, steps=3, warmup=1):
 def run_sweep(dev, stream, steps, warmup):
     """The decode step over the metric's context range (see the module docstring)."""
     out = []
-    points = [(wl, f) for f in ("bf16", "mxfp4", "fp8") for wl in configs.CSA_DECODE_SWEEP]
-    points += [(configs.CSA_DECODE_K1024, "bf16")] + [(wl, "bf16") for wl in configs.HCA_DECODE_SWEEP]
-    for wl, kfmt in points:
-        res, layers = run_decode(wl, dev, stream, steps, warmup, kfmt, max_sets=MAX_SETS)
+    points = [(wl, f, "f32") for f in ("bf16", "mxfp4", "fp8") for wl in configs.CSA_DECODE_SWEEP]
+    # the selector on bf16 scores: the headline batch and 1M context
+    points += [(configs.CSA_DECODE_BF16, "bf16", "bf16"), (configs.CSA_DECODE_SWEEP[-1], "bf16", "bf16")]
+    points += [(configs.CSA_DECODE_K1024, "bf16", "f32")] + [(wl, "bf16", "f32") for wl in configs.HCA_DECODE_SWEEP]
+    for wl, kfmt, scores in points:
+        res, layers = run_decode(wl, dev, stream, steps, warmup, kfmt, max_sets=MAX_SETS, scores=scores)
         out.append(res)
         del layers
         torch.cuda.empty_cache()

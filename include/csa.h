@@ -158,11 +158,28 @@ int csa_index_score(const csa_seqs* seqs, const csa_rows* qI, const float* w, in
 int csa_topk(const csa_seqs* seqs, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
              void* ws, size_t ws_bytes, void* stream);
 
+/* csa_index_score_bf16 / csa_topk_bf16 -- the selector with bf16 index scores ("DeepSeek-V4
+ * 深度分析报告" section 3.4: the index scores are quantised from FP32 to BF16, halving what the
+ * top-k selector reads).  csa_index_score_bf16 computes each score exactly as
+ * csa_index_score and stores its bf16 rounding (nearest even) as 16-bit patterns in
+ * score[t * score_stride + i].  csa_topk_bf16 selects as csa_topk on those values (each
+ * bf16 score compares as the float32 value it stands for; equal scores, now far more
+ * common, go to the lower index).  Arguments and errors as csa_index_score / csa_topk. */
+int csa_index_score_bf16(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI,
+                         int ratio, uint16_t* score, int64_t score_stride, void* stream);
+int csa_topk_bf16(const csa_seqs* seqs, const uint16_t* score, int64_t score_stride, int ratio, int k, int32_t* idx,
+                  void* ws, size_t ws_bytes, void* stream);
+
 /* csa_index_topk -- csa_index_score into the workspace followed by csa_topk (its
  * candidate lists after the scores).  ws_bytes must be >=
  * csa_workspace_bytes(CSA_OP_INDEX_TOPK, ...). */
 int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
                    int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* csa_index_topk_bf16 -- csa_index_score_bf16 into the workspace followed by csa_topk_bf16.
+ * ws_bytes must be >= csa_workspace_bytes(CSA_OP_INDEX_TOPK_BF16, ...). */
+int csa_index_topk_bf16(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI,
+                        int ratio, int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /* csa_index_topk_noalloc -- csa_index_topk for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
@@ -220,11 +237,12 @@ int hca_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows*
                float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace sizing (host only; reads only the host scalars of `seqs`). */
-enum { CSA_OP_INDEX_TOPK = 1, CSA_OP_CSA_ATTEND = 2, CSA_OP_HCA_ATTEND = 3, CSA_OP_TOPK = 4 };
-/* op CSA_OP_INDEX_TOPK: ratio, k used; CSA_OP_CSA_ATTEND: n_h, dim, k, n_win used;
+enum { CSA_OP_INDEX_TOPK = 1, CSA_OP_CSA_ATTEND = 2, CSA_OP_HCA_ATTEND = 3, CSA_OP_TOPK = 4, CSA_OP_INDEX_TOPK_BF16 = 5 };
+/* op CSA_OP_INDEX_TOPK(_BF16): ratio, k used; CSA_OP_CSA_ATTEND: n_h, dim, k, n_win used;
  * CSA_OP_HCA_ATTEND: n_h, dim, ratio, n_win used; CSA_OP_TOPK: ratio, k used.  Returns
- * the bytes the call uses: for CSA_OP_INDEX_TOPK total_q * floor(max_ctx/ratio) float32
- * scores plus the selection's candidate lists (mandatory); for CSA_OP_TOPK the candidate
+ * the bytes the call uses: for CSA_OP_INDEX_TOPK total_q * S float32 scores, S =
+ * floor(max_ctx/ratio) rounded up to a multiple of 8 (padded to 256 bytes), plus the selection's candidate lists (mandatory), for
+ * CSA_OP_INDEX_TOPK_BF16 the same with bf16 scores; for CSA_OP_TOPK the candidate
  * lists of the sliced selection (optional, see csa_topk); for the
  * attention ops the chunk partials when the call would split its key lists (see
  * csa_attend), else 0.  Returns 0 for an invalid op. */

@@ -209,19 +209,31 @@ int scratch_on_current_device(void** out) {
   return CSA_OK;
 }
 
-// Index scores into `score` (float32 [total_q, stride]) then the selection; arguments
-// already validated.
+// Row stride (elements) of the score matrix in an index + top-k workspace: a multiple of 8,
+// so every row starts on a 16-byte boundary for the selection's vector loads.
+int64_t score_stride_ws(const csa_seqs* seqs, int ratio) {
+  const int64_t max_vis = seqs->max_ctx / ratio;
+  return ((max_vis > 0 ? max_vis : 1) + 7) / 8 * 8;
+}
+
+// Bytes of that score matrix, padded to 256 so that the candidate lists after it stay aligned.
+size_t score_bytes(const csa_seqs* seqs, int ratio, int bf16) {
+  const size_t b = (size_t)seqs->total_q * (size_t)score_stride_ws(seqs, ratio) * (bf16 ? 2 : 4);
+  return (b + 255) / 256 * 256;
+}
+
+// Index scores into the workspace (float32 or bf16, [total_q, floor(max_ctx/ratio)]) then
+// the selection, its candidate lists after the scores; arguments already validated.
 int index_topk_launch(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
-                      int k, int32_t* idx, float* score, hipStream_t s) {
+                      int k, int32_t* idx, void* ws, int bf16, hipStream_t s) {
   const int max_vis = seqs->max_ctx / ratio;
-  const int64_t stride = max_vis > 0 ? max_vis : 1;
-  hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio, score, stride,
-                                         max_vis, seqs->max_q, s);
+  const int64_t stride = score_stride_ws(seqs, ratio);
+  hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio,
+                                         csa::ScoreOut{ws, stride, bf16}, max_vis, seqs->max_q, s);
   if (e != hipSuccess) return hip_status(e, "index_topk score launch");
-  // the selection's candidate lists follow the scores in the workspace
   const size_t cand = csa::topk_workspace_bytes(seqs->total_q, max_vis, k);
-  e = csa::launch_topk(dev_seqs(seqs), score, stride, ratio, k, idx, max_vis, seqs->max_q,
-                       score + (size_t)seqs->total_q * stride, cand, s);
+  e = csa::launch_topk(dev_seqs(seqs), ws, bf16, stride, ratio, k, idx, max_vis, seqs->max_q,
+                       static_cast<uint8_t*>(ws) + score_bytes(seqs, ratio, bf16), cand, s);
   return hip_status(e, "index_topk select launch");
 }
 
@@ -304,8 +316,8 @@ static int index_checks(const csa_seqs* seqs, const csa_rows* qI, const float* w
   return CSA_OK;
 }
 
-int csa_index_score(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
-                    float* score, int64_t score_stride, void* stream) {
+static int index_score_common(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI,
+                              int ratio, void* score, int bf16, int64_t score_stride, void* stream, const char* name) {
   int st;
   if ((st = index_checks(seqs, qI, w, n_I, kI, ratio))) return st;
   if (!score) return fail(CSA_EINVAL, "score: null pointer");
@@ -313,13 +325,25 @@ int csa_index_score(const csa_seqs* seqs, const csa_rows* qI, const float* w, in
   if (score_stride < max_vis)
     return fail(CSA_EINVAL, "score_stride %lld < floor(max_ctx/ratio) = %d", (long long)score_stride, max_vis);
   if (seqs->total_q == 0) return ok();
-  hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio, score,
-                                         score_stride, max_vis, seqs->max_q, static_cast<hipStream_t>(stream));
-  return hip_status(e, "csa_index_score launch");
+  hipError_t e = csa::launch_index_score(dev_seqs(seqs), dev_rows(qI), w, n_I, dev_rows(kI), ratio,
+                                         csa::ScoreOut{score, score_stride, bf16}, max_vis, seqs->max_q,
+                                         static_cast<hipStream_t>(stream));
+  return hip_status(e, name);
 }
 
-int csa_topk(const csa_seqs* seqs, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
-             void* ws, size_t ws_bytes, void* stream) {
+int csa_index_score(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
+                    float* score, int64_t score_stride, void* stream) {
+  return index_score_common(seqs, qI, w, n_I, kI, ratio, score, 0, score_stride, stream, "csa_index_score launch");
+}
+
+int csa_index_score_bf16(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI,
+                         int ratio, uint16_t* score, int64_t score_stride, void* stream) {
+  return index_score_common(seqs, qI, w, n_I, kI, ratio, score, 1, score_stride, stream,
+                            "csa_index_score_bf16 launch");
+}
+
+static int topk_common(const csa_seqs* seqs, const void* score, int bf16, int64_t score_stride, int ratio, int k,
+                       int32_t* idx, void* ws, size_t ws_bytes, void* stream, const char* name) {
   int st;
   if ((st = check_seqs(seqs))) return st;
   if (!score || !idx) return fail(CSA_EINVAL, "score/idx: null pointer");
@@ -329,23 +353,44 @@ int csa_topk(const csa_seqs* seqs, const float* score, int64_t score_stride, int
   if (score_stride < max_vis)
     return fail(CSA_EINVAL, "score_stride %lld < floor(max_ctx/ratio) = %d", (long long)score_stride, max_vis);
   if (seqs->total_q == 0) return ok();
-  hipError_t e = csa::launch_topk(dev_seqs(seqs), score, score_stride, ratio, k, idx, max_vis, seqs->max_q, ws,
+  hipError_t e = csa::launch_topk(dev_seqs(seqs), score, bf16, score_stride, ratio, k, idx, max_vis, seqs->max_q, ws,
                                   ws ? ws_bytes : 0, static_cast<hipStream_t>(stream));
-  return hip_status(e, "csa_topk launch");
+  return hip_status(e, name);
 }
 
-int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
-                   int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+int csa_topk(const csa_seqs* seqs, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
+             void* ws, size_t ws_bytes, void* stream) {
+  return topk_common(seqs, score, 0, score_stride, ratio, k, idx, ws, ws_bytes, stream, "csa_topk launch");
+}
+
+int csa_topk_bf16(const csa_seqs* seqs, const uint16_t* score, int64_t score_stride, int ratio, int k, int32_t* idx,
+                  void* ws, size_t ws_bytes, void* stream) {
+  return topk_common(seqs, score, 1, score_stride, ratio, k, idx, ws, ws_bytes, stream, "csa_topk_bf16 launch");
+}
+
+static int index_topk_common(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI,
+                             int ratio, int k, int32_t* idx, void* ws, size_t ws_bytes, int bf16, void* stream,
+                             const char* name) {
   int st;
   if ((st = index_checks(seqs, qI, w, n_I, kI, ratio))) return st;
   if (!idx) return fail(CSA_EINVAL, "idx: null pointer");
   if (k < 1 || k > 4096) return fail(CSA_EINVAL, "k %d out of [1, 4096]", k);
-  const size_t need = csa_workspace_bytes(CSA_OP_INDEX_TOPK, seqs, 0, 0, k, ratio, 0);
+  const size_t need =
+      csa_workspace_bytes(bf16 ? CSA_OP_INDEX_TOPK_BF16 : CSA_OP_INDEX_TOPK, seqs, 0, 0, k, ratio, 0);
   if (need && (!ws || ws_bytes < need))
-    return fail(CSA_EWORKSPACE, "csa_index_topk needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    return fail(CSA_EWORKSPACE, "%s needs %zu workspace bytes, got %zu", name, need, ws ? ws_bytes : 0);
   if (seqs->total_q == 0) return ok();
-  return index_topk_launch(seqs, qI, w, n_I, kI, ratio, k, idx, static_cast<float*>(ws),
-                           static_cast<hipStream_t>(stream));
+  return index_topk_launch(seqs, qI, w, n_I, kI, ratio, k, idx, ws, bf16, static_cast<hipStream_t>(stream));
+}
+
+int csa_index_topk(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI, int ratio,
+                   int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return index_topk_common(seqs, qI, w, n_I, kI, ratio, k, idx, ws, ws_bytes, 0, stream, "csa_index_topk");
+}
+
+int csa_index_topk_bf16(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI,
+                        int ratio, int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return index_topk_common(seqs, qI, w, n_I, kI, ratio, k, idx, ws, ws_bytes, 1, stream, "csa_index_topk_bf16");
 }
 
 int csa_index_topk_noalloc(const csa_seqs* seqs, const csa_rows* qI, const float* w, int n_I, const csa_rows* kI,
@@ -357,14 +402,13 @@ int csa_index_topk_noalloc(const csa_seqs* seqs, const csa_rows* qI, const float
   const size_t need = csa_workspace_bytes(CSA_OP_INDEX_TOPK, seqs, 0, 0, k, ratio, 0);
   if (need > kNoallocScratchBytes)
     return fail(CSA_EWORKSPACE,
-                "csa_index_topk_noalloc needs %zu bytes of scores and candidates, more than "
-                "its fixed %zu-byte scratch",
+                "csa_index_topk_noalloc needs %zu bytes of scores and candidates, more than its fixed %zu-byte "
+                "scratch",
                 need, kNoallocScratchBytes);
   if (seqs->total_q == 0) return ok();
   void* ptr = nullptr;
   if ((st = scratch_on_current_device(&ptr))) return st;
-  return index_topk_launch(seqs, qI, w, n_I, kI, ratio, k, idx, static_cast<float*>(ptr),
-                           static_cast<hipStream_t>(stream));
+  return index_topk_launch(seqs, qI, w, n_I, kI, ratio, k, idx, ptr, 0, static_cast<hipStream_t>(stream));
 }
 
 int csa_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows* kv, const int32_t* idx, int k,
@@ -405,11 +449,11 @@ int hca_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows*
 size_t csa_workspace_bytes(int op, const csa_seqs* seqs, int n_h, int dim, int k, int ratio, int n_win) {
   if (!seqs || seqs->total_q <= 0) return 0;
   switch (op) {
-    case CSA_OP_INDEX_TOPK: {
+    case CSA_OP_INDEX_TOPK:
+    case CSA_OP_INDEX_TOPK_BF16: {
       if (ratio < 1 || k < 1) return 0;
-      const int64_t max_vis = seqs->max_ctx / ratio;
-      return (size_t)seqs->total_q * (size_t)(max_vis > 0 ? max_vis : 1) * sizeof(float) +
-             csa::topk_workspace_bytes(seqs->total_q, (int)max_vis, k);
+      return score_bytes(seqs, ratio, op == CSA_OP_INDEX_TOPK_BF16) +
+             csa::topk_workspace_bytes(seqs->total_q, seqs->max_ctx / ratio, k);
     }
     case CSA_OP_TOPK: {
       if (ratio < 1 || k < 1) return 0;

@@ -69,6 +69,31 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// Index scores: float32, or bfloat16 bits rounded to nearest even from the float32 score
+// (the selector's bf16 scores of "DeepSeek-V4 深度分析报告" section 3.4).  Rows of `stride`
+// elements per query token.
+struct ScoreOut {
+  void* p;
+  int64_t stride;
+  int bf16;
+};
+
+struct ScoreRow {
+  void* p;
+  int bf16;
+  __device__ __forceinline__ void store(int64_t e, float s) const {
+    if (bf16) reinterpret_cast<uint16_t*>(p)[e] = (uint16_t)f32_to_bf16_bits(s);
+    else reinterpret_cast<float*>(p)[e] = s;
+  }
+};
+
+__device__ __forceinline__ ScoreRow score_row(const ScoreOut& o, int64_t t) {
+  ScoreRow r;
+  r.p = reinterpret_cast<uint8_t*>(o.p) + t * o.stride * (o.bf16 ? 2 : 4);
+  r.bf16 = o.bf16;
+  return r;
+}
+
 // ------------------------------------------------------------------------- fp8 e4m3fn
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {

@@ -20,8 +20,7 @@ constexpr int kIdxTile = 256;
 template <int DI>
 __global__ void __launch_bounds__(256) index_score_valu_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
                                                                int n_I, RowsDev kI, int ratio,
-                                                               float* __restrict__ score, int64_t score_stride,
-                                                               int n_tiles) {
+                                                               ScoreOut score, int n_tiles) {
   __shared__ float qs[64 * DI];
   __shared__ float ws[64];
   const int t = blockIdx.x / n_tiles;
@@ -51,39 +50,36 @@ __global__ void __launch_bounds__(256) index_score_valu_kernel(SeqsDev S, RowsDe
     for (int d = 0; d < DI; ++d) dot = __builtin_fmaf(qs[h * DI + d], kr[d], dot);
     s = __builtin_fmaf(ws[h], fmaxf(dot, 0.f), s);
   }
-  score[(int64_t)t * score_stride + e] = s;
+  score_row(score, t).store(e, s);
 }
 
-bool index_mfma_supported(const RowsDev& qI, const RowsDev& kI, int n_I, int64_t score_stride);
+bool index_mfma_supported(const RowsDev& qI, const RowsDev& kI, int n_I);
 bool index_mx_supported(const RowsDev& qI, const RowsDev& kI, int n_I);
 hipError_t launch_index_score_mx(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
-                                 int ratio, float* score, int64_t score_stride, int max_vis, int max_q,
-                                 hipStream_t stream);
+                                 int ratio, ScoreOut score, int max_vis, int max_q, hipStream_t stream);
 hipError_t launch_index_score_mfma(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
-                                   int ratio, float* score, int64_t score_stride, int max_vis, hipStream_t stream);
+                                   int ratio, ScoreOut score, int max_vis, hipStream_t stream);
 
 hipError_t launch_index_score(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
-                              int ratio, float* score, int64_t score_stride, int max_vis, int max_q,
-                              hipStream_t stream) {
-  if (index_mfma_supported(qI, kI, n_I, score_stride))
-    return launch_index_score_mfma(S, qI, w, n_I, kI, ratio, score, score_stride, max_vis, stream);
+                              int ratio, ScoreOut score, int max_vis, int max_q, hipStream_t stream) {
+  if (index_mfma_supported(qI, kI, n_I)) return launch_index_score_mfma(S, qI, w, n_I, kI, ratio, score, max_vis, stream);
   if (index_mx_supported(qI, kI, n_I))
-    return launch_index_score_mx(S, qI, w, n_I, kI, ratio, score, score_stride, max_vis, max_q, stream);
+    return launch_index_score_mx(S, qI, w, n_I, kI, ratio, score, max_vis, max_q, stream);
   const int n_tiles = (max_vis + kIdxTile - 1) / kIdxTile;
   const int64_t blocks = (int64_t)S.total_q * n_tiles;
   if (blocks == 0) return hipSuccess;
   switch (kI.dim) {
     case 32:
       hipLaunchKernelGGL(index_score_valu_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I, kI,
-                         ratio, score, score_stride, n_tiles);
+                         ratio, score, n_tiles);
       break;
     case 64:
       hipLaunchKernelGGL(index_score_valu_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I, kI,
-                         ratio, score, score_stride, n_tiles);
+                         ratio, score, n_tiles);
       break;
     case 128:
       hipLaunchKernelGGL(index_score_valu_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I,
-                         kI, ratio, score, score_stride, n_tiles);
+                         kI, ratio, score, n_tiles);
       break;
     default:
       return hipErrorInvalidValue;

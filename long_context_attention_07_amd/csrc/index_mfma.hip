@@ -48,8 +48,7 @@ __device__ __forceinline__ void wait_tiles_in_flight(int n) {
 template <int RING, int TILES>
 __device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], int t, const TokenCtx& ctx, int part,
                                             const RowsDev& qI, const float* __restrict__ w, int n_I,
-                                            const RowsDev& kI, int ratio, float* __restrict__ score,
-                                            int64_t score_stride) {
+                                            const RowsDev& kI, int ratio, ScoreOut score) {
   static_assert(RING >= 2 && RING <= 4, "ring depth");
   const int64_t V = (ctx.p + 1) / ratio;
   const int64_t e_begin = (int64_t)part * kIT * TILES;
@@ -122,7 +121,7 @@ __device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], 
       qa[hb][kk] = *reinterpret_cast<const ibf16x8_t*>(qrow + (((g + 4 * kk) ^ c16) * 16));
   }
 
-  float* srow = score + (int64_t)t * score_stride;
+  const ScoreRow srow = score_row(score, t);
   for (int i = 0; i < n_tiles; ++i) {
     const int issued_after = min(n_tiles - 1, i + RING - 2) - i;
     wait_tiles_in_flight(issued_after);
@@ -154,7 +153,7 @@ __device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], 
       s = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
     }
     const int64_t e = e_begin + (int64_t)i * kIT + 16 * wv + c16;
-    if (g == 0 && e < V) srow[e] = s;
+    if (g == 0 && e < V) srow.store(e, s);
   }
 }
 
@@ -164,15 +163,14 @@ __device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], 
 template <int RING, int TILES>
 __global__ void __launch_bounds__(256) index_score_mfma_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
                                                                int n_I, RowsDev kI, int ratio,
-                                                               float* __restrict__ score, int64_t score_stride,
-                                                               int n_parts, int n_logical) {
+                                                               ScoreOut score, int n_parts, int n_logical) {
   __shared__ __align__(16) uint8_t ring[RING][kIT * kIRow];
   const int lid = blockIdx.x;
   if (lid >= n_logical) return;
   const int t = lid / n_parts;
   const int part = lid % n_parts;
   const TokenCtx ctx = token_ctx(S, t);
-  score_range<RING, TILES>(ring, t, ctx, lid % n_parts, qI, w, n_I, kI, ratio, score, score_stride);
+  score_range<RING, TILES>(ring, t, ctx, lid % n_parts, qI, w, n_I, kI, ratio, score);
 }
 
 // Few sequences and query rows (decode): the (token, range) units with entries to score
@@ -195,8 +193,7 @@ __device__ __forceinline__ int wave_incl_sum(int x) {
 template <int RING, int TILES>
 __global__ void __launch_bounds__(256) index_score_mfma_units_kernel(SeqsDev S, RowsDev qI,
                                                                      const float* __restrict__ w, int n_I,
-                                                                     RowsDev kI, int ratio, float* __restrict__ score,
-                                                                     int64_t score_stride) {
+                                                                     RowsDev kI, int ratio, ScoreOut score) {
   __shared__ __align__(16) uint8_t ring[RING][kIT * kIRow];
   constexpr int64_t kPer = (int64_t)kIT * TILES;
   const int lane = threadIdx.x & 63;
@@ -235,20 +232,19 @@ __global__ void __launch_bounds__(256) index_score_mfma_units_kernel(SeqsDev S, 
     ctx.entry0 = readlane64(e0, b);
     ctx.tok0 = 0;
     ctx.tok_lo = 0;
-    score_range<RING, TILES>(ring, bq0 + j, ctx, rem, qI, w, n_I, kI, ratio, score, score_stride);
+    score_range<RING, TILES>(ring, bq0 + j, ctx, rem, qI, w, n_I, kI, ratio, score);
   }
 }
 
 constexpr int kUnitsMaxRows = 64;  // query rows up to which the dense unit numbering is used
 
-bool index_mfma_supported(const RowsDev& qI, const RowsDev& kI, int n_I, int64_t score_stride) {
-  (void)score_stride;
+bool index_mfma_supported(const RowsDev& qI, const RowsDev& kI, int n_I) {
   return qI.dtype == DT_BF16 && kI.dtype == DT_BF16 && kI.dim == 128 && n_I <= 64 && qI.stride % 16 == 0 &&
          kI.stride % 16 == 0;
 }
 
 hipError_t launch_index_score_mfma(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
-                                   int ratio, float* score, int64_t score_stride, int max_vis, hipStream_t stream) {
+                                   int ratio, ScoreOut score, int max_vis, hipStream_t stream) {
   constexpr int kRing = 3, kTiles = 7;  // 48 KiB of LDS (3 workgroups per CU), 448 entries each
   const int per_wg = kIT * kTiles;
   const int n_parts = (max_vis + per_wg - 1) / per_wg;
@@ -256,11 +252,11 @@ hipError_t launch_index_score_mfma(const SeqsDev& S, const RowsDev& qI, const fl
   if (n_log == 0) return hipSuccess;
   if (S.n_seqs <= 64 && S.total_q <= kUnitsMaxRows) {
     hipLaunchKernelGGL((index_score_mfma_units_kernel<kRing, kTiles>), dim3((unsigned)n_log), dim3(256), 0, stream, S,
-                       qI, w, n_I, kI, ratio, score, score_stride);
+                       qI, w, n_I, kI, ratio, score);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((index_score_mfma_kernel<kRing, kTiles>), dim3((unsigned)n_log), dim3(256), 0, stream, S, qI, w,
-                     n_I, kI, ratio, score, score_stride, n_parts, (int)n_log);
+                     n_I, kI, ratio, score, n_parts, (int)n_log);
   return hipGetLastError();
 }
 

@@ -108,8 +108,8 @@ __device__ __forceinline__ float head_sum(const mx_v4f (&acc)[4], const float (&
 
 template <int QB, bool F8>
 __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
-                                                             int n_I, RowsDev kI, int ratio, float* __restrict__ score,
-                                                             int64_t score_stride, int n_parts) {
+                                                             int n_I, RowsDev kI, int ratio, ScoreOut score,
+                                                             int n_parts) {
   const int rb = blockIdx.x / n_parts, part = blockIdx.x % n_parts;
   const int t_blk = rb * QB;
   const int t_end = min(t_blk + QB, S.total_q);
@@ -175,7 +175,7 @@ __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev 
             if (F8) s *= kb[u].sc;
             const int64_t e = eb + c16;
             const int64_t v_i = (ctx.p + i + 1) / ratio;
-            if (g == 0 && e < v_i && e < e_stop) score[(int64_t)(t0 + i) * score_stride + e] = s;
+            if (g == 0 && e < v_i && e < e_stop) score_row(score, t0 + i).store(e, s);
           }
         }
       }
@@ -205,7 +205,7 @@ __device__ __forceinline__ float pair_sum32(float x) {
 template <bool F8>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 index_score_mx_block_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w, int n_I, RowsDev kI, int ratio,
-                            float* __restrict__ score, int64_t score_stride, int n_parts) {
+                            ScoreOut score, int n_parts) {
   // Consecutive workgroups (dealt round-robin to the eight XCDs) take consecutive query
   // blocks of one part, the latest (most entries) first, so every XCD gets an even share
   // of the causal triangle and the longest rows start early.
@@ -246,7 +246,7 @@ index_score_mx_block_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w, 
       // entries this lane stores: below both the stored row's visible count and the part's end
       const bool row_on = g < 2 && my_row < nq;
       const int e_lim = row_on ? min((int)((ctx.p + my_row + 1) / ratio), e_stop) : 0;
-      float* srow = score + (int64_t)(t0 + (row_on ? my_row : 0)) * score_stride;
+      const ScoreRow srow = score_row(score, t0 + (row_on ? my_row : 0));
       // key fragments of a step's four 16-entry blocks (entries past the run's last visible
       // one read that entry instead: a valid row, never stored)
       auto fetch = [&](int e0, MxOperand<F8>* kb) {
@@ -273,7 +273,7 @@ index_score_mx_block_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w, 
           float tot = pair_sum32(pair_sum16(sr[1], sr[0]));
           if (F8) tot *= kb[u].sc;
           const int e = eb + c16;
-          if (e < e_lim) srow[e] = tot;
+          if (e < e_lim) srow.store(e, tot);
         }
       };
       // two register sets in turn: the next step's fragments load during this step
@@ -299,28 +299,27 @@ bool index_mx_supported(const RowsDev& qI, const RowsDev& kI, int n_I) {
 
 template <bool F8>
 static void launch_mx(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI, int ratio,
-                      float* score, int64_t score_stride, int max_vis, int max_q, hipStream_t stream) {
+                      ScoreOut score, int max_vis, int max_q, hipStream_t stream) {
   if (max_q >= 16) {
     const int parts = (max_vis + kMxPart - 1) / kMxPart;
     const int64_t blocks = (int64_t)((S.total_q + 4 * kMxQW - 1) / (4 * kMxQW)) * parts;
     hipLaunchKernelGGL(index_score_mx_block_kernel<F8>, dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I,
-                       kI, ratio, score, score_stride, parts);
+                       kI, ratio, score, parts);
   } else {
     const int n_parts = (max_vis + kMxRange - 1) / kMxRange;
     const int64_t blocks = (int64_t)S.total_q * n_parts;
     hipLaunchKernelGGL((index_score_mx_kernel<1, F8>), dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I,
-                       kI, ratio, score, score_stride, n_parts);
+                       kI, ratio, score, n_parts);
   }
 }
 
 hipError_t launch_index_score_mx(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
-                                 int ratio, float* score, int64_t score_stride, int max_vis, int max_q,
-                                 hipStream_t stream) {
+                                 int ratio, ScoreOut score, int max_vis, int max_q, hipStream_t stream) {
   if (max_vis <= 0 || S.total_q == 0) return hipSuccess;
   if (qI.dtype == DT_FP8_B128)
-    launch_mx<true>(S, qI, w, n_I, kI, ratio, score, score_stride, max_vis, max_q, stream);
+    launch_mx<true>(S, qI, w, n_I, kI, ratio, score, max_vis, max_q, stream);
   else
-    launch_mx<false>(S, qI, w, n_I, kI, ratio, score, score_stride, max_vis, max_q, stream);
+    launch_mx<false>(S, qI, w, n_I, kI, ratio, score, max_vis, max_q, stream);
   return hipGetLastError();
 }
 

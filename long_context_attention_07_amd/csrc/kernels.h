@@ -15,15 +15,14 @@ hipError_t launch_compress2(const SeqsDev& S, const RowsDev& c0, const RowsDev& 
                             int max_q, hipStream_t stream);
 
 hipError_t launch_index_score(const SeqsDev& S, const RowsDev& qI, const float* w, int n_I, const RowsDev& kI,
-                              int ratio, float* score, int64_t score_stride, int max_vis, int max_q,
-                              hipStream_t stream);
+                              int ratio, ScoreOut score, int max_vis, int max_q, hipStream_t stream);
 
 // Top-k selection.  With ws_bytes >= topk_workspace_bytes(...) rows longer than 32768
 // candidates run on several workgroups per token (slices, then a merge); the selection is
 // the same.
 size_t topk_workspace_bytes(int total_q, int max_vis, int k);
-hipError_t launch_topk(const SeqsDev& S, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
-                       int max_vis, int max_q, void* ws, size_t ws_bytes, hipStream_t stream);
+hipError_t launch_topk(const SeqsDev& S, const void* score, int score_bf16, int64_t score_stride, int ratio, int k,
+                       int32_t* idx, int max_vis, int max_q, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Attention over per-token key lists.  mode_csa: keys = idx entries (k slots) then the
 // window; otherwise keys = entries 0..V(p)-1 then the window.

@@ -13,7 +13,8 @@
 // registers (8, 16 or 32 consecutive keys per thread), each pass has its own LDS histogram
 // and the digit searches and the compaction offsets use DPP wave scans.  Longer lists run
 // in two stages over several workgroups when a workspace is given (below), else one
-// workgroup re-reads the scores from memory every pass.
+// workgroup re-reads the scores from memory every pass.  Scores are float32, or bf16 (the
+// selector's bf16 scores of section 3.4), keyed as the float32 values they stand for.
 
 #include "common.cuh"
 #include "kernels.h"
@@ -27,6 +28,9 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   if ((u & 0x7fffffffu) == 0) u = 0;  // -0 == +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// bf16 scores: the key of the float32 value the bf16 bits stand for, so both score types
+// order and tie alike.
+__device__ __forceinline__ uint32_t score_key(uint16_t b) { return score_key(__uint_as_float((uint32_t)b << 16)); }
 
 // Exclusive prefix sums over the 1024 threads of two counters at once; `red` needs 32
 // words.  Returns the exclusive prefixes and writes the totals.
@@ -72,8 +76,8 @@ struct TopkLds {
 
 // Selection for key lists longer than the register path takes: every pass re-reads the
 // scores from memory; contiguous segments per thread for the compaction.
-__device__ void topk_select_mem(const float* __restrict__ src, int n, int k, int32_t* __restrict__ out,
-                                TopkLds& sh) {
+template <typename ST>
+__device__ void topk_select_mem(const ST* __restrict__ src, int n, int k, int32_t* __restrict__ out, TopkLds& sh) {
   uint32_t* hist = sh.hist;
   uint32_t* red = sh.red;
   const int tid = threadIdx.x;
@@ -218,17 +222,24 @@ __device__ __forceinline__ uint3 topk_find_digit(const uint32_t* hist, int nbins
 // writes its kept indices in ascending order.
 // Thread tid's keys NPT tid .. NPT tid + NPT-1 of the row, those below `lim` (16 bytes at a
 // time when the row is 16-byte aligned); the rest 0.
-template <int NPT>
-__device__ __forceinline__ void topk_load_keys(const float* __restrict__ src, int lim, uint32_t (&key)[NPT]) {
+template <int NPT, typename ST>
+__device__ __forceinline__ void topk_load_keys(const ST* __restrict__ src, int lim, uint32_t (&key)[NPT]) {
   const int i0 = NPT * (int)threadIdx.x;
-  if ((reinterpret_cast<uintptr_t>(src) & 15u) == 0 && i0 + NPT <= lim) {
+  constexpr int per16 = 16 / (int)sizeof(ST);  // scores per 16-byte load
+  if ((reinterpret_cast<uintptr_t>(src + i0) & 15u) == 0 && i0 + NPT <= lim) {
 #pragma unroll
-    for (int q = 0; q < NPT / 4; ++q) {
-      const float4 v = reinterpret_cast<const float4*>(src + i0)[q];
-      key[4 * q] = score_key(v.x);
-      key[4 * q + 1] = score_key(v.y);
-      key[4 * q + 2] = score_key(v.z);
-      key[4 * q + 3] = score_key(v.w);
+    for (int q = 0; q < NPT / per16; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(src + i0)[q];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (sizeof(ST) == 4) {
+          key[4 * q + u] = score_key(__uint_as_float(w4[u]));
+        } else {
+          key[per16 * q + 2 * u] = score_key((uint16_t)(w4[u] & 0xffffu));
+          key[per16 * q + 2 * u + 1] = score_key((uint16_t)(w4[u] >> 16));
+        }
+      }
     }
   } else {
 #pragma unroll
@@ -239,7 +250,10 @@ __device__ __forceinline__ void topk_load_keys(const float* __restrict__ src, in
 // The selection over keys held as above; keys at n and beyond take no part.  Every kept
 // key j of this thread is handed to emit(pos, j, key[j]), pos being its rank among the
 // kept keys in ascending position order (0 .. min(k, n) - 1).
-template <int NPT, class Emit>
+// LOWC: the keys come from bf16 scores, so their low 16 bits are fixed by the sign (0 for
+// keys of scores >= 0, all ones below): keys that agree in their top 24 bits are equal,
+// and the last digit pass is skipped.
+template <int NPT, bool LOWC, class Emit>
 __device__ __forceinline__ void topk_select_keys_emit(const uint32_t (&key)[NPT], int n, int k, TopkRegLds& sh,
                                                       Emit emit) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -277,6 +291,8 @@ __device__ __forceinline__ void topk_select_keys_emit(const uint32_t (&key)[NPT]
     if (r.z == remaining && p1 != 0u) {
       T = (p1 << 8) - 1u;
       remaining = 0u;
+    } else if (LOWC) {
+      T = (p1 << 8) | (((p1 >> 23) & 1u) ? 0x00u : 0xffu);  // every key of the bin equals T
     } else {
 #pragma unroll
       for (int j = 0; j < NPT; ++j)
@@ -317,22 +333,23 @@ __device__ __forceinline__ void topk_select_keys_emit(const uint32_t (&key)[NPT]
   }
 }
 
-template <int NPT>
+template <int NPT, bool LOWC>
 __device__ void topk_select_keys(const uint32_t (&key)[NPT], int n, int k, int32_t* __restrict__ out,
                                  TopkRegLds& sh) {
   const int i0 = NPT * (int)threadIdx.x;
-  topk_select_keys_emit<NPT>(key, n, k, sh, [&](uint32_t pos, int j, uint32_t) { out[pos] = i0 + j; });
+  topk_select_keys_emit<NPT, LOWC>(key, n, k, sh, [&](uint32_t pos, int j, uint32_t) { out[pos] = i0 + j; });
 }
 
-template <int NPT>
-__device__ __forceinline__ void topk_select_reg(const float* __restrict__ src, int n, int k, int32_t* __restrict__ out,
+template <int NPT, typename ST>
+__device__ __forceinline__ void topk_select_reg(const ST* __restrict__ src, int n, int k, int32_t* __restrict__ out,
                                                 TopkRegLds& sh) {
   uint32_t key[NPT];
   topk_load_keys<NPT>(src, n, key);
-  topk_select_keys<NPT>(key, n, k, out, sh);
+  topk_select_keys<NPT, sizeof(ST) == 2>(key, n, k, out, sh);
 }
 
-__global__ void __launch_bounds__(kTopkThreads) topk_kernel(SeqsDev S, const float* __restrict__ score,
+template <typename ST>
+__global__ void __launch_bounds__(kTopkThreads) topk_kernel(SeqsDev S, const ST* __restrict__ score,
                                                             int64_t score_stride, int ratio, int k,
                                                             int32_t* __restrict__ idx) {
   __shared__ TopkLds sh;
@@ -341,7 +358,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(SeqsDev S, const flo
   const TokenCtx ctx = token_ctx(S, t);
   const int64_t V = (ctx.p + 1) / ratio;
   int32_t* out = idx + (int64_t)t * k;
-  const float* src = score + (int64_t)t * score_stride;
+  const ST* src = score + (int64_t)t * score_stride;
   if (V <= k) {
     for (int i = threadIdx.x; i < k; i += kTopkThreads) out[i] = (i < V) ? i : -1;
     return;
@@ -356,14 +373,14 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(SeqsDev S, const flo
 // lookup, so the keys below min(row stride, 1024 NPT) are requested first and the lookup
 // overlaps them; keys at V and beyond take no part.  The selection is the same function
 // of the row, so a token's indices do not depend on the kernel.
-template <int NPT>
-__global__ void __launch_bounds__(kTopkThreads) topk_decode_kernel(SeqsDev S, const float* __restrict__ score,
+template <int NPT, typename ST>
+__global__ void __launch_bounds__(kTopkThreads) topk_decode_kernel(SeqsDev S, const ST* __restrict__ score,
                                                                    int64_t score_stride, int ratio, int k,
                                                                    int32_t* __restrict__ idx) {
   __shared__ TopkLds sh;
   __shared__ TopkRegLds rsh;
   const int t = blockIdx.x;
-  const float* src = score + (int64_t)t * score_stride;
+  const ST* src = score + (int64_t)t * score_stride;
   uint32_t key[NPT];
   topk_load_keys<NPT>(src, (int)min(score_stride, (int64_t)NPT * kTopkThreads), key);
   const TokenCtx ctx = token_ctx(S, t);
@@ -377,7 +394,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_decode_kernel(SeqsDev S, co
     topk_select_mem(src, (int)V, k, out, sh);
     return;
   }
-  topk_select_keys<NPT>(key, (int)V, k, out, rsh);
+  topk_select_keys<NPT, sizeof(ST) == 2>(key, (int)V, k, out, rsh);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -395,8 +412,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_decode_kernel(SeqsDev S, co
 
 constexpr int kTopkRegMax = 32 * kTopkThreads;  // longest row the one-workgroup path holds in registers
 
-template <int NPT>
-__global__ void __launch_bounds__(kTopkThreads) topk_slice_kernel(SeqsDev S, const float* __restrict__ score,
+template <int NPT, typename ST>
+__global__ void __launch_bounds__(kTopkThreads) topk_slice_kernel(SeqsDev S, const ST* __restrict__ score,
                                                                   int64_t score_stride, int ratio, int k,
                                                                   int32_t* __restrict__ idx,
                                                                   uint32_t* __restrict__ cand_key,
@@ -407,7 +424,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_slice_kernel(SeqsDev S, con
   const TokenCtx ctx = token_ctx(S, t);
   const int64_t V = (ctx.p + 1) / ratio;
   const int ns = (int)((V + SL - 1) / SL);
-  const float* row = score + (int64_t)t * score_stride;
+  const ST* row = score + (int64_t)t * score_stride;
   if (ns <= 1) {  // the whole row is one slice: the final selection
     if (s != 0) return;
     int32_t* out = idx + (int64_t)t * k;
@@ -421,7 +438,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_slice_kernel(SeqsDev S, con
   if (s >= ns) return;
   const int64_t base = (int64_t)s * SL;
   const int len = (int)min((int64_t)SL, V - base);
-  const float* src = row + base;
+  const ST* src = row + base;
   uint32_t* ck = cand_key + ((int64_t)t * n_slices + s) * k;
   int32_t* ci = cand_idx + ((int64_t)t * n_slices + s) * k;
   if (len <= k) {
@@ -434,7 +451,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_slice_kernel(SeqsDev S, con
   uint32_t key[NPT];
   topk_load_keys<NPT>(src, len, key);
   const int i0 = NPT * (int)threadIdx.x;
-  topk_select_keys_emit<NPT>(key, len, k, rsh, [&](uint32_t pos, int j, uint32_t kv) {
+  topk_select_keys_emit<NPT, sizeof(ST) == 2>(key, len, k, rsh, [&](uint32_t pos, int j, uint32_t kv) {
     ck[pos] = kv;
     ci[pos] = (int32_t)(base + i0 + j);
   });
@@ -459,7 +476,7 @@ __device__ __forceinline__ void topk_load_u32(const uint32_t* __restrict__ src, 
   }
 }
 
-template <int NPT>
+template <int NPT, bool LOWC>
 __global__ void __launch_bounds__(kTopkThreads) topk_merge_kernel(SeqsDev S, int ratio, int k, int SL,
                                                                   int32_t* __restrict__ idx,
                                                                   const uint32_t* __restrict__ cand_key,
@@ -477,7 +494,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_merge_kernel(SeqsDev S, int
   topk_load_u32<NPT>(ck, n, key);
   int32_t* out = idx + (int64_t)t * k;
   const int i0 = NPT * (int)threadIdx.x;
-  topk_select_keys_emit<NPT>(key, n, k, rsh, [&](uint32_t pos, int j, uint32_t) { out[pos] = ci[i0 + j]; });
+  topk_select_keys_emit<NPT, LOWC>(key, n, k, rsh, [&](uint32_t pos, int j, uint32_t) { out[pos] = ci[i0 + j]; });
 }
 
 // Slice length of the two-stage path for rows up to max_vis and this k, or 0 when the
@@ -498,8 +515,9 @@ size_t topk_workspace_bytes(int total_q, int max_vis, int k) {
   return (size_t)total_q * (size_t)ns * (size_t)k * (sizeof(uint32_t) + sizeof(int32_t));
 }
 
-hipError_t launch_topk(const SeqsDev& S, const float* score, int64_t score_stride, int ratio, int k, int32_t* idx,
-                       int max_vis, int max_q, void* ws, size_t ws_bytes, hipStream_t stream) {
+template <typename ST>
+static hipError_t launch_topk_t(const SeqsDev& S, const ST* score, int64_t score_stride, int ratio, int k, int32_t* idx,
+                                int max_vis, int max_q, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (S.total_q == 0) return hipSuccess;
   const size_t need = topk_workspace_bytes(S.total_q, max_vis, k);
   if (need > 0 && ws != nullptr && ws_bytes >= need) {
@@ -509,40 +527,49 @@ hipError_t launch_topk(const SeqsDev& S, const float* score, int64_t score_strid
     int32_t* ci = reinterpret_cast<int32_t*>(ck + (size_t)S.total_q * ns * k);
     const dim3 grid1((unsigned)((int64_t)S.total_q * ns));
     if (SL == 16 * kTopkThreads)
-      hipLaunchKernelGGL(topk_slice_kernel<16>, grid1, dim3(kTopkThreads), 0, stream, S, score, score_stride, ratio, k,
+      hipLaunchKernelGGL((topk_slice_kernel<16, ST>), grid1, dim3(kTopkThreads), 0, stream, S, score, score_stride, ratio, k,
                          idx, ck, ci, ns);
     else
-      hipLaunchKernelGGL(topk_slice_kernel<32>, grid1, dim3(kTopkThreads), 0, stream, S, score, score_stride, ratio, k,
+      hipLaunchKernelGGL((topk_slice_kernel<32, ST>), grid1, dim3(kTopkThreads), 0, stream, S, score, score_stride, ratio, k,
                          idx, ck, ci, ns);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t cands = (int64_t)ns * k;
     const dim3 grid2((unsigned)S.total_q);
     if (cands <= 8 * kTopkThreads)
-      hipLaunchKernelGGL(topk_merge_kernel<8>, grid2, dim3(kTopkThreads), 0, stream, S, ratio, k, SL, idx, ck, ci, ns);
+      hipLaunchKernelGGL((topk_merge_kernel<8, sizeof(ST) == 2>), grid2, dim3(kTopkThreads), 0, stream, S, ratio, k, SL, idx, ck, ci, ns);
     else if (cands <= 16 * kTopkThreads)
-      hipLaunchKernelGGL(topk_merge_kernel<16>, grid2, dim3(kTopkThreads), 0, stream, S, ratio, k, SL, idx, ck, ci,
+      hipLaunchKernelGGL((topk_merge_kernel<16, sizeof(ST) == 2>), grid2, dim3(kTopkThreads), 0, stream, S, ratio, k, SL, idx, ck, ci,
                          ns);
     else
-      hipLaunchKernelGGL(topk_merge_kernel<32>, grid2, dim3(kTopkThreads), 0, stream, S, ratio, k, SL, idx, ck, ci,
+      hipLaunchKernelGGL((topk_merge_kernel<32, sizeof(ST) == 2>), grid2, dim3(kTopkThreads), 0, stream, S, ratio, k, SL, idx, ck, ci,
                          ns);
     return hipGetLastError();
   }
   if (max_q == 1 && max_vis > k && max_vis <= 32 * kTopkThreads) {
     if (max_vis <= 8 * kTopkThreads)
-      hipLaunchKernelGGL(topk_decode_kernel<8>, dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score, score_stride,
+      hipLaunchKernelGGL((topk_decode_kernel<8, ST>), dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score, score_stride,
                          ratio, k, idx);
     else if (max_vis <= 16 * kTopkThreads)
-      hipLaunchKernelGGL(topk_decode_kernel<16>, dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score,
+      hipLaunchKernelGGL((topk_decode_kernel<16, ST>), dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score,
                          score_stride, ratio, k, idx);
     else
-      hipLaunchKernelGGL(topk_decode_kernel<32>, dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score,
+      hipLaunchKernelGGL((topk_decode_kernel<32, ST>), dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score,
                          score_stride, ratio, k, idx);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(topk_kernel, dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score, score_stride, ratio, k,
+  hipLaunchKernelGGL(topk_kernel<ST>, dim3(S.total_q), dim3(kTopkThreads), 0, stream, S, score, score_stride, ratio, k,
                      idx);
   return hipGetLastError();
+}
+
+hipError_t launch_topk(const SeqsDev& S, const void* score, int score_bf16, int64_t score_stride, int ratio, int k,
+                       int32_t* idx, int max_vis, int max_q, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (score_bf16)
+    return launch_topk_t(S, static_cast<const uint16_t*>(score), score_stride, ratio, k, idx, max_vis, max_q, ws,
+                         ws_bytes, stream);
+  return launch_topk_t(S, static_cast<const float*>(score), score_stride, ratio, k, idx, max_vis, max_q, ws, ws_bytes,
+                       stream);
 }
 
 }  // namespace csa

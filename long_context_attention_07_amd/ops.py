@@ -15,10 +15,11 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
 F32, BF16, KV_SPLIT, MXFP4, FP8_B128 = 0, 1, 2, 3, 4
 KV_SPLIT_BF16_DIMS = 64
-OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND, OP_TOPK = 1, 2, 3, 4
+OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND, OP_TOPK, OP_INDEX_TOPK_BF16 = 1, 2, 3, 4, 5
 
-EXPORTS = ("csa_compress", "csa_compress2", "csa_index_score", "csa_topk", "csa_index_topk", "csa_index_topk_noalloc",
-           "csa_attend", "hca_attend", "csa_workspace_bytes", "csa_strerror", "csa_last_error", "csa_version")
+EXPORTS = ("csa_compress", "csa_compress2", "csa_index_score", "csa_index_score_bf16", "csa_topk", "csa_topk_bf16",
+           "csa_index_topk", "csa_index_topk_bf16", "csa_index_topk_noalloc", "csa_attend", "hca_attend",
+           "csa_workspace_bytes", "csa_strerror", "csa_last_error", "csa_version")
 
 
 class CsaError(RuntimeError):
@@ -56,6 +57,9 @@ def lib():
                                     P(csa_rows), P(csa_rows), vp, i32, P(csa_rows), vp]
         L.csa_index_score.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, vp, i64, vp]
         L.csa_topk.argtypes = [P(csa_seqs), vp, i64, i32, i32, vp, vp, sz, vp]
+        L.csa_topk_bf16.argtypes = [P(csa_seqs), vp, i64, i32, i32, vp, vp, sz, vp]
+        L.csa_index_score_bf16.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, vp, i64, vp]
+        L.csa_index_topk_bf16.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, i32, vp, vp, sz, vp]
         L.csa_index_topk.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, i32, vp, vp, sz, vp]
         L.csa_index_topk_noalloc.argtypes = [P(csa_seqs), P(csa_rows), vp, i32, P(csa_rows), i32, i32, vp, vp]
         L.csa_attend.argtypes = [P(csa_seqs), P(csa_rows), i32, P(csa_rows), vp, i32, P(csa_rows), i32, vp, f32, i32,
@@ -69,8 +73,9 @@ def lib():
         L.csa_last_error.argtypes = []
         L.csa_last_error.restype = ctypes.c_char_p
         L.csa_version.restype = i32
-        for f in ("csa_compress", "csa_compress2", "csa_index_score", "csa_topk", "csa_index_topk",
-                  "csa_index_topk_noalloc", "csa_attend", "hca_attend"):
+        for f in ("csa_compress", "csa_compress2", "csa_index_score", "csa_index_score_bf16", "csa_topk",
+                  "csa_topk_bf16", "csa_index_topk", "csa_index_topk_bf16", "csa_index_topk_noalloc", "csa_attend",
+                  "hca_attend"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -173,6 +178,24 @@ def csa_topk(seqs, score, ratio, k, idx, ws=None, stream=None):
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib().csa_topk(ctypes.byref(seqs.c), _ptr(score), score.stride(0), ratio, k, _ptr(idx), _ptr(ws), nbytes,
                           _stream(stream)), "csa_topk")
+
+
+def csa_index_score_bf16(seqs, qI, w, n_I, kI, ratio, score, stream=None):
+    """score: int16 (or uint16) tensor [total_q, stride] receiving the bf16 bit patterns."""
+    _check(lib().csa_index_score_bf16(ctypes.byref(seqs.c), ctypes.byref(qI.c), _ptr(w), n_I, ctypes.byref(kI.c),
+                                      ratio, _ptr(score), score.stride(0), _stream(stream)), "csa_index_score_bf16")
+
+
+def csa_topk_bf16(seqs, score, ratio, k, idx, ws=None, stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().csa_topk_bf16(ctypes.byref(seqs.c), _ptr(score), score.stride(0), ratio, k, _ptr(idx), _ptr(ws),
+                               nbytes, _stream(stream)), "csa_topk_bf16")
+
+
+def csa_index_topk_bf16(seqs, qI, w, n_I, kI, ratio, k, idx, ws=None, stream=None):
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().csa_index_topk_bf16(ctypes.byref(seqs.c), ctypes.byref(qI.c), _ptr(w), n_I, ctypes.byref(kI.c), ratio,
+                                     k, _ptr(idx), _ptr(ws), nbytes, _stream(stream)), "csa_index_topk_bf16")
 
 
 def csa_index_topk(seqs, qI, w, n_I, kI, ratio, k, idx, ws=None, stream=None):

@@ -15,10 +15,15 @@ Readings:
   are <= p, i.e. i < V(p) = floor((p + 1) / m);
 * top-k: the k largest scores, equal scores ordered by the lower entry index; the
   selected indices are returned in ascending order and padded with -1; when V(p) <= k
-  every visible entry is selected.
+  every visible entry is selected;
+* bf16 selector (section 3.4: the index scores are quantised from FP32 to BF16 to make
+  the selector faster): each score is rounded to bf16, nearest even, and the same top-k
+  runs on the rounded values (more scores now tie, and ties go to the lower index).
 """
 
 import numpy as np
+
+from .formats import bf16_round
 
 
 def visible(p, ratio):
@@ -45,3 +50,14 @@ def topk_select(scores, k):
     order = np.lexsort((np.arange(E), -s))   # primary: score descending, then index
     out[:] = np.sort(order[:k])
     return out
+
+
+def bf16_scores(scores):
+    """The selector's bf16 scores: float64 scores rounded to bf16 (RNE), as float64."""
+    return bf16_round(np.asarray(scores, dtype=np.float64))
+
+
+def index_topk_bf16(qI, w, kI, k):
+    """Top-k on bf16-rounded index scores; returns (idx, bf16 scores)."""
+    s = bf16_scores(index_scores(qI, w, kI))
+    return topk_select(s, k), s

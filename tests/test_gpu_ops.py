@@ -321,6 +321,86 @@ def test_topk_sliced_rows_exact(k):
         assert list(gi[r]) == list(ref), f"row {r} (V={L}, k={k})"
 
 
+@pytest.mark.parametrize("k", [64, 512, 1024])
+def test_topk_bf16_scores_exact(k):
+    """Selection on bf16 scores (exact ties are common): against the oracle's selection on
+    the same values, for rows held in registers, streamed (no workspace) and sliced (with
+    one), next to a row of only +-0 and one with every score equal."""
+    g = np.random.default_rng(51 + k)
+    ratio = 1
+    ctx = [300, 5000, 16384, 40000, 70000, 3000, 1200]
+    ob, sq, _, _ = make_batch([1] * len(ctx), ctx, ratio)
+    stride = max(ctx) + 8
+    vals = np.zeros((len(ctx), stride), dtype=np.float32)
+    for r, L in enumerate(ctx):
+        if r == 5:
+            vals[r, :L] = np.where(g.random(L) < 0.5, 0.0, -0.0)
+        elif r == 6:
+            vals[r, :L] = 2.5
+        else:
+            vals[r, :L] = (g.standard_normal(L) * 3 + 12).astype(np.float32)
+    bits = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).to(DEV)
+    ref_vals = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float64).numpy()
+    ws = torch.empty(ops.csa_workspace_bytes(ops.OP_TOPK, sq, k=k, ratio=ratio) // 4 + 1, device=DEV)
+    got = torch.full((len(ctx), k), -7, dtype=torch.int32, device=DEV)
+    one = torch.full((len(ctx), k), -9, dtype=torch.int32, device=DEV)
+    ops.csa_topk_bf16(sq, bits, ratio, k, got, ws=ws)
+    ops.csa_topk_bf16(sq, bits, ratio, k, one)
+    torch.cuda.synchronize()
+    assert torch.equal(got, one), "sliced and one-workgroup selections differ"
+    gi = got.cpu().numpy()
+    for r, L in enumerate(ctx):
+        ref = topk_select(ref_vals[r, :L], k)
+        assert list(gi[r]) == list(ref), f"row {r} (V={L}, k={k})"
+
+
+@pytest.mark.parametrize("fmt,d_I,n_I", [(ops.BF16, 128, 64), (ops.MXFP4, 128, 64), (ops.FP8_B128, 128, 64),
+                                         (ops.F32, 32, 4)])
+def test_index_scores_bf16_and_fused_selection(fmt, d_I, n_I):
+    """bf16 index scores: every one is the nearest-even bf16 of the float32 score the same
+    kernel writes (bit for bit), and within the code-domain rule of the oracle's score (the
+    neighbouring bf16 value only where the oracle's score lies within the float32 error
+    bound of a rounding boundary); the fused index + top-k equals the two calls and the
+    oracle's selection on the GPU's bf16 scores."""
+    g = np.random.default_rng(61 + d_I + fmt)
+    ratio, k = 4, 64
+    n_q = [3, 1, 40, 1, 30]
+    ctx = [700, 2051, 1900, 140000, 90]
+    ob, sq, n_ent, _ = make_batch(n_q, ctx, ratio)
+    kI_rows, kI_val = _rows_in(fmt, g.standard_normal((n_ent, d_I)))
+    qI_rows, qI_val = _rows_in(fmt, g.standard_normal((sq.total_q * n_I, d_I)))
+    w_t, w_val = f32(g.standard_normal((sq.total_q, n_I)) / math.sqrt(n_I))
+    stride = sq.max_ctx // ratio + 3
+    s32 = torch.full((sq.total_q, stride), float("nan"), dtype=torch.float32, device=DEV)
+    s16 = torch.full((sq.total_q, stride), -1, dtype=torch.int16, device=DEV)
+    ops.csa_index_score(sq, qI_rows, w_t, n_I, kI_rows, ratio, s32)
+    ops.csa_index_score_bf16(sq, qI_rows, w_t, n_I, kI_rows, ratio, s16)
+    idx2 = torch.full((sq.total_q, k), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(ops.csa_workspace_bytes(ops.OP_TOPK, sq, k=k, ratio=ratio) // 4 + 1, device=DEV)
+    ops.csa_topk_bf16(sq, s16, ratio, k, idx2, ws=ws)
+    idx = torch.full((sq.total_q, k), -9, dtype=torch.int32, device=DEV)
+    wsf = torch.empty(ops.csa_workspace_bytes(ops.OP_INDEX_TOPK_BF16, sq, k=k, ratio=ratio) // 4 + 1, device=DEV)
+    ops.csa_index_topk_bf16(sq, qI_rows, w_t, n_I, kI_rows, ratio, k, idx, ws=wsf)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2), "fused bf16 index + top-k differs from the two calls"
+    sb = s16.cpu().numpy().view(np.uint16)
+    s32h = s32.cpu().numpy()
+    gi = idx.cpu().numpy()
+    for row, b, p in ob.tokens():
+        V = visible(p, ratio)
+        want = torch.from_numpy(s32h[row, :V].copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(sb[row, :V], want), f"token {row}: bf16 score is not the rounding of the float32 one"
+        assert np.all(sb[row, V:] == 0xFFFF), f"token {row}: columns >= V written"
+        kI = kI_val[ob.entry_off[b]: ob.entry_off[b] + V]
+        qI = qI_val[row * n_I:(row + 1) * n_I]
+        ref = index_scores(qI, w_val[row], kI)
+        band = score_error_bound(qI, w_val[row], kI) if V else np.zeros(0)
+        got = F.decode_bf16(sb[row, :V])
+        lo, hi = F.bf16_round(ref - band), F.bf16_round(ref + band)
+        assert np.all((got >= lo) & (got <= hi)), f"token {row}: bf16 score off the allowed codes"
+        assert list(gi[row]) == list(topk_select(got, k)), f"token {row}: selection differs on the GPU's scores"
+
+
 @pytest.mark.parametrize("keep", ["all", "upto16384"])
 def test_topk_bin_taken_whole(keep):
     """Rows built so that the bin of the k-th key holds exactly the keys still needed after

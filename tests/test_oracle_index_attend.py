@@ -10,7 +10,7 @@ import torch
 from oracle import pipeline as P
 from oracle.attention import attend_core, attend_token, token_keys, window_positions
 from oracle.compress import compress_entries
-from oracle.indexer import index_scores, topk_select, visible
+from oracle.indexer import bf16_scores, index_scores, index_topk_bf16, topk_select, visible
 from oracle.rope import rope
 
 
@@ -68,6 +68,43 @@ def test_topk_small_and_invariances():
     a = topk_select(index_scores(qI, w, kI), 32)
     b = topk_select(index_scores(qI, 3.7 * w, kI), 32)
     assert list(a) == list(b)
+
+
+def test_bf16_selector_matches_torch_cast_and_stable_sort():
+    """The bf16 selector against library routines: torch's bf16 cast of the float64 scores,
+    then torch's stable descending sort (equal values keep index order), first k indices
+    in ascending order."""
+    g = np.random.default_rng(4)
+    for trial in range(20):
+        E = int(g.integers(50, 3000))
+        k = int(g.integers(1, 300))
+        # positive float32 values near 10 (a bf16 ulp is 1/16: many ties); float32 inputs, so
+        # torch rounds once, from float32
+        s = (np.abs(g.standard_normal(E)) * 4 + 10).astype(np.float32).astype(np.float64)
+        idx, sb = index_topk_bf16(np.ones((1, 1)), np.ones(1), s[:, None], k)
+        tb = torch.from_numpy(s.astype(np.float32)).to(torch.bfloat16)
+        np.testing.assert_array_equal(sb, tb.to(torch.float64).numpy())
+        order = torch.sort(tb.to(torch.float32), descending=True, stable=True).indices.numpy()
+        ref = sorted(order[:min(k, E)].tolist())
+        assert list(idx) == ref + [-1] * (k - len(ref))
+
+
+def test_bf16_selector_ties_and_difference_from_float():
+    """Scores that differ in float but round to one bf16 value tie, and the lower index
+    wins; the float selection keeps the larger score instead."""
+    s = np.array([1.0, 1.0 + 2.0 ** -10, 1.0 + 2.0 ** -9, 0.5, 1.0 + 2.0 ** -7])
+    # bf16 spacing at 1 is 2^-7: the first three round to 1.0, the last is the next value
+    np.testing.assert_array_equal(bf16_scores(s), [1.0, 1.0, 1.0, 0.5, 1.0 + 2.0 ** -7])
+    assert list(topk_select(s, 2)) == [2, 4]
+    assert list(topk_select(bf16_scores(s), 2)) == [0, 4]
+    # the fused helper: scores from the indexer formula, then the same rounding
+    qI, w = np.array([[1.0]]), np.array([1.0])
+    idx, sb = index_topk_bf16(qI, w, s[:, None], 2)
+    assert list(idx) == [0, 4] and np.array_equal(sb, bf16_scores(s))
+    # ties exactly at a rounding midpoint go to the even bf16 pattern
+    mid = 1.0 + 2.0 ** -8
+    assert bf16_scores(np.array([mid]))[0] == 1.0
+    assert bf16_scores(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
 
 
 def test_visibility():

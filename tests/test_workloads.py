@@ -165,6 +165,27 @@ def test_csa_decode_full_size():
         worst["lse"] = max(worst["lse"], assert_close(l_gpu[b], lr, 1e-2, f"c2 lse seq {b}"))
     log(f"c2: worst scaled errors {worst}, top-k tie swaps {swaps}")
 
+    # the selector on bf16 scores: exact on the GPU's own bf16 scores, each score the
+    # rounding of the float32 one; recall of the float32 selection reported
+    s16 = torch.full((n, stride), -1, dtype=torch.int16, device=DEV)
+    ops.csa_index_score_bf16(sq, R["qI"], x["w"], wl.n_I, R["kI"], ratio, s16)
+    idx16 = torch.empty((n, k), dtype=torch.int32, device=DEV)
+    ws16 = torch.empty(ops.csa_workspace_bytes(ops.OP_INDEX_TOPK_BF16, sq, k=k, ratio=ratio) // 4 + 1, device=DEV)
+    ops.csa_index_topk_bf16(sq, R["qI"], x["w"], wl.n_I, R["kI"], ratio, k, idx16, ws=ws16)
+    torch.cuda.synchronize()
+    want16 = score.to(torch.bfloat16).view(torch.int16)
+    sb = s16.cpu().numpy().view(np.uint16)
+    gi16 = idx16.cpu().numpy()
+    recall = []
+    for b, L in enumerate(lens):
+        V = visible(L - 1, ratio)
+        assert torch.equal(s16[b, :V], want16[b, :V]), f"c2 seq {b}: bf16 scores are not the rounded float32 ones"
+        vals = (sb[b, :V].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert list(gi16[b]) == list(topk_select(vals, k)), f"c2 seq {b}: bf16 selection"
+        recall.append(len(set(gi16[b]) & set(gidx[b])) / k)
+    log(f"c2: bf16-score selector recall of the float32 selection: mean {np.mean(recall):.4f}, "
+        f"min {np.min(recall):.4f}")
+
 
 # ----------------------------------------------------------------------------- c3
 

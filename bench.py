@@ -12,7 +12,8 @@ overlapped compression, a 64-head x 128-dim indexer, k = 512, window 128, bf16.
 
 The same JSON line carries, under `sweep`, the decode step over the metric's whole context
 range: CSA at 64K / 256K / 1M (batch 32, k = 512) with bf16, MXFP4 and fp8 (1x128)
-indexer keys and queries, CSA with k = 1024 (batch 32, 8K-64K), and HCA at 64K / 256K / 1M (batch 4);
+indexer keys and queries, CSA with k = 1024 (batch 32, 8K-64K), HCA at 64K / 256K / 1M (batch 4),
+and the headline batch and HCA at 1M over paged entry pools with token rings;
 each with tokens/s, median / p10 / p90 step times, the per-operation times and the
 roofline entry of its dominant operation.  Under `prefill` it carries the mixed-precision
 prefill (131072 causal tokens, fp8 1x128 KV rows with bf16 RoPE dims, MXFP4 indexer,
@@ -122,13 +123,36 @@ class DecodeLayer:
     indexer format: "bf16", "mxfp4" or "fp8" (keys, queries and the keys the compress step
     writes)."""
 
-    def __init__(self, wl, lens, seed, dev, kfmt="bf16", scores="f32"):
-        self.wl, self.kfmt, self.scores = wl, kfmt, scores
+    def __init__(self, wl, lens, seed, dev, kfmt="bf16", scores="f32", paged=False):
+        self.wl, self.kfmt, self.scores, self.paged = wl, kfmt, scores, paged
         n, D, ratio = wl.n_seqs, wl.d_c, wl.ratio
         x = synth.decode_inputs(wl, lens, seed, dev)
         self.lens, self.E = x["lens"], x["E"]
         self.entry_off, self.tok_off, self.tok_lo = x["entry_off"], x["tok_off"], x["tok_lo"]
-        self.seqs = ops.Seqs([1] * n, lens, self.entry_off, self.tok_off, self.tok_lo, device=dev)
+        if paged:
+            # paged entry pools (blocks of 128 tokens, placed by a seeded permutation) and a
+            # 512-row token ring per sequence; the pools are redrawn at the paged sizes
+            epb = 128 // ratio
+            nblk = [max(1, -(-e // epb)) for e in self.E]
+            perm = [int(v) for v in synth.rng(seed).permutation(sum(nblk))]
+            table, o = [], 0
+            for nb in nblk:
+                table.append(perm[o:o + nb])
+                o += nb
+            ring = 512
+            self.tok_off = [b * ring for b in range(n)]
+            self.seqs = ops.Seqs([1] * n, lens, [0] * n, self.tok_off, self.tok_lo, device=dev, block_table=table,
+                                 block_entries=epb, tok_ring=ring)
+            rows = sum(nblk) * epb
+            x["kv"] = synth.device_normal((rows, D), synth.sub_seed(seed, 31), dev).to(torch.bfloat16)
+            for key in ("c", "z"):
+                x[key] = synth.device_normal((n * ring, D), synth.sub_seed(seed, 32), dev).to(torch.bfloat16)
+            if "kI" in x:
+                x["kI"] = synth.device_normal((rows, wl.d_I), synth.sub_seed(seed, 33), dev).to(torch.bfloat16)
+                for key in ("cI", "zI"):
+                    x[key] = synth.device_normal((n * ring, wl.d_I), synth.sub_seed(seed, 34), dev).to(torch.bfloat16)
+        else:
+            self.seqs = ops.Seqs([1] * n, lens, self.entry_off, self.tok_off, self.tok_lo, device=dev)
         for key in ("kv", "c", "z", "bias", "q", "sink"):
             setattr(self, key, x[key])
         bf = torch.bfloat16
@@ -259,16 +283,16 @@ def time_fn(fn, layers, reps, stream):
     return e0.elapsed_time(e1) / (n * len(layers))
 
 
-def build_layers(wl, dev, kfmt="bf16", max_sets=MAX_SETS, min_sets=2, scores="f32"):
+def build_layers(wl, dev, kfmt="bf16", max_sets=MAX_SETS, min_sets=2, scores="f32", paged=False):
     """Layer sets for a decode workload: enough independent sets that the bytes their steps
     touch exceed SET_BYTES together (twice the Infinity Cache, so no set's rows stay there
     from one use to the next), between min_sets and max_sets."""
     lens = make_lengths(wl)
-    layers = [DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100), dev, kfmt, scores)]
+    layers = [DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100), dev, kfmt, scores, paged)]
     touched = sum(b for b, _ in layers[0].work().values())
     n_sets = int(min(max_sets, max(min_sets, math.ceil(SET_BYTES / max(touched, 1.0)))))
     for i in range(1, n_sets):
-        layers.append(DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100 + i), dev, kfmt, scores))
+        layers.append(DecodeLayer(wl, lens, synth.sub_seed(wl.seed, 100 + i), dev, kfmt, scores, paged))
     return layers, lens
 
 
@@ -347,18 +371,19 @@ def op_breakdown(layers, reps, stream):
     return kernels, roof, work
 
 
-def run_decode(wl, dev, stream, steps, warmup, kfmt="bf16", graph=True, max_sets=MAX_SETS, scores="f32"):
+def run_decode(wl, dev, stream, steps, warmup, kfmt="bf16", graph=True, max_sets=MAX_SETS, scores="f32",
+               paged=False):
     """One decode workload: tokens/s over exactly `steps` steps, step-time percentiles,
     per-operation times and the dominant operation's roofline entry."""
-    layers, lens = build_layers(wl, dev, kfmt, max_sets=max_sets, scores=scores)
+    layers, lens = build_layers(wl, dev, kfmt, max_sets=max_sets, scores=scores, paged=paged)
     torch.cuda.synchronize()
-    log(f"{wl.name} ({kfmt} indexer, {scores} scores): {wl.n_seqs} seqs, ctx {min(lens)}..{max(lens)}, {len(layers)} layer sets, "
+    log(f"{wl.name} ({kfmt} indexer, {scores} scores{', paged' if paged else ''}): {wl.n_seqs} seqs, ctx {min(lens)}..{max(lens)}, {len(layers)} layer sets, "
         f"{torch.cuda.memory_allocated() / 2**30:.2f} GiB allocated")
     ms, per_step, wall = timed_steps(layers, steps, warmup, stream, graph)
     kernels, roof, work = op_breakdown(layers, max(64, steps // 4), stream)
     step_bytes = sum(b for b, _ in work.values())
     res = {"workload": wl.name, "indexer": kfmt if layers[0].csa else None,
-           "scores": scores if layers[0].csa else None, "tokens_per_s": round(wl.n_seqs / (ms * 1e-3), 1),
+           "scores": scores if layers[0].csa else None, "paged": paged, "tokens_per_s": round(wl.n_seqs / (ms * 1e-3), 1),
            "ms_per_step": round(ms, 5), "step_time": percentiles(per_step), "wall_s": round(wall, 3),
            "batch": wl.n_seqs, "ctx": [min(lens), max(lens)], "k": wl.k if layers[0].csa else None,
            "layer_sets": len(layers),
@@ -768,12 +793,15 @@ def run_prefill(dev, stream, steps=3, warmup=1):
 def run_sweep(dev, stream, steps, warmup):
     """The decode step over the metric's context range (see the module docstring)."""
     out = []
-    points = [(wl, f, "f32") for f in ("bf16", "mxfp4", "fp8") for wl in configs.CSA_DECODE_SWEEP]
+    points = [(wl, f, "f32", False) for f in ("bf16", "mxfp4", "fp8") for wl in configs.CSA_DECODE_SWEEP]
     # the selector on bf16 scores: the headline batch and 1M context
-    points += [(configs.CSA_DECODE_BF16, "bf16", "bf16"), (configs.CSA_DECODE_SWEEP[-1], "bf16", "bf16")]
-    points += [(configs.CSA_DECODE_K1024, "bf16", "f32")] + [(wl, "bf16", "f32") for wl in configs.HCA_DECODE_SWEEP]
-    for wl, kfmt, scores in points:
-        res, layers = run_decode(wl, dev, stream, steps, warmup, kfmt, max_sets=MAX_SETS, scores=scores)
+    points += [(configs.CSA_DECODE_BF16, "bf16", "bf16", False), (configs.CSA_DECODE_SWEEP[-1], "bf16", "bf16", False)]
+    points += [(configs.CSA_DECODE_K1024, "bf16", "f32", False)]
+    points += [(wl, "bf16", "f32", False) for wl in configs.HCA_DECODE_SWEEP]
+    # paged entry pools and token rings: the headline batch and HCA at 1M
+    points += [(configs.CSA_DECODE_BF16, "bf16", "f32", True), (configs.HCA_DECODE_1M_BF16, "bf16", "f32", True)]
+    for wl, kfmt, scores, paged in points:
+        res, layers = run_decode(wl, dev, stream, steps, warmup, kfmt, max_sets=MAX_SETS, scores=scores, paged=paged)
         out.append(res)
         del layers
         torch.cuda.empty_cache()

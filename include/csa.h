@@ -76,21 +76,43 @@ typedef struct {
 /* Ragged batch.  Sequence b has n_b = q_off[b+1] - q_off[b] new (query) tokens, stored as
  * consecutive rows q_off[b] .. q_off[b+1]-1 of every per-token array (q, qI, w, idx, out,
  * lse, score); its context length L_b = ctx_len[b] includes them, so query j of sequence b
- * sits at position p = L_b - n_b + j.  Compressed entry i of sequence b is row
- * entry_off[b] + i of the entry pools; token position t of sequence b is row
- * tok_off[b] + (t - tok_lo[b]) of the token pools (valid for t >= tok_lo[b]).
+ * sits at position p = L_b - n_b + j.
+ *
+ * Entry pools ("DeepSeek-V4 深度分析报告" section 3.5: the Classical KV Cache holds the
+ * compressed entries in blocks of lcm(m, m') tokens):
+ *   contiguous (block_table == NULL)  entry i of sequence b is row entry_off[b] + i;
+ *   paged                             entry i is row block_table[b * bt_stride + i / E] * E
+ *                                     + i % E with E = block_entries, the entries of one
+ *                                     block in the pools this call addresses (a power of two:
+ *                                     for blocks of 128 tokens, 32 for CSA with m = 4 and 1
+ *                                     for HCA with m' = 128; KV rows and indexer keys share
+ *                                     the layout).  entry_off is then unused and may be NULL.
+ * Token pools (section 3.5: the State Cache, of fixed size, holds the window rows and the
+ * uncompressed tail):
+ *   contiguous (tok_ring == 0)        position t of sequence b is row tok_off[b] + (t -
+ *                                     tok_lo[b]) (valid for t >= tok_lo[b]);
+ *   ring (tok_ring = R > 0)           position t is row tok_off[b] + t mod R; the ring must
+ *                                     hold every position a call reads: the window
+ *                                     [p - n_win + 1, p] of each query and the sources of
+ *                                     each new entry, so R >= max_q + n_win (attention) and
+ *                                     R >= max_q + 2 m (compression, overlapped); positions
+ *                                     below tok_lo[b] are still treated as absent.
  * The arrays are device pointers; the host scalars only size launch grids and must be
  * upper bounds of the device data (total_q exact). */
 typedef struct {
   int32_t n_seqs;
-  const int32_t* q_off;      /* [n_seqs + 1], q_off[0] = 0, non-decreasing                 */
-  const int32_t* ctx_len;    /* [n_seqs], L_b >= n_b                                         */
-  const int64_t* entry_off;  /* [n_seqs]                                                     */
-  const int64_t* tok_off;    /* [n_seqs]                                                     */
-  const int32_t* tok_lo;     /* [n_seqs]                                                     */
-  int32_t total_q;           /* q_off[n_seqs]                                                */
-  int32_t max_q;             /* >= every n_b                                                 */
-  int32_t max_ctx;           /* >= every L_b                                                 */
+  const int32_t* q_off;        /* [n_seqs + 1], q_off[0] = 0, non-decreasing               */
+  const int32_t* ctx_len;      /* [n_seqs], L_b >= n_b                                       */
+  const int64_t* entry_off;    /* [n_seqs] (contiguous entry pools)                          */
+  const int64_t* tok_off;      /* [n_seqs]                                                   */
+  const int32_t* tok_lo;       /* [n_seqs]                                                   */
+  int32_t total_q;             /* q_off[n_seqs]                                              */
+  int32_t max_q;               /* >= every n_b                                               */
+  int32_t max_ctx;             /* >= every L_b                                               */
+  const int32_t* block_table;  /* NULL, or [n_seqs, bt_stride] physical block ids (paged)    */
+  int32_t bt_stride;           /* table entries per sequence (paged)                         */
+  int32_t block_entries;       /* entries per block, a power of two (paged)                  */
+  int32_t tok_ring;            /* 0, or the ring size R of the token pools                   */
 } csa_seqs;
 
 /* ---------------------------------------------------------------------------------------

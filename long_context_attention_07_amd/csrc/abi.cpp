@@ -109,8 +109,14 @@ int check_seqs(const csa_seqs* s) {
     if (s->total_q != 0) return fail(CSA_EINVAL, "seqs: total_q %d with no sequences", s->total_q);
     return CSA_OK;
   }
-  if (!s->q_off || !s->ctx_len || !s->entry_off || !s->tok_off || !s->tok_lo)
+  if (!s->q_off || !s->ctx_len || !s->tok_off || !s->tok_lo || (!s->entry_off && !s->block_table))
     return fail(CSA_EINVAL, "seqs: null device array");
+  if (s->block_table) {
+    if (s->bt_stride < 1) return fail(CSA_EINVAL, "seqs: bt_stride %d < 1 with a block table", s->bt_stride);
+    if (s->block_entries < 1 || (s->block_entries & (s->block_entries - 1)) || s->block_entries > (1 << 20))
+      return fail(CSA_EINVAL, "seqs: block_entries %d must be a power of two in [1, 2^20]", s->block_entries);
+  }
+  if (s->tok_ring < 0) return fail(CSA_EINVAL, "seqs: tok_ring %d < 0", s->tok_ring);
   if (s->max_q > s->max_ctx) return fail(CSA_EINVAL, "seqs: max_q %d > max_ctx %d", s->max_q, s->max_ctx);
   if ((int64_t)s->total_q > (int64_t)s->n_seqs * s->max_q)
     return fail(CSA_EINVAL, "seqs: total_q %d exceeds n_seqs*max_q", s->total_q);
@@ -126,6 +132,12 @@ csa::SeqsDev dev_seqs(const csa_seqs* s) {
   d.tok_lo = s->tok_lo;
   d.n_seqs = s->n_seqs;
   d.total_q = s->total_q;
+  d.block_table = s->block_table;
+  d.bt_stride = s->block_table ? s->bt_stride : 0;
+  d.be_shift = 0;
+  if (s->block_table)
+    while ((1 << d.be_shift) < s->block_entries) ++d.be_shift;
+  d.tok_ring = s->tok_ring;
   return d;
 }
 

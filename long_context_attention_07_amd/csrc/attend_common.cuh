@@ -69,13 +69,13 @@ __device__ __forceinline__ SlotRef resolve_slot(const AttendArgs& a, int t, cons
     int64_t e = a.csa ? (int64_t)a.idx[(int64_t)t * a.k + s] : s;
     if (e >= 0) {
       r.kind = 1;
-      r.row = ctx.entry0 + e;
+      r.row = entry_row(a.S, ctx.b, ctx.entry0, e);
     }
   } else if (s < n_ent + a.n_win) {
     int64_t pos = ctx.p - a.n_win + 1 + (s - n_ent);
     if (pos >= 0 && pos >= ctx.tok_lo) {
       r.kind = 2;
-      r.row = ctx.tok0 + (pos - ctx.tok_lo);
+      r.row = tok_row(a.S, ctx.tok0, ctx.tok_lo, pos);
       r.pos = pos;
     }
   }

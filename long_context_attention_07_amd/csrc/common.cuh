@@ -40,7 +40,10 @@ struct RowsOut {
   int64_t stride;
 };
 
-// Ragged batch descriptor (device arrays).
+// Ragged batch descriptor (device arrays).  Entry pools are contiguous per sequence
+// (entry_off) or paged: entry e of sequence b at row block_table[b, e >> be_shift] <<
+// be_shift | (e & (2^be_shift - 1)).  Token pools are contiguous from tok_lo (tok_off) or a
+// ring of tok_ring rows: position t at row tok_off[b] + t mod tok_ring.
 struct SeqsDev {
   const int32_t* q_off;
   const int32_t* ctx_len;
@@ -49,6 +52,10 @@ struct SeqsDev {
   const int32_t* tok_lo;
   int n_seqs;
   int total_q;
+  const int32_t* block_table;  // nullptr: contiguous entry pools
+  int64_t bt_stride;           // table entries per sequence
+  int be_shift;                // log2 of the entries per block
+  int tok_ring;                // 0: contiguous token pools
 };
 
 // Inverse frequencies of the rotated pairs, computed once on the host in float64.
@@ -274,7 +281,7 @@ __device__ __forceinline__ TokenCtx token_ctx(const SeqsDev& S, int t) {
   const int q0 = S.q_off[bc];
   const int q1 = S.q_off[bc + 1];
   const int cl = S.ctx_len[bc];
-  const int64_t e0 = S.entry_off[bc];
+  const int64_t e0 = S.entry_off ? S.entry_off[bc] : 0;
   const int64_t t0 = S.tok_off[bc];
   const int tl = S.tok_lo[bc];
   const int win = __popcll(__ballot(in && q0 <= t)) - 1;  // >= 0: q_off[lo] <= t
@@ -287,6 +294,65 @@ __device__ __forceinline__ TokenCtx token_ctx(const SeqsDev& S, int t) {
   c.tok0 = readlane64(t0, win);
   c.tok_lo = __builtin_amdgcn_readlane(tl, win);
   return c;
+}
+
+// ------------------------------------------------------------------------- pool rows
+
+// Pool row of entry e of sequence b (entry0 = entry_off[b]; unused for paged pools).
+__device__ __forceinline__ int64_t entry_row(const SeqsDev& S, int b, int64_t entry0, int64_t e) {
+  if (!S.block_table) return entry0 + e;
+  const int64_t blk = S.block_table[(int64_t)b * S.bt_stride + (e >> S.be_shift)];
+  return (blk << S.be_shift) | (e & ((int64_t(1) << S.be_shift) - 1));
+}
+
+// Token-pool row of position pos of a sequence (tok0 = tok_off[b], tok_lo = tok_lo[b]).
+__device__ __forceinline__ int64_t tok_row(const SeqsDev& S, int64_t tok0, int64_t tok_lo, int64_t pos) {
+  return S.tok_ring ? tok0 + pos % S.tok_ring : tok0 + (pos - tok_lo);
+}
+
+// Kernels that stream consecutive entries of one sequence from a paged pool preload the
+// ids of the run's first 64 blocks, block first + l in lane l; rows of later blocks are
+// looked up in the table.  Every lane must call pool_row (it exchanges across lanes).
+struct BlockIds {
+  int32_t id;
+  int64_t first;
+};
+
+__device__ __forceinline__ BlockIds load_block_ids(const SeqsDev& S, int b, int64_t e_first) {
+  BlockIds B;
+  B.id = 0;
+  B.first = 0;
+  if (S.block_table) {
+    const int lane = threadIdx.x & 63;
+    B.first = e_first >> S.be_shift;
+    if (B.first + lane < S.bt_stride) B.id = S.block_table[(int64_t)b * S.bt_stride + B.first + lane];
+  }
+  return B;
+}
+
+__device__ __forceinline__ int64_t pool_row(const SeqsDev& S, const BlockIds& B, int b, int64_t entry0, int64_t e) {
+  if (!S.block_table) return entry0 + e;
+  const int64_t rel = (e >> S.be_shift) - B.first;
+  const int32_t near = __shfl(B.id, (int)(rel < 63 ? (rel < 0 ? 0 : rel) : 63), 64);
+  const int64_t blk = (rel >= 0 && rel < 64) ? near : S.block_table[(int64_t)b * S.bt_stride + (e >> S.be_shift)];
+  return (blk << S.be_shift) | (e & ((int64_t(1) << S.be_shift) - 1));
+}
+
+// pool_row for a wave whose lanes usually read rows of one block (consecutive entries of a
+// 16-entry group): then the block id is taken with one scalar read of its lane; otherwise
+// pool_row.  Every lane must call it.
+__device__ __forceinline__ int64_t pool_row_wave(const SeqsDev& S, const BlockIds& B, int b, int64_t entry0,
+                                                 int64_t e) {
+  if (!S.block_table) return entry0 + e;
+  const int64_t blk_l = e >> S.be_shift;
+  const int64_t blk0 = (int64_t)__builtin_amdgcn_readfirstlane((int)blk_l) |
+                       ((int64_t)__builtin_amdgcn_readfirstlane((int)(blk_l >> 32)) << 32);
+  const int64_t rel0 = blk0 - B.first;
+  if (__all(blk_l == blk0) && rel0 >= 0 && rel0 < 64) {
+    const int64_t blk = __builtin_amdgcn_readlane(B.id, (int)rel0);
+    return (blk << S.be_shift) | (e & ((int64_t(1) << S.be_shift) - 1));
+  }
+  return pool_row(S, B, b, entry0, e);
 }
 
 // ------------------------------------------------------------------------- softmax fold

@@ -49,15 +49,17 @@ __device__ __forceinline__ float2 load_pair_as(const RowsDev& R, int64_t r, int 
 // repeat the last row and are skipped), with the row format fixed at compile time.
 template <int CD, int ZD, int NB>
 __device__ __forceinline__ PoolState pool_rows(const RowsDev& c, const RowsDev& z, const float* __restrict__ bsrc,
-                                               int D, int64_t tok_shift, int64_t j0, int64_t j1, int pair) {
+                                               int D, const SeqsDev& S, int64_t tok0, int64_t tok_lo, int64_t j0,
+                                               int64_t j1, int pair) {
   float m0 = -INFINITY, m1 = -INFINITY, s0 = 0.f, s1 = 0.f, a0 = 0.f, a1 = 0.f;
   for (int64_t jb = j0; jb < j1; jb += NB) {
     float2 cv[NB], zv[NB], bv[NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int64_t j = min(jb + u, j1 - 1);
-      cv[u] = load_pair_as<CD>(c, tok_shift + j, pair);
-      zv[u] = load_pair_as<ZD>(z, tok_shift + j, pair);
+      const int64_t row = tok_row(S, tok0, tok_lo, j);
+      cv[u] = load_pair_as<CD>(c, row, pair);
+      zv[u] = load_pair_as<ZD>(z, row, pair);
       bv[u] = reinterpret_cast<const float2*>(bsrc + j * D)[pair];
     }
     __builtin_amdgcn_sched_barrier(0);  // the batch's loads all go out before its updates
@@ -127,11 +129,11 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
     const int64_t j1 = min(hi, j0 + share);
     const float* bsrc = bias - lo * D;  // row j of the slot bias is bsrc + j * D
     if (c.dtype == DT_BF16 && z.dtype == DT_BF16)
-      st = pool_rows<DT_BF16, DT_BF16, 8>(c, z, bsrc, D, tok0 - tok_lo, j0, j1, pair);
+      st = pool_rows<DT_BF16, DT_BF16, 8>(c, z, bsrc, D, S, tok0, tok_lo, j0, j1, pair);
     else if (c.dtype == DT_F32 && z.dtype == DT_F32)
-      st = pool_rows<DT_F32, DT_F32, 8>(c, z, bsrc, D, tok0 - tok_lo, j0, j1, pair);
+      st = pool_rows<DT_F32, DT_F32, 8>(c, z, bsrc, D, S, tok0, tok_lo, j0, j1, pair);
     else
-      st = pool_rows<-1, -1, 8>(c, z, bsrc, D, tok0 - tok_lo, j0, j1, pair);
+      st = pool_rows<-1, -1, 8>(c, z, bsrc, D, S, tok0, tok_lo, j0, j1, pair);
   }
   if (RG > 1) {
     if (grp > 0) s_part[grp - 1][tp] = st;
@@ -165,7 +167,7 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
   }
 
   // ---- store
-  const int64_t orow = S.entry_off[b] + i;
+  const int64_t orow = entry_row(S, b, S.entry_off ? S.entry_off[b] : 0, i);
   uint8_t* dst = out.data + orow * out.stride;
   const int lane = threadIdx.x & 63;
   switch (out.dtype) {

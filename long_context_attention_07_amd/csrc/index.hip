@@ -40,7 +40,7 @@ __global__ void __launch_bounds__(256) index_score_valu_kernel(SeqsDev S, RowsDe
   const int64_t e = e0 + threadIdx.x;
   if (e >= V) return;
   float kr[DI];
-  const int64_t row = ctx.entry0 + e;
+  const int64_t row = entry_row(S, ctx.b, ctx.entry0, e);
 #pragma unroll
   for (int d = 0; d < DI; ++d) kr[d] = load_elem(kI, row, d);
   float s = 0.f;

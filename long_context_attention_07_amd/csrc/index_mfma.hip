@@ -46,7 +46,8 @@ __device__ __forceinline__ void wait_tiles_in_flight(int n) {
 // Entries [part * 64 TILES, (part + 1) * 64 TILES) of token t (position ctx.p, pool row of
 // entry 0 ctx.entry0), by the whole workgroup.
 template <int RING, int TILES>
-__device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], int t, const TokenCtx& ctx, int part,
+__device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], const SeqsDev& S, int t,
+                                            const TokenCtx& ctx, int part,
                                             const RowsDev& qI, const float* __restrict__ w, int n_I,
                                             const RowsDev& kI, int ratio, ScoreOut score) {
   static_assert(RING >= 2 && RING <= 4, "ring depth");
@@ -58,7 +59,7 @@ __device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], 
 
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
-  const uint8_t* kbase = kI.data + ctx.entry0 * kI.stride;
+  const BlockIds bids = load_block_ids(S, ctx.b, e_begin);
 
   // tile i -> ring slot i % RING; wave wv moves rows 16wv .. 16wv+15 (4 rows per instruction)
   auto issue = [&](int i) {
@@ -70,7 +71,7 @@ __device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], 
       int64_t e = e_tile + r;
       if (e >= V) e = V - 1;  // rows past the end re-read a valid row; their scores are not written
       const int chunk = (lane & 15) ^ (r & 15);
-      const uint8_t* src = kbase + e * kI.stride + chunk * 16;
+      const uint8_t* src = kI.data + pool_row_wave(S, bids, ctx.b, ctx.entry0, e) * kI.stride + chunk * 16;
       __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)(slot + (16 * wv + 4 * q) * kIRow), 16, 0, 0);
     }
   };
@@ -170,7 +171,7 @@ __global__ void __launch_bounds__(256) index_score_mfma_kernel(SeqsDev S, RowsDe
   const int t = lid / n_parts;
   const int part = lid % n_parts;
   const TokenCtx ctx = token_ctx(S, t);
-  score_range<RING, TILES>(ring, t, ctx, lid % n_parts, qI, w, n_I, kI, ratio, score);
+  score_range<RING, TILES>(ring, S, t, ctx, lid % n_parts, qI, w, n_I, kI, ratio, score);
 }
 
 // Few sequences and query rows (decode): the (token, range) units with entries to score
@@ -201,7 +202,7 @@ __global__ void __launch_bounds__(256) index_score_mfma_units_kernel(SeqsDev S, 
   const int q0 = in ? S.q_off[lane] : 0;
   const int q1 = in ? S.q_off[lane + 1] : 0;
   const int len = in ? S.ctx_len[lane] : 0;
-  const int64_t e0 = in ? S.entry_off[lane] : 0;
+  const int64_t e0 = (in && S.entry_off) ? S.entry_off[lane] : 0;
   int units = 0;
   for (int j = 0; j < q1 - q0; ++j) {
     const int64_t V = ((int64_t)len - (q1 - q0) + j + 1) / ratio;
@@ -232,7 +233,7 @@ __global__ void __launch_bounds__(256) index_score_mfma_units_kernel(SeqsDev S, 
     ctx.entry0 = readlane64(e0, b);
     ctx.tok0 = 0;
     ctx.tok_lo = 0;
-    score_range<RING, TILES>(ring, bq0 + j, ctx, rem, qI, w, n_I, kI, ratio, score);
+    score_range<RING, TILES>(ring, S, bq0 + j, ctx, rem, qI, w, n_I, kI, ratio, score);
   }
 }
 

@@ -149,6 +149,7 @@ __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev 
             wr[i][hb][j] = wv_;
           }
       const int64_t e_stop = min(e_begin + (int64_t)kMxRange, v_max);
+      const BlockIds bids = load_block_ids(S, ctx.b, e_begin);
       // wave wv takes the 16-entry blocks e_begin + 16 (wv + 4 it); 4 blocks in flight
       for (int64_t e0 = e_begin + 16 * wv; e0 < e_stop; e0 += 4 * 64) {
         MxOperand<F8> kb[4];
@@ -156,7 +157,7 @@ __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev 
         for (int u = 0; u < 4; ++u) {
           int64_t e = e0 + 64 * u + c16;
           if (e >= v_max) e = v_max - 1;  // past the run's last visible entry: a valid row, not written
-          kb[u] = load_operand<F8>(kI, ctx.entry0 + e, g);
+          kb[u] = load_operand<F8>(kI, pool_row_wave(S, bids, ctx.b, ctx.entry0, e), g);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -243,6 +244,7 @@ index_score_mx_block_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w, 
           }
         }
       const int e_stop = min(e_begin + kMxPart, v_max);
+      const BlockIds bids = load_block_ids(S, ctx.b, e_begin);
       // entries this lane stores: below both the stored row's visible count and the part's end
       const bool row_on = g < 2 && my_row < nq;
       const int e_lim = row_on ? min((int)((ctx.p + my_row + 1) / ratio), e_stop) : 0;
@@ -253,7 +255,7 @@ index_score_mx_block_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w, 
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int e = min(e0 + 16 * u + c16, v_max - 1);
-          kb[u] = load_operand<F8>(kI, ctx.entry0 + e, g);
+          kb[u] = load_operand<F8>(kI, pool_row_wave(S, bids, ctx.b, ctx.entry0, e), g);
         }
       };
       // the 64 entries e0 .. e0+63: 8 MFMAs per 16-entry block, then the head sums

@@ -36,7 +36,9 @@ class csa_rows(ctypes.Structure):
 class csa_seqs(ctypes.Structure):
     _fields_ = [("n_seqs", ctypes.c_int32), ("q_off", ctypes.c_void_p), ("ctx_len", ctypes.c_void_p),
                 ("entry_off", ctypes.c_void_p), ("tok_off", ctypes.c_void_p), ("tok_lo", ctypes.c_void_p),
-                ("total_q", ctypes.c_int32), ("max_q", ctypes.c_int32), ("max_ctx", ctypes.c_int32)]
+                ("total_q", ctypes.c_int32), ("max_q", ctypes.c_int32), ("max_ctx", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("bt_stride", ctypes.c_int32), ("block_entries", ctypes.c_int32),
+                ("tok_ring", ctypes.c_int32)]
 
 
 _lib = None
@@ -115,9 +117,12 @@ class Rows:
 
 
 class Seqs:
-    """Ragged batch descriptor; host lists are copied to int tensors on `device`."""
+    """Ragged batch descriptor; host lists are copied to int tensors on `device`.  Paged entry
+    pools: `block_table` (one list of physical block ids per sequence) with `block_entries`
+    entries per block; a ring of token rows: `tok_ring` (see include/csa.h)."""
 
-    def __init__(self, n_q, ctx_len, entry_off, tok_off=None, tok_lo=None, device="cuda"):
+    def __init__(self, n_q, ctx_len, entry_off, tok_off=None, tok_lo=None, device="cuda", block_table=None,
+                 block_entries=0, tok_ring=0):
         n = len(n_q)
         tok_off = list(tok_off) if tok_off is not None else [0] * n
         tok_lo = list(tok_lo) if tok_lo is not None else [0] * n
@@ -134,9 +139,15 @@ class Seqs:
         self.total_q = q_off[-1]
         self.max_q = max(self.n_q) if n else 0
         self.max_ctx = max(self.ctx_len) if n else 0
+        self.bt_t, bt_stride = None, 0
+        if block_table is not None:
+            bt_stride = max(1, max(len(r) for r in block_table))
+            rows = [list(r) + [0] * (bt_stride - len(r)) for r in block_table]
+            self.bt_t = torch.tensor(rows, dtype=torch.int32, device=device)
         self.c = csa_seqs(n, self.q_off_t.data_ptr(), self.ctx_t.data_ptr(), self.entry_t.data_ptr(),
                           self.tok_off_t.data_ptr(), self.tok_lo_t.data_ptr(), self.total_q, self.max_q,
-                          self.max_ctx)
+                          self.max_ctx, self.bt_t.data_ptr() if self.bt_t is not None else None, bt_stride,
+                          int(block_entries), int(tok_ring))
 
 
 def csa_version():

@@ -41,9 +41,10 @@ def test_strings_and_version(lib):
     assert ops.csa_version() >= 100
 
 
-def _seqs(n_seqs=1, total_q=1, max_q=1, max_ctx=100):
+def _seqs(n_seqs=1, total_q=1, max_q=1, max_ctx=100, block_table=None, bt_stride=0, block_entries=0, tok_ring=0):
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
-    return ops.csa_seqs(n_seqs, fake, fake, fake, fake, fake, total_q, max_q, max_ctx)
+    return ops.csa_seqs(n_seqs, fake, fake, fake, fake, fake, total_q, max_q, max_ctx, block_table, bt_stride,
+                        block_entries, tok_ring)
 
 
 def _rows(dtype=ops.BF16, dim=512, data=0x2000, scales=None, stride=0):
@@ -188,3 +189,21 @@ def test_topk_workspace_sizes(lib):
     # 1M candidates per row with k = 4096 would need 32 slices of 32768: one workgroup instead
     big = _seqs(n_seqs=1, total_q=1, max_q=1, max_ctx=1 << 20)
     assert lib.csa_workspace_bytes(ops.OP_TOPK, P(big), 0, 0, 4096, 1, 0) == 0
+
+
+def test_paged_and_ring_descriptor_validation(lib):
+    """Paged entry pools need a table stride >= 1 and a power-of-two block size; the token
+    ring size cannot be negative (refused before any launch)."""
+    P = ctypes.byref
+    q, kv = _rows(), _rows()
+    sink, idx = ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000)
+
+    def attend(s):
+        return lib.csa_attend(P(s), P(q), 8, P(kv), idx, 16, P(kv), 128, sink, 0.1, 64, 10000.0, P(q), None, None, 0,
+                              None)
+
+    bt = ctypes.c_void_p(0x5000)
+    assert attend(_seqs(block_table=bt, bt_stride=0, block_entries=32)) == -1 and "bt_stride" in ops.csa_last_error()
+    assert attend(_seqs(block_table=bt, bt_stride=4, block_entries=24)) == -1
+    assert "power of two" in ops.csa_last_error()
+    assert attend(_seqs(tok_ring=-1)) == -1 and "tok_ring" in ops.csa_last_error()

@@ -18,10 +18,11 @@ Modules
   indexer    Lightning-Indexer scores and exact top-k selection
   attention  shared-KV MQA over (selected or all) entries plus the sliding window, with sink
   pipeline   per-token composition of the steps over a ragged batch
+  outproj    the grouped output projection of the attention output (two stages)
 
 Parity status: every function here is pinned by tests in tests/test_oracle_*.py
 (closed forms, special cases reducing to textbook routines, brute force, invariants),
 except the compressor's exact form, which the pages leave open; see compress.py.
 """
 
-from . import formats, rope, compress, indexer, attention, pipeline  # noqa: F401
+from . import formats, rope, compress, indexer, attention, pipeline, outproj  # noqa: F401

@@ -18,7 +18,7 @@ each with tokens/s, median / p10 / p90 step times, the per-operation times and t
 roofline entry of its dominant operation.  Under `prefill` it carries the mixed-precision
 prefill (131072 causal tokens, fp8 1x128 KV rows with bf16 RoPE dims, MXFP4 indexer,
 k = 1024), priced against the fp8 matrix-core peak with the peak of the instruction used
-beside it.
+beside it; under `out_proj` the grouped output projection that follows the attention.
 
 Inputs are synthetic, seeded and resident in HBM before timing.  Several independent layer
 sets (more than 512 MB in all) are rotated step by step so that no set stays in the 256 MB
@@ -788,7 +788,54 @@ def run_prefill(dev, stream, steps=3, warmup=1):
     return res
 
 
-# ----------------------------------------------------------------------------- main
+# ----------------------------------------------------------------------------- output projection
+
+OUT_PROJ = {"n_h": 64, "dim": 512, "groups": 8, "d_g": 1024, "d_out": 4096}
+
+
+def run_out_proj(dev, stream, reps=20):
+    """The grouped output projection after attention (64 heads x 512 dims in 8 groups ->
+    1024 dims each -> 4096): a decode batch of 32 tokens (bound by the 128 MB weight read;
+    four weight sets rotated so none stays in the Infinity Cache) and a 16384-token prefill
+    chunk (bound by the matrix cores)."""
+    c = OUT_PROJ
+    n_h, dim, G, d_g, d_out = c["n_h"], c["dim"], c["groups"], c["d_g"], c["d_out"]
+    hpg = n_h // G
+    sets = []
+    for i in range(4):
+        w1 = synth.device_normal((G, d_g, hpg * dim), synth.sub_seed(40, i), dev, 1 / math.sqrt(hpg * dim))
+        w2 = synth.device_normal((d_out, G * d_g), synth.sub_seed(41, i), dev, 1 / math.sqrt(G * d_g))
+        sets.append((w1.to(torch.bfloat16), w2.to(torch.bfloat16)))
+    res = {"config": dict(c)}
+    for name, M in (("decode_32", 32), ("prefill_16384", 16384)):
+        o = synth.device_normal((M, n_h * dim), synth.sub_seed(42, M), dev).to(torch.bfloat16)
+        y = torch.empty((M, G * d_g), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((M, d_out), dtype=torch.bfloat16, device=dev)
+        fn = lambda w: ops.csa_grouped_out_proj(o, n_h, dim, G, d_g, w[0], w[1], d_out, y, out)  # noqa: E731
+        ms = time_fn(fn, sets, reps * len(sets), stream)
+        flops = 2.0 * M * (d_g * n_h * dim + d_out * G * d_g)
+        wbytes = 2.0 * (G * d_g * hpg * dim + d_out * G * d_g)
+        abytes = 2.0 * M * (n_h * dim + 2 * G * d_g + d_out)
+        t = ms * 1e-3
+        entry = {"tokens": M, "us": round(ms * 1e3, 2), "tokens_per_s": round(M / t, 1),
+                 "TFLOP/s": round(flops / t / 1e12, 1), "GB/s": round((wbytes + abytes) / t / 1e9, 1),
+                 "flops": int(flops), "bytes": int(wbytes + abytes)}
+        if M <= 64:
+            entry["roofline"] = {"bound": "hbm", "achieved": entry["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round((wbytes + abytes) / t / 1e9 / HBM_PEAK_GBS, 4)}
+        else:
+            entry["roofline"] = {"bound": "mfma", "achieved": entry["TFLOP/s"], "peak": BF16_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        res[name] = entry
+        log(f"out proj {name}: {entry['us']} us, {entry['roofline']['frac']:.3f} of the {entry['roofline']['bound']} "
+            f"peak")
+        del o, y, out
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- main# ----------------------------------------------------------------------------- main
 
 def run_sweep(dev, stream, steps, warmup):
     """The decode step over the metric's context range (see the module docstring)."""
@@ -865,10 +912,11 @@ def main():
             log(f"oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} cores")
         del layers
         torch.cuda.empty_cache()
-        sweep = prefill = None
+        sweep = prefill = out_proj = None
         if not args.no_sweep:
             sweep = run_sweep(dev, stream, args.sweep_steps, max(8, args.warmup // 4))
             prefill = run_prefill(dev, stream)
+            out_proj = run_out_proj(dev, stream)
         achievable = None
         if not args.no_probe:
             achievable = achievable_peaks(stream)
@@ -890,6 +938,7 @@ def main():
         "kernels": main_res["kernels"],
         "sweep": sweep,
         "prefill": prefill,
+        "out_proj": out_proj,
         "achievable": achievable,
         "cpu_baseline": cpu,
     }

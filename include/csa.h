@@ -235,6 +235,11 @@ int csa_index_topk_noalloc(const csa_seqs* seqs, const csa_rows* qI, const float
  *   idx   device int32 [total_q, k];  sink device float32 [n_h] (may be -inf)
  *   out   rows [total_q * n_h, D] (F32 or BF16);  lse device float32 [total_q, n_h] or NULL
  *   n_h 1..128;  n_win 0..1024;  k 1..4096
+ *   KV_SPLIT rows: the logits are formed on the matrix cores in fp16 from the fp8 codes
+ *         (exact) and from q and the rows' bf16 dims converted to fp16, so |q| and the bf16
+ *         dims must stay below 65504 (larger values become infinite); the fp8 dims and
+ *         their block scales have no such limit (the value side works in a power-of-two
+ *         frame per tile).
  *   ws/ws_bytes  optional scratch.  csa_workspace_bytes(CSA_OP_CSA_ATTEND, ...) is what the
  *         call can use: nonzero only when a token's key list has more than one chunk and
  *         the batch is small (fewer than 512 workgroups of one token and 16 heads for
@@ -258,7 +263,27 @@ int hca_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows*
                int n_win, const float* sink, float scale, int rope_dims, double rope_theta, const csa_rows* out,
                float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace sizing (host only; reads only the host scalars of `seqs`). */
+/* ---------------------------------------------------------------------------------------
+ * csa_grouped_out_proj -- the grouped output projection of the attention output
+ * ("DeepSeek-V4 深度分析报告", list "其他注意力技术细节": the heads are split into groups and
+ * projected in two stages, lowering the output projection's cost; Figure 2 "Shared KV MQA
+ * + Grouped Output Projection").  For each of the n_tok tokens, with hpg = n_h / groups:
+ *     y[t, j*d_g + e] = bf16( sum_{i < hpg*dim} o[t, j*hpg*dim + i] * w1[j][e][i] )
+ *     out[t, n]       = bf16( sum_{c < groups*d_g} y[t, c] * w2[n][c] )
+ * accumulated in float32 over the inputs in a fixed order (steps of 32, ascending; no split),
+ * so every token's rows are independent of the batch.
+ *   o    bf16 [n_tok, n_h * dim]: the attention output (csa_attend / hca_attend rows of one
+ *        token, heads contiguous)
+ *   w1   bf16 [groups][d_g][hpg * dim]   (each group's weight, [output, input])
+ *   w2   bf16 [d_out][groups * d_g]
+ *   y    bf16 [n_tok, groups * d_g]: the stage-one output (written)
+ *   out  bf16 [n_tok, d_out] (written)
+ *   groups divides n_h; dim, d_g multiples of 8, d_out of 4; hpg*dim and groups*d_g
+ *   multiples of 32; every pointer a 16-byte aligned device pointer. */
+int csa_grouped_out_proj(int n_tok, const void* o, int n_h, int dim, int groups, int d_g, const void* w1,
+                         const void* w2, int d_out, void* y, void* out, void* stream);
+
+/* Workspace sizing (host only; reads only the host scalars of `seqs`). *//* Workspace sizing (host only; reads only the host scalars of `seqs`). */
 enum { CSA_OP_INDEX_TOPK = 1, CSA_OP_CSA_ATTEND = 2, CSA_OP_HCA_ATTEND = 3, CSA_OP_TOPK = 4, CSA_OP_INDEX_TOPK_BF16 = 5 };
 /* op CSA_OP_INDEX_TOPK(_BF16): ratio, k used; CSA_OP_CSA_ATTEND: n_h, dim, k, n_win used;
  * CSA_OP_HCA_ATTEND: n_h, dim, ratio, n_win used; CSA_OP_TOPK: ratio, k used.  Returns

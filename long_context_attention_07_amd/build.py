@@ -23,7 +23,7 @@ PROBE_LIB = os.path.join(PKG, "libcsa_probe.so")
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["abi.cpp", "compress.hip", "index.hip", "index_mfma.hip", "index_mx.hip", "topk.hip", "attend.hip",
-           "attend_mfma.hip"]
+           "attend_mfma.hip", "outproj.hip"]
 PROBE_SOURCES = ["probe.hip"]
 
 COMMON_FLAGS = [

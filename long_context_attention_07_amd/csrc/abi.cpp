@@ -458,6 +458,26 @@ int hca_attend(const csa_seqs* seqs, const csa_rows* q, int n_h, const csa_rows*
   return hip_status(csa::launch_attend(a, ws, ws_bytes, static_cast<hipStream_t>(stream)), "hca_attend launch");
 }
 
+int csa_grouped_out_proj(int n_tok, const void* o, int n_h, int dim, int groups, int d_g, const void* w1,
+                         const void* w2, int d_out, void* y, void* out, void* stream) {
+  if (n_tok < 0) return fail(CSA_EINVAL, "n_tok %d < 0", n_tok);
+  if (!o || !w1 || !w2 || !y || !out) return fail(CSA_EINVAL, "o/w1/w2/y/out: null pointer");
+  if (n_h < 1 || groups < 1 || n_h % groups) return fail(CSA_EINVAL, "groups %d must divide n_h %d", groups, n_h);
+  if (dim < 8 || dim % 8 || d_g < 8 || d_g % 8 || d_out < 4 || d_out % 4)
+    return fail(CSA_EINVAL, "dim %d and d_g %d must be multiples of 8 and d_out %d of 4", dim, d_g, d_out);
+  if (((int64_t)(n_h / groups) * dim) % 32 || ((int64_t)groups * d_g) % 32)
+    return fail(CSA_EUNSUPPORTED, "stage inputs (n_h/groups * dim = %d, groups * d_g = %d) must be multiples of 32",
+                (n_h / groups) * dim, groups * d_g);
+  for (const void* p : {o, w1, w2, static_cast<const void*>(y), static_cast<const void*>(out)})
+    if (reinterpret_cast<uintptr_t>(p) % 16) return fail(CSA_EINVAL, "o/w1/w2/y/out must be 16-byte aligned");
+  if (n_tok == 0) return ok();
+  hipError_t e = csa::launch_grouped_out_proj(n_tok, static_cast<const uint8_t*>(o), n_h, dim, groups, d_g,
+                                              static_cast<const uint8_t*>(w1), static_cast<const uint8_t*>(w2), d_out,
+                                              static_cast<uint8_t*>(y), static_cast<uint8_t*>(out),
+                                              static_cast<hipStream_t>(stream));
+  return hip_status(e, "csa_grouped_out_proj launch");
+}
+
 size_t csa_workspace_bytes(int op, const csa_seqs* seqs, int n_h, int dim, int k, int ratio, int n_win) {
   if (!seqs || seqs->total_q <= 0) return 0;
   switch (op) {

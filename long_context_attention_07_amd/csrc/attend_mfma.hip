@@ -272,6 +272,19 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// fp8 rows, value side: P times a key's block scale is rounded to fp16 for the product,
+// whose normal range (6.1e-5 .. 65504) would cut rows of very small or very large scale.
+// Each set of value blocks therefore works in a frame 2^-E, E = floor(log2) of the largest
+// block scale among the tile's keys (m >= 0; 1 for a zero, subnormal or non-finite m): the
+// operands become P * scale * 2^-E < 2^9, and the set's O accumulators hold O * 2^-E,
+// rescaled exactly (a power of two) when E changes and converted back at the chunk end.
+// For values already in fp16's normal range the bits are the same as without the frame.
+__device__ __forceinline__ float scale_frame(float m) {
+  const uint32_t e = (__float_as_uint(m) >> 23) & 0xffu;
+  if (e == 0u || e >= 254u) return 1.0f;
+  return __uint_as_float((254u - e) << 23);  // 2^(127 - e)
+}
+
 // Window rows among rows row0 .. row0+NR-1 of the tile (already staged; window bits and
 // positions are bit and offset it0 + i of st): when `winmask` (the rows whose logits read the
 // residual tile together with these) holds a window row, rotate the window rows among them
@@ -481,6 +494,7 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
 #pragma unroll
   for (int nb = 0; nb < 16; ++nb) OT[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  float fr_run[3] = {1.0f, 1.0f, 1.0f};  // fp8 rows: the value-set frames OT is held in
 
   auto tiles_in = [&](int c) -> int {
     const int64_t rem = n_slots - (int64_t)c * chunk_slots;
@@ -600,13 +614,29 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
         // set A for dims 256 h2 .. +127, set B for the next 64 (h2 = 1) or 128 (h2 = 0)
         // dims, and for half 1's last 64 dims (the bf16 tail) P itself
         const float a0[4] = {sA.x, sA.y, sA.z, sA.w}, b0[4] = {sB.x, sB.y, sB.z, sB.w};
+        // frames of the pair's 16 keys (keys 16p + 4g + j: the max over j, then the groups)
+        float fr[3];
+        fr[0] = scale_frame(rows_max(fmaxf(fmaxf(a0[0], a0[1]), fmaxf(a0[2], a0[3]))));
+        fr[1] = scale_frame(rows_max(fmaxf(fmaxf(b0[0], b0[1]), fmaxf(b0[2], b0[3]))));
+        fr[2] = h2 == 0 ? fr[1] : 1.0f;
+#pragma unroll
+        for (int set = 0; set < 3; ++set) {
+          const float f = fr[set] / fr_run[set];  // a power of two: exact
+          if (f != 1.0f) {
+            const int lo = set == 0 ? 0 : (set == 1 ? 8 : 12), hi = set == 0 ? 8 : (set == 1 ? 12 : 16);
+#pragma unroll
+            for (int nb = 0; nb < 16; ++nb)
+              if (nb >= lo && nb < hi) OT[nb] *= f;
+            fr_run[set] = fr[set];
+          }
+        }
         f16x4_t ph[3];
 #pragma unroll
         for (int set = 0; set < 3; ++set)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float sc = set == 0 ? a0[j] : (set == 1 ? b0[j] : (h2 == 0 ? b0[j] : 1.0f));
-            ph[set][j] = (_Float16)(pr[j] * sc);
+            ph[set][j] = (_Float16)((pr[j] * sc) * fr[set]);
           }
 #pragma unroll
         for (int nb = 0; nb < 16; ++nb) {
@@ -643,6 +673,15 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(AttendArgs a, float* _
         ws_ml[2 * base + 1] = lh;
       }
       float* scratch = reinterpret_cast<float*>(L.k);
+      if (KVF) {  // back from the value-set frames (exact)
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) {
+          const int set = nb < 8 ? 0 : (nb < 12 ? 1 : 2);
+          OT[nb] *= 1.0f / fr_run[set];
+        }
+#pragma unroll
+        for (int set = 0; set < 3; ++set) fr_run[set] = 1.0f;
+      }
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         if (h2 == r) {
@@ -856,6 +895,7 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
 #pragma unroll
   for (int nb = 0; nb < 16; ++nb) OT[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  float fr_run[3] = {1.0f, 1.0f, 1.0f};  // fp8 rows: the value-set frames OT is held in
   const int ntile = (int)((n_slots + kT - 1) / kT);
 
   for (int tile = 0;; ++tile) {
@@ -998,6 +1038,32 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
       // half 1).
 #pragma unroll
       for (int set = 0; set < (KVF ? 3 : 1); ++set) {
+        const int nb_lo = KVF ? (set == 0 ? 0 : (set == 1 ? 8 : 12)) : 0;
+        const int nb_hi = KVF ? (set == 0 ? 8 : (set == 1 ? 12 : 16)) : 16;
+        float sc[2][8];
+        float smax = 0.f;
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int kb = 2 * kp + i / 4, j = i % 4;
+            sc[kp][i] = 1.0f;
+            if (KVF && !(set == 2 && h2 == 1)) sc[kp][i] = L.scl[set == 0 ? 2 * h2 : 2 * h2 + 1][16 * kb + 4 * g + j];
+            smax = fmaxf(smax, sc[kp][i]);
+          }
+        // the set's frame over the tile's 64 keys (keys 16kb + 4g + j: the max over the
+        // lane's keys, then the groups)
+        float fr = 1.0f;
+        if (KVF && !(set == 2 && h2 == 1)) {
+          fr = scale_frame(rows_max(smax));
+          const float f = fr / fr_run[set];  // a power of two: exact
+          if (f != 1.0f) {
+#pragma unroll
+            for (int nb = 0; nb < 16; ++nb)
+              if (nb >= nb_lo && nb < nb_hi) OT[nb] *= f;
+            fr_run[set] = fr;
+          }
+        }
         uint4 pk[2];
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
@@ -1005,15 +1071,11 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int kb = 2 * kp + i / 4, j = i % 4;
-            float sc = 1.0f;
-            if (KVF && !(set == 2 && h2 == 1)) sc = L.scl[set == 0 ? 2 * h2 : 2 * h2 + 1][16 * kb + 4 * g + j];
-            x[i] = pr[kb][j] * sc;
+            x[i] = KVF ? (pr[kb][j] * sc[kp][i]) * fr : pr[kb][j];
           }
           pk[kp] = make_uint4(pack16<KVF>(x[0], x[1]), pack16<KVF>(x[2], x[3]), pack16<KVF>(x[4], x[5]),
                               pack16<KVF>(x[6], x[7]));
         }
-        const int nb_lo = KVF ? (set == 0 ? 0 : (set == 1 ? 8 : 12)) : 0;
-        const int nb_hi = KVF ? (set == 0 ? 8 : (set == 1 ? 12 : 16)) : 16;
         // V^T operands of 2 dim blocks read together, then their MFMAs
 #pragma unroll
         for (int nb0 = nb_lo; nb0 < nb_hi; nb0 += 2) {
@@ -1041,6 +1103,13 @@ __global__ void __launch_bounds__(512) attend_long_kernel(AttendArgs a, int n_hg
     if (!has_next) break;
   }
 
+  if (KVF) {  // back from the value-set frames (exact)
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) {
+      const int set = nb < 8 ? 0 : (nb < 12 ? 1 : 2);
+      OT[nb] *= 1.0f / fr_run[set];
+    }
+  }
   // the fold from the sink over the single chunk: O = 0 * fa + O_chunk * fb
   float fa, fb;
   fold_step(fs, m_run, l_run, &fa, &fb);

@@ -63,4 +63,10 @@ size_t attend_partials_bytes(const AttendArgs& a);
 size_t attend_workspace_bytes(const AttendArgs& a);
 hipError_t launch_attend(const AttendArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
 
+// The grouped output projection: stage one batched over the head groups into the bf16
+// intermediate y, stage two from y into out (both batch-invariant bf16 GEMMs).
+hipError_t launch_grouped_out_proj(int n_tok, const uint8_t* o, int n_h, int dim, int groups, int d_g,
+                                   const uint8_t* w1, const uint8_t* w2, int d_out, uint8_t* y, uint8_t* out,
+                                   hipStream_t stream);
+
 }  // namespace csa

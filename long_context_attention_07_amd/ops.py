@@ -19,7 +19,7 @@ OP_INDEX_TOPK, OP_CSA_ATTEND, OP_HCA_ATTEND, OP_TOPK, OP_INDEX_TOPK_BF16 = 1, 2,
 
 EXPORTS = ("csa_compress", "csa_compress2", "csa_index_score", "csa_index_score_bf16", "csa_topk", "csa_topk_bf16",
            "csa_index_topk", "csa_index_topk_bf16", "csa_index_topk_noalloc", "csa_attend", "hca_attend",
-           "csa_workspace_bytes", "csa_strerror", "csa_last_error", "csa_version")
+           "csa_grouped_out_proj", "csa_workspace_bytes", "csa_strerror", "csa_last_error", "csa_version")
 
 
 class CsaError(RuntimeError):
@@ -68,6 +68,8 @@ def lib():
                                  f64, P(csa_rows), vp, vp, sz, vp]
         L.hca_attend.argtypes = [P(csa_seqs), P(csa_rows), i32, P(csa_rows), i32, P(csa_rows), i32, vp, f32, i32, f64,
                                  P(csa_rows), vp, vp, sz, vp]
+        L.csa_grouped_out_proj.argtypes = [i32, vp, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp]
+        L.csa_grouped_out_proj.restype = i32
         L.csa_workspace_bytes.argtypes = [i32, P(csa_seqs), i32, i32, i32, i32, i32]
         L.csa_workspace_bytes.restype = sz
         L.csa_strerror.argtypes = [i32]
@@ -234,3 +236,10 @@ def hca_attend(seqs, q, n_h, kv, ratio, tok, n_win, sink, scale, rope_dims, rope
     _check(lib().hca_attend(ctypes.byref(seqs.c), ctypes.byref(q.c), n_h, ctypes.byref(kv.c), ratio,
                             ctypes.byref(tok.c), n_win, _ptr(sink), scale, rope_dims, rope_theta, ctypes.byref(out.c),
                             _ptr(lse), _ptr(ws), nbytes, _stream(stream)), "hca_attend")
+
+
+def csa_grouped_out_proj(o, n_h, dim, groups, d_g, w1, w2, d_out, y, out, stream=None):
+    """o bf16 [n_tok, n_h * dim]; w1 bf16 [groups, d_g, n_h/groups * dim]; w2 bf16 [d_out, groups * d_g];
+    y bf16 [n_tok, groups * d_g] and out bf16 [n_tok, d_out] are written."""
+    _check(lib().csa_grouped_out_proj(int(o.shape[0]), _ptr(o), n_h, dim, groups, d_g, _ptr(w1), _ptr(w2), d_out,
+                                      _ptr(y), _ptr(out), _stream(stream)), "csa_grouped_out_proj")

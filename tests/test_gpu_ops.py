@@ -525,6 +525,58 @@ def test_attend_matches_oracle(case):
     assert_close(lse.cpu().numpy(), ref_l, tol, "attend lse")
 
 
+@pytest.mark.parametrize("row_scale", ["1e-3", "3e5", "mixed"])
+@pytest.mark.parametrize("k", [256, 1024])
+def test_attend_fp8_rows_far_from_unit_scale(row_scale, k):
+    """fp8 (KV split) rows whose fp8 dims are scaled far from 1: by 1e-3 (P times the block
+    scale would fall into fp16 subnormals), by 3e5 (it would overflow fp16) and per row by
+    exp(U(-7, 7)) (scales within a tile spread over six decades).  The bf16 tail stays N(0,1)
+    (it enters the fp16 logits, whose range it must respect).  Errors are measured against
+    each block of dims' own output scale: per (token, head), max |gpu - oracle| over the fp8
+    dims divided by max |oracle| over them (and likewise for the tail), at most 1e-2; the
+    pair kernel (k = 256) and the 64-head kernel (k = 1024)."""
+    g = np.random.default_rng(57 + k + len(row_scale))
+    D, n_h, n_win, ratio = 512, 64, 128, 4
+    n_q, ctx = [1, 2, 1, 3], [5000, 2047, 9000, 700]
+    ob, sq, n_ent, n_tok = make_batch(n_q, ctx, ratio, tok_hist=n_win + 3)
+
+    def rows(n):
+        x = g.standard_normal((max(n, 1), D))
+        if row_scale == "mixed":
+            sc = np.exp(g.uniform(-7, 7, (x.shape[0], 1)))
+        else:
+            sc = float(row_scale)
+        x[:, :D - 64] *= sc
+        return kv_split(x)
+
+    q_rows, q_val = _rows_in(ops.BF16, g.standard_normal((sq.total_q * n_h, D)))
+    kv_rows, kv_val = rows(n_ent)
+    tok_rows, tok_val = rows(n_tok)
+    sink_t, sink_val = f32(g.standard_normal(n_h))
+    idx = np.full((sq.total_q, k), -1, dtype=np.int32)
+    for row, b, p in ob.tokens():
+        V = visible(p, ratio)
+        idx[row, :min(V, k)] = np.sort(g.choice(V, size=min(V, k), replace=False))
+    scale = 1.0 / math.sqrt(D)
+    out = empty_rows(sq.total_q * n_h, D, ops.BF16)
+    lse = torch.zeros((sq.total_q, n_h), dtype=torch.float32, device=DEV)
+    ops.csa_attend(sq, q_rows, n_h, kv_rows, torch.from_numpy(idx).to(DEV), k, tok_rows, n_win, sink_t, scale, 64,
+                   10000.0, out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = _oracle_attend(ob, q_val, kv_val, tok_val, idx, n_win, sink_val, scale, 64, n_h, D, True, ratio)
+    got = rows_values(out).reshape(sq.total_q, n_h, D)
+    assert np.all(np.isfinite(got)), "non-finite outputs"
+    worst = 0.0
+    for lo, hi in ((0, D - 64), (D - 64, D)):
+        num = np.max(np.abs(got[..., lo:hi] - ref_o[..., lo:hi]), axis=-1)
+        den = np.maximum(np.max(np.abs(ref_o[..., lo:hi]), axis=-1), 1e-300)
+        rel = float(np.max(num / den))
+        assert rel <= 1e-2, f"dims {lo}:{hi}: error {rel:.3e} of the output's scale"
+        worst = max(worst, rel)
+    assert_close(lse.cpu().numpy(), ref_l, 1e-2, "attend lse")
+    log(f"fp8 rows scaled {row_scale}, k={k}: error {worst:.2e} of the output's scale")
+
+
 @pytest.mark.parametrize("fmt,k,rope,n_win", [(ops.BF16, 512, 32, 128), (ops.BF16, 1024, 32, 128),
                                               (ops.KV_SPLIT, 1024, 0, 128), (ops.BF16, 1024, 64, 0),
                                               (ops.KV_SPLIT, 256, 32, 128)])

@@ -23,7 +23,7 @@ PROBE_LIB = os.path.join(PKG, "libcsa_probe.so")
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["abi.cpp", "compress.hip", "index.hip", "index_mfma.hip", "index_mx.hip", "topk.hip", "attend.hip",
-           "attend_mfma.hip", "outproj.hip"]
+           "attend_mfma.hip", "attend_wave.hip", "outproj.hip"]
 PROBE_SOURCES = ["probe.hip"]
 
 COMMON_FLAGS = [
@@ -37,6 +37,11 @@ COMMON_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+# Per-source additions.  The wave kernel rescales its matrix-core accumulators with vector
+# instructions between products; with the accumulators in ordinary vector registers the
+# compiler keeps each in place across the loop instead of copying all of them per step.
+SOURCE_FLAGS = {"attend_wave.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -48,7 +53,7 @@ def hipcc():
 def _compile(src):
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + COMMON_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + COMMON_FLAGS + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc()] + COMMON_FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

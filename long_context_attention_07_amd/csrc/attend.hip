@@ -19,7 +19,7 @@
 // keys per tile, logits and P.V on the vector ALUs; bf16 rows of 512 dims go to the
 // matrix-core kernel (attend_mfma.hip).
 
-#include "attend_common.cuh"
+#include "attend_common.h"
 
 namespace csa {
 

@@ -3,7 +3,7 @@
 // that folds chunk partials in chunk order from the sink.
 #pragma once
 
-#include "common.cuh"
+#include "common.h"
 #include "kernels.h"
 
 namespace csa {

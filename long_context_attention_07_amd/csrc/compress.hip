@@ -15,7 +15,7 @@
 // the result depends on the entry alone.  Memory bound: the grid is (sequence, new entry), entries of a sequence being
 // consecutive workgroups.
 
-#include "common.cuh"
+#include "common.h"
 #include "kernels.h"
 
 namespace csa {

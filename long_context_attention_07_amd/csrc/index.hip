@@ -10,7 +10,7 @@
 // LDS, the entry's key row decoded into registers; dims then heads are summed in
 // ascending order, so a score depends on its token and entry only.
 
-#include "common.cuh"
+#include "common.h"
 #include "kernels.h"
 
 namespace csa {

@@ -20,7 +20,7 @@
 //   row-swap permutes across the lane groups finish the head sum, so a score depends on its
 //   token and entry only.
 
-#include "common.cuh"
+#include "common.h"
 #include "kernels.h"
 
 namespace csa {

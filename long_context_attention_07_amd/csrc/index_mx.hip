@@ -30,7 +30,7 @@
 // (g2 + g3); so its bits do not depend on the kernel or on which other queries share the
 // workgroup.
 
-#include "common.cuh"
+#include "common.h"
 #include "kernels.h"
 
 namespace csa {

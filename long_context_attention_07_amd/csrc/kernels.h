@@ -3,7 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "common.cuh"
+#include "common.h"
 
 namespace csa {
 

@@ -20,7 +20,7 @@
 // transposed (W fragments as the A operand), so a lane holds 4 consecutive outputs of one
 // row and stores them as one 8-byte write.
 
-#include "common.cuh"
+#include "common.h"
 #include "kernels.h"
 
 namespace csa {

@@ -16,7 +16,7 @@
 // workgroup re-reads the scores from memory every pass.  Scores are float32, or bf16 (the
 // selector's bf16 scores of section 3.4), keyed as the float32 values they stand for.
 
-#include "common.cuh"
+#include "common.h"
 #include "kernels.h"
 
 namespace csa {

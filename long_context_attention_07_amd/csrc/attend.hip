@@ -190,17 +190,13 @@ int64_t attend_max_chunks(const AttendArgs& a) {
 }
 
 // Whether a call cuts its key lists over several workgroups (the combine kernel then folds
-// the chunk partials): only when a list has more than one chunk, the kernel family works
-// chunk by chunk (the 64-head long-list kernel for CSA with k >= 1024 over 512-dim rows
-// walks whole lists), and the batch is too small to fill the chip with one workgroup per
-// token and head group.  Depends on host scalars only, never on the row format, so the
-// workspace query and the launch agree.
+// the chunk partials): only when a list has more than one chunk and the batch is too small
+// to fill the chip with one workgroup per token and head group.  Depends on host scalars
+// only, never on the row format, so the workspace query and the launch agree (the 64-head
+// kernel for fp8 rows with k >= 1024, which walks whole lists, leaves the workspace unused).
 bool attend_split_wanted(const AttendArgs& a) {
   if (attend_max_chunks(a) <= 1) return false;
-  if (a.q.dim == kMfmaHeadDim) {
-    if (a.csa && a.k >= kLongListKeys) return false;
-    return (int64_t)a.S.total_q * ((a.n_h + 15) / 16) < 512;
-  }
+  if (a.q.dim == kMfmaHeadDim) return (int64_t)a.S.total_q * ((a.n_h + 15) / 16) < 512;
   return (int64_t)a.S.total_q * ((a.n_h + kValuHG - 1) / kValuHG) < 1024;
 }
 

@@ -162,16 +162,18 @@ __global__ void __launch_bounds__(256) attend_combine_kernel(AttendArgs a, const
   if (a.lse && l32 == 0) a.lse[orow] = lse_natural(f);
 }
 
-// Chunk length in key slots: CSA key lists have a fixed length k + n_win, cut into
-// ceil((k + n_win) / 384) equal chunks rounded up to whole 64-key tiles, except that lists
-// with k >= 1024 are one chunk (their kernel gives each token all 64 heads at once);
-// HCA lists grow with the context and use 576-slot (9-tile) chunks.  Depends on op
-// parameters only.
+// Chunk length in key slots: CSA key lists have a fixed length S = k + n_win, cut into
+// n = ceil(S / 576) equal chunks rounded up to whole 64-key tiles (at most 576 slots:
+// S / n <= 576, a multiple of 64), so k = 512 with the 128-token window is two chunks of
+// 320 and k = 1024 two of 576; HCA lists grow with the context and use 576-slot (9-tile)
+// chunks.  Depends on op parameters only.  (The 64-head kernel for fp8 rows with
+// k >= 1024 walks whole lists and takes no chunks.)
+constexpr int kMaxChunkSlots = 576;
 __host__ __device__ inline int chunk_slots_for(int csa, int k, int n_win) {
-  if (!csa) return 576;
-  if (k >= 1024) return ((k + n_win + 63) / 64) * 64;
+  if (!csa) return kMaxChunkSlots;
   const int S = k + n_win;
-  const int n = (S + 383) / 384;
+  if (S <= 0) return 64;  // an empty list (no entries, no window): one empty chunk
+  const int n = (S + kMaxChunkSlots - 1) / kMaxChunkSlots;
   const int c = (S + n - 1) / n;
   return ((c + 63) / 64) * 64;
 }

@@ -4,10 +4,12 @@
 // the 128-token window concatenated; list "其他注意力技术细节": partial RoPE on the last 64
 // dims, inverse RoPE of the output, learnable sink; section 3.4: fp8 KV with 1x128 scales).
 //
-// Two kernels.  The pair kernel (HCA, and CSA with k < 1024): workgroup = (token, group of
-// 16 query heads, chunk of the token's key list), 8 waves in 4 pairs.  The long-list kernel
-// (CSA with k >= 1024, one chunk): workgroup = (token, 64 heads), 8 waves, so each gathered
-// row is read once per token (see the kernels).  The key list is walked in tiles of 64 rows
+// Two kernels for fp8 (KV split) rows; bf16 rows take the wave kernel (attend_wave.hip),
+// which has the pair kernel's arithmetic.  The templates below also take bf16 rows (KVF =
+// false), which no launch uses.  The pair kernel (HCA, and CSA with k < 1024): workgroup =
+// (token, group of 16 query heads, chunk of the token's key list), 8 waves in 4 pairs.  The
+// long-list kernel (CSA with k >= 1024, whole lists): workgroup = (token, 64 heads), 8 waves,
+// so each gathered row is read once per token (see the kernels).  The key list is walked in tiles of 64 rows
 // staged in LDS (rows padded to 1056 bytes); each wave prefetches its share of the next
 // tile into registers, or for fp8 rows in the long-list kernel straight into LDS (one row
 // per wave instruction, any row order, so the top-k gather is fully coalesced).
@@ -973,8 +975,10 @@ static void launch_attend_mfma_kernel(const AttendArgs& a, float* ws_o, float* w
 }
 
 // Which kernel a call uses depends on the operation's parameters only (the key list
-// length), never on the batch, so a token's bits do not depend on the batch either.
-static bool attend_long_lists(const AttendArgs& a) { return a.csa && a.k >= kLongKeys; }
+// length and the row format), never on the batch, so a token's bits do not depend on the
+// batch either: bf16 rows take the wave kernel at every k, fp8 rows the pair kernel below
+// k = 1024 and the 64-head kernel from there.
+static bool attend_long_lists(const AttendArgs& a) { return a.csa && a.k >= kLongKeys && a.kv.dtype == DT_KV_SPLIT; }
 
 constexpr int64_t kCombineWideWgs = 256;  // combine workgroups from which 8 dims per lane are used
 
@@ -983,10 +987,7 @@ hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hi
     const int n_hg = (a.n_h + kHeadsLong - 1) / kHeadsLong;
     const int64_t n_log = (int64_t)a.S.total_q * n_hg;
     const int64_t n_phys = (n_log + 7) / 8 * 8;
-    if (a.kv.dtype == DT_KV_SPLIT)
-      hipLaunchKernelGGL((attend_long_kernel<true>), dim3((unsigned)n_phys), dim3(512), 0, stream, a, n_hg, (int)n_log);
-    else
-      hipLaunchKernelGGL((attend_long_kernel<false>), dim3((unsigned)n_phys), dim3(512), 0, stream, a, n_hg, (int)n_log);
+    hipLaunchKernelGGL((attend_long_kernel<true>), dim3((unsigned)n_phys), dim3(512), 0, stream, a, n_hg, (int)n_log);
     return hipGetLastError();
   }
   const int n_hg = (a.n_h + kHG - 1) / kHG;

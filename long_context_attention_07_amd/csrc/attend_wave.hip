@@ -25,7 +25,7 @@ namespace csa {
 // 8, the four wave states merged in wave order at the chunk end through LDS, and the same
 // fold and finalisation, so the two kernels give the same bits for bf16 rows.
 constexpr int kWaveStages = 2;
-constexpr int kWaveIdx = kLongListKeys;  // entry ids a workgroup keeps (CSA k < 1024)
+constexpr int kWaveIdx = kMaxChunkSlots;  // entry ids of one CSA chunk
 constexpr int kWaveMergeStride = kDM + 4;  // floats per (wave, head) row of the merge scratch
 constexpr int kStageBytes = 16 * kKStride;
 constexpr int kStageLoBytes = 16 * kLoStride;
@@ -33,7 +33,7 @@ constexpr int kStageLoBytes = 16 * kLoStride;
 struct __align__(16) WaveLds {
   uint8_t ring[4][kWaveStages][kStageBytes];    // each wave's stages; merge scratch at chunk ends
   uint8_t klo[4][kWaveStages][kStageLoBytes];   // window rows: residuals of their rotated last 64 dims
-  int32_t sidx[kWaveIdx];                       // idx[t, s_lo .. s_hi) of this workgroup's chunks
+  int32_t sidx[kWaveIdx];                       // idx[t, chunk start ..) of the chunk in hand
   float red_max[4][kHG];                        // wave states at the end of a chunk
   float red_sum[4][kHG];
 };
@@ -141,13 +141,17 @@ attend_wave_kernel(AttendArgs a, float* __restrict__ ws_o,
       raw[i] = hq_ok ? *reinterpret_cast<const uint4*>(qrow + (32 * i + 8 * g) * 2) : make_uint4(0u, 0u, 0u, 0u);
   }
   const int c_begin = SPLIT ? c_only : 0;
-  const int64_t s_lo = (int64_t)c_begin * chunk_slots;
-  if (a.csa) {
-    const int n_chunks_csa = (int)(((int64_t)a.k + a.n_win + chunk_slots - 1) / chunk_slots);
-    const int64_t s_hi = min((int64_t)(SPLIT ? c_only + 1 : n_chunks_csa) * chunk_slots, (int64_t)a.k);
-    const int32_t* src = a.idx + (int64_t)t * a.k;
-    for (int64_t s = s_lo + tid; s < s_hi; s += 256) L.sidx[s - s_lo] = src[s];
-  }
+  int64_t s_lo = (int64_t)c_begin * chunk_slots;  // first slot of the chunk in hand
+  // the chunk's entry ids into LDS (CSA): the first chunk's here, later ones (single
+  // launch) when their chunk starts
+  auto load_sidx = [&]() {
+    if (a.csa) {
+      const int64_t s_hi = min(s_lo + chunk_slots, (int64_t)a.k);
+      const int32_t* src = a.idx + (int64_t)t * a.k;
+      for (int64_t s = s_lo + tid; s < s_hi; s += 256) L.sidx[s - s_lo] = src[s];
+    }
+  };
+  load_sidx();
   load_freqs(F, a.rope);
   // merge layout: thread (head th, dims 128 r + 8 td + 4 i4 + e)
   const int th = tid >> 4, td = tid & 15;
@@ -229,18 +233,36 @@ attend_wave_kernel(AttendArgs a, float* __restrict__ ws_o,
       wave_rotate8(rows, lo, sm.win, 0, sm.pos0, lane, dn, F);
       wave_rotate8(rows, lo, sm.win, 8, sm.pos0, lane, dn, F);
     }
-    // ---- S^T = K Q^T: dims 0..255 and 256..511 in two chains, added
+    // ---- S^T = K Q^T: dims 0..255 and 256..511 in two chains, added.  The key fragments
+    // are read a batch of four k-steps ahead of their products (two register sets), so the
+    // LDS latency overlaps the matrix core.
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
     {
+      // batch b: k-steps 2b, 2b + 1 (first chain) and 8 + 2b, 9 + 2b (second chain), so the
+      // two chains alternate on the matrix core; each chain keeps its k-step order
       const uint8_t* krow = rows + c16 * kKStride + 16 * g;
+      auto kstep = [](int b, int i) { return (i < 2 ? 2 * b : 8 + 2 * b - 2) + i; };
+      uint4 ka[2][4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        acc0 = mfma16<false>(*reinterpret_cast<const uint4*>(krow + 64 * i), qf[i], acc0);
+      for (int i = 0; i < 4; ++i) ka[0][i] = *reinterpret_cast<const uint4*>(krow + 64 * kstep(0, i));
 #pragma unroll
-      for (int i = 8; i < 16; ++i) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(krow + 64 * i);
-        acc1 = mfma16<false>(ka, qf[i], acc1);
-        if (i >= 14) acc1 = mfma16<false>(ka, qlo[i - 14], acc1);
+      for (int b = 0; b < 4; ++b) {
+        if (b < 3) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ka[(b + 1) & 1][i] = *reinterpret_cast<const uint4*>(krow + 64 * kstep(b + 1, i));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = kstep(b, i);
+          if (kk < 8) {
+            acc0 = mfma16<false>(ka[b & 1][i], qf[kk], acc0);
+          } else {
+            acc1 = mfma16<false>(ka[b & 1][i], qf[kk], acc1);
+            if (kk >= 14) acc1 = mfma16<false>(ka[b & 1][i], qlo[kk - 14], acc1);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (sm.win != 0u) {
         const uint8_t* lrow = lo + c16 * kLoStride + 16 * g;
@@ -277,12 +299,24 @@ attend_wave_kernel(AttendArgs a, float* __restrict__ ws_o,
 #pragma unroll
       for (int nb = 0; nb < 32; ++nb) OT[nb] *= alpha;
     }
+    // V^T fragments read eight dim blocks ahead of their products (two register sets)
     const uint8_t* vbase = rows + (4 * g + (c16 >> 2)) * kKStride + 4 * (c16 & 3) * 2;
     const i16x4_t pv = __builtin_bit_cast(i16x4_t, make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)));
+    i16x4_t vt[2][8];
 #pragma unroll
-    for (int nb = 0; nb < 32; ++nb) {
-      const i16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vbase + 32 * nb));
-      OT[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pv, OT[nb], 0, 0, 0);
+    for (int i = 0; i < 8; ++i) vt[0][i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vbase + 32 * i));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b < 3) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          vt[(b + 1) & 1][i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(vbase + 32 * (8 * (b + 1) + i)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        OT[8 * b + i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[b & 1][i], pv, OT[8 * b + i], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -306,7 +340,12 @@ attend_wave_kernel(AttendArgs a, float* __restrict__ ws_o,
     for (int nb = 0; nb < 32; ++nb) OT[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m_run = -INFINITY;
     l_run = 0.f;
-    if (cc != c_begin) request_first(cc);
+    if (cc != c_begin) {
+      s_lo = (int64_t)cc * chunk_slots;
+      load_sidx();
+      __syncthreads();
+      request_first(cc);
+    }
     for (int j = 0; j < ntile; ++j) {
       if (j + 1 < ntile)
         asm volatile("s_waitcnt vmcnt(16)" ::: "memory");

@@ -52,7 +52,7 @@ int attend_chunk_slots(const AttendArgs& a);
 // Number of chunks of the longest key list the launch can see (grid / workspace sizing).
 int64_t attend_max_chunks(const AttendArgs& a);
 constexpr int kMfmaHeadDim = 512;    // head dim of the matrix-core attention kernels
-constexpr int kLongListKeys = 1024;  // CSA key lists from this k run whole on the 64-head kernel
+constexpr int kLongListKeys = 1024;  // fp8 (KV split) CSA lists from this k run whole on the 64-head kernel
 
 // Whether the call splits key lists over workgroups (host scalars only).
 bool attend_split_wanted(const AttendArgs& a);

@@ -132,19 +132,20 @@ def test_workspace_sizes(lib):
 
 def test_workspace_sizes_follow_the_launch(lib):
     """The attention workspace is exactly what the call would use: the chunk partials when
-    key lists are cut over several workgroups, 0 when they are not (one chunk per list,
-    the whole-list kernel for CSA with k >= 1024 over 512-dim rows, or a batch that fills
-    the chip with one workgroup per token and head group)."""
+    key lists are cut over several workgroups, 0 when they are not (one chunk per list, or
+    a batch that fills the chip with one workgroup per token and head group; the 64-head
+    kernel that fp8 rows with k >= 1024 take leaves it unused)."""
     P = ctypes.byref
     ws = lambda s, op, n_h, d, k, r, w: lib.csa_workspace_bytes(op, P(s), n_h, d, k, r, w)  # noqa: E731
     c2 = _seqs(n_seqs=32, total_q=32, max_q=1, max_ctx=65536)
     # k = 512, window 128: 640 slots in two 320-slot chunks
     assert ws(c2, ops.OP_CSA_ATTEND, 64, 512, 512, 4, 128) == 32 * 2 * 64 * 514 * 4 + 32 * 16
-    # k >= 1024: whole lists on the 64-head kernel, no workspace (prefill and decode alike)
+    # k = 1024: 1152 slots in two 576-slot chunks for a decode batch; the prefill batch
+    # fills the chip without splitting
     c4 = _seqs(n_seqs=1, total_q=131072, max_q=131072, max_ctx=131072)
     assert ws(c4, ops.OP_CSA_ATTEND, 64, 512, 1024, 4, 128) == 0
-    assert ws(c2, ops.OP_CSA_ATTEND, 64, 512, 1024, 4, 128) == 0
-    # one chunk per list: k + window <= 384 slots
+    assert ws(c2, ops.OP_CSA_ATTEND, 64, 512, 1024, 4, 128) == 32 * 2 * 64 * 514 * 4 + 32 * 16
+    # one chunk per list: k + window <= 576 slots
     assert ws(c2, ops.OP_CSA_ATTEND, 64, 512, 64, 4, 128) == 0
     # large batches run one workgroup per (token, 16 heads): 128 tokens x 4 groups = 512
     big = _seqs(n_seqs=128, total_q=128, max_q=1, max_ctx=65536)

@@ -485,8 +485,9 @@ ATTEND_CASES = [
     (ops.BF16, 512, 16, True, 4, 100, 0),
     (ops.KV_SPLIT, 512, 64, True, 4, 256, 128),
     (ops.KV_SPLIT, 512, 64, False, 128, 0, 128),
-    # the 64-head kernel for k >= 1024: tokens with no visible entry (whole tiles absent),
-    # a part-filled head group, a 64-token window
+    # k >= 1024 (fp8 rows: the 64-head kernel over whole lists; bf16 rows: the wave kernel
+    # over 384-slot chunks): tokens with no visible entry (whole tiles absent), a
+    # part-filled head group, a 64-token window
     (ops.BF16, 512, 64, True, 4, 2048, 128),
     (ops.KV_SPLIT, 512, 64, True, 4, 1024, 128),
     (ops.KV_SPLIT, 512, 40, True, 4, 4096, 64),
@@ -581,8 +582,8 @@ def test_attend_fp8_rows_far_from_unit_scale(row_scale, k):
                                               (ops.KV_SPLIT, 1024, 0, 128), (ops.BF16, 1024, 64, 0),
                                               (ops.KV_SPLIT, 256, 32, 128)])
 def test_attend_rope_widths_and_no_window(fmt, k, rope, n_win):
-    """Rotary widths other than 64 (32 dims, none) in the pair kernel (k < 1024) and the
-    64-head kernel (k >= 1024), and the 64-head kernel without a window."""
+    """Rotary widths other than 64 (32 dims, none) for bf16 rows (the wave kernel) and fp8
+    rows with k >= 1024 (the 64-head kernel), and bf16 rows with k >= 1024 and no window."""
     log(f"attend rope={rope} fmt={fmt} k={k} n_win={n_win}")
     g = np.random.default_rng(71 + k + rope + n_win)
     D, n_h, ratio = 512, 64, 4
@@ -606,7 +607,7 @@ def test_attend_split_and_single_modes_bit_identical(fmt, D, n_h):
     workgroup walks them.  The outputs must agree bit for bit."""
     g = np.random.default_rng(5)
     n_q, ctx = [1, 1, 2], [4000, 70000, 600]
-    for csa, ratio, k in ((True, 4, 512), (False, 128, 0), (False, 4, 0)):
+    for csa, ratio, k in ((True, 4, 512), (True, 4, 1024), (True, 4, 2048), (False, 128, 0), (False, 4, 0)):
         data = _attend_inputs(g, fmt, D, n_h, n_q, ctx, ratio, k, 128, tok_hist=140)
         ob, sq, q_rows, _, kv_rows, _, tok_rows, _, sink_t, _, idx = data
         idx_t = torch.from_numpy(idx).to(DEV)

@@ -130,15 +130,20 @@ attend_wave_kernel(AttendArgs a, float* __restrict__ ws_o,
   const int g = lane >> 4, c16 = lane & 15;
   const int dn = kDM - a.rope.dims;
 
-  // query fragments of head 16 hg + c16, dims 32i + 8g .. +7 (i = 0..15), into registers
+  // the query block of the head group (16 heads x 1 KiB) into LDS once per workgroup, at the
+  // stage slot wave 3's second stage takes (free until the first requests): thread tid
+  // moves 64 bytes of head tid / 16 (zeros for heads past n_h)
   const uint8_t* q0row = a.q.data + ((int64_t)t * a.n_h + hg * kHG) * a.q.stride;
-  const bool hq_ok = hg * kHG + c16 < a.n_h;
-  uint4 raw[16];
+  uint8_t* const qblk = L.ring[3][1];
   {
-    const uint8_t* qrow = q0row + (int64_t)(hq_ok ? c16 : 0) * a.q.stride;
+    const int hh = tid >> 4, part = tid & 15;
+    const bool ok = hg * kHG + hh < a.n_h;
+    const uint4* src = reinterpret_cast<const uint4*>(q0row + (int64_t)(ok ? hh : 0) * a.q.stride + 64 * part);
+    uint4 v[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      raw[i] = hq_ok ? *reinterpret_cast<const uint4*>(qrow + (32 * i + 8 * g) * 2) : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 4; ++i) v[i] = ok ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(qblk + hh * kKStride + 64 * part + 16 * i) = v[i];
   }
   const int c_begin = SPLIT ? c_only : 0;
   int64_t s_lo = (int64_t)c_begin * chunk_slots;  // first slot of the chunk in hand
@@ -171,6 +176,10 @@ attend_wave_kernel(AttendArgs a, float* __restrict__ ws_o,
   const int c_end = SPLIT ? c_only + 1 : n_chunks;
   __syncthreads();
 
+  // query fragments of head 16 hg + c16, dims 32i + 8g .. +7 (i = 0..15)
+  uint4 raw[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) raw[i] = *reinterpret_cast<const uint4*>(qblk + c16 * kKStride + 64 * i + 16 * g);
   uint4 qf[16];
   uint4 qlo[2];  // residuals of the rotated dims among 448..511
 #pragma unroll
@@ -187,6 +196,7 @@ attend_wave_kernel(AttendArgs a, float* __restrict__ ws_o,
   for (int i = 0; i < 16; ++i) pin_acc(qf[i]);
   pin_acc(qlo[0]);
   pin_acc(qlo[1]);
+  __syncthreads();  // the query block read: its slot may take rows
 
   FoldState fs = fold_init(h_m < a.n_h ? sink_m * kLog2e : -INFINITY);
   float ofold[SPLIT ? 1 : 32];

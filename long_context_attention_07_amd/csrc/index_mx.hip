@@ -38,7 +38,9 @@ namespace csa {
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int mx_v8i;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float mx_v4f;
 
-constexpr int kMxRange = 1024;  // entries per workgroup, one query row each
+constexpr int kMxRange = 1024;  // entries per workgroup, one query row each (at least)
+constexpr int kMxRangeMax = 16384;
+constexpr int kMxTargetWgs = 2048;  // decode launches aim at about this many workgroups
 constexpr int kMxPart = 32768;  // entries per workgroup, 8 query rows each
 constexpr int kMxFmtE2M1 = 4;   // operand format codes of the scaled MFMA: e2m1
 constexpr int kMxFmtE4M3 = 0;   // and fp8 e4m3
@@ -109,11 +111,11 @@ __device__ __forceinline__ float head_sum(const mx_v4f (&acc)[4], const float (&
 template <int QB, bool F8>
 __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
                                                              int n_I, RowsDev kI, int ratio, ScoreOut score,
-                                                             int n_parts) {
+                                                             int n_parts, int range) {
   const int rb = blockIdx.x / n_parts, part = blockIdx.x % n_parts;
   const int t_blk = rb * QB;
   const int t_end = min(t_blk + QB, S.total_q);
-  const int64_t e_begin = (int64_t)part * kMxRange;
+  const int64_t e_begin = (int64_t)part * range;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
 
@@ -148,7 +150,7 @@ __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev 
             if (F8 && on) wv_ *= reinterpret_cast<const float*>(qI.scales)[row];
             wr[i][hb][j] = wv_;
           }
-      const int64_t e_stop = min(e_begin + (int64_t)kMxRange, v_max);
+      const int64_t e_stop = min(e_begin + (int64_t)range, v_max);
       const BlockIds bids = load_block_ids(S, ctx.b, e_begin);
       // wave wv takes the 16-entry blocks e_begin + 16 (wv + 4 it); 4 blocks in flight
       for (int64_t e0 = e_begin + 16 * wv; e0 < e_stop; e0 += 4 * 64) {
@@ -308,10 +310,16 @@ static void launch_mx(const SeqsDev& S, const RowsDev& qI, const float* w, int n
     hipLaunchKernelGGL(index_score_mx_block_kernel<F8>, dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I,
                        kI, ratio, score, parts);
   } else {
-    const int n_parts = (max_vis + kMxRange - 1) / kMxRange;
+    // entries per workgroup: kMxRange, or more when the launch would otherwise hold many
+    // more workgroups than the chip runs at once (each has a prologue of its own: context,
+    // query operands, weights); a score's bits do not depend on the split
+    const int64_t total = (int64_t)S.total_q * max_vis;
+    int range = kMxRange;
+    while (range < kMxRangeMax && total / range > kMxTargetWgs) range *= 2;
+    const int n_parts = (max_vis + range - 1) / range;
     const int64_t blocks = (int64_t)S.total_q * n_parts;
     hipLaunchKernelGGL((index_score_mx_kernel<1, F8>), dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I,
-                       kI, ratio, score, n_parts);
+                       kI, ratio, score, n_parts, range);
   }
 }
 

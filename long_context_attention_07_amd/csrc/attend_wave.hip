@@ -87,10 +87,13 @@ struct StageMeta {
 // the ring's stages apart), which would undo the staging; the kernel waits on the vector
 // memory counter itself, per stage.
 // M0 (the LDS address register of the load) is saved and restored around it, as the
-// compiler does not expect assembly to change it.
+// compiler does not expect assembly to change it.  The compiler does not look inside the
+// statement for hazards either: the row address usually comes from v_readlane, and a
+// vector-memory instruction needs 5 wait states after a VALU write of an SGPR it reads
+// (and one after the M0 write), so the statement waits 5 itself.
 __device__ __forceinline__ void dma_row(uint64_t row, uint32_t voff, uint32_t lds) {
   uint32_t keep;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
                : "=&s"(keep)
                : "v"(voff), "s"(row), "s"(lds)
                : "memory");

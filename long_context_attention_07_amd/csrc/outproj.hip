@@ -158,19 +158,20 @@ __global__ void __launch_bounds__(256) gemm_nt_bf16_kernel(GemmArgs g, int tiles
 }
 
 // Few rows (M <= 64, a decode batch): the weight stream is the whole cost.  No LDS and no
-// barriers: wave w of a workgroup owns the 16 output columns n0 + 16 w .. +15 for all rows,
-// and streams its weight fragments (and the rows' fragments, small and cached) straight
-// into registers, U k-steps per batch with the next batch's loads in flight.  The per-
-// element arithmetic is the tiled kernel's: acc = mfma(W fragment, row fragment, acc) over
-// k in steps of 32, ascending.
+// barriers: a workgroup is one wave and owns the 16 output columns n0 .. n0+15 for all
+// rows (so even the 4096 columns of a single projection spread over 256 workgroups), and
+// streams its weight fragments (and the rows' fragments, small and cached) straight into
+// registers, U k-steps per batch with the next batch's loads in flight.  The per-element
+// arithmetic is the tiled kernel's: acc = mfma(W fragment, row fragment, acc) over k in
+// steps of 32, ascending.
 template <int FM, int U>
-__global__ void __launch_bounds__(256) gemm_nt_bf16_skinny_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(64) gemm_nt_bf16_skinny_kernel(GemmArgs g) {
   const uint8_t* A = g.A + (int64_t)blockIdx.y * g.a_batch;
   const uint8_t* W = g.W + (int64_t)blockIdx.y * g.w_batch;
   uint8_t* C = g.C + (int64_t)blockIdx.y * g.c_batch;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
-  const int n0 = (blockIdx.x * 4 + wv) * 16;
+  const int n0 = blockIdx.x * 16;
   if (n0 >= g.N) return;
   const uint8_t* wrow = W + (int64_t)min(n0 + c16, g.N - 1) * g.ldw + g4 * 16;
   const uint8_t* arow[FM];
@@ -242,13 +243,13 @@ static hipError_t launch_gemm(const GemmArgs& g, int batch, hipStream_t stream) 
   } else if (g.M > 64) {
     launch_gemm_tiles<64, 64, 8>(g, batch, stream);
   } else {
-    const dim3 grid((unsigned)((g.N + 63) / 64), (unsigned)batch);
+    const dim3 grid((unsigned)((g.N + 15) / 16), (unsigned)batch);
     if (g.M > 32)
-      hipLaunchKernelGGL((gemm_nt_bf16_skinny_kernel<4, 8>), grid, dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_nt_bf16_skinny_kernel<4, 8>), grid, dim3(64), 0, stream, g);
     else if (g.M > 16)
-      hipLaunchKernelGGL((gemm_nt_bf16_skinny_kernel<2, 8>), grid, dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_nt_bf16_skinny_kernel<2, 8>), grid, dim3(64), 0, stream, g);
     else
-      hipLaunchKernelGGL((gemm_nt_bf16_skinny_kernel<1, 8>), grid, dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((gemm_nt_bf16_skinny_kernel<1, 8>), grid, dim3(64), 0, stream, g);
   }
   return hipGetLastError();
 }

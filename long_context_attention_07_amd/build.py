@@ -23,7 +23,7 @@ PROBE_LIB = os.path.join(PKG, "libcsa_probe.so")
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["abi.cpp", "compress.hip", "index.hip", "index_mfma.hip", "index_mx.hip", "topk.hip", "attend.hip",
-           "attend_mfma.hip", "attend_wave.hip", "outproj.hip"]
+           "attend_mfma.hip", "attend_shared.hip", "outproj.hip"]
 PROBE_SOURCES = ["probe.hip"]
 
 COMMON_FLAGS = [
@@ -40,7 +40,7 @@ COMMON_FLAGS = [
 # Per-source additions.  The wave kernel rescales its matrix-core accumulators with vector
 # instructions between products; with the accumulators in ordinary vector registers the
 # compiler keeps each in place across the loop instead of copying all of them per step.
-SOURCE_FLAGS = {"attend_wave.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"attend_shared.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():

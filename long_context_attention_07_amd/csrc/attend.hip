@@ -19,6 +19,8 @@
 // keys per tile, logits and P.V on the vector ALUs; bf16 rows of 512 dims go to the
 // matrix-core kernel (attend_mfma.hip).
 
+#include <algorithm>
+
 #include "attend_common.h"
 
 namespace csa {
@@ -186,7 +188,14 @@ int attend_chunk_slots(const AttendArgs& a) { return chunk_slots_for(a.csa, a.k,
 int64_t attend_max_chunks(const AttendArgs& a) {
   const int64_t n_ent = a.csa ? (int64_t)a.k : (int64_t)a.max_ctx / a.ratio;
   const int64_t C = attend_chunk_slots(a);
-  return (n_ent + a.n_win + C - 1) / C;
+  int64_t mc = (n_ent + a.n_win + C - 1) / C;
+  if (a.q.dim == kMfmaHeadDim) {
+    // the row format is not a host scalar of the workspace query: cover the chunking of
+    // the bf16-row kernel too
+    const int64_t C2 = attend_shared_chunk_slots(a.csa, a.k, a.n_win);
+    mc = std::max(mc, (n_ent + a.n_win + C2 - 1) / C2);
+  }
+  return mc;
 }
 
 // Whether a call cuts its key lists over several workgroups (the combine kernel then folds

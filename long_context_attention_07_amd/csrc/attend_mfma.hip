@@ -971,7 +971,7 @@ static void launch_attend_mfma_kernel(const AttendArgs& a, float* ws_o, float* w
     hipLaunchKernelGGL((attend_pair_kernel<SPLIT, true>), dim3((unsigned)n_phys), dim3(512), 0, stream, a, ws_o, ws_ml,
                        n_hg, mc, C, (int)n_log);
   else
-    launch_attend_wave(SPLIT, a, ws_o, ws_ml, n_hg, mc, C, n_log, stream);
+    launch_attend_shared(SPLIT, a, ws_o, ws_ml, n_hg, mc, C, n_log, stream);
 }
 
 // Which kernel a call uses depends on the operation's parameters only (the key list
@@ -990,8 +990,12 @@ hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hi
     hipLaunchKernelGGL((attend_long_kernel<true>), dim3((unsigned)n_phys), dim3(512), 0, stream, a, n_hg, (int)n_log);
     return hipGetLastError();
   }
-  const int n_hg = (a.n_h + kHG - 1) / kHG;
-  const int C = chunk_slots_for(a.csa, a.k, a.n_win);
+  // bf16 rows: the shared-stage kernel (32 heads per workgroup, its own chunking); fp8 rows:
+  // the pair kernel (16 heads per workgroup)
+  const bool shared = a.kv.dtype != DT_KV_SPLIT;
+  const int hpw = shared ? kSharedHeads : kHG;
+  const int n_hg = (a.n_h + hpw - 1) / hpw;
+  const int C = shared ? attend_shared_chunk_slots(a.csa, a.k, a.n_win) : chunk_slots_for(a.csa, a.k, a.n_win);
   const int64_t mc = attend_max_chunks(a);
   const size_t need = attend_workspace_bytes(a);
   const int64_t single = (int64_t)a.S.total_q * n_hg;
@@ -1005,15 +1009,13 @@ hipError_t launch_attend_mfma(const AttendArgs& a, void* ws, size_t ws_bytes, hi
     // dims per lane: the widest split that still gives every compute unit a workgroup
     // (which lanes fold which dims does not change the result)
     const int64_t wg8 = a.S.total_q * ((a.n_h + 3) / 4);
+    const dim3 g8((unsigned)wg8), g4((unsigned)(a.S.total_q * ((a.n_h + 1) / 2))), g2((unsigned)(a.S.total_q * a.n_h));
     if (wg8 >= kCombineWideWgs)
-      hipLaunchKernelGGL(attend_combine_mfma_kernel<8>, dim3((unsigned)wg8), dim3(256), 0, stream, a, ws_o, ws_ml,
-                         (int)mc);
+      hipLaunchKernelGGL(attend_combine_mfma_kernel<8>, g8, dim3(256), 0, stream, a, ws_o, ws_ml, (int)mc);
     else if (2 * wg8 >= kCombineWideWgs)
-      hipLaunchKernelGGL(attend_combine_mfma_kernel<4>, dim3((unsigned)(a.S.total_q * ((a.n_h + 1) / 2))), dim3(256),
-                         0, stream, a, ws_o, ws_ml, (int)mc);
+      hipLaunchKernelGGL(attend_combine_mfma_kernel<4>, g4, dim3(256), 0, stream, a, ws_o, ws_ml, (int)mc);
     else
-      hipLaunchKernelGGL(attend_combine_mfma_kernel<2>, dim3((unsigned)(a.S.total_q * a.n_h)), dim3(256), 0, stream,
-                         a, ws_o, ws_ml, (int)mc);
+      hipLaunchKernelGGL(attend_combine_mfma_kernel<2>, g2, dim3(256), 0, stream, a, ws_o, ws_ml, (int)mc);
   } else {
     launch_attend_mfma_kernel<false>(a, nullptr, nullptr, n_hg, 1, C, single, stream);
   }

@@ -269,9 +269,11 @@ __device__ __forceinline__ float scale_frame(float m) {
 typedef const __attribute__((address_space(1))) void* global_cvp;
 typedef __attribute__((address_space(3))) void* lds_vp;
 
-// Launch of the wave kernel (bf16 rows, chunked key lists): split = one workgroup per
-// (token, head group, chunk) writing chunk partials, else one per (token, head group).
-void launch_attend_wave(bool split, const AttendArgs& a, float* ws_o, float* ws_ml, int n_hg, int max_chunks,
-                        int chunk_slots, int64_t n_logical, hipStream_t stream);
+// Launch of the shared-stage kernel (bf16 rows, chunked key lists, 32 heads per
+// workgroup): split = one workgroup per (token, head group, chunk) writing chunk partials,
+// else one per (token, head group) walking its chunks.
+constexpr int kSharedHeads = 32;
+void launch_attend_shared(bool split, const AttendArgs& a, float* ws_o, float* ws_ml, int n_hg, int max_chunks,
+                          int chunk_slots, int64_t n_logical, hipStream_t stream);
 
 }  // namespace csa

@@ -49,6 +49,8 @@ struct AttendArgs {
 // Fixed chunk length (key slots) of a token's key list, per kernel family.  Changing it
 // changes rounding, never batch invariance.
 int attend_chunk_slots(const AttendArgs& a);
+// Chunk length of the shared-stage kernel (bf16 rows of 512 dims).
+int attend_shared_chunk_slots(int csa, int k, int n_win);
 // Number of chunks of the longest key list the launch can see (grid / workspace sizing).
 int64_t attend_max_chunks(const AttendArgs& a);
 constexpr int kMfmaHeadDim = 512;    // head dim of the matrix-core attention kernels

@@ -53,7 +53,7 @@ OP_KERNELS = {"compress": ["compress2_kernel", "compress_kernel"],
               "index_score": ["index_score_mfma_kernel", "index_score_mfma_units_kernel", "index_score_mx_kernel",
                               "index_score_mx_block_kernel"],
               "topk": ["topk_kernel", "topk_decode_kernel"],
-              "attend": ["attend_wave_kernel", "attend_pair_kernel", "attend_combine_mfma_kernel", "attend_long_kernel"]}
+              "attend": ["attend_shared_kernel", "attend_pair_kernel", "attend_combine_mfma_kernel", "attend_long_kernel"]}
 PREFILL_KERNELS = {"compress": ["compress2_kernel"], "index_score": ["index_score_mx_block_kernel"],
                    "topk": ["topk_kernel"], "attend": ["attend_long_kernel"]}
 CALIB_BYTES = 256 << 20  # plain device copy used to calibrate the HBM byte counters

@@ -37,9 +37,9 @@ COMMON_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-# Per-source additions.  The wave kernel rescales its matrix-core accumulators with vector
-# instructions between products; with the accumulators in ordinary vector registers the
-# compiler keeps each in place across the loop instead of copying all of them per step.
+# Per-source additions.  The shared-stage kernel rescales its matrix-core accumulators with
+# vector instructions between products; with the accumulators in ordinary vector registers
+# the compiler keeps each in place across the loop instead of copying all of them per step.
 SOURCE_FLAGS = {"attend_shared.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

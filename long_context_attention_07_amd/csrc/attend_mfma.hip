@@ -4,8 +4,8 @@
 // the 128-token window concatenated; list "其他注意力技术细节": partial RoPE on the last 64
 // dims, inverse RoPE of the output, learnable sink; section 3.4: fp8 KV with 1x128 scales).
 //
-// Two kernels for fp8 (KV split) rows; bf16 rows take the wave kernel (attend_wave.hip),
-// which has the pair kernel's arithmetic.  The templates below also take bf16 rows (KVF =
+// Two kernels for fp8 (KV split) rows; bf16 rows take the shared-stage kernel
+// (attend_shared.hip), which has the pair kernel's per-stage arithmetic.  The templates below also take bf16 rows (KVF =
 // false), which no launch uses.  The pair kernel (HCA, and CSA with k < 1024): workgroup =
 // (token, group of 16 query heads, chunk of the token's key list), 8 waves in 4 pairs.  The
 // long-list kernel (CSA with k >= 1024, whole lists): workgroup = (token, 64 heads), 8 waves,
@@ -976,7 +976,7 @@ static void launch_attend_mfma_kernel(const AttendArgs& a, float* ws_o, float* w
 
 // Which kernel a call uses depends on the operation's parameters only (the key list
 // length and the row format), never on the batch, so a token's bits do not depend on the
-// batch either: bf16 rows take the wave kernel at every k, fp8 rows the pair kernel below
+// batch either: bf16 rows take the shared-stage kernel at every k, fp8 rows the pair kernel below
 // k = 1024 and the 64-head kernel from there.
 static bool attend_long_lists(const AttendArgs& a) { return a.csa && a.k >= kLongKeys && a.kv.dtype == DT_KV_SPLIT; }
 

@@ -1,5 +1,5 @@
 // Pieces shared by the matrix-core attention kernels over rows of 512 dims (the pair,
-// long-list and wave kernels): tile geometry, bf16 / fp16 packing, the MFMA step, rotary
+// long-list and shared-stage kernels): tile geometry, bf16 / fp16 packing, the MFMA step, rotary
 // pieces of query and window rows, cross-row reductions and the split-launch record.
 #pragma once
 

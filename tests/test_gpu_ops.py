@@ -485,8 +485,8 @@ ATTEND_CASES = [
     (ops.BF16, 512, 16, True, 4, 100, 0),
     (ops.KV_SPLIT, 512, 64, True, 4, 256, 128),
     (ops.KV_SPLIT, 512, 64, False, 128, 0, 128),
-    # k >= 1024 (fp8 rows: the 64-head kernel over whole lists; bf16 rows: the wave kernel
-    # over 384-slot chunks): tokens with no visible entry (whole tiles absent), a
+    # k >= 1024 (fp8 rows: the 64-head kernel over whole lists; bf16 rows: the shared-stage
+    # kernel over four chunks): tokens with no visible entry (whole tiles absent), a
     # part-filled head group, a 64-token window
     (ops.BF16, 512, 64, True, 4, 2048, 128),
     (ops.KV_SPLIT, 512, 64, True, 4, 1024, 128),
@@ -582,7 +582,7 @@ def test_attend_fp8_rows_far_from_unit_scale(row_scale, k):
                                               (ops.KV_SPLIT, 1024, 0, 128), (ops.BF16, 1024, 64, 0),
                                               (ops.KV_SPLIT, 256, 32, 128)])
 def test_attend_rope_widths_and_no_window(fmt, k, rope, n_win):
-    """Rotary widths other than 64 (32 dims, none) for bf16 rows (the wave kernel) and fp8
+    """Rotary widths other than 64 (32 dims, none) for bf16 rows (the shared-stage kernel) and fp8
     rows with k >= 1024 (the 64-head kernel), and bf16 rows with k >= 1024 and no window."""
     log(f"attend rope={rope} fmt={fmt} k={k} n_win={n_win}")
     g = np.random.default_rng(71 + k + rope + n_win)

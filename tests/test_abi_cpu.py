@@ -122,7 +122,7 @@ def test_compress_and_index_validation_errors(lib):
 def test_workspace_sizes(lib):
     s = _seqs(n_seqs=4, total_q=4, max_q=1, max_ctx=1 << 20)
     P = ctypes.byref
-    assert lib.csa_workspace_bytes(ops.OP_INDEX_TOPK, P(s), 0, 0, 512, 4, 0) == 4 * (1 << 18) * 4 + 4 * 16 * 512 * 8
+    assert lib.csa_workspace_bytes(ops.OP_INDEX_TOPK, P(s), 0, 0, 512, 4, 0) == 4 * (1 << 18) * 4 + 4 * 8 * 512 * 8
     assert lib.csa_workspace_bytes(99, P(s), 64, 512, 0, 128, 128) == 0
     hca = lib.csa_workspace_bytes(ops.OP_HCA_ATTEND, P(s), 64, 512, 0, 128, 128)
     # 4 tokens x 29 chunks (8192 entries + 128 window slots: 288-slot chunks for bf16 rows,
@@ -181,15 +181,18 @@ def test_noalloc_validation_before_any_device_call(lib):
 
 def test_topk_workspace_sizes(lib):
     """The sliced selection's candidate lists: rows above 32768 candidates, slices of 16384
-    (or 32768 when k would overflow the merge), k (key, index) pairs of 8 bytes per slice;
-    none for rows that fit one workgroup's registers."""
+    while a row has at most 8 of them (or 32768 beyond, or when k would overflow the merge),
+    k (key, index) pairs of 8 bytes per slice; none for rows that fit one workgroup's
+    registers."""
     P = ctypes.byref
-    s = _seqs(n_seqs=32, total_q=32, max_q=1, max_ctx=1 << 20)
-    assert lib.csa_workspace_bytes(ops.OP_TOPK, P(s), 0, 0, 512, 4, 0) == 32 * 16 * 512 * 8
+    s = _seqs(n_seqs=32, total_q=32, max_q=1, max_ctx=1 << 20)  # 262144 candidates: 8 slices of 32768
+    assert lib.csa_workspace_bytes(ops.OP_TOPK, P(s), 0, 0, 512, 4, 0) == 32 * 8 * 512 * 8
     assert lib.csa_workspace_bytes(ops.OP_TOPK, P(s), 0, 0, 4096, 4, 0) == 32 * 8 * 4096 * 8
-    assert lib.csa_workspace_bytes(ops.OP_INDEX_TOPK, P(s), 0, 0, 512, 4, 0) == 32 * (1 << 18) * 4 + 32 * 16 * 512 * 8
+    assert lib.csa_workspace_bytes(ops.OP_INDEX_TOPK, P(s), 0, 0, 512, 4, 0) == 32 * (1 << 18) * 4 + 32 * 8 * 512 * 8
     c2 = _seqs(n_seqs=32, total_q=32, max_q=1, max_ctx=65536)
     assert lib.csa_workspace_bytes(ops.OP_TOPK, P(c2), 0, 0, 512, 4, 0) == 0
+    mid = _seqs(n_seqs=32, total_q=32, max_q=1, max_ctx=1 << 18)  # 65536 candidates: 4 slices of 16384
+    assert lib.csa_workspace_bytes(ops.OP_TOPK, P(mid), 0, 0, 512, 4, 0) == 32 * 4 * 512 * 8
     # 1M candidates per row with k = 4096 would need 32 slices of 32768: one workgroup instead
     big = _seqs(n_seqs=1, total_q=1, max_q=1, max_ctx=1 << 20)
     assert lib.csa_workspace_bytes(ops.OP_TOPK, P(big), 0, 0, 4096, 1, 0) == 0

@@ -279,16 +279,18 @@ def test_topk_exact_on_identical_scores(keep):
                 assert list(got[r]) == list(ref), f"token {r} (V={L}, k={k}, row stride {st.stride(0)})"
 
 
+@pytest.mark.parametrize("longest", [262144, 131072])
 @pytest.mark.parametrize("k", [1, 512, 1024, 4096])
-def test_topk_sliced_rows_exact(k):
+def test_topk_sliced_rows_exact(k, longest):
     """Rows longer than 32768 candidates on several workgroups (slices, then a merge):
     exact against the oracle's selection on the same float32 scores, with heavy ties, a row
     whose every score ties, the k largest all in one slice, +-0, a row with a ragged last
     slice shorter than k, and rows that fit one slice next to them; the one-workgroup
-    path (no workspace) gives the same indices."""
+    path (no workspace) gives the same indices.  A longest row of 262144 candidates cuts
+    every row in slices of 32768, one of 131072 in slices of 16384."""
     g = np.random.default_rng(31 + k)
     ratio = 1
-    ctx = [262144, 40000, 32769, 98304 + 7, 65536 + k // 2, 20000, 3000]
+    ctx = [longest, 40000, 32769, 98304 + 7, 65536 + k // 2, 20000, 3000]
     ob, sq, _, _ = make_batch([1] * len(ctx), ctx, ratio)
     stride = max(ctx) + 3
     s = np.full((len(ctx), stride), np.nan, dtype=np.float32)

@@ -333,9 +333,13 @@ __device__ __forceinline__ BlockIds load_block_ids(const SeqsDev& S, int b, int6
 __device__ __forceinline__ int64_t pool_row(const SeqsDev& S, const BlockIds& B, int b, int64_t entry0, int64_t e) {
   if (!S.block_table) return entry0 + e;
   const int64_t rel = (e >> S.be_shift) - B.first;
-  const int32_t near = __shfl(B.id, (int)(rel < 63 ? (rel < 0 ? 0 : rel) : 63), 64);
-  const int64_t blk = (rel >= 0 && rel < 64) ? near : S.block_table[(int64_t)b * S.bt_stride + (e >> S.be_shift)];
-  return (blk << S.be_shift) | (e & ((int64_t(1) << S.be_shift) - 1));
+  int32_t blk = __shfl(B.id, (int)(rel < 63 ? (rel < 0 ? 0 : rel) : 63), 64);
+  if (rel < 0 || rel >= 64) {
+    blk = S.block_table[(int64_t)b * S.bt_stride + (e >> S.be_shift)];
+    // take the value inside the branch, so that the common path never waits on this load
+    asm volatile("" : "+v"(blk));
+  }
+  return ((int64_t)blk << S.be_shift) | (e & ((int64_t(1) << S.be_shift) - 1));
 }
 
 // pool_row for a wave whose lanes usually read rows of one block (consecutive entries of a

@@ -33,6 +33,15 @@ typedef __attribute__((address_space(1))) void* gbl_void_ptr;
 constexpr int kIT = 64;            // entries per tile
 constexpr int kIRow = 256;         // bytes per key row (128 bf16)
 
+// Barrier for LDS data only: the waits for direct-to-LDS loads are explicit (a full
+// __syncthreads would also drain every load still in flight).
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Wait until this wave's direct-to-LDS loads of a tile have landed: n later tiles (4
 // instructions each) may still be in flight.  Counting is conservative: stores issued
 // after those loads only make the wait longer.
@@ -44,9 +53,14 @@ __device__ __forceinline__ void wait_tiles_in_flight(int n) {
 }
 
 // Entries [part * 64 TILES, (part + 1) * 64 TILES) of token t (position ctx.p, pool row of
-// entry 0 ctx.entry0), by the whole workgroup.
-template <int RING, int TILES>
-__device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], const SeqsDev& S, int t,
+// entry 0 ctx.entry0), by the whole workgroup.  PAGED: the pool is addressed through the
+// block table (a separate instantiation, so that the contiguous case carries no block-id
+// load for the compiler to wait on).  The head weights sit in the 256 bytes after the
+// ring; both are one shared array, which keeps the compiler from draining the loads in
+// flight before each read of a tile.
+template <int RING, int TILES, bool PAGED>
+__device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], float (&wsh)[64], const SeqsDev& S,
+                                            int t,
                                             const TokenCtx& ctx, int part,
                                             const RowsDev& qI, const float* __restrict__ w, int n_I,
                                             const RowsDev& kI, int ratio, ScoreOut score) {
@@ -59,22 +73,6 @@ __device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], 
 
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, c16 = lane & 15;
-  const BlockIds bids = load_block_ids(S, ctx.b, e_begin);
-
-  // tile i -> ring slot i % RING; wave wv moves rows 16wv .. 16wv+15 (4 rows per instruction)
-  auto issue = [&](int i) {
-    const int64_t e_tile = e_begin + (int64_t)i * kIT;
-    uint8_t* slot = ring[i % RING];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 16 * wv + 4 * q + (lane >> 4);
-      int64_t e = e_tile + r;
-      if (e >= V) e = V - 1;  // rows past the end re-read a valid row; their scores are not written
-      const int chunk = (lane & 15) ^ (r & 15);
-      const uint8_t* src = kI.data + pool_row_wave(S, bids, ctx.b, ctx.entry0, e) * kI.stride + chunk * 16;
-      __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)(slot + (16 * wv + 4 * q) * kIRow), 16, 0, 0);
-    }
-  };
 
   // The token's indexer queries (n_I rows of 256 B, the A operand) are staged once per
   // workgroup in the last ring slot, which no key tile uses before the loop starts: one
@@ -97,21 +95,52 @@ __device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], 
       __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)(qslot + r0 * kIRow), 16, 0, 0);
     }
   }
+  // The head weights go the same way (wave 0, one dword per lane), so that no register
+  // waits on a global load once the tiles are in flight.
+  if (wv == 0) {
+    const float* src = w + (int64_t)t * n_I + min(lane, n_I - 1);
+    __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)wsh, 4, 0, 0);
+  }
+  // paged pools: every tile's addresses need the block ids; wait for them once, here
+  BlockIds bids;
+  bids.id = 0;
+  bids.first = 0;
+  if constexpr (PAGED) {
+    bids = load_block_ids(S, ctx.b, e_begin);
+    asm volatile("" ::"v"(bids.id));
+  }
+
+  // tile i -> ring slot i % RING; wave wv moves rows 16wv .. 16wv+15 (4 rows per instruction)
+  auto issue = [&](int i) {
+    const int64_t e_tile = e_begin + (int64_t)i * kIT;
+    uint8_t* slot = ring[i % RING];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * wv + 4 * q + (lane >> 4);
+      int64_t e = e_tile + r;
+      if (e >= V) e = V - 1;  // rows past the end re-read a valid row; their scores are not written
+      const int chunk = (lane & 15) ^ (r & 15);
+      const int64_t row = PAGED ? pool_row_wave(S, bids, ctx.b, ctx.entry0, e) : ctx.entry0 + e;
+      const uint8_t* src = kI.data + row * kI.stride + chunk * 16;
+      __builtin_amdgcn_global_load_lds((gbl_void_ptr)src, (lds_void_ptr)(slot + (16 * wv + 4 * q) * kIRow), 16, 0, 0);
+    }
+  };
+
+  const int prologue = min(n_tiles, RING - 1);
+  for (int i = 0; i < prologue; ++i) issue(i);
+
+  // queries and weights landed (only the prologue tiles may still be in flight), visible
+  // to all waves
+  wait_tiles_in_flight(prologue);
+  ring_barrier();
   float wh[4][4];
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int hr = 4 * g + j + 16 * hb;
-      wh[hb][j] = hr < n_I ? w[(int64_t)t * n_I + hr] : 0.f;
+      wh[hb][j] = hr < n_I ? wsh[hr] : 0.f;
     }
-
-  const int prologue = min(n_tiles, RING - 1);
-  for (int i = 0; i < prologue; ++i) issue(i);
-
-  // queries landed (only the prologue tiles may still be in flight), visible to all waves
-  wait_tiles_in_flight(prologue);
-  __syncthreads();
   // A operand: heads c16 + 16 hb, dims 8g + 32 kk .. +7
   ibf16x8_t qa[4][4];
 #pragma unroll
@@ -126,7 +155,7 @@ __device__ __forceinline__ void score_range(uint8_t (&ring)[RING][kIT * kIRow], 
   for (int i = 0; i < n_tiles; ++i) {
     const int issued_after = min(n_tiles - 1, i + RING - 2) - i;
     wait_tiles_in_flight(issued_after);
-    __syncthreads();  // tile i visible to all waves; slot (i-1) % RING free
+    ring_barrier();  // tile i visible to all waves; slot (i-1) % RING free
     if (i + RING - 1 < n_tiles) issue(i + RING - 1);
 
     const uint8_t* rowp = ring[i % RING] + (16 * wv + c16) * kIRow;
@@ -165,13 +194,16 @@ template <int RING, int TILES>
 __global__ void __launch_bounds__(256) index_score_mfma_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
                                                                int n_I, RowsDev kI, int ratio,
                                                                ScoreOut score, int n_parts, int n_logical) {
-  __shared__ __align__(16) uint8_t ring[RING][kIT * kIRow];
+  __shared__ __align__(16) uint8_t lds[RING * kIT * kIRow + 256];
+  auto& ring = *reinterpret_cast<uint8_t(*)[RING][kIT * kIRow]>(lds);
+  auto& wsh = *reinterpret_cast<float(*)[64]>(lds + RING * kIT * kIRow);
   const int lid = blockIdx.x;
   if (lid >= n_logical) return;
   const int t = lid / n_parts;
   const int part = lid % n_parts;
   const TokenCtx ctx = token_ctx(S, t);
-  score_range<RING, TILES>(ring, S, t, ctx, lid % n_parts, qI, w, n_I, kI, ratio, score);
+  if (S.block_table) score_range<RING, TILES, true>(ring, wsh, S, t, ctx, part, qI, w, n_I, kI, ratio, score);
+  else score_range<RING, TILES, false>(ring, wsh, S, t, ctx, part, qI, w, n_I, kI, ratio, score);
 }
 
 // Few sequences and query rows (decode): the (token, range) units with entries to score
@@ -195,7 +227,9 @@ template <int RING, int TILES>
 __global__ void __launch_bounds__(256) index_score_mfma_units_kernel(SeqsDev S, RowsDev qI,
                                                                      const float* __restrict__ w, int n_I,
                                                                      RowsDev kI, int ratio, ScoreOut score) {
-  __shared__ __align__(16) uint8_t ring[RING][kIT * kIRow];
+  __shared__ __align__(16) uint8_t lds[RING * kIT * kIRow + 256];
+  auto& ring = *reinterpret_cast<uint8_t(*)[RING][kIT * kIRow]>(lds);
+  auto& wsh = *reinterpret_cast<float(*)[64]>(lds + RING * kIT * kIRow);
   constexpr int64_t kPer = (int64_t)kIT * TILES;
   const int lane = threadIdx.x & 63;
   const bool in = lane < S.n_seqs;
@@ -233,7 +267,8 @@ __global__ void __launch_bounds__(256) index_score_mfma_units_kernel(SeqsDev S, 
     ctx.entry0 = readlane64(e0, b);
     ctx.tok0 = 0;
     ctx.tok_lo = 0;
-    score_range<RING, TILES>(ring, S, bq0 + j, ctx, rem, qI, w, n_I, kI, ratio, score);
+    if (S.block_table) score_range<RING, TILES, true>(ring, wsh, S, bq0 + j, ctx, rem, qI, w, n_I, kI, ratio, score);
+    else score_range<RING, TILES, false>(ring, wsh, S, bq0 + j, ctx, rem, qI, w, n_I, kI, ratio, score);
   }
 }
 

@@ -40,7 +40,10 @@ COMMON_FLAGS = [
 # Per-source additions.  The shared-stage kernel rescales its matrix-core accumulators with
 # vector instructions between products; with the accumulators in ordinary vector registers
 # the compiler keeps each in place across the loop instead of copying all of them per step.
-SOURCE_FLAGS = {"attend_shared.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# The decode scaled-product indexer reads every accumulator element per block; in vector
+# registers that needs no copy out of the accumulation registers first.
+SOURCE_FLAGS = {"attend_shared.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "index_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():

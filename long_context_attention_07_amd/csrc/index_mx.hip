@@ -30,6 +30,8 @@
 // (g2 + g3); so its bits do not depend on the kernel or on which other queries share the
 // workgroup.
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -108,8 +110,9 @@ __device__ __forceinline__ float head_sum(const mx_v4f (&acc)[4], const float (&
   return (t[0] + t[1]) + (t[2] + t[3]);
 }
 
-template <int QB, bool F8>
-__global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
+// Four waves per SIMD where the registers allow it without spills (the contiguous case).
+template <int QB, bool F8, bool PAGED>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PAGED ? 3 : 4, 8))) index_score_mx_kernel(SeqsDev S, RowsDev qI, const float* __restrict__ w,
                                                              int n_I, RowsDev kI, int ratio, ScoreOut score,
                                                              int n_parts, int range) {
   const int rb = blockIdx.x / n_parts, part = blockIdx.x % n_parts;
@@ -150,20 +153,38 @@ __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev 
             if (F8 && on) wv_ *= reinterpret_cast<const float*>(qI.scales)[row];
             wr[i][hb][j] = wv_;
           }
-      const int64_t e_stop = min(e_begin + (int64_t)range, v_max);
-      const BlockIds bids = load_block_ids(S, ctx.b, e_begin);
-      // wave wv takes the 16-entry blocks e_begin + 16 (wv + 4 it); 4 blocks in flight
-      for (int64_t e0 = e_begin + 16 * wv; e0 < e_stop; e0 += 4 * 64) {
-        MxOperand<F8> kb[4];
+      // Entry numbers within a sequence fit in 32 bits (positions are int32); the pool row
+      // is formed in 64 bits.  PAGED (block-table pools) is a separate instantiation, so
+      // the contiguous case carries no block-id load for the compiler to wait on.
+      const int e_stop = (int)min(e_begin + (int64_t)range, v_max);
+      const int v_last = (int)v_max - 1;
+      int v_row[QB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          int64_t e = e0 + 64 * u + c16;
-          if (e >= v_max) e = v_max - 1;  // past the run's last visible entry: a valid row, not written
-          kb[u] = load_operand<F8>(kI, pool_row_wave(S, bids, ctx.b, ctx.entry0, e), g);
+      for (int i = 0; i < QB; ++i) v_row[i] = (int)((ctx.p + i + 1) / ratio);
+      BlockIds bids;
+      bids.id = 0;
+      bids.first = 0;
+      if constexpr (PAGED) {
+        bids = load_block_ids(S, ctx.b, e_begin);
+        asm volatile("" ::"v"(bids.id));
+      }
+      // Wave wv takes the 16-entry blocks e_begin + 16 wv + 64 k.  Stages of NB blocks
+      // alternate between two register sets: the next stage's loads are issued before the
+      // current stage is scored (an unrolled pair, so no register copy waits on a load).
+      // Blocks past the range load the run's last visible row and score nothing.
+      constexpr int NB = F8 ? 2 : 4;
+      auto load_stage = [&](MxOperand<F8>(&k)[NB], int e0) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int e = min(e0 + 64 * u + c16, v_last);
+          const int64_t row = PAGED ? pool_row_wave(S, bids, ctx.b, ctx.entry0, e) : ctx.entry0 + e;
+          k[u] = load_operand<F8>(kI, row, g);
         }
+      };
+      auto score_stage = [&](const MxOperand<F8>(&k)[NB], int e0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t eb = e0 + 64 * u;
+        for (int u = 0; u < NB; ++u) {
+          const int eb = e0 + 64 * u;
           if (eb >= e_stop) break;
 #pragma unroll
           for (int i = 0; i < QB; ++i) {
@@ -171,15 +192,40 @@ __global__ void __launch_bounds__(256) index_score_mx_kernel(SeqsDev S, RowsDev 
             mx_v4f acc[4];
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb)  // acc[hb][j] = qI[head 4g+j+16hb] . kI[entry eb + c16]
-              acc[hb] = mx_dot<F8>(qa[i][hb], kb[u]);
+              acc[hb] = mx_dot<F8>(qa[i][hb], k[u]);
             float s = head_sum(acc, wr[i]);
-            s += __shfl_xor(s, 16, 64);
-            s += __shfl_xor(s, 32, 64);
-            if (F8) s *= kb[u].sc;
-            const int64_t e = eb + c16;
-            const int64_t v_i = (ctx.p + i + 1) / ratio;
-            if (g == 0 && e < v_i && e < e_stop) score_row(score, t0 + i).store(e, s);
+            // (g0 + g1) + (g2 + g3) across the lane groups by the row-swap permutes
+            {
+              auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+              s = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+              auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+              s = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+            }
+            if (F8) {
+              // in every lane: kept out of the store's branch, the row scale's load would be
+              // issued there and waited for on its own
+              s *= k[u].sc;
+              asm volatile("" : "+v"(s));
+            }
+            const int e = eb + c16;
+            if (g == 0 && e < v_row[i] && e < e_stop) score_row(score, t0 + i).store(e, s);
           }
+        }
+      };
+      int e0 = (int)e_begin + 16 * wv;
+      if (e0 < e_stop) {
+        MxOperand<F8> ka[NB], kb[NB];
+        load_stage(ka, e0);
+        for (;;) {
+          const int e1 = e0 + 64 * NB;
+          load_stage(kb, e1);
+          score_stage(ka, e0);
+          if (e1 >= e_stop) break;
+          const int e2 = e1 + 64 * NB;
+          load_stage(ka, e2);
+          score_stage(kb, e1);
+          if (e2 >= e_stop) break;
+          e0 = e2;
         }
       }
     }
@@ -313,13 +359,20 @@ static void launch_mx(const SeqsDev& S, const RowsDev& qI, const float* w, int n
     // entries per workgroup: kMxRange, or more when the launch would otherwise hold many
     // more workgroups than the chip runs at once (each has a prologue of its own: context,
     // query operands, weights); a score's bits do not depend on the split
+    // Paged pools: a workgroup's block ids are one wave-wide load (64 blocks), so its range
+    // stays within 64 blocks where the block size allows it.
     const int64_t total = (int64_t)S.total_q * max_vis;
+    const int range_max = S.block_table ? std::max(kMxRange, std::min(kMxRangeMax, 64 << S.be_shift)) : kMxRangeMax;
     int range = kMxRange;
-    while (range < kMxRangeMax && total / range > kMxTargetWgs) range *= 2;
+    while (range < range_max && total / range > kMxTargetWgs) range *= 2;
     const int n_parts = (max_vis + range - 1) / range;
     const int64_t blocks = (int64_t)S.total_q * n_parts;
-    hipLaunchKernelGGL((index_score_mx_kernel<1, F8>), dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w, n_I,
-                       kI, ratio, score, n_parts, range);
+    if (S.block_table)
+      hipLaunchKernelGGL((index_score_mx_kernel<1, F8, true>), dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w,
+                         n_I, kI, ratio, score, n_parts, range);
+    else
+      hipLaunchKernelGGL((index_score_mx_kernel<1, F8, false>), dim3((unsigned)blocks), dim3(256), 0, stream, S, qI, w,
+                         n_I, kI, ratio, score, n_parts, range);
   }
 }
 

@@ -184,16 +184,30 @@ attend_shared_kernel(AttendArgs a, float* __restrict__ ws_o, float* __restrict__
   // ids need no context lookup): thread tid holds slots s_lo + tid + 256 j
   constexpr int kIdsPerThread = (kMaxChunkSlots + 255) / 256;
   int32_t ids[kIdsPerThread];
+  // (issued unconditionally, clamped into the token's list, and not looked at before the
+  // slot table is built: the ids, the RoPE table and the token context are then requested
+  // together, one round trip, instead of one after another; slots past the chunk or the
+  // list never read their id)
+  // (HCA reads a word of the sequence table instead: its slots take no ids)
   auto load_ids = [&]() {
+    const int32_t* src = a.csa ? a.idx + (int64_t)t * a.k : a.S.q_off;
+    const int64_t last = a.csa ? (int64_t)a.k - 1 : 0;
 #pragma unroll
-    for (int j = 0; j < kIdsPerThread; ++j) {
-      const int64_t s = s_lo + tid + 256 * j;
-      ids[j] = (a.csa && s < min(s_lo + chunk_slots, (int64_t)a.k)) ? a.idx[(int64_t)t * a.k + s] : -1;
-    }
+    for (int j = 0; j < kIdsPerThread; ++j) ids[j] = src[min(s_lo + tid + 256 * j, last)];
   };
   load_ids();
-  load_freqs(F, a.rope);
+  static_assert(kMaxRopePairs <= 256, "one RoPE pair per thread");
+  const bool f_on = tid < a.rope.dims / 2;
+  double f_rad = 0.0, f_rev = 0.0;
+  if (f_on) {
+    f_rad = a.rope.inv_freq[tid];
+    f_rev = a.rope.inv_freq_rev[tid];
+  }
   const TokenCtx ctx = token_ctx(a.S, t);
+  if (f_on) {
+    F.rad[tid] = f_rad;
+    F.rev[tid] = f_rev;
+  }
   const int64_t n_ent = entry_slots(a, ctx);
   const int64_t n_slots = n_ent + a.n_win;
   const int n_chunks = (int)((n_slots + chunk_slots - 1) / chunk_slots);
@@ -214,6 +228,23 @@ attend_shared_kernel(AttendArgs a, float* __restrict__ ws_o, float* __restrict__
   auto build_table = [&]() {
     const int64_t c_len = min((int64_t)chunk_slots, n_slots - s_lo);
     const int64_t n_tab = (c_len + 15) / 16 * 16;
+    // paged pools: the block ids of all the thread's entry slots are requested before any
+    // is used (one round trip, not one per slot)
+    int64_t erow[kIdsPerThread];
+#pragma unroll
+    for (int j = 0; j < kIdsPerThread; ++j) {
+      const int64_t i = tid + 256 * j;
+      erow[j] = ctx.entry0 + (a.csa ? (int64_t)ids[j] : s_lo + i);
+    }
+    if (a.S.block_table) {
+#pragma unroll
+      for (int j = 0; j < kIdsPerThread; ++j) {
+        const int64_t i = tid + 256 * j;
+        const int64_t e = a.csa ? (int64_t)ids[j] : s_lo + i;
+        const bool ent = i < c_len && s_lo + i < n_ent && e >= 0;  // else block 0 of the sequence
+        erow[j] = a.S.block_table[(int64_t)ctx.b * a.S.bt_stride + (ent ? (e >> a.S.be_shift) : 0)];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kIdsPerThread; ++j) {
       const int64_t i = tid + 256 * j;
@@ -223,9 +254,10 @@ attend_shared_kernel(AttendArgs a, float* __restrict__ ws_o, float* __restrict__
         if (i < c_len) {
           if (s < n_ent) {
             const int64_t e = a.csa ? (int64_t)ids[j] : s;
+            const int64_t row =
+                a.S.block_table ? (erow[j] << a.S.be_shift) | (e & ((int64_t(1) << a.S.be_shift) - 1)) : erow[j];
             if (e >= 0)
-              v = (reinterpret_cast<uint64_t>(a.kv.data) +
-                   (uint64_t)(entry_row(a.S, ctx.b, ctx.entry0, e) * a.kv.stride)) | 1u;
+              v = (reinterpret_cast<uint64_t>(a.kv.data) + (uint64_t)(row * a.kv.stride)) | 1u;
           } else {
             const int64_t pos = ctx.p - a.n_win + 1 + (s - n_ent);
             if (pos >= 0 && pos >= ctx.tok_lo)

@@ -176,43 +176,63 @@ struct TopkRegLds {
   uint32_t hist0[4096];  // first digit (12 bits)
   uint32_t hist1[4096];  // second digit (12 bits)
   uint32_t hist2[256];   // last digit (8 bits)
-  uint32_t red[2][16];
-  uint32_t digit, above, count;
+  uint32_t red[5][16];   // wave totals: one set per digit pass, two for the final counts
 };
 
+// The three histograms cleared; a barrier must follow before they are counted into.
+__device__ __forceinline__ void topk_clear_hists(TopkRegLds& sh) {
+  const int tid = threadIdx.x;
+  for (int b = tid; b < 4096; b += kTopkThreads) {
+    sh.hist0[b] = 0u;
+    sh.hist1[b] = 0u;
+  }
+  if (tid < 256) sh.hist2[tid] = 0u;
+}
+
 // Find the digit holding the `remaining`-th largest key of a histogram of `nbins` digits
-// (4096 or 256): thread t owns nbins / 1024 (at least 1) consecutive digits counted from the
-// top; a wave scan plus the 16 wave totals give each thread the count above its digits.
-// Returns (digit, keys above it, keys in it) to every thread.
-__device__ __forceinline__ uint3 topk_find_digit(const uint32_t* hist, int nbins, uint32_t remaining,
-                                                 TopkRegLds& sh) {
+// (4096 or 256; its total is at least `remaining`): thread t owns nbins / 1024 (at least 1)
+// consecutive digits counted from the top.  Each wave publishes its total (`red`, one
+// barrier); then every wave finds the target on its own, alike: the wave range from the 16
+// totals, the thread within it from a scan of that wave's digit sums, the digit within the
+// thread's digits.  Returns (digit, keys above it, keys in it) to every thread; no barrier
+// follows, so `red` must not be written again before the next barrier.
+__device__ __forceinline__ uint3 topk_find_digit(const uint32_t* hist, int nbins, uint32_t remaining, uint32_t* red) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int per = nbins >= kTopkThreads ? nbins / kTopkThreads : 1;
   const int owners = nbins / per;
-  const int d_hi = nbins - tid * per;
-  uint32_t loc = 0;
-  if (tid < owners)
-    for (int d = 0; d < per; ++d) loc += hist[d_hi - 1 - d];
-  const uint32_t incl = wave_incl_scan(loc);
-  if (lane == 63) sh.red[0][wv] = incl;
-  __syncthreads();
-  // keys in the waves before this one: lane i < wv reads wave i's total, one scan sums them
-  const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(lane < wv ? sh.red[0][lane] : 0u), 63);
-  uint32_t ab = base + incl - loc;
-  if (tid < owners && ab < remaining && ab + loc >= remaining) {
-    for (int d = 0; d < per; ++d) {
-      const uint32_t h = hist[d_hi - 1 - d];
-      if (ab + h >= remaining) {
-        sh.digit = (uint32_t)(d_hi - 1 - d);
-        sh.above = ab;
-        sh.count = h;
-        break;
-      }
-      ab += h;
+  auto digits_of = [&](int th) -> uint32_t {
+    uint32_t sum = 0;
+    if (th < owners) {
+      const int d_hi = nbins - th * per;
+      for (int d = 0; d < per; ++d) sum += hist[d_hi - 1 - d];
     }
-  }
+    return sum;
+  };
+  const uint32_t incl = wave_incl_scan(digits_of(tid));
+  if (lane == 63) red[wv] = incl;
   __syncthreads();
-  return make_uint3(sh.digit, sh.above, sh.count);
+  const uint32_t wt = lane < kTopkThreads / 64 ? red[lane] : 0u;
+  const uint32_t wincl = wave_incl_scan(wt);
+  const uint64_t wh = __ballot(lane < kTopkThreads / 64 && wincl >= remaining);
+  const int ws = wh ? __builtin_ctzll(wh) : kTopkThreads / 64 - 1;
+  const uint32_t above_w = (uint32_t)__builtin_amdgcn_readlane((int)(wincl - wt), ws);
+  const uint32_t l2 = digits_of(64 * ws + lane);
+  const uint32_t i2 = wave_incl_scan(l2);
+  const uint64_t th_hit = __ballot(above_w + i2 >= remaining);
+  const int ls = th_hit ? __builtin_ctzll(th_hit) : 63;
+  uint32_t ab = above_w + (uint32_t)__builtin_amdgcn_readlane((int)(i2 - l2), ls);
+  const int d_hi = nbins - (64 * ws + ls) * per;
+  uint32_t digit = (uint32_t)(d_hi - 1), cnt = 0u;
+  for (int d = 0; d < per; ++d) {
+    const uint32_t h = hist[d_hi - 1 - d];
+    if (ab + h >= remaining) {
+      digit = (uint32_t)(d_hi - 1 - d);
+      cnt = h;
+      break;
+    }
+    ab += h;
+  }
+  return make_uint3(digit, ab, cnt);
 }
 
 // Selection with the keys held in registers: thread tid holds the NPT consecutive keys
@@ -253,16 +273,13 @@ __device__ __forceinline__ void topk_load_keys(const ST* __restrict__ src, int l
 // LOWC: the keys come from bf16 scores, so their low 16 bits are fixed by the sign (0 for
 // keys of scores >= 0, all ones below): keys that agree in their top 24 bits are equal,
 // and the last digit pass is skipped.
-template <int NPT, bool LOWC, class Emit>
+// CLEARED: the caller has cleared the histograms (topk_clear_hists) already.
+template <int NPT, bool LOWC, bool CLEARED = false, class Emit>
 __device__ __forceinline__ void topk_select_keys_emit(const uint32_t (&key)[NPT], int n, int k, TopkRegLds& sh,
                                                       Emit emit) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int i0 = NPT * tid;
-  for (int b = tid; b < 4096; b += kTopkThreads) {
-    sh.hist0[b] = 0u;
-    sh.hist1[b] = 0u;
-  }
-  if (tid < 256) sh.hist2[tid] = 0u;
+  if (!CLEARED) topk_clear_hists(sh);
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < NPT; ++j)
@@ -274,7 +291,7 @@ __device__ __forceinline__ void topk_select_keys_emit(const uint32_t (&key)[NPT]
   // skipped (same set).
   uint32_t remaining = (uint32_t)k;
   uint32_t T;
-  uint3 r = topk_find_digit(sh.hist0, 4096, remaining, sh);
+  uint3 r = topk_find_digit(sh.hist0, 4096, remaining, sh.red[0]);
   const uint32_t d0 = r.x;
   remaining -= r.y;
   if (r.z == remaining && d0 != 0u) {
@@ -285,7 +302,7 @@ __device__ __forceinline__ void topk_select_keys_emit(const uint32_t (&key)[NPT]
     for (int j = 0; j < NPT; ++j)
       if (i0 + j < n && (key[j] >> 20) == d0) atomicAdd(&sh.hist1[(key[j] >> 8) & 0xfffu], 1u);
     __syncthreads();
-    r = topk_find_digit(sh.hist1, 4096, remaining, sh);
+    r = topk_find_digit(sh.hist1, 4096, remaining, sh.red[1]);
     const uint32_t p1 = (d0 << 12) | r.x;  // top 24 bits
     remaining -= r.y;
     if (r.z == remaining && p1 != 0u) {
@@ -298,7 +315,7 @@ __device__ __forceinline__ void topk_select_keys_emit(const uint32_t (&key)[NPT]
       for (int j = 0; j < NPT; ++j)
         if (i0 + j < n && (key[j] >> 8) == p1) atomicAdd(&sh.hist2[key[j] & 0xffu], 1u);
       __syncthreads();
-      r = topk_find_digit(sh.hist2, 256, remaining, sh);
+      r = topk_find_digit(sh.hist2, 256, remaining, sh.red[2]);
       T = (p1 << 8) | r.x;  // the k-th largest key
       remaining -= r.y;     // keys == T still to take, lowest index first
     }
@@ -313,12 +330,12 @@ __device__ __forceinline__ void topk_select_keys_emit(const uint32_t (&key)[NPT]
   }
   const uint32_t ig = wave_incl_scan(gt), ie = wave_incl_scan(eq);
   if (lane == 63) {
-    sh.red[0][wv] = ig;
-    sh.red[1][wv] = ie;
+    sh.red[3][wv] = ig;
+    sh.red[4][wv] = ie;
   }
   __syncthreads();
-  const uint32_t bg = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(lane < wv ? sh.red[0][lane] : 0u), 63);
-  const uint32_t be = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(lane < wv ? sh.red[1][lane] : 0u), 63);
+  const uint32_t bg = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(lane < wv ? sh.red[3][lane] : 0u), 63);
+  const uint32_t be = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(lane < wv ? sh.red[4][lane] : 0u), 63);
   uint32_t eq_rank = be + ie - eq;
   uint32_t pos = bg + ig - gt + min(eq_rank, remaining);
 #pragma unroll
@@ -383,6 +400,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_decode_kernel(SeqsDev S, co
   const ST* src = score + (int64_t)t * score_stride;
   uint32_t key[NPT];
   topk_load_keys<NPT>(src, (int)min(score_stride, (int64_t)NPT * kTopkThreads), key);
+  topk_clear_hists(rsh);  // while the keys and the context are in flight
   const TokenCtx ctx = token_ctx(S, t);
   const int64_t V = (ctx.p + 1) / ratio;
   int32_t* out = idx + (int64_t)t * k;
@@ -394,7 +412,9 @@ __global__ void __launch_bounds__(kTopkThreads) topk_decode_kernel(SeqsDev S, co
     topk_select_mem(src, (int)V, k, out, sh);
     return;
   }
-  topk_select_keys<NPT, sizeof(ST) == 2>(key, (int)V, k, out, rsh);
+  const int i0 = NPT * (int)threadIdx.x;
+  topk_select_keys_emit<NPT, sizeof(ST) == 2, true>(key, (int)V, k, rsh,
+                                                   [&](uint32_t pos, int j, uint32_t) { out[pos] = i0 + j; });
 }
 
 // ---------------------------------------------------------------------------------------

@@ -97,12 +97,20 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
   const int b = blk / max_new;
   const int jn = blk % max_new;
   if (b >= S.n_seqs) return;
-  const int n_b = S.q_off[b + 1] - S.q_off[b];
+  // the sequence's fields, requested together (one round trip, not one per use)
+  const int q_0 = S.q_off[b], q_1 = S.q_off[b + 1];
   const int64_t L = S.ctx_len[b];
+  const int64_t tok_lo = S.tok_lo[b];
+  const int64_t tok0 = S.tok_off[b];
+  const int64_t e_off = S.entry_off ? S.entry_off[b] : 0;
+  asm volatile("" ::"s"(q_0), "s"(q_1), "s"(L), "s"(tok_lo), "s"(tok0), "s"(e_off));  // (not sunk past the exits)
+  const int n_b = q_1 - q_0;
   const int64_t i_lo = (L - n_b) / ratio;
   const int64_t i_hi = L / ratio;
   const int64_t i = i_lo + jn;
   if (i >= i_hi) return;
+  // the output row (paged pools: a block-table load, in flight during the pooling)
+  const int64_t orow = entry_row(S, b, e_off, i);
 
   const int D = c.dim;
   if (2 * CW * cg >= D) return;
@@ -112,8 +120,6 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
   const bool active = 2 * pair < D;
   const int64_t lo = (i - overlap) * ratio;
   const int64_t hi = (i + 1) * ratio;
-  const int64_t tok_lo = S.tok_lo[b];
-  const int64_t tok0 = S.tok_off[b];
 
   __shared__ double s_freq[kMaxRopePairs];
   __shared__ PoolState s_part[RG > 1 ? RG - 1 : 1][CW];
@@ -167,7 +173,6 @@ __device__ __forceinline__ void compress_block(const SeqsDev& S, const RowsDev& 
   }
 
   // ---- store
-  const int64_t orow = entry_row(S, b, S.entry_off ? S.entry_off[b] : 0, i);
   uint8_t* dst = out.data + orow * out.stride;
   const int lane = threadIdx.x & 63;
   switch (out.dtype) {

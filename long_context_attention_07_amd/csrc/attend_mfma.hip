@@ -889,24 +889,27 @@ __global__ void __launch_bounds__(256) attend_combine_mfma_kernel(AttendArgs a, 
   const int lane = (int)threadIdx.x % TPH;
   const bool on = h < a.n_h;
   const int hh = on ? h : 0;
-  const int64_t* meta = split_meta(const_cast<float*>(ws_ml), a, max_chunks);
-  const int64_t p = meta[2 * t];
-  const int n_chunks = (int)meta[2 * t + 1];
   const int d0 = DPL * lane;
   const int64_t base0 = (int64_t)t * max_chunks * a.n_h + hh;
-  FoldState f = fold_init(on ? a.sink[hh] * kLog2e : -INFINITY);
+  // The RoPE table, the sink, the first batch of partials (every chunk slot the workspace
+  // holds: in bounds, unused past the token's chunk count) and the token record are all
+  // requested before any of them is used.
+  const bool f_on = (int)threadIdx.x < a.rope.dims / 2;
+  double f_rad = 0.0, f_rev = 0.0;
+  if (f_on) {
+    f_rad = a.rope.inv_freq[threadIdx.x];
+    f_rev = a.rope.inv_freq_rev[threadIdx.x];
+  }
   float O[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) O[i] = 0.f;
-  load_freqs(F, a.rope);
-  for (int c0 = 0; c0 < max_chunks; c0 += kCB) {
-    float2 ml[kCB];
-    float o[kCB][DPL];
+  float2 ml[kCB];
+  float o[kCB][DPL];
+  auto load_batch = [&](int c0, int lim) {
 #pragma unroll
     for (int i = 0; i < kCB; ++i) {
-      // first batch: every chunk slot the workspace holds (in bounds, unused past n_chunks)
       const int c = c0 + i;
-      if (c < (c0 == 0 ? max_chunks : n_chunks)) {
+      if (c < lim) {
         const int64_t b = base0 + (int64_t)c * a.n_h;
         ml[i] = *reinterpret_cast<const float2*>(ws_ml + 2 * b);
         const float* po = ws_o + b * kDM + d0;
@@ -926,6 +929,19 @@ __global__ void __launch_bounds__(256) attend_combine_mfma_kernel(AttendArgs a, 
         }
       }
     }
+  };
+  load_batch(0, max_chunks);
+  const int64_t* meta = split_meta(const_cast<float*>(ws_ml), a, max_chunks);
+  const int64_t p = meta[2 * t];
+  const int n_chunks = (int)meta[2 * t + 1];
+  const float sink = a.sink[hh];
+  if (f_on) {
+    F.rad[threadIdx.x] = f_rad;
+    F.rev[threadIdx.x] = f_rev;
+  }
+  FoldState f = fold_init(on ? sink * kLog2e : -INFINITY);
+  for (int c0 = 0;; c0 += kCB) {
+    if (c0 > 0) load_batch(c0, n_chunks);
 #pragma unroll
     for (int i = 0; i < kCB; ++i) {
       if (c0 + i < n_chunks) {

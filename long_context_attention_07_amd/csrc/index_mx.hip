@@ -140,6 +140,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PAGED 
         }
       // weights of the result rows: head 4g + j + 16 hb (fp8: times the head's query scale)
       float wr[QB][4][4];
+      float qs[QB][4][4];
 #pragma unroll
       for (int i = 0; i < QB; ++i)
 #pragma unroll
@@ -149,10 +150,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PAGED 
             const int h = 4 * g + j + 16 * hb;
             const bool on = i < nq && h < n_I;
             const int64_t row = (int64_t)(t0 + i) * n_I + h;
-            float wv_ = on ? w[row] : 0.f;
-            if (F8 && on) wv_ *= reinterpret_cast<const float*>(qI.scales)[row];
-            wr[i][hb][j] = wv_;
+            wr[i][hb][j] = on ? w[row] : 0.f;
+            if (F8) qs[i][hb][j] = on ? reinterpret_cast<const float*>(qI.scales)[row] : 0.f;
           }
+      // (the products after all the loads: taken in the loads' branches, each would be
+      // waited for on its own)
+      if (F8) {
+#pragma unroll
+        for (int i = 0; i < QB; ++i)
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wr[i][hb][j] *= qs[i][hb][j];
+      }
       // Entry numbers within a sequence fit in 32 bits (positions are int32); the pool row
       // is formed in 64 bits.  PAGED (block-table pools) is a separate instantiation, so
       // the contiguous case carries no block-id load for the compiler to wait on.

@@ -241,54 +241,30 @@ __device__ __forceinline__ uint3 topk_find_digit(const uint32_t* hist, int nbins
 // thread counts its keys > T and == T, one block scan gives its output offsets, and it
 // writes its kept indices in ascending order.
 // Thread tid's keys NPT tid .. NPT tid + NPT-1 of the row, those below `lim` (16 bytes at a
-// time when the row is 16-byte aligned, else one score at a time, clamped into the row); the
-// rest 0.  The loads (issue) and the keying (keys) are apart, so that other loads can be
-// requested in between: a use of a loaded value makes the wave wait for it there.
-template <int NPT, typename ST>
-struct TopkKeyLoads {
-  static constexpr int kPer16 = 16 / (int)sizeof(ST);  // scores per 16-byte load
-  uint4 vec[NPT / kPer16];
-  ST one[NPT];
-  bool wide;
-  __device__ __forceinline__ void issue(const ST* __restrict__ src, int lim) {
-    const int i0 = NPT * (int)threadIdx.x;
-    wide = (reinterpret_cast<uintptr_t>(src + i0) & 15u) == 0 && i0 + NPT <= lim;
-    if (wide) {
-#pragma unroll
-      for (int q = 0; q < NPT / kPer16; ++q) vec[q] = reinterpret_cast<const uint4*>(src + i0)[q];
-    } else {
-#pragma unroll
-      for (int j = 0; j < NPT; ++j) one[j] = src[min(i0 + j, lim - 1)];
-    }
-  }
-  __device__ __forceinline__ void keys(int lim, uint32_t (&key)[NPT]) const {
-    const int i0 = NPT * (int)threadIdx.x;
-    if (wide) {
-#pragma unroll
-      for (int q = 0; q < NPT / kPer16; ++q) {
-        const uint32_t w4[4] = {vec[q].x, vec[q].y, vec[q].z, vec[q].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if constexpr (sizeof(ST) == 4) {
-            key[4 * q + u] = score_key(__uint_as_float(w4[u]));
-          } else {
-            key[kPer16 * q + 2 * u] = score_key((uint16_t)(w4[u] & 0xffffu));
-            key[kPer16 * q + 2 * u + 1] = score_key((uint16_t)(w4[u] >> 16));
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NPT; ++j) key[j] = i0 + j < lim ? score_key(one[j]) : 0u;
-    }
-  }
-};
-
+// time when the row is 16-byte aligned); the rest 0.
 template <int NPT, typename ST>
 __device__ __forceinline__ void topk_load_keys(const ST* __restrict__ src, int lim, uint32_t (&key)[NPT]) {
-  TopkKeyLoads<NPT, ST> loads;
-  loads.issue(src, lim);
-  loads.keys(lim, key);
+  const int i0 = NPT * (int)threadIdx.x;
+  constexpr int per16 = 16 / (int)sizeof(ST);  // scores per 16-byte load
+  if ((reinterpret_cast<uintptr_t>(src + i0) & 15u) == 0 && i0 + NPT <= lim) {
+#pragma unroll
+    for (int q = 0; q < NPT / per16; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(src + i0)[q];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (sizeof(ST) == 4) {
+          key[4 * q + u] = score_key(__uint_as_float(w4[u]));
+        } else {
+          key[per16 * q + 2 * u] = score_key((uint16_t)(w4[u] & 0xffffu));
+          key[per16 * q + 2 * u + 1] = score_key((uint16_t)(w4[u] >> 16));
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) key[j] = i0 + j < lim ? score_key(src[i0 + j]) : 0u;
+  }
 }
 
 // The selection over keys held as above; keys at n and beyond take no part.  Every kept
@@ -422,9 +398,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_decode_kernel(SeqsDev S, co
   __shared__ TopkRegLds rsh;
   const int t = blockIdx.x;
   const ST* src = score + (int64_t)t * score_stride;
-  const int lim = (int)min(score_stride, (int64_t)NPT * kTopkThreads);
-  TopkKeyLoads<NPT, ST> loads;
-  loads.issue(src, lim);
+  uint32_t key[NPT];
+  topk_load_keys<NPT>(src, (int)min(score_stride, (int64_t)NPT * kTopkThreads), key);
   topk_clear_hists(rsh);  // while the keys and the context are in flight
   const TokenCtx ctx = token_ctx(S, t);
   const int64_t V = (ctx.p + 1) / ratio;
@@ -437,8 +412,6 @@ __global__ void __launch_bounds__(kTopkThreads) topk_decode_kernel(SeqsDev S, co
     topk_select_mem(src, (int)V, k, out, sh);
     return;
   }
-  uint32_t key[NPT];
-  loads.keys(lim, key);
   const int i0 = NPT * (int)threadIdx.x;
   topk_select_keys_emit<NPT, sizeof(ST) == 2, true>(key, (int)V, k, rsh,
                                                    [&](uint32_t pos, int j, uint32_t) { out[pos] = i0 + j; });

@@ -264,3 +264,62 @@ def test_paged_mixed_precision_prefill_equals_contiguous():
     assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16)), "out bits differ"
     assert torch.equal(a[2].view(torch.int32), b[2].view(torch.int32)), "lse bits differ"
     log("paged prefill chunks (fp8 KV, MXFP4 keys): bit-identical to contiguous pools")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
+def test_paged_scaled_indexer_decode_equals_contiguous(fmt):
+    """The decode indexer on the scaled matrix cores (MXFP4 or fp8 1x128 keys, one query row
+    per sequence) over paged key pools gives the contiguous pools' score bits.  64 sequences
+    of 524288 tokens (131072 entries each): enough work that the contiguous launch takes
+    ranges of 4096 entries while the paged one keeps each range within one block-id load
+    (2048 entries of 32-entry blocks), so the two launches also split the rows differently.
+    Key bytes are drawn directly in the format (any e2m1 code; e8m0 scales near 1; e4m3
+    codes without the NaN pattern, fp32 row scales), which is all bit equality needs."""
+    n, L, ratio, n_I, d_I, epb = 64, 524288, 4, 64, 128, 32
+    V = L // ratio
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(71)
+
+    def rows(count, seed_shift):
+        gen.manual_seed(71 + seed_shift)
+        if fmt == "mxfp4":
+            data = torch.randint(0, 256, (count, d_I // 2), generator=gen, device=DEV, dtype=torch.uint8)
+            sc = torch.randint(122, 133, (count, d_I // 32), generator=gen, device=DEV, dtype=torch.uint8)
+            return data, sc
+        data = torch.randint(0, 256, (count, d_I), generator=gen, device=DEV, dtype=torch.uint8)
+        data = torch.where((data & 0x7f) == 0x7f, data - 1, data)  # no NaN code
+        sc = torch.rand((count, 1), generator=gen, device=DEV, dtype=torch.float32) * 0.01 + 0.001
+        return data, sc
+
+    kind = ops.MXFP4 if fmt == "mxfp4" else ops.FP8_B128
+    k_data, k_sc = rows(n * V, 0)
+    q_data, q_sc = rows(n * n_I, 1)
+    w = (torch.randn((n, n_I), generator=gen, device=DEV) / 8).contiguous()
+    qI = ops.Rows(q_data, kind, d_I, q_sc)
+
+    # paged copy: the blocks of all sequences placed by a random permutation among 7 spare ones
+    nblk = V // epb
+    total = n * nblk + 7
+    perm = torch.randperm(total, generator=gen, device=DEV)
+    table = perm[: n * nblk].view(n, nblk)
+    erow = (table.repeat_interleave(epb, dim=1) * epb + torch.arange(V, device=DEV) % epb).reshape(-1)
+    pk_data = torch.randint(0, 256, (total * epb,) + tuple(k_data.shape[1:]), generator=gen, device=DEV,
+                            dtype=torch.uint8)
+    if fmt == "fp8":
+        pk_data = torch.where((pk_data & 0x7f) == 0x7f, pk_data - 1, pk_data)
+    pk_sc = torch.ones((total * epb,) + tuple(k_sc.shape[1:]), device=DEV, dtype=k_sc.dtype)
+    pk_data[erow] = k_data
+    pk_sc[erow] = k_sc
+
+    lens = [L] * n
+    sq_c = ops.Seqs([1] * n, lens, [b * V for b in range(n)], [0] * n, [L - 1] * n)
+    sq_p = ops.Seqs([1] * n, lens, [0] * n, [0] * n, [L - 1] * n, block_table=table.cpu().tolist(),
+                    block_entries=epb)
+    s_c = torch.full((n, V), float("nan"), device=DEV)
+    s_p = torch.full((n, V), float("nan"), device=DEV)
+    ops.csa_index_score(sq_c, qI, w, n_I, ops.Rows(k_data, kind, d_I, k_sc), ratio, s_c)
+    ops.csa_index_score(sq_p, qI, w, n_I, ops.Rows(pk_data, kind, d_I, pk_sc), ratio, s_p)
+    torch.cuda.synchronize()
+    assert torch.isfinite(s_c).all(), "every visible entry scored, finite"
+    assert torch.equal(s_c.view(torch.int32), s_p.view(torch.int32)), "paged scores differ from contiguous"
+    log(f"paged {fmt} decode indexer: {n} x {V} scores bit-identical to contiguous pools")

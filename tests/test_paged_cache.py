@@ -266,16 +266,18 @@ def test_paged_mixed_precision_prefill_equals_contiguous():
     log("paged prefill chunks (fp8 KV, MXFP4 keys): bit-identical to contiguous pools")
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "fp8"])
-def test_paged_scaled_indexer_decode_equals_contiguous(fmt):
+@pytest.mark.parametrize("fmt,epb", [("mxfp4", 32), ("fp8", 32), ("mxfp4", 4)])
+def test_paged_scaled_indexer_decode_equals_contiguous(fmt, epb):
     """The decode indexer on the scaled matrix cores (MXFP4 or fp8 1x128 keys, one query row
     per sequence) over paged key pools gives the contiguous pools' score bits.  64 sequences
     of 524288 tokens (131072 entries each): enough work that the contiguous launch takes
     ranges of 4096 entries while the paged one keeps each range within one block-id load
     (2048 entries of 32-entry blocks), so the two launches also split the rows differently.
+    With 4-entry blocks a range spans more blocks than one load holds, and the later rows
+    take their block ids from the table one by one.
     Key bytes are drawn directly in the format (any e2m1 code; e8m0 scales near 1; e4m3
     codes without the NaN pattern, fp32 row scales), which is all bit equality needs."""
-    n, L, ratio, n_I, d_I, epb = 64, 524288, 4, 64, 128, 32
+    n, L, ratio, n_I, d_I = 64, 524288, 4, 64, 128
     V = L // ratio
     gen = torch.Generator(device=DEV)
     gen.manual_seed(71)

@@ -266,17 +266,19 @@ def test_paged_mixed_precision_prefill_equals_contiguous():
     log("paged prefill chunks (fp8 KV, MXFP4 keys): bit-identical to contiguous pools")
 
 
-@pytest.mark.parametrize("fmt,epb", [("mxfp4", 32), ("fp8", 32), ("mxfp4", 4)])
-def test_paged_scaled_indexer_decode_equals_contiguous(fmt, epb):
-    """The decode indexer on the scaled matrix cores (MXFP4 or fp8 1x128 keys, one query row
-    per sequence) over paged key pools gives the contiguous pools' score bits.  64 sequences
+@pytest.mark.parametrize("fmt,epb", [("mxfp4", 32), ("fp8", 32), ("mxfp4", 4), ("bf16", 32), ("bf16", 4)])
+def test_paged_decode_indexer_equals_contiguous(fmt, epb):
+    """The decode indexer (MXFP4 or fp8 1x128 keys on the scaled matrix cores, or bf16 keys,
+    one query row per sequence) over paged key pools gives the contiguous pools' score bits.  64 sequences
     of 524288 tokens (131072 entries each): enough work that the contiguous launch takes
     ranges of 4096 entries while the paged one keeps each range within one block-id load
     (2048 entries of 32-entry blocks), so the two launches also split the rows differently.
     With 4-entry blocks a range spans more blocks than one load holds, and the later rows
     take their block ids from the table one by one.
+    (The bf16 kernel's ranges are 448 entries: 4-entry blocks take it past one load too.)
     Key bytes are drawn directly in the format (any e2m1 code; e8m0 scales near 1; e4m3
-    codes without the NaN pattern, fp32 row scales), which is all bit equality needs."""
+    codes without the NaN pattern, fp32 row scales; bf16 from N(0,1)), which is all bit
+    equality needs."""
     n, L, ratio, n_I, d_I = 64, 524288, 4, 64, 128
     V = L // ratio
     gen = torch.Generator(device=DEV)
@@ -284,6 +286,9 @@ def test_paged_scaled_indexer_decode_equals_contiguous(fmt, epb):
 
     def rows(count, seed_shift):
         gen.manual_seed(71 + seed_shift)
+        if fmt == "bf16":
+            data = torch.randn((count, d_I), generator=gen, device=DEV).to(torch.bfloat16)
+            return data, None
         if fmt == "mxfp4":
             data = torch.randint(0, 256, (count, d_I // 2), generator=gen, device=DEV, dtype=torch.uint8)
             sc = torch.randint(122, 133, (count, d_I // 32), generator=gen, device=DEV, dtype=torch.uint8)
@@ -293,7 +298,7 @@ def test_paged_scaled_indexer_decode_equals_contiguous(fmt, epb):
         sc = torch.rand((count, 1), generator=gen, device=DEV, dtype=torch.float32) * 0.01 + 0.001
         return data, sc
 
-    kind = ops.MXFP4 if fmt == "mxfp4" else ops.FP8_B128
+    kind = {"mxfp4": ops.MXFP4, "fp8": ops.FP8_B128, "bf16": ops.BF16}[fmt]
     k_data, k_sc = rows(n * V, 0)
     q_data, q_sc = rows(n * n_I, 1)
     w = (torch.randn((n, n_I), generator=gen, device=DEV) / 8).contiguous()
@@ -305,13 +310,17 @@ def test_paged_scaled_indexer_decode_equals_contiguous(fmt, epb):
     perm = torch.randperm(total, generator=gen, device=DEV)
     table = perm[: n * nblk].view(n, nblk)
     erow = (table.repeat_interleave(epb, dim=1) * epb + torch.arange(V, device=DEV) % epb).reshape(-1)
-    pk_data = torch.randint(0, 256, (total * epb,) + tuple(k_data.shape[1:]), generator=gen, device=DEV,
-                            dtype=torch.uint8)
-    if fmt == "fp8":
-        pk_data = torch.where((pk_data & 0x7f) == 0x7f, pk_data - 1, pk_data)
-    pk_sc = torch.ones((total * epb,) + tuple(k_sc.shape[1:]), device=DEV, dtype=k_sc.dtype)
+    if fmt == "bf16":
+        pk_data = torch.randn((total * epb, d_I), generator=gen, device=DEV).to(torch.bfloat16)
+        pk_sc = None
+    else:
+        pk_data = torch.randint(0, 256, (total * epb,) + tuple(k_data.shape[1:]), generator=gen, device=DEV,
+                                dtype=torch.uint8)
+        if fmt == "fp8":
+            pk_data = torch.where((pk_data & 0x7f) == 0x7f, pk_data - 1, pk_data)
+        pk_sc = torch.ones((total * epb,) + tuple(k_sc.shape[1:]), device=DEV, dtype=k_sc.dtype)
+        pk_sc[erow] = k_sc
     pk_data[erow] = k_data
-    pk_sc[erow] = k_sc
 
     lens = [L] * n
     sq_c = ops.Seqs([1] * n, lens, [b * V for b in range(n)], [0] * n, [L - 1] * n)

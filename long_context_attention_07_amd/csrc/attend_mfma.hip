@@ -545,21 +545,23 @@ __device__ __forceinline__ TileAddr resolve_tile64(const AttendArgs& a, const To
 
 // fp8 rows 8w .. 8w+7 of the tile straight into the raw row buffer (576 bytes a row, lanes
 // 0..35 one 16-byte piece each) and their four block scales into rsc (lanes 0..7, one row
-// each), by the memory-to-LDS path: no registers hold rows in flight.
+// each), by the memory-to-LDS path (assembly: the caller waits on the vector memory counter
+// before reading them): no registers hold rows in flight, and no LDS read of the current
+// tile waits for them.
 __device__ __forceinline__ void issue_rows_lds(int w, int lane, const TileStage& st, const TileAddr& ad, uint8_t* raw,
                                                float* rsc) {
+  const uint32_t raw0 = lds_addr(raw);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 8 * w + i;
     if ((st.valid >> r) & 1ull) {
       const uint64_t rowp = readlane_u64(ad.row, r);
       if (lane < kSplitLanes)
-        __builtin_amdgcn_global_load_lds((global_cvp)(rowp + 16u * lane), (lds_vp)(raw + r * kSplitRowBytes), 16, 0, 0);
+        dma_row(rowp, 16u * lane, __builtin_amdgcn_readfirstlane(raw0 + (uint32_t)(r * kSplitRowBytes)));
     }
   }
   const uint64_t scp = __shfl(ad.sc, 8 * w + (lane & 7));
-  if (lane < 8 && ((st.valid >> (8 * w + lane)) & 1ull))
-    __builtin_amdgcn_global_load_lds((global_cvp)scp, (lds_vp)(rsc + 32 * w), 16, 0, 0);
+  if (lane < 8 && ((st.valid >> (8 * w + lane)) & 1ull)) dma_lanes(scp, lds_addr(rsc + 32 * w));
 }
 
 __device__ __forceinline__ uint2 finalize4(const float* x, int d0, int dn, int64_t p, const FreqLds& F) {

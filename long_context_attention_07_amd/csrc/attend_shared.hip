@@ -57,19 +57,6 @@ __host__ __device__ inline int chunk_slots_shared(int csa, int k, int n_win) {
 }
 int attend_shared_chunk_slots(int csa, int k, int n_win) { return chunk_slots_shared(csa, k, n_win); }
 
-// One 1 KiB row from global memory (uniform base `row`, byte `voff` of it per lane) into
-// LDS at `lds` + 16 lane, by the memory-to-LDS path.  Written as assembly: the compiler
-// would otherwise make every LDS read wait for all such loads in flight; the kernel waits
-// on the vector memory counter itself.  M0 is saved and restored around it; the statement
-// waits out the hazards of a VALU-written SGPR and of the M0 write itself (5 wait states).
-__device__ __forceinline__ void dma_row_sh(uint64_t row, uint32_t voff, uint32_t lds) {
-  uint32_t keep;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-               : "=&s"(keep)
-               : "v"(voff), "s"(row), "s"(lds)
-               : "memory");
-}
-
 // Wait until at most 8 n of this wave's row loads are in flight (n = 0, 1, 2).
 __device__ __forceinline__ void wait_rows(int n) {
   if (n >= 2)
@@ -174,7 +161,7 @@ attend_shared_kernel(AttendArgs a, float* __restrict__ ws_o, float* __restrict__
     for (int i = 0; i < 8; ++i) {
       const int r = 8 * w + i;
       const int hr = hg * kShHeads + r < a.n_h ? r : 0;
-      dma_row_sh(readlane_u64(reinterpret_cast<uint64_t>(q0row + (int64_t)hr * a.q.stride), 0), 16u * lane,
+      dma_row(readlane_u64(reinterpret_cast<uint64_t>(q0row + (int64_t)hr * a.q.stride), 0), 16u * lane,
                  lds0 + (uint32_t)(((r >> 4) * kShStageBytes) + (r & 15) * kKStride));
     }
   }
@@ -288,7 +275,7 @@ attend_shared_kernel(AttendArgs a, float* __restrict__ ws_o, float* __restrict__
   };
   // row i (0..7) of this wave's share of a resolved stage, memory -> LDS
   auto issue = [&](const ShReq& q, int i) {
-    dma_row_sh(readlane_u64(q.addr, 8 * hgi + i), 16u * lane, q.lds0 + (uint32_t)(i * kKStride));
+    dma_row(readlane_u64(q.addr, 8 * hgi + i), 16u * lane, q.lds0 + (uint32_t)(i * kKStride));
   };
   auto request = [&](int st) -> ShStage {
     const ShReq q = resolve(st);

@@ -269,6 +269,34 @@ __device__ __forceinline__ float scale_frame(float m) {
 typedef const __attribute__((address_space(1))) void* global_cvp;
 typedef __attribute__((address_space(3))) void* lds_vp;
 
+// LDS address of a pointer into a __shared__ array, uniform across the wave.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((lds_vp)p));
+}
+
+// Memory-to-LDS loads written as assembly: 16 bytes per active lane, lane l's bytes landing
+// at LDS address `lds` + 16 l.  The compiler does not see these as LDS writes, so it never
+// makes a later LDS read wait for them (with the builtin it made reads of other LDS arrays
+// wait for every such load in flight, draining the prefetch); the kernels wait on the vector
+// memory counter themselves.  M0 is saved and restored around the load; the statement waits
+// out the hazards of a VALU-written SGPR and of the M0 write itself (5 wait states).
+// Uniform base `row` (an SGPR pair) plus a per-lane 32-bit byte offset:
+__device__ __forceinline__ void dma_row(uint64_t row, uint32_t voff, uint32_t lds) {
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep)
+               : "v"(voff), "s"(row), "s"(lds)
+               : "memory");
+}
+// A 64-bit address per lane:
+__device__ __forceinline__ void dma_lanes(uint64_t addr, uint32_t lds) {
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep)
+               : "v"(addr), "s"(lds)
+               : "memory");
+}
+
 // Launch of the shared-stage kernel (bf16 rows, chunked key lists, 32 heads per
 // workgroup): split = one workgroup per (token, head group, chunk) writing chunk partials,
 // else one per (token, head group) walking its chunks.

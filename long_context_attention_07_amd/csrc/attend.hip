@@ -192,8 +192,7 @@ int64_t attend_max_chunks(const AttendArgs& a) {
   if (a.q.dim == kMfmaHeadDim) {
     // the row format is not a host scalar of the workspace query: cover the chunking of
     // the bf16-row kernel too
-    const int64_t C2 = attend_shared_chunk_slots(a.csa, a.k, a.n_win);
-    mc = std::max(mc, (n_ent + a.n_win + C2 - 1) / C2);
+    mc = std::max(mc, attend_shared_max_chunks(a.csa, a.k, a.n_win, n_ent));
   }
   return mc;
 }

@@ -41,21 +41,47 @@ struct __align__(16) SharedLds {
 static_assert(4 * kHG * kShMergeStride * 4 <= (int)sizeof(SharedLds::ring), "merge scratch fits the ring");
 static_assert(2 * kShStageBytes >= kShHeads * kKStride, "query block fits two slots");
 
-// Chunk length in key slots: a CSA list of S = k + n_win slots is cut into four chunks
-// (more when a quarter would exceed the entry-id table), rounded up to whole stage pairs;
-// HCA lists, which grow with the context, in chunks of 288 slots.  Depends on operation
-// parameters only.
+// Chunk length C in key slots.  A list longer than one chunk has its entry slots and its
+// window slots cut into chunks of C separately, entries first: the window rows, which the
+// kernel rotates as they are staged (a longer stage), then never share a chunk with
+// entries, so the chunk holding the window is no longer the slowest of a token's chunks.
+// A list of at most C slots is one chunk.  CSA: the k entry slots in three
+// chunks (more when a third would exceed the entry-id table), rounded up to whole stage
+// pairs, at least 64 slots; with k = 512 and a 128-row window, chunks of 192, 192, 128
+// entries and the window's 128 rows.  HCA lists, which grow with the context, in chunks of
+// 288 slots.  Depends on operation parameters only.
 constexpr int kShHcaChunk = 288;
 __host__ __device__ inline int chunk_slots_shared(int csa, int k, int n_win) {
+  (void)n_win;
   if (!csa) return kShHcaChunk;
-  const int S = k + n_win;
-  if (S <= 0) return 32;
-  int n = (S + kMaxChunkSlots - 1) / kMaxChunkSlots;
-  if (n < 4) n = 4;
-  const int c = (S + n - 1) / n;
-  return ((c + 31) / 32) * 32;
+  if (k <= 0) return 64;
+  int n = (k + kMaxChunkSlots - 1) / kMaxChunkSlots;
+  if (n < 3) n = 3;
+  const int c = ((k + n - 1) / n + 31) / 32 * 32;
+  return c < 64 ? 64 : c;
+}
+// Chunks of a list with n_ent entry slots and n_win window slots (a non-decreasing function
+// of n_ent), and chunk cc's first slot and length (entry chunks, then window chunks).
+__host__ __device__ inline int64_t chunks_shared(int64_t n_ent, int n_win, int C) {
+  if (n_ent + n_win <= C) return n_ent + n_win > 0 ? 1 : 0;
+  return (n_ent + C - 1) / C + ((int64_t)n_win + C - 1) / C;
+}
+__host__ __device__ inline int64_t chunk_lo_shared(int cc, int64_t n_ent, int n_win, int C) {
+  if (n_ent + n_win <= C) return 0;
+  const int64_t n_ec = (n_ent + C - 1) / C;
+  return cc < n_ec ? (int64_t)cc * C : n_ent + (cc - n_ec) * C;
+}
+__host__ __device__ inline int64_t chunk_len_shared(int cc, int64_t n_ent, int n_win, int C) {
+  if (n_ent + n_win <= C) return n_ent + n_win;
+  const int64_t n_ec = (n_ent + C - 1) / C;
+  const int64_t lo = cc < n_ec ? (int64_t)cc * C : (cc - n_ec) * C;
+  const int64_t hi = cc < n_ec ? n_ent : (int64_t)n_win;
+  return hi - lo < C ? hi - lo : C;
 }
 int attend_shared_chunk_slots(int csa, int k, int n_win) { return chunk_slots_shared(csa, k, n_win); }
+int64_t attend_shared_max_chunks(int csa, int k, int n_win, int64_t max_ent) {
+  return chunks_shared(max_ent, n_win, chunk_slots_shared(csa, k, n_win));
+}
 
 // Wait until at most 8 n of this wave's row loads are in flight (n = 0, 1, 2).
 __device__ __forceinline__ void wait_rows(int n) {
@@ -166,9 +192,12 @@ attend_shared_kernel(AttendArgs a, float* __restrict__ ws_o, float* __restrict__
     }
   }
   const int c_begin = SPLIT ? c_only : 0;
-  int64_t s_lo = (int64_t)c_begin * chunk_slots;  // first slot of the chunk in hand
+  // first slot of the chunk in hand: before the context lookup, the slot it has if it is an
+  // entry chunk (set for good below)
+  int64_t s_lo = (int64_t)c_begin * chunk_slots;
   // the entry ids of the chunk's slots (CSA lists start with their k entry slots, so the
-  // ids need no context lookup): thread tid holds slots s_lo + tid + 256 j
+  // ids of an entry chunk need no context lookup; a window chunk never reads them): thread
+  // tid holds slots s_lo + tid + 256 j
   constexpr int kIdsPerThread = (kMaxChunkSlots + 255) / 256;
   int32_t ids[kIdsPerThread];
   // (issued unconditionally, clamped into the token's list, and not looked at before the
@@ -196,8 +225,7 @@ attend_shared_kernel(AttendArgs a, float* __restrict__ ws_o, float* __restrict__
     F.rev[tid] = f_rev;
   }
   const int64_t n_ent = entry_slots(a, ctx);
-  const int64_t n_slots = n_ent + a.n_win;
-  const int n_chunks = (int)((n_slots + chunk_slots - 1) / chunk_slots);
+  const int n_chunks = (int)chunks_shared(n_ent, a.n_win, chunk_slots);
   if (SPLIT && c_only == 0 && hg == 0 && tid == 0) {
     int64_t* meta = split_meta(ws_ml, a, max_chunks);
     meta[2 * t] = ctx.p;
@@ -206,6 +234,11 @@ attend_shared_kernel(AttendArgs a, float* __restrict__ ws_o, float* __restrict__
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the query rows are in LDS
   if (SPLIT && c_only >= n_chunks) return;
   const int c_end = SPLIT ? c_only + 1 : n_chunks;
+  int64_t c_len = 0;  // slots of the chunk in hand
+  if (c_begin < n_chunks) {
+    s_lo = chunk_lo_shared(c_begin, n_ent, a.n_win, chunk_slots);
+    c_len = chunk_len_shared(c_begin, n_ent, a.n_win, chunk_slots);
+  }
 
   const uint64_t standin = reinterpret_cast<uint64_t>(q0row);
   const int64_t win_lo = n_ent, win_hi = n_ent + a.n_win;  // slots of the window
@@ -213,7 +246,6 @@ attend_shared_kernel(AttendArgs a, float* __restrict__ ws_o, float* __restrict__
   // the address with the slot's kind in the low bits (rows are 16-byte aligned): 0 no key
   // (the stand-in row), 1 entry, 2 window token.
   auto build_table = [&]() {
-    const int64_t c_len = min((int64_t)chunk_slots, n_slots - s_lo);
     const int64_t n_tab = (c_len + 15) / 16 * 16;
     // paged pools: the block ids of all the thread's entry slots are requested before any
     // is used (one round trip, not one per slot)
@@ -290,7 +322,6 @@ attend_shared_kernel(AttendArgs a, float* __restrict__ ws_o, float* __restrict__
   ShStage m0, m1;
   int ns = 0, n_it = 0;
   auto prime = [&]() {
-    const int64_t c_len = min((int64_t)chunk_slots, n_slots - s_lo);
     ns = (int)((c_len + 15) / 16);
     n_it = (ns + 1) / 2;
     m0.valid = m0.win = 0u;
@@ -421,7 +452,8 @@ attend_shared_kernel(AttendArgs a, float* __restrict__ ws_o, float* __restrict__
   for (int cc = c_begin; cc < c_end; ++cc) {
     if (cc != c_begin) {
       // single launch, next chunk: its entry ids (the ring is drained, nothing in flight)
-      s_lo = (int64_t)cc * chunk_slots;
+      s_lo = chunk_lo_shared(cc, n_ent, a.n_win, chunk_slots);
+      c_len = chunk_len_shared(cc, n_ent, a.n_win, chunk_slots);
       load_ids();
       build_table();
       __syncthreads();

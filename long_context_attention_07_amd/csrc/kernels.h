@@ -51,6 +51,7 @@ struct AttendArgs {
 int attend_chunk_slots(const AttendArgs& a);
 // Chunk length of the shared-stage kernel (bf16 rows of 512 dims).
 int attend_shared_chunk_slots(int csa, int k, int n_win);
+int64_t attend_shared_max_chunks(int csa, int k, int n_win, int64_t max_ent);
 // Number of chunks of the longest key list the launch can see (grid / workspace sizing).
 int64_t attend_max_chunks(const AttendArgs& a);
 constexpr int kMfmaHeadDim = 512;    // head dim of the matrix-core attention kernels

@@ -125,10 +125,11 @@ def test_workspace_sizes(lib):
     assert lib.csa_workspace_bytes(ops.OP_INDEX_TOPK, P(s), 0, 0, 512, 4, 0) == 4 * (1 << 18) * 4 + 4 * 8 * 512 * 8
     assert lib.csa_workspace_bytes(99, P(s), 64, 512, 0, 128, 128) == 0
     hca = lib.csa_workspace_bytes(ops.OP_HCA_ATTEND, P(s), 64, 512, 0, 128, 128)
-    # 4 tokens x 29 chunks (8192 entries + 128 window slots: 288-slot chunks for bf16 rows,
-    # 15 of 576 for fp8 rows; the query does not know the row format and covers the larger
-    # count) x 64 heads x (512 dims + m, l) floats, plus a 16-byte record per token
-    assert hca == 4 * 29 * 64 * 514 * 4 + 4 * 16
+    # 4 tokens x 30 chunks (bf16 rows: the 8192 entries in 29 chunks of 288 slots, the 128
+    # window slots in one of their own; fp8 rows: 15 chunks of 576 over all 8320 slots; the
+    # query does not know the row format and covers the larger count) x 64 heads x (512 dims
+    # + m, l) floats, plus a 16-byte record per token
+    assert hca == 4 * 30 * 64 * 514 * 4 + 4 * 16
 
 
 def test_workspace_sizes_follow_the_launch(lib):
@@ -139,15 +140,17 @@ def test_workspace_sizes_follow_the_launch(lib):
     P = ctypes.byref
     ws = lambda s, op, n_h, d, k, r, w: lib.csa_workspace_bytes(op, P(s), n_h, d, k, r, w)  # noqa: E731
     c2 = _seqs(n_seqs=32, total_q=32, max_q=1, max_ctx=65536)
-    # k = 512, window 128: 640 slots in four 160-slot chunks (bf16 rows; two of 320 for fp8
-    # rows)
+    # k = 512, window 128: four chunks for bf16 rows (entries in 192, 192 and 128 slots, the
+    # window in one of 128); two of 320 over all 640 slots for fp8 rows
     assert ws(c2, ops.OP_CSA_ATTEND, 64, 512, 512, 4, 128) == 32 * 4 * 64 * 514 * 4 + 32 * 16
-    # k = 1024: 1152 slots in four 288-slot chunks (two of 576 for fp8 rows) for a decode
-    # batch; the prefill batch fills the chip without splitting
+    # k = 1024: four chunks for bf16 rows (entries in 352, 352 and 320 slots, then the
+    # window), two of 576 for fp8 rows, for a decode batch; the prefill batch fills the chip
+    # without splitting
     c4 = _seqs(n_seqs=1, total_q=131072, max_q=131072, max_ctx=131072)
     assert ws(c4, ops.OP_CSA_ATTEND, 64, 512, 1024, 4, 128) == 0
     assert ws(c2, ops.OP_CSA_ATTEND, 64, 512, 1024, 4, 128) == 32 * 4 * 64 * 514 * 4 + 32 * 16
-    # k = 64: 192 slots, one chunk for fp8 rows, three of 64 for bf16 rows
+    # k = 64: one chunk for fp8 rows; three of 64 slots for bf16 rows (the entries, then
+    # the window in two)
     assert ws(c2, ops.OP_CSA_ATTEND, 64, 512, 64, 4, 128) == 32 * 3 * 64 * 514 * 4 + 32 * 16
     # large batches run one workgroup per (token, head group) without splitting: from 128
     # tokens (512 groups of 16 heads, 256 of 32)

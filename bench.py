@@ -867,7 +867,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="csa_decode", choices=["csa_decode", "hca_decode", "csa_prefill"])
+    ap.add_argument("--workload", default="csa_decode", choices=["csa_decode", "csa_decode_1m", "hca_decode", "csa_prefill"],
+                    help="csa_decode_1m: the CSA decode batch at 1M context (one point of the sweep) on its own")
+    ap.add_argument("--indexer", default="bf16", choices=["bf16", "mxfp4", "fp8"],
+                    help="indexer key format of the CSA decode workloads")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-probe", action="store_true", help="skip the achievable-peak probes")
@@ -878,7 +881,9 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs of --profile-run into profiles/traffic_<workload>.json")
     args = ap.parse_args()
-    wl = configs.CSA_DECODE_BF16 if args.workload == "csa_decode" else configs.HCA_DECODE_1M_BF16
+    wl = {"csa_decode": configs.CSA_DECODE_BF16, "csa_decode_1m": configs.CSA_DECODE_SWEEP[-1]}.get(
+        args.workload, configs.HCA_DECODE_1M_BF16)
+    kfmt = args.indexer if wl.kind == "csa_decode" else "bf16"
     if args.traffic:
         traffic_from_counters(args.traffic[0], args.traffic[1], wl.name,
                               os.path.join(PROFILES, f"traffic_{wl.name}.json"))
@@ -902,13 +907,13 @@ def main():
             print(json.dumps(out), flush=True)
             return
         if args.profile_run:
-            layers, _ = build_layers(wl, dev)
+            layers, _ = build_layers(wl, dev, kfmt)
             for L_ in layers:
                 L_.step()
             profile_run(layers, stream, args.profile_run)
             log("profile run done")
             return
-        main_res, layers = run_decode(wl, dev, stream, args.steps, args.warmup, graph=not args.no_graph)
+        main_res, layers = run_decode(wl, dev, stream, args.steps, args.warmup, kfmt, graph=not args.no_graph)
         traffic = load_traffic(wl)
         t_op = traffic["ops"].get(main_res["roofline"]["kernel"]) if traffic else None
         main_res["roofline"]["traffic"] = t_op["bytes_per_launch"] if t_op else None
@@ -936,7 +941,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.n_seqs, "ctx": f"log-uniform [{wl.ctx_lo}, {wl.ctx_hi}] "
                    f"seed {wl.seed}", "n_h": wl.n_h, "d_c": wl.d_c, "ratio": wl.ratio,
                    "k": wl.k if wl.kind == "csa_decode" else None, "n_win": wl.n_win,
-                   "indexer": f"{wl.n_I}x{wl.d_I} bf16" if wl.kind == "csa_decode" else None,
+                   "indexer": f"{wl.n_I}x{wl.d_I} {kfmt}" if wl.kind == "csa_decode" else None,
                    "layer_sets": main_res["layer_sets"], "graph": not args.no_graph},
         "step_time": main_res["step_time"],
         "roofline": main_res["roofline"],

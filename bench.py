@@ -914,7 +914,7 @@ def main():
             log("profile run done")
             return
         main_res, layers = run_decode(wl, dev, stream, args.steps, args.warmup, kfmt, graph=not args.no_graph)
-        traffic = load_traffic(wl)
+        traffic = load_traffic(wl) if kfmt == "bf16" else None  # counters are taken with bf16 keys
         t_op = traffic["ops"].get(main_res["roofline"]["kernel"]) if traffic else None
         main_res["roofline"]["traffic"] = t_op["bytes_per_launch"] if t_op else None
         cpu = None

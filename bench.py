@@ -52,7 +52,7 @@ MAX_SETS = 64
 OP_KERNELS = {"compress": ["compress2_kernel", "compress_kernel"],
               "index_score": ["index_score_mfma_kernel", "index_score_mfma_units_kernel", "index_score_mx_kernel",
                               "index_score_mx_block_kernel"],
-              "topk": ["topk_kernel", "topk_decode_kernel"],
+              "topk": ["topk_kernel", "topk_decode_kernel", "topk_slice_kernel", "topk_merge_kernel"],
               "attend": ["attend_shared_kernel", "attend_pair_kernel", "attend_combine_mfma_kernel", "attend_long_kernel"]}
 PREFILL_KERNELS = {"compress": ["compress2_kernel"], "index_score": ["index_score_mx_block_kernel"],
                    "topk": ["topk_kernel"], "attend": ["attend_long_kernel"]}
@@ -605,14 +605,20 @@ def traffic_from_counters(fetch_dir, write_dir, workload, out_path):
     print(json.dumps(res, indent=1))
 
 
-def load_traffic(wl):
+def traffic_name(wl, kfmt="bf16"):
+    """Name of a workload's counter-traffic file: the indexer key format joins the name when
+    it is not bf16."""
+    return wl.name if kfmt == "bf16" else f"{wl.name}_{kfmt}"
+
+
+def load_traffic(wl, kfmt="bf16"):
     """Counter bytes for `wl` when they were taken on the current sources and the copy
     calibration is one the counters explain; else None.  WRITE_SIZE must read the copy's
     bytes within 25%.  FETCH_SIZE must read them within 25% or at half (a factor of 2
     within 10%): the L2's read requests to memory are 128 bytes here (a plain copy counts
     one TCC_EA0_RDREQ per 128 bytes, TCC_BUBBLE stays 0), and FETCH_SIZE prices each at 64.
     Any other factor means the counters saw only part of the chip."""
-    path = os.path.join(PROFILES, f"traffic_{wl.name}.json")
+    path = os.path.join(PROFILES, f"traffic_{traffic_name(wl, kfmt)}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -885,8 +891,8 @@ def main():
         args.workload, configs.HCA_DECODE_1M_BF16)
     kfmt = args.indexer if wl.kind == "csa_decode" else "bf16"
     if args.traffic:
-        traffic_from_counters(args.traffic[0], args.traffic[1], wl.name,
-                              os.path.join(PROFILES, f"traffic_{wl.name}.json"))
+        traffic_from_counters(args.traffic[0], args.traffic[1], traffic_name(wl, kfmt),
+                              os.path.join(PROFILES, f"traffic_{traffic_name(wl, kfmt)}.json"))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path shards by sequence "
@@ -914,7 +920,7 @@ def main():
             log("profile run done")
             return
         main_res, layers = run_decode(wl, dev, stream, args.steps, args.warmup, kfmt, graph=not args.no_graph)
-        traffic = load_traffic(wl) if kfmt == "bf16" else None  # counters are taken with bf16 keys
+        traffic = load_traffic(wl, kfmt)
         t_op = traffic["ops"].get(main_res["roofline"]["kernel"]) if traffic else None
         main_res["roofline"]["traffic"] = t_op["bytes_per_launch"] if t_op else None
         cpu = None
